@@ -1,0 +1,183 @@
+/*
+ * oracle.c — the reference semantics of causal linear-attention sequence
+ * mixing with a fixed d_k x d_v state per head, written as the plain
+ * token-by-token recurrence in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker for the HIP path.  Only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It shares no code, header or constant with the HIP library and it
+ * never sees a value that the HIP library produced.
+ *
+ * Sources (page titles as published):
+ *   [LAV]  "Linear Attention, Visualized" (snowchord.com; wpnews.pro copy)
+ *   [BA]   "Beyond attention" (learning.iampt.xyz)
+ *   [ASF]  "All sorts of famous Attention Layers" (harsh-ps-2003 blog)
+ *
+ * What is computed, per (batch b, head h), independently, for t = 1..T, with
+ * S_0 given (zero when no initial state is passed):
+ *
+ *   a_t  = exp(g_t)          log-gate g; scalar per token, or one value per
+ *                            key channel (row of S).  No gate: a_t = 1.
+ *   S'   = a_t * S_{t-1}     scalar gate: the whole state shrinks
+ *                            ([LAV] "Mamba-2: input-dependent scalar decay",
+ *                             [BA] "Three ways to update the state": Decay)
+ *        = Diag(a_t) S_{t-1} channel gate: row i (key channel i) shrinks by
+ *                            a_t[i] ([LAV] "Gated Linear Attention (GLA)")
+ *   add  : S_t = S' + k_t^T v_t
+ *                            ([LAV] "Naive linear attention"; [BA] "Add")
+ *   delta: vhat = k_t S' ; u = beta_t (v_t - vhat) ; S_t = S' + k_t^T u
+ *                            ([LAV] "DeltaNet: correcting memory collisions",
+ *                             recurrent form with the scaled correction u_t;
+ *                             [ASF] "DeltaNet": read v_old at k, write the
+ *                             beta-scaled difference).  With a gate this is
+ *                             Gated DeltaNet ([LAV] "Gated DeltaNet (GDN)")
+ *                             and, for a channel gate, Kimi Delta Attention,
+ *                             which decays first and then applies the delta
+ *                             correction ([LAV] "Kimi Delta Attention (KDA)").
+ *   o_t  = q_t S_t           read-out after the token's own write, so the
+ *                            output includes token t ([LAV] "Naive linear
+ *                            attention", inclusive causal mask).
+ *
+ * Row-vector convention as in [LAV] "Self-attention recap": q_t, k_t are
+ * 1 x d_k, v_t is 1 x d_v, S is d_k x d_v, stored row-major (S[i*dv + j]).
+ * No query scaling, no normaliser: neither appears in the read-out on [LAV].
+ *
+ * Arithmetic: IEEE fp64, plain loops, fixed order per head.  OpenMP
+ * parallelises over independent (b, h) pairs only, so the result does not
+ * depend on the thread count.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_RULE_ADD = 0, ORACLE_RULE_DELTA = 1 };
+enum { ORACLE_GATE_NONE = 0, ORACLE_GATE_SCALAR = 1, ORACLE_GATE_CHANNEL = 2 };
+
+/* One token of one head, in place on S (dk x dv).  u is dv doubles of scratch. */
+static void token_update(int dk, int dv, int rule, int gate,
+                         const double *q, const double *k, const double *v,
+                         const double *g, double beta,
+                         double *S, double *o, double *u)
+{
+    int i, j;
+    /* decay the previous state: S' = a S (scalar) or Diag(a) S (channel) */
+    if (gate == ORACLE_GATE_SCALAR) {
+        double a = exp(g[0]);
+        for (i = 0; i < dk * dv; ++i) S[i] *= a;
+    } else if (gate == ORACLE_GATE_CHANNEL) {
+        for (i = 0; i < dk; ++i) {
+            double a = exp(g[i]);
+            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
+        }
+    }
+    /* the value written at k_t: v itself (add) or beta (v - k S') (delta) */
+    if (rule == ORACLE_RULE_DELTA) {
+        for (j = 0; j < dv; ++j) {
+            double vhat = 0.0;
+            for (i = 0; i < dk; ++i) vhat += k[i] * S[(size_t)i * dv + j];
+            u[j] = beta * (v[j] - vhat);
+        }
+    } else {
+        for (j = 0; j < dv; ++j) u[j] = v[j];
+    }
+    /* rank-one write k^T u */
+    for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * u[j];
+    /* read-out o = q S (after the write) */
+    for (j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+        o[j] = acc;
+    }
+}
+
+static int check_args(int64_t B, int64_t H, int64_t T, int dk, int dv, int rule, int gate,
+                      const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, const void *o)
+{
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 2;
+    if (rule != ORACLE_RULE_ADD && rule != ORACLE_RULE_DELTA) return 3;
+    if (gate < ORACLE_GATE_NONE || gate > ORACLE_GATE_CHANNEL) return 3;
+    if (B * H * T > 0 && (!q || !k || !v || !o)) return 1;
+    if (gate != ORACLE_GATE_NONE && B * H * T > 0 && !g) return 1;
+    if (rule == ORACLE_RULE_DELTA && B * H * T > 0 && !beta) return 1;
+    return 0;
+}
+
+/*
+ * Full forward over a sequence.  Layouts (row-major, contiguous):
+ *   q, k  [B,H,T,dk]   v, o  [B,H,T,dv]
+ *   g     [B,H,T] (scalar gate) | [B,H,T,dk] (channel gate) | NULL (no gate)
+ *   beta  [B,H,T] (delta rule)  | NULL (add rule)
+ *   s0    [B,H,dk,dv] or NULL (zero initial state)
+ *   s_final [B,H,dk,dv] or NULL
+ * Returns 0 on success, nonzero on invalid arguments (nothing written).
+ */
+int oracle_recurrence(int64_t B, int64_t H, int64_t T, int dk, int dv, int rule, int gate,
+                      const double *q, const double *k, const double *v,
+                      const double *g, const double *beta, const double *s0,
+                      double *o, double *s_final, int nthreads)
+{
+    int rc = check_args(B, H, T, dk, dv, rule, gate, q, k, v, g, beta, o);
+    if (rc) return rc;
+    int64_t nheads = B * H;
+    size_t ss = (size_t)dk * dv;
+    int64_t bh;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (bh = 0; bh < nheads; ++bh) {
+        double *S = (double *)malloc(ss * sizeof(double));
+        double *u = (double *)malloc((size_t)dv * sizeof(double));
+        if (!S || !u) { free(S); free(u); failed |= 1; continue; }
+        if (s0) memcpy(S, s0 + (size_t)bh * ss, ss * sizeof(double));
+        else memset(S, 0, ss * sizeof(double));
+        int64_t t;
+        for (t = 0; t < T; ++t) {
+            size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+            const double *gt = NULL;
+            if (gate == ORACLE_GATE_SCALAR) gt = g + tok;
+            else if (gate == ORACLE_GATE_CHANNEL) gt = g + tok * dk;
+            double bt = (rule == ORACLE_RULE_DELTA) ? beta[tok] : 0.0;
+            token_update(dk, dv, rule, gate, q + tok * dk, k + tok * dk, v + tok * dv,
+                         gt, bt, S, o + tok * dv, u);
+        }
+        if (s_final) memcpy(s_final + (size_t)bh * ss, S, ss * sizeof(double));
+        free(S);
+        free(u);
+    }
+    return failed ? 6 : 0;
+}
+
+/*
+ * One decode step: the same recurrence with one token per (sequence n, head h),
+ * applied to the state in place.  Layouts: q, k [N,H,dk]; v, o [N,H,dv];
+ * g [N,H] | [N,H,dk] | NULL; beta [N,H] | NULL; state [N,H,dk,dv] (in/out).
+ */
+int oracle_decode_step(int64_t N, int64_t H, int dk, int dv, int rule, int gate,
+                       const double *q, const double *k, const double *v,
+                       const double *g, const double *beta, double *state,
+                       double *o, int nthreads)
+{
+    int rc = check_args(N, H, 1, dk, dv, rule, gate, q, k, v, g, beta, o);
+    if (rc) return rc;
+    if (N * H > 0 && !state) return 1;
+    return oracle_recurrence(N, H, 1, dk, dv, rule, gate, q, k, v, g, beta, state, o, state,
+                             nthreads);
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,160 @@
+"""Python face of the fp64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  The oracle is the checker for the HIP library: only
+the tests, the smoke check and the benchmark's CPU-baseline leg may import it.
+It imports nothing from the HIP package and the HIP package never imports it.
+
+``recurrence`` runs the token-by-token recurrence of causal linear attention
+(add rule, decay with a scalar or per-key-channel gate, delta rule) described
+in ``oracle.c``; ``decode_step`` runs one token per (sequence, head) in place.
+Every input is widened to float64 exactly (bf16 and fp32 values are exact in
+fp64), so the oracle sees the very values a GPU kernel received.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+RULES = {"add": 0, "delta": 1}
+GATES = {"none": 0, "scalar": 1, "channel": 2}
+
+_lock = threading.Lock()
+_default = None
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a CPU torch tensor (bf16 included): widen exactly
+        import torch
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile ``oracle.c`` (or another source, e.g. in a test) with gcc:
+    fp64, no fast-math, no FMA contraction, OpenMP over heads."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-o", tmp, src, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+class OracleLib:
+    """ctypes handle on one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        d = ctypes.POINTER(ctypes.c_double)
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        lib.oracle_recurrence.argtypes = [i64, i64, i64, i32, i32, i32, i32,
+                                          d, d, d, d, d, d, d, d, i32]
+        lib.oracle_recurrence.restype = i32
+        lib.oracle_decode_step.argtypes = [i64, i64, i32, i32, i32, i32,
+                                           d, d, d, d, d, d, d, i32]
+        lib.oracle_decode_step.restype = i32
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i32
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    def recurrence(self, q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar",
+                   nthreads: int = 0):
+        """fp64 token recurrence.  Shapes: q,k [B,H,T,dk]; v [B,H,T,dv];
+        g [B,H,T] or [B,H,T,dk]; beta [B,H,T]; s0 [B,H,dk,dv].
+        Returns (o [B,H,T,dv], S_T [B,H,dk,dv]) as float64 arrays."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        g, beta, s0 = _f64(g), _f64(beta), _f64(s0)
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        if k.shape != (B, H, T, dk) or v.shape != (B, H, T, dv):
+            raise ValueError("q/k/v shapes disagree")
+        if gate == "scalar" and (g is None or g.shape != (B, H, T)):
+            raise ValueError("scalar gate needs g of shape [B,H,T]")
+        if gate == "channel" and (g is None or g.shape != (B, H, T, dk)):
+            raise ValueError("channel gate needs g of shape [B,H,T,dk]")
+        if rule == "delta" and (beta is None or beta.shape != (B, H, T)):
+            raise ValueError("delta rule needs beta of shape [B,H,T]")
+        if s0 is not None and s0.shape != (B, H, dk, dv):
+            raise ValueError("s0 must be [B,H,dk,dv]")
+        if gate == "none":
+            g = None
+        if rule == "add":
+            beta = None
+        o = np.empty((B, H, T, dv), dtype=np.float64)
+        s = np.empty((B, H, dk, dv), dtype=np.float64)
+        rc = self.lib.oracle_recurrence(B, H, T, dk, dv, RULES[rule], GATES[gate],
+                                        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(s0), _ptr(o), _ptr(s), int(nthreads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_recurrence failed with code {rc}")
+        return o, s
+
+    def decode_step(self, q, k, v, g, beta, state, *, rule="delta", gate="scalar",
+                    nthreads: int = 0):
+        """One recurrent step for N sequences x H heads.  Shapes: q,k [N,H,dk];
+        v [N,H,dv]; g [N,H] or [N,H,dk]; beta [N,H]; state [N,H,dk,dv].
+        Returns (o [N,H,dv], new_state) as float64; the input is not modified."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        g, beta = _f64(g), _f64(beta)
+        st = np.array(_f64(state), dtype=np.float64, copy=True)
+        N, H, dk = q.shape
+        dv = v.shape[-1]
+        if st.shape != (N, H, dk, dv):
+            raise ValueError("state must be [N,H,dk,dv]")
+        if gate == "none":
+            g = None
+        if rule == "add":
+            beta = None
+        o = np.empty((N, H, dv), dtype=np.float64)
+        rc = self.lib.oracle_decode_step(N, H, dk, dv, RULES[rule], GATES[gate],
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(st), _ptr(o), int(nthreads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_decode_step failed with code {rc}")
+        return o, st
+
+
+def default() -> OracleLib:
+    """The oracle built from ``oracle.c`` in this directory."""
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            _default = OracleLib(_LIB)
+    return _default
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+def recurrence(*args, **kw):
+    """See :meth:`OracleLib.recurrence`."""
+    return default().recurrence(*args, **kw)
+
+
+def decode_step(*args, **kw):
+    """See :meth:`OracleLib.decode_step`."""
+    return default().decode_step(*args, **kw)

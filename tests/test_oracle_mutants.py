@@ -1,0 +1,60 @@
+"""Plant plausible mistakes into copies of the oracle (on the CPU) and check
+that every one of them trips at least one pin.  The real oracle source is
+never modified: each mutant is a text edit of ``oracle/oracle.c`` compiled
+into a temporary directory."""
+import os
+
+import pytest
+
+import oracle
+from oracle.oracle import _SRC, OracleLib
+from pins import PINS
+
+WRITE = "for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * u[j];"
+READ_BLOCK = """    for (j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+        o[j] = acc;
+    }"""
+
+# (name, [(old, new), ...]) — each `old` must occur in oracle.c exactly once.
+MUTANTS = [
+    ("delta_sign", [("u[j] = beta * (v[j] - vhat);", "u[j] = beta * (v[j] + vhat);")]),
+    ("delta_no_beta", [("u[j] = beta * (v[j] - vhat);", "u[j] = (v[j] - vhat);")]),
+    ("predict_with_query", [("vhat += k[i] * S[(size_t)i * dv + j];",
+                             "vhat += q[i] * S[(size_t)i * dv + j];")]),
+    ("read_with_key", [("acc += q[i] * S[(size_t)i * dv + j];",
+                        "acc += k[i] * S[(size_t)i * dv + j];")]),
+    ("read_before_write", [("    /* rank-one write k^T u */\n    for (i = 0; i < dk; ++i)\n        " + WRITE,
+                            "    /* rank-one write moved below */"),
+                           (READ_BLOCK, READ_BLOCK + "\n    for (i = 0; i < dk; ++i)\n        " + WRITE)]),
+    ("gate_off_by_one", [("if (gate == ORACLE_GATE_SCALAR) gt = g + tok;",
+                          "if (gate == ORACLE_GATE_SCALAR) gt = g + (t > 0 ? tok - 1 : tok);")]),
+    ("beta_off_by_one", [("? beta[tok] : 0.0;", "? beta[t > 0 ? tok - 1 : tok] : 0.0;")]),
+    ("channel_gate_reversed", [("double a = exp(g[i]);", "double a = exp(g[dk - 1 - i]);")]),
+    ("channel_gate_first_only", [("double a = exp(g[i]);", "double a = exp(g[0]);")]),
+    ("scalar_gate_not_exp", [("double a = exp(g[0]);", "double a = 1.0 + g[0];")]),
+    ("ignore_initial_state", [("if (s0) memcpy(", "if (0) memcpy(")]),
+    ("write_uses_v_not_u", [(WRITE, WRITE.replace("u[j]", "v[j]"))]),
+    ("write_half", [(WRITE, WRITE.replace("k[i] * u[j]", "0.5 * k[i] * u[j]"))]),
+]
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, edits):
+    src = open(_SRC).read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+        src = src.replace(old, new)
+    path = os.path.join(tmp_path, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = oracle.build(force=True, src=path, out=os.path.join(tmp_path, f"lib{name}.so"))
+    orc = OracleLib(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passes every pin"
