@@ -1,0 +1,221 @@
+"""Benchmark: chunkwise forward (gated delta rule, B=8, H=16, T=8192,
+dk=dv=128, bf16 tokens, fp32 state, chunk 64) and the decode step (256
+sequences x 32 heads, dk=dv=128, fp32 state, bf16 tokens, 1000 steps) on one
+MI355X.
+
+One step = one chunkwise forward over the whole batch; ``value`` is its
+throughput in tokens/s (B*T per step).  The decode step is timed separately
+over its own step count and reported under ``decode`` as state GB/s against
+the HBM peak.  Inputs are seeded synthetic tensors already resident in HBM
+when timing starts.  Kernel times come from HIP events recorded on the stream
+the kernels are launched on (torch's current stream).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s chunk fwd (H=16,d=128,T=8192) + decode state GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def chunk_alg_bytes(B, H, T, dk, dv, s, rule, gate, with_state=True):
+    """Bytes the chunk forward must move at minimum: q, k, v in, o out, the
+    gate and beta, the fp32 final state."""
+    per_tok = (2 * dk + 2 * dv) * s
+    if gate == "scalar":
+        per_tok += s
+    elif gate == "channel":
+        per_tok += dk * s
+    if rule == "delta":
+        per_tok += s
+    return B * H * T * per_tok + (B * H * dk * dv * 4 if with_state else 0)
+
+
+def chunk_nominal_flops(B, H, T, dk, dv, rule, C=64):
+    """Nominal FLOPs per head-token at chunk size C (dense C x C tiles, the
+    O(C^2) triangular solve excluded)."""
+    if rule == "delta":
+        f = 2 * (3 * C * dk + 2 * C * dv + 3 * dk * dv)
+    else:
+        f = 2 * (C * dk + C * dv + 2 * dk * dv)
+    return B * H * T * f
+
+
+def decode_alg_bytes(N, H, dk, dv, s, rule, gate):
+    per_head = 2 * dk * dv * 4 + (2 * dk + 2 * dv) * s
+    if gate == "scalar":
+        per_head += s
+    elif gate == "channel":
+        per_head += dk * s
+    if rule == "delta":
+        per_head += s
+    return N * H * per_head
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="heads of the workload the CPU oracle runs for its baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              "multi-GPU path; each head's recurrence is independent, so a multi-GPU run "
+              "would shard heads with no communication", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_27_amd as la
+    import synthetic as syn
+    if not os.path.exists(la.LIB_PATH):
+        from gated_delta_rule_27_amd import build
+        build.build(verbose=False)
+    la.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- chunkwise forward -------------------------------------
+    case = syn.CFG3
+    B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
+    x = syn.chunk_inputs_torch(case, dev)
+    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        la.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, rule=case.rule,
+                     gate=case.gate, out=out, s_final=s_fin)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = B * T / (ms * 1e-3)
+    abytes = chunk_alg_bytes(B, H, T, dk, dv, 2, case.rule, case.gate)
+    aflops = chunk_nominal_flops(B, H, T, dk, dv, case.rule)
+    gbps = abytes / (ms * 1e-3) / 1e9
+    tflops = aflops / (ms * 1e-3) / 1e12
+
+    # ---------------- decode step --------------------------------------------
+    decode = None
+    if args.decode_steps > 0:
+        dc = syn.CFG5
+        nsteps = args.decode_steps
+        tok = syn.decode_tokens_torch(dc, nsteps, dev)
+        state = syn.decode_state_torch(dc, dev)
+        od = torch.empty((dc.N, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
+
+        def dstep(i):
+            la.decode_step(tok["q"][i], tok["k"][i], tok["v"][i], tok["g"][i], tok["beta"][i],
+                           state, rule=dc.rule, gate=dc.gate, out=od)
+
+        for i in range(min(10, nsteps)):
+            dstep(i)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for i in range(nsteps):
+            dstep(i)
+        d1.record()
+        torch.cuda.synchronize()
+        us = d0.elapsed_time(d1) * 1e3 / nsteps
+        dbytes = decode_alg_bytes(dc.N, dc.H, dc.dk, dc.dv, 2, dc.rule, dc.gate)
+        dgbps = dbytes / (us * 1e-6) / 1e9
+        decode = {
+            "workload": f"gdn_decode N={dc.N} H={dc.H} dk={dc.dk} dv={dc.dv} bf16 tokens, "
+                        f"fp32 state, {nsteps} steps",
+            "us_per_step": round(us, 3),
+            "tokens_per_s": round(dc.N / (us * 1e-6), 1),
+            "state_GBps": round(dgbps, 1),
+            "hbm_frac": round(dgbps / HBM_PEAK_GBPS, 4),
+            "alg_bytes_per_step": dbytes,
+        }
+        del tok, state
+
+    # ---------------- CPU oracle baseline ------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        import oracle
+        nh = max(1, min(args.cpu_heads, B * H))
+        sel = lambda t: t.reshape(B * H, *t.shape[2:])[:nh].unsqueeze(0).to("cpu", torch.float64).numpy()
+        xs = {n: sel(x[n]) for n in ("q", "k", "v", "g", "beta")}
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        oracle.recurrence(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], None, rule=case.rule,
+                          gate=case.gate, nthreads=cores)
+        wall = time.perf_counter() - t0
+        cpu = {
+            "value": round(nh * T / H / wall, 1),
+            "unit": "tokens/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": f"{nh} of {B * H} heads x {T} tokens of the same workload (fp64 "
+                      f"token recurrence, OpenMP over heads), {wall:.2f} s wall; tokens/s = "
+                      f"head-tokens / {H} heads / wall",
+            "cpu_model": cpu_model(),
+        }
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gdn_chunk_fwd B={B} H={H} T={T} dk={dk} dv={dv} chunk=64 "
+                               f"bf16 tokens fp32 state",
+                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
+                   "rule": case.rule, "gate": case.gate, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "chunk_fused_kernel", "alg_bytes_per_launch": abytes},
+        "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 2),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "nominal_flops_per_launch": aflops},
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

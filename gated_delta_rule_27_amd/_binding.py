@@ -1,0 +1,206 @@
+"""ctypes binding of ``liblinattn.so`` (see ``include/linattn.h``).
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity), their device pointers and torch's current HIP stream are handed
+to the C ABI, and a nonzero status becomes an exception.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblinattn.so")
+
+RULES = {"add": 0, "delta": 1}
+GATES = {"none": 0, "scalar": 1, "channel": 2}
+DTYPES = {"fp32": 0, "bf16": 1}
+
+# Every function the header declares; a test checks the two stay in step.
+EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_workspace_bytes",
+           "linattn_chunk_fwd", "linattn_decode_step")
+
+
+class LinattnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class ChunkArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("rule", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("rule", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it first (python -m gated_delta_rule_27_amd.build "
+                "or __graft_entry__.build()); there is no non-HIP fallback")
+        lib = ctypes.CDLL(path)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.linattn_abi_version.argtypes = []
+        lib.linattn_abi_version.restype = ctypes.c_int
+        lib.linattn_status_string.argtypes = [ctypes.c_int]
+        lib.linattn_status_string.restype = ctypes.c_char_p
+        lib.linattn_chunk_workspace_bytes.argtypes = [ctypes.POINTER(ChunkArgs)]
+        lib.linattn_chunk_workspace_bytes.restype = sz
+        lib.linattn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkArgs), vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, sz, vp]
+        lib.linattn_chunk_fwd.restype = ctypes.c_int
+        lib.linattn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), vp, vp, vp, vp, vp, vp,
+                                            vp, vp]
+        lib.linattn_decode_step.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return int(load().linattn_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load().linattn_status_string(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _token_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "fp32"
+    raise TypeError(f"token tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_args(B, H, T, dk, dv, *, rule, gate, dtype, chunk=64) -> ChunkArgs:
+    return ChunkArgs(B, H, T, dk, dv, chunk, RULES[rule], GATES[gate], DTYPES[dtype])
+
+
+def chunk_workspace_bytes(B, H, T, dk, dv, *, rule, gate, dtype="bf16", chunk=64) -> int:
+    a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=dtype, chunk=chunk)
+    return int(load().linattn_chunk_workspace_bytes(ctypes.byref(a)))
+
+
+def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar", chunk=64,
+              out=None, s_final=None, return_state=True, workspace=None):
+    """Chunkwise forward over whole sequences on the GPU.
+
+    q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] (scalar gate) or [B,H,T,dk]
+    (channel gate) or None; beta [B,H,T] (delta rule) or None; s0
+    [B,H,dk,dv] fp32 or None.  Returns (o [B,H,T,dv], S_T [B,H,dk,dv] fp32 or
+    None).  Runs on torch's current stream of q's device, asynchronously.
+    """
+    import torch
+    lib = load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    dtype = _token_dtype(q)
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    if gate == "scalar":
+        _check(g, "g", (B, H, T), dt, dev)
+    elif gate == "channel":
+        _check(g, "g", (B, H, T, dk), dt, dev)
+    elif g is not None:
+        raise ValueError("g must be None when gate='none'")
+    if rule == "delta":
+        _check(beta, "beta", (B, H, T), dt, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None for the add rule")
+    if s0 is not None:
+        _check(s0, "s0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    if s_final is None and return_state:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif s_final is not None:
+        _check(s_final, "s_final", (B, H, dk, dv), torch.float32, dev)
+    a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=dtype, chunk=chunk)
+    need = int(lib.linattn_chunk_workspace_bytes(ctypes.byref(a)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(s0), _ptr(out), _ptr(s_final), _ptr(workspace), ws_bytes,
+                               stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_chunk_fwd")
+    return out, s_final
+
+
+def decode_step(q, k, v, g, beta, state, *, rule="delta", gate="scalar", out=None):
+    """One decode step for N sequences x H heads; ``state`` [N,H,dk,dv] fp32 is
+    updated in place.  q, k [N,H,dk]; v [N,H,dv]; g [N,H] | [N,H,dk] | None;
+    beta [N,H] | None.  Returns o [N,H,dv]."""
+    import torch
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    dtype = _token_dtype(q)
+    _check(k, "k", (N, H, dk), dt, dev)
+    _check(v, "v", (N, H, dv), dt, dev)
+    _check(q, "q", (N, H, dk), dt, dev)
+    if gate == "scalar":
+        _check(g, "g", (N, H), dt, dev)
+    elif gate == "channel":
+        _check(g, "g", (N, H, dk), dt, dev)
+    elif g is not None:
+        raise ValueError("g must be None when gate='none'")
+    if rule == "delta":
+        _check(beta, "beta", (N, H), dt, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None for the add rule")
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, H, dv), dt, dev)
+    a = DecodeArgs(N, H, dk, dv, RULES[rule], GATES[gate], DTYPES[dtype])
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_decode_step(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(out), stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_decode_step")
+    return out

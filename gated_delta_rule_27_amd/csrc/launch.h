@@ -1,0 +1,46 @@
+// launch.h — internal interface between the C-ABI layer (linattn_api.hip) and
+// the kernel files.  Problems arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace linattn {
+
+enum { kRuleAdd = 0, kRuleDelta = 1 };
+enum { kGateNone = 0, kGateScalar = 1, kGateChannel = 2 };
+enum { kF32 = 0, kBF16 = 1 };
+
+struct DecodeProblem {
+    int64_t N, H;
+    int dk, dv, rule, gate, dtype;
+    const void *q, *k, *v, *g, *beta;
+    float* state;
+    void* o;
+};
+
+struct ChunkProblem {
+    int64_t B, H, T;
+    int dk, dv, chunk, rule, gate, dtype;
+    const void *q, *k, *v, *g, *beta;
+    const float* s0;
+    void* o;
+    float* s_final;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+hipError_t launch_decode_step(const DecodeProblem& p, hipStream_t stream);
+
+// Single-pass chunk kernel (gate NONE or SCALAR).
+bool chunk_fused_supported(const ChunkProblem& p);
+hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t stream);
+
+// Two-kernel chunk path (intra-chunk precompute, then the state pass with the
+// output); used for the per-channel gate.
+bool chunk_split_supported(const ChunkProblem& p);
+size_t chunk_split_workspace_bytes(const ChunkProblem& p);
+hipError_t launch_chunk_split(const ChunkProblem& p, hipStream_t stream);
+
+}  // namespace linattn

@@ -1,0 +1,153 @@
+// linattn_api.hip — the C ABI declared in include/linattn.h: argument
+// validation (before anything is enqueued) and dispatch to the kernels.
+#include "../../include/linattn.h"
+#include "launch.h"
+
+#include <hip/hip_runtime.h>
+
+using namespace linattn;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+linattn_status check_enums(int rule, int gate, int dtype)
+{
+    if (rule != LINATTN_RULE_ADD && rule != LINATTN_RULE_DELTA) return LINATTN_ERR_ARG;
+    if (gate != LINATTN_GATE_NONE && gate != LINATTN_GATE_SCALAR && gate != LINATTN_GATE_CHANNEL)
+        return LINATTN_ERR_ARG;
+    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_ARG;
+    return LINATTN_OK;
+}
+
+// Shared pointer checks: required tensors present, gate/beta present exactly
+// when the rule/gate need them, everything 16-byte aligned.
+linattn_status check_pointers(int rule, int gate, const void* q, const void* k, const void* v,
+                              const void* g, const void* beta, const void* st, const void* o)
+{
+    if (!q || !k || !v || !o || !st) return LINATTN_ERR_NULL;
+    if ((gate == LINATTN_GATE_NONE) != (g == nullptr)) return g ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
+    if ((rule == LINATTN_RULE_DELTA) != (beta != nullptr))
+        return beta ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, g, beta, st, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return LINATTN_ERR_UNSUPPORTED;
+    return LINATTN_OK;
+}
+
+linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
+{
+    if (!a) return LINATTN_ERR_NULL;
+    if (a->B < 0 || a->H < 0 || a->T < 0 || a->dk <= 0 || a->dv <= 0 || a->chunk < 0)
+        return LINATTN_ERR_SHAPE;
+    linattn_status st = check_enums(a->rule, a->gate, a->dtype);
+    if (st != LINATTN_OK) return st;
+    int64_t bh, bht, tot;
+    if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->T, &bht) ||
+        !mul_ok(bht, (int64_t)(a->dk > a->dv ? a->dk : a->dv), &tot) || bh > (int64_t)INT32_MAX)
+        return LINATTN_ERR_SHAPE;
+    if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv)) return LINATTN_ERR_UNSUPPORTED;
+    p->B = a->B; p->H = a->H; p->T = a->T;
+    p->dk = a->dk; p->dv = a->dv;
+    p->chunk = a->chunk == 0 ? 64 : a->chunk;
+    p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
+    const bool fused = p->gate != kGateChannel;
+    if (fused ? !chunk_fused_supported(*p) : !chunk_split_supported(*p))
+        return LINATTN_ERR_UNSUPPORTED;
+    return LINATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int linattn_abi_version(void) { return LINATTN_ABI_VERSION; }
+
+const char* linattn_status_string(int s)
+{
+    switch (s) {
+    case LINATTN_OK: return "ok";
+    case LINATTN_ERR_NULL: return "a required pointer is NULL";
+    case LINATTN_ERR_SHAPE: return "invalid or overflowing sizes";
+    case LINATTN_ERR_UNSUPPORTED: return "unsupported head size, chunk size, dtype or alignment";
+    case LINATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case LINATTN_ERR_LAUNCH: return "kernel launch failed";
+    case LINATTN_ERR_ARG: return "inconsistent arguments";
+    default: return "unknown status";
+    }
+}
+
+size_t linattn_chunk_workspace_bytes(const linattn_chunk_args* a)
+{
+    ChunkProblem p{};
+    if (validate_chunk(a, &p) != LINATTN_OK) return 0;
+    if (p.gate != kGateChannel) return 0;
+    return chunk_split_workspace_bytes(p);
+}
+
+linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, const void* k,
+                                 const void* v, const void* g, const void* beta, const float* s0,
+                                 void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                                 void* stream)
+{
+    ChunkProblem p{};
+    linattn_status st = validate_chunk(a, &p);
+    if (st != LINATTN_OK) return st;
+    if (p.B * p.H == 0) return LINATTN_OK;
+    // q,k,v,o may be absent only when there are no tokens; pass q as the
+    // stand-in for the state pointer check in that case.
+    if (p.T > 0) {
+        st = check_pointers(p.rule, p.gate, q, k, v, g, beta, q, o);
+        if (st != LINATTN_OK) return st;
+    }
+    if ((s0 && !aligned16(s0)) || (s_final && !aligned16(s_final))) return LINATTN_ERR_UNSUPPORTED;
+    // s_final may alias s0 exactly, but must not partially overlap it
+    if (s0 && s_final && s0 != s_final) {
+        const char* a0 = reinterpret_cast<const char*>(s0);
+        const char* a1 = reinterpret_cast<const char*>(s_final);
+        const size_t n = (size_t)(p.B * p.H) * p.dk * p.dv * sizeof(float);
+        if (a0 < a1 + n && a1 < a0 + n) return LINATTN_ERR_ARG;
+    }
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s0 = s0; p.o = o; p.s_final = s_final;
+    p.workspace = workspace; p.workspace_bytes = workspace_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (p.gate != kGateChannel) {
+        err = launch_chunk_fused(p, s);
+    } else {
+        const size_t need = chunk_split_workspace_bytes(p);
+        if (need > 0 && (!workspace || workspace_bytes < need)) return LINATTN_ERR_WORKSPACE;
+        if (workspace && !aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+        err = launch_chunk_split(p, s);
+    }
+    return err == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+}
+
+linattn_status linattn_decode_step(const linattn_decode_args* a, const void* q, const void* k,
+                                   const void* v, const void* g, const void* beta, float* state,
+                                   void* o, void* stream)
+{
+    if (!a) return LINATTN_ERR_NULL;
+    if (a->N < 0 || a->H < 0 || a->dk <= 0 || a->dv <= 0) return LINATTN_ERR_SHAPE;
+    linattn_status st = check_enums(a->rule, a->gate, a->dtype);
+    if (st != LINATTN_OK) return st;
+    int64_t heads, tot;
+    if (!mul_ok(a->N, a->H, &heads) || !mul_ok(heads, (int64_t)a->dk * a->dv, &tot) ||
+        heads > (int64_t)INT32_MAX)
+        return LINATTN_ERR_SHAPE;
+    if (!head_dim_ok(a->dk) || !head_dim_ok(a->dv)) return LINATTN_ERR_UNSUPPORTED;
+    if (heads == 0) return LINATTN_OK;
+    st = check_pointers(a->rule, a->gate, q, k, v, g, beta, state, o);
+    if (st != LINATTN_OK) return st;
+    DecodeProblem p{a->N, a->H, a->dk, a->dv, a->rule, a->gate, a->dtype,
+                    q, k, v, g, beta, state, o};
+    hipError_t err = launch_decode_step(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

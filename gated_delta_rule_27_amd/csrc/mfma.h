@@ -1,0 +1,107 @@
+// mfma.h — 16x16 matrix-core tile helpers for gfx950 (CDNA4, wave64).
+//
+// Every product here is written as D = A * B^T with both operands stored
+// row-major with the contraction index contiguous ("NT" form), so each lane's
+// operand fragment is one contiguous LDS read.  Fragment layouts:
+//   bf16 v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][k0+8(l/16) .. +7]
+//   fp32 v_mfma_f32_16x16x4_f32:   lane l holds A[l%16][k0+(l/16)]
+// (B the same with its own rows), and the 16x16 fp32 result is spread as
+//   lane l, register r  <->  D[4(l/16)+r][l%16].
+// Writing a result tile "transposed" (dst[col][row..row+3]) is therefore a
+// single 4-element contiguous store per lane; the kernels use that to produce
+// whichever orientation the next product needs.
+#pragma once
+
+#include "device_common.h"
+
+namespace linattn {
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+    static constexpr int kStep = 32;
+    typedef bf16x8 frag;
+    __device__ static __forceinline__ floatx4 mma(frag a, frag b, floatx4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ frag load(const bf16* row0, int ld, int k0, int lane)
+    {
+        return *reinterpret_cast<const frag*>(row0 + (lane & 15) * ld + k0 + 8 * (lane >> 4));
+    }
+};
+
+template <> struct Mfma<float> {
+    static constexpr int kStep = 4;
+    typedef float frag;
+    __device__ static __forceinline__ floatx4 mma(frag a, frag b, floatx4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ frag load(const float* row0, int ld, int k0, int lane)
+    {
+        return row0[(lane & 15) * ld + k0 + (lane >> 4)];
+    }
+};
+
+// acc += A[0:16][kb:ke] * B[0:16][kb:ke]^T, A and B pointing at their first row.
+template <typename T>
+__device__ __forceinline__ floatx4 mma_nt(floatx4 acc, const T* A, int lda, const T* B, int ldb,
+                                          int kb, int ke, int lane)
+{
+    for (int k = kb; k < ke; k += Mfma<T>::kStep)
+        acc = Mfma<T>::mma(Mfma<T>::load(A, lda, k, lane), Mfma<T>::load(B, ldb, k, lane), acc);
+    return acc;
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// Store the 4 values a lane holds of a result tile D (rows 4(l/16)+r, column
+// l%16) into dst as D^T: dst[(l%16)*ld + 4(l/16) + r], r = 0..3.
+template <typename T>
+__device__ __forceinline__ void store_tile_t(T* dst, int ld, floatx4 v, int lane)
+{
+    T* p = dst + (lane & 15) * ld + 4 * (lane >> 4);
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 w;
+        w[0] = from_f32<bf16>(v[0]); w[1] = from_f32<bf16>(v[1]);
+        w[2] = from_f32<bf16>(v[2]); w[3] = from_f32<bf16>(v[3]);
+        *reinterpret_cast<bf16x4*>(p) = w;
+    } else {
+        *reinterpret_cast<floatx4*>(p) = v;
+    }
+}
+
+// 16x16x16 product with fp32 operands held in fp32: A from LDS (row-major,
+// lane reads A[l%16][4(l/16)..+3]), B given in the result layout (lane holds
+// B[4(l/16)+r][l%16]).  The contraction index is assigned to (lane group,
+// register) as k = 4(l/16)+r on both sides, so a previous result tile can be
+// fed straight back as B.  T selects the arithmetic: bf16 operands through
+// v_mfma_f32_16x16x16_bf16, or fp32 through four v_mfma_f32_16x16x4_f32.
+template <typename T>
+__device__ __forceinline__ floatx4 mm16(const float* A, int lda, floatx4 b, floatx4 acc, int lane)
+{
+    const floatx4 a = *reinterpret_cast<const floatx4*>(A + (lane & 15) * lda + 4 * (lane >> 4));
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 ab, bb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { ab[r] = from_f32<bf16>(a[r]); bb[r] = from_f32<bf16>(b[r]); }
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// Load a 16x16 fp32 block from LDS in the result layout (lane holds
+// B[4(l/16)+r][l%16]).
+__device__ __forceinline__ floatx4 load_tile_rl(const float* B, int ldb, int lane)
+{
+    floatx4 b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = B[(4 * (lane >> 4) + r) * ldb + (lane & 15)];
+    return b;
+}
+
+}  // namespace linattn

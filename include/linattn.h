@@ -1,0 +1,147 @@
+/*
+ * linattn.h — C ABI of the MI355X (gfx950) library for causal linear-attention
+ * sequence mixing with a fixed d_k x d_v fp32 state per head.
+ *
+ * The operation (page titles as published):
+ *   "Linear Attention, Visualized" — sections "Naive linear attention" (state
+ *   S_t, inclusive causal read-out), "Mamba-2: input-dependent scalar decay",
+ *   "Gated Linear Attention (GLA)" (per-key-channel decay), "DeltaNet:
+ *   correcting memory collisions" (recurrent form with the scaled correction),
+ *   "Gated DeltaNet (GDN)" and "Kimi Delta Attention (KDA)" (decay first, then
+ *   the delta correction), and "Chunkwise algorithm" (the exact chunk
+ *   regrouping that the prefill kernels use);
+ *   "Beyond attention" — "Three ways to update the state".
+ *
+ * Per (batch b, head h), for t = 1..T, row-vector convention (q_t, k_t are
+ * 1 x dk, v_t is 1 x dv, S is dk x dv; key channel i is row i of S):
+ *   a_t = exp(g_t)                       (g is the log of the forget gate)
+ *   S'  = S_{t-1}                        LINATTN_GATE_NONE
+ *       = a_t S_{t-1}                    LINATTN_GATE_SCALAR  (one g per token)
+ *       = Diag(a_t) S_{t-1}              LINATTN_GATE_CHANNEL (one g per token and key channel)
+ *   LINATTN_RULE_ADD  : S_t = S' + k_t^T v_t
+ *   LINATTN_RULE_DELTA: S_t = S' + k_t^T beta_t (v_t - k_t S')
+ *   o_t = q_t S_t                        (after the write; no query scale, no normaliser)
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays; the
+ *     caller allocates and owns every buffer.  The library never allocates,
+ *     frees or keeps device memory, and holds no mutable global state.
+ *   - Token tensors (q, k, v, g, beta, o) share one dtype (linattn_dtype); the
+ *     state is always fp32.  Every pointer must be 16-byte aligned.
+ *   - Calls only validate arguments and enqueue kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream); they return before the work
+ *     finishes.  Device faults surface at the caller's next synchronisation.
+ *   - A nonzero status means nothing was enqueued (argument errors are found
+ *     before any launch) or, for LINATTN_ERR_LAUNCH, that a launch failed.
+ *   - Thread-safe for distinct buffers; no exception crosses the ABI.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINATTN_ABI_VERSION 1
+
+typedef enum {
+    LINATTN_OK = 0,
+    LINATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    LINATTN_ERR_SHAPE = 2,       /* negative or overflowing sizes */
+    LINATTN_ERR_UNSUPPORTED = 3, /* valid but not built: head size, chunk, dtype, alignment */
+    LINATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    LINATTN_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
+    LINATTN_ERR_ARG = 6          /* inconsistent arguments (rule/gate/pointer mismatch) */
+} linattn_status;
+
+typedef enum { LINATTN_RULE_ADD = 0, LINATTN_RULE_DELTA = 1 } linattn_rule;
+typedef enum { LINATTN_GATE_NONE = 0, LINATTN_GATE_SCALAR = 1, LINATTN_GATE_CHANNEL = 2 } linattn_gate;
+typedef enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 } linattn_dtype;
+
+/* Chunk-forward problem description.  rule/gate/dtype hold the enum values. */
+typedef struct {
+    int64_t B, H, T;   /* batch, heads, tokens per sequence (T >= 0) */
+    int32_t dk, dv;    /* key and value head sizes */
+    int32_t chunk;     /* tokens per chunk C; 0 selects the default (64) */
+    int32_t rule, gate, dtype;
+} linattn_chunk_args;
+
+/* Decode problem description: N sequences x H heads, one token each. */
+typedef struct {
+    int64_t N, H;
+    int32_t dk, dv;
+    int32_t rule, gate, dtype;
+} linattn_decode_args;
+
+/* ABI version the library was built with (LINATTN_ABI_VERSION). */
+int linattn_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *linattn_status_string(int status);
+
+/*
+ * Device workspace, in bytes, that linattn_chunk_fwd needs for this problem:
+ * 0 when the single-pass kernel serves it, else the size of the per-chunk
+ * operand tiles the two-kernel path stages in HBM.  Returns 0 for invalid
+ * arguments as well (linattn_chunk_fwd reports those).
+ */
+size_t linattn_chunk_workspace_bytes(const linattn_chunk_args *a);
+
+/*
+ * Chunkwise-parallel forward over whole sequences (prefill / training
+ * forward).  "Linear Attention, Visualized", "Chunkwise algorithm": within a
+ * chunk the parallel (masked, decay-weighted) form, between chunks the state
+ * recurrence; for the delta rule the per-chunk triangular system
+ * (I + diag(beta) L) is solved once ("Optional: Use UT to share the triangular
+ * transform") and the incoming state corrects the chunk's writes ("Correct the
+ * incoming state").  The result equals the token recurrence above up to
+ * rounding for every chunk size.
+ *
+ *   q, k     [B,H,T,dk]              token dtype
+ *   v        [B,H,T,dv]              token dtype
+ *   g        [B,H,T] (SCALAR) | [B,H,T,dk] (CHANNEL) | NULL (NONE); log-gate, token dtype
+ *   beta     [B,H,T] (DELTA) | NULL (ADD); token dtype
+ *   s0       [B,H,dk,dv] fp32 initial state, or NULL for zero
+ *   o        [B,H,T,dv] output, token dtype (fp32 accumulation)
+ *   s_final  [B,H,dk,dv] fp32 final state, or NULL; may alias s0 exactly
+ *   workspace, workspace_bytes: device scratch of at least
+ *            linattn_chunk_workspace_bytes(a) bytes (may be NULL when that is 0)
+ *   stream   hipStream_t
+ * Supported: dk, dv in {64, 128}; chunk 64; bf16 tokens for any gate; fp32
+ * tokens for dk = 64 with gate NONE or SCALAR.  T need not be a multiple of
+ * the chunk size.
+ */
+linattn_status linattn_chunk_fwd(const linattn_chunk_args *a,
+                                 const void *q, const void *k, const void *v,
+                                 const void *g, const void *beta,
+                                 const float *s0, void *o, float *s_final,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for N sequences x H heads, updating the state in
+ * place ("Linear Attention, Visualized", "Optional: Linear attention as an
+ * RNN" and the DeltaNet recurrent form; "All sorts of famous Attention
+ * Layers", "DeltaNet": read at the key, write the beta-scaled difference, then
+ * read with the query).  Memory-bound: each state is read and written once.
+ *
+ *   q, k   [N,H,dk]                 token dtype
+ *   v      [N,H,dv]                 token dtype
+ *   g      [N,H] | [N,H,dk] | NULL  log-gate (SCALAR | CHANNEL | NONE)
+ *   beta   [N,H] | NULL             (DELTA | ADD)
+ *   state  [N,H,dk,dv] fp32, read and overwritten in place
+ *   o      [N,H,dv] token dtype
+ * Supported: dk, dv in {64, 128}; bf16 or fp32 tokens; every rule and gate.
+ */
+linattn_status linattn_decode_step(const linattn_decode_args *a,
+                                   const void *q, const void *k, const void *v,
+                                   const void *g, const void *beta,
+                                   float *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -130,8 +130,10 @@ int oracle_recurrence(int64_t B, int64_t H, int64_t T, int dk, int dv, int rule,
     int64_t bh;
     int failed = 0;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : failed)
+#else
+    (void)nthreads;
 #endif
     for (bh = 0; bh < nheads; ++bh) {
         double *S = (double *)malloc(ss * sizeof(double));

@@ -216,3 +216,67 @@ def decode_tokens(case: DecodeCase, step: int, seed: int = SEED) -> dict:
         "g": None if case.gate == "none" else g,
         "beta": beta if case.rule == "delta" else None,
     }
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for the benchmark (multi-GB inputs).  Same laws as
+# above, drawn with torch's generator on the device; values differ from the
+# numpy streams, which are the ones parity tests use.
+# ---------------------------------------------------------------------------
+def _torch_laws(t, law):
+    import torch
+    if law == "l2":
+        return t / t.norm(dim=-1, keepdim=True).clamp_min(1e-6)
+    if law == "elu1":
+        return torch.nn.functional.elu(t) + 1.0
+    return t
+
+
+def chunk_inputs_torch(case: Case, device, seed: int = SEED) -> dict:
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000 + (case.case_id if isinstance(case.case_id, int) else 0))
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    shp = (case.B, case.H, case.T)
+    rn = lambda *s: torch.randn(*s, generator=gen, device=device, dtype=torch.float32)
+    out = {"q": _torch_laws(rn(*shp, case.dk), case.qk).to(dt),
+           "k": _torch_laws(rn(*shp, case.dk), case.qk).to(dt),
+           "v": rn(*shp, case.dv).to(dt)}
+    b = torch.sigmoid(rn(*shp))
+    if case.beta_mode == "zero":
+        b = torch.zeros_like(b)
+    elif case.beta_mode == "one":
+        b = torch.ones_like(b)
+    out["beta"] = b.to(dt) if case.rule == "delta" else None
+    gshape = shp + ((case.dk,) if case.gate == "channel" else ())
+    g = -torch.nn.functional.softplus(rn(*gshape)) * case.gate_scale
+    out["g"] = None if case.gate == "none" else g.to(dt)
+    out["s0"] = None
+    return out
+
+
+def decode_tokens_torch(case: DecodeCase, steps: int, device, seed: int = SEED) -> dict:
+    """Tokens for `steps` decode steps at once: q,k [steps,N,H,dk], v [steps,N,H,dv],
+    g [steps,N,H] | [steps,N,H,dk], beta [steps,N,H]."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000 + case.case_id)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    shp = (steps, case.N, case.H)
+    rn = lambda *s: torch.randn(*s, generator=gen, device=device, dtype=torch.float32)
+    out = {"q": _torch_laws(rn(*shp, case.dk), case.qk).to(dt),
+           "k": _torch_laws(rn(*shp, case.dk), case.qk).to(dt),
+           "v": rn(*shp, case.dv).to(dt),
+           "beta": torch.sigmoid(rn(*shp)).to(dt) if case.rule == "delta" else None}
+    gshape = shp + ((case.dk,) if case.gate == "channel" else ())
+    g = -torch.nn.functional.softplus(rn(*gshape)) * case.gate_scale
+    out["g"] = None if case.gate == "none" else g.to(dt)
+    return out
+
+
+def decode_state_torch(case: DecodeCase, device, seed: int = SEED):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000 + case.case_id + 7)
+    return torch.randn(case.N, case.H, case.dk, case.dv, generator=gen, device=device,
+                       dtype=torch.float32) * case.state_std

@@ -1,0 +1,100 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/linattn.h declares, and rejects bad arguments before touching a
+device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_27_amd as la
+from gated_delta_rule_27_amd import _binding as bd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "linattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        from gated_delta_rule_27_amd import build
+        build.build(verbose=False)
+    return la.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(linattn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert names == sorted(bd.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert la.abi_version() == 1
+    for s in range(7):
+        assert la.status_string(s)
+    assert la.status_string(99) == "unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def call_chunk(lib, a, q=FAKE, k=FAKE, v=FAKE, g=None, beta=FAKE, s0=None, o=FAKE, sf=None,
+               ws=None, wsb=0):
+    return lib.linattn_chunk_fwd(ctypes.byref(a), q, k, v, g, beta, s0, o, sf, ws, wsb, None)
+
+
+def test_chunk_validation(lib):
+    mk = lambda **kw: bd.chunk_args(**{**dict(B=1, H=1, T=64, dk=64, dv=64, rule="delta",
+                                              gate="none", dtype="bf16"), **kw})
+    assert lib.linattn_chunk_fwd(None, *([None] * 9), 0, None) == 1
+    assert call_chunk(lib, mk(dk=96)) == 3                       # unsupported head size
+    assert call_chunk(lib, mk(chunk=48)) == 3                    # unsupported chunk
+    assert call_chunk(lib, mk(T=-1)) == 2
+    assert call_chunk(lib, mk(B=1 << 40, H=1 << 30)) == 2        # overflow
+    assert call_chunk(lib, mk(), q=None) == 1
+    assert call_chunk(lib, mk(), beta=None) == 1                 # delta needs beta
+    assert call_chunk(lib, mk(rule="add")) == 6                  # add rule with beta
+    assert call_chunk(lib, mk(gate="scalar")) == 1               # scalar gate needs g
+    assert call_chunk(lib, mk(), g=FAKE) == 6                    # g given without a gate
+    assert call_chunk(lib, mk(), q=FAKE + 8) == 3                # misaligned
+    assert call_chunk(lib, mk(dtype="fp32", dk=128)) == 3        # fp32 needs dk = 64
+    a = mk()
+    a.rule = 7
+    assert call_chunk(lib, a) == 6
+    assert call_chunk(lib, mk(), s0=FAKE, sf=FAKE + 16) == 6     # partial overlap
+    assert call_chunk(lib, mk(B=0)) == 0                         # nothing to do
+    assert lib.linattn_chunk_workspace_bytes(ctypes.byref(mk())) == 0
+
+
+def test_decode_validation(lib):
+    mk = lambda **kw: bd.DecodeArgs(*[{**dict(N=2, H=2, dk=64, dv=64, rule=1, gate=1, dtype=1),
+                                        **kw}[f] for f in ("N", "H", "dk", "dv", "rule", "gate",
+                                                           "dtype")])
+    call = lambda a, **p: lib.linattn_decode_step(
+        ctypes.byref(a), *[p.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "state", "o")],
+        None)
+    assert call(mk(dk=32)) == 3
+    assert call(mk(N=-1)) == 2
+    assert call(mk(), state=None) == 1
+    assert call(mk(), g=None) == 1
+    assert call(mk(gate=0)) == 6
+    assert call(mk(rule=0)) == 6
+    assert call(mk(), o=FAKE + 4) == 3
+    assert call(mk(N=0)) == 0
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        bd._lib_saved = bd._lib
+        try:
+            bd._lib = None
+            bd.load(str(tmp_path / "nope.so"))
+        finally:
+            bd._lib = bd._lib_saved
