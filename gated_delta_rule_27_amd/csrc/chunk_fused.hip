@@ -25,16 +25,26 @@
 //   c1  O = diag(gamma) Q S_r + Aq Z
 // Operands are bf16 (fp32 for fp32 tokens) in LDS, accumulation is fp32; the
 // state stays fp32 and is rounded to the operand type only as an operand.
+//
+// Schedule of one chunk (5 LDS barriers; the next chunk's tokens are loaded
+// into registers during the whole chunk):
+//   P1  registers -> LDS (Q, K, V), gate scan, issue next chunk's loads
+//   P2  K^T, V^T (matrix-core transposes), Aq and N tiles
+//   P3  wave 0: the whole triangular solve (no barrier inside);
+//       waves 1..: R = V - gamma K S_r and the history part gamma Q S_r of O
+//   P4  Z = Tb R
+//   P5  O += Aq Z (to HBM), S_{r+1}
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
+#include "tsolve.h"
 
 namespace linattn {
 
 namespace {
 
 constexpr int kC = 64;      // chunk length
-constexpr int kNW = 4;      // waves per workgroup
+constexpr int kNW = 8;      // waves per workgroup
 constexpr int kNT = kNW * kWave;
 
 template <typename T, int DK, int DVB, int RULE, int GATE>
@@ -43,11 +53,29 @@ struct FusedCfg {
     static constexpr int LDQ = DK + PADE;         // rows of length dk: Qs, Ks, ST
     static constexpr int LDC = kC + PADE;         // rows of length C: KsT, VsT, Aq, Tb, RT, ZT
     static constexpr int LDN = kC + 4;            // fp32 rows of N / T
+    static constexpr int LDV = DVB + PADE;        // row-major V staging
     static constexpr bool DELTA = RULE == kRuleDelta;
     static constexpr bool GATED = GATE == kGateScalar;
-    static constexpr int NS = (DK / 16) * (DVB / 16) / kNW;   // state tiles per wave
-    static_assert((DK / 16) * (DVB / 16) % kNW == 0, "state tiles per wave");
+    static constexpr int NTS = (DK / 16) * (DVB / 16);       // state tiles
+    static constexpr int NS = (NTS + kNW - 1) / kNW;         // state tiles per wave (max)
+    static constexpr int NTO = (DVB / 16) * (kC / 16);       // output / R / Z tiles
+    static constexpr int NOW = DELTA ? kNW - 1 : kNW;        // waves holding O tiles
+    static constexpr int NO = (NTO + NOW - 1) / NOW;         // O tiles per wave (max)
+    static constexpr int E = 16 / sizeof(T);                 // elements per 16-byte load
+    static constexpr int NQ = kC * DK / (E * kNT);           // Q/K vectors per thread
+    static constexpr int NV = (kC * DVB + E * kNT - 1) / (E * kNT);
+    static constexpr int ZSZ = (DVB * LDC > kC * LDV) ? DVB * LDC : kC * LDV;
+    static constexpr int NPAIR = (kC / 16) * (kC / 16 + 1) / 2;   // causal 16x16 tiles
+    static_assert(NQ >= 1 && (kC * DK) % (E * kNT) == 0, "Q/K load split");
 };
+
+// (lj, mi) of the p-th causal tile, mi <= lj, row-major over lj
+__device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
+{
+    lj = 0;
+    while (p > lj) { p -= lj + 1; ++lj; }
+    mi = p;
+}
 
 template <typename T, int DK, int DVB, int RULE, int GATE>
 __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
@@ -56,10 +84,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     float* s_final, int64_t Tlen, int DV, int nblocks)
 {
     using Cfg = FusedCfg<T, DK, DVB, RULE, GATE>;
-    constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDN = Cfg::LDN;
+    constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDN = Cfg::LDN, LDV = Cfg::LDV;
     constexpr bool DELTA = Cfg::DELTA, GATED = Cfg::GATED;
-    constexpr int NS = Cfg::NS;
-    constexpr int E = 16 / sizeof(T);            // elements per 16-byte load
+    constexpr int NS = Cfg::NS, NTS = Cfg::NTS, NTO = Cfg::NTO, NOW = Cfg::NOW, NO = Cfg::NO;
+    constexpr int E = Cfg::E, NQ = Cfg::NQ, NV = Cfg::NV;
+    constexpr int KS = Mfma<T>::kStep;
 
     __shared__ __align__(16) T Qs[kC * LDQ];
     __shared__ __align__(16) T Ks[kC * LDQ];
@@ -67,18 +96,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     __shared__ __align__(16) T VsT[DVB * LDC];
     __shared__ __align__(16) T Aq[kC * LDC];
     __shared__ __align__(16) T ST[2][DVB * LDQ];
-    __shared__ __align__(16) T ZT[DVB * LDC];
+    __shared__ __align__(16) T ZT[Cfg::ZSZ];        // also stages V row-major
     __shared__ __align__(16) T ZrT[GATED ? DVB * LDC : 1];
     __shared__ __align__(16) float Nf[DELTA ? kC * LDN : 4];
     __shared__ __align__(16) T Tb[DELTA ? kC * LDC : 1];
+    __shared__ __align__(16) T RT[DELTA ? DVB * LDC : 1];
     __shared__ float Gs[kC], gam[kC], rho[kC], bet[kC];
-
-    T* RT = reinterpret_cast<T*>(Nf);            // R^T reuses N's space after the solve
-    T* ZrTp = GATED ? ZrT : ZT;                  // no gate: rho == 1
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int nvb = DV / DVB;
 
     // Workgroups of one head land on the same XCD (dispatch is round-robin
@@ -98,6 +125,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int t = wave + i * kNW;
+        sacc[i] = zero4();
+        if (NTS % kNW != 0 && t >= NTS) continue;
         const int di = t / (DVB / 16), nj = t % (DVB / 16);
         const int d = di * 16 + 4 * (lane >> 4), n = nj * 16 + (lane & 15);
 #pragma unroll
@@ -110,49 +139,67 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     if constexpr (DELTA)
         for (int i = tid; i < kC * LDC; i += kNT) Tb[i] = from_f32<T>(0.f);
 
+    typedef __attribute__((__vector_size__(16))) int i4;
     const int64_t nchunks = (Tlen + kC - 1) / kC;
+
+    // Next chunk's tokens travel in registers while the current chunk computes.
+    // Loads never wait here: rows past the end read the last row (in bounds)
+    // and are zeroed when stored, and the gate values stay raw until used.
+    i4 qreg[NQ], kreg[NQ], vreg[NV];
+    T greg = from_f32<T>(0.f), breg = from_f32<T>(0.f);
+    auto fetch = [&](int64_t t0) {
+#pragma unroll
+        for (int p = 0; p < NQ; ++p) {
+            const int idx = (p * kNT + tid) * E;
+            const int row = idx / DK, col = idx % DK;
+            const int64_t tr = t0 + row < Tlen ? t0 + row : Tlen - 1;
+            qreg[p] = *reinterpret_cast<const i4*>(qh + tr * DK + col);
+            kreg[p] = *reinterpret_cast<const i4*>(kh + tr * DK + col);
+        }
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = (p * kNT + tid) * E;
+            const int row = (idx / DVB) % kC, col = idx % DVB;
+            const int64_t tr = t0 + row < Tlen ? t0 + row : Tlen - 1;
+            vreg[p] = *reinterpret_cast<const i4*>(vh + tr * DV + col);
+        }
+        if (wave == 0) {
+            const int64_t tr = t0 + lane < Tlen ? t0 + lane : Tlen - 1;
+            if constexpr (GATED) greg = g[bh * Tlen + tr];
+            if constexpr (DELTA) breg = beta[bh * Tlen + tr];
+        }
+    };
+    if (nchunks > 0) fetch(0);
+
     for (int64_t r = 0; r < nchunks; ++r) {
         const int64_t t0 = r * kC;
         const int cur = (int)(r & 1);
         const T* STc = ST[cur];
         T* STn = ST[cur ^ 1];
-        __syncthreads();
+        T* Vs = ZT;
+        lds_barrier();
 
-        // ---- load the chunk: Q, K row-major and K^T, V^T (zero past the end)
+        // ---- P1: the chunk into LDS; a1 gate scan; next chunk's loads --------
 #pragma unroll
-        for (int p = 0; p < kC * DK / (E * kNT); ++p) {
+        for (int p = 0; p < NQ; ++p) {
             const int idx = (p * kNT + tid) * E;
             const int row = idx / DK, col = idx % DK;
-            typedef __attribute__((__vector_size__(16))) int i4;
-            i4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0};
-            if (t0 + row < Tlen) {
-                qv = *reinterpret_cast<const i4*>(qh + (t0 + row) * DK + col);
-                kv = *reinterpret_cast<const i4*>(kh + (t0 + row) * DK + col);
-            }
-            *reinterpret_cast<i4*>(&Qs[row * LDQ + col]) = qv;
-            *reinterpret_cast<i4*>(&Ks[row * LDQ + col]) = kv;
-            const T* ke = reinterpret_cast<const T*>(&kv);
-#pragma unroll
-            for (int e = 0; e < E; ++e) KsT[(col + e) * LDC + row] = ke[e];
+            const bool ok = t0 + row < Tlen;
+            *reinterpret_cast<i4*>(&Qs[row * LDQ + col]) = ok ? qreg[p] : i4{0, 0, 0, 0};
+            *reinterpret_cast<i4*>(&Ks[row * LDQ + col]) = ok ? kreg[p] : i4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int p = 0; p < kC * DVB / (E * kNT); ++p) {
+        for (int p = 0; p < NV; ++p) {
             const int idx = (p * kNT + tid) * E;
-            const int row = idx / DVB, col = idx % DVB;
-            typedef __attribute__((__vector_size__(16))) int i4;
-            i4 vv = {0, 0, 0, 0};
-            if (t0 + row < Tlen) vv = *reinterpret_cast<const i4*>(vh + (t0 + row) * DV + col);
-            const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-            for (int e = 0; e < E; ++e) VsT[(col + e) * LDC + row] = ve[e];
+            if (idx < kC * DVB) {
+                const int row = idx / DVB, col = idx % DVB;
+                const bool ok = t0 + row < Tlen;
+                *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = ok ? vreg[p] : i4{0, 0, 0, 0};
+            }
         }
-        // ---- a1: gate prefix sums and boundary factors (wave 0) -------------
         if (wave == 0) {
-            const bool valid = t0 + lane < Tlen;
-            float gl = 0.f, bl = 0.f;
-            if constexpr (GATED) gl = valid ? to_f32(g[bh * Tlen + t0 + lane]) : 0.f;
-            if constexpr (DELTA) bl = valid ? to_f32(beta[bh * Tlen + t0 + lane]) : 0.f;
-            float G = gl;
+            const bool ok = t0 + lane < Tlen;
+            float G = ok ? to_f32(greg) : 0.f;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const float up = __shfl_up(G, off, kWave);
@@ -162,187 +209,197 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             Gs[lane] = G;
             gam[lane] = GATED ? expf(G) : 1.f;
             rho[lane] = GATED ? expf(Glast - G) : 1.f;
-            bet[lane] = bl;
+            bet[lane] = ok ? to_f32(breg) : 0.f;
         }
-        __syncthreads();
+        if (r + 1 < nchunks) fetch(t0 + kC);
+        lds_barrier();
 
-        // ---- a2: Aq (and N) tiles on the causal lower half -------------------
+        // ---- P2: K^T, V^T through the matrix core; a2 Aq and N tiles ---------
+#pragma unroll
+        for (int i = 0; i < (kC / 16) * (DK / 16) / kNW; ++i) {
+            const int t = wave + i * kNW;
+            const int li = t / (DK / 16), dj = t % (DK / 16);
+            const floatx4 d = ident_tile(&Ks[li * 16 * LDQ + dj * 16], LDQ, lane);
+            store_tile_t(&KsT[dj * 16 * LDC + li * 16], LDC, d, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < ((kC / 16) * (DVB / 16) + kNW - 1) / kNW; ++i) {
+            const int t = wave + i * kNW;
+            if (t < (kC / 16) * (DVB / 16)) {
+                const int li = t / (DVB / 16), nj = t % (DVB / 16);
+                const floatx4 d = ident_tile(&Vs[li * 16 * LDV + nj * 16], LDV, lane);
+                store_tile_t(&VsT[nj * 16 * LDC + li * 16], LDC, d, lane);
+            }
+        }
         {
-            int cnt = 0;
+            constexpr int NPROD = Cfg::NPAIR * (DELTA ? 2 : 1);
+            constexpr int NPW = (NPROD + kNW - 1) / kNW;
+            floatx4 acc[NPW];
+            int plj[NPW], pmi[NPW];
 #pragma unroll
-            for (int lj = 0; lj < kC / 16; ++lj) {
+            for (int i = 0; i < NPW; ++i) {
+                const int c = wave + i * kNW;
+                const int which = c % (DELTA ? 2 : 1);
+                causal_pair(c / (DELTA ? 2 : 1), plj[i], pmi[i]);
+                acc[i] = zero4();
+                if (c < NPROD) {
+                    // X[m][l] = k_m . (q_l | k_l)
+                    const T* Bop = which == 0 ? &Qs[plj[i] * 16 * LDQ] : &Ks[plj[i] * 16 * LDQ];
+                    acc[i] = mma_nt_k<T, DK>(zero4(), &Ks[pmi[i] * 16 * LDQ], LDQ, Bop, LDQ, lane);
+                }
+            }
 #pragma unroll
-                for (int mi = 0; mi <= lj; ++mi) {
+            for (int i = 0; i < NPW; ++i) {
+                const int c = wave + i * kNW;
+                if (c >= NPROD) continue;
+                const int which = c % (DELTA ? 2 : 1);
+                const int l = plj[i] * 16 + (lane & 15);
+                const int m0 = pmi[i] * 16 + 4 * (lane >> 4);
+                const float Gl = Gs[l];
+                floatx4 val;
 #pragma unroll
-                    for (int which = 0; which < (DELTA ? 2 : 1); ++which, ++cnt) {
-                        if (cnt % kNW != wave) continue;
-                        // X[m][l] = k_m . (q_l | k_l)
-                        const T* Bop = which == 0 ? &Qs[lj * 16 * LDQ] : &Ks[lj * 16 * LDQ];
-                        floatx4 acc = mma_nt(zero4(), &Ks[mi * 16 * LDQ], LDQ, Bop, LDQ, 0, DK, lane);
-                        const int l = lj * 16 + (lane & 15);
-                        const int m0 = mi * 16 + 4 * (lane >> 4);
-                        const float Gl = Gs[l];
-                        floatx4 val;
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int m = m0 + rr;
+                    const float dec = GATED ? expf(Gl - Gs[m]) : 1.f;
+                    if (which == 0) val[rr] = (m <= l) ? acc[i][rr] * dec : 0.f;
+                    else val[rr] = (m < l) ? bet[l] * acc[i][rr] * dec : 0.f;
+                }
+                if (which == 0) store_tile_t(&Aq[plj[i] * 16 * LDC + pmi[i] * 16], LDC, val, lane);
+                else store_tile_t(&Nf[plj[i] * 16 * LDN + pmi[i] * 16], LDN, val, lane);
+            }
+        }
+        lds_barrier();
+
+        // ---- P3: triangular solve (wave 0) || R and gamma Q S_r (others) ------
+        floatx4 oacc[NO];
 #pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int m = m0 + rr;
-                            const float dec = GATED ? expf(Gl - Gs[m]) : 1.f;
-                            if (which == 0) val[rr] = (m <= l) ? acc[rr] * dec : 0.f;
-                            else val[rr] = (m < l) ? bet[l] * acc[rr] * dec : 0.f;
-                        }
-                        if (which == 0) store_tile_t(&Aq[lj * 16 * LDC + mi * 16], LDC, val, lane);
-                        else store_tile_t(&Nf[lj * 16 * LDN + mi * 16], LDN, val, lane);
+        for (int i = 0; i < NO; ++i) oacc[i] = zero4();
+        const int ow = DELTA ? wave - 1 : wave;     // index among the O-tile waves
+        if (DELTA && wave == 0) {
+            // a3/a4 (see tsolve.h)
+            tsolve64_wave<T>(Nf, LDN, Tb, LDC, bet, lane);
+        } else {
+            if constexpr (DELTA) {
+                // b1: R = V - diag(gamma) K S_r  ->  R^T  (tiles spread over waves 1..)
+                constexpr int NR = (NTO + kNW - 2) / (kNW - 1);
+                floatx4 racc[NR];
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    const int t = (wave - 1) + i * (kNW - 1);
+                    racc[i] = zero4();
+                    if (t < NTO) {
+                        const int li = t / (DVB / 16), nj = t % (DVB / 16);
+                        racc[i] = mma_nt_k<T, DK>(zero4(), &Ks[li * 16 * LDQ], LDQ,
+                                                  &STc[nj * 16 * LDQ], LDQ, lane);
                     }
+                }
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    const int t = (wave - 1) + i * (kNW - 1);
+                    if (t >= NTO) continue;
+                    const int li = t / (DVB / 16), nj = t % (DVB / 16);
+                    const int l0 = li * 16 + 4 * (lane >> 4), n = nj * 16 + (lane & 15);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        racc[i][rr] = to_f32(VsT[n * LDC + l0 + rr]) - gam[l0 + rr] * racc[i][rr];
+                    store_tile_t(&RT[nj * 16 * LDC + li * 16], LDC, racc[i], lane);
+                }
+            }
+            // c1 (history part): O^T tile = (S_r^T Q^T) diag(gamma), kept in registers
+#pragma unroll
+            for (int i = 0; i < NO; ++i) {
+                const int t = ow + i * NOW;
+                if (t < NTO) {
+                    const int nj = t / (kC / 16), lj = t % (kC / 16);
+                    oacc[i] = mma_nt_k<T, DK>(zero4(), &STc[nj * 16 * LDQ], LDQ,
+                                              &Qs[lj * 16 * LDQ], LDQ, lane);
+                    const float gl = gam[lj * 16 + (lane & 15)];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) oacc[i][rr] *= gl;
                 }
             }
         }
-        __syncthreads();
+        if constexpr (!DELTA && GATED) {
+            // add rule: Z = V, the state update takes (rho V)^T
+            for (int i = tid; i < DVB * kC; i += kNT) {
+                const int n = i / kC, l = i % kC;
+                ZrT[n * LDC + l] = from_f32<T>(to_f32(VsT[n * LDC + l]) * rho[l]);
+            }
+        }
+        lds_barrier();
 
         if constexpr (DELTA) {
-            // ---- a3/a4: T = (I + N)^-1, Tb = T diag(beta) -----------------------
-            // diagonal 16x16 blocks: wave w inverts block w, lane c < 16 owns column c
-            {
-                const int w = wave;
-                float* Nb = &Nf[(w * 16) * LDN + w * 16];
-                if (lane < 16) {
-                    const int c = lane;
-                    float x[16];
+            // ---- P4: Z = Tb R  ->  Z^T and (rho Z)^T ------------------------------
+            constexpr int NZ = (NTO + kNW - 1) / kNW;
+            floatx4 zacc[NZ];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float acc = (i == c) ? 1.f : 0.f;
-#pragma unroll
-                        for (int j = 0; j < i; ++j) acc = fmaf(-Nb[i * LDN + j], x[j], acc);
-                        x[i] = acc;
-                    }
-                    const float bc = bet[w * 16 + c];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        Nb[i * LDN + c] = x[i];
-                        Tb[(w * 16 + i) * LDC + w * 16 + c] = from_f32<T>(x[i] * bc);
-                    }
+            for (int i = 0; i < NZ; ++i) {
+                const int t = wave + i * kNW;
+                zacc[i] = zero4();
+                if (t < NTO) {
+                    const int li = t / (DVB / 16), nj = t % (DVB / 16);
+                    const int nk = (li * 16 + 16 + KS - 1) / KS;
+                    zacc[i] = mma_nt_k<T, kC>(zero4(), &Tb[li * 16 * LDC], LDC, &RT[nj * 16 * LDC],
+                                              LDC, lane, nk);
                 }
             }
-            __syncthreads();
-            // level 1: T10 = -X11 N10 X00 (wave 0), T32 = -X33 N32 X22 (wave 1)
-            if (wave < 2) {
-                const int i = 2 * wave + 1, j = 2 * wave;
-                const floatx4 xjj = load_tile_rl(&Nf[j * 16 * LDN + j * 16], LDN, lane);
-                const floatx4 y = mm16<T>(&Nf[i * 16 * LDN + j * 16], LDN, xjj, zero4(), lane);
-                floatx4 t = mm16<T>(&Nf[i * 16 * LDN + i * 16], LDN, y, zero4(), lane);
-                const int row = i * 16 + 4 * (lane >> 4), col = j * 16 + (lane & 15);
-                const float bc = bet[col];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    t[rr] = -t[rr];
-                    Nf[(row + rr) * LDN + col] = t[rr];
-                    Tb[(row + rr) * LDC + col] = from_f32<T>(t[rr] * bc);
-                }
-            }
-            __syncthreads();
-            // level 2: the lower-left 32x32 block, T_BA = -T_B N_BA T_A.
-            // wave qc handles column block qc of it (qc = 0, 1).
-            if (wave < 2) {
-                const int qc = wave;
-                // Y_p = sum_s N[2+p][s] T_A[s][qc], s = qc..1   (p = 0, 1)
-                floatx4 y[2];
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    y[p] = zero4();
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        if (s < qc) continue;
-                        const floatx4 tb = load_tile_rl(&Nf[s * 16 * LDN + qc * 16], LDN, lane);
-                        y[p] = mm16<T>(&Nf[(2 + p) * 16 * LDN + s * 16], LDN, tb, y[p], lane);
-                    }
-                }
-                // T[2][qc] = -X22 Y_0 ; T[3][qc] = -(T32 Y_0 + X33 Y_1)
-                floatx4 t2 = mm16<T>(&Nf[2 * 16 * LDN + 2 * 16], LDN, y[0], zero4(), lane);
-                floatx4 t3 = mm16<T>(&Nf[3 * 16 * LDN + 2 * 16], LDN, y[0], zero4(), lane);
-                t3 = mm16<T>(&Nf[3 * 16 * LDN + 3 * 16], LDN, y[1], t3, lane);
-                const int col = qc * 16 + (lane & 15);
-                const float bc = bet[col];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int row = 4 * (lane >> 4) + rr;
-                    Tb[(32 + row) * LDC + col] = from_f32<T>(-t2[rr] * bc);
-                    Tb[(48 + row) * LDC + col] = from_f32<T>(-t3[rr] * bc);
-                }
-            }
-            __syncthreads();
-
-            // ---- b1: R = V - diag(gamma) K S_r  ->  R^T ---------------------------
-#pragma unroll
-            for (int t = wave; t < (kC / 16) * (DVB / 16); t += kNW) {
+            for (int i = 0; i < NZ; ++i) {
+                const int t = wave + i * kNW;
+                if (t >= NTO) continue;
                 const int li = t / (DVB / 16), nj = t % (DVB / 16);
-                floatx4 acc = mma_nt(zero4(), &Ks[li * 16 * LDQ], LDQ, &STc[nj * 16 * LDQ], LDQ, 0, DK, lane);
-                const int l0 = li * 16 + 4 * (lane >> 4), n = nj * 16 + (lane & 15);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    acc[rr] = to_f32(VsT[n * LDC + l0 + rr]) - gam[l0 + rr] * acc[rr];
-                store_tile_t(&RT[nj * 16 * LDC + li * 16], LDC, acc, lane);
-            }
-            __syncthreads();
-            // ---- b1: Z = Tb R  ->  Z^T and (rho Z)^T -------------------------------
-#pragma unroll
-            for (int t = wave; t < (kC / 16) * (DVB / 16); t += kNW) {
-                const int li = t / (DVB / 16), nj = t % (DVB / 16);
-                const int ke = ((li * 16 + 16 + Mfma<T>::kStep - 1) / Mfma<T>::kStep) * Mfma<T>::kStep;
-                floatx4 acc = mma_nt(zero4(), &Tb[li * 16 * LDC], LDC, &RT[nj * 16 * LDC], LDC, 0,
-                                     ke < kC ? ke : kC, lane);
-                store_tile_t(&ZT[nj * 16 * LDC + li * 16], LDC, acc, lane);
+                store_tile_t(&ZT[nj * 16 * LDC + li * 16], LDC, zacc[i], lane);
                 if constexpr (GATED) {
                     const int l0 = li * 16 + 4 * (lane >> 4);
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) acc[rr] *= rho[l0 + rr];
-                    store_tile_t(&ZrT[nj * 16 * LDC + li * 16], LDC, acc, lane);
+                    for (int rr = 0; rr < 4; ++rr) zacc[i][rr] *= rho[l0 + rr];
+                    store_tile_t(&ZrT[nj * 16 * LDC + li * 16], LDC, zacc[i], lane);
                 }
             }
-            __syncthreads();
-        } else {
-            // add rule: Z = V (Z^T is V^T); the gated copy carries rho
-            if constexpr (GATED) {
-                for (int i = tid; i < DVB * kC; i += kNT) {
-                    const int n = i / kC, l = i % kC;
-                    ZrT[n * LDC + l] = from_f32<T>(to_f32(VsT[n * LDC + l]) * rho[l]);
-                }
-            }
-            __syncthreads();
+            lds_barrier();
         }
         const T* ZTs = DELTA ? ZT : VsT;
-        const T* ZrTs = DELTA ? ZrTp : (GATED ? ZrT : VsT);
+        const T* ZrTs = GATED ? ZrT : ZTs;
 
-        // ---- c1: O^T = (S_r^T Q^T) diag(gamma) + Z^T Aq^T, written to HBM -------
+        // ---- P5: c1 O^T += Z^T Aq^T, written to HBM; b1 S_{r+1} ---------------
+        if (!DELTA || wave > 0) {
 #pragma unroll
-        for (int t = wave; t < (DVB / 16) * (kC / 16); t += kNW) {
-            const int nj = t / (kC / 16), lj = t % (kC / 16);
-            floatx4 acc = mma_nt(zero4(), &STc[nj * 16 * LDQ], LDQ, &Qs[lj * 16 * LDQ], LDQ, 0, DK, lane);
-            const int l = lj * 16 + (lane & 15);
-            const float gl = gam[l];
+            for (int i = 0; i < NO; ++i) {
+                const int t = ow + i * NOW;
+                if (t >= NTO) continue;
+                const int nj = t / (kC / 16), lj = t % (kC / 16);
+                const int nk = (lj * 16 + 16 + KS - 1) / KS;
+                oacc[i] = mma_nt_k<T, kC>(oacc[i], &ZTs[nj * 16 * LDC], LDC, &Aq[lj * 16 * LDC], LDC,
+                                          lane, nk);
+                const int l = lj * 16 + (lane & 15);
+                if (t0 + l < Tlen) {
+                    T* dst = oh + (t0 + l) * DV + nj * 16 + 4 * (lane >> 4);
+                    if constexpr (sizeof(T) == 2) {
+                        bf16x4 w;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] *= gl;
-            const int ke = ((lj * 16 + 16 + Mfma<T>::kStep - 1) / Mfma<T>::kStep) * Mfma<T>::kStep;
-            acc = mma_nt(acc, &ZTs[nj * 16 * LDC], LDC, &Aq[lj * 16 * LDC], LDC, 0, ke < kC ? ke : kC, lane);
-            if (t0 + l < Tlen) {
-                T* dst = oh + (t0 + l) * DV + nj * 16 + 4 * (lane >> 4);
-                if constexpr (sizeof(T) == 2) {
-                    bf16x4 w;
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<bf16>(acc[rr]);
-                    *reinterpret_cast<bf16x4*>(dst) = w;
-                } else {
-                    *reinterpret_cast<floatx4*>(dst) = acc;
+                        for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<bf16>(oacc[i][rr]);
+                        *reinterpret_cast<bf16x4*>(dst) = w;
+                    } else {
+                        *reinterpret_cast<floatx4*>(dst) = oacc[i];
+                    }
                 }
             }
         }
-        // ---- b1: S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z ----------------------
         const float gC = gam[kC - 1];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int t = wave + i * kNW;
+            if (NTS % kNW != 0 && t >= NTS) continue;
             const int di = t / (DVB / 16), nj = t % (DVB / 16);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sacc[i][rr] *= gC;
-            sacc[i] = mma_nt(sacc[i], &KsT[di * 16 * LDC], LDC, &ZrTs[nj * 16 * LDC], LDC, 0, kC, lane);
+            sacc[i] = mma_nt_k<T, kC>(sacc[i], &KsT[di * 16 * LDC], LDC, &ZrTs[nj * 16 * LDC], LDC, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int t = wave + i * kNW;
+            if (NTS % kNW != 0 && t >= NTS) continue;
+            const int di = t / (DVB / 16), nj = t % (DVB / 16);
             store_tile_t(&STn[nj * 16 * LDQ + di * 16], LDQ, sacc[i], lane);
         }
     }
@@ -352,6 +409,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int t = wave + i * kNW;
+            if (NTS % kNW != 0 && t >= NTS) continue;
             const int di = t / (DVB / 16), nj = t % (DVB / 16);
             const int d = di * 16 + 4 * (lane >> 4), n = nj * 16 + (lane & 15);
 #pragma unroll

@@ -56,6 +56,36 @@ __device__ __forceinline__ floatx4 mma_nt(floatx4 acc, const T* A, int lda, cons
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// acc += A[0:16][0:K] * B[0:16][0:K]^T with every fragment loaded before the
+// first MFMA issues, so the LDS reads overlap instead of each MFMA waiting on
+// its own pair.  Only the first `nk` steps are accumulated (nk <= K / step);
+// the later fragments are read but unused (they must be in bounds).
+template <typename T, int K>
+__device__ __forceinline__ floatx4 mma_nt_k(floatx4 acc, const T* A, int lda, const T* B, int ldb,
+                                            int lane, int nk = K / Mfma<T>::kStep)
+{
+    constexpr int NK = K / Mfma<T>::kStep;
+    typename Mfma<T>::frag a[NK], b[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        a[i] = Mfma<T>::load(A, lda, i * Mfma<T>::kStep, lane);
+        b[i] = Mfma<T>::load(B, ldb, i * Mfma<T>::kStep, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+        if (i < nk) acc = Mfma<T>::mma(a[i], b[i], acc);
+    return acc;
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
+// then s_barrier.  Global loads in flight (prefetch of the next chunk) stay in
+// flight across it; no kernel here communicates through global memory inside
+// a workgroup.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Store the 4 values a lane holds of a result tile D (rows 4(l/16)+r, column
 // l%16) into dst as D^T: dst[(l%16)*ld + 4(l/16) + r], r = 0..3.
 template <typename T>
@@ -87,6 +117,78 @@ __device__ __forceinline__ floatx4 mm16(const float* A, int lda, floatx4 b, floa
 #pragma unroll
         for (int r = 0; r < 4; ++r) { ab[r] = from_f32<bf16>(a[r]); bb[r] = from_f32<bf16>(b[r]); }
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// Transpose through the matrix core: D = A * I for a 16x16 block of A
+// (row-major in LDS), returned in the result layout (lane holds
+// A[4(l/16)+r][l%16]); store_tile_t then writes A^T with contiguous stores.
+// Exact: every product is by 1 or 0 and every sum has one nonzero term.
+template <typename T>
+__device__ __forceinline__ floatx4 ident_tile(const T* A, int lda, int lane)
+{
+    const int c = lane & 15, g4 = 4 * (lane >> 4);
+    if constexpr (sizeof(T) == 2) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + c * lda + g4);
+        bf16x4 b;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = from_f32<bf16>(g4 + r == c ? 1.f : 0.f);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, zero4(), 0, 0, 0);
+    } else {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(A + c * lda + g4);
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], g4 + r == c ? 1.f : 0.f, acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K = 16 products with register-resident operands.
+//
+// For v_mfma_f32_16x16x16_bf16 lane l supplies A[l%16][4(l/16)+r] and
+// B[4(l/16)+r][l%16] (r = 0..3), exactly the positions a lane holds of a
+// 16x16 result tile X (X[4(l/16)+r][l%16]).  Hence a result tile can be fed
+// back without any data movement: as B it is X, as A it is X^T.  From a
+// row-major block M in LDS a lane reads M[l%16][4(l/16)..+3] (one 8-byte read
+// for bf16): as A that is M, as B it is M^T.  With fp32 operands the same
+// bookkeeping runs through four v_mfma_f32_16x16x4_f32 (register r in the
+// r-th instruction).
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag16;
+template <> struct Frag16<bf16> { typedef bf16x4 type; };
+template <> struct Frag16<float> { typedef floatx4 type; };
+
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type frag16_lds(const T* M, int ld, int lane)
+{
+    return *reinterpret_cast<const typename Frag16<T>::type*>(M + (lane & 15) * ld + 4 * (lane >> 4));
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type frag16_acc(floatx4 x)
+{
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = from_f32<bf16>(x[r]);
+        return f;
+    } else {
+        return x;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ floatx4 mma16(typename Frag16<T>::type a, typename Frag16<T>::type b,
+                                         floatx4 acc)
+{
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
     } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);

@@ -71,6 +71,11 @@ def test_chunk_validation(lib):
     assert call_chunk(lib, mk(), s0=FAKE, sf=FAKE + 16) == 6     # partial overlap
     assert call_chunk(lib, mk(B=0)) == 0                         # nothing to do
     assert lib.linattn_chunk_workspace_bytes(ctypes.byref(mk())) == 0
+    # the per-channel gate runs the two-kernel path, which stages per-chunk tiles
+    wa = mk(gate="channel", dk=128, dv=128, T=130)
+    assert lib.linattn_chunk_workspace_bytes(ctypes.byref(wa)) == 3 * 66048
+    assert call_chunk(lib, wa, g=FAKE) == 4                      # workspace missing
+    assert call_chunk(lib, mk(gate="channel", dtype="fp32"), g=FAKE) == 3
 
 
 def test_decode_validation(lib):
