@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the workload the CPU oracle runs for its baseline")
+    ap.add_argument("--path", choices=["fused", "split"], default=None,
+                    help="chunk path for the scalar gate (default: the library's choice, fused)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -102,6 +104,8 @@ def main():
               "would shard heads with no communication", file=sys.stderr)
         sys.exit(2)
 
+    if args.path:
+        os.environ["LINATTN_CHUNK_PATH"] = args.path
     import torch
 
     import gated_delta_rule_27_amd as la
@@ -119,10 +123,12 @@ def main():
     x = syn.chunk_inputs_torch(case, dev)
     out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
     s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    wsb = la.chunk_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
     def step():
         la.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, rule=case.rule,
-                     gate=case.gate, out=out, s_final=s_fin)
+                     gate=case.gate, out=out, s_final=s_fin, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -215,10 +221,13 @@ def main():
         "config": {"workload": f"gdn_chunk_fwd B={B} H={H} T={T} dk={dk} dv={dv} chunk=64 "
                                f"bf16 tokens fp32 state",
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
-                   "rule": case.rule, "gate": case.gate, "parallelism": "single GPU"},
+                   "rule": case.rule, "gate": case.gate, "parallelism": "single GPU",
+                   "path": "split" if wsb else "fused"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "chunk_fused_kernel", "alg_bytes_per_launch": abytes},
+                     "kernel": "chunk_fused_kernel" if not wsb else
+                               "chunk_intra_channel_kernel + chunk_chain_kernel",
+                     "alg_bytes_per_launch": abytes},
         "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 2),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),

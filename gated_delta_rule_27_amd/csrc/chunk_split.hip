@@ -1,6 +1,6 @@
 // chunk_split.hip — two-kernel chunkwise forward for the per-key-channel
 // gate (GLA-style decay with the add rule, Kimi Delta Attention with the delta
-// rule).
+// rule); it also takes a scalar gate (every channel equal) when selected.
 //
 // Sources: "Linear Attention, Visualized" — "Gated Linear Attention (GLA)"
 // (channelwise prefix products, decayed query <-Q and right-boundary key ->K,
@@ -60,7 +60,7 @@ typedef __attribute__((__vector_size__(16))) int i4;
 // ===========================================================================
 // Kernel A
 // ===========================================================================
-template <int DK, int RULE>
+template <int DK, int RULE, int GATE>
 __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ g,
     const bf16* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks)
@@ -98,13 +98,20 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
         const i4 z = {0, 0, 0, 0};
         const i4 qv = ok ? *reinterpret_cast<const i4*>(q + off) : z;
         const i4 kv = ok ? *reinterpret_cast<const i4*>(k + off) : z;
-        const i4 gv = ok ? *reinterpret_cast<const i4*>(g + off) : z;
         *reinterpret_cast<i4*>(&qs[row * LDQ + col]) = qv;
         *reinterpret_cast<i4*>(&ks[row * LDQ + col]) = kv;
-        const bf16* ge = reinterpret_cast<const bf16*>(&gv);
         floatx4 lo, hi;
+        if constexpr (GATE == kGateChannel) {
+            const i4 gv = ok ? *reinterpret_cast<const i4*>(g + off) : z;
+            const bf16* ge = reinterpret_cast<const bf16*>(&gv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { lo[e] = to_f32(ge[e]); hi[e] = to_f32(ge[4 + e]); }
+            for (int e = 0; e < 4; ++e) { lo[e] = to_f32(ge[e]); hi[e] = to_f32(ge[4 + e]); }
+        } else {
+            // a scalar gate is the channel gate with every channel equal
+            const float gs = ok ? to_f32(g[bh * Tlen + t0 + row]) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { lo[e] = gs; hi[e] = gs; }
+        }
         *reinterpret_cast<floatx4*>(&Gf[row * LDG + col]) = lo;
         *reinterpret_cast<floatx4*>(&Gf[row * LDG + col + 4]) = hi;
     }
@@ -431,14 +438,14 @@ __global__ __launch_bounds__(256, 1) void chunk_chain_kernel(
     }
 }
 
-template <int DK, int RULE>
+template <int DK, int RULE, int GATE>
 hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
 {
     const int64_t nchunks = (p.T + kC - 1) / kC;
     const int64_t bh = p.B * p.H;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE>), dim3((unsigned)(bh * nchunks)),
+        hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)),
                            dim3(512), 0, s, static_cast<const bf16*>(p.q),
                            static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.g),
                            static_cast<const bf16*>(p.beta), ws, p.T, nchunks);
@@ -456,7 +463,7 @@ hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
 
 bool chunk_split_supported(const ChunkProblem& p)
 {
-    return p.gate == kGateChannel && p.chunk == kC && p.dtype == kBF16 &&
+    return p.gate != kGateNone && p.chunk == kC && p.dtype == kBF16 &&
            (p.dk == 64 || p.dk == 128) && (p.dv == 64 || p.dv == 128);
 }
 
@@ -467,11 +474,19 @@ size_t chunk_split_workspace_bytes(const ChunkProblem& p)
     return (size_t)(p.B * p.H) * nchunks * per;
 }
 
+template <int DK>
+hipError_t split_by_rule_gate(const ChunkProblem& p, hipStream_t s)
+{
+    if (p.gate == kGateChannel)
+        return p.rule == kRuleDelta ? launch_split<DK, kRuleDelta, kGateChannel>(p, s)
+                                    : launch_split<DK, kRuleAdd, kGateChannel>(p, s);
+    return p.rule == kRuleDelta ? launch_split<DK, kRuleDelta, kGateScalar>(p, s)
+                                : launch_split<DK, kRuleAdd, kGateScalar>(p, s);
+}
+
 hipError_t launch_chunk_split(const ChunkProblem& p, hipStream_t s)
 {
-    if (p.dk == 64)
-        return p.rule == kRuleDelta ? launch_split<64, kRuleDelta>(p, s) : launch_split<64, kRuleAdd>(p, s);
-    return p.rule == kRuleDelta ? launch_split<128, kRuleDelta>(p, s) : launch_split<128, kRuleAdd>(p, s);
+    return p.dk == 64 ? split_by_rule_gate<64>(p, s) : split_by_rule_gate<128>(p, s);
 }
 
 }  // namespace linattn

@@ -5,6 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
+
 using namespace linattn;
 
 namespace {
@@ -14,6 +17,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Which chunk path serves a problem: the per-channel gate always takes the
+// two-kernel path; a scalar gate takes it when LINATTN_CHUNK_PATH=split (for
+// A/B measurement), otherwise the single-pass kernel.
+bool use_split(const ChunkProblem& p)
+{
+    if (p.gate == kGateChannel) return true;
+    const char* e = getenv("LINATTN_CHUNK_PATH");
+    return e && strcmp(e, "split") == 0 && chunk_split_supported(p);
+}
 
 linattn_status check_enums(int rule, int gate, int dtype)
 {
@@ -55,8 +68,7 @@ linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
     p->dk = a->dk; p->dv = a->dv;
     p->chunk = a->chunk == 0 ? 64 : a->chunk;
     p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
-    const bool fused = p->gate != kGateChannel;
-    if (fused ? !chunk_fused_supported(*p) : !chunk_split_supported(*p))
+    if (use_split(*p) ? !chunk_split_supported(*p) : !chunk_fused_supported(*p))
         return LINATTN_ERR_UNSUPPORTED;
     return LINATTN_OK;
 }
@@ -85,8 +97,7 @@ size_t linattn_chunk_workspace_bytes(const linattn_chunk_args* a)
 {
     ChunkProblem p{};
     if (validate_chunk(a, &p) != LINATTN_OK) return 0;
-    if (p.gate != kGateChannel) return 0;
-    return chunk_split_workspace_bytes(p);
+    return use_split(p) ? chunk_split_workspace_bytes(p) : 0;
 }
 
 linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, const void* k,
@@ -117,7 +128,7 @@ linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, con
     p.workspace = workspace; p.workspace_bytes = workspace_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
-    if (p.gate != kGateChannel) {
+    if (!use_split(p)) {
         err = launch_chunk_fused(p, s);
     } else {
         const size_t need = chunk_split_workspace_bytes(p);

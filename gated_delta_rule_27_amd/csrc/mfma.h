@@ -124,6 +124,23 @@ __device__ __forceinline__ floatx4 mm16(const float* A, int lda, floatx4 b, floa
     }
 }
 
+// The same product with A already in registers as a row fragment (lane holds
+// A[l%16][4(l/16)..+3]).
+template <typename T>
+__device__ __forceinline__ floatx4 mm16r(floatx4 a, floatx4 b, floatx4 acc)
+{
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 ab, bb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { ab[r] = from_f32<bf16>(a[r]); bb[r] = from_f32<bf16>(b[r]); }
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+        return acc;
+    }
+}
+
 // Transpose through the matrix core: D = A * I for a 16x16 block of A
 // (row-major in LDS), returned in the result layout (lane holds
 // A[4(l/16)+r][l%16]); store_tile_t then writes A^T with contiguous stores.
@@ -131,7 +148,9 @@ __device__ __forceinline__ floatx4 mm16(const float* A, int lda, floatx4 b, floa
 template <typename T>
 __device__ __forceinline__ floatx4 ident_tile(const T* A, int lda, int lane)
 {
-    const int c = lane & 15, g4 = 4 * (lane >> 4);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // rebuild the identity here, not once per kernel
+    const int c = ln & 15, g4 = 4 * (ln >> 4);
     if constexpr (sizeof(T) == 2) {
         const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + c * lda + g4);
         bf16x4 b;

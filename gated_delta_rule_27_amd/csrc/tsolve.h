@@ -31,8 +31,21 @@ template <typename T>
 __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt, const float* bet,
                                               int lane)
 {
+    // the off-diagonal N blocks used by the block products, read up front so
+    // their LDS latency hides behind the diagonal substitution
+    const int ra = lane & 15, ca = 4 * (lane >> 4);
+    auto rowfrag = [&](int bi, int bj) {
+        return *reinterpret_cast<const floatx4*>(&Nf[(bi * 16 + ra) * ldn + bj * 16 + ca]);
+    };
+    const floatx4 n10 = rowfrag(1, 0), n32 = rowfrag(3, 2);
+    const floatx4 n20 = rowfrag(2, 0), n21 = rowfrag(2, 1), n30 = rowfrag(3, 0), n31 = rowfrag(3, 1);
     {
-        const int b = lane >> 4, c = lane & 15;
+        // an opaque copy of the lane index keeps the compiler from hoisting the
+        // identity below out of the caller's chunk loop (it would stay live,
+        // and spill, across the whole loop)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int b = ln >> 4, c = ln & 15;
         float* Nb = &Nf[(b * 16) * ldn + b * 16];
         float x[16];
 #pragma unroll
@@ -51,8 +64,8 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
     {
         const floatx4 x00 = load_tile_rl(&Nf[0 * 16 * ldn + 0 * 16], ldn, lane);
         const floatx4 x22 = load_tile_rl(&Nf[2 * 16 * ldn + 2 * 16], ldn, lane);
-        const floatx4 y1 = mm16<T>(&Nf[1 * 16 * ldn + 0 * 16], ldn, x00, zero4(), lane);
-        const floatx4 y3 = mm16<T>(&Nf[3 * 16 * ldn + 2 * 16], ldn, x22, zero4(), lane);
+        const floatx4 y1 = mm16r<T>(n10, x00, zero4());
+        const floatx4 y3 = mm16r<T>(n32, x22, zero4());
         floatx4 t10 = mm16<T>(&Nf[1 * 16 * ldn + 1 * 16], ldn, y1, zero4(), lane);
         floatx4 t32 = mm16<T>(&Nf[3 * 16 * ldn + 3 * 16], ldn, y3, zero4(), lane);
         const int rw = 4 * (lane >> 4), cl = lane & 15;
@@ -69,15 +82,15 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
     }
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
+        // Y_p = sum_{s >= qc} N[2+p][s] T_A[s][qc]
         floatx4 y[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            y[p] = zero4();
-#pragma unroll
-            for (int s = qc; s < 2; ++s) {
-                const floatx4 tb = load_tile_rl(&Nf[s * 16 * ldn + qc * 16], ldn, lane);
-                y[p] = mm16<T>(&Nf[(2 + p) * 16 * ldn + s * 16], ldn, tb, y[p], lane);
-            }
+        const floatx4 ta1 = load_tile_rl(&Nf[1 * 16 * ldn + qc * 16], ldn, lane);
+        y[0] = mm16r<T>(n21, ta1, zero4());
+        y[1] = mm16r<T>(n31, ta1, zero4());
+        if (qc == 0) {
+            const floatx4 ta0 = load_tile_rl(&Nf[0], ldn, lane);
+            y[0] = mm16r<T>(n20, ta0, y[0]);
+            y[1] = mm16r<T>(n30, ta0, y[1]);
         }
         const floatx4 t2 = mm16<T>(&Nf[2 * 16 * ldn + 2 * 16], ldn, y[0], zero4(), lane);
         floatx4 t3 = mm16<T>(&Nf[3 * 16 * ldn + 2 * 16], ldn, y[0], zero4(), lane);

@@ -226,3 +226,13 @@ def test_cfg4_kda_bf16_full_size_sampled():
         es = rel_l2(host(s[b, h]), sref[i, 0])
         note(f"    head ({b},{h}): rel L2 o={eo:.3e} S={es:.3e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("rule", ["add", "delta"])
+def test_scalar_gate_on_two_kernel_path(monkeypatch, rule):
+    # LINATTN_CHUNK_PATH=split routes scalar gates through the two-kernel path
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", "split")
+    case = syn.Case("split", 2, 2, 333, 128, 128, rule, "scalar", "bf16", gate_scale=0.1,
+                    s0_std=0.2, case_id=113)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
