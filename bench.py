@@ -25,6 +25,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tokens/s chunk fwd (H=16,d=128,T=8192) + decode state GB/s vs peak"
+CSRC = os.path.join(ROOT, "gated_delta_rule_27_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# the sources each measured kernel is built from: counter figures in profiles/
+# are valid only while these hash to the value recorded with them
+CHUNK_SOURCES = ("chunk_fused.hip", "mfma.h", "tsolve.h", "device_common.h", "launch.h")
+DECODE_SOURCES = ("decode_step.hip", "device_common.h", "launch.h")
+CHUNK_PROFILE = "chunk_fused_gdn_B8_H16_T8192_d128.md"
+DECODE_PROFILE = "decode_step_gdn_N256_H32_d128.md"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
@@ -61,6 +69,34 @@ def decode_alg_bytes(N, H, dk, dv, s, rule, gate):
     if rule == "delta":
         per_head += s
     return N * H * per_head
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(profile, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    path = os.path.join(PROFILES, profile)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            key, _, val = line.partition(":")
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_sources_sha256") != sources_sha256(sources):
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_model():
@@ -179,6 +215,7 @@ def main():
             "state_GBps": round(dgbps, 1),
             "hbm_frac": round(dgbps / HBM_PEAK_GBPS, 4),
             "alg_bytes_per_step": dbytes,
+            "traffic": counter_traffic(DECODE_PROFILE, DECODE_SOURCES),
         }
         del tok, state
 
@@ -224,7 +261,8 @@ def main():
                    "rule": case.rule, "gate": case.gate, "parallelism": "single GPU",
                    "path": "split" if wsb else "fused"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": counter_traffic(CHUNK_PROFILE, CHUNK_SOURCES) if not wsb else None,
                      "kernel": "chunk_fused_kernel" if not wsb else
                                "chunk_intra_channel_kernel + chunk_chain_kernel",
                      "alg_bytes_per_launch": abytes},
