@@ -51,6 +51,7 @@ constexpr int kC = 64;      // chunk length
 constexpr int kNW = 8;      // waves per workgroup
 constexpr int kNT = kNW * kWave;
 constexpr int kDVB = 64;    // value columns per workgroup (4 state waves x 16)
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T, int DK, int RULE, int GATE>
 struct FusedCfg {
@@ -185,8 +186,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = ok ? vreg[p] : i4{0, 0, 0, 0};
         }
         if (wave == 4) {
+            // G is kept in base 2 (log2 e * prefix sum) so every decay factor is
+            // one hardware exp2
             const bool ok = t0 + lane < Tlen;
-            float G = (GATED && ok) ? to_f32(greg) : 0.f;
+            float G = (GATED && ok) ? to_f32(greg) * kLog2e : 0.f;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const float up = __shfl_up(G, off, kWave);
@@ -194,8 +197,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
             const float Glast = __shfl(G, kWave - 1, kWave);
             Gs[lane] = G;
-            gam[lane] = GATED ? expf(G) : 1.f;
-            rho[lane] = GATED ? expf(Glast - G) : 1.f;
+            gam[lane] = GATED ? fast_exp2(G) : 1.f;
+            rho[lane] = GATED ? fast_exp2(Glast - G) : 1.f;
             bet[lane] = (DELTA && ok) ? to_f32(breg) : 0.f;
         }
         if (r + 1 < nchunks) fetch(t0 + kC);
@@ -253,19 +256,31 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int m = m0 + rr;
-                    const float dec = GATED ? expf(Gl - Gs[m]) : 1.f;
+                    const float dec = GATED ? fast_exp2(Gl - Gs[m]) : 1.f;
                     va[rr] = (m <= l) ? xa[rr] * dec : 0.f;
                     vn[rr] = (m < l) ? bl * xn[rr] * dec : 0.f;
                 }
                 store_tile_t(&Aq[lj * 16 * LDC + mi * 16], LDC, va, lane);
                 if constexpr (DELTA) store_tile_t(&Nf[lj * 16 * LDN + mi * 16], LDN, vn, lane);
             }
+            {
+                // K^T through the matrix core, all of this wave's tiles in flight
+                constexpr int NKT = NL * ND / 4;
+                typename Frag16<T>::type af[NKT];
 #pragma unroll
-            for (int i = 0; i < NL * ND / 4; ++i) {
-                const int t = iw + 4 * i;
-                const int li = t / ND, dj = t % ND;
-                const floatx4 d = ident_tile(&Ks[li * 16 * LDQ + dj * 16], LDQ, lane);
-                store_tile_t(&KsT[dj * 16 * LDC + li * 16], LDC, d, lane);
+                for (int i = 0; i < NKT; ++i) {
+                    const int t = iw + 4 * i;
+                    af[i] = frag16_lds(&Ks[(t / ND) * 16 * LDQ + (t % ND) * 16], LDQ, lane);
+                }
+                const auto id = ident_frag<T>(lane);
+                floatx4 d[NKT];     // separate accumulators, so the products overlap
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) d[i] = mma16<T>(af[i], id, zero4());
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) {
+                    const int t = iw + 4 * i;
+                    store_tile_t(&KsT[(t % ND) * 16 * LDC + (t / ND) * 16], LDC, d[i], lane);
+                }
             }
         }
         lds_barrier();

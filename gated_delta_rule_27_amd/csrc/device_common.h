@@ -24,6 +24,9 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // convert, which rounds to nearest even.
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
+// 2^x through the hardware transcendental unit (v_exp_f32)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 }  // namespace linattn

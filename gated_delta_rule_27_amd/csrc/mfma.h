@@ -215,6 +215,21 @@ __device__ __forceinline__ floatx4 mma16(typename Frag16<T>::type a, typename Fr
     }
 }
 
+// Identity as a K = 16 right factor (lane holds I[4(l/16)+r][l%16]): mma16
+// with it returns the left factor's block in the result layout, i.e. an exact
+// transpose when stored with store_tile_t.
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type ident_frag(int lane)
+{
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // rebuild here, not once per kernel
+    const int c = ln & 15, g4 = 4 * (ln >> 4);
+    floatx4 b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = (g4 + r == c) ? 1.f : 0.f;
+    return frag16_acc<T>(b);
+}
+
 // Load a 16x16 fp32 block from LDS in the result layout (lane holds
 // B[4(l/16)+r][l%16]).
 __device__ __forceinline__ floatx4 load_tile_rl(const float* B, int ldb, int lane)

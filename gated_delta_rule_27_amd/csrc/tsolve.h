@@ -7,101 +7,135 @@
 // (I + N) U = diag(beta) V; the chunk kernels need T = (I + N)^-1 once and
 // apply Tb = T diag(beta) by matrix products.
 //
-// For C = 64 the inverse is built in 16x16 blocks:
-//   * the four diagonal blocks X_bb = (I + N_bb)^-1 by forward substitution,
-//     one lane group of 16 per block and one lane per column, sweeping columns
-//     so that each step's updates are independent;
-//   * level 1: T10 = -X11 N10 X00 and T32 = -X33 N32 X22;
-//   * level 2: the lower-left 32x32 block -T_B (N_BA T_A) (block inverse of a
-//     2x2 lower-triangular block matrix), 16 columns at a time.
-// Diagonal blocks are fp32; the block products use the operand type T (bf16
-// MFMA with fp32 accumulation, or fp32 MFMA).  No workgroup barrier is needed:
-// the wave only reads what it wrote itself.
+// For C = 64 the inverse is built in 16x16 blocks (X_bb = (I + N_bb)^-1):
+//   * the four diagonal blocks on the matrix core as the finite product
+//     (I - N)(I + N^2)(I + N^4)(I + N^8) (N_bb is nilpotent, N^16 = 0);
+//   * the off-diagonal blocks from the block inverse of a 2x2 lower-triangular
+//     block matrix, [[A,0],[C,D]]^-1 = [[A^-1,0],[-D^-1 C A^-1, D^-1]]:
+//       T10 = -X11 N10 X00,   T32 = -X33 N32 X22            (level 1)
+//       for each 16-column block q of the lower-left 32x32 block:
+//         Y0 = N20 T_A[0][q] + N21 T_A[1][q],  Y1 = N30 T_A[0][q] + N31 T_A[1][q]
+//         T2q = -X22 Y0,  T3q = -(T32 Y0 + X33 Y1) = -X33 (N32 T2q + Y1)
+//     The last form (T32 = -X33 N32 X22, T2q = -X22 Y0) keeps every left
+//     factor a block read once from LDS and every right factor a register tile.
+// All products use the operand type T (bf16 MFMA with fp32 accumulation, or
+// fp32 MFMA); everything stays in registers after N is read, and no barrier is
+// needed.
 #pragma once
 
 #include "mfma.h"
 
 namespace linattn {
 
-// Nf: fp32 [64][ldn]; on entry its strictly lower part holds N (the diagonal
-// and upper part are ignored), on exit its block-lower part holds pieces of T.
+// Nf: fp32 [64][ldn]; its block-lower part holds N with zeros on and above the
+// diagonal of the diagonal blocks.  It is only read.
 // Tb: operand type [64][ldt], receives T diag(beta) on and below the diagonal
 // (the strictly upper blocks are never written).  bet: beta of the 64 rows.
 template <typename T>
 __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt, const float* bet,
                                               int lane)
 {
-    // the off-diagonal N blocks used by the block products, read up front so
-    // their LDS latency hides behind the diagonal substitution
-    const int ra = lane & 15, ca = 4 * (lane >> 4);
+    // an opaque copy of the lane index keeps the compiler from hoisting the
+    // identity below out of the caller's chunk loop (it would stay live, and
+    // spill, across the whole loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int ra = ln & 15, ca = 4 * (ln >> 4);
+    // row fragment (lane holds M[ra][ca..ca+3]) of block (bi, bj)
     auto rowfrag = [&](int bi, int bj) {
         return *reinterpret_cast<const floatx4*>(&Nf[(bi * 16 + ra) * ldn + bj * 16 + ca]);
     };
+    // off-diagonal N blocks, read before the substitution so their latency hides
     const floatx4 n10 = rowfrag(1, 0), n32 = rowfrag(3, 2);
     const floatx4 n20 = rowfrag(2, 0), n21 = rowfrag(2, 1), n30 = rowfrag(3, 0), n31 = rowfrag(3, 1);
+
+    // ---- diagonal blocks on the matrix core ------------------------------------
+    // X_bb = (I + N_bb)^-1 = (I + M)(I + M^2)(I + M^4)(I + M^8), M = -N_bb
+    // (N_bb is strictly lower, so M^16 = 0).  A K = 16 product of register tiles
+    // gives A^T B (mfma.h), so every matrix is carried together with its
+    // transpose; the four blocks are four independent chains of depth four.
+    floatx4 X[4], Xt[4];           // X_bb as right factor, and as left factor (row fragment)
     {
-        // an opaque copy of the lane index keeps the compiler from hoisting the
-        // identity below out of the caller's chunk loop (it would stay live,
-        // and spill, across the whole loop)
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int b = ln >> 4, c = ln & 15;
-        float* Nb = &Nf[(b * 16) * ldn + b * 16];
-        float x[16];
+        floatx4 id;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+        for (int r = 0; r < 4; ++r) id[r] = (ca + r == ra) ? 1.f : 0.f;
+        floatx4 M[4], Mt[4], P[4], Pt[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int b = 0; b < 4; ++b) {
+            const floatx4 nb = load_tile_rl(&Nf[(b * 16) * ldn + b * 16], ldn, lane);
+            const floatx4 nbt = rowfrag(b, b);
 #pragma unroll
-            for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-Nb[i * ldn + j], x[j], x[i]);
-        const float bc = bet[b * 16 + c];
+            for (int r = 0; r < 4; ++r) {
+                M[b][r] = -nb[r];
+                Mt[b][r] = -nbt[r];
+                P[b][r] = id[r] + M[b][r];
+                Pt[b][r] = id[r] + Mt[b][r];
+            }
+        }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            Nb[i * ldn + c] = x[i];
-            Tb[(b * 16 + i) * ldt + b * 16 + c] = from_f32<T>(x[i] * bc);
+        for (int step = 0; step < 3; ++step) {
+            floatx4 M2[4], M2t[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                M2[b] = mm16r<T>(Mt[b], M[b], zero4());      // M M
+                M2t[b] = mm16r<T>(M[b], Mt[b], zero4());     // M^T M^T
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const floatx4 p = P[b];
+                P[b] = mm16r<T>(Pt[b], M2[b], p);            // P + P M2
+                Pt[b] = mm16r<T>(M2[b], Pt[b], Pt[b]);       // P^T + M2^T P^T
+                M[b] = M2[b];
+                Mt[b] = M2t[b];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            X[b] = P[b];
+            Xt[b] = Pt[b];
+            // Tb diagonal block: X diag(beta), stored from the row fragment
+            floatx4 w = Xt[b];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] *= bet[b * 16 + ca + r];
+            store_tile_t(&Tb[(b * 16) * ldt + b * 16], ldt, w, lane);
         }
     }
-    {
-        const floatx4 x00 = load_tile_rl(&Nf[0 * 16 * ldn + 0 * 16], ldn, lane);
-        const floatx4 x22 = load_tile_rl(&Nf[2 * 16 * ldn + 2 * 16], ldn, lane);
-        const floatx4 y1 = mm16r<T>(n10, x00, zero4());
-        const floatx4 y3 = mm16r<T>(n32, x22, zero4());
-        floatx4 t10 = mm16<T>(&Nf[1 * 16 * ldn + 1 * 16], ldn, y1, zero4(), lane);
-        floatx4 t32 = mm16<T>(&Nf[3 * 16 * ldn + 3 * 16], ldn, y3, zero4(), lane);
-        const int rw = 4 * (lane >> 4), cl = lane & 15;
-        const float b0 = bet[cl], b2 = bet[32 + cl];
+    const floatx4 x00 = X[0], x11 = X[1], x22 = X[2];
+    const floatx4 x11r = Xt[1], x22r = Xt[2], x33r = Xt[3];
+
+    // ---- level 1 ----------------------------------------------------------------
+    floatx4 t10 = mm16r<T>(x11r, mm16r<T>(n10, x00, zero4()), zero4());
+    floatx4 t32 = mm16r<T>(x33r, mm16r<T>(n32, x22, zero4()), zero4());
+    const int rw = 4 * (lane >> 4), cl = lane & 15;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            t10[rr] = -t10[rr];
-            t32[rr] = -t32[rr];
-            Nf[(16 + rw + rr) * ldn + cl] = t10[rr];
-            Nf[(48 + rw + rr) * ldn + 32 + cl] = t32[rr];
-            Tb[(16 + rw + rr) * ldt + cl] = from_f32<T>(t10[rr] * b0);
-            Tb[(48 + rw + rr) * ldt + 32 + cl] = from_f32<T>(t32[rr] * b2);
-        }
+    for (int rr = 0; rr < 4; ++rr) {
+        t10[rr] = -t10[rr];
+        t32[rr] = -t32[rr];
+        Tb[(16 + rw + rr) * ldt + cl] = from_f32<T>(t10[rr] * bet[cl]);
+        Tb[(48 + rw + rr) * ldt + 32 + cl] = from_f32<T>(t32[rr] * bet[32 + cl]);
     }
+
+    // ---- level 2: lower-left 32x32 block, 16 columns at a time ------------------
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
-        // Y_p = sum_{s >= qc} N[2+p][s] T_A[s][qc]
-        floatx4 y[2];
-        const floatx4 ta1 = load_tile_rl(&Nf[1 * 16 * ldn + qc * 16], ldn, lane);
-        y[0] = mm16r<T>(n21, ta1, zero4());
-        y[1] = mm16r<T>(n31, ta1, zero4());
-        if (qc == 0) {
-            const floatx4 ta0 = load_tile_rl(&Nf[0], ldn, lane);
-            y[0] = mm16r<T>(n20, ta0, y[0]);
-            y[1] = mm16r<T>(n30, ta0, y[1]);
+        const floatx4 ta1 = qc == 0 ? t10 : x11;          // T_A[1][qc]
+        floatx4 y0 = mm16r<T>(n21, ta1, zero4());
+        floatx4 y1 = mm16r<T>(n31, ta1, zero4());
+        if (qc == 0) {                                    // T_A[0][0] = X00, T_A[0][1] = 0
+            y0 = mm16r<T>(n20, x00, y0);
+            y1 = mm16r<T>(n30, x00, y1);
         }
-        const floatx4 t2 = mm16<T>(&Nf[2 * 16 * ldn + 2 * 16], ldn, y[0], zero4(), lane);
-        floatx4 t3 = mm16<T>(&Nf[3 * 16 * ldn + 2 * 16], ldn, y[0], zero4(), lane);
-        t3 = mm16<T>(&Nf[3 * 16 * ldn + 3 * 16], ldn, y[1], t3, lane);
-        const int col = qc * 16 + (lane & 15);
+        floatx4 t2 = mm16r<T>(x22r, y0, zero4());
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) t2[rr] = -t2[rr];
+        const floatx4 u = mm16r<T>(n32, t2, y1);
+        const floatx4 t3 = mm16r<T>(x33r, u, zero4());
+        const int col = qc * 16 + cl;
         const float bc = bet[col];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int row = 4 * (lane >> 4) + rr;
-            Tb[(32 + row) * ldt + col] = from_f32<T>(-t2[rr] * bc);
-            Tb[(48 + row) * ldt + col] = from_f32<T>(-t3[rr] * bc);
+            Tb[(32 + rw + rr) * ldt + col] = from_f32<T>(t2[rr] * bc);
+            Tb[(48 + rw + rr) * ldt + col] = from_f32<T>(-t3[rr] * bc);
         }
     }
 }
