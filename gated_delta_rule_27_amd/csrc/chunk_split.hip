@@ -77,7 +77,7 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     __shared__ __align__(16) float Nf[DELTA ? kC * LDN : 4];
     __shared__ __align__(16) bf16 Aq[kC * LDC];
     __shared__ __align__(16) bf16 Tb[DELTA ? kC * LDC : 8];
-    __shared__ float bet[kC];
+    __shared__ __align__(16) float bet[kC];
     __shared__ float tot[NT / DK][DK];
 
     const int tid = threadIdx.x;

@@ -27,6 +27,53 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return sta
 // 2^x through the hardware transcendental unit (v_exp_f32)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An opaque copy of a value: the compiler cannot see through it, so lane
+// arithmetic derived from it inside a loop is recomputed there instead of
+// being hoisted out and held in registers for the whole loop.
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// A float the compiler must compute where it stands: used for a value that
+// feeds a per-lane select, which the compiler would otherwise turn into a
+// branch around the value's load and arithmetic.
+__device__ __forceinline__ float opaquef(float x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// DPP move of a float (lanes whose source is outside the row, or whose row is
+// masked off, read 0)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP (no LDS):
+// Hillis-Steele steps of 1, 2, 4, 8 inside each row of 16 lanes, then the row
+// totals carried by the row broadcasts of lane 15 (to rows 1 and 3) and of
+// lane 31 (to rows 2 and 3).
+__device__ __forceinline__ float wave_prefix_sum(float x)
+{
+    x += dpp_move<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_move<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_move<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_move<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_move<0x142, 0xa>(x);   // row_bcast:15
+    x += dpp_move<0x143, 0xc>(x);   // row_bcast:31
+    return x;
+}
+
+// value of lane 63 in every lane
+__device__ __forceinline__ float wave_last(float x)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 }  // namespace linattn

@@ -16,23 +16,30 @@
 //       for each 16-column block q of the lower-left 32x32 block:
 //         Y0 = N20 T_A[0][q] + N21 T_A[1][q],  Y1 = N30 T_A[0][q] + N31 T_A[1][q]
 //         T2q = -X22 Y0,  T3q = -(T32 Y0 + X33 Y1) = -X33 (N32 T2q + Y1)
-//     The last form (T32 = -X33 N32 X22, T2q = -X22 Y0) keeps every left
-//     factor a block read once from LDS and every right factor a register tile.
+//     The last form (T32 = -X33 N32 X22, T2q = -X22 Y0) needs every left
+//     factor only as a row fragment and every right factor only as a tile.
 // All products use the operand type T (bf16 MFMA with fp32 accumulation, or
-// fp32 MFMA); everything stays in registers after N is read, and no barrier is
-// needed.
+// fp32 MFMA) on register tiles; only Tb is written, and no barrier is needed.
 #pragma once
 
 #include "mfma.h"
 
 namespace linattn {
 
-// Nf: fp32 [64][ldn]; its block-lower part holds N with zeros on and above the
-// diagonal of the diagonal blocks.  It is only read.
+// The ten 16x16 blocks of N on and below the diagonal come in registers, in the
+// MFMA result-tile layout (lane l holds rows 4(l/16)..+3 of column l%16):
+//   nd[b]  = tile(N_bb)       nt[b] = tile(N_bb^T)        (diagonal blocks)
+//   n10, n20, n21, n30, n31, n32 = tile(N_ij^T)           (below the diagonal)
+// A tile of X^T is, lane by lane, the row fragment of X (lane holds
+// X[l%16][4(l/16)..+3]), i.e. the left operand that makes an MFMA product X B.
 // Tb: operand type [64][ldt], receives T diag(beta) on and below the diagonal
-// (the strictly upper blocks are never written).  bet: beta of the 64 rows.
+// (the strictly upper blocks are never written).  beta in registers:
+// brow[b][r] = beta[16 b + 4(l/16) + r] and bcol[b] = beta[16 b + l%16].
 template <typename T>
-__device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt, const float* bet,
+__device__ __forceinline__ void tsolve64_regs(const floatx4 (&nd)[4], const floatx4 (&nt)[4],
+                                              floatx4 n10, floatx4 n20, floatx4 n21, floatx4 n30,
+                                              floatx4 n31, floatx4 n32, T* Tb, int ldt,
+                                              const floatx4 (&brow)[4], const float (&bcol)[4],
                                               int lane)
 {
     // an opaque copy of the lane index keeps the compiler from hoisting the
@@ -41,13 +48,6 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int ra = ln & 15, ca = 4 * (ln >> 4);
-    // row fragment (lane holds M[ra][ca..ca+3]) of block (bi, bj)
-    auto rowfrag = [&](int bi, int bj) {
-        return *reinterpret_cast<const floatx4*>(&Nf[(bi * 16 + ra) * ldn + bj * 16 + ca]);
-    };
-    // off-diagonal N blocks, read before the substitution so their latency hides
-    const floatx4 n10 = rowfrag(1, 0), n32 = rowfrag(3, 2);
-    const floatx4 n20 = rowfrag(2, 0), n21 = rowfrag(2, 1), n30 = rowfrag(3, 0), n31 = rowfrag(3, 1);
 
     // ---- diagonal blocks on the matrix core ------------------------------------
     // X_bb = (I + N_bb)^-1 = (I + M)(I + M^2)(I + M^4)(I + M^8), M = -N_bb
@@ -62,12 +62,10 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
         floatx4 M[4], Mt[4], P[4], Pt[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const floatx4 nb = load_tile_rl(&Nf[(b * 16) * ldn + b * 16], ldn, lane);
-            const floatx4 nbt = rowfrag(b, b);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                M[b][r] = -nb[r];
-                Mt[b][r] = -nbt[r];
+                M[b][r] = -nd[b][r];
+                Mt[b][r] = -nt[b][r];
                 P[b][r] = id[r] + M[b][r];
                 Pt[b][r] = id[r] + Mt[b][r];
             }
@@ -96,7 +94,7 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
             // Tb diagonal block: X diag(beta), stored from the row fragment
             floatx4 w = Xt[b];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[r] *= bet[b * 16 + ca + r];
+            for (int r = 0; r < 4; ++r) w[r] *= brow[b][r];
             store_tile_t(&Tb[(b * 16) * ldt + b * 16], ldt, w, lane);
         }
     }
@@ -111,8 +109,8 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
     for (int rr = 0; rr < 4; ++rr) {
         t10[rr] = -t10[rr];
         t32[rr] = -t32[rr];
-        Tb[(16 + rw + rr) * ldt + cl] = from_f32<T>(t10[rr] * bet[cl]);
-        Tb[(48 + rw + rr) * ldt + 32 + cl] = from_f32<T>(t32[rr] * bet[32 + cl]);
+        Tb[(16 + rw + rr) * ldt + cl] = from_f32<T>(t10[rr] * bcol[0]);
+        Tb[(48 + rw + rr) * ldt + 32 + cl] = from_f32<T>(t32[rr] * bcol[2]);
     }
 
     // ---- level 2: lower-left 32x32 block, 16 columns at a time ------------------
@@ -131,13 +129,42 @@ __device__ __forceinline__ void tsolve64_wave(float* Nf, int ldn, T* Tb, int ldt
         const floatx4 u = mm16r<T>(n32, t2, y1);
         const floatx4 t3 = mm16r<T>(x33r, u, zero4());
         const int col = qc * 16 + cl;
-        const float bc = bet[col];
+        const float bc = bcol[qc];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             Tb[(32 + rw + rr) * ldt + col] = from_f32<T>(t2[rr] * bc);
             Tb[(48 + rw + rr) * ldt + col] = from_f32<T>(-t3[rr] * bc);
         }
     }
+}
+
+// The same transform with N and beta read from LDS.  Nf: fp32 [64][ldn]; its
+// block-lower part holds N with zeros on and above the diagonal of the diagonal
+// blocks.  bet: beta of the 64 rows, 16-byte aligned.
+template <typename T>
+__device__ __forceinline__ void tsolve64_wave(const float* Nf, int ldn, T* Tb, int ldt,
+                                              const float* bet, int lane)
+{
+    const int ra = lane & 15, ca = 4 * (lane >> 4);
+    // tile of the transpose of block (bi, bj) = its row fragment
+    auto tile_t = [&](int bi, int bj) {
+        return *reinterpret_cast<const floatx4*>(&Nf[(bi * 16 + ra) * ldn + bj * 16 + ca]);
+    };
+    floatx4 nd[4], nt[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        nd[b] = load_tile_rl(&Nf[(b * 16) * ldn + b * 16], ldn, lane);
+        nt[b] = tile_t(b, b);
+    }
+    floatx4 brow[4];
+    float bcol[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + ca]);
+        bcol[b] = bet[16 * b + ra];
+    }
+    tsolve64_regs<T>(nd, nt, tile_t(1, 0), tile_t(2, 0), tile_t(2, 1), tile_t(3, 0), tile_t(3, 1),
+                     tile_t(3, 2), Tb, ldt, brow, bcol, lane);
 }
 
 }  // namespace linattn
