@@ -24,25 +24,30 @@
 //
 // Eight waves in three roles, each running its own copy of the chunk loop (so
 // the register allocation of one role does not burden another); all of them
-// meet at the same two LDS barriers per chunk:
+// meet at the same three LDS barriers per chunk:
 //   * state waves 0..3: wave w owns value columns 16w..16w+15 and keeps
 //     S[:, those columns] (fp32) as dk/16 MFMA result tiles for the whole
 //     sequence.  S, R and Z never leave registers: a result tile is directly a
-//     K = 16 MFMA operand (mfma.h), so LDS only supplies Q, K, K^T, V, Aq, Tb.
-//   * wave 4: the gate scan; for the delta rule the N blocks (kept in
+//     K = 16 MFMA operand (mfma.h), and two of them make one K = 32 operand, so
+//     LDS only supplies Q, K, K^T, V, Aq, Tb.
+//   * wave 4: the gate scan; for the delta rule the diagonal N blocks (in
 //     registers) and the triangular transform.
-//   * waves 5..7 (4..7 for the add rule): the Aq tiles, K^T (matrix-core
-//     transpose) and the copy of the previous chunk's output to HBM.
+//   * waves 5..7 (4..7 for the add rule): the N blocks below the diagonal, the
+//     Aq tiles and the copy of the previous chunk's output to HBM.
 // Schedule of one chunk (the next chunk's tokens are loaded into registers
 // during the whole chunk):
-//   P1  all: registers -> LDS; issue next chunk's loads; wave 4: gate scan
-//   --- barrier
-//   P2  state waves: R = V - gamma K S_r and the inter-chunk output gamma Q S_r
-//       wave 4: N, then T and Tb                                    [delta]
-//       waves 5..7: previous output to HBM, Aq tiles, K^T
-//   --- barrier
-//   P4  state waves: Z = Tb R, O = gamma Q S_r + Aq Z (to LDS), S_{r+1}
-//       (the other waves go on with the next chunk's P1)
+//   P1   all: registers -> LDS; issue next chunk's loads; wave 4: gate scan
+//   ---  barrier
+//   P2a  state waves: R = V - gamma K S_r (add rule: also gamma Q S_r)
+//        wave 4: diagonal N blocks, their inverses, diagonal blocks of Tb
+//        waves 5..7: N blocks below the diagonal (to LDS), Aq tiles
+//   ---  barrier
+//   P2b  state waves: (delta) gamma Q S_r; K^T by matrix-core transposes
+//        wave 4: off-diagonal blocks of Tb                          [delta]
+//        waves 5..7: previous chunk's output to HBM
+//   ---  barrier
+//   P4   state waves: Z = Tb R, O = gamma Q S_r + Aq Z (to LDS), S_{r+1}
+//        (the other waves go on with the next chunk's P1)
 // Operands are bf16 (fp32 for fp32 tokens), accumulation is fp32; the state
 // stays fp32 and is rounded to the operand type only as an operand.
 #include "device_common.h"
@@ -92,11 +97,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     float* s_final, int64_t Tlen, int DV, int nblocks)
 {
     using Cfg = FusedCfg<T, DK, RULE, GATE>;
+    using F = typename Frag16<T>::type;
     constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDV = Cfg::LDV;
     constexpr bool DELTA = Cfg::DELTA, GATED = Cfg::GATED;
     constexpr int ND = Cfg::ND, NL = Cfg::NL, E = Cfg::E, NQ = Cfg::NQ, NV = Cfg::NV;
     constexpr int NK = DK / Mfma<T>::kStep;          // MFMA steps over the key dimension
-    // waves kW0..7 share the Aq tiles, K^T and the output copy
+    // waves kW0..7 share the Aq tiles and the output copy
     constexpr int kW0 = DELTA ? 5 : 4, kNIW = kNW - kW0;
 
     __shared__ __align__(16) T Qs[kC * LDQ];
@@ -106,6 +112,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     __shared__ __align__(16) T Aq[kC * LDC];
     __shared__ __align__(16) T Os[kC * LDV];
     __shared__ __align__(16) T Tb[DELTA ? kC * LDC : 8];
+    // the six N blocks below the diagonal as row fragments, lane by lane
+    __shared__ __align__(16) floatx4 Nlo[DELTA ? 6 * kWave : 1];
     // gate values alternate between two buffers: the state waves still read the
     // previous chunk's while wave 4 writes this chunk's
     __shared__ __align__(16) float Gsb[2][kC], gamb[2][kC], rhob[2][kC], betb[2][kC];
@@ -176,10 +184,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     if (nchunks > 0) fetch(0);
 
     // The output of a chunk is staged in LDS (Os) by the state waves and written
-    // to HBM by waves kW0..7 during the next chunk's P2, after that chunk's loads
-    // were issued: loads and stores share one vector-memory counter, so a store
-    // issued between a load and its wait would make the wait include the store.
-    // Rows of 64 columns go out as full 16-byte vectors.
+    // to HBM by waves kW0..7 during the next chunk, after that chunk's loads were
+    // issued: loads and stores share one vector-memory counter, so a store issued
+    // between a load and its wait would make the wait include the store.  Rows of
+    // 64 columns go out as full 16-byte vectors.
     auto copy_out = [&](int64_t tb, int cw, int ln) {
         constexpr int NCOPY = kC * kDVB / E, NROUND = (NCOPY + kNIW * kWave - 1) / (kNIW * kWave);
         T* oh = o + bh * Tlen * DV + vb * kDVB;
@@ -195,49 +203,42 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
     };
 
-    // a2 Aq tiles and K^T through the matrix core, shared by kNIW waves (iw-th)
-    auto aq_kt = [&](const float* Gs, int iw, int ln) {
+    // x[rr] = sum_c A[16 mi + g4 + rr][c] B[16 lj + cl][c] (A, B: Ks or Qs rows)
+    auto dot_tile = [&](const T* A, const T* B, int mi, int lj, int ln) {
+        typename Mfma<T>::frag fa[NK], fb[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            fa[i] = Mfma<T>::load(&A[mi * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
+            fb[i] = Mfma<T>::load(&B[lj * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
+        }
+        floatx4 x = zero4();
+#pragma unroll
+        for (int i = 0; i < NK; ++i) x = Mfma<T>::mma(fa[i], fb[i], x);
+        return x;
+    };
+    // a2 Aq tile (lj, mi), mi <= lj: Aq[l][m] = (q_l . k_m) exp(G_l - G_m), m <= l
+    auto aq_tile = [&](const float* Gs, int lj, int mi, int ln) {
         const int cl = ln & 15, g4 = 4 * (ln >> 4);
-        for (int p = iw; p < Cfg::NPAIR; p += kNIW) {
-            int lj, mi;
-            causal_pair(p, lj, mi);
-            floatx4 xa = zero4();    // xa[rr] = k_m . q_l, m = 16 mi + g4 + rr, l = 16 lj + cl
-            typename Mfma<T>::frag fa[NK], fq[NK];
+        const floatx4 xa = dot_tile(Ks, Qs, mi, lj, ln);
+        const float Gl = Gs[lj * 16 + cl];
+        const floatx4 Gm = *reinterpret_cast<const floatx4*>(&Gs[mi * 16 + g4]);
+        floatx4 va;
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                fa[i] = Mfma<T>::load(&Ks[mi * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
-                fq[i] = Mfma<T>::load(&Qs[lj * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
-            }
-#pragma unroll
-            for (int i = 0; i < NK; ++i) xa = Mfma<T>::mma(fa[i], fq[i], xa);
-            const int l = lj * 16 + cl;
-            const float Gl = Gs[l];
-            floatx4 va;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int m = mi * 16 + g4 + rr;
-                const float dec = GATED ? opaquef(fast_exp2(Gl - Gs[m])) : 1.f;
-                va[rr] = (m <= l) ? xa[rr] * dec : 0.f;
-            }
-            store_tile_t(&Aq[lj * 16 * LDC + mi * 16], LDC, va, ln);
+        for (int rr = 0; rr < 4; ++rr) {
+            const float dec = GATED ? fast_exp2(Gl - Gm[rr]) : 1.f;
+            va[rr] = (mi < lj || g4 + rr <= cl) ? xa[rr] * dec : 0.f;
         }
-        // all of this wave's transposes in flight, with separate accumulators
-        constexpr int NKTT = NL * ND, NKT = (NKTT + kNIW - 1) / kNIW;
-        typename Frag16<T>::type af[NKT];
+        store_tile_t(&Aq[lj * 16 * LDC + mi * 16], LDC, va, ln);
+    };
+    // this wave's share (iw of nw) of the ten causal Aq tiles
+    auto aq_share = [&](const float* Gs, int iw, int nw, int ln) {
 #pragma unroll
-        for (int i = 0; i < NKT; ++i) {
-            const int t = iw + kNIW * i;
-            if (t < NKTT) af[i] = frag16_lds(&Ks[(t / ND) * 16 * LDQ + (t % ND) * 16], LDQ, ln);
-        }
-        const auto id = ident_frag<T>(ln);
-        floatx4 d[NKT];
-#pragma unroll
-        for (int i = 0; i < NKT; ++i)
-            if (iw + kNIW * i < NKTT) d[i] = mma16<T>(af[i], id, zero4());
-#pragma unroll
-        for (int i = 0; i < NKT; ++i) {
-            const int t = iw + kNIW * i;
-            if (t < NKTT) store_tile_t(&KsT[(t % ND) * 16 * LDC + (t / ND) * 16], LDC, d[i], ln);
+        for (int p = 0; p < Cfg::NPAIR; ++p) {
+            if (p % nw == iw) {
+                int lj, mi;
+                causal_pair(p, lj, mi);
+                aq_tile(Gs, lj, mi, ln);
+            }
         }
     };
 
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             if (r + 1 < nchunks) fetch(t0 + kC);
             lds_barrier();
 
-            // ---- P2: R = V - gamma K S_r (delta; V for add) ; O^T = (S_r^T Q^T) gamma
+            // ---- P2a: R = V - gamma K S_r (delta; V for add) --------------------------
             floatx4 R[NL], Ot[NL];
 #pragma unroll
             for (int li = 0; li < NL; ++li)
@@ -282,77 +283,122 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
                 for (int li = 0; li < NL; ++li) P[li] = zero4();
 #pragma unroll
-                for (int db = 0; db < ND; ++db) {
-                    const auto sf = frag16_acc<T>(S[db]);
+                for (int db = 0; db < ND; db += 2) {
+                    const F s0f = frag16_acc<T>(S[db]), s1f = frag16_acc<T>(S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        P[li] = mma16<T>(frag16_lds(&Ks[16 * li * LDQ + 16 * db], LDQ, ln), sf, P[li]);
+                        P[li] = mma16x2<T>(frag16_lds(&Ks[16 * li * LDQ + 16 * db], LDQ, ln),
+                                           frag16_lds(&Ks[16 * li * LDQ + 16 * db + 16], LDQ, ln), s0f, s1f, P[li]);
                 }
 #pragma unroll
-                for (int li = 0; li < NL; ++li)
+                for (int li = 0; li < NL; ++li) {
+                    const floatx4 gr = *reinterpret_cast<const floatx4*>(&gam[16 * li + g4]);
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) R[li][rr] -= gam[16 * li + g4 + rr] * P[li][rr];
+                    for (int rr = 0; rr < 4; ++rr) R[li][rr] -= gr[rr] * P[li][rr];
+                }
             }
+            // O^T = (S_r^T Q^T) gamma: here for the add rule, after the barrier for
+            // the delta rule (whose P2a is longer elsewhere)
+            auto ohist = [&]() {
 #pragma unroll
-            for (int li = 0; li < NL; ++li) Ot[li] = zero4();
+                for (int li = 0; li < NL; ++li) Ot[li] = zero4();
 #pragma unroll
-            for (int db = 0; db < ND; ++db) {
-                const auto sf = frag16_acc<T>(S[db]);
+                for (int db = 0; db < ND; db += 2) {
+                    const F s0f = frag16_acc<T>(S[db]), s1f = frag16_acc<T>(S[db + 1]);
 #pragma unroll
-                for (int li = 0; li < NL; ++li)
-                    Ot[li] = mma16<T>(sf, frag16_lds(&Qs[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
-            }
+                    for (int li = 0; li < NL; ++li)
+                        Ot[li] = mma16x2<T>(s0f, s1f, frag16_lds(&Qs[16 * li * LDQ + 16 * db], LDQ, ln),
+                                            frag16_lds(&Qs[16 * li * LDQ + 16 * db + 16], LDQ, ln), Ot[li]);
+                }
 #pragma unroll
-            for (int li = 0; li < NL; ++li) {
-                const float gl = gam[16 * li + cl];
+                for (int li = 0; li < NL; ++li) {
+                    const float gl = gam[16 * li + cl];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) Ot[li][rr] *= gl;
+                    for (int rr = 0; rr < 4; ++rr) Ot[li][rr] *= gl;
+                }
+            };
+            if constexpr (!DELTA) ohist();
+            lds_barrier();
+
+            // ---- P2b: (delta) O^T history ; K^T through the matrix core -------------
+            if constexpr (DELTA) ohist();
+            {
+                constexpr int NKT = NL * ND / 4;             // transposes per state wave
+                F af[NKT];
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) {
+                    const int t = wave + 4 * i;
+                    af[i] = frag16_lds(&Ks[(t / ND) * 16 * LDQ + (t % ND) * 16], LDQ, ln);
+                }
+                const F id = ident_frag<T>(ln);
+                floatx4 d[NKT];
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) d[i] = mma16<T>(af[i], id, zero4());
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) {
+                    const int t = wave + 4 * i;
+                    store_tile_t(&KsT[(t % ND) * 16 * LDC + (t / ND) * 16], LDC, d[i], ln);
+                }
             }
             lds_barrier();
 
             // ---- P4: b1 Z = Tb R ; c1 O^T += Z^T Aq^T ; S_{r+1} -----------------------
+            F rf[NL];
+#pragma unroll
+            for (int li = 0; li < NL; ++li) rf[li] = frag16_acc<T>(R[li]);
             floatx4 Z[NL];
             if constexpr (DELTA) {
-#pragma unroll
-                for (int li = 0; li < NL; ++li) Z[li] = zero4();
-#pragma unroll
-                for (int mj = 0; mj < NL; ++mj) {
-                    const auto rb = frag16_acc<T>(R[mj]);
-#pragma unroll
-                    for (int li = mj; li < NL; ++li)
-                        Z[li] = mma16<T>(frag16_lds(&Tb[16 * li * LDC + 16 * mj], LDC, ln), rb, Z[li]);
-                }
+                // Z[li] = sum_{mj <= li} Tb(li, mj) R[mj].  An accumulation chain keeps
+                // one MFMA shape (mfma.h), so block row 2 takes the zero block (2, 3).
+                auto tbf = [&](int li, int mj) { return frag16_lds(&Tb[16 * li * LDC + 16 * mj], LDC, ln); };
+                Z[0] = mma16<T>(tbf(0, 0), rf[0], zero4());
+                Z[1] = mma16x2<T>(tbf(1, 0), tbf(1, 1), rf[0], rf[1], zero4());
+                Z[2] = mma16x2<T>(tbf(2, 2), tbf(2, 3), rf[2], rf[3],     // Tb(2, 3) = 0
+                                  mma16x2<T>(tbf(2, 0), tbf(2, 1), rf[0], rf[1], zero4()));
+                Z[3] = mma16x2<T>(tbf(3, 2), tbf(3, 3), rf[2], rf[3],
+                                  mma16x2<T>(tbf(3, 0), tbf(3, 1), rf[0], rf[1], zero4()));
             } else {
 #pragma unroll
                 for (int li = 0; li < NL; ++li) Z[li] = R[li];
             }
+            F zf[NL];
 #pragma unroll
-            for (int mj = 0; mj < NL; ++mj) {
-                const auto za = frag16_acc<T>(Z[mj]);
-#pragma unroll
-                for (int lj = mj; lj < NL; ++lj)
-                    Ot[lj] = mma16<T>(za, frag16_lds(&Aq[16 * lj * LDC + 16 * mj], LDC, ln), Ot[lj]);
+            for (int li = 0; li < NL; ++li) zf[li] = frag16_acc<T>(Z[li]);
+            {
+                // Ot[lj] += sum_{mj <= lj} Z[mj]^T Aq(lj, mj)^T
+                auto aqf = [&](int lj, int mj) { return frag16_lds(&Aq[16 * lj * LDC + 16 * mj], LDC, ln); };
+                Ot[0] = mma16<T>(zf[0], aqf(0, 0), Ot[0]);
+                Ot[1] = mma16x2<T>(zf[0], zf[1], aqf(1, 0), aqf(1, 1), Ot[1]);
+                Ot[2] = mma16x2<T>(zf[2], zf[3], aqf(2, 2), aqf(2, 3),    // Aq(2, 3) = 0
+                                   mma16x2<T>(zf[0], zf[1], aqf(2, 0), aqf(2, 1), Ot[2]));
+                Ot[3] = mma16x2<T>(zf[2], zf[3], aqf(3, 2), aqf(3, 3),
+                                   mma16x2<T>(zf[0], zf[1], aqf(3, 0), aqf(3, 1), Ot[3]));
             }
             // O^T tile -> Os[token][column]
 #pragma unroll
             for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
             // S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z
             const float gC = gam[kC - 1];
+            F zr[NL];
+            if constexpr (GATED) {
 #pragma unroll
-            for (int db = 0; db < ND; ++db)
+                for (int lj = 0; lj < NL; ++lj) {
+                    const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
+                    floatx4 z = Z[lj];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) z[rr] *= rh[rr];
+                    zr[lj] = frag16_acc<T>(z);
+                }
+            } else {
+#pragma unroll
+                for (int lj = 0; lj < NL; ++lj) zr[lj] = zf[lj];
+            }
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gC;
-#pragma unroll
-            for (int lj = 0; lj < NL; ++lj) {
-                floatx4 zr = Z[lj];
-                if constexpr (GATED) {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) zr[rr] *= rho[16 * lj + g4 + rr];
-                }
-                const auto zb = frag16_acc<T>(zr);
-#pragma unroll
-                for (int db = 0; db < ND; ++db)
-                    S[db] = mma16<T>(frag16_lds(&KsT[16 * db * LDC + 16 * lj], LDC, ln), zb, S[db]);
+                auto ktf = [&](int lj) { return frag16_lds(&KsT[16 * db * LDC + 16 * lj], LDC, ln); };
+                S[db] = mma16x2<T>(ktf(2), ktf(3), zr[2], zr[3], mma16x2<T>(ktf(0), ktf(1), zr[0], zr[1], S[db]));
             }
         }
         if (s_final) {
@@ -364,7 +410,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     s_final[(bh * DK + 16 * db + g4 + rr) * DV + vb * kDVB + n0 + cl] = S[db][rr];
         }
     } else if (wave == 4) {
-        // ======== wave 4: a1 gate scan; delta rule: a2 N blocks and a3/a4 T -------
+        // ======== wave 4: a1 gate scan; delta rule: a2 diagonal N blocks, a3/a4 T --
         T greg = from_f32<T>(0.f), breg = from_f32<T>(0.f);
         auto fetch_gate = [&](int64_t t0) {
             const int64_t tr = t0 + lane < Tlen ? t0 + lane : Tlen - 1;
@@ -398,70 +444,72 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             lds_barrier();
 
             if constexpr (DELTA) {
-                // ---- P2: N blocks in registers, then the triangular transform.
-                // x = K_mi K_lj^T; as k_m . k_l is symmetric, one product gives a
-                // diagonal block both as tile(N_bb^T) and as tile(N_bb).
-                typename Mfma<T>::frag kf[NL][NK];
-#pragma unroll
-                for (int b = 0; b < NL; ++b)
-#pragma unroll
-                    for (int i = 0; i < NK; ++i) kf[b][i] = Mfma<T>::load(&Ks[16 * b * LDQ], LDQ, i * Mfma<T>::kStep, ln);
-                // gate and beta of this lane's rows (16 b + g4 + rr) and column (16 b + cl)
-                floatx4 Grow[NL], brow[NL];
-                float Gcol[NL], bcol[NL];
+                // ---- P2a: diagonal N blocks in registers and their inverses.
+                // x = K_b K_b^T is symmetric, so one product gives N_bb both as
+                // tile(N_bb^T) (N[l][m], l = 16 b + cl) and as tile(N_bb).
+                floatx4 brow[NL], nd[NL], nt[NL], X[NL], Xt[NL];
 #pragma unroll
                 for (int b = 0; b < NL; ++b) {
-                    Grow[b] = *reinterpret_cast<const floatx4*>(&Gs[16 * b + g4]);
+                    const floatx4 x = dot_tile(Ks, Ks, b, b, ln);
+                    const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * b + g4]);
                     brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
-                    Gcol[b] = Gs[16 * b + cl];
-                    bcol[b] = bet[16 * b + cl];
-                }
-                floatx4 nd[NL], nt[NL], no[NL * (NL - 1) / 2];
+                    const float Gcol = Gs[16 * b + cl], bcol = bet[16 * b + cl];
 #pragma unroll
-                for (int lj = 0; lj < NL; ++lj) {
-#pragma unroll
-                    for (int mi = 0; mi <= lj; ++mi) {
-                        floatx4 x = zero4();     // x[rr] = k_m . k_l, m = 16 mi + g4 + rr, l = 16 lj + cl
-#pragma unroll
-                        for (int i = 0; i < NK; ++i) x = Mfma<T>::mma(kf[mi][i], kf[lj][i], x);
-                        floatx4 t;               // N[l][m]
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const float dec = GATED ? fast_exp2(Gcol[lj] - Grow[mi][rr]) : 1.f;
-                            t[rr] = (mi < lj || g4 + rr < cl) ? bcol[lj] * x[rr] * dec : 0.f;
-                        }
-                        if (mi == lj) {
-                            floatx4 u;           // N[m][l]
-#pragma unroll
-                            for (int rr = 0; rr < 4; ++rr) {
-                                const float dec = GATED ? fast_exp2(Grow[mi][rr] - Gcol[lj]) : 1.f;
-                                u[rr] = (cl < g4 + rr) ? brow[mi][rr] * x[rr] * dec : 0.f;
-                            }
-                            nt[lj] = t;
-                            nd[lj] = u;
-                        } else {
-                            no[lj * (lj - 1) / 2 + mi] = t;
-                        }
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const float dlm = GATED ? fast_exp2(Gcol - Grow[rr]) : 1.f;   // exp(G_l - G_m)
+                        const float dml = GATED ? fast_exp2(Grow[rr] - Gcol) : 1.f;
+                        nt[b][rr] = (g4 + rr < cl) ? bcol * x[rr] * dlm : 0.f;
+                        nd[b][rr] = (cl < g4 + rr) ? brow[b][rr] * x[rr] * dml : 0.f;
                     }
                 }
-                tsolve64_regs<T>(nd, nt, no[0], no[1], no[2], no[3], no[4], no[5], Tb, LDC, brow, bcol, ln);
+                tsolve_diag<T>(nd, nt, X, Xt, Tb, LDC, brow, ln);
+                lds_barrier();
+                // ---- P2b: off-diagonal blocks of T from the N blocks of waves 5..7
+                const floatx4* nl = Nlo + ln;
+                tsolve_offdiag<T>(X, Xt, nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
+                                  nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
             } else {
+                aq_share(Gs, 0, kNIW, ln);
+                lds_barrier();
                 if (r > 0) copy_out(t0 - kC, 0, ln);
-                aq_kt(Gs, 0, ln);
             }
             lds_barrier();
         }
     } else {
-        // ======== waves kW0..7: output copy, a2 Aq tiles, K^T -----------------------
+        // ======== waves kW0..7: (delta) N blocks below the diagonal, Aq tiles,
+        // output copy -------------------------------------------------------------
         const int iw = wave - kW0;
         for (int64_t r = 0; r < nchunks; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
+            const int cl = ln & 15, g4 = 4 * (ln >> 4);
+            const float* const Gs = Gsb[r & 1];
+            const float* const bet = betb[r & 1];
             stage(t0);
             if (r + 1 < nchunks) fetch(t0 + kC);
             lds_barrier();
+            // ---- P2a ----
+            if constexpr (DELTA) {
+                // N[l][m] for block (lj, mi), mi < lj, as a row fragment; slot
+                // lj (lj - 1) / 2 + mi of Nlo
+                auto n_block = [&](int lj, int mi) {
+                    const floatx4 x = dot_tile(Ks, Ks, mi, lj, ln);
+                    const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * mi + g4]);
+                    const float Gcol = Gs[16 * lj + cl], bcol = bet[16 * lj + cl];
+                    floatx4 t;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) t[rr] = bcol * x[rr] * (GATED ? fast_exp2(Gcol - Grow[rr]) : 1.f);
+                    Nlo[(lj * (lj - 1) / 2 + mi) * kWave + ln] = t;
+                };
+                // level 1 of the transform needs (1,0) and (3,2) first
+                if (iw == 0) { n_block(1, 0); n_block(3, 2); }
+                if (iw == 1) { n_block(2, 0); n_block(2, 1); }
+                if (iw == 2) { n_block(3, 0); n_block(3, 1); }
+            }
+            aq_share(Gs, iw, kNIW, ln);
+            lds_barrier();
+            // ---- P2b ----
             if (r > 0) copy_out(t0 - kC, iw, ln);
-            aq_kt(Gsb[r & 1], iw, ln);
             lds_barrier();
         }
     }

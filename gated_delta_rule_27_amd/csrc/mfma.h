@@ -215,6 +215,28 @@ __device__ __forceinline__ floatx4 mma16(typename Frag16<T>::type a, typename Fr
     }
 }
 
+// Two K = 16 products summed, D = A0 B0 + A1 B1 + acc, as one K = 32 matrix-core
+// op in bf16 (the 16x16x16 bf16 form takes as long as the 16x16x32 one).  The
+// K = 32 op sums over its 32 k slots, and lane group g holds slots 8g..8g+7;
+// filling them with k-block 0's k = 4g..4g+3 and then k-block 1's (the same
+// k in both operands) keeps every K = 16 register tile usable as is.
+// Do not feed the accumulator of a 16x16x32 bf16 op straight into a 16x16x16
+// bf16 op (or back): on gfx950 that chain read stale accumulator values with
+// the wait states the compiler inserted, so every chain here keeps one shape.
+template <typename T>
+__device__ __forceinline__ floatx4 mma16x2(typename Frag16<T>::type a0, typename Frag16<T>::type a1,
+                                           typename Frag16<T>::type b0, typename Frag16<T>::type b1,
+                                           floatx4 acc)
+{
+    if constexpr (sizeof(T) == 2) {
+        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    } else {
+        return mma16<T>(a1, b1, mma16<T>(a0, b0, acc));
+    }
+}
+
 // Identity as a K = 16 right factor (lane holds I[4(l/16)+r][l%16]): mma16
 // with it returns the left factor's block in the result layout, i.e. an exact
 // transpose when stored with store_tile_t.
