@@ -109,6 +109,42 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
+def time_chunk(la, syn, case, dev, steps, warmup=2):
+    """Event-timed chunk forward of one workload (inputs resident in HBM); the
+    figures of a secondary line beside the headline one."""
+    import torch
+    B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
+    x = syn.chunk_inputs_torch(case, dev)
+    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    wsb = la.chunk_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+    def step():
+        la.chunk_fwd(x["q"], x["k"], x["v"], x.get("g"), x.get("beta"), None, rule=case.rule,
+                     gate=case.gate, out=out, s_final=s_fin, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    s = 2 if case.dtype == "bf16" else 4
+    abytes = chunk_alg_bytes(B, H, T, dk, dv, s, case.rule, case.gate)
+    aflops = chunk_nominal_flops(B, H, T, dk, dv, case.rule)
+    return {"workload": f"{case.rule}/{case.gate} chunk_fwd B={B} H={H} T={T} dk={dk} dv={dv} "
+                        f"{case.dtype} tokens fp32 state",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "path": "split" if wsb else "fused", "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,10 +152,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32,
+    ap.add_argument("--cpu-heads", type=int, default=128,
                     help="heads of the workload the CPU oracle runs for its baseline")
     ap.add_argument("--path", choices=["fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice, fused)")
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4",
+                    help="comma-separated secondary chunk workloads to time after the headline "
+                         "one (cfg2, cfg3b, cfg4), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -182,6 +221,16 @@ def main():
     gbps = abytes / (ms * 1e-3) / 1e9
     tflops = aflops / (ms * 1e-3) / 1e12
 
+    # ---------------- secondary chunk workloads (reported beside the headline) ----
+    others = []
+    names = [n for n in args.other_configs.split(",") if n and n != "none"]
+    del x, out, s_fin, ws
+    torch.cuda.empty_cache()
+    for name in names:
+        oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
+        others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))
+        torch.cuda.empty_cache()
+
     # ---------------- decode step --------------------------------------------
     decode = None
     if args.decode_steps > 0:
@@ -225,7 +274,9 @@ def main():
         import oracle
         nh = max(1, min(args.cpu_heads, B * H))
         sel = lambda t: t.reshape(B * H, *t.shape[2:])[:nh].unsqueeze(0).to("cpu", torch.float64).numpy()
+        x = syn.chunk_inputs_torch(case, dev)
         xs = {n: sel(x[n]) for n in ("q", "k", "v", "g", "beta")}
+        del x
         cores = len(os.sched_getaffinity(0))
         t0 = time.perf_counter()
         oracle.recurrence(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], None, rule=case.rule,
@@ -271,6 +322,7 @@ def main():
                           "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                           "nominal_flops_per_launch": aflops},
         "decode": decode,
+        "other_chunk_workloads": others,
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(dev),
     }
