@@ -164,14 +164,26 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             vreg[p] = *reinterpret_cast<const i4*>(vh + tr * DV + col);
         }
     };
+    // Q and K rows go to LDS with their columns in pcol order (mfma.h), 8 bytes
+    // (four columns) at a time for bf16
     auto stage = [&](int64_t t0) {
 #pragma unroll
         for (int p = 0; p < NQ; ++p) {
             const int idx = (p * kNT + tid) * E;
             const int row = idx / DK, col = idx % DK;
             const bool ok = t0 + row < Tlen;
-            *reinterpret_cast<i4*>(&Qs[row * LDQ + col]) = ok ? qreg[p] : i4{0, 0, 0, 0};
-            *reinterpret_cast<i4*>(&Ks[row * LDQ + col]) = ok ? kreg[p] : i4{0, 0, 0, 0};
+            const i4 qv = ok ? qreg[p] : i4{0, 0, 0, 0};
+            const i4 kv = ok ? kreg[p] : i4{0, 0, 0, 0};
+            if constexpr (E == 8) {
+                typedef __attribute__((__vector_size__(8))) int i2;
+                *reinterpret_cast<i2*>(&Qs[row * LDQ + pcol(col)]) = i2{qv[0], qv[1]};
+                *reinterpret_cast<i2*>(&Qs[row * LDQ + pcol(col + 4)]) = i2{qv[2], qv[3]};
+                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col)]) = i2{kv[0], kv[1]};
+                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col + 4)]) = i2{kv[2], kv[3]};
+            } else {
+                *reinterpret_cast<i4*>(&Qs[row * LDQ + pcol(col)]) = qv;
+                *reinterpret_cast<i4*>(&Ks[row * LDQ + pcol(col)]) = kv;
+            }
         }
 #pragma unroll
         for (int p = 0; p < NV; ++p) {
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const float dec = GATED ? fast_exp2(Gl - Gm[rr]) : 1.f;
             va[rr] = (mi < lj || g4 + rr <= cl) ? xa[rr] * dec : 0.f;
         }
-        store_tile_t(&Aq[lj * 16 * LDC + mi * 16], LDC, va, ln);
+        store_tile_t_pc(&Aq[lj * 16 * LDC], LDC, mi, va, ln);
     };
     // this wave's share (iw of nw) of the ten causal Aq tiles
     auto aq_share = [&](const float* Gs, int iw, int nw, int ln) {
@@ -259,6 +271,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 }
             }
         }
+        wait_vmem_all();
         for (int64_t r = 0; r < nchunks; ++r) {
             const int64_t t0 = r * kC;
             // lane indices recomputed per chunk so the LDS addresses derived from
@@ -284,11 +297,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 for (int li = 0; li < NL; ++li) P[li] = zero4();
 #pragma unroll
                 for (int db = 0; db < ND; db += 2) {
-                    const F s0f = frag16_acc<T>(S[db]), s1f = frag16_acc<T>(S[db + 1]);
+                    const auto sp = pair_regs<T>(S[db], S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        P[li] = mma16x2<T>(frag16_lds(&Ks[16 * li * LDQ + 16 * db], LDQ, ln),
-                                           frag16_lds(&Ks[16 * li * LDQ + 16 * db + 16], LDQ, ln), s0f, s1f, P[li]);
+                        P[li] = mma_pair<T>(pair_lds(&Ks[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
                 }
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
@@ -304,11 +316,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 for (int li = 0; li < NL; ++li) Ot[li] = zero4();
 #pragma unroll
                 for (int db = 0; db < ND; db += 2) {
-                    const F s0f = frag16_acc<T>(S[db]), s1f = frag16_acc<T>(S[db + 1]);
+                    const auto sp = pair_regs<T>(S[db], S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        Ot[li] = mma16x2<T>(s0f, s1f, frag16_lds(&Qs[16 * li * LDQ + 16 * db], LDQ, ln),
-                                            frag16_lds(&Qs[16 * li * LDQ + 16 * db + 16], LDQ, ln), Ot[li]);
+                        Ot[li] = mma_pair<T>(sp, pair_lds(&Qs[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
                 }
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
                 for (int i = 0; i < NKT; ++i) {
                     const int t = wave + 4 * i;
-                    af[i] = frag16_lds(&Ks[(t / ND) * 16 * LDQ + (t % ND) * 16], LDQ, ln);
+                    af[i] = frag16_lds_pc(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
                 }
                 const F id = ident_frag<T>(ln);
                 floatx4 d[NKT];
@@ -337,68 +348,60 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
                 for (int i = 0; i < NKT; ++i) {
                     const int t = wave + 4 * i;
-                    store_tile_t(&KsT[(t % ND) * 16 * LDC + (t / ND) * 16], LDC, d[i], ln);
+                    store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
                 }
             }
             lds_barrier();
 
             // ---- P4: b1 Z = Tb R ; c1 O^T += Z^T Aq^T ; S_{r+1} -----------------------
-            F rf[NL];
-#pragma unroll
-            for (int li = 0; li < NL; ++li) rf[li] = frag16_acc<T>(R[li]);
+            // Products over token blocks run in pairs (blocks 0,1 and 2,3); the
+            // causal blocks above the diagonal of Tb and Aq are zero, so block rows
+            // 0 and 2 take them as partners and every accumulation chain keeps one
+            // MFMA shape (mfma.h).
             floatx4 Z[NL];
             if constexpr (DELTA) {
-                // Z[li] = sum_{mj <= li} Tb(li, mj) R[mj].  An accumulation chain keeps
-                // one MFMA shape (mfma.h), so block row 2 takes the zero block (2, 3).
-                auto tbf = [&](int li, int mj) { return frag16_lds(&Tb[16 * li * LDC + 16 * mj], LDC, ln); };
-                Z[0] = mma16<T>(tbf(0, 0), rf[0], zero4());
-                Z[1] = mma16x2<T>(tbf(1, 0), tbf(1, 1), rf[0], rf[1], zero4());
-                Z[2] = mma16x2<T>(tbf(2, 2), tbf(2, 3), rf[2], rf[3],     // Tb(2, 3) = 0
-                                  mma16x2<T>(tbf(2, 0), tbf(2, 1), rf[0], rf[1], zero4()));
-                Z[3] = mma16x2<T>(tbf(3, 2), tbf(3, 3), rf[2], rf[3],
-                                  mma16x2<T>(tbf(3, 0), tbf(3, 1), rf[0], rf[1], zero4()));
+                // Z[li] = sum_{mj <= li} Tb(li, mj) R[mj]
+                const auto r01 = pair_regs<T>(R[0], R[1]), r23 = pair_regs<T>(R[2], R[3]);
+#pragma unroll
+                for (int li = 0; li < NL; ++li) {
+                    Z[li] = mma_pair<T>(pair_lds(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
+                    if (li >= 2) Z[li] = mma_pair<T>(pair_lds(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                }
             } else {
 #pragma unroll
                 for (int li = 0; li < NL; ++li) Z[li] = R[li];
             }
-            F zf[NL];
-#pragma unroll
-            for (int li = 0; li < NL; ++li) zf[li] = frag16_acc<T>(Z[li]);
             {
                 // Ot[lj] += sum_{mj <= lj} Z[mj]^T Aq(lj, mj)^T
-                auto aqf = [&](int lj, int mj) { return frag16_lds(&Aq[16 * lj * LDC + 16 * mj], LDC, ln); };
-                Ot[0] = mma16<T>(zf[0], aqf(0, 0), Ot[0]);
-                Ot[1] = mma16x2<T>(zf[0], zf[1], aqf(1, 0), aqf(1, 1), Ot[1]);
-                Ot[2] = mma16x2<T>(zf[2], zf[3], aqf(2, 2), aqf(2, 3),    // Aq(2, 3) = 0
-                                   mma16x2<T>(zf[0], zf[1], aqf(2, 0), aqf(2, 1), Ot[2]));
-                Ot[3] = mma16x2<T>(zf[2], zf[3], aqf(3, 2), aqf(3, 3),
-                                   mma16x2<T>(zf[0], zf[1], aqf(3, 0), aqf(3, 1), Ot[3]));
+                const auto z01 = pair_regs<T>(Z[0], Z[1]), z23 = pair_regs<T>(Z[2], Z[3]);
+#pragma unroll
+                for (int lj = 0; lj < NL; ++lj) {
+                    Ot[lj] = mma_pair<T>(z01, pair_lds(&Aq[16 * lj * LDC], LDC, ln), Ot[lj]);
+                    if (lj >= 2) Ot[lj] = mma_pair<T>(z23, pair_lds(&Aq[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
+                }
             }
             // O^T tile -> Os[token][column]
 #pragma unroll
             for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
             // S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z
             const float gC = gam[kC - 1];
-            F zr[NL];
-            if constexpr (GATED) {
+            floatx4 zr[NL];
 #pragma unroll
-                for (int lj = 0; lj < NL; ++lj) {
+            for (int lj = 0; lj < NL; ++lj) {
+                zr[lj] = Z[lj];
+                if constexpr (GATED) {
                     const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
-                    floatx4 z = Z[lj];
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) z[rr] *= rh[rr];
-                    zr[lj] = frag16_acc<T>(z);
+                    for (int rr = 0; rr < 4; ++rr) zr[lj][rr] *= rh[rr];
                 }
-            } else {
-#pragma unroll
-                for (int lj = 0; lj < NL; ++lj) zr[lj] = zf[lj];
             }
+            const auto zr01 = pair_regs<T>(zr[0], zr[1]), zr23 = pair_regs<T>(zr[2], zr[3]);
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gC;
-                auto ktf = [&](int lj) { return frag16_lds(&KsT[16 * db * LDC + 16 * lj], LDC, ln); };
-                S[db] = mma16x2<T>(ktf(2), ktf(3), zr[2], zr[3], mma16x2<T>(ktf(0), ktf(1), zr[0], zr[1], S[db]));
+                S[db] = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
+                                    mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
             }
         }
         if (s_final) {
@@ -462,11 +465,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                         nd[b][rr] = (cl < g4 + rr) ? brow[b][rr] * x[rr] * dml : 0.f;
                     }
                 }
-                tsolve_diag<T>(nd, nt, X, Xt, Tb, LDC, brow, ln);
+                tsolve_diag<T, true>(nd, nt, X, Xt, Tb, LDC, brow, ln);
                 lds_barrier();
                 // ---- P2b: off-diagonal blocks of T from the N blocks of waves 5..7
                 const floatx4* nl = Nlo + ln;
-                tsolve_offdiag<T>(X, Xt, nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
+                tsolve_offdiag<T, true>(X, Xt, nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
                                   nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
             } else {
                 aq_share(Gs, 0, kNIW, ln);

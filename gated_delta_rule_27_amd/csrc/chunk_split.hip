@@ -307,6 +307,7 @@ __global__ __launch_bounds__(256, 1) void chunk_chain_kernel(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
             S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
+    wait_vmem_all();
 
     i4 rq[VQ], rk[VQ], rkr[VQ], ra[VA], rt[VA], rv[VV];
     i4 rg = {0, 0, 0, 0};

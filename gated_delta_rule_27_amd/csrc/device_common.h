@@ -27,6 +27,14 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return sta
 // 2^x through the hardware transcendental unit (v_exp_f32)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for every outstanding vector-memory access (gfx9 s_waitcnt: vmcnt 0,
+// expcnt and lgkmcnt left at their maxima).  After registers were filled by
+// global loads before a loop, this tells the compiler's wait-count tracking
+// that they are ready; otherwise it keeps them "pending" at the loop head and
+// places a full wait inside the loop, which also waits for the loads the loop
+// issues to prefetch its next iteration.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // An opaque copy of a value: the compiler cannot see through it, so lane
 // arithmetic derived from it inside a loop is recomputed there instead of
 // being hoisted out and held in registers for the whole loop.

@@ -237,6 +237,72 @@ __device__ __forceinline__ floatx4 mma16x2(typename Frag16<T>::type a0, typename
     }
 }
 
+// ---- paired (K = 32) operands from LDS ---------------------------------------
+// Column order of LDS tiles that feed paired products: inside every group of 32
+// columns, column 16h + 4g + j is stored at 8g + 4h + j.  The eight values lane
+// group g needs for a paired operand (k-block 0's 4g..4g+3, then k-block 1's,
+// the slot order of mma16x2) are then one 16-byte read, and every aligned run of
+// four columns stays contiguous (so K = 16 fragments and transposed tile stores
+// keep 8-byte accesses).  A 16x16x32 fragment read straight from such a tile is
+// the same k permutation, which any product of two tiles stored alike allows.
+__host__ __device__ constexpr int pcol(int c)
+{
+    return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+}
+
+template <typename T> struct Pair;
+template <> struct Pair<bf16> { typedef bf16x8 type; };
+template <> struct Pair<float> { struct type { floatx4 lo, hi; }; };
+
+// paired operand of the row block at M (columns 32p..32p+31 of the block start
+// at M, stored in pcol order): lane holds row l%16, k-blocks 2p and 2p+1
+template <typename T>
+__device__ __forceinline__ typename Pair<T>::type pair_lds(const T* M, int ld, int lane)
+{
+    const T* p = M + (lane & 15) * ld + 8 * (lane >> 4);
+    if constexpr (sizeof(T) == 2) {
+        return *reinterpret_cast<const bf16x8*>(p);
+    } else {
+        return {*reinterpret_cast<const floatx4*>(p), *reinterpret_cast<const floatx4*>(p + 4)};
+    }
+}
+
+// paired operand from two result tiles (k-block 0 = x0, k-block 1 = x1)
+template <typename T>
+__device__ __forceinline__ typename Pair<T>::type pair_regs(floatx4 x0, floatx4 x1)
+{
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_shufflevector(frag16_acc<bf16>(x0), frag16_acc<bf16>(x1), 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        return {x0, x1};
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ floatx4 mma_pair(typename Pair<T>::type a, typename Pair<T>::type b, floatx4 acc)
+{
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    } else {
+        return mma16<float>(a.hi, b.hi, mma16<float>(a.lo, b.lo, acc));
+    }
+}
+
+// K = 16 fragment (as frag16_lds) of k-block kb of a row block stored in pcol order
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type frag16_lds_pc(const T* M, int ld, int kb, int lane)
+{
+    return *reinterpret_cast<const typename Frag16<T>::type*>(
+        M + (lane & 15) * ld + 32 * (kb >> 1) + 4 * (kb & 1) + 8 * (lane >> 4));
+}
+
+// store_tile_t into column block kb of a row block stored in pcol order
+template <typename T>
+__device__ __forceinline__ void store_tile_t_pc(T* M, int ld, int kb, floatx4 v, int lane)
+{
+    store_tile_t(M + 32 * (kb >> 1) + 4 * (kb & 1) + 4 * (lane >> 4), ld, v, lane);
+}
+
 // Identity as a K = 16 right factor (lane holds I[4(l/16)+r][l%16]): mma16
 // with it returns the left factor's block in the result layout, i.e. an exact
 // transpose when stored with store_tile_t.

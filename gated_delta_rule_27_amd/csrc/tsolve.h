@@ -31,10 +31,19 @@
 
 namespace linattn {
 
+// Tb block (rb, qb) from -tile(C^T)-style data: with PC the columns of Tb are
+// stored in pcol order (mfma.h).
+template <typename T, bool PC>
+__device__ __forceinline__ void store_tb(T* Tb, int ldt, int rb, int qb, floatx4 v, int lane)
+{
+    if constexpr (PC) store_tile_t_pc(&Tb[(rb * 16) * ldt], ldt, qb, v, lane);
+    else store_tile_t(&Tb[(rb * 16) * ldt + qb * 16], ldt, v, lane);
+}
+
 // Diagonal blocks.  nd[b] = tile(N_bb), nt[b] = tile(N_bb^T).  Returns
 // X[b] = tile(X_bb) and Xt[b] = tile(X_bb^T) (fp32) and stores the diagonal
 // blocks of Tb = T diag(beta); brow[b][r] = beta[16 b + 4(l/16) + r].
-template <typename T>
+template <typename T, bool PC = false>
 __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[4], const floatx4 (&nt)[4],
                                             floatx4 (&X)[4], floatx4 (&Xt)[4], T* Tb, int ldt,
                                             const floatx4 (&brow)[4], int lane)
@@ -90,13 +99,13 @@ __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[4], const floatx
         floatx4 w = Xt[b];
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] *= brow[b][r];
-        store_tile_t(&Tb[(b * 16) * ldt + b * 16], ldt, w, lane);
+        store_tb<T, PC>(Tb, ldt, b, b, w, lane);
     }
 }
 
 // Off-diagonal blocks from X, Xt (tsolve_diag) and the row fragments of the six
 // N blocks below the diagonal, n_ij = tile(N_ij^T); stores them into Tb.
-template <typename T>
+template <typename T, bool PC = false>
 __device__ __forceinline__ void tsolve_offdiag(const floatx4 (&X)[4], const floatx4 (&Xt)[4],
                                                floatx4 n10, floatx4 n20, floatx4 n21, floatx4 n30,
                                                floatx4 n31, floatx4 n32, T* Tb, int ldt,
@@ -111,7 +120,7 @@ __device__ __forceinline__ void tsolve_offdiag(const floatx4 (&X)[4], const floa
     auto store_neg = [&](floatx4 ct, int rb, int qb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) ct[r] = -ct[r] * brow[qb][r];
-        store_tile_t(&Tb[(rb * 16) * ldt + qb * 16], ldt, ct, lane);
+        store_tb<T, PC>(Tb, ldt, rb, qb, ct, lane);
     };
 
     // ---- level 1 ----------------------------------------------------------------
