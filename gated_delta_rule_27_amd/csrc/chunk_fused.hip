@@ -112,8 +112,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     __shared__ __align__(16) T Aq[kC * LDC];
     __shared__ __align__(16) T Os[kC * LDV];
     __shared__ __align__(16) T Tb[DELTA ? kC * LDC : 8];
-    // the six N blocks below the diagonal as row fragments, lane by lane
+    // the six N blocks below the diagonal as row fragments, lane by lane, and the
+    // X tiles the two halves of the off-diagonal transform exchange (X11 from
+    // wave 4; X22^T and X33^T from wave 5)
     __shared__ __align__(16) floatx4 Nlo[DELTA ? 6 * kWave : 1];
+    __shared__ __align__(16) floatx4 Xx[DELTA ? 3 * kWave : 1];
     // gate values alternate between two buffers: the state waves still read the
     // previous chunk's while wave 4 writes this chunk's
     __shared__ __align__(16) float Gsb[2][kC], gamb[2][kC], rhob[2][kC], betb[2][kC];
@@ -215,23 +218,31 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
     };
 
-    // x[rr] = sum_c A[16 mi + g4 + rr][c] B[16 lj + cl][c] (A, B: Ks or Qs rows)
-    auto dot_tile = [&](const T* A, const T* B, int mi, int lj, int ln) {
-        typename Mfma<T>::frag fa[NK], fb[NK];
+    // All matrix-core fragments (every k step) of the 16-row block b of a [C][DK]
+    // tile (Qs or Ks); a wave loads each block it needs once per chunk and forms
+    // its tiles from the registers.
+    using Fr = typename Mfma<T>::frag;
+    auto block_frags = [&](const T* A, int b, int ln, Fr (&f)[NK]) {
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            fa[i] = Mfma<T>::load(&A[mi * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
-            fb[i] = Mfma<T>::load(&B[lj * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
-        }
+        for (int i = 0; i < NK; ++i) f[i] = Mfma<T>::load(&A[b * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
+    };
+    // x[rr] = sum_c A[16 mi + g4 + rr][c] B[16 lj + cl][c] from the blocks' fragments
+    auto tile_dot = [&](const Fr (&fa)[NK], const Fr (&fb)[NK]) {
         floatx4 x = zero4();
 #pragma unroll
         for (int i = 0; i < NK; ++i) x = Mfma<T>::mma(fa[i], fb[i], x);
         return x;
     };
-    // a2 Aq tile (lj, mi), mi <= lj: Aq[l][m] = (q_l . k_m) exp(G_l - G_m), m <= l
-    auto aq_tile = [&](const float* Gs, int lj, int mi, int ln) {
+    auto dot_tile = [&](const T* A, const T* B, int mi, int lj, int ln) {
+        Fr fa[NK], fb[NK];
+        block_frags(A, mi, ln, fa);
+        block_frags(B, lj, ln, fb);
+        return tile_dot(fa, fb);
+    };
+    // a2 Aq tile (lj, mi), mi <= lj, from xa[rr] = k_m . q_l:
+    // Aq[l][m] = (q_l . k_m) exp(G_l - G_m), m <= l
+    auto aq_store = [&](const float* Gs, int lj, int mi, floatx4 xa, int ln) {
         const int cl = ln & 15, g4 = 4 * (ln >> 4);
-        const floatx4 xa = dot_tile(Ks, Qs, mi, lj, ln);
         const float Gl = Gs[lj * 16 + cl];
         const floatx4 Gm = *reinterpret_cast<const floatx4*>(&Gs[mi * 16 + g4]);
         floatx4 va;
@@ -241,6 +252,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             va[rr] = (mi < lj || g4 + rr <= cl) ? xa[rr] * dec : 0.f;
         }
         store_tile_t_pc(&Aq[lj * 16 * LDC], LDC, mi, va, ln);
+    };
+    auto aq_tile = [&](const float* Gs, int lj, int mi, int ln) {
+        aq_store(Gs, lj, mi, dot_tile(Ks, Qs, mi, lj, ln), ln);
     };
     // this wave's share (iw of nw) of the ten causal Aq tiles
     auto aq_share = [&](const float* Gs, int iw, int nw, int ln) {
@@ -252,6 +266,43 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 aq_tile(Gs, lj, mi, ln);
             }
         }
+    };
+
+    // a2 diagonal N blocks b0 and b0 + 1 in registers.  x = K_b K_b^T is
+    // symmetric, so one product gives N_bb both as tile(N_bb^T) (lane value
+    // N[l][m], l = 16 b + cl) and as tile(N_bb); at most one of the two is
+    // nonzero at each position, so one exp2 serves both.
+    // br[i][rr] = beta[16 (b0 + i) + g4 + rr].  Both blocks' loads are issued
+    // before their products, which are interleaved.
+    auto diag_blocks2 = [&](const float* Gs, const float* bet, int b0, int ln, floatx4 (&nd)[2],
+                            floatx4 (&nt)[2], floatx4 (&br)[2]) {
+        const int cl = ln & 15, g4 = 4 * (ln >> 4);
+        Fr kb[2][NK];
+        block_frags(Ks, b0, ln, kb[0]);
+        block_frags(Ks, b0 + 1, ln, kb[1]);
+        floatx4 Grow[2];
+        float Gcol[2], bcol[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            Grow[i] = *reinterpret_cast<const floatx4*>(&Gs[16 * (b0 + i) + g4]);
+            br[i] = *reinterpret_cast<const floatx4*>(&bet[16 * (b0 + i) + g4]);
+            Gcol[i] = Gs[16 * (b0 + i) + cl];
+            bcol[i] = bet[16 * (b0 + i) + cl];
+        }
+        floatx4 x[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) x[i] = Mfma<T>::mma(kb[i][k], kb[i][k], x[i]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const bool up = g4 + rr < cl;                   // N[l][m] with m < l
+                const float d = GATED ? fast_exp2(up ? Gcol[i] - Grow[i][rr] : Grow[i][rr] - Gcol[i]) : 1.f;
+                nt[i][rr] = up ? bcol[i] * x[i][rr] * d : 0.f;
+                nd[i][rr] = (cl < g4 + rr) ? br[i][rr] * x[i][rr] * d : 0.f;
+            }
     };
 
     if (wave < 4) {
@@ -328,7 +379,38 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     for (int rr = 0; rr < 4; ++rr) Ot[li][rr] *= gl;
                 }
             };
-            if constexpr (!DELTA) ohist();
+            if constexpr (!DELTA) {
+                ohist();
+            } else {
+                // a2 Aq tiles, grouped so each wave loads few blocks: wave 0 the
+                // query blocks 0-1, wave 1 block 2, waves 2-3 block 3
+                const float* const Gs = Gsb[r & 1];
+                Fr fq[NK], fa[NK], fb[NK];
+                if (wave == 0) {
+                    block_frags(Ks, 0, ln, fa);
+                    block_frags(Qs, 0, ln, fq);
+                    aq_store(Gs, 0, 0, tile_dot(fa, fq), ln);
+                    block_frags(Qs, 1, ln, fq);
+                    aq_store(Gs, 1, 0, tile_dot(fa, fq), ln);
+                    block_frags(Ks, 1, ln, fb);
+                    aq_store(Gs, 1, 1, tile_dot(fb, fq), ln);
+                } else if (wave == 1) {
+                    block_frags(Qs, 2, ln, fq);
+                    block_frags(Ks, 0, ln, fa);
+                    aq_store(Gs, 2, 0, tile_dot(fa, fq), ln);
+                    block_frags(Ks, 1, ln, fb);
+                    aq_store(Gs, 2, 1, tile_dot(fb, fq), ln);
+                    block_frags(Ks, 2, ln, fa);
+                    aq_store(Gs, 2, 2, tile_dot(fa, fq), ln);
+                } else {
+                    const int m0 = wave == 2 ? 0 : 2;
+                    block_frags(Qs, 3, ln, fq);
+                    block_frags(Ks, m0, ln, fa);
+                    aq_store(Gs, 3, m0, tile_dot(fa, fq), ln);
+                    block_frags(Ks, m0 + 1, ln, fb);
+                    aq_store(Gs, 3, m0 + 1, tile_dot(fb, fq), ln);
+                }
+            }
             lds_barrier();
 
             // ---- P2b: (delta) O^T history ; K^T through the matrix core -------------
@@ -447,30 +529,20 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             lds_barrier();
 
             if constexpr (DELTA) {
-                // ---- P2a: diagonal N blocks in registers and their inverses.
-                // x = K_b K_b^T is symmetric, so one product gives N_bb both as
-                // tile(N_bb^T) (N[l][m], l = 16 b + cl) and as tile(N_bb).
-                floatx4 brow[NL], nd[NL], nt[NL], X[NL], Xt[NL];
-#pragma unroll
-                for (int b = 0; b < NL; ++b) {
-                    const floatx4 x = dot_tile(Ks, Ks, b, b, ln);
-                    const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * b + g4]);
-                    brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
-                    const float Gcol = Gs[16 * b + cl], bcol = bet[16 * b + cl];
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const float dlm = GATED ? fast_exp2(Gcol - Grow[rr]) : 1.f;   // exp(G_l - G_m)
-                        const float dml = GATED ? fast_exp2(Grow[rr] - Gcol) : 1.f;
-                        nt[b][rr] = (g4 + rr < cl) ? bcol * x[rr] * dlm : 0.f;
-                        nd[b][rr] = (cl < g4 + rr) ? brow[b][rr] * x[rr] * dml : 0.f;
-                    }
-                }
-                tsolve_diag<T, true>(nd, nt, X, Xt, Tb, LDC, brow, ln);
+                // ---- P2a: diagonal N blocks 0, 1 and their inverses; X11 to LDS
+                floatx4 nd[2], nt[2], X[2], Xt[2], br[2];
+                diag_blocks2(Gs, bet, 0, ln, nd, nt, br);
+                tsolve_diag<T, true, 2, 0>(nd, nt, X, Xt, Tb, LDC, br, ln);
+                Xx[0 * kWave + ln] = X[1];
                 lds_barrier();
-                // ---- P2b: off-diagonal blocks of T from the N blocks of waves 5..7
+                // ---- P2b: half A of the off-diagonal blocks (column block 0, T10)
+                floatx4 brow[NL];
+#pragma unroll
+                for (int b = 0; b < NL; ++b) brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
                 const floatx4* nl = Nlo + ln;
-                tsolve_offdiag<T, true>(X, Xt, nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
-                                  nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
+                tsolve_offdiag_a<T, true>(X[0], Xt[1], Xx[1 * kWave + ln], Xx[2 * kWave + ln], nl[0 * kWave],
+                                          nl[1 * kWave], nl[2 * kWave], nl[3 * kWave], nl[4 * kWave],
+                                          nl[5 * kWave], Tb, LDC, brow, ln);
             } else {
                 aq_share(Gs, 0, kNIW, ln);
                 lds_barrier();
@@ -478,9 +550,38 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
             lds_barrier();
         }
+    } else if (DELTA && wave == 5) {
+        // ======== wave 5 (delta): a2 diagonal N blocks 2, 3 and their inverses;
+        // half B of the off-diagonal blocks; output copy -------------------------
+        for (int64_t r = 0; r < nchunks; ++r) {
+            const int64_t t0 = r * kC;
+            const int ln = opaque(lane);
+            const int g4 = 4 * (ln >> 4);
+            const float* const Gs = Gsb[r & 1];
+            const float* const bet = betb[r & 1];
+            stage(t0);
+            if (r + 1 < nchunks) fetch(t0 + kC);
+            lds_barrier();
+            // ---- P2a ----
+            floatx4 nd[2], nt[2], X[2], Xt[2], br[2];
+            diag_blocks2(Gs, bet, 2, ln, nd, nt, br);
+            tsolve_diag<T, true, 2, 2>(nd, nt, X, Xt, Tb, LDC, br, ln);
+            Xx[1 * kWave + ln] = Xt[0];
+            Xx[2 * kWave + ln] = Xt[1];
+            lds_barrier();
+            // ---- P2b: column block 1 and T32; output copy ----
+            floatx4 brow[NL];
+#pragma unroll
+            for (int b = 0; b < NL; ++b) brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
+            const floatx4* nl = Nlo + ln;
+            tsolve_offdiag_b<T, true>(Xx[0 * kWave + ln], X[0], Xt[0], Xt[1], nl[2 * kWave], nl[4 * kWave],
+                                      nl[5 * kWave], Tb, LDC, brow, ln);
+            if (r > 0) copy_out(t0 - kC, 0, ln);
+            lds_barrier();
+        }
     } else {
-        // ======== waves kW0..7: (delta) N blocks below the diagonal, Aq tiles,
-        // output copy -------------------------------------------------------------
+        // ======== waves 6, 7 (delta): N blocks below the diagonal; waves 4..7
+        // (add): Aq tiles.  Both: output copy ----------------------------------------
         const int iw = wave - kW0;
         for (int64_t r = 0; r < nchunks; ++r) {
             const int64_t t0 = r * kC;
@@ -494,9 +595,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             // ---- P2a ----
             if constexpr (DELTA) {
                 // N[l][m] for block (lj, mi), mi < lj, as a row fragment; slot
-                // lj (lj - 1) / 2 + mi of Nlo
-                auto n_block = [&](int lj, int mi) {
-                    const floatx4 x = dot_tile(Ks, Ks, mi, lj, ln);
+                // lj (lj - 1) / 2 + mi of Nlo.  Wave 6 takes the blocks of rows
+                // 1-2 (K0-K2), wave 7 those of row 3 (K0-K3); each K block's
+                // fragments are loaded once.
+                auto n_block = [&](int lj, int mi, const Fr (&fm)[NK], const Fr (&fl)[NK]) {
+                    const floatx4 x = tile_dot(fm, fl);
                     const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * mi + g4]);
                     const float Gcol = Gs[16 * lj + cl], bcol = bet[16 * lj + cl];
                     floatx4 t;
@@ -504,12 +607,24 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     for (int rr = 0; rr < 4; ++rr) t[rr] = bcol * x[rr] * (GATED ? fast_exp2(Gcol - Grow[rr]) : 1.f);
                     Nlo[(lj * (lj - 1) / 2 + mi) * kWave + ln] = t;
                 };
-                // level 1 of the transform needs (1,0) and (3,2) first
-                if (iw == 0) { n_block(1, 0); n_block(3, 2); }
-                if (iw == 1) { n_block(2, 0); n_block(2, 1); }
-                if (iw == 2) { n_block(3, 0); n_block(3, 1); }
+                Fr k0[NK], k1[NK], k2[NK];
+                block_frags(Ks, 0, ln, k0);
+                block_frags(Ks, 1, ln, k1);
+                block_frags(Ks, 2, ln, k2);
+                if (wave == 6) {
+                    n_block(1, 0, k0, k1);
+                    n_block(2, 0, k0, k2);
+                    n_block(2, 1, k1, k2);
+                } else {
+                    Fr k3[NK];
+                    block_frags(Ks, 3, ln, k3);
+                    n_block(3, 0, k0, k3);
+                    n_block(3, 1, k1, k3);
+                    n_block(3, 2, k2, k3);
+                }
+            } else {
+                aq_share(Gs, iw, kNIW, ln);
             }
-            aq_share(Gs, iw, kNIW, ln);
             lds_barrier();
             // ---- P2b ----
             if (r > 0) copy_out(t0 - kC, iw, ln);

@@ -40,13 +40,14 @@ __device__ __forceinline__ void store_tb(T* Tb, int ldt, int rb, int qb, floatx4
     else store_tile_t(&Tb[(rb * 16) * ldt + qb * 16], ldt, v, lane);
 }
 
-// Diagonal blocks.  nd[b] = tile(N_bb), nt[b] = tile(N_bb^T).  Returns
-// X[b] = tile(X_bb) and Xt[b] = tile(X_bb^T) (fp32) and stores the diagonal
-// blocks of Tb = T diag(beta); brow[b][r] = beta[16 b + 4(l/16) + r].
-template <typename T, bool PC = false>
-__device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[4], const floatx4 (&nt)[4],
-                                            floatx4 (&X)[4], floatx4 (&Xt)[4], T* Tb, int ldt,
-                                            const floatx4 (&brow)[4], int lane)
+// Diagonal blocks B0 .. B0+NB-1 (index i of the arrays is block B0 + i).
+// nd[i] = tile(N_bb), nt[i] = tile(N_bb^T).  Returns X[i] = tile(X_bb) and
+// Xt[i] = tile(X_bb^T) (fp32) and stores those diagonal blocks of
+// Tb = T diag(beta); brow[i][r] = beta[16 b + 4(l/16) + r].
+template <typename T, bool PC = false, int NB = 4, int B0 = 0>
+__device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[NB], const floatx4 (&nt)[NB],
+                                            floatx4 (&X)[NB], floatx4 (&Xt)[NB], T* Tb, int ldt,
+                                            const floatx4 (&brow)[NB], int lane)
 {
     using F = typename Frag16<T>::type;
     // an opaque copy of the lane index keeps the compiler from hoisting the
@@ -60,9 +61,9 @@ __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[4], const floatx
 
     // P = I + M with M = -N_bb, then P <- P (I + M^2), P (I + M^4), P (I + M^8);
     // the four blocks are independent chains, interleaved
-    F fM[4], fMt[4];
+    F fM[NB], fMt[NB];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < NB; ++b) {
         floatx4 M, Mt;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -76,14 +77,14 @@ __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[4], const floatx
     }
 #pragma unroll
     for (int step = 0; step < 3; ++step) {
-        floatx4 M2[4], M2t[4];
+        floatx4 M2[NB], M2t[NB];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < NB; ++b) {
             M2[b] = mma16<T>(fMt[b], fM[b], zero4());                    // M M
             if (step < 2) M2t[b] = mma16<T>(fM[b], fMt[b], zero4());     // M^T M^T
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < NB; ++b) {
             const F fM2 = frag16_acc<T>(M2[b]);
             const F fPt = frag16_acc<T>(Xt[b]);
             X[b] = mma16<T>(fPt, fM2, X[b]);                             // P + P M2
@@ -95,62 +96,89 @@ __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[4], const floatx
         }
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < NB; ++b) {
         floatx4 w = Xt[b];
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] *= brow[b][r];
-        store_tb<T, PC>(Tb, ldt, b, b, w, lane);
+        store_tb<T, PC>(Tb, ldt, B0 + b, B0 + b, w, lane);
     }
 }
 
-// Off-diagonal blocks from X, Xt (tsolve_diag) and the row fragments of the six
-// N blocks below the diagonal, n_ij = tile(N_ij^T); stores them into Tb.
+// Off-diagonal blocks of T, in two independent halves (each one wave's work):
+//   half A: T10 = -X11 N10 X00, then column block 0 of the lower-left quarter,
+//           Y0 = N20 X00 + N21 T10, Y1 = N30 X00 + N31 T10, T20 = -X22 Y0,
+//           T30 = -X33 (N32 T20 + Y1)
+//   half B: T32 = -X33 N32 X22, then column block 1,
+//           Y0 = N21 X11, Y1 = N31 X11, T21 = -X22 Y0, T31 = -X33 (N32 T21 + Y1)
+// Arguments are fp32 tiles: x_bb = tile(X_bb), xt_bb = tile(X_bb^T) and
+// n_ij = tile(N_ij^T); brow as for tsolve_diag (all four blocks).
+template <typename T, bool PC>
+__device__ __forceinline__ void tb_store_neg(T* Tb, int ldt, floatx4 ct, int rb, int qb,
+                                             const floatx4 (&brow)[4], int lane)
+{
+    // store -tile(C^T) scaled by beta of C's columns (block qb) as block (rb, qb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ct[r] = -ct[r] * brow[qb][r];
+    store_tb<T, PC>(Tb, ldt, rb, qb, ct, lane);
+}
+
+template <typename T, bool PC = false>
+__device__ __forceinline__ void tsolve_offdiag_a(floatx4 x00, floatx4 xt11, floatx4 xt22, floatx4 xt33,
+                                                 floatx4 n10, floatx4 n20, floatx4 n21, floatx4 n30,
+                                                 floatx4 n31, floatx4 n32, T* Tb, int ldt,
+                                                 const floatx4 (&brow)[4], int lane)
+{
+    using F = typename Frag16<T>::type;
+    const F fx00 = frag16_acc<T>(x00), fx11r = frag16_acc<T>(xt11);
+    const F fx22r = frag16_acc<T>(xt22), fx33r = frag16_acc<T>(xt33);
+    const F fu10 = frag16_acc<T>(mma16<T>(frag16_acc<T>(n10), fx00, zero4()));   // N10 X00
+    floatx4 t10 = mma16<T>(fx11r, fu10, zero4());                                 // -T10
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t10[r] = -t10[r];
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu10, fx11r, zero4()), 1, 0, brow, lane);
+    const F ft10 = frag16_acc<T>(t10);
+    floatx4 y0 = mma16<T>(frag16_acc<T>(n20), fx00, mma16<T>(frag16_acc<T>(n21), ft10, zero4()));
+    floatx4 y1 = mma16<T>(frag16_acc<T>(n30), fx00, mma16<T>(frag16_acc<T>(n31), ft10, zero4()));
+    const F fy0 = frag16_acc<T>(y0);
+    floatx4 t2 = mma16<T>(fx22r, fy0, zero4());                                   // -T20
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t2[r] = -t2[r];
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fy0, fx22r, zero4()), 2, 0, brow, lane);
+    const F fu = frag16_acc<T>(mma16<T>(frag16_acc<T>(n32), frag16_acc<T>(t2), y1));
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu, fx33r, zero4()), 3, 0, brow, lane);
+}
+
+template <typename T, bool PC = false>
+__device__ __forceinline__ void tsolve_offdiag_b(floatx4 x11, floatx4 x22, floatx4 xt22, floatx4 xt33,
+                                                 floatx4 n21, floatx4 n31, floatx4 n32, T* Tb, int ldt,
+                                                 const floatx4 (&brow)[4], int lane)
+{
+    using F = typename Frag16<T>::type;
+    const F fx11 = frag16_acc<T>(x11), fx22 = frag16_acc<T>(x22);
+    const F fx22r = frag16_acc<T>(xt22), fx33r = frag16_acc<T>(xt33);
+    const F fn32 = frag16_acc<T>(n32);
+    const F fu32 = frag16_acc<T>(mma16<T>(fn32, fx22, zero4()));                 // N32 X22
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu32, fx33r, zero4()), 3, 2, brow, lane);
+    const floatx4 y0 = mma16<T>(frag16_acc<T>(n21), fx11, zero4());
+    const floatx4 y1 = mma16<T>(frag16_acc<T>(n31), fx11, zero4());
+    const F fy0 = frag16_acc<T>(y0);
+    floatx4 t2 = mma16<T>(fx22r, fy0, zero4());                                   // -T21
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t2[r] = -t2[r];
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fy0, fx22r, zero4()), 2, 1, brow, lane);
+    const F fu = frag16_acc<T>(mma16<T>(fn32, frag16_acc<T>(t2), y1));
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu, fx33r, zero4()), 3, 1, brow, lane);
+}
+
+// Both halves on one wave, from X, Xt of tsolve_diag.
 template <typename T, bool PC = false>
 __device__ __forceinline__ void tsolve_offdiag(const floatx4 (&X)[4], const floatx4 (&Xt)[4],
                                                floatx4 n10, floatx4 n20, floatx4 n21, floatx4 n30,
                                                floatx4 n31, floatx4 n32, T* Tb, int ldt,
                                                const floatx4 (&brow)[4], int lane)
 {
-    using F = typename Frag16<T>::type;
-    const F fx00 = frag16_acc<T>(X[0]), fx11 = frag16_acc<T>(X[1]), fx22 = frag16_acc<T>(X[2]);
-    const F fx11r = frag16_acc<T>(Xt[1]), fx22r = frag16_acc<T>(Xt[2]), fx33r = frag16_acc<T>(Xt[3]);
-    const F fn10 = frag16_acc<T>(n10), fn20 = frag16_acc<T>(n20), fn21 = frag16_acc<T>(n21);
-    const F fn30 = frag16_acc<T>(n30), fn31 = frag16_acc<T>(n31), fn32 = frag16_acc<T>(n32);
-    // store -tile(C^T) scaled by beta of C's columns (block qb) as block (rb, qb) of Tb
-    auto store_neg = [&](floatx4 ct, int rb, int qb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ct[r] = -ct[r] * brow[qb][r];
-        store_tb<T, PC>(Tb, ldt, rb, qb, ct, lane);
-    };
-
-    // ---- level 1 ----------------------------------------------------------------
-    const F fu10 = frag16_acc<T>(mma16<T>(fn10, fx00, zero4()));     // N10 X00
-    floatx4 t10 = mma16<T>(fx11r, fu10, zero4());                     // X11 N10 X00 = -T10
-#pragma unroll
-    for (int r = 0; r < 4; ++r) t10[r] = -t10[r];
-    store_neg(mma16<T>(fu10, fx11r, zero4()), 1, 0);
-    const F fu32 = frag16_acc<T>(mma16<T>(fn32, fx22, zero4()));     // N32 X22
-    store_neg(mma16<T>(fu32, fx33r, zero4()), 3, 2);
-
-    // ---- level 2: lower-left 32x32 block, 16 columns at a time ------------------
-    const F ft10 = frag16_acc<T>(t10);
-#pragma unroll
-    for (int qc = 0; qc < 2; ++qc) {
-        const F fta1 = qc == 0 ? ft10 : fx11;                          // T_A[1][qc]
-        floatx4 y0 = mma16<T>(fn21, fta1, zero4());
-        floatx4 y1 = mma16<T>(fn31, fta1, zero4());
-        if (qc == 0) {                                                 // T_A[0][0] = X00, T_A[0][1] = 0
-            y0 = mma16<T>(fn20, fx00, y0);
-            y1 = mma16<T>(fn30, fx00, y1);
-        }
-        const F fy0 = frag16_acc<T>(y0);
-        floatx4 t2 = mma16<T>(fx22r, fy0, zero4());                    // X22 Y0 = -T2q
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t2[r] = -t2[r];
-        store_neg(mma16<T>(fy0, fx22r, zero4()), 2, qc);
-        const F fu = frag16_acc<T>(mma16<T>(fn32, frag16_acc<T>(t2), y1));   // N32 T2q + Y1
-        store_neg(mma16<T>(fu, fx33r, zero4()), 3, qc);                        // T3q = -X33 (..)
-    }
+    tsolve_offdiag_a<T, PC>(X[0], Xt[1], Xt[2], Xt[3], n10, n20, n21, n30, n31, n32, Tb, ldt, brow, lane);
+    tsolve_offdiag_b<T, PC>(X[1], X[2], Xt[2], Xt[3], n21, n31, n32, Tb, ldt, brow, lane);
 }
 
 // Both steps with every N block in registers: nd, nt as for tsolve_diag and
