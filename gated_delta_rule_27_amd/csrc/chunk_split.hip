@@ -41,7 +41,6 @@ namespace linattn {
 namespace {
 
 constexpr int kC = 64;
-constexpr float kSpanMax = 80.f;   // exp(80) ~ 5.5e34 < bf16 / fp32 max
 
 // Workspace of one chunk of one head (bf16 operands, fp32 channel factors).
 template <int DK>
@@ -58,206 +57,314 @@ struct SplitWs {
 typedef __attribute__((__vector_size__(16))) int i4;
 
 // ===========================================================================
-// Kernel A
+// Kernel A: persistent.  Workgroup w walks the chunk-heads w, w + grid, ...;
+// the next one's q, k, g and beta are loaded into registers while the current
+// one is processed.  Gates are kept in base 2 (log2 e . g) so every decay
+// factor is one hardware exp2.
+//
+// With G the per-channel prefix inside the chunk, block b = rows 16b..16b+15,
+// s(b) the row before it (G_{-1} = 0) and e(b) its last row, every row l of
+// block b gets two block-local factors per channel, both at most 1 for decays:
+//   u_l = 2^(G_l - G_s(b)),   w_l = 2^(G_e(b) - G_l)
+// and the staged operands Qu = u.q, Ku = u.k, Kw = w.k.  Then, per channel,
+//   off the diagonal (i > j):  2^(G_l - G_m) = u_l . 2^(G_s(i) - G_e(j)) . w_m
+//   on the diagonal  (i = j):  2^(G_l - G_m) = (u_l 2^(G_s - G_mid)) . (w_m 2^(G_mid - G_e))
+// so every 16x16 score tile is one matrix-core product of Kw scaled by a
+// channel vector and Qu (or Ku), scaled by a channel vector on the diagonal.
+// The diagonal factors stay within 2^(span/2) (span = the block's largest
+// per-channel decay); a block whose span exceeds kSpan2Max is computed element
+// by element instead, from the raw tokens, before they are overwritten.  The
+// decayed operands of kernel B follow from the same factors:
+//   Qd = Qu . 2^G_s(b),  Kd = Ku . 2^G_s(b),  Kr = Kw . 2^(G_63 - G_e(b)).
 // ===========================================================================
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSpan2Max = 120.f;   // 2^60 per factor, far inside bf16 / fp32 range
+
 template <int DK, int RULE, int GATE>
 __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ g,
-    const bf16* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks)
+    const bf16* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks,
+    int64_t ntasks)
 {
     using W = SplitWs<DK>;
     constexpr int NT = 512;
     constexpr bool DELTA = RULE == kRuleDelta;
-    constexpr int LDQ = DK + 8, LDG = DK + 4, LDN = kC + 4, LDC = kC + 8;
+    constexpr int LDQ = DK + 8, LDN = kC + 4, LDC = kC + 8;
+    constexpr int NK = DK / 32;                       // 16x16x32 steps over the channels
+    constexpr int NV = kC * DK / (8 * NT);            // 16-byte vectors per thread of a [C][DK] tile
+    static_assert(NV >= 1, "tile split");
 
-    __shared__ __align__(16) bf16 qs[kC * LDQ];
-    __shared__ __align__(16) bf16 ks[kC * LDQ];
-    __shared__ __align__(16) float Gf[kC * LDG];
-    __shared__ __align__(16) bf16 scr[4][3][16 * LDQ];
+    __shared__ __align__(16) bf16 qs[kC * LDQ];       // q, then Qu
+    __shared__ __align__(16) bf16 ks[kC * LDQ];       // k, then Ku
+    __shared__ __align__(16) bf16 kw[kC * LDQ];       // Kw
+    __shared__ __align__(16) bf16 gs[kC * LDQ];       // raw gate (channel gate)
+    __shared__ __align__(16) float tot[4][DK];        // block sums of the base-2 gate
+    __shared__ __align__(16) float Es[4][DK];         // 2^G_s(b)
+    __shared__ __align__(16) float Fe[4][DK];         // 2^(G_63 - G_e(b))
+    __shared__ __align__(16) float Pv[4][DK];         // 2^(G_s(b) - G_mid(b))
+    __shared__ __align__(16) float Rv[4][DK];         // 2^(G_mid(b) - G_e(b))
+    __shared__ __align__(16) float Dt[6][DK];         // 2^(G_s(i) - G_e(j)), pairs (1,0)(2,0)(2,1)(3,0)(3,1)(3,2)
     __shared__ __align__(16) float Nf[DELTA ? kC * LDN : 4];
     __shared__ __align__(16) bf16 Aq[kC * LDC];
     __shared__ __align__(16) bf16 Tb[DELTA ? kC * LDC : 8];
     __shared__ __align__(16) float bet[kC];
-    __shared__ float tot[NT / DK][DK];
+    __shared__ float gsc[kC];                         // scalar gate, base 2
+    __shared__ float spanw[8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int64_t bh = blockIdx.x / nchunks;
-    const int64_t r = blockIdx.x % nchunks;
-    const int64_t t0 = r * kC;
-    unsigned char* wc = ws + (bh * nchunks + r) * W::BYTES;
+    const int cl = lane & 15, g4 = 4 * (lane >> 4);
+    using Fr = typename Mfma<bf16>::frag;
 
-    // ---- load q, k, g (fp32), beta; zero past the end ---------------------
-#pragma unroll
-    for (int p = 0; p < kC * DK / (8 * NT); ++p) {
-        const int idx = (p * NT + tid) * 8;
-        const int row = idx / DK, col = idx % DK;
-        const bool ok = t0 + row < Tlen;
-        const int64_t off = (bh * Tlen + t0 + row) * DK + col;
-        const i4 z = {0, 0, 0, 0};
-        const i4 qv = ok ? *reinterpret_cast<const i4*>(q + off) : z;
-        const i4 kv = ok ? *reinterpret_cast<const i4*>(k + off) : z;
-        *reinterpret_cast<i4*>(&qs[row * LDQ + col]) = qv;
-        *reinterpret_cast<i4*>(&ks[row * LDQ + col]) = kv;
-        floatx4 lo, hi;
-        if constexpr (GATE == kGateChannel) {
-            const i4 gv = ok ? *reinterpret_cast<const i4*>(g + off) : z;
-            const bf16* ge = reinterpret_cast<const bf16*>(&gv);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { lo[e] = to_f32(ge[e]); hi[e] = to_f32(ge[4 + e]); }
-        } else {
-            // a scalar gate is the channel gate with every channel equal
-            const float gs = ok ? to_f32(g[bh * Tlen + t0 + row]) : 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { lo[e] = gs; hi[e] = gs; }
-        }
-        *reinterpret_cast<floatx4*>(&Gf[row * LDG + col]) = lo;
-        *reinterpret_cast<floatx4*>(&Gf[row * LDG + col + 4]) = hi;
-    }
-    if (tid < kC) bet[tid] = (DELTA && t0 + tid < Tlen) ? to_f32(beta[bh * Tlen + t0 + tid]) : 0.f;
+    // the causal blocks above the diagonal stay zero
     for (int i = tid; i < kC * LDC; i += NT) Aq[i] = from_f32<bf16>(0.f);
     if constexpr (DELTA)
         for (int i = tid; i < kC * LDC; i += NT) Tb[i] = from_f32<bf16>(0.f);
-    __syncthreads();
 
-    // ---- a1: prefix sums over the chunk, per channel -------------------------
-    {
-        constexpr int NSEG = NT / DK, SEG = kC / NSEG;
-        const int c = tid % DK, seg = tid / DK;
-        float x[SEG];
+    i4 qreg[NV], kreg[NV], greg[NV];
+    bf16 gsreg = from_f32<bf16>(0.f), breg = from_f32<bf16>(0.f);
+    auto fetch = [&](int64_t task) {
+        const int64_t bh = task / nchunks, t0 = (task % nchunks) * kC;
 #pragma unroll
-        for (int i = 0; i < SEG; ++i) x[i] = Gf[(seg * SEG + i) * LDG + c];
-#pragma unroll
-        for (int i = 1; i < SEG; ++i) x[i] += x[i - 1];
-        tot[seg][c] = x[SEG - 1];
-        __syncthreads();
-        float off = 0.f;
-        for (int s2 = 0; s2 < seg; ++s2) off += tot[s2][c];
-#pragma unroll
-        for (int i = 0; i < SEG; ++i) Gf[(seg * SEG + i) * LDG + c] = x[i] + off;
-    }
-    __syncthreads();
-
-    // ---- decayed operands straight to the workspace ---------------------------
-    {
-        bf16* Qd = reinterpret_cast<bf16*>(wc + W::QD);
-        bf16* Kd = reinterpret_cast<bf16*>(wc + W::KD);
-        bf16* KrT = reinterpret_cast<bf16*>(wc + W::KRT);
-        float* gC = reinterpret_cast<float*>(wc + W::GC);
-#pragma unroll
-        for (int p = 0; p < kC * DK / (8 * NT); ++p) {
+        for (int p = 0; p < NV; ++p) {
             const int idx = (p * NT + tid) * 8;
             const int row = idx / DK, col = idx % DK;
-            bf16x8 qo, ko;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = expf(Gf[row * LDG + col + e]);
-                qo[e] = from_f32<bf16>(to_f32(qs[row * LDQ + col + e]) * d);
-                ko[e] = from_f32<bf16>(to_f32(ks[row * LDQ + col + e]) * d);
-            }
-            *reinterpret_cast<bf16x8*>(Qd + row * DK + col) = qo;
-            if constexpr (DELTA) *reinterpret_cast<bf16x8*>(Kd + row * DK + col) = ko;
+            const int64_t tr = t0 + row < Tlen ? t0 + row : Tlen - 1;
+            const int64_t off = (bh * Tlen + tr) * DK + col;
+            qreg[p] = *reinterpret_cast<const i4*>(q + off);
+            kreg[p] = *reinterpret_cast<const i4*>(k + off);
+            if constexpr (GATE == kGateChannel) greg[p] = *reinterpret_cast<const i4*>(g + off);
         }
-#pragma unroll
-        for (int p = 0; p < kC * DK / (8 * NT); ++p) {
-            const int idx = (p * NT + tid) * 8;         // over [DK][C]
-            const int c = idx / kC, l0 = idx % kC;
-            const float Gend = Gf[(kC - 1) * LDG + c];
-            bf16x8 kr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                kr[e] = from_f32<bf16>(to_f32(ks[(l0 + e) * LDQ + c]) * expf(Gend - Gf[(l0 + e) * LDG + c]));
-            *reinterpret_cast<bf16x8*>(KrT + c * kC + l0) = kr;
+        if (tid < kC) {
+            const int64_t tr = t0 + tid < Tlen ? t0 + tid : Tlen - 1;
+            if constexpr (GATE != kGateChannel) gsreg = g[bh * Tlen + tr];
+            if constexpr (DELTA) breg = beta[bh * Tlen + tr];
         }
-        if (tid < DK) gC[tid] = expf(Gf[(kC - 1) * LDG + tid]);
-    }
+    };
+    if (blockIdx.x < ntasks) fetch(blockIdx.x);
 
-    // ---- a2: Aq and N tiles (waves 0..3) ------------------------------------------
-    if (wave < 4) {
-        bf16* Xq = scr[wave][0];
-        bf16* Xk = scr[wave][1];
-        bf16* Km = scr[wave][2];
-        for (int task = wave; task < 10; task += 4) {
-            int i, j;
-            if (task < 4) { i = task; j = task; }
-            else { const int pi[6] = {1, 2, 2, 3, 3, 3}, pj[6] = {0, 0, 1, 0, 1, 2};
-                   i = pi[task - 4]; j = pj[task - 4]; }
-            const bool diag = i == j;
-            // reference row: before the query block (off-diagonal) or its middle row
-            const int p = diag ? 16 * i + 7 : 16 * i - 1;
-            bool safe = true;
-            if (diag) {
-                float span = 0.f;
-                for (int c = lane; c < DK; c += 64) {
-                    const float gs = i > 0 ? Gf[(16 * i - 1) * LDG + c] : 0.f;
-                    span = fmaxf(span, gs - Gf[(16 * i + 15) * LDG + c]);
-                }
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off, 64));
-                safe = span <= kSpanMax;
-            }
-            if (safe) {
-                for (int e = lane; e < 16 * DK; e += 64) {
-                    const int rr = e / DK, c = e % DK;
-                    const float Gp = Gf[p * LDG + c];
-                    const float fl = expf(Gf[(16 * i + rr) * LDG + c] - Gp);
-                    const float fm = expf(Gp - Gf[(16 * j + rr) * LDG + c]);
-                    Xq[rr * LDQ + c] = from_f32<bf16>(to_f32(qs[(16 * i + rr) * LDQ + c]) * fl);
-                    if constexpr (DELTA)
-                        Xk[rr * LDQ + c] = from_f32<bf16>(to_f32(ks[(16 * i + rr) * LDQ + c]) * fl);
-                    Km[rr * LDQ + c] = from_f32<bf16>(to_f32(ks[(16 * j + rr) * LDQ + c]) * fm);
-                }
-                // D[m][l] = sum_c Km[m][c] X[l][c]; stored transposed as [l][m]
-                const floatx4 da = mma_nt_k<bf16, DK>(zero4(), Km, LDQ, Xq, LDQ, lane);
-                floatx4 dn = zero4();
-                if constexpr (DELTA) dn = mma_nt_k<bf16, DK>(zero4(), Km, LDQ, Xk, LDQ, lane);
-                const int l = 16 * i + (lane & 15);
-                const int m0 = 16 * j + 4 * (lane >> 4);
-                floatx4 va, vn;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int m = m0 + rr;
-                    va[rr] = (m <= l) ? da[rr] : 0.f;
-                    vn[rr] = (m < l) ? bet[l] * dn[rr] : 0.f;
-                }
-                store_tile_t(&Aq[16 * i * LDC + 16 * j], LDC, va, lane);
-                if constexpr (DELTA) store_tile_t(&Nf[16 * i * LDN + 16 * j], LDN, vn, lane);
-            } else {
-                // exact element-wise fallback for a diagonal block with extreme decay
-                for (int e = lane; e < 256; e += 64) {
-                    const int l = 16 * i + e / 16, m = 16 * i + e % 16;
-                    float a = 0.f, n = 0.f;
-                    if (m <= l) {
-                        for (int c = 0; c < DK; ++c) {
-                            const float d = expf(Gf[l * LDG + c] - Gf[m * LDG + c]);
-                            const float km = to_f32(ks[m * LDQ + c]) * d;
-                            a = fmaf(to_f32(qs[l * LDQ + c]), km, a);
-                            n = fmaf(to_f32(ks[l * LDQ + c]), km, n);
-                        }
-                    }
-                    Aq[l * LDC + m] = from_f32<bf16>(a);
-                    if constexpr (DELTA) Nf[l * LDN + m] = (m < l) ? bet[l] * n : 0.f;
-                }
-            }
-        }
-    }
-    __syncthreads();
+    for (int64_t task = blockIdx.x; task < ntasks; task += gridDim.x) {
+        const int64_t bh = task / nchunks, r = task % nchunks, t0 = r * kC;
+        unsigned char* wc = ws + task * W::BYTES;     // task = bh * nchunks + r
 
-    // ---- a3/a4: triangular transform (wave 0) -----------------------------------
-    if constexpr (DELTA) {
-        if (wave == 0) tsolve64_wave<bf16>(Nf, LDN, Tb, LDC, bet, lane);
+        // ---- stage the chunk; issue the next chunk-head's loads ---------------------
         __syncthreads();
-    }
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = (p * NT + tid) * 8;
+            const int row = idx / DK, col = idx % DK;
+            const bool ok = t0 + row < Tlen;
+            const i4 z = {0, 0, 0, 0};
+            *reinterpret_cast<i4*>(&qs[row * LDQ + col]) = ok ? qreg[p] : z;
+            *reinterpret_cast<i4*>(&ks[row * LDQ + col]) = ok ? kreg[p] : z;
+            if constexpr (GATE == kGateChannel) *reinterpret_cast<i4*>(&gs[row * LDQ + col]) = ok ? greg[p] : z;
+        }
+        if (tid < kC) {
+            // a scalar gate is the channel gate with every channel equal
+            if constexpr (GATE != kGateChannel) gsc[tid] = (t0 + tid < Tlen) ? to_f32(gsreg) * kLog2e : 0.f;
+            bet[tid] = (DELTA && t0 + tid < Tlen) ? to_f32(breg) : 0.f;
+        }
+        if (task + gridDim.x < ntasks) fetch(task + gridDim.x);
+        __syncthreads();
 
-    // ---- Aq and Tb to the workspace --------------------------------------------------
-    {
-        bf16* Aqw = reinterpret_cast<bf16*>(wc + W::AQ);
-        bf16* Tbw = reinterpret_cast<bf16*>(wc + W::TB);
-        const int row = tid / (kC / 8), col = (tid % (kC / 8)) * 8;
-        *reinterpret_cast<i4*>(Aqw + row * kC + col) = *reinterpret_cast<const i4*>(&Aq[row * LDC + col]);
-        if constexpr (DELTA)
-            *reinterpret_cast<i4*>(Tbw + row * kC + col) = *reinterpret_cast<const i4*>(&Tb[row * LDC + col]);
+        // ---- a1: per-channel prefix, block factors, tables ------------------------------
+        // thread (c, b): channel c, block b (the first 4 DK threads)
+        float Gl[16];
+        const int pc = tid % DK, pb = tid / DK;
+        const bool pre = tid < 4 * DK;
+        if (pre) {
+            float acc = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float gv;
+                if constexpr (GATE == kGateChannel) gv = to_f32(gs[(16 * pb + rr) * LDQ + pc]) * kLog2e;
+                else gv = gsc[16 * pb + rr];
+                acc += gv;
+                Gl[rr] = acc;                          // G_l - G_s(b)
+            }
+            tot[pb][pc] = acc;
+        }
+        __syncthreads();
+        float span = 0.f;
+        if (pre) {
+            float off = 0.f, all = 0.f, ends[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                all += tot[b][pc];
+                ends[b] = all;                         // G_e(b)
+                if (b < pb) off += tot[b][pc];
+            }
+            const float Gst = off;
+            Es[pb][pc] = fast_exp2(Gst);
+            Fe[pb][pc] = fast_exp2(all - ends[pb]);
+            Pv[pb][pc] = fast_exp2(-Gl[7]);
+            Rv[pb][pc] = fast_exp2(Gl[7] - Gl[15]);
+            // pair (pb, j) for j < pb: slot pb (pb - 1) / 2 + j
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                if (j < pb) Dt[pb * (pb - 1) / 2 + j][pc] = fast_exp2(Gst - ends[j]);
+            if (pb == 0) reinterpret_cast<float*>(wc + W::GC)[pc] = fast_exp2(all);
+            span = -Gl[15];
+        }
+        // largest decay span of each diagonal block (waves of one block combine)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, shfl_xor(span, off));
+        if (lane == 0) spanw[wave] = span;
+        __syncthreads();
+        constexpr int WPB = DK / 64;                   // waves per block in the prefix mapping
+        bool safe[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float sp = spanw[b * WPB];
+            if constexpr (WPB == 2) sp = fmaxf(sp, spanw[b * WPB + 1]);
+            safe[b] = sp <= kSpan2Max;
+        }
+
+        // ---- exact element-wise diagonal blocks where the span is too large ----------
+        // (raw q, k and g still in LDS; wave b takes block b)
+        if (wave < 4 && !safe[wave]) {
+            const int b = wave;
+            for (int e = lane; e < 256; e += 64) {
+                const int l = 16 * b + e / 16, m = 16 * b + e % 16;
+                float a = 0.f, n = 0.f;
+                if (m <= l) {
+                    for (int c = 0; c < DK; ++c) {
+                        float dG = 0.f;                // G_l - G_m, base 2
+                        for (int s2 = m + 1; s2 <= l; ++s2) {
+                            if constexpr (GATE == kGateChannel) dG += to_f32(gs[s2 * LDQ + c]) * kLog2e;
+                            else dG += gsc[s2];
+                        }
+                        const float km = to_f32(ks[m * LDQ + c]) * fast_exp2(dG);
+                        a = fmaf(to_f32(qs[l * LDQ + c]), km, a);
+                        n = fmaf(to_f32(ks[l * LDQ + c]), km, n);
+                    }
+                }
+                Aq[l * LDC + m] = from_f32<bf16>(a);
+                if constexpr (DELTA) Nf[l * LDN + m] = (m < l) ? bet[l] * n : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- staged operands Qu, Ku, Kw ---------------------------------------------
+        if (pre) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 16 * pb + rr;
+                const float u = fast_exp2(Gl[rr]), w = fast_exp2(Gl[15] - Gl[rr]);
+                const float qv = to_f32(qs[row * LDQ + pc]), kv = to_f32(ks[row * LDQ + pc]);
+                qs[row * LDQ + pc] = from_f32<bf16>(qv * u);
+                ks[row * LDQ + pc] = from_f32<bf16>(kv * u);
+                kw[row * LDQ + pc] = from_f32<bf16>(kv * w);
+            }
+        }
+        __syncthreads();
+
+        // ---- a2: score and N tiles (10 causal pairs over the 8 waves) ------------------
+        for (int p = wave; p < 10; p += 8) {
+            // p < 4: diagonal block p; else pair slot p - 4 of (1,0)(2,0)(2,1)(3,0)(3,1)(3,2)
+            const int qn = p - 4;
+            const int i = p < 4 ? p : (qn < 1 ? 1 : (qn < 3 ? 2 : 3));
+            const int j = p < 4 ? p : qn - i * (i - 1) / 2;
+            const bool diag = i == j;
+            if (diag && !safe[i]) continue;
+            const float* dk_ = diag ? Rv[j] : Dt[p - 4];   // channel scale of the key side
+            floatx4 xa = zero4(), xn = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int c0 = 32 * kk + 8 * (lane >> 4);
+                // key side: Kw rows of block j, scaled per channel
+                const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&kw[(16 * j + cl) * LDQ + c0]);
+                const floatx4 s0 = *reinterpret_cast<const floatx4*>(&dk_[c0]);
+                const floatx4 s1 = *reinterpret_cast<const floatx4*>(&dk_[c0 + 4]);
+                bf16x8 ka;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ka[e] = from_f32<bf16>(to_f32(kv[e]) * s0[e]);
+                    ka[4 + e] = from_f32<bf16>(to_f32(kv[4 + e]) * s1[e]);
+                }
+                // query side: Qu (and Ku) rows of block i, scaled on the diagonal
+                bf16x8 qb = *reinterpret_cast<const bf16x8*>(&qs[(16 * i + cl) * LDQ + c0]);
+                bf16x8 kb = *reinterpret_cast<const bf16x8*>(&ks[(16 * i + cl) * LDQ + c0]);
+                if (diag) {
+                    const floatx4 p0 = *reinterpret_cast<const floatx4*>(&Pv[i][c0]);
+                    const floatx4 p1 = *reinterpret_cast<const floatx4*>(&Pv[i][c0 + 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qb[e] = from_f32<bf16>(to_f32(qb[e]) * p0[e]);
+                        qb[4 + e] = from_f32<bf16>(to_f32(qb[4 + e]) * p1[e]);
+                        kb[e] = from_f32<bf16>(to_f32(kb[e]) * p0[e]);
+                        kb[4 + e] = from_f32<bf16>(to_f32(kb[4 + e]) * p1[e]);
+                    }
+                }
+                xa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb, xa, 0, 0, 0);
+                if constexpr (DELTA) xn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, kb, xn, 0, 0, 0);
+            }
+            // D[m][l]: m = 16 j + g4 + rr (key), l = 16 i + cl (query); stored as [l][m]
+            const int l = 16 * i + cl;
+            floatx4 va, vn;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int m = 16 * j + g4 + rr;
+                va[rr] = (m <= l) ? xa[rr] : 0.f;
+                vn[rr] = (m < l) ? bet[l] * xn[rr] : 0.f;
+            }
+            store_tile_t(&Aq[16 * i * LDC + 16 * j], LDC, va, lane);
+            if constexpr (DELTA) store_tile_t(&Nf[16 * i * LDN + 16 * j], LDN, vn, lane);
+        }
+
+        // ---- decayed operands of kernel B straight to the workspace ------------------
+        {
+            bf16* Qd = reinterpret_cast<bf16*>(wc + W::QD);
+            bf16* Kd = reinterpret_cast<bf16*>(wc + W::KD);
+            bf16* KrT = reinterpret_cast<bf16*>(wc + W::KRT);
+#pragma unroll
+            for (int p = 0; p < NV; ++p) {
+                const int idx = (p * NT + tid) * 8;
+                const int row = idx / DK, col = idx % DK, b = row / 16;
+                const bf16x8 qu = *reinterpret_cast<const bf16x8*>(&qs[row * LDQ + col]);
+                const bf16x8 ku = *reinterpret_cast<const bf16x8*>(&ks[row * LDQ + col]);
+                const floatx4 e0 = *reinterpret_cast<const floatx4*>(&Es[b][col]);
+                const floatx4 e1 = *reinterpret_cast<const floatx4*>(&Es[b][col + 4]);
+                bf16x8 qo, ko;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qo[e] = from_f32<bf16>(to_f32(qu[e]) * e0[e]);
+                    qo[4 + e] = from_f32<bf16>(to_f32(qu[4 + e]) * e1[e]);
+                    ko[e] = from_f32<bf16>(to_f32(ku[e]) * e0[e]);
+                    ko[4 + e] = from_f32<bf16>(to_f32(ku[4 + e]) * e1[e]);
+                }
+                *reinterpret_cast<bf16x8*>(Qd + row * DK + col) = qo;
+                if constexpr (DELTA) *reinterpret_cast<bf16x8*>(Kd + row * DK + col) = ko;
+            }
+#pragma unroll
+            for (int p = 0; p < NV; ++p) {
+                const int idx = (p * NT + tid) * 8;         // over [DK][C]
+                const int c = idx / kC, l0 = idx % kC;
+                const float f = Fe[l0 / 16][c];
+                bf16x8 kr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kr[e] = from_f32<bf16>(to_f32(kw[(l0 + e) * LDQ + c]) * f);
+                *reinterpret_cast<bf16x8*>(KrT + c * kC + l0) = kr;
+            }
+        }
+        __syncthreads();
+
+        // ---- a3/a4: triangular transform (wave 0) -----------------------------------
+        if constexpr (DELTA) {
+            if (wave == 0) tsolve64_wave<bf16>(Nf, LDN, Tb, LDC, bet, lane);
+            __syncthreads();
+        }
+
+        // ---- Aq and Tb to the workspace ------------------------------------------------
+        {
+            bf16* Aqw = reinterpret_cast<bf16*>(wc + W::AQ);
+            bf16* Tbw = reinterpret_cast<bf16*>(wc + W::TB);
+            const int row = tid / (kC / 8), col = (tid % (kC / 8)) * 8;
+            *reinterpret_cast<i4*>(Aqw + row * kC + col) = *reinterpret_cast<const i4*>(&Aq[row * LDC + col]);
+            if constexpr (DELTA)
+                *reinterpret_cast<i4*>(Tbw + row * kC + col) = *reinterpret_cast<const i4*>(&Tb[row * LDC + col]);
+        }
     }
 }
 
@@ -446,10 +553,17 @@ hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
     const int64_t bh = p.B * p.H;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)),
-                           dim3(512), 0, s, static_cast<const bf16*>(p.q),
-                           static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.g),
-                           static_cast<const bf16*>(p.beta), ws, p.T, nchunks);
+        // persistent: one workgroup per CU (its LDS use allows no second one)
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+            ncu = 256;
+        const int64_t ntasks = bh * nchunks;
+        const int64_t grid = ntasks < ncu ? ntasks : ncu;
+        hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE>), dim3((unsigned)grid), dim3(512), 0, s,
+                           static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
+                           static_cast<const bf16*>(p.g), static_cast<const bf16*>(p.beta), ws, p.T,
+                           nchunks, ntasks);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
