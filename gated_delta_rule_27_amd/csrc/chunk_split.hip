@@ -313,7 +313,9 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
             if constexpr (DELTA) store_tile_t(&Nf[16 * i * LDN + 16 * j], LDN, vn, lane);
         }
 
-        // ---- decayed operands of kernel B straight to the workspace ------------------
+        // ---- decayed operands of kernel B to the workspace -----------------------------
+        // Columns go in pcol order (mfma.h): the 8 values stored at position P are
+        // the logical columns c0..c0+3 and c0+16..c0+19, c0 = pcol_first(P).
         {
             bf16* Qd = reinterpret_cast<bf16*>(wc + W::QD);
             bf16* Kd = reinterpret_cast<bf16*>(wc + W::KD);
@@ -321,31 +323,38 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 #pragma unroll
             for (int p = 0; p < NV; ++p) {
                 const int idx = (p * NT + tid) * 8;
-                const int row = idx / DK, col = idx % DK, b = row / 16;
-                const bf16x8 qu = *reinterpret_cast<const bf16x8*>(&qs[row * LDQ + col]);
-                const bf16x8 ku = *reinterpret_cast<const bf16x8*>(&ks[row * LDQ + col]);
-                const floatx4 e0 = *reinterpret_cast<const floatx4*>(&Es[b][col]);
-                const floatx4 e1 = *reinterpret_cast<const floatx4*>(&Es[b][col + 4]);
+                const int row = idx / DK, P = idx % DK, b = row / 16;
+                const int c0 = pcol_first(P), c1 = c0 + 16;
+                const bf16x4 qa = *reinterpret_cast<const bf16x4*>(&qs[row * LDQ + c0]);
+                const bf16x4 qb = *reinterpret_cast<const bf16x4*>(&qs[row * LDQ + c1]);
+                const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&ks[row * LDQ + c0]);
+                const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&ks[row * LDQ + c1]);
+                const floatx4 e0 = *reinterpret_cast<const floatx4*>(&Es[b][c0]);
+                const floatx4 e1 = *reinterpret_cast<const floatx4*>(&Es[b][c1]);
                 bf16x8 qo, ko;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    qo[e] = from_f32<bf16>(to_f32(qu[e]) * e0[e]);
-                    qo[4 + e] = from_f32<bf16>(to_f32(qu[4 + e]) * e1[e]);
-                    ko[e] = from_f32<bf16>(to_f32(ku[e]) * e0[e]);
-                    ko[4 + e] = from_f32<bf16>(to_f32(ku[4 + e]) * e1[e]);
+                    qo[e] = from_f32<bf16>(to_f32(qa[e]) * e0[e]);
+                    qo[4 + e] = from_f32<bf16>(to_f32(qb[e]) * e1[e]);
+                    ko[e] = from_f32<bf16>(to_f32(ka[e]) * e0[e]);
+                    ko[4 + e] = from_f32<bf16>(to_f32(kb[e]) * e1[e]);
                 }
-                *reinterpret_cast<bf16x8*>(Qd + row * DK + col) = qo;
-                if constexpr (DELTA) *reinterpret_cast<bf16x8*>(Kd + row * DK + col) = ko;
+                *reinterpret_cast<bf16x8*>(Qd + row * DK + P) = qo;
+                if constexpr (DELTA) *reinterpret_cast<bf16x8*>(Kd + row * DK + P) = ko;
             }
 #pragma unroll
             for (int p = 0; p < NV; ++p) {
                 const int idx = (p * NT + tid) * 8;         // over [DK][C]
-                const int c = idx / kC, l0 = idx % kC;
-                const float f = Fe[l0 / 16][c];
+                const int c = idx / kC, P = idx % kC;
+                const int l0 = pcol_first(P), l1 = l0 + 16;
+                const float f0 = Fe[l0 / 16][c], f1 = Fe[l1 / 16][c];
                 bf16x8 kr;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kr[e] = from_f32<bf16>(to_f32(kw[(l0 + e) * LDQ + c]) * f);
-                *reinterpret_cast<bf16x8*>(KrT + c * kC + l0) = kr;
+                for (int e = 0; e < 4; ++e) {
+                    kr[e] = from_f32<bf16>(to_f32(kw[(l0 + e) * LDQ + c]) * f0);
+                    kr[4 + e] = from_f32<bf16>(to_f32(kw[(l1 + e) * LDQ + c]) * f1);
+                }
+                *reinterpret_cast<bf16x8*>(KrT + c * kC + P) = kr;
             }
         }
         __syncthreads();
@@ -356,37 +365,57 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
             __syncthreads();
         }
 
-        // ---- Aq and Tb to the workspace ------------------------------------------------
+        // ---- Aq and Tb to the workspace, columns in pcol order -----------------------------
         {
             bf16* Aqw = reinterpret_cast<bf16*>(wc + W::AQ);
             bf16* Tbw = reinterpret_cast<bf16*>(wc + W::TB);
-            const int row = tid / (kC / 8), col = (tid % (kC / 8)) * 8;
-            *reinterpret_cast<i4*>(Aqw + row * kC + col) = *reinterpret_cast<const i4*>(&Aq[row * LDC + col]);
+            const int row = tid / (kC / 8), P = (tid % (kC / 8)) * 8;
+            const int c0 = pcol_first(P), c1 = c0 + 16;
+            *reinterpret_cast<bf16x8*>(Aqw + row * kC + P) =
+                __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(&Aq[row * LDC + c0]),
+                                        *reinterpret_cast<const bf16x4*>(&Aq[row * LDC + c1]), 0, 1, 2, 3, 4, 5, 6, 7);
             if constexpr (DELTA)
-                *reinterpret_cast<i4*>(Tbw + row * kC + col) = *reinterpret_cast<const i4*>(&Tb[row * LDC + col]);
+                *reinterpret_cast<bf16x8*>(Tbw + row * kC + P) =
+                    __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(&Tb[row * LDC + c0]),
+                                            *reinterpret_cast<const bf16x4*>(&Tb[row * LDC + c1]), 0, 1, 2, 3, 4, 5, 6, 7);
         }
     }
 }
 
 // ===========================================================================
-// Kernel B: state pass + output.  Wave w owns value columns 16w..16w+15 of the
-// workgroup's 64-column block and keeps S[:, those columns] as dk/16 result
-// tiles; every product takes S, R or Z straight from registers (see mfma.h,
-// K = 16 products), so LDS only supplies the per-chunk operand tiles.
+// Kernel B: state pass + output.  One workgroup per (b, h, 64 value columns),
+// chunks in order, 8 waves:
+//   * state waves 0..3: wave w owns value columns 16w..16w+15 and keeps
+//     S[:, those columns] (fp32) as dk/16 MFMA result tiles; every product
+//     takes S, R or Z straight from registers (mfma.h), paired into K = 32
+//     products whose LDS operands are single 16-byte reads (pcol order, as
+//     kernel A stores them).
+//   * helper waves 4..7 move everything between HBM and LDS: the chunk's
+//     staged operands, loaded into registers one chunk ahead, and the output.
+//     The state waves touch no global memory inside the loop.
+// Two LDS barriers per chunk split it into
+//   phase 1: R = V - Kd S_r, Z = Tb R (delta; add rule: Z = V), O^T = S_r^T Qd^T
+//            (needs Kd, V, Tb, Qd: group 1);  helpers stage group 2 of this
+//            chunk and copy the previous chunk's output to HBM
+//   phase 2: O^T += Z^T Aq^T (to LDS), S_{r+1} = Diag(gC) S_r + Kr^T Z
+//            (needs Aq, Kr^T, gC: group 2);  helpers stage group 1 of the next
+//            chunk
+// so each LDS region is refilled while the other phase runs.
 // ===========================================================================
 template <int DK, int RULE>
-__global__ __launch_bounds__(256, 1) void chunk_chain_kernel(
+__global__ __launch_bounds__(512, 1) void chunk_chain_kernel(
     const bf16* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0,
     bf16* __restrict__ o, float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks)
 {
     using W = SplitWs<DK>;
-    constexpr int NT = 256, DVB = 64, ND = DK / 16, NL = kC / 16;
+    constexpr int NH = 256, DVB = 64, ND = DK / 16, NL = kC / 16;
     constexpr bool DELTA = RULE == kRuleDelta;
     constexpr int LDQ = DK + 8, LDC = kC + 8, LDV = DVB + 8;
-    constexpr int VQ = kC * DK / (8 * NT);       // 16-byte vectors per thread, [C][DK] tile
-    constexpr int VA = kC * kC / (8 * NT);       // [C][C] tile
-    constexpr int VV = kC * DVB / (8 * NT);      // V block
-    static_assert(VQ >= 1 && VA >= 1 && VV >= 1, "tile split");
+    constexpr int VQ = kC * DK / (8 * NH);       // 16-byte vectors per helper thread, [C][DK] tile
+    constexpr int VA = kC * kC / (8 * NH);       // [C][C] tile
+    constexpr int VV = kC * DVB / (8 * NH);      // V block
+    constexpr int VK = DK * kC / (8 * NH);       // Kr^T [DK][C]
+    static_assert(VQ >= 1 && VA >= 1 && VV >= 1 && VK >= 1, "tile split");
 
     __shared__ __align__(16) bf16 Qd[kC * LDQ];
     __shared__ __align__(16) bf16 Kd[DELTA ? kC * LDQ : 8];
@@ -394,6 +423,7 @@ __global__ __launch_bounds__(256, 1) void chunk_chain_kernel(
     __shared__ __align__(16) bf16 Aq[kC * LDC];
     __shared__ __align__(16) bf16 Tb[DELTA ? kC * LDC : 8];
     __shared__ __align__(16) bf16 Vs[kC * LDV];
+    __shared__ __align__(16) bf16 Os[kC * LDV];
     __shared__ __align__(16) float gC[DK];
 
     const int tid = threadIdx.x;
@@ -404,145 +434,207 @@ __global__ __launch_bounds__(256, 1) void chunk_chain_kernel(
     if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
     const int64_t bh = blk / nvb;
     const int vb = blk % nvb;
-    const int n0 = vb * DVB + 16 * wave;          // first value column of this wave
-    const int cl = lane & 15, g4 = 4 * (lane >> 4);
 
-    // S[16 db + g4 + rr][n0 + cl]
-    floatx4 S[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
-    wait_vmem_all();
-
-    i4 rq[VQ], rk[VQ], rkr[VQ], ra[VA], rt[VA], rv[VV];
-    i4 rg = {0, 0, 0, 0};
-    auto fetch = [&](int64_t c) {
-        const unsigned char* wc = ws + (bh * nchunks + c) * W::BYTES;
-#pragma unroll
-        for (int p = 0; p < VQ; ++p) {
-            const int e = (p * NT + tid) * 8;
-            rq[p] = *reinterpret_cast<const i4*>(wc + W::QD + 2 * e);
-            if constexpr (DELTA) rk[p] = *reinterpret_cast<const i4*>(wc + W::KD + 2 * e);
-            rkr[p] = *reinterpret_cast<const i4*>(wc + W::KRT + 2 * e);
-        }
-#pragma unroll
-        for (int p = 0; p < VA; ++p) {
-            const int e = (p * NT + tid) * 8;
-            ra[p] = *reinterpret_cast<const i4*>(wc + W::AQ + 2 * e);
-            if constexpr (DELTA) rt[p] = *reinterpret_cast<const i4*>(wc + W::TB + 2 * e);
-        }
-#pragma unroll
-        for (int p = 0; p < VV; ++p) {
-            const int e = (p * NT + tid) * 8;
-            const int row = e / DVB, col = e % DVB;
-            const int64_t tr = c * kC + row < Tlen ? c * kC + row : Tlen - 1;
-            rv[p] = *reinterpret_cast<const i4*>(v + (bh * Tlen + tr) * DV + vb * DVB + col);
-        }
-        if (tid < DK / 4) rg = *reinterpret_cast<const i4*>(wc + W::GC + 16 * tid);
-    };
-    if (nchunks > 0) fetch(0);
-
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * kC;
-        lds_barrier();
-#pragma unroll
-        for (int p = 0; p < VQ; ++p) {
-            const int e = (p * NT + tid) * 8;
-            const int row = e / DK, col = e % DK;
-            *reinterpret_cast<i4*>(&Qd[row * LDQ + col]) = rq[p];
-            if constexpr (DELTA) *reinterpret_cast<i4*>(&Kd[row * LDQ + col]) = rk[p];
-            const int rt_ = e / kC, ct = e % kC;
-            *reinterpret_cast<i4*>(&KrT[rt_ * LDC + ct]) = rkr[p];
-        }
-#pragma unroll
-        for (int p = 0; p < VA; ++p) {
-            const int e = (p * NT + tid) * 8;
-            const int row = e / kC, col = e % kC;
-            *reinterpret_cast<i4*>(&Aq[row * LDC + col]) = ra[p];
-            if constexpr (DELTA) *reinterpret_cast<i4*>(&Tb[row * LDC + col]) = rt[p];
-        }
-#pragma unroll
-        for (int p = 0; p < VV; ++p) {
-            const int e = (p * NT + tid) * 8;
-            const int row = e / DVB, col = e % DVB;
-            const i4 z = {0, 0, 0, 0};
-            *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = (t0 + row < Tlen) ? rv[p] : z;
-        }
-        if (tid < DK / 4) *reinterpret_cast<i4*>(&gC[4 * tid]) = rg;
-        if (c + 1 < nchunks) fetch(c + 1);
-        lds_barrier();
-
-        // ---- b1: Z = Tb (V - Kd S_r)  (add rule: Z = V) ----------------------
-        floatx4 Z[NL];
-#pragma unroll
-        for (int li = 0; li < NL; ++li) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) Z[li][rr] = to_f32(Vs[(16 * li + g4 + rr) * LDV + 16 * wave + cl]);
-        }
-        if constexpr (DELTA) {
-            floatx4 R[NL];
-#pragma unroll
-            for (int li = 0; li < NL; ++li) {
-                floatx4 acc = zero4();
-#pragma unroll
-                for (int db = 0; db < ND; ++db)
-                    acc = mma16<bf16>(frag16_lds(&Kd[16 * li * LDQ + 16 * db], LDQ, lane),
-                                      frag16_acc<bf16>(S[db]), acc);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) R[li][rr] = Z[li][rr] - acc[rr];
-            }
-#pragma unroll
-            for (int li = 0; li < NL; ++li) {
-                floatx4 acc = zero4();
-#pragma unroll
-                for (int mj = 0; mj <= li; ++mj)
-                    acc = mma16<bf16>(frag16_lds(&Tb[16 * li * LDC + 16 * mj], LDC, lane),
-                                      frag16_acc<bf16>(R[mj]), acc);
-                Z[li] = acc;
-            }
-        }
-        // ---- c1: O^T = S_r^T Qd^T + Z^T Aq^T, straight to HBM ----------------------
-#pragma unroll
-        for (int lj = 0; lj < NL; ++lj) {
-            floatx4 acc = zero4();
+    if (wave < 4) {
+        // ======== state waves ============================================================
+        const int n0 = 16 * wave;                 // first column of this wave in the block
+        floatx4 S[ND];
+        {
+            const int cl = lane & 15, g4 = 4 * (lane >> 4);
 #pragma unroll
             for (int db = 0; db < ND; ++db)
-                acc = mma16<bf16>(frag16_acc<bf16>(S[db]), frag16_lds(&Qd[16 * lj * LDQ + 16 * db], LDQ, lane),
-                                  acc);
 #pragma unroll
-            for (int mj = 0; mj <= lj; ++mj)
-                acc = mma16<bf16>(frag16_acc<bf16>(Z[mj]), frag16_lds(&Aq[16 * lj * LDC + 16 * mj], LDC, lane),
-                                  acc);
-            const int64_t l = t0 + 16 * lj + cl;
-            if (l < Tlen) {
-                bf16x4 w;
+                for (int rr = 0; rr < 4; ++rr)
+                    S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + vb * DVB + n0 + cl] : 0.f;
+        }
+        wait_vmem_all();
+        __syncthreads();                          // group 1 of chunk 0 staged
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int ln = opaque(lane);
+            const int cl = ln & 15, g4 = 4 * (ln >> 4);
+            // ---- phase 1: R = V - Kd S_r ; Z = Tb R ; O^T = S_r^T Qd^T ----------------
+            floatx4 R[NL], Z[NL], Ot[NL];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) w[rr] = from_f32<bf16>(acc[rr]);
-                *reinterpret_cast<bf16x4*>(o + (bh * Tlen + l) * DV + n0 + g4) = w;
+            for (int li = 0; li < NL; ++li)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) R[li][rr] = to_f32(Vs[(16 * li + g4 + rr) * LDV + n0 + cl]);
+            if constexpr (DELTA) {
+                floatx4 P[NL];
+#pragma unroll
+                for (int li = 0; li < NL; ++li) P[li] = zero4();
+#pragma unroll
+                for (int db = 0; db < ND; db += 2) {
+                    const auto sp = pair_regs<bf16>(S[db], S[db + 1]);
+#pragma unroll
+                    for (int li = 0; li < NL; ++li)
+                        P[li] = mma_pair<bf16>(pair_lds(&Kd[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
+                }
+#pragma unroll
+                for (int li = 0; li < NL; ++li)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) R[li][rr] -= P[li][rr];
+                // Z[li] = sum_{mj <= li} Tb(li, mj) R[mj]; block rows 0 and 2 take the
+                // zero causal block as a partner (one MFMA shape per chain)
+                const auto r01 = pair_regs<bf16>(R[0], R[1]), r23 = pair_regs<bf16>(R[2], R[3]);
+#pragma unroll
+                for (int li = 0; li < NL; ++li) {
+                    Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
+                    if (li >= 2) Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                }
+            } else {
+#pragma unroll
+                for (int li = 0; li < NL; ++li) Z[li] = R[li];
             }
+#pragma unroll
+            for (int li = 0; li < NL; ++li) Ot[li] = zero4();
+#pragma unroll
+            for (int db = 0; db < ND; db += 2) {
+                const auto sp = pair_regs<bf16>(S[db], S[db + 1]);
+#pragma unroll
+                for (int li = 0; li < NL; ++li)
+                    Ot[li] = mma_pair<bf16>(sp, pair_lds(&Qd[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
+            }
+            lds_barrier();
+            // ---- phase 2: O^T += Z^T Aq^T ; S_{r+1} = Diag(gC) S_r + Kr^T Z ------------
+            const auto z01 = pair_regs<bf16>(Z[0], Z[1]), z23 = pair_regs<bf16>(Z[2], Z[3]);
+#pragma unroll
+            for (int lj = 0; lj < NL; ++lj) {
+                Ot[lj] = mma_pair<bf16>(z01, pair_lds(&Aq[16 * lj * LDC], LDC, ln), Ot[lj]);
+                if (lj >= 2) Ot[lj] = mma_pair<bf16>(z23, pair_lds(&Aq[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
+            }
+#pragma unroll
+            for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                const floatx4 gd = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gd[rr];
+                S[db] = mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC + 32], LDC, ln), z23,
+                                       mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC], LDC, ln), z01, S[db]));
+            }
+            lds_barrier();
         }
-        // ---- b1: S_{r+1} = Diag(gC) S_r + Kr^T Z ----------------------------------
+        if (s_final) {
+            const int cl = lane & 15, g4 = 4 * (lane >> 4);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            floatx4 acc = S[db];
+            for (int db = 0; db < ND; ++db)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] *= gC[16 * db + g4 + rr];
-#pragma unroll
-            for (int lj = 0; lj < NL; ++lj)
-                acc = mma16<bf16>(frag16_lds(&KrT[16 * db * LDC + 16 * lj], LDC, lane),
-                                  frag16_acc<bf16>(Z[lj]), acc);
-            S[db] = acc;
+                for (int rr = 0; rr < 4; ++rr)
+                    s_final[(bh * DK + 16 * db + g4 + rr) * DV + vb * DVB + n0 + cl] = S[db][rr];
         }
-    }
-
-    if (s_final) {
+        __syncthreads();                          // the last output is in Os
+    } else {
+        // ======== helper waves =============================================================
+        const int ht = tid - 256;
+        // group 1: Kd, Qd, V, Tb ; group 2: Aq, Kr^T, gC
+        i4 rkd[VQ], rqd[VQ], rv[VV], rtb[VA];
+        i4 raq[VA], rkr[VK], rg = {0, 0, 0, 0};
+        auto load1 = [&](int64_t c) {
+            const unsigned char* wc = ws + (bh * nchunks + c) * W::BYTES;
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
+            for (int p = 0; p < VQ; ++p) {
+                const int e = (p * NH + ht) * 8;
+                rqd[p] = *reinterpret_cast<const i4*>(wc + W::QD + 2 * e);
+                if constexpr (DELTA) rkd[p] = *reinterpret_cast<const i4*>(wc + W::KD + 2 * e);
+            }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                s_final[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] = S[db][rr];
+            for (int p = 0; p < VA; ++p) {
+                const int e = (p * NH + ht) * 8;
+                if constexpr (DELTA) rtb[p] = *reinterpret_cast<const i4*>(wc + W::TB + 2 * e);
+            }
+#pragma unroll
+            for (int p = 0; p < VV; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / DVB, col = e % DVB;
+                const int64_t tr = c * kC + row < Tlen ? c * kC + row : Tlen - 1;
+                rv[p] = *reinterpret_cast<const i4*>(v + (bh * Tlen + tr) * DV + vb * DVB + col);
+            }
+        };
+        auto stage1 = [&](int64_t c) {
+#pragma unroll
+            for (int p = 0; p < VQ; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / DK, col = e % DK;
+                *reinterpret_cast<i4*>(&Qd[row * LDQ + col]) = rqd[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(&Kd[row * LDQ + col]) = rkd[p];
+            }
+#pragma unroll
+            for (int p = 0; p < VA; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / kC, col = e % kC;
+                if constexpr (DELTA) *reinterpret_cast<i4*>(&Tb[row * LDC + col]) = rtb[p];
+            }
+#pragma unroll
+            for (int p = 0; p < VV; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / DVB, col = e % DVB;
+                const i4 z = {0, 0, 0, 0};
+                *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = (c * kC + row < Tlen) ? rv[p] : z;
+            }
+        };
+        auto load2 = [&](int64_t c) {
+            const unsigned char* wc = ws + (bh * nchunks + c) * W::BYTES;
+#pragma unroll
+            for (int p = 0; p < VA; ++p) {
+                const int e = (p * NH + ht) * 8;
+                raq[p] = *reinterpret_cast<const i4*>(wc + W::AQ + 2 * e);
+            }
+#pragma unroll
+            for (int p = 0; p < VK; ++p) {
+                const int e = (p * NH + ht) * 8;
+                rkr[p] = *reinterpret_cast<const i4*>(wc + W::KRT + 2 * e);
+            }
+            if (ht < DK / 4) rg = *reinterpret_cast<const i4*>(wc + W::GC + 16 * ht);
+        };
+        auto stage2 = [&]() {
+#pragma unroll
+            for (int p = 0; p < VA; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / kC, col = e % kC;
+                *reinterpret_cast<i4*>(&Aq[row * LDC + col]) = raq[p];
+            }
+#pragma unroll
+            for (int p = 0; p < VK; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / kC, col = e % kC;
+                *reinterpret_cast<i4*>(&KrT[row * LDC + col]) = rkr[p];
+            }
+            if (ht < DK / 4) *reinterpret_cast<i4*>(&gC[4 * ht]) = rg;
+        };
+        // output block of chunk c from Os, 16-byte rows
+        auto copy_out = [&](int64_t c) {
+#pragma unroll
+            for (int p = 0; p < VV; ++p) {
+                const int e = (p * NH + ht) * 8;
+                const int row = e / DVB, col = e % DVB;
+                const int64_t l = c * kC + row;
+                if (l < Tlen)
+                    *reinterpret_cast<i4*>(o + (bh * Tlen + l) * DV + vb * DVB + col) =
+                        *reinterpret_cast<const i4*>(&Os[row * LDV + col]);
+            }
+        };
+        if (nchunks > 0) {
+            load1(0);
+            load2(0);
+            stage1(0);
+            if (nchunks > 1) load1(1);
+        }
+        __syncthreads();                          // group 1 of chunk 0 staged
+        for (int64_t c = 0; c < nchunks; ++c) {
+            // ---- phase 1 ----
+            stage2();
+            if (c + 1 < nchunks) load2(c + 1);
+            if (c > 0) copy_out(c - 1);
+            lds_barrier();
+            // ---- phase 2 ----
+            if (c + 1 < nchunks) {
+                stage1(c + 1);
+                if (c + 2 < nchunks) load1(c + 2);
+            }
+            lds_barrier();
+        }
+        __syncthreads();                          // the last output is in Os
+        if (nchunks > 0) copy_out(nchunks - 1);
     }
 }
 
@@ -568,7 +660,7 @@ hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     const int nblocks = (int)(bh * (p.dv / 64));
-    hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE>), dim3((unsigned)nblocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE>), dim3((unsigned)nblocks), dim3(512), 0, s,
                        static_cast<const bf16*>(p.v), ws, p.s0, static_cast<bf16*>(p.o), p.s_final,
                        p.T, nchunks, p.dv, nblocks);
     return hipGetLastError();

@@ -250,6 +250,10 @@ __host__ __device__ constexpr int pcol(int c)
     return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
 }
 
+// first logical column of the 8 stored at position P (a multiple of 8) in pcol
+// order: they are columns c0..c0+3 and c0+16..c0+19
+__host__ __device__ constexpr int pcol_first(int P) { return (P & ~31) | ((P & 24) >> 1); }
+
 template <typename T> struct Pair;
 template <> struct Pair<bf16> { typedef bf16x8 type; };
 template <> struct Pair<float> { struct type { floatx4 lo, hi; }; };
