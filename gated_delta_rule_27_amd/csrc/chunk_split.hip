@@ -313,16 +313,23 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
             if constexpr (DELTA) store_tile_t(&Nf[16 * i * LDN + 16 * j], LDN, vn, lane);
         }
 
-        // ---- decayed operands of kernel B to the workspace -----------------------------
-        // Columns go in pcol order (mfma.h): the 8 values stored at position P are
-        // the logical columns c0..c0+3 and c0+16..c0+19, c0 = pcol_first(P).
-        {
+        __syncthreads();
+
+        // ---- wave 0: a3/a4 triangular transform; waves 1..7 meanwhile write the
+        // decayed operands of kernel B and Aq to the workspace, columns in pcol
+        // order (mfma.h): the 8 values stored at position P are the logical
+        // columns c0..c0+3 and c0+16..c0+19, c0 = pcol_first(P) ---------------------
+        if (wave == 0) {
+            if constexpr (DELTA) tsolve64_wave<bf16>(Nf, LDN, Tb, LDC, bet, lane);
+        } else {
+            constexpr int NW1 = NT - 64;              // threads of waves 1..7
+            const int wt = tid - 64;
             bf16* Qd = reinterpret_cast<bf16*>(wc + W::QD);
             bf16* Kd = reinterpret_cast<bf16*>(wc + W::KD);
             bf16* KrT = reinterpret_cast<bf16*>(wc + W::KRT);
-#pragma unroll
-            for (int p = 0; p < NV; ++p) {
-                const int idx = (p * NT + tid) * 8;
+            bf16* Aqw = reinterpret_cast<bf16*>(wc + W::AQ);
+            for (int v8 = wt; v8 < kC * DK / 8; v8 += NW1) {
+                const int idx = v8 * 8;
                 const int row = idx / DK, P = idx % DK, b = row / 16;
                 const int c0 = pcol_first(P), c1 = c0 + 16;
                 const bf16x4 qa = *reinterpret_cast<const bf16x4*>(&qs[row * LDQ + c0]);
@@ -342,9 +349,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
                 *reinterpret_cast<bf16x8*>(Qd + row * DK + P) = qo;
                 if constexpr (DELTA) *reinterpret_cast<bf16x8*>(Kd + row * DK + P) = ko;
             }
-#pragma unroll
-            for (int p = 0; p < NV; ++p) {
-                const int idx = (p * NT + tid) * 8;         // over [DK][C]
+            for (int v8 = wt; v8 < DK * kC / 8; v8 += NW1) {
+                const int idx = v8 * 8;                 // over [DK][C]
                 const int c = idx / kC, P = idx % kC;
                 const int l0 = pcol_first(P), l1 = l0 + 16;
                 const float f0 = Fe[l0 / 16][c], f1 = Fe[l1 / 16][c];
@@ -356,28 +362,23 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
                 }
                 *reinterpret_cast<bf16x8*>(KrT + c * kC + P) = kr;
             }
+            for (int v8 = wt; v8 < kC * kC / 8; v8 += NW1) {
+                const int row = v8 / (kC / 8), P = (v8 % (kC / 8)) * 8;
+                const int c0 = pcol_first(P), c1 = c0 + 16;
+                *reinterpret_cast<bf16x8*>(Aqw + row * kC + P) =
+                    __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(&Aq[row * LDC + c0]),
+                                            *reinterpret_cast<const bf16x4*>(&Aq[row * LDC + c1]), 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         }
-        __syncthreads();
-
-        // ---- a3/a4: triangular transform (wave 0) -----------------------------------
         if constexpr (DELTA) {
-            if (wave == 0) tsolve64_wave<bf16>(Nf, LDN, Tb, LDC, bet, lane);
             __syncthreads();
-        }
-
-        // ---- Aq and Tb to the workspace, columns in pcol order -----------------------------
-        {
-            bf16* Aqw = reinterpret_cast<bf16*>(wc + W::AQ);
+            // ---- Tb to the workspace, columns in pcol order --------------------------------
             bf16* Tbw = reinterpret_cast<bf16*>(wc + W::TB);
             const int row = tid / (kC / 8), P = (tid % (kC / 8)) * 8;
             const int c0 = pcol_first(P), c1 = c0 + 16;
-            *reinterpret_cast<bf16x8*>(Aqw + row * kC + P) =
-                __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(&Aq[row * LDC + c0]),
-                                        *reinterpret_cast<const bf16x4*>(&Aq[row * LDC + c1]), 0, 1, 2, 3, 4, 5, 6, 7);
-            if constexpr (DELTA)
-                *reinterpret_cast<bf16x8*>(Tbw + row * kC + P) =
-                    __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(&Tb[row * LDC + c0]),
-                                            *reinterpret_cast<const bf16x4*>(&Tb[row * LDC + c1]), 0, 1, 2, 3, 4, 5, 6, 7);
+            *reinterpret_cast<bf16x8*>(Tbw + row * kC + P) =
+                __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(&Tb[row * LDC + c0]),
+                                        *reinterpret_cast<const bf16x4*>(&Tb[row * LDC + c1]), 0, 1, 2, 3, 4, 5, 6, 7);
         }
     }
 }
@@ -601,36 +602,41 @@ __global__ __launch_bounds__(512, 1) void chunk_chain_kernel(
             }
             if (ht < DK / 4) *reinterpret_cast<i4*>(&gC[4 * ht]) = rg;
         };
-        // output block of chunk c from Os, 16-byte rows
+        // Output block of chunk c from Os, 16-byte rows, through a buffer resource
+        // over this head's rows: rows past the end fall outside it and the
+        // hardware drops them, so no branch hides a store from the compiler's
+        // wait counts.  Likewise every chunk issues the same loads (the chunk
+        // index clamped to the last one), so a wait for one group never includes
+        // the group loaded after it.
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            o + bh * Tlen * DV, (short)0, (int)(Tlen * DV * 2), 0x00020000);
         auto copy_out = [&](int64_t c) {
 #pragma unroll
             for (int p = 0; p < VV; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / DVB, col = e % DVB;
-                const int64_t l = c * kC + row;
-                if (l < Tlen)
-                    *reinterpret_cast<i4*>(o + (bh * Tlen + l) * DV + vb * DVB + col) =
-                        *reinterpret_cast<const i4*>(&Os[row * LDV + col]);
+                const int off = (int)(((c * kC + row) * DV + vb * DVB + col) * 2);
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i4*>(&Os[row * LDV + col]), orsrc,
+                                                       off, 0, 0);
             }
         };
+        const int64_t last = nchunks - 1;
         if (nchunks > 0) {
             load1(0);
             load2(0);
             stage1(0);
-            if (nchunks > 1) load1(1);
+            load1(1 < last ? 1 : last);
         }
         __syncthreads();                          // group 1 of chunk 0 staged
         for (int64_t c = 0; c < nchunks; ++c) {
             // ---- phase 1 ----
             stage2();
-            if (c + 1 < nchunks) load2(c + 1);
+            load2(c + 1 < last ? c + 1 : last);
             if (c > 0) copy_out(c - 1);
             lds_barrier();
             // ---- phase 2 ----
-            if (c + 1 < nchunks) {
-                stage1(c + 1);
-                if (c + 2 < nchunks) load1(c + 2);
-            }
+            if (c + 1 < nchunks) stage1(c + 1);
+            load1(c + 2 < last ? c + 2 : last);
             lds_barrier();
         }
         __syncthreads();                          // the last output is in Os
