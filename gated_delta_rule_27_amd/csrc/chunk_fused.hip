@@ -102,8 +102,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     constexpr bool DELTA = Cfg::DELTA, GATED = Cfg::GATED;
     constexpr int ND = Cfg::ND, NL = Cfg::NL, E = Cfg::E, NQ = Cfg::NQ, NV = Cfg::NV;
     constexpr int NK = DK / Mfma<T>::kStep;          // MFMA steps over the key dimension
-    // waves kW0..7 share the Aq tiles and the output copy
-    constexpr int kW0 = DELTA ? 5 : 4, kNIW = kNW - kW0;
+    // waves kW0..7 share the output copy (add rule: also the Aq tiles)
+    constexpr int kW0 = DELTA ? 6 : 4, kNIW = kNW - kW0;
 
     __shared__ __align__(16) T Qs[kC * LDQ];
     __shared__ __align__(16) T Ks[kC * LDQ];
@@ -113,10 +113,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     __shared__ __align__(16) T Os[kC * LDV];
     __shared__ __align__(16) T Tb[DELTA ? kC * LDC : 8];
     // the six N blocks below the diagonal as row fragments, lane by lane, and the
-    // X tiles the two halves of the off-diagonal transform exchange (X11 from
-    // wave 4; X22^T and X33^T from wave 5)
+    // X tiles the two halves of the off-diagonal transform need from the other
+    // waves: X11^T (wave 5), X22 and X22^T (wave 6), X33^T (wave 7)
     __shared__ __align__(16) floatx4 Nlo[DELTA ? 6 * kWave : 1];
-    __shared__ __align__(16) floatx4 Xx[DELTA ? 3 * kWave : 1];
+    __shared__ __align__(16) floatx4 Xx[DELTA ? 4 * kWave : 1];
     // gate values alternate between two buffers: the state waves still read the
     // previous chunk's while wave 4 writes this chunk's
     __shared__ __align__(16) float Gsb[2][kC], gamb[2][kC], rhob[2][kC], betb[2][kC];
@@ -203,21 +203,26 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     // issued: loads and stores share one vector-memory counter, so a store issued
     // between a load and its wait would make the wait include the store.  Rows of
     // 64 columns go out as full 16-byte vectors.
+    // The stores go through a buffer resource over this head's rows: rows past
+    // the end (and the spare lanes of the last round) fall outside it and the
+    // hardware drops them, so no branch hides a store from the compiler's wait
+    // counts (the next chunk's loads are likewise issued unconditionally).
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        o + bh * Tlen * DV, (short)0, (int)(Tlen * DV * (int64_t)sizeof(T)), 0x00020000);
     auto copy_out = [&](int64_t tb, int cw, int ln) {
         constexpr int NCOPY = kC * kDVB / E, NROUND = (NCOPY + kNIW * kWave - 1) / (kNIW * kWave);
-        T* oh = o + bh * Tlen * DV + vb * kDVB;
 #pragma unroll
         for (int p = 0; p < NROUND; ++p) {
             const int idx = (p * kNIW + cw) * kWave + ln;
-            if (idx < NCOPY) {
-                const int row = idx / (kDVB / E), col = (idx % (kDVB / E)) * E;
-                const int64_t l = tb + row;
-                if (l < Tlen)
-                    *reinterpret_cast<i4*>(oh + l * DV + col) = *reinterpret_cast<const i4*>(&Os[row * LDV + col]);
-            }
+            const int row = idx / (kDVB / E), col = (idx % (kDVB / E)) * E;
+            const int off = idx < NCOPY ? (int)(((tb + row) * DV + vb * kDVB + col) * (int64_t)sizeof(T))
+                                        : 0x7fffffff;
+            const int ro = idx < NCOPY ? row : 0;
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i4*>(&Os[ro * LDV + col]), orsrc, off,
+                                                   0, 0);
         }
     };
-
+    const int64_t tlast = (nchunks - 1) * kC;     // start of the last chunk
     // All matrix-core fragments (every k step) of the 16-row block b of a [C][DK]
     // tile (Qs or Ks); a wave loads each block it needs once per chunk and forms
     // its tiles from the registers.
@@ -268,41 +273,71 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
     };
 
-    // a2 diagonal N blocks b0 and b0 + 1 in registers.  x = K_b K_b^T is
-    // symmetric, so one product gives N_bb both as tile(N_bb^T) (lane value
-    // N[l][m], l = 16 b + cl) and as tile(N_bb); at most one of the two is
-    // nonzero at each position, so one exp2 serves both.
-    // br[i][rr] = beta[16 (b0 + i) + g4 + rr].  Both blocks' loads are issued
-    // before their products, which are interleaved.
-    auto diag_blocks2 = [&](const float* Gs, const float* bet, int b0, int ln, floatx4 (&nd)[2],
-                            floatx4 (&nt)[2], floatx4 (&br)[2]) {
+    // a2 diagonal N block b in registers.  x = K_b K_b^T is symmetric, so one
+    // product gives N_bb both as tile(N_bb^T) (lane value N[l][m], l = 16 b + cl)
+    // and as tile(N_bb); at most one of the two is nonzero at each position, so
+    // one exp2 serves both.  br[rr] = beta[16 b + g4 + rr]; kb returns K_b's
+    // fragments for the wave's other tiles.
+    auto diag_block = [&](const float* Gs, const float* bet, int b, int ln, floatx4& nd, floatx4& nt,
+                          floatx4& br, Fr (&kb)[NK]) {
         const int cl = ln & 15, g4 = 4 * (ln >> 4);
-        Fr kb[2][NK];
-        block_frags(Ks, b0, ln, kb[0]);
-        block_frags(Ks, b0 + 1, ln, kb[1]);
-        floatx4 Grow[2];
-        float Gcol[2], bcol[2];
+        block_frags(Ks, b, ln, kb);
+        const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * b + g4]);
+        br = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
+        const float Gcol = Gs[16 * b + cl], bcol = bet[16 * b + cl];
+        const floatx4 x = tile_dot(kb, kb);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            Grow[i] = *reinterpret_cast<const floatx4*>(&Gs[16 * (b0 + i) + g4]);
-            br[i] = *reinterpret_cast<const floatx4*>(&bet[16 * (b0 + i) + g4]);
-            Gcol[i] = Gs[16 * (b0 + i) + cl];
-            bcol[i] = bet[16 * (b0 + i) + cl];
+        for (int rr = 0; rr < 4; ++rr) {
+            const bool up = g4 + rr < cl;                       // N[l][m] with m < l
+            const float d = GATED ? fast_exp2(up ? Gcol - Grow[rr] : Grow[rr] - Gcol) : 1.f;
+            nt[rr] = up ? bcol * x[rr] * d : 0.f;
+            nd[rr] = (cl < g4 + rr) ? br[rr] * x[rr] * d : 0.f;
         }
-        floatx4 x[2] = {zero4(), zero4()};
+    };
+    // a2 N block (lj, mi), mi < lj, from K_mi and K_lj fragments, as a row
+    // fragment into slot lj (lj - 1) / 2 + mi of Nlo
+    auto n_block = [&](const float* Gs, const float* bet, int lj, int mi, const Fr (&fm)[NK],
+                       const Fr (&fl)[NK], int ln) {
+        const int cl = ln & 15, g4 = 4 * (ln >> 4);
+        const floatx4 x = tile_dot(fm, fl);
+        const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * mi + g4]);
+        const float Gcol = Gs[16 * lj + cl], bcol = bet[16 * lj + cl];
+        floatx4 t;
 #pragma unroll
-        for (int k = 0; k < NK; ++k)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) x[i] = Mfma<T>::mma(kb[i][k], kb[i][k], x[i]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const bool up = g4 + rr < cl;                   // N[l][m] with m < l
-                const float d = GATED ? fast_exp2(up ? Gcol[i] - Grow[i][rr] : Grow[i][rr] - Gcol[i]) : 1.f;
-                nt[i][rr] = up ? bcol[i] * x[i][rr] * d : 0.f;
-                nd[i][rr] = (cl < g4 + rr) ? br[i][rr] * x[i][rr] * d : 0.f;
-            }
+        for (int rr = 0; rr < 4; ++rr) t[rr] = bcol * x[rr] * (GATED ? fast_exp2(Gcol - Grow[rr]) : 1.f);
+        Nlo[(lj * (lj - 1) / 2 + mi) * kWave + ln] = t;
+    };
+    // delta rule, P2a of intra wave b = wave - 4: diagonal block b and its
+    // inverse, the wave's N blocks below the diagonal, and the X tiles the two
+    // off-diagonal halves need from it.  Returns X_bb and X_bb^T.
+    auto intra_p2a = [&](const float* Gs, const float* bet, int b, int ln, floatx4& X, floatx4& Xt) {
+        floatx4 nd[1], nt[1], br[1], Xa[1], Xta[1];
+        Fr kb[NK], k2[NK];
+        diag_block(Gs, bet, b, ln, nd[0], nt[0], br[0], kb);
+        tsolve_diag<T, true, 1>(nd, nt, Xa, Xta, Tb, LDC, br, ln, b);
+        X = Xa[0];
+        Xt = Xta[0];
+        if (b == 0) {                                  // N(1,0)
+            block_frags(Ks, 1, ln, k2);
+            n_block(Gs, bet, 1, 0, kb, k2, ln);
+        } else if (b == 1) {                           // N(2,1); X11^T
+            block_frags(Ks, 2, ln, k2);
+            n_block(Gs, bet, 2, 1, kb, k2, ln);
+            Xx[0 * kWave + ln] = Xt;
+        } else if (b == 2) {                           // N(3,2), N(2,0); X22, X22^T
+            block_frags(Ks, 3, ln, k2);
+            n_block(Gs, bet, 3, 2, kb, k2, ln);
+            block_frags(Ks, 0, ln, k2);
+            n_block(Gs, bet, 2, 0, k2, kb, ln);
+            Xx[1 * kWave + ln] = X;
+            Xx[2 * kWave + ln] = Xt;
+        } else {                                       // N(3,0), N(3,1); X33^T
+            block_frags(Ks, 0, ln, k2);
+            n_block(Gs, bet, 3, 0, k2, kb, ln);
+            block_frags(Ks, 1, ln, k2);
+            n_block(Gs, bet, 3, 1, k2, kb, ln);
+            Xx[3 * kWave + ln] = Xt;
+        }
     };
 
     if (wave < 4) {
@@ -333,7 +368,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const float* const rho = rhob[r & 1];
 
             stage(t0);
-            if (r + 1 < nchunks) fetch(t0 + kC);
+            fetch(t0 + kC < tlast ? t0 + kC : tlast);
             lds_barrier();
 
             // ---- P2a: R = V - gamma K S_r (delta; V for add) --------------------------
@@ -379,6 +414,25 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     for (int rr = 0; rr < 4; ++rr) Ot[li][rr] *= gl;
                 }
             };
+            // K^T through the matrix core (this wave's quarter of the tiles)
+            auto ksT = [&]() {
+                constexpr int NKT = NL * ND / 4;             // transposes per state wave
+                F af[NKT];
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) {
+                    const int t = wave + 4 * i;
+                    af[i] = frag16_lds_pc(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
+                }
+                const F id = ident_frag<T>(ln);
+                floatx4 d[NKT];
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) d[i] = mma16<T>(af[i], id, zero4());
+#pragma unroll
+                for (int i = 0; i < NKT; ++i) {
+                    const int t = wave + 4 * i;
+                    store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
+                }
+            };
             if constexpr (!DELTA) {
                 ohist();
             } else {
@@ -410,29 +464,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     block_frags(Ks, m0 + 1, ln, fb);
                     aq_store(Gs, 3, m0 + 1, tile_dot(fb, fq), ln);
                 }
+                ksT();
             }
             lds_barrier();
 
-            // ---- P2b: (delta) O^T history ; K^T through the matrix core -------------
+            // ---- P2b: (delta) O^T history; (add) K^T through the matrix core -------
             if constexpr (DELTA) ohist();
-            {
-                constexpr int NKT = NL * ND / 4;             // transposes per state wave
-                F af[NKT];
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) {
-                    const int t = wave + 4 * i;
-                    af[i] = frag16_lds_pc(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
-                }
-                const F id = ident_frag<T>(ln);
-                floatx4 d[NKT];
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) d[i] = mma16<T>(af[i], id, zero4());
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) {
-                    const int t = wave + 4 * i;
-                    store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
-                }
-            }
+            else ksT();
             lds_barrier();
 
             // ---- P4: b1 Z = Tb R ; c1 O^T += Z^T Aq^T ; S_{r+1} -----------------------
@@ -522,27 +560,23 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 rhob[r & 1][lane] = GATED ? fast_exp2(Glast - G) : 1.f;
                 bet[lane] = (DELTA && ok) ? to_f32(breg) : 0.f;
             }
-            if (r + 1 < nchunks) {
-                fetch(t0 + kC);
-                fetch_gate(t0 + kC);
-            }
+            fetch(t0 + kC < tlast ? t0 + kC : tlast);
+            fetch_gate(t0 + kC < tlast ? t0 + kC : tlast);
             lds_barrier();
 
             if constexpr (DELTA) {
-                // ---- P2a: diagonal N blocks 0, 1 and their inverses; X11 to LDS
-                floatx4 nd[2], nt[2], X[2], Xt[2], br[2];
-                diag_blocks2(Gs, bet, 0, ln, nd, nt, br);
-                tsolve_diag<T, true, 2, 0>(nd, nt, X, Xt, Tb, LDC, br, ln);
-                Xx[0 * kWave + ln] = X[1];
+                // ---- P2a: diagonal block 0, its inverse, N(1,0) ----
+                floatx4 X0, Xt0;
+                intra_p2a(Gs, bet, 0, ln, X0, Xt0);
                 lds_barrier();
                 // ---- P2b: half A of the off-diagonal blocks (column block 0, T10)
                 floatx4 brow[NL];
 #pragma unroll
                 for (int b = 0; b < NL; ++b) brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
                 const floatx4* nl = Nlo + ln;
-                tsolve_offdiag_a<T, true>(X[0], Xt[1], Xx[1 * kWave + ln], Xx[2 * kWave + ln], nl[0 * kWave],
-                                          nl[1 * kWave], nl[2 * kWave], nl[3 * kWave], nl[4 * kWave],
-                                          nl[5 * kWave], Tb, LDC, brow, ln);
+                tsolve_offdiag_a<T, true>(X0, Xx[0 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
+                                          nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
+                                          nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
             } else {
                 aq_share(Gs, 0, kNIW, ln);
                 lds_barrier();
@@ -551,8 +585,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             lds_barrier();
         }
     } else if (DELTA && wave == 5) {
-        // ======== wave 5 (delta): a2 diagonal N blocks 2, 3 and their inverses;
-        // half B of the off-diagonal blocks; output copy -------------------------
+        // ======== wave 5 (delta): a2 diagonal block 1, its inverse, N(2,1); half B
+        // of the off-diagonal blocks -------------------------------------------------
         for (int64_t r = 0; r < nchunks; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
@@ -560,23 +594,19 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const float* const Gs = Gsb[r & 1];
             const float* const bet = betb[r & 1];
             stage(t0);
-            if (r + 1 < nchunks) fetch(t0 + kC);
+            fetch(t0 + kC < tlast ? t0 + kC : tlast);
             lds_barrier();
             // ---- P2a ----
-            floatx4 nd[2], nt[2], X[2], Xt[2], br[2];
-            diag_blocks2(Gs, bet, 2, ln, nd, nt, br);
-            tsolve_diag<T, true, 2, 2>(nd, nt, X, Xt, Tb, LDC, br, ln);
-            Xx[1 * kWave + ln] = Xt[0];
-            Xx[2 * kWave + ln] = Xt[1];
+            floatx4 X1, Xt1;
+            intra_p2a(Gs, bet, 1, ln, X1, Xt1);
             lds_barrier();
-            // ---- P2b: column block 1 and T32; output copy ----
+            // ---- P2b: column block 1 and T32 ----
             floatx4 brow[NL];
 #pragma unroll
             for (int b = 0; b < NL; ++b) brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
             const floatx4* nl = Nlo + ln;
-            tsolve_offdiag_b<T, true>(Xx[0 * kWave + ln], X[0], Xt[0], Xt[1], nl[2 * kWave], nl[4 * kWave],
-                                      nl[5 * kWave], Tb, LDC, brow, ln);
-            if (r > 0) copy_out(t0 - kC, 0, ln);
+            tsolve_offdiag_b<T, true>(X1, Xx[1 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
+                                      nl[2 * kWave], nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
             lds_barrier();
         }
     } else {
@@ -590,38 +620,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const float* const Gs = Gsb[r & 1];
             const float* const bet = betb[r & 1];
             stage(t0);
-            if (r + 1 < nchunks) fetch(t0 + kC);
+            fetch(t0 + kC < tlast ? t0 + kC : tlast);
             lds_barrier();
             // ---- P2a ----
             if constexpr (DELTA) {
-                // N[l][m] for block (lj, mi), mi < lj, as a row fragment; slot
-                // lj (lj - 1) / 2 + mi of Nlo.  Wave 6 takes the blocks of rows
-                // 1-2 (K0-K2), wave 7 those of row 3 (K0-K3); each K block's
-                // fragments are loaded once.
-                auto n_block = [&](int lj, int mi, const Fr (&fm)[NK], const Fr (&fl)[NK]) {
-                    const floatx4 x = tile_dot(fm, fl);
-                    const floatx4 Grow = *reinterpret_cast<const floatx4*>(&Gs[16 * mi + g4]);
-                    const float Gcol = Gs[16 * lj + cl], bcol = bet[16 * lj + cl];
-                    floatx4 t;
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) t[rr] = bcol * x[rr] * (GATED ? fast_exp2(Gcol - Grow[rr]) : 1.f);
-                    Nlo[(lj * (lj - 1) / 2 + mi) * kWave + ln] = t;
-                };
-                Fr k0[NK], k1[NK], k2[NK];
-                block_frags(Ks, 0, ln, k0);
-                block_frags(Ks, 1, ln, k1);
-                block_frags(Ks, 2, ln, k2);
-                if (wave == 6) {
-                    n_block(1, 0, k0, k1);
-                    n_block(2, 0, k0, k2);
-                    n_block(2, 1, k1, k2);
-                } else {
-                    Fr k3[NK];
-                    block_frags(Ks, 3, ln, k3);
-                    n_block(3, 0, k0, k3);
-                    n_block(3, 1, k1, k3);
-                    n_block(3, 2, k2, k3);
-                }
+                floatx4 X, Xt;
+                intra_p2a(Gs, bet, wave - 4, ln, X, Xt);
             } else {
                 aq_share(Gs, iw, kNIW, ln);
             }

@@ -40,14 +40,15 @@ __device__ __forceinline__ void store_tb(T* Tb, int ldt, int rb, int qb, floatx4
     else store_tile_t(&Tb[(rb * 16) * ldt + qb * 16], ldt, v, lane);
 }
 
-// Diagonal blocks B0 .. B0+NB-1 (index i of the arrays is block B0 + i).
+// Diagonal blocks b0 .. b0+NB-1 (index i of the arrays is block b0 + i; b0
+// defaults to B0).
 // nd[i] = tile(N_bb), nt[i] = tile(N_bb^T).  Returns X[i] = tile(X_bb) and
 // Xt[i] = tile(X_bb^T) (fp32) and stores those diagonal blocks of
 // Tb = T diag(beta); brow[i][r] = beta[16 b + 4(l/16) + r].
 template <typename T, bool PC = false, int NB = 4, int B0 = 0>
 __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[NB], const floatx4 (&nt)[NB],
                                             floatx4 (&X)[NB], floatx4 (&Xt)[NB], T* Tb, int ldt,
-                                            const floatx4 (&brow)[NB], int lane)
+                                            const floatx4 (&brow)[NB], int lane, int b0 = B0)
 {
     using F = typename Frag16<T>::type;
     // an opaque copy of the lane index keeps the compiler from hoisting the
@@ -100,7 +101,7 @@ __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[NB], const float
         floatx4 w = Xt[b];
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] *= brow[b][r];
-        store_tb<T, PC>(Tb, ldt, B0 + b, B0 + b, w, lane);
+        store_tb<T, PC>(Tb, ldt, b0 + b, b0 + b, w, lane);
     }
 }
 
