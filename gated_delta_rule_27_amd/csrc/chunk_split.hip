@@ -9,9 +9,9 @@
 // triangular transform), "Correct the incoming state" and the GDN chunkwise
 // table with Diag(lambda[1:C]) as the state decay.
 //
-// Kernel A (intra-chunk, one workgroup per (b, h, chunk), all chunks in
-// parallel) computes what does not depend on the incoming state and stages it
-// in the workspace:
+// Kernel A (intra-chunk, persistent workgroups walking the (b, h, chunk)
+// tasks, all chunks in parallel) computes what does not depend on the incoming
+// state and stages it in the workspace:
 //   a1  G[l][c] = sum_{s<=l} g[s][c]  (per key channel)
 //       Qd = exp(G) . Q, Kd = exp(G) . K, Kr = exp(G_{C-1} - G) . K, gC = exp(G_{C-1})
 //   a2  Aq[l][m] = sum_c q_lc exp(G_lc - G_mc) k_mc   (m <= l)
@@ -23,14 +23,10 @@
 //       S_{r+1} = Diag(gC) S_r + Kr^T Z
 //   c1  O = Qd S_r + Aq Z
 //
-// The channelwise scores need exp(G_lc - G_mc) inside a sum over channels.  For
-// a 16x16 tile it is split as exp(G_l - G_p) exp(G_p - G_m) with a reference
-// row p, so the tile is one matrix-core product of two decayed operands.  Off
-// the diagonal p is the row just before the query block: both factors are at
-// most 1 and nothing can overflow.  On a diagonal block p is its middle row;
-// each factor then stays within exp(span) where span is the block's largest
-// per-channel decay, and a block whose span exceeds kSpanMax is computed
-// element by element in fp32 instead.
+// The channelwise scores need exp(G_lc - G_mc) inside a sum over channels.
+// Kernel A splits it into per-row factors local to each 16-row block, so every
+// 16x16 score tile is one matrix-core product of two decayed operands (the
+// factorisation and its overflow guard are described at kernel A).
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
