@@ -33,9 +33,13 @@ struct ChunkProblem {
 
 hipError_t launch_decode_step(const DecodeProblem& p, hipStream_t stream);
 
-// Single-pass chunk kernel (gate NONE or SCALAR).
+// Single-pass chunk kernel (gate NONE or SCALAR), three phases per chunk.
 bool chunk_fused_supported(const ChunkProblem& p);
 hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t stream);
+// Single-pass chunk kernel for bf16 tokens (gate NONE or SCALAR), pipelined:
+// chunk r+1's intra-chunk work beside chunk r's state pass.
+bool chunk_pipe_supported(const ChunkProblem& p);
+hipError_t launch_chunk_pipe(const ChunkProblem& p, hipStream_t stream);
 
 // Two-kernel chunk path (intra-chunk precompute, then the state pass with the
 // output); used for the per-channel gate.

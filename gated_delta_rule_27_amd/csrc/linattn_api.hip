@@ -19,14 +19,20 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 // Which chunk path serves a problem: the per-channel gate always takes the
-// two-kernel path; a scalar gate takes it when LINATTN_CHUNK_PATH=split (for
-// A/B measurement), otherwise the single-pass kernel.
-bool use_split(const ChunkProblem& p)
+// two-kernel path.  Otherwise bf16 tokens take the pipelined single-pass
+// kernel and fp32 tokens the three-phase one.  LINATTN_CHUNK_PATH=split or
+// =fused selects the two-kernel or the three-phase path instead (for A/B
+// measurement) where they support the problem.
+enum ChunkPath { kPathSplit, kPathFused, kPathPipe };
+ChunkPath chunk_path(const ChunkProblem& p)
 {
-    if (p.gate == kGateChannel) return true;
+    if (p.gate == kGateChannel) return kPathSplit;
     const char* e = getenv("LINATTN_CHUNK_PATH");
-    return e && strcmp(e, "split") == 0 && chunk_split_supported(p);
+    if (e && strcmp(e, "split") == 0 && chunk_split_supported(p)) return kPathSplit;
+    if (e && strcmp(e, "fused") == 0 && chunk_fused_supported(p)) return kPathFused;
+    return p.dtype == kBF16 ? kPathPipe : kPathFused;
 }
+bool use_split(const ChunkProblem& p) { return chunk_path(p) == kPathSplit; }
 
 linattn_status check_enums(int rule, int gate, int dtype)
 {
@@ -68,8 +74,15 @@ linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
     p->dk = a->dk; p->dv = a->dv;
     p->chunk = a->chunk == 0 ? 64 : a->chunk;
     p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
-    if (use_split(*p) ? !chunk_split_supported(*p) : !chunk_fused_supported(*p))
-        return LINATTN_ERR_UNSUPPORTED;
+    const ChunkPath path = chunk_path(*p);
+    const bool ok = path == kPathSplit ? chunk_split_supported(*p)
+                  : path == kPathPipe  ? chunk_pipe_supported(*p)
+                                       : chunk_fused_supported(*p);
+    if (!ok) return LINATTN_ERR_UNSUPPORTED;
+    // the single-pass kernels address one head's output through a buffer
+    // resource with a 31-bit byte range
+    const int64_t esz = a->dtype == LINATTN_BF16 ? 2 : 4;
+    if (path != kPathSplit && a->T * a->dv * esz >= ((int64_t)1 << 31)) return LINATTN_ERR_UNSUPPORTED;
     return LINATTN_OK;
 }
 
@@ -128,7 +141,9 @@ linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, con
     p.workspace = workspace; p.workspace_bytes = workspace_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
-    if (!use_split(p)) {
+    if (chunk_path(p) == kPathPipe) {
+        err = launch_chunk_pipe(p, s);
+    } else if (chunk_path(p) == kPathFused) {
         err = launch_chunk_fused(p, s);
     } else {
         const size_t need = chunk_split_workspace_bytes(p);

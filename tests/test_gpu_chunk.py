@@ -73,7 +73,20 @@ def test_small_cases_ragged(dtype, dk, dv, rule, gate):
     check_chunk(case, x, s0=x["s0"])
 
 
-@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 129])
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("rule,gate", [("add", "none"), ("add", "scalar"), ("delta", "none"),
+                                       ("delta", "scalar")])
+def test_three_phase_kernel_bf16(monkeypatch, dk, rule, gate):
+    # LINATTN_CHUNK_PATH=fused routes bf16 tokens through the three-phase
+    # single-pass kernel (the default for fp32) instead of the pipelined one
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", "fused")
+    case = syn.Case("fused3", 2, 2, 200, dk, 128, rule, gate, "bf16", gate_scale=1 / 16,
+                    s0_std=0.3, case_id=114)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
+
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 129, 192, 257])
 def test_lengths_around_chunk_boundaries(T):
     case = syn.Case("len", 1, 2, T, 128, 128, "delta", "scalar", "bf16", gate_scale=0.1,
                     s0_std=0.2, case_id=101)
