@@ -380,14 +380,14 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 }
 
 // ===========================================================================
-// Kernel B: state pass + output.  One workgroup per (b, h, 64 value columns),
-// chunks in order, 8 waves:
-//   * state waves 0..3: wave w owns value columns 16w..16w+15 and keeps
+// Kernel B: state pass + output.  One workgroup per (b, h, DVB = 64 or 32 value
+// columns), chunks in order, DVB/16 + 4 waves:
+//   * state waves 0..DVB/16-1: wave w owns value columns 16w..16w+15 and keeps
 //     S[:, those columns] (fp32) as dk/16 MFMA result tiles; every product
 //     takes S, R or Z straight from registers (mfma.h), paired into K = 32
 //     products whose LDS operands are single 16-byte reads (pcol order, as
 //     kernel A stores them).
-//   * helper waves 4..7 move everything between HBM and LDS: the chunk's
+//   * the four helper waves after them move everything between HBM and LDS: the chunk's
 //     staged operands, loaded into registers one chunk ahead, and the output.
 //     The state waves touch no global memory inside the loop.
 // Two LDS barriers per chunk split it into
@@ -399,13 +399,14 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 //            chunk
 // so each LDS region is refilled while the other phase runs.
 // ===========================================================================
-template <int DK, int RULE>
-__global__ __launch_bounds__(512, 1) void chunk_chain_kernel(
+template <int DK, int RULE, int DVB>
+__global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const bf16* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0,
     bf16* __restrict__ o, float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks)
 {
     using W = SplitWs<DK>;
-    constexpr int NH = 256, DVB = 64, ND = DK / 16, NL = kC / 16;
+    constexpr int NSW = DVB / 16;                // state waves, 16 value columns each
+    constexpr int NH = 256, ND = DK / 16, NL = kC / 16;
     constexpr bool DELTA = RULE == kRuleDelta;
     constexpr int LDQ = DK + 8, LDC = kC + 8, LDV = DVB + 8;
     constexpr int VQ = kC * DK / (8 * NH);       // 16-byte vectors per helper thread, [C][DK] tile
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void chunk_chain_kernel(
     const int64_t bh = blk / nvb;
     const int vb = blk % nvb;
 
-    if (wave < 4) {
+    if (wave < NSW) {
         // ======== state waves ============================================================
         const int n0 = 16 * wave;                 // first column of this wave in the block
         floatx4 S[ND];
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(512, 1) void chunk_chain_kernel(
         __syncthreads();                          // the last output is in Os
     } else {
         // ======== helper waves =============================================================
-        const int ht = tid - 256;
+        const int ht = tid - NSW * 64;
         // group 1: Kd, Qd, V, Tb ; group 2: Aq, Kr^T, gC
         i4 rkd[VQ], rqd[VQ], rv[VV], rtb[VA];
         i4 raq[VA], rkr[VK], rg = {0, 0, 0, 0};
@@ -646,12 +647,12 @@ hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
     const int64_t nchunks = (p.T + kC - 1) / kC;
     const int64_t bh = p.B * p.H;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        ncu = 256;
     if (nchunks > 0) {
         // persistent: one workgroup per CU (its LDS use allows no second one)
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-            ncu = 256;
         const int64_t ntasks = bh * nchunks;
         const int64_t grid = ntasks < ncu ? ntasks : ncu;
         hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE>), dim3((unsigned)grid), dim3(512), 0, s,
@@ -661,10 +662,21 @@ hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int nblocks = (int)(bh * (p.dv / 64));
-    hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE>), dim3((unsigned)nblocks), dim3(512), 0, s,
-                       static_cast<const bf16*>(p.v), ws, p.s0, static_cast<bf16*>(p.o), p.s_final,
-                       p.T, nchunks, p.dv, nblocks);
+    // The state pass runs one workgroup per (b, h, value block).  With few heads
+    // (fewer 64-column blocks than CUs) the blocks are 32 columns wide, which
+    // doubles the number of independent chains; each staged tile is then read
+    // by twice as many workgroups (mostly from L2).
+    if (bh * (p.dv / 64) < ncu) {
+        const int nblocks = (int)(bh * (p.dv / 32));
+        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 32>), dim3((unsigned)nblocks), dim3(6 * 64), 0, s,
+                           static_cast<const bf16*>(p.v), ws, p.s0, static_cast<bf16*>(p.o), p.s_final,
+                           p.T, nchunks, p.dv, nblocks);
+    } else {
+        const int nblocks = (int)(bh * (p.dv / 64));
+        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 64>), dim3((unsigned)nblocks), dim3(8 * 64), 0, s,
+                           static_cast<const bf16*>(p.v), ws, p.s0, static_cast<bf16*>(p.o), p.s_final,
+                           p.T, nchunks, p.dv, nblocks);
+    }
     return hipGetLastError();
 }
 

@@ -183,6 +183,16 @@ def test_channel_gate_small_ragged(dk, dv, rule):
     check_chunk(case, x, s0=x["s0"])
 
 
+@pytest.mark.parametrize("rule", ["add", "delta"])
+def test_channel_gate_many_heads(rule):
+    # 256 heads x two 64-column blocks fill more workgroups than CUs, so the
+    # state pass runs 64-column blocks (fewer heads take 32-column blocks)
+    case = syn.Case("chanwide", 2, 128, 130, 128, 128, rule, "channel", "bf16", gate_scale=1 / 16,
+                    s0_std=0.3, case_id=116)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
+
+
 @pytest.mark.parametrize("gate_scale", [1.0, 12.0])
 def test_channel_gate_decay_laws(gate_scale):
     # gate_scale 12: per-token log-decay ~ -10 per channel, so 16-token
