@@ -79,10 +79,10 @@ linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
                   : path == kPathPipe  ? chunk_pipe_supported(*p)
                                        : chunk_fused_supported(*p);
     if (!ok) return LINATTN_ERR_UNSUPPORTED;
-    // the single-pass kernels address one head's output through a buffer
-    // resource with a 31-bit byte range
+    // every chunk kernel addresses one head's output through a buffer resource
+    // with a 31-bit byte range
     const int64_t esz = a->dtype == LINATTN_BF16 ? 2 : 4;
-    if (path != kPathSplit && a->T * a->dv * esz >= ((int64_t)1 << 31)) return LINATTN_ERR_UNSUPPORTED;
+    if (a->T * a->dv * esz >= ((int64_t)1 << 31)) return LINATTN_ERR_UNSUPPORTED;
     return LINATTN_OK;
 }
 

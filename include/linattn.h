@@ -111,8 +111,9 @@ size_t linattn_chunk_workspace_bytes(const linattn_chunk_args *a);
  *            linattn_chunk_workspace_bytes(a) bytes (may be NULL when that is 0)
  *   stream   hipStream_t
  * Supported: dk, dv in {64, 128}; chunk 64; bf16 tokens for any gate; fp32
- * tokens for dk = 64 with gate NONE or SCALAR.  T need not be a multiple of
- * the chunk size.
+ * tokens for dk = 64 with gate NONE or SCALAR; one head's output under 2 GiB
+ * (T * dv * element size < 2^31, else LINATTN_ERR_UNSUPPORTED).  T need not
+ * be a multiple of the chunk size.
  */
 linattn_status linattn_chunk_fwd(const linattn_chunk_args *a,
                                  const void *q, const void *k, const void *v,

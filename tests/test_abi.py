@@ -70,6 +70,8 @@ def test_chunk_validation(lib):
     assert call_chunk(lib, a) == 6
     assert call_chunk(lib, mk(), s0=FAKE, sf=FAKE + 16) == 6     # partial overlap
     assert call_chunk(lib, mk(B=0)) == 0                         # nothing to do
+    assert call_chunk(lib, mk(T=1 << 24, dv=128)) == 3           # one head's output >= 2 GiB
+    assert call_chunk(lib, mk(T=1 << 23, dv=128, gate="channel", dk=128), g=FAKE) == 3
     assert lib.linattn_chunk_workspace_bytes(ctypes.byref(mk())) == 0
     # the per-channel gate runs the two-kernel path, which stages per-chunk tiles
     wa = mk(gate="channel", dk=128, dv=128, T=130)
