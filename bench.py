@@ -29,9 +29,9 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_27_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources each measured kernel is built from: counter figures in profiles/
 # are valid only while these hash to the value recorded with them
-CHUNK_SOURCES = ("chunk_fused.hip", "mfma.h", "tsolve.h", "device_common.h", "launch.h")
+CHUNK_SOURCES = ("chunk_pipe.hip", "mfma.h", "tsolve.h", "device_common.h", "launch.h")
 DECODE_SOURCES = ("decode_step.hip", "device_common.h", "launch.h")
-CHUNK_PROFILE = "chunk_fused_gdn_B8_H16_T8192_d128.md"
+CHUNK_PROFILE = "chunk_pipe_gdn_B8_H16_T8192_d128.md"
 DECODE_PROFILE = "decode_step_gdn_N256_H32_d128.md"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -142,7 +142,21 @@ def time_chunk(la, syn, case, dev, steps, warmup=2):
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "path": "split" if wsb else "fused", "steps": steps}
+            "path": chunk_path(case, wsb), "steps": steps}
+
+
+def chunk_path(case, wsb):
+    """Which chunk kernel the library runs for this case (its dispatch rule)."""
+    if wsb:
+        return "split"
+    env = os.environ.get("LINATTN_CHUNK_PATH")
+    if env in ("fused", "pipe") and (env == "fused" or case.dtype == "bf16"):
+        return env
+    return "pipe" if case.dtype == "bf16" and case.rule == "delta" else "fused"
+
+
+CHUNK_KERNELS = {"pipe": "chunk_pipe_kernel", "fused": "chunk_fused_kernel",
+                 "split": "chunk_intra_channel_kernel + chunk_chain_kernel"}
 
 
 def main():
@@ -154,8 +168,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128,
                     help="heads of the workload the CPU oracle runs for its baseline")
-    ap.add_argument("--path", choices=["fused", "split"], default=None,
-                    help="chunk path for the scalar gate (default: the library's choice, fused)")
+    ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
+                    help="chunk path for the scalar gate (default: the library's choice: the "
+                         "pipelined single-pass kernel for the delta rule with bf16 tokens)")
     ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4",
                     help="comma-separated secondary chunk workloads to time after the headline "
                          "one (cfg2, cfg3b, cfg4), or 'none'")
@@ -200,6 +215,7 @@ def main():
     s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     wsb = la.chunk_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    path = chunk_path(case, wsb)
 
     def step():
         la.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, rule=case.rule,
@@ -310,12 +326,11 @@ def main():
                                f"bf16 tokens fp32 state",
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
                    "rule": case.rule, "gate": case.gate, "parallelism": "single GPU",
-                   "path": "split" if wsb else "fused"},
+                   "path": path},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(CHUNK_PROFILE, CHUNK_SOURCES) if not wsb else None,
-                     "kernel": "chunk_fused_kernel" if not wsb else
-                               "chunk_intra_channel_kernel + chunk_chain_kernel",
+                     "traffic": counter_traffic(CHUNK_PROFILE, CHUNK_SOURCES) if path == "pipe" else None,
+                     "kernel": CHUNK_KERNELS[path],
                      "alg_bytes_per_launch": abytes},
         "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 2),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -19,10 +19,11 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 // Which chunk path serves a problem: the per-channel gate always takes the
-// two-kernel path.  Otherwise bf16 tokens take the pipelined single-pass
-// kernel and fp32 tokens the three-phase one.  LINATTN_CHUNK_PATH=split or
-// =fused selects the two-kernel or the three-phase path instead (for A/B
-// measurement) where they support the problem.
+// two-kernel path.  Otherwise the delta rule with bf16 tokens takes the
+// pipelined single-pass kernel (its intra-chunk work is large enough to pay
+// for the pipelining), everything else the three-phase one.
+// LINATTN_CHUNK_PATH=split, =fused or =pipe selects that path instead (for A/B
+// measurement) where it supports the problem.
 enum ChunkPath { kPathSplit, kPathFused, kPathPipe };
 ChunkPath chunk_path(const ChunkProblem& p)
 {
@@ -30,7 +31,8 @@ ChunkPath chunk_path(const ChunkProblem& p)
     const char* e = getenv("LINATTN_CHUNK_PATH");
     if (e && strcmp(e, "split") == 0 && chunk_split_supported(p)) return kPathSplit;
     if (e && strcmp(e, "fused") == 0 && chunk_fused_supported(p)) return kPathFused;
-    return p.dtype == kBF16 ? kPathPipe : kPathFused;
+    if (e && strcmp(e, "pipe") == 0 && chunk_pipe_supported(p)) return kPathPipe;
+    return p.dtype == kBF16 && p.rule == kRuleDelta ? kPathPipe : kPathFused;
 }
 bool use_split(const ChunkProblem& p) { return chunk_path(p) == kPathSplit; }
 

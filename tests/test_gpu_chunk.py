@@ -76,10 +76,11 @@ def test_small_cases_ragged(dtype, dk, dv, rule, gate):
 @pytest.mark.parametrize("dk", [64, 128])
 @pytest.mark.parametrize("rule,gate", [("add", "none"), ("add", "scalar"), ("delta", "none"),
                                        ("delta", "scalar")])
-def test_three_phase_kernel_bf16(monkeypatch, dk, rule, gate):
-    # LINATTN_CHUNK_PATH=fused routes bf16 tokens through the three-phase
-    # single-pass kernel (the default for fp32) instead of the pipelined one
-    monkeypatch.setenv("LINATTN_CHUNK_PATH", "fused")
+def test_other_single_pass_kernel_bf16(monkeypatch, dk, rule, gate):
+    # each bf16 case through the single-pass kernel the library does not pick
+    # for it: the three-phase kernel for the delta rule, the pipelined one for
+    # the add rule (LINATTN_CHUNK_PATH)
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", "fused" if rule == "delta" else "pipe")
     case = syn.Case("fused3", 2, 2, 200, dk, 128, rule, gate, "bf16", gate_scale=1 / 16,
                     s0_std=0.3, case_id=114)
     x = syn.chunk_inputs(case)
