@@ -175,6 +175,80 @@ int oracle_decode_step(int64_t N, int64_t H, int dk, int dv, int rule, int gate,
                              nthreads);
 }
 
+/*
+ * Gated DeltaProduct ([LAV] "Gated Delta Product (GDP)"): each token applies
+ * an ordered product of n_h generalized Householder transitions, each with its
+ * own key, value and correction gate, after decaying the previous state once:
+ *
+ *   S = a_t S_{t-1}                                  (scalar gate; none: a_t = 1)
+ *   for j = 1..n_h:  S = S + k_{t,j}^T beta_{t,j} (v_{t,j} - k_{t,j} S)
+ *   S_t = S ;  o_t = q_t S_t                         (query after the last substep)
+ *
+ * Layouts: q [B,H,T,dk]; k [B,H,T,nh,dk]; v [B,H,T,nh,dv]; beta [B,H,T,nh];
+ * g [B,H,T] or NULL; s0, s_final [B,H,dk,dv]; o [B,H,T,dv].  Written as its own
+ * loop (not through token_update), so that checking n_h = 1 against the delta
+ * rule above compares two separate codes.
+ */
+int oracle_deltaproduct(int64_t B, int64_t H, int64_t T, int nh, int dk, int dv, int gate,
+                        const double *q, const double *k, const double *v,
+                        const double *g, const double *beta, const double *s0,
+                        double *o, double *s_final, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || nh <= 0 || dk <= 0 || dv <= 0) return 2;
+    if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_SCALAR) return 3;
+    if (B * H * T > 0 && (!q || !k || !v || !beta || !o)) return 1;
+    if (gate == ORACLE_GATE_SCALAR && B * H * T > 0 && !g) return 1;
+    int64_t nheads = B * H;
+    size_t ss = (size_t)dk * dv;
+    int64_t bh;
+    int failed = 0;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : failed)
+#else
+    (void)nthreads;
+#endif
+    for (bh = 0; bh < nheads; ++bh) {
+        double *S = (double *)malloc(ss * sizeof(double));
+        double *w = (double *)malloc((size_t)dv * sizeof(double));
+        if (!S || !w) { free(S); free(w); failed |= 1; continue; }
+        if (s0 != NULL) memcpy(S, s0 + (size_t)bh * ss, ss * sizeof(double));
+        else memset(S, 0, ss * sizeof(double));
+        int64_t t;
+        int i, j, c;
+        for (t = 0; t < T; ++t) {
+            size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+            if (gate == ORACLE_GATE_SCALAR) {
+                double a = exp(g[tok]);
+                for (i = 0; i < dk * dv; ++i) S[i] *= a;
+            }
+            for (j = 0; j < nh; ++j) {
+                const double *kj = k + (tok * nh + j) * dk;
+                const double *vj = v + (tok * nh + j) * dv;
+                double bj = beta[tok * nh + j];
+                /* w = beta (v - k S): the correction written at k */
+                for (c = 0; c < dv; ++c) {
+                    double pred = 0.0;
+                    for (i = 0; i < dk; ++i) pred += kj[i] * S[(size_t)i * dv + c];
+                    w[c] = bj * (vj[c] - pred);
+                }
+                for (i = 0; i < dk; ++i)
+                    for (c = 0; c < dv; ++c) S[(size_t)i * dv + c] += kj[i] * w[c];
+            }
+            const double *qt = q + tok * dk;
+            for (c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (i = 0; i < dk; ++i) acc += qt[i] * S[(size_t)i * dv + c];
+                o[tok * dv + c] = acc;
+            }
+        }
+        if (s_final) memcpy(s_final + (size_t)bh * ss, S, ss * sizeof(double));
+        free(S);
+        free(w);
+    }
+    return failed ? 6 : 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -6,7 +6,8 @@ It imports nothing from the HIP package and the HIP package never imports it.
 
 ``recurrence`` runs the token-by-token recurrence of causal linear attention
 (add rule, decay with a scalar or per-key-channel gate, delta rule) described
-in ``oracle.c``; ``decode_step`` runs one token per (sequence, head) in place.
+in ``oracle.c``; ``decode_step`` runs one token per (sequence, head) in place;
+``deltaproduct`` runs the Gated DeltaProduct recurrence (n_h substeps per token).
 Every input is widened to float64 exactly (bf16 and fp32 values are exact in
 fp64), so the oracle sees the very values a GPU kernel received.
 """
@@ -70,6 +71,9 @@ class OracleLib:
         lib.oracle_decode_step.argtypes = [i64, i64, i32, i32, i32, i32,
                                            d, d, d, d, d, d, d, i32]
         lib.oracle_decode_step.restype = i32
+        lib.oracle_deltaproduct.argtypes = [i64, i64, i64, i32, i32, i32, i32,
+                                            d, d, d, d, d, d, d, d, i32]
+        lib.oracle_deltaproduct.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         self.lib = lib
@@ -135,6 +139,39 @@ class OracleLib:
         return o, st
 
 
+def _deltaproduct(self, q, k, v, g=None, beta=None, s0=None, *, gate="scalar", nthreads: int = 0):
+    """fp64 Gated DeltaProduct recurrence (see ``oracle.c``).  Shapes: q [B,H,T,dk];
+    k [B,H,T,nh,dk]; v [B,H,T,nh,dv]; beta [B,H,T,nh]; g [B,H,T] (scalar gate)
+    or None; s0 [B,H,dk,dv].  Returns (o [B,H,T,dv], S_T [B,H,dk,dv])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g, beta, s0 = _f64(g), _f64(beta), _f64(s0)
+    B, H, T, dk = q.shape
+    nh, dv = k.shape[3], v.shape[-1]
+    if k.shape != (B, H, T, nh, dk) or v.shape != (B, H, T, nh, dv):
+        raise ValueError("k/v must be [B,H,T,nh,d]")
+    if beta is None or beta.shape != (B, H, T, nh):
+        raise ValueError("beta must be [B,H,T,nh]")
+    if gate == "scalar" and (g is None or g.shape != (B, H, T)):
+        raise ValueError("scalar gate needs g of shape [B,H,T]")
+    if gate not in ("none", "scalar"):
+        raise ValueError("Gated DeltaProduct takes no gate or a scalar gate")
+    if s0 is not None and s0.shape != (B, H, dk, dv):
+        raise ValueError("s0 must be [B,H,dk,dv]")
+    if gate == "none":
+        g = None
+    o = np.empty((B, H, T, dv), dtype=np.float64)
+    s = np.empty((B, H, dk, dv), dtype=np.float64)
+    rc = self.lib.oracle_deltaproduct(B, H, T, nh, dk, dv, GATES[gate], _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(s),
+                                      int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_deltaproduct failed with code {rc}")
+    return o, s
+
+
+OracleLib.deltaproduct = _deltaproduct
+
+
 def default() -> OracleLib:
     """The oracle built from ``oracle.c`` in this directory."""
     global _default
@@ -158,3 +195,8 @@ def recurrence(*args, **kw):
 def decode_step(*args, **kw):
     """See :meth:`OracleLib.decode_step`."""
     return default().decode_step(*args, **kw)
+
+
+def deltaproduct(*args, **kw):
+    """See :meth:`OracleLib.deltaproduct`."""
+    return default().deltaproduct(*args, **kw)

@@ -389,6 +389,96 @@ def pin_decode_and_resume(orc):
             assert rel_err(S2, S) < TOL, "resume final state"
 
 
+# ---------------------------------------------------------------------------
+# V12 Gated DeltaProduct with one substep is Gated DeltaNet
+#     ([LAV] "Gated Delta Product (GDP)": GDP replaces GDN's single transition
+#     per token by a product of n_h of them; n_h = 1 is GDN itself).
+# ---------------------------------------------------------------------------
+def pin_deltaproduct_one_substep_is_gdn(orc):
+    rng = np.random.default_rng(113)
+    B, H, T, dk, dv = 2, 2, 23, 5, 4
+    for gate in ("none", "scalar"):
+        q, k, v, g, beta, S0 = rand_case(rng, B, H, T, dk, dv, gate=gate)
+        a = orc.recurrence(q, k, v, g, beta, S0, rule="delta", gate=gate)
+        b = orc.deltaproduct(q, k[:, :, :, None], v[:, :, :, None], g, beta[..., None], S0,
+                             gate=gate)
+        assert rel_err(b[0], a[0]) < TOL and rel_err(b[1], a[1]) < TOL, \
+            f"GDP with n_h = 1 != GDN ({gate})"
+
+
+def _gdp_case(rng, B, H, T, nh, dk, dv, gate):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, nh, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, T, nh, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T, nh))))
+    g = -_softplus(rng.standard_normal((B, H, T))) * 0.5 if gate == "scalar" else None
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.5
+    return q, k, v, g, beta, S0
+
+
+# ---------------------------------------------------------------------------
+# V13 Gated DeltaProduct as a product of dense transitions on tiny inputs:
+#     S_t = H_{n_h} ... H_1 a_t S_{t-1} + sum_j H_{n_h} ... H_{j+1} beta_j k_j^T v_j,
+#     H_j = I - beta_j k_j^T k_j  ([LAV] "Gated Delta Product (GDP)": the decay
+#     before the first substep, the transitions in order, the query after the
+#     last).  Rectangular d_k != d_v.
+# ---------------------------------------------------------------------------
+def pin_deltaproduct_dense_product(orc):
+    rng = np.random.default_rng(114)
+    for (nh, dk, dv) in ((2, 3, 4), (3, 4, 2)):
+        T = 6
+        for gate in ("none", "scalar"):
+            q, k, v, g, beta, S0 = _gdp_case(rng, 1, 1, T, nh, dk, dv, gate)
+            o, S = orc.deltaproduct(q, k, v, g, beta, S0, gate=gate)
+            St = S0[0, 0].copy()
+            for t in range(T):
+                a = np.exp(g[0, 0, t]) if gate == "scalar" else 1.0
+                Hs = [np.eye(dk) - beta[0, 0, t, j] * np.outer(k[0, 0, t, j], k[0, 0, t, j])
+                      for j in range(nh)]
+                P = np.eye(dk)
+                for j in range(nh):
+                    P = Hs[j] @ P                      # H_j ... H_1
+                acc = P @ (a * St)
+                for j in range(nh):
+                    Pj = np.eye(dk)
+                    for i in range(j + 1, nh):
+                        Pj = Hs[i] @ Pj                # H_{n_h} ... H_{j+1}
+                    acc = acc + beta[0, 0, t, j] * Pj @ np.outer(k[0, 0, t, j], v[0, 0, t, j])
+                St = acc
+                assert rel_err(o[0, 0, t], q[0, 0, t] @ St) < TOL, \
+                    f"GDP dense product read-out (n_h={nh}, {gate}, t={t})"
+            assert rel_err(S[0, 0], St) < TOL, f"GDP dense product state (n_h={nh}, {gate})"
+
+
+# ---------------------------------------------------------------------------
+# V14 Gated DeltaProduct is GDN over the virtual sequence of n_h T steps
+#     ([LAV] "GDP as GDN over a virtual sequence": keys, values and correction
+#     gates flattened in order, the decay on each token's first virtual step
+#     and 1 elsewhere, the query on its last virtual step and 0 elsewhere,
+#     every n_h-th output retained).
+# ---------------------------------------------------------------------------
+def pin_deltaproduct_virtual_sequence(orc):
+    rng = np.random.default_rng(115)
+    B, H, T, nh, dk, dv = 2, 2, 9, 3, 4, 5
+    for gate in ("none", "scalar"):
+        q, k, v, g, beta, S0 = _gdp_case(rng, B, H, T, nh, dk, dv, gate)
+        o, S = orc.deltaproduct(q, k, v, g, beta, S0, gate=gate)
+        qv = np.zeros((B, H, T, nh, dk))
+        qv[:, :, :, nh - 1] = q
+        gv = None
+        if gate == "scalar":
+            gv = np.zeros((B, H, T, nh))
+            gv[:, :, :, 0] = g
+            gv = gv.reshape(B, H, T * nh)
+        ov, Sv = orc.recurrence(qv.reshape(B, H, T * nh, dk), k.reshape(B, H, T * nh, dk),
+                                v.reshape(B, H, T * nh, dv), gv, beta.reshape(B, H, T * nh), S0,
+                                rule="delta", gate=gate)
+        assert rel_err(o, ov.reshape(B, H, T, nh, dv)[:, :, :, nh - 1]) < TOL, \
+            f"GDP != GDN over the virtual sequence ({gate})"
+        assert rel_err(S, Sv) < TOL, f"GDP state != virtual-sequence state ({gate})"
+
+
 PINS = [
     pin_add_equals_masked_quadratic,
     pin_decay_equals_gamma_form,
@@ -404,4 +494,7 @@ PINS = [
     pin_equal_channels_is_scalar,
     pin_chunk_form_any_C,
     pin_decode_and_resume,
+    pin_deltaproduct_one_substep_is_gdn,
+    pin_deltaproduct_dense_product,
+    pin_deltaproduct_virtual_sequence,
 ]

@@ -37,6 +37,18 @@ MUTANTS = [
     ("ignore_initial_state", [("if (s0) memcpy(", "if (0) memcpy(")]),
     ("write_uses_v_not_u", [(WRITE, WRITE.replace("u[j]", "v[j]"))]),
     ("write_half", [(WRITE, WRITE.replace("k[i] * u[j]", "0.5 * k[i] * u[j]"))]),
+    # Gated DeltaProduct
+    ("gdp_substeps_reversed", [("for (j = 0; j < nh; ++j) {", "for (j = nh - 1; j >= 0; --j) {")]),
+    ("gdp_decay_every_substep", [("                for (i = 0; i < dk * dv; ++i) S[i] *= a;\n            }\n"
+                                  "            for (j = 0; j < nh; ++j) {",
+                                  "            }\n            for (j = 0; j < nh; ++j) {\n"
+                                  "                if (gate == ORACLE_GATE_SCALAR)\n"
+                                  "                    for (i = 0; i < dk * dv; ++i) S[i] *= exp(g[tok]);")]),
+    ("gdp_no_beta", [("w[c] = bj * (vj[c] - pred);", "w[c] = (vj[c] - pred);")]),
+    ("gdp_first_key_only", [("const double *kj = k + (tok * nh + j) * dk;",
+                             "const double *kj = k + (tok * nh) * dk;")]),
+    ("gdp_beta_of_first_substep", [("double bj = beta[tok * nh + j];", "double bj = beta[tok * nh];")]),
+    ("gdp_ignore_initial_state", [("if (s0 != NULL) memcpy(", "if (0) memcpy(")]),
 ]
 
 
