@@ -145,6 +145,44 @@ def time_chunk(la, syn, case, dev, steps, warmup=2):
             "path": chunk_path(case, wsb), "steps": steps}
 
 
+def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
+    """Event-timed Gated DeltaProduct forward (inputs resident in HBM).  Minimal
+    bytes: q and o once, k, v and beta per substep, the gate and the final
+    state; nominal FLOPs: the GDN count over the n_h T virtual steps."""
+    import torch
+    B, H, T, nh, dk, dv = case.B, case.H, case.T, case.nh, case.dk, case.dv
+    x = syn.deltaproduct_inputs_torch(case, dev)
+    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    wsb = la.deltaproduct_workspace_bytes(B, H, T, nh, dk, dv, gate=case.gate)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+    def step():
+        la.deltaproduct_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, gate=case.gate,
+                            out=out, s_final=s_fin, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    s = 2
+    abytes = B * H * T * ((dk + dv) * s + nh * (dk + dv + 1) * s + (s if case.gate == "scalar" else 0)) \
+        + B * H * dk * dv * 4
+    aflops = chunk_nominal_flops(B, H, T * nh, dk, dv, "delta")
+    return {"workload": f"gated deltaproduct n_h={nh} B={B} H={H} T={T} dk={dk} dv={dv} "
+                        f"bf16 tokens fp32 state (virtual length {T * nh})",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "path": "expand + pipe + gather", "steps": steps}
+
+
 def chunk_path(case, wsb):
     """Which chunk kernel the library runs for this case (its dispatch rule)."""
     if wsb:
@@ -171,9 +209,9 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4",
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -243,8 +281,11 @@ def main():
     del x, out, s_fin, ws
     torch.cuda.empty_cache()
     for name in names:
-        oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
-        others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))
+        if name == "gdp2":
+            others.append(time_deltaproduct(la, syn, syn.GDP2, dev, steps=10))
+        else:
+            oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
+            others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))
         torch.cuda.empty_cache()
 
     # ---------------- decode step --------------------------------------------

@@ -21,7 +21,8 @@ DTYPES = {"fp32": 0, "bf16": 1}
 
 # Every function the header declares; a test checks the two stay in step.
 EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_workspace_bytes",
-           "linattn_chunk_fwd", "linattn_decode_step")
+           "linattn_chunk_fwd", "linattn_decode_step", "linattn_deltaproduct_workspace_bytes",
+           "linattn_deltaproduct_fwd")
 
 
 class LinattnError(RuntimeError):
@@ -34,6 +35,12 @@ class ChunkArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("rule", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class DeltaProductArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("nh", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -70,6 +77,11 @@ def load(path: str = LIB_PATH):
         lib.linattn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), vp, vp, vp, vp, vp, vp,
                                             vp, vp]
         lib.linattn_decode_step.restype = ctypes.c_int
+        lib.linattn_deltaproduct_workspace_bytes.argtypes = [ctypes.POINTER(DeltaProductArgs)]
+        lib.linattn_deltaproduct_workspace_bytes.restype = sz
+        lib.linattn_deltaproduct_fwd.argtypes = [ctypes.POINTER(DeltaProductArgs), vp, vp, vp, vp, vp,
+                                                 vp, vp, vp, vp, sz, vp]
+        lib.linattn_deltaproduct_fwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -204,3 +216,60 @@ def decode_step(q, k, v, g, beta, state, *, rule="delta", gate="scalar", out=Non
     if st != 0:
         raise LinattnError(st, "linattn_decode_step")
     return out
+
+
+def deltaproduct_args(B, H, T, nh, dk, dv, *, gate, dtype, chunk=64) -> DeltaProductArgs:
+    return DeltaProductArgs(B, H, T, nh, dk, dv, chunk, GATES[gate], DTYPES[dtype])
+
+
+def deltaproduct_workspace_bytes(B, H, T, nh, dk, dv, *, gate="scalar", dtype="bf16",
+                                 chunk=64) -> int:
+    a = deltaproduct_args(B, H, T, nh, dk, dv, gate=gate, dtype=dtype, chunk=chunk)
+    return int(load().linattn_deltaproduct_workspace_bytes(ctypes.byref(a)))
+
+
+def deltaproduct_fwd(q, k, v, g=None, beta=None, s0=None, *, gate="scalar", chunk=64, out=None,
+                     s_final=None, return_state=True, workspace=None):
+    """Gated DeltaProduct forward on the GPU (n_h delta-rule substeps per token).
+
+    q [B,H,T,dk]; k [B,H,T,nh,dk]; v [B,H,T,nh,dv]; g [B,H,T] (scalar gate) or
+    None; beta [B,H,T,nh]; s0 [B,H,dk,dv] fp32 or None.  Returns
+    (o [B,H,T,dv], S_T [B,H,dk,dv] fp32 or None).  Runs on torch's current
+    stream of q's device, asynchronously.
+    """
+    import torch
+    lib = load()
+    B, H, T, dk = q.shape
+    nh, dv = k.shape[3], v.shape[-1]
+    dev, dt = q.device, q.dtype
+    dtype = _token_dtype(q)
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, nh, dk), dt, dev)
+    _check(v, "v", (B, H, T, nh, dv), dt, dev)
+    _check(beta, "beta", (B, H, T, nh), dt, dev)
+    if gate == "scalar":
+        _check(g, "g", (B, H, T), dt, dev)
+    elif gate != "none" or g is not None:
+        raise ValueError("Gated DeltaProduct takes gate='scalar' with g, or gate='none'")
+    if s0 is not None:
+        _check(s0, "s0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    if s_final is None and return_state:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif s_final is not None:
+        _check(s_final, "s_final", (B, H, dk, dv), torch.float32, dev)
+    a = deltaproduct_args(B, H, T, nh, dk, dv, gate=gate, dtype=dtype, chunk=chunk)
+    need = int(lib.linattn_deltaproduct_workspace_bytes(ctypes.byref(a)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_deltaproduct_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(s0), _ptr(out), _ptr(s_final), _ptr(workspace), ws_bytes,
+                                      stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_deltaproduct_fwd")
+    return out, s_final

@@ -33,6 +33,20 @@ struct ChunkProblem {
 
 hipError_t launch_decode_step(const DecodeProblem& p, hipStream_t stream);
 
+// Gated DeltaProduct over its virtual sequence: the expanded query and
+// log-gate (qv [B,H,T*nh,dk], gv [B,H,T*nh] or NULL), and the gather of every
+// nh-th output of the virtual sequence (ov [B,H,T*nh,dv]) into o [B,H,T,dv].
+struct DeltaProductProblem {
+    int64_t B, H, T;
+    int nh, dk, dv, dtype;
+    const void *q, *g;
+    void *qv, *gv;
+    const void* ov;
+    void* o;
+};
+hipError_t launch_dp_expand(const DeltaProductProblem& p, hipStream_t stream);
+hipError_t launch_dp_gather(const DeltaProductProblem& p, hipStream_t stream);
+
 // Single-pass chunk kernel (gate NONE or SCALAR), three phases per chunk.
 bool chunk_fused_supported(const ChunkProblem& p);
 hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t stream);

@@ -88,6 +88,52 @@ linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
     return LINATTN_OK;
 }
 
+// Initial and final state: 16-byte aligned; s_final may alias s0 exactly, but
+// must not partially overlap it.
+linattn_status check_states(const ChunkProblem& p, const float* s0, const float* s_final)
+{
+    if ((s0 && !aligned16(s0)) || (s_final && !aligned16(s_final))) return LINATTN_ERR_UNSUPPORTED;
+    if (s0 && s_final && s0 != s_final) {
+        const char* a0 = reinterpret_cast<const char*>(s0);
+        const char* a1 = reinterpret_cast<const char*>(s_final);
+        const size_t n = (size_t)(p.B * p.H) * p.dk * p.dv * sizeof(float);
+        if (a0 < a1 + n && a1 < a0 + n) return LINATTN_ERR_ARG;
+    }
+    return LINATTN_OK;
+}
+
+// Gated DeltaProduct: the virtual GDN problem (n_h T steps) it runs as.
+linattn_status validate_dp(const linattn_deltaproduct_args* a, linattn_chunk_args* va, ChunkProblem* vp)
+{
+    if (!a) return LINATTN_ERR_NULL;
+    if (a->nh < 1 || a->T < 0) return LINATTN_ERR_SHAPE;
+    if (a->gate == LINATTN_GATE_CHANNEL) return LINATTN_ERR_UNSUPPORTED;
+    int64_t tv;
+    if (!mul_ok(a->T, (int64_t)a->nh, &tv)) return LINATTN_ERR_SHAPE;
+    *va = linattn_chunk_args{a->B, a->H, tv, a->dk, a->dv, a->chunk, LINATTN_RULE_DELTA, a->gate, a->dtype};
+    return validate_chunk(va, vp);
+}
+
+// Workspace of an n_h > 1 problem, 256-byte aligned pieces: expanded queries
+// [B,H,T*nh,dk], expanded log-gates [B,H,T*nh] (scalar gate), virtual outputs
+// [B,H,T*nh,dv], then whatever the chunk path needs.
+struct DpLayout {
+    size_t qv, gv, ov, cws, total;
+};
+DpLayout dp_layout(const linattn_chunk_args& va, const ChunkProblem& vp)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t esz = va.dtype == LINATTN_BF16 ? 2 : 4;
+    const size_t steps = (size_t)(va.B * va.H) * (size_t)va.T;
+    DpLayout l{};
+    l.qv = 0;
+    l.gv = up(steps * va.dk * esz);
+    l.ov = l.gv + (va.gate == LINATTN_GATE_SCALAR ? up(steps * esz) : 0);
+    l.cws = l.ov + up(steps * va.dv * esz);
+    l.total = l.cws + (use_split(vp) ? chunk_split_workspace_bytes(vp) : 0);
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,14 +176,8 @@ linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, con
         st = check_pointers(p.rule, p.gate, q, k, v, g, beta, q, o);
         if (st != LINATTN_OK) return st;
     }
-    if ((s0 && !aligned16(s0)) || (s_final && !aligned16(s_final))) return LINATTN_ERR_UNSUPPORTED;
-    // s_final may alias s0 exactly, but must not partially overlap it
-    if (s0 && s_final && s0 != s_final) {
-        const char* a0 = reinterpret_cast<const char*>(s0);
-        const char* a1 = reinterpret_cast<const char*>(s_final);
-        const size_t n = (size_t)(p.B * p.H) * p.dk * p.dv * sizeof(float);
-        if (a0 < a1 + n && a1 < a0 + n) return LINATTN_ERR_ARG;
-    }
+    st = check_states(p, s0, s_final);
+    if (st != LINATTN_OK) return st;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = s0; p.o = o; p.s_final = s_final;
     p.workspace = workspace; p.workspace_bytes = workspace_bytes;
@@ -176,6 +216,51 @@ linattn_status linattn_decode_step(const linattn_decode_args* a, const void* q, 
                     q, k, v, g, beta, state, o};
     hipError_t err = launch_decode_step(p, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+}
+
+size_t linattn_deltaproduct_workspace_bytes(const linattn_deltaproduct_args* a)
+{
+    linattn_chunk_args va{};
+    ChunkProblem vp{};
+    if (validate_dp(a, &va, &vp) != LINATTN_OK) return 0;
+    if (a->nh == 1) return linattn_chunk_workspace_bytes(&va);
+    return dp_layout(va, vp).total;
+}
+
+linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args* a, const void* q, const void* k,
+                                        const void* v, const void* g, const void* beta, const float* s0,
+                                        void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                                        void* stream)
+{
+    linattn_chunk_args va{};
+    ChunkProblem vp{};
+    linattn_status st = validate_dp(a, &va, &vp);
+    if (st != LINATTN_OK) return st;
+    // one substep per token: the virtual sequence is the sequence itself
+    if (a->nh == 1)
+        return linattn_chunk_fwd(&va, q, k, v, g, beta, s0, o, s_final, workspace, workspace_bytes, stream);
+    if (vp.B * vp.H == 0) return LINATTN_OK;
+    const DpLayout l = dp_layout(va, vp);
+    st = check_states(vp, s0, s_final);
+    if (st != LINATTN_OK) return st;
+    if (a->T > 0) {
+        st = check_pointers(LINATTN_RULE_DELTA, a->gate, q, k, v, g, beta, q, o);
+        if (st != LINATTN_OK) return st;
+        if (!workspace || workspace_bytes < l.total) return LINATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    DeltaProductProblem p{a->B, a->H, a->T, a->nh, a->dk, a->dv, a->dtype, q, g,
+                          a->T > 0 ? ws + l.qv : nullptr,
+                          a->T > 0 && a->gate == LINATTN_GATE_SCALAR ? ws + l.gv : nullptr,
+                          a->T > 0 ? ws + l.ov : nullptr, o};
+    if (a->T > 0 && launch_dp_expand(p, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+    st = linattn_chunk_fwd(&va, p.qv, k, v, p.gv, beta, s0, a->T > 0 ? ws + l.ov : nullptr, s_final,
+                           a->T > 0 ? ws + l.cws : nullptr, a->T > 0 ? workspace_bytes - l.cws : 0, stream);
+    if (st != LINATTN_OK) return st;
+    if (a->T > 0 && launch_dp_gather(p, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+    return LINATTN_OK;
 }
 
 }  // extern "C"

@@ -121,6 +121,50 @@ linattn_status linattn_chunk_fwd(const linattn_chunk_args *a,
                                  const float *s0, void *o, float *s_final,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Gated DeltaProduct problem description: n_h delta-rule substeps per token.
+ * gate holds LINATTN_GATE_NONE or LINATTN_GATE_SCALAR; dtype as above. */
+typedef struct {
+    int64_t B, H, T;   /* batch, heads, tokens per sequence (T >= 0) */
+    int32_t nh;        /* substeps per token (>= 1) */
+    int32_t dk, dv;    /* key and value head sizes */
+    int32_t chunk;     /* tokens per chunk of the virtual sequence; 0 = 64 */
+    int32_t gate, dtype;
+} linattn_deltaproduct_args;
+
+/*
+ * Device workspace, in bytes, that linattn_deltaproduct_fwd needs: for n_h > 1
+ * the expanded queries and log-gates and the n_h T virtual outputs (plus what
+ * the chunk path needs for them); for n_h = 1 what linattn_chunk_fwd needs.
+ * Returns 0 for invalid arguments as well.
+ */
+size_t linattn_deltaproduct_workspace_bytes(const linattn_deltaproduct_args *a);
+
+/*
+ * Gated DeltaProduct forward ("Linear Attention, Visualized", "Gated Delta
+ * Product (GDP)"): token t decays the state once by a_t = exp(g_t), then
+ * applies n_h delta-rule substeps in order, substep j with key k_{t,j}, value
+ * v_{t,j} and correction gate beta_{t,j}; the query reads the state after the
+ * last substep.  Computed as Gated DeltaNet over the virtual sequence of n_h T
+ * steps ("GDP as GDN over a virtual sequence") by the chunk kernels.
+ *
+ *   q        [B,H,T,dk]              token dtype
+ *   k        [B,H,T,nh,dk]           token dtype
+ *   v        [B,H,T,nh,dv]           token dtype
+ *   g        [B,H,T] (SCALAR) | NULL (NONE); log-gate, token dtype
+ *   beta     [B,H,T,nh]              token dtype
+ *   s0, o, s_final, stream: as for linattn_chunk_fwd
+ *   workspace, workspace_bytes: at least
+ *            linattn_deltaproduct_workspace_bytes(a) bytes, 16-byte aligned
+ * Supported: as linattn_chunk_fwd for the delta rule with the virtual length
+ * n_h T (so one head's virtual output must stay under 2 GiB); the channel
+ * gate is not supported (LINATTN_ERR_UNSUPPORTED).
+ */
+linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args *a,
+                                        const void *q, const void *k, const void *v,
+                                        const void *g, const void *beta,
+                                        const float *s0, void *o, float *s_final,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * One recurrent decode step for N sequences x H heads, updating the state in
  * place ("Linear Attention, Visualized", "Optional: Linear attention as an

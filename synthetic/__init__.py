@@ -194,6 +194,87 @@ def iter_heads(case: Case, seed: int = SEED) -> Iterable[tuple]:
             yield (b, h), head_inputs(case, b, h, seed)
 
 
+@dataclasses.dataclass(frozen=True)
+class DeltaProductCase:
+    """A Gated DeltaProduct workload: nh (key, value, beta) substeps per token."""
+    name: str
+    B: int
+    H: int
+    T: int
+    nh: int
+    dk: int
+    dv: int
+    gate: str = "scalar"         # "none" | "scalar"
+    dtype: str = "bf16"
+    gate_scale: float = 1.0
+    s0_std: float = 0.0
+    case_id: int = 6
+
+    def with_(self, **kw) -> "DeltaProductCase":
+        return dataclasses.replace(self, **kw)
+
+
+# Gated DeltaProduct with two substeps at the GDN workload's head size
+# (virtual length 2 T = 8192, the GDN workload's sequence length)
+GDP2 = DeltaProductCase("gdp2_fwd_B8_H16_T4096_d128_bf16", 8, 16, 4096, 2, 128, 128, case_id=6)
+
+
+def deltaproduct_head_inputs(case: DeltaProductCase, b: int, h: int, seed: int = SEED) -> dict:
+    """Inputs of one head: q [T,dk]; k [T,nh,dk] and q L2-normalised per
+    (token, substep); v [T,nh,dv] N(0,1); beta [T,nh] sigmoid(N(0,1));
+    g [T] -softplus(N(0,1)) * gate_scale or None; s0 [dk,dv] or None.  Draw
+    order q, k, v, beta-logits, gate-logits, initial state."""
+    rng = np.random.default_rng([seed, case.case_id, b, h])
+    T, nh, dk, dv = case.T, case.nh, case.dk, case.dv
+    q = to_dtype(_qk(rng, (T, dk), "l2"), case.dtype)
+    k = to_dtype(_qk(rng, (T, nh, dk), "l2"), case.dtype)
+    v = to_dtype(rng.standard_normal((T, nh, dv), dtype=np.float32), case.dtype)
+    beta = to_dtype(_beta(rng, (T, nh), "sigmoid"), case.dtype)
+    g = to_dtype(-_softplus(rng.standard_normal((T,), dtype=np.float32))
+                 * np.float32(case.gate_scale), case.dtype)
+    s0 = None
+    if case.s0_std > 0:
+        s0 = (rng.standard_normal((dk, dv), dtype=np.float32)
+              * np.float32(case.s0_std)).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "beta": beta,
+            "g": None if case.gate == "none" else g, "s0": s0}
+
+
+def deltaproduct_inputs(case: DeltaProductCase, heads: Optional[Sequence[tuple]] = None,
+                        seed: int = SEED) -> dict:
+    """All heads ([B,H,...] arrays) or the listed (b,h) heads ([n,...] arrays)."""
+    idx = [(b, h) for b in range(case.B) for h in range(case.H)] if heads is None else list(heads)
+    parts = [deltaproduct_head_inputs(case, b, h, seed) for (b, h) in idx]
+    out = {}
+    for key in ("q", "k", "v", "g", "beta", "s0"):
+        if parts[0][key] is None:
+            out[key] = None
+            continue
+        arr = np.stack([p[key] for p in parts])
+        if heads is None:
+            arr = arr.reshape((case.B, case.H) + arr.shape[1:])
+        out[key] = arr
+    return out
+
+
+def deltaproduct_inputs_torch(case: DeltaProductCase, device, seed: int = SEED) -> dict:
+    """The same laws drawn with torch's device generator (large workloads)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000 + case.case_id)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    shp = (case.B, case.H, case.T)
+    rn = lambda *s: torch.randn(*s, generator=gen, device=device, dtype=torch.float32)
+    out = {"q": _torch_laws(rn(*shp, case.dk), "l2").to(dt),
+           "k": _torch_laws(rn(*shp, case.nh, case.dk), "l2").to(dt),
+           "v": rn(*shp, case.nh, case.dv).to(dt),
+           "beta": torch.sigmoid(rn(*shp, case.nh)).to(dt)}
+    g = -torch.nn.functional.softplus(rn(*shp)) * case.gate_scale
+    out["g"] = None if case.gate == "none" else g.to(dt)
+    out["s0"] = None
+    return out
+
+
 def decode_state(case: DecodeCase, seed: int = SEED) -> np.ndarray:
     rng = np.random.default_rng([seed, case.case_id, 1 << 20])
     s = rng.standard_normal((case.N, case.H, case.dk, case.dv), dtype=np.float32)

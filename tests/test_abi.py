@@ -80,6 +80,32 @@ def test_chunk_validation(lib):
     assert call_chunk(lib, mk(gate="channel", dtype="fp32"), g=FAKE) == 3
 
 
+def test_deltaproduct_validation(lib):
+    mk = lambda **kw: bd.deltaproduct_args(**{**dict(B=1, H=1, T=64, nh=2, dk=64, dv=64,
+                                                     gate="scalar", dtype="bf16"), **kw})
+    call = lambda a, **p: lib.linattn_deltaproduct_fwd(
+        ctypes.byref(a), *[p.get(n, FAKE) for n in ("q", "k", "v", "g", "beta")], p.get("s0"),
+        p.get("o", FAKE), p.get("sf"), p.get("ws"), p.get("wsb", 0), None)
+    assert lib.linattn_deltaproduct_fwd(None, *([None] * 9), 0, None) == 1
+    assert call(mk(nh=0)) == 2
+    assert call(mk(T=-1)) == 2
+    assert call(mk(gate="channel")) == 3                          # no per-channel gate
+    assert call(mk(dk=96)) == 3
+    assert call(mk(), q=None) == 1
+    assert call(mk(), beta=None) == 1
+    assert call(mk(gate="none")) == 6                             # g given without a gate
+    assert call(mk(), s0=FAKE, sf=FAKE + 16) == 6                 # partial state overlap
+    assert call(mk()) == 4                                        # workspace missing
+    assert call(mk(T=1 << 22, nh=4, dv=128)) == 3                 # virtual output >= 2 GiB
+    assert call(mk(B=0)) == 0
+    # expanded queries + expanded gates + virtual outputs, 256-byte pieces
+    assert lib.linattn_deltaproduct_workspace_bytes(ctypes.byref(mk())) == \
+        128 * 64 * 2 + 256 + 128 * 64 * 2
+    assert lib.linattn_deltaproduct_workspace_bytes(ctypes.byref(mk(gate="none"))) == \
+        128 * 64 * 2 * 2
+    assert lib.linattn_deltaproduct_workspace_bytes(ctypes.byref(mk(nh=1))) == 0
+
+
 def test_decode_validation(lib):
     mk = lambda **kw: bd.DecodeArgs(*[{**dict(N=2, H=2, dk=64, dv=64, rule=1, gate=1, dtype=1),
                                         **kw}[f] for f in ("N", "H", "dk", "dv", "rule", "gate",
