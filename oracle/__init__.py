@@ -3,5 +3,6 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package.  It shares no code with the HIP library.
 """
-from .oracle import (GATES, RULES, OracleLib, build, decode_step, default,  # noqa: F401
-                     deltaproduct, max_threads, recurrence)
+from .oracle import (BETA_MAPS, GATE_MAPS, GATES, QK_MAPS, RULES, OracleLib,  # noqa: F401
+                     build, decode_step, default, deltaproduct, max_threads, prepare_beta,
+                     prepare_gate, prepare_qk, recurrence)

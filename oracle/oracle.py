@@ -172,6 +172,47 @@ def _deltaproduct(self, q, k, v, g=None, beta=None, s0=None, *, gate="scalar", n
 OracleLib.deltaproduct = _deltaproduct
 
 
+# Input preparation from raw projections, fp64 ([ASF] "DeltaNet": keys and
+# queries L2-normalised per token and the write strength beta a sigmoid;
+# "Linear Magic": the positive feature map elu + 1; [LAV] "Mamba-2" and "Gated
+# DeltaNet (GDN)": the forget gate alpha = exp(-softplus(x)) in (0, 1), so the
+# log-gate is -softplus(x)).  L2 uses x / max(|x|, 1e-6).
+QK_MAPS = ("identity", "l2", "elu1")
+GATE_MAPS = ("log", "neg_softplus")
+BETA_MAPS = ("identity", "sigmoid")
+L2_EPS = 1e-6
+
+
+def prepare_qk(x, qk_map):
+    x = _f64(x)
+    if qk_map == "identity":
+        return x
+    if qk_map == "l2":
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return x / np.maximum(n, L2_EPS)
+    if qk_map == "elu1":
+        return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    raise ValueError(f"unknown q/k map {qk_map!r}")
+
+
+def prepare_gate(g, gate_map):
+    g = _f64(g)
+    if g is None or gate_map == "log":
+        return g
+    if gate_map == "neg_softplus":
+        return -(np.maximum(g, 0.0) + np.log1p(np.exp(-np.abs(g))))
+    raise ValueError(f"unknown gate map {gate_map!r}")
+
+
+def prepare_beta(beta, beta_map):
+    beta = _f64(beta)
+    if beta is None or beta_map == "identity":
+        return beta
+    if beta_map == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-beta))
+    raise ValueError(f"unknown beta map {beta_map!r}")
+
+
 def default() -> OracleLib:
     """The oracle built from ``oracle.c`` in this directory."""
     global _default
