@@ -145,6 +145,45 @@ def time_chunk(la, syn, case, dev, steps, warmup=2):
             "path": chunk_path(case, wsb), "steps": steps}
 
 
+def time_prep(la, case, dev, steps, warmup=2):
+    """Event-timed chunk forward from raw projections with the input
+    preparation fused into the kernel (q, k L2-normalised, log-gate
+    -softplus, beta sigmoid), at the shape of ``case``; raw inputs drawn on the
+    device (q, k N(0,1) * 2, gate and beta logits N(0,1))."""
+    import torch
+    B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(27 * 1000 + 77)
+    rn = lambda *sh: torch.randn(*sh, generator=gen, device=dev, dtype=torch.float32)
+    q, k = (rn(B, H, T, dk) * 2).bfloat16(), (rn(B, H, T, dk) * 2).bfloat16()
+    v, g, beta = rn(B, H, T, dv).bfloat16(), rn(B, H, T).bfloat16(), rn(B, H, T).bfloat16()
+    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        la.chunk_fwd(q, k, v, g, beta, None, rule="delta", gate="scalar", out=out, s_final=s_fin,
+                     qk_map="l2", gate_map="neg_softplus", beta_map="sigmoid")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    abytes = chunk_alg_bytes(B, H, T, dk, dv, 2, "delta", "scalar")
+    aflops = chunk_nominal_flops(B, H, T, dk, dv, "delta")
+    return {"workload": f"gdn chunk_fwd from raw projections (fused L2 q/k, -softplus gate, "
+                        f"sigmoid beta) B={B} H={H} T={T} dk={dk} dv={dv} bf16",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "path": "pipe with input preparation", "steps": steps}
+
+
 def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
     """Event-timed Gated DeltaProduct forward (inputs resident in HBM).  Minimal
     bytes: q and o once, k, v and beta per substep, the gate and the final
@@ -209,9 +248,9 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2",
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4, gdp2), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -283,6 +322,8 @@ def main():
     for name in names:
         if name == "gdp2":
             others.append(time_deltaproduct(la, syn, syn.GDP2, dev, steps=10))
+        elif name == "cfg3prep":
+            others.append(time_prep(la, syn.CFG3, dev, steps=10))
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
             others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))

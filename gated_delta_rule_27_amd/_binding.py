@@ -22,7 +22,10 @@ DTYPES = {"fp32": 0, "bf16": 1}
 # Every function the header declares; a test checks the two stay in step.
 EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_workspace_bytes",
            "linattn_chunk_fwd", "linattn_decode_step", "linattn_deltaproduct_workspace_bytes",
-           "linattn_deltaproduct_fwd")
+           "linattn_deltaproduct_fwd", "linattn_chunk_fwd_prep")
+QK_MAPS = {"as_is": 0, "l2": 1, "elu1": 2}
+GATE_MAPS = {"as_is": 0, "neg_softplus": 1}
+BETA_MAPS = {"as_is": 0, "sigmoid": 1}
 
 
 class LinattnError(RuntimeError):
@@ -35,6 +38,11 @@ class ChunkArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("rule", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class PrepArgs(ctypes.Structure):
+    _fields_ = [("qk_map", ctypes.c_int32), ("gate_map", ctypes.c_int32),
+                ("beta_map", ctypes.c_int32)]
 
 
 class DeltaProductArgs(ctypes.Structure):
@@ -82,6 +90,9 @@ def load(path: str = LIB_PATH):
         lib.linattn_deltaproduct_fwd.argtypes = [ctypes.POINTER(DeltaProductArgs), vp, vp, vp, vp, vp,
                                                  vp, vp, vp, vp, sz, vp]
         lib.linattn_deltaproduct_fwd.restype = ctypes.c_int
+        lib.linattn_chunk_fwd_prep.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.POINTER(PrepArgs),
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.linattn_chunk_fwd_prep.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -130,13 +141,17 @@ def chunk_workspace_bytes(B, H, T, dk, dv, *, rule, gate, dtype="bf16", chunk=64
 
 
 def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar", chunk=64,
-              out=None, s_final=None, return_state=True, workspace=None):
+              out=None, s_final=None, return_state=True, workspace=None, qk_map="as_is",
+              gate_map="as_is", beta_map="as_is"):
     """Chunkwise forward over whole sequences on the GPU.
 
     q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] (scalar gate) or [B,H,T,dk]
     (channel gate) or None; beta [B,H,T] (delta rule) or None; s0
     [B,H,dk,dv] fp32 or None.  Returns (o [B,H,T,dv], S_T [B,H,dk,dv] fp32 or
     None).  Runs on torch's current stream of q's device, asynchronously.
+    qk_map ("as_is" | "l2" | "elu1"), gate_map ("as_is" | "neg_softplus") and
+    beta_map ("as_is" | "sigmoid") treat q/k, g and beta as raw projections
+    mapped inside the kernel (linattn_chunk_fwd_prep).
     """
     import torch
     lib = load()
@@ -173,11 +188,19 @@ def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib.linattn_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                               _ptr(s0), _ptr(out), _ptr(s_final), _ptr(workspace), ws_bytes,
-                               stream)
+    if (qk_map, gate_map, beta_map) == ("as_is", "as_is", "as_is"):
+        st = lib.linattn_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(s0), _ptr(out), _ptr(s_final), _ptr(workspace), ws_bytes,
+                                   stream)
+        what = "linattn_chunk_fwd"
+    else:
+        pa = PrepArgs(QK_MAPS[qk_map], GATE_MAPS[gate_map], BETA_MAPS[beta_map])
+        st = lib.linattn_chunk_fwd_prep(ctypes.byref(a), ctypes.byref(pa), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(g), _ptr(beta), _ptr(s0), _ptr(out), _ptr(s_final),
+                                        _ptr(workspace), ws_bytes, stream)
+        what = "linattn_chunk_fwd_prep"
     if st != 0:
-        raise LinattnError(st, "linattn_chunk_fwd")
+        raise LinattnError(st, what)
     return out, s_final
 
 

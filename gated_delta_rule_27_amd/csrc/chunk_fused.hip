@@ -53,6 +53,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
+#include "prep.h"
 #include "tsolve.h"
 
 namespace linattn {
@@ -94,7 +95,7 @@ template <typename T, int DK, int RULE, int GATE>
 __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const float* s0, T* __restrict__ o,
-    float* s_final, int64_t Tlen, int DV, int nblocks)
+    float* s_final, int64_t Tlen, int DV, int nblocks, int prep)
 {
     using Cfg = FusedCfg<T, DK, RULE, GATE>;
     using F = typename Frag16<T>::type;
@@ -168,15 +169,20 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
     };
     // Q and K rows go to LDS with their columns in pcol order (mfma.h), 8 bytes
-    // (four columns) at a time for bf16
+    // (four columns) at a time for bf16; raw projections first go through the
+    // q/k map of prep.h, and rows past the end are zeroed after it
     auto stage = [&](int64_t t0) {
+        const int qk_map = prep_qk_map(prep);
 #pragma unroll
         for (int p = 0; p < NQ; ++p) {
             const int idx = (p * kNT + tid) * E;
             const int row = idx / DK, col = idx % DK;
             const bool ok = t0 + row < Tlen;
-            const i4 qv = ok ? qreg[p] : i4{0, 0, 0, 0};
-            const i4 kv = ok ? kreg[p] : i4{0, 0, 0, 0};
+            // every lane maps its vector (the L2 norm is reduced across lanes)
+            const i4 qp = prep_qk<T, DK / E>(qreg[p], qk_map);
+            const i4 kp = prep_qk<T, DK / E>(kreg[p], qk_map);
+            const i4 qv = ok ? qp : i4{0, 0, 0, 0};
+            const i4 kv = ok ? kp : i4{0, 0, 0, 0};
             if constexpr (E == 8) {
                 typedef __attribute__((__vector_size__(8))) int i2;
                 *reinterpret_cast<i2*>(&Qs[row * LDQ + pcol(col)]) = i2{qv[0], qv[1]};
@@ -553,12 +559,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 // G is kept in base 2 (log2 e * prefix sum) so every decay factor
                 // is one hardware exp2
                 const bool ok = t0 + lane < Tlen;
-                const float G = wave_prefix_sum((GATED && ok) ? to_f32(greg) * kLog2e : 0.f);
+                const float G = wave_prefix_sum((GATED && ok) ? prep_gate(to_f32(greg), prep) * kLog2e : 0.f);
                 const float Glast = wave_last(G);
                 Gs[lane] = G;
                 gamb[r & 1][lane] = GATED ? fast_exp2(G) : 1.f;
                 rhob[r & 1][lane] = GATED ? fast_exp2(Glast - G) : 1.f;
-                bet[lane] = (DELTA && ok) ? to_f32(breg) : 0.f;
+                bet[lane] = (DELTA && ok) ? prep_beta(to_f32(breg), prep) : 0.f;
             }
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
             fetch_gate(t0 + kC < tlast ? t0 + kC : tlast);
@@ -650,7 +656,7 @@ hipError_t launch_t(const ChunkProblem& p, hipStream_t s)
                        s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
                        static_cast<const T*>(p.v), static_cast<const T*>(p.g),
                        static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, p.T,
-                       p.dv, (int)nblocks);
+                       p.dv, (int)nblocks, p.prep);
     return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
+#include "prep.h"
 #include "tsolve.h"
 
 namespace linattn {
@@ -91,7 +92,7 @@ template <int DK, int RULE, int GATE>
 __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const float* s0, bf16* __restrict__ o,
-    float* s_final, int64_t Tlen, int DV, int nblocks)
+    float* s_final, int64_t Tlen, int DV, int nblocks, int prep)
 {
     using T = bf16;
     using Cfg = PipeCfg<DK, RULE, GATE>;
@@ -180,15 +181,21 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     };
     // Q and K rows go to LDS with their columns in pcol order (mfma.h), four
     // columns (8 bytes) at a time
+    // (raw projections first go through the q/k map of prep.h; rows past the
+    // end are zeroed after it)
     auto stage_qk = [&](const Pref& P, int64_t t0, T* Qb, T* Kb) {
         typedef __attribute__((__vector_size__(8))) int i2;
+        const int qk_map = prep_qk_map(prep);
 #pragma unroll
         for (int p = 0; p < NQ; ++p) {
             const int idx = (p * kNS + st) * E;
             const int row = idx / DK, col = idx % DK;
             const bool ok = t0 + row < Tlen;
-            const i4 qv = ok ? P.q[p] : i4{0, 0, 0, 0};
-            const i4 kv = ok ? P.k[p] : i4{0, 0, 0, 0};
+            // every lane maps its vector (the L2 norm is reduced across lanes)
+            const i4 qp = prep_qk<T, DK / E>(P.q[p], qk_map);
+            const i4 kp = prep_qk<T, DK / E>(P.k[p], qk_map);
+            const i4 qv = ok ? qp : i4{0, 0, 0, 0};
+            const i4 kv = ok ? kp : i4{0, 0, 0, 0};
             *reinterpret_cast<i2*>(&Qb[row * LDQ + pcol(col)]) = i2{qv[0], qv[1]};
             *reinterpret_cast<i2*>(&Qb[row * LDQ + pcol(col + 4)]) = i2{qv[2], qv[3]};
             *reinterpret_cast<i2*>(&Kb[row * LDQ + pcol(col)]) = i2{kv[0], kv[1]};
@@ -208,12 +215,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     // (log2 e * prefix sum) so every decay factor is one hardware exp2.
     auto scan = [&](const Pref& P, int64_t t0, int sl) {
         const bool ok = t0 + lane < Tlen;
-        const float G = wave_prefix_sum((GATED && ok) ? to_f32(P.g) * kLog2e : 0.f);
+        const float G = wave_prefix_sum((GATED && ok) ? prep_gate(to_f32(P.g), prep) * kLog2e : 0.f);
         const float Glast = wave_last(G);
         Gsb[sl][lane] = G;
         gamb[sl][lane] = GATED ? fast_exp2(G) : 1.f;
         rhob[sl][lane] = GATED ? fast_exp2(Glast - G) : 1.f;
-        betb[sl][lane] = (DELTA && ok) ? to_f32(P.b) : 0.f;
+        betb[sl][lane] = (DELTA && ok) ? prep_beta(to_f32(P.b), prep) : 0.f;
     };
 
     // The output of chunk r is staged in LDS (Os) by the state waves and written
@@ -642,7 +649,7 @@ hipError_t launch_t(const ChunkProblem& p, hipStream_t s)
                        static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                        static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.g),
                        static_cast<const bf16*>(p.beta), p.s0, static_cast<bf16*>(p.o), p.s_final, p.T,
-                       p.dv, (int)nblocks);
+                       p.dv, (int)nblocks, p.prep);
     return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ struct ChunkProblem {
     float* s_final;
     void* workspace;
     size_t workspace_bytes;
+    int prep;          // input preparation flags (prep.h); the single-pass kernels only
 };
 
 hipError_t launch_decode_step(const DecodeProblem& p, hipStream_t stream);

@@ -29,7 +29,7 @@ ChunkPath chunk_path(const ChunkProblem& p)
 {
     if (p.gate == kGateChannel) return kPathSplit;
     const char* e = getenv("LINATTN_CHUNK_PATH");
-    if (e && strcmp(e, "split") == 0 && chunk_split_supported(p)) return kPathSplit;
+    if (e && strcmp(e, "split") == 0 && p.prep == 0 && chunk_split_supported(p)) return kPathSplit;
     if (e && strcmp(e, "fused") == 0 && chunk_fused_supported(p)) return kPathFused;
     if (e && strcmp(e, "pipe") == 0 && chunk_pipe_supported(p)) return kPathPipe;
     return p.dtype == kBF16 && p.rule == kRuleDelta ? kPathPipe : kPathFused;
@@ -60,7 +60,24 @@ linattn_status check_pointers(int rule, int gate, const void* q, const void* k, 
     return LINATTN_OK;
 }
 
-linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
+// Input-preparation maps as the kernels' packed flags (prep.h): bits 0-1 the
+// q/k map, bit 2 the gate map, bit 3 the beta map.
+linattn_status prep_flags(const linattn_prep_args* pa, int rule, int gate, int* out)
+{
+    *out = 0;
+    if (!pa) return LINATTN_OK;
+    if (pa->qk_map < LINATTN_QK_AS_IS || pa->qk_map > LINATTN_QK_ELU1 ||
+        (pa->gate_map != LINATTN_GMAP_AS_IS && pa->gate_map != LINATTN_GMAP_NEG_SOFTPLUS) ||
+        (pa->beta_map != LINATTN_BMAP_AS_IS && pa->beta_map != LINATTN_BMAP_SIGMOID))
+        return LINATTN_ERR_ARG;
+    if (pa->gate_map != LINATTN_GMAP_AS_IS && gate == LINATTN_GATE_NONE) return LINATTN_ERR_ARG;
+    if (pa->beta_map != LINATTN_BMAP_AS_IS && rule == LINATTN_RULE_ADD) return LINATTN_ERR_ARG;
+    *out = pa->qk_map | (pa->gate_map << 2) | (pa->beta_map << 3);
+    return LINATTN_OK;
+}
+
+linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p,
+                              const linattn_prep_args* prep = nullptr)
 {
     if (!a) return LINATTN_ERR_NULL;
     if (a->B < 0 || a->H < 0 || a->T < 0 || a->dk <= 0 || a->dv <= 0 || a->chunk < 0)
@@ -76,7 +93,11 @@ linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p)
     p->dk = a->dk; p->dv = a->dv;
     p->chunk = a->chunk == 0 ? 64 : a->chunk;
     p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
+    st = prep_flags(prep, a->rule, a->gate, &p->prep);
+    if (st != LINATTN_OK) return st;
     const ChunkPath path = chunk_path(*p);
+    // the two-kernel path stages prepared operands already; it takes no maps
+    if (path == kPathSplit && p->prep != 0) return LINATTN_ERR_UNSUPPORTED;
     const bool ok = path == kPathSplit ? chunk_split_supported(*p)
                   : path == kPathPipe  ? chunk_pipe_supported(*p)
                                        : chunk_fused_supported(*p);
@@ -166,8 +187,17 @@ linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, con
                                  void* o, float* s_final, void* workspace, size_t workspace_bytes,
                                  void* stream)
 {
+    return linattn_chunk_fwd_prep(a, nullptr, q, k, v, g, beta, s0, o, s_final, workspace,
+                                  workspace_bytes, stream);
+}
+
+linattn_status linattn_chunk_fwd_prep(const linattn_chunk_args* a, const linattn_prep_args* prep,
+                                      const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta, const float* s0, void* o, float* s_final,
+                                      void* workspace, size_t workspace_bytes, void* stream)
+{
     ChunkProblem p{};
-    linattn_status st = validate_chunk(a, &p);
+    linattn_status st = validate_chunk(a, &p, prep);
     if (st != LINATTN_OK) return st;
     if (p.B * p.H == 0) return LINATTN_OK;
     // q,k,v,o may be absent only when there are no tokens; pass q as the

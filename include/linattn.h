@@ -121,6 +121,37 @@ linattn_status linattn_chunk_fwd(const linattn_chunk_args *a,
                                  const float *s0, void *o, float *s_final,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Input preparation from raw projections, fused into the chunk forward
+ * (linattn_chunk_fwd_prep): "All sorts of famous Attention Layers", "DeltaNet"
+ * (keys and queries L2-normalised per token, x / max(|x|, 1e-6); beta a
+ * sigmoid) and "Linear Magic" (the positive feature map elu(x) + 1); "Linear
+ * Attention, Visualized", "Mamba-2" / "Gated DeltaNet (GDN)" (forget gate
+ * exp(-softplus(x)) in (0, 1), i.e. log-gate -softplus(x)).  The maps run in
+ * fp32 on the raw values as the kernel stages them; the prepared q and k are
+ * then rounded to the token dtype once. */
+typedef enum { LINATTN_QK_AS_IS = 0, LINATTN_QK_L2 = 1, LINATTN_QK_ELU1 = 2 } linattn_qk_map;
+typedef enum { LINATTN_GMAP_AS_IS = 0, LINATTN_GMAP_NEG_SOFTPLUS = 1 } linattn_gate_map;
+typedef enum { LINATTN_BMAP_AS_IS = 0, LINATTN_BMAP_SIGMOID = 1 } linattn_beta_map;
+typedef struct {
+    int32_t qk_map;     /* applied to q and to k (linattn_qk_map) */
+    int32_t gate_map;   /* linattn_gate_map; needs a scalar gate */
+    int32_t beta_map;   /* linattn_beta_map; needs the delta rule */
+} linattn_prep_args;
+
+/*
+ * linattn_chunk_fwd with q, k, g and beta given as raw projections and mapped
+ * inside the kernel as prep says (NULL prep: no maps, same as
+ * linattn_chunk_fwd).  A map the problem has no operand for (a gate map without
+ * a gate, a beta map for the add rule) or an unknown map value is
+ * LINATTN_ERR_ARG; the per-channel gate takes no maps (LINATTN_ERR_UNSUPPORTED).
+ * Same arguments, layouts and workspace as linattn_chunk_fwd otherwise.
+ */
+linattn_status linattn_chunk_fwd_prep(const linattn_chunk_args *a, const linattn_prep_args *prep,
+                                      const void *q, const void *k, const void *v,
+                                      const void *g, const void *beta,
+                                      const float *s0, void *o, float *s_final,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Gated DeltaProduct problem description: n_h delta-rule substeps per token.
  * gate holds LINATTN_GATE_NONE or LINATTN_GATE_SCALAR; dtype as above. */
 typedef struct {

@@ -187,6 +187,35 @@ def chunk_inputs(case: Case, heads: Optional[Sequence[tuple]] = None, seed: int 
     return out
 
 
+def raw_inputs(case: Case, seed: int = SEED) -> dict:
+    """Raw projections for the fused input preparation, all heads: q, k
+    N(0,1) * 2 (not normalised), v N(0,1), beta logits N(0,1), gate logits
+    N(0,1) * gate_scale ([B,H,T] scalar gate), initial state as in
+    ``head_inputs``; same draw order per (b,h) head."""
+    parts = []
+    for b in range(case.B):
+        for h in range(case.H):
+            rng = np.random.default_rng([seed, case.case_id, b, h])
+            T, dk, dv = case.T, case.dk, case.dv
+            q = to_dtype(rng.standard_normal((T, dk), dtype=np.float32) * np.float32(2), case.dtype)
+            k = to_dtype(rng.standard_normal((T, dk), dtype=np.float32) * np.float32(2), case.dtype)
+            v = to_dtype(rng.standard_normal((T, dv), dtype=np.float32), case.dtype)
+            beta = to_dtype(rng.standard_normal((T,), dtype=np.float32), case.dtype)
+            g = to_dtype(rng.standard_normal((T,), dtype=np.float32) * np.float32(case.gate_scale),
+                         case.dtype)
+            s0 = None
+            if case.s0_std > 0:
+                s0 = (rng.standard_normal((dk, dv), dtype=np.float32)
+                      * np.float32(case.s0_std)).astype(np.float32)
+            parts.append({"q": q, "k": k, "v": v, "beta": beta if case.rule == "delta" else None,
+                          "g": None if case.gate == "none" else g, "s0": s0})
+    out = {}
+    for key in ("q", "k", "v", "g", "beta", "s0"):
+        out[key] = None if parts[0][key] is None else \
+            np.stack([p[key] for p in parts]).reshape((case.B, case.H) + parts[0][key].shape)
+    return out
+
+
 def iter_heads(case: Case, seed: int = SEED) -> Iterable[tuple]:
     """Yield ((b,h), inputs) one head at a time (for workloads too big to hold twice)."""
     for b in range(case.B):

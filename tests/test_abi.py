@@ -80,6 +80,22 @@ def test_chunk_validation(lib):
     assert call_chunk(lib, mk(gate="channel", dtype="fp32"), g=FAKE) == 3
 
 
+def test_prep_validation(lib):
+    mk = lambda **kw: bd.chunk_args(**{**dict(B=1, H=1, T=64, dk=64, dv=64, rule="delta",
+                                              gate="scalar", dtype="bf16"), **kw})
+    call = lambda a, pr, **p: lib.linattn_chunk_fwd_prep(
+        ctypes.byref(a), None if pr is None else ctypes.byref(bd.PrepArgs(*pr)),
+        *[p.get(n, FAKE) for n in ("q", "k", "v", "g", "beta")], None, FAKE, None, None, 0, None)
+    assert call(mk(), (3, 0, 0)) == 6                             # unknown q/k map
+    assert call(mk(), (0, 2, 0)) == 6
+    assert call(mk(), (0, 0, -1)) == 6
+    assert call(mk(gate="none"), (0, 1, 0), g=None) == 6          # gate map without a gate
+    assert call(mk(rule="add"), (0, 0, 1), beta=None) == 6        # beta map for the add rule
+    assert call(mk(gate="channel", dk=128, dv=128), (1, 0, 0)) == 3   # the channel path takes no maps
+    assert call(mk(dk=96), (1, 0, 0)) == 3
+    assert call(mk(), (1, 1, 1), q=None) == 1
+
+
 def test_deltaproduct_validation(lib):
     mk = lambda **kw: bd.deltaproduct_args(**{**dict(B=1, H=1, T=64, nh=2, dk=64, dv=64,
                                                      gate="scalar", dtype="bf16"), **kw})
