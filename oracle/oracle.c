@@ -249,6 +249,72 @@ int oracle_deltaproduct(int64_t B, int64_t H, int64_t T, int nh, int dk, int dv,
     return failed ? 6 : 0;
 }
 
+/*
+ * Normalised linear attention ("All sorts of famous Attention Layers",
+ * "Linear Magic" and the normaliser of the linear-attention layer there): the
+ * add rule with a second state z_t, the (decayed) running sum of the keys, and
+ * the read-out divided by q_t . z_t:
+ *
+ *   a_t = exp(g_t) (scalar gate) or 1;  S_t = a_t S_{t-1} + k_t^T v_t;
+ *   z_t = a_t z_{t-1} + k_t;  o_t = (q_t S_t) / (q_t . z_t)
+ *
+ * q, k are the feature-mapped queries and keys (positive for elu + 1, so the
+ * denominator is positive).  Layouts: q, k [B,H,T,dk]; v, o [B,H,T,dv];
+ * g [B,H,T] or NULL; s0, s_final [B,H,dk,dv]; z0, z_final [B,H,dk].
+ */
+int oracle_normalized(int64_t B, int64_t H, int64_t T, int dk, int dv, int gate,
+                      const double *q, const double *k, const double *v, const double *g,
+                      const double *s0, const double *z0, double *o, double *s_final,
+                      double *z_final, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 2;
+    if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_SCALAR) return 3;
+    if (B * H * T > 0 && (!q || !k || !v || !o)) return 1;
+    if (gate == ORACLE_GATE_SCALAR && B * H * T > 0 && !g) return 1;
+    int64_t nheads = B * H;
+    size_t ss = (size_t)dk * dv;
+    int64_t bh;
+    int failed = 0;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : failed)
+#else
+    (void)nthreads;
+#endif
+    for (bh = 0; bh < nheads; ++bh) {
+        double *S = (double *)malloc(ss * sizeof(double));
+        double *z = (double *)malloc((size_t)dk * sizeof(double));
+        if (!S || !z) { free(S); free(z); failed |= 1; continue; }
+        if (s0 != 0) memcpy(S, s0 + (size_t)bh * ss, ss * sizeof(double));
+        else memset(S, 0, ss * sizeof(double));
+        if (z0 != NULL) memcpy(z, z0 + (size_t)bh * dk, (size_t)dk * sizeof(double));
+        else memset(z, 0, (size_t)dk * sizeof(double));
+        int64_t t;
+        int r, c;
+        for (t = 0; t < T; ++t) {
+            size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+            const double *qt = q + tok * dk, *kt = k + tok * dk, *vt = v + tok * dv;
+            double a = gate == ORACLE_GATE_SCALAR ? exp(g[tok]) : 1.0;
+            for (r = 0; r < dk; ++r) {
+                z[r] = a * z[r] + kt[r];
+                for (c = 0; c < dv; ++c) S[(size_t)r * dv + c] = a * S[(size_t)r * dv + c] + kt[r] * vt[c];
+            }
+            double den = 0.0;
+            for (r = 0; r < dk; ++r) den += qt[r] * z[r];
+            for (c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (r = 0; r < dk; ++r) num += qt[r] * S[(size_t)r * dv + c];
+                o[tok * dv + c] = num / den;
+            }
+        }
+        if (s_final) memcpy(s_final + (size_t)bh * ss, S, ss * sizeof(double));
+        if (z_final) memcpy(z_final + (size_t)bh * dk, z, (size_t)dk * sizeof(double));
+        free(S);
+        free(z);
+    }
+    return failed ? 6 : 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -74,6 +74,9 @@ class OracleLib:
         lib.oracle_deltaproduct.argtypes = [i64, i64, i64, i32, i32, i32, i32,
                                             d, d, d, d, d, d, d, d, i32]
         lib.oracle_deltaproduct.restype = i32
+        lib.oracle_normalized.argtypes = [i64, i64, i64, i32, i32, i32, d, d, d, d, d, d, d, d, d,
+                                          i32]
+        lib.oracle_normalized.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         self.lib = lib
@@ -172,6 +175,35 @@ def _deltaproduct(self, q, k, v, g=None, beta=None, s0=None, *, gate="scalar", n
 OracleLib.deltaproduct = _deltaproduct
 
 
+def _normalized(self, q, k, v, g=None, s0=None, z0=None, *, gate="none", nthreads: int = 0):
+    """fp64 normalised linear attention (see ``oracle.c``).  Shapes: q, k
+    [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] or None; s0 [B,H,dk,dv]; z0 [B,H,dk].
+    Returns (o [B,H,T,dv], S_T [B,H,dk,dv], z_T [B,H,dk])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g, s0, z0 = _f64(g), _f64(s0), _f64(z0)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, H, T, dk) or v.shape != (B, H, T, dv):
+        raise ValueError("q/k/v shapes disagree")
+    if gate == "scalar" and (g is None or g.shape != (B, H, T)):
+        raise ValueError("scalar gate needs g of shape [B,H,T]")
+    if gate not in ("none", "scalar"):
+        raise ValueError("normalised linear attention takes no gate or a scalar gate")
+    if gate == "none":
+        g = None
+    o = np.empty((B, H, T, dv), dtype=np.float64)
+    s = np.empty((B, H, dk, dv), dtype=np.float64)
+    z = np.empty((B, H, dk), dtype=np.float64)
+    rc = self.lib.oracle_normalized(B, H, T, dk, dv, GATES[gate], _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(s0), _ptr(z0), _ptr(o), _ptr(s), _ptr(z), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_normalized failed with code {rc}")
+    return o, s, z
+
+
+OracleLib.normalized = _normalized
+
+
 # Input preparation from raw projections, fp64 ([ASF] "DeltaNet": keys and
 # queries L2-normalised per token and the write strength beta a sigmoid;
 # "Linear Magic": the positive feature map elu + 1; [LAV] "Mamba-2" and "Gated
@@ -241,3 +273,8 @@ def decode_step(*args, **kw):
 def deltaproduct(*args, **kw):
     """See :meth:`OracleLib.deltaproduct`."""
     return default().deltaproduct(*args, **kw)
+
+
+def normalized(*args, **kw):
+    """See :meth:`OracleLib.normalized`."""
+    return default().normalized(*args, **kw)

@@ -479,6 +479,62 @@ def pin_deltaproduct_virtual_sequence(orc):
         assert rel_err(S, Sv) < TOL, f"GDP state != virtual-sequence state ({gate})"
 
 
+# ---------------------------------------------------------------------------
+# V15 normalised linear attention == the masked, decay-weighted quadratic form
+#     divided by its row sums: o_t = sum_j w_tj v_j / sum_j w_tj with
+#     w_tj = (q_t . k_j) prod_{s=j+1..t} a_s for j <= t ([ASF] "Linear Magic":
+#     the normaliser of the feature-map attention; [LAV] "Mamba-2": the decay
+#     weights of the parallel form).  Carried states (S_0, z_0) enter as an
+#     extra decayed term in numerator and denominator.
+# ---------------------------------------------------------------------------
+def _norm_case(rng, B, H, T, dk, dv, gate):
+    q = np.abs(rng.standard_normal((B, H, T, dk))) + 0.1
+    k = np.abs(rng.standard_normal((B, H, T, dk))) + 0.1
+    v = rng.standard_normal((B, H, T, dv))
+    g = -_softplus(rng.standard_normal((B, H, T))) * 0.3 if gate == "scalar" else None
+    S0 = np.abs(rng.standard_normal((B, H, dk, dv)))
+    z0 = np.abs(rng.standard_normal((B, H, dk))) + 0.5
+    return q, k, v, g, S0, z0
+
+
+def pin_normalized_quadratic_form(orc):
+    rng = np.random.default_rng(116)
+    B, H, T, dk, dv = 1, 2, 13, 5, 3
+    for gate in ("none", "scalar"):
+        q, k, v, g, S0, z0 = _norm_case(rng, B, H, T, dk, dv, gate)
+        o, S, z = orc.normalized(q, k, v, g, S0, z0, gate=gate)
+        for h in range(H):
+            G = np.cumsum(g[0, h]) if gate == "scalar" else np.zeros(T)
+            W = (q[0, h] @ k[0, h].T) * np.exp(G[:, None] - G[None, :])
+            W = np.tril(W)
+            lam = np.exp(G)                               # decay of the carried states
+            num = W @ v[0, h] + lam[:, None] * (q[0, h] @ S0[0, h])
+            den = W.sum(axis=1) + lam * (q[0, h] @ z0[0, h])
+            assert rel_err(o[0, h], num / den[:, None]) < TOL, f"normalised LA quadratic form ({gate})"
+            zT = lam[-1] * z0[0, h] + (np.exp(G[-1] - G)[:, None] * k[0, h]).sum(axis=0)
+            assert rel_err(z[0, h], zT) < TOL, f"normaliser state ({gate})"
+
+
+# ---------------------------------------------------------------------------
+# V16 normalisation invariants: a constant value vector comes back unchanged
+#     (the weights sum to one) when the carried state holds that value too, and
+#     scaling every query by c > 0 leaves the output unchanged.
+# ---------------------------------------------------------------------------
+def pin_normalized_invariants(orc):
+    rng = np.random.default_rng(117)
+    B, H, T, dk, dv = 2, 1, 17, 4, 3
+    for gate in ("none", "scalar"):
+        q, k, v, g, S0, z0 = _norm_case(rng, B, H, T, dk, dv, gate)
+        c = rng.standard_normal(dv)
+        vc = np.broadcast_to(c, v.shape).copy()
+        Sc = z0[..., None] * c                           # S0 = z0^T c: the same constant
+        oc, _, _ = orc.normalized(q, k, vc, g, Sc, z0, gate=gate)
+        assert rel_err(oc, np.broadcast_to(c, oc.shape)) < TOL, f"constant value ({gate})"
+        o1, _, _ = orc.normalized(q, k, v, g, S0, z0, gate=gate)
+        o2, _, _ = orc.normalized(q * 3.7, k, v, g, S0, z0, gate=gate)
+        assert rel_err(o2, o1) < TOL, f"query scale ({gate})"
+
+
 PINS = [
     pin_add_equals_masked_quadratic,
     pin_decay_equals_gamma_form,
@@ -497,4 +553,6 @@ PINS = [
     pin_deltaproduct_one_substep_is_gdn,
     pin_deltaproduct_dense_product,
     pin_deltaproduct_virtual_sequence,
+    pin_normalized_quadratic_form,
+    pin_normalized_invariants,
 ]

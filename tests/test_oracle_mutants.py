@@ -49,6 +49,12 @@ MUTANTS = [
                              "const double *kj = k + (tok * nh) * dk;")]),
     ("gdp_beta_of_first_substep", [("double bj = beta[tok * nh + j];", "double bj = beta[tok * nh];")]),
     ("gdp_ignore_initial_state", [("if (s0 != NULL) memcpy(", "if (0) memcpy(")]),
+    # normalised linear attention
+    ("norm_no_decay_on_z", [("z[r] = a * z[r] + kt[r];", "z[r] = z[r] + kt[r];")]),
+    ("norm_den_with_key", [("den += qt[r] * z[r];", "den += kt[r] * z[r];")]),
+    ("norm_ignore_z0", [("if (z0 != NULL) memcpy(", "if (0) memcpy(")]),
+    ("norm_ignore_s0", [("if (s0 != 0) memcpy(", "if (0) memcpy(")]),
+    ("norm_not_divided", [("o[tok * dv + c] = num / den;", "o[tok * dv + c] = num;")]),
 ]
 
 
