@@ -184,6 +184,43 @@ def time_prep(la, case, dev, steps, warmup=2):
             "path": "pipe with input preparation", "steps": steps}
 
 
+def time_normalized(la, syn, case, dev, steps, warmup=2):
+    """Event-timed normalised linear attention (two add-rule passes and the
+    division) at the shape and input laws of ``case``; minimal bytes as for the
+    add rule plus the fp32 key sum."""
+    import torch
+    B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
+    x = syn.chunk_inputs_torch(case, dev)
+    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    z_fin = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    wsb = la.normalized_workspace_bytes(B, H, T, dk, dv, gate=case.gate)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        la.chunk_fwd_normalized(x["q"], x["k"], x["v"], x["g"], None, None, gate=case.gate, out=out,
+                                s_final=s_fin, z_final=z_fin, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    abytes = chunk_alg_bytes(B, H, T, dk, dv, 2, "add", case.gate) + B * H * dk * 4
+    aflops = chunk_nominal_flops(B, H, T, dk, dv, "add")
+    return {"workload": f"normalised {case.gate}-gate linear attention (elu+1 features) "
+                        f"B={B} H={H} T={T} dk={dk} dv={dv} bf16",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "path": "fused (values) + fused (ones) + divide", "steps": steps}
+
+
 def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
     """Event-timed Gated DeltaProduct forward (inputs resident in HBM).  Minimal
     bytes: q and o once, k, v and beta per substep, the gate and the final
@@ -248,9 +285,9 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep",
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -324,6 +361,8 @@ def main():
             others.append(time_deltaproduct(la, syn, syn.GDP2, dev, steps=10))
         elif name == "cfg3prep":
             others.append(time_prep(la, syn.CFG3, dev, steps=10))
+        elif name == "cfg2norm":
+            others.append(time_normalized(la, syn, syn.CFG2, dev, steps=10))
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
             others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))

@@ -1,5 +1,6 @@
-"""MI355X (gfx950) causal linear attention: chunkwise forward, decode step and
-the Gated DeltaProduct forward.
+"""MI355X (gfx950) causal linear attention: chunkwise forward (optionally from
+raw projections, or normalised), decode step and the Gated DeltaProduct
+forward.
 
 The compute runs in hand-written HIP kernels behind the C ABI of
 ``include/linattn.h`` (``liblinattn.so``); this package only marshals torch
@@ -7,9 +8,10 @@ tensors to it.  Importing the package does not load the library; the first
 call does, and fails loudly if it has not been built.
 """
 from ._binding import (EXPORTS, LIB_PATH, LinattnError, abi_version, chunk_fwd,  # noqa: F401
-                       chunk_workspace_bytes, decode_step, deltaproduct_fwd,
-                       deltaproduct_workspace_bytes, load, status_string)
+                       chunk_fwd_normalized, chunk_workspace_bytes, decode_step, deltaproduct_fwd,
+                       deltaproduct_workspace_bytes, load, normalized_workspace_bytes,
+                       status_string)
 
-__all__ = ["chunk_fwd", "decode_step", "deltaproduct_fwd", "chunk_workspace_bytes",
-           "deltaproduct_workspace_bytes", "abi_version", "status_string", "load", "LinattnError",
-           "LIB_PATH", "EXPORTS"]
+__all__ = ["chunk_fwd", "chunk_fwd_normalized", "decode_step", "deltaproduct_fwd",
+           "chunk_workspace_bytes", "normalized_workspace_bytes", "deltaproduct_workspace_bytes",
+           "abi_version", "status_string", "load", "LinattnError", "LIB_PATH", "EXPORTS"]

@@ -22,7 +22,8 @@ DTYPES = {"fp32": 0, "bf16": 1}
 # Every function the header declares; a test checks the two stay in step.
 EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_workspace_bytes",
            "linattn_chunk_fwd", "linattn_decode_step", "linattn_deltaproduct_workspace_bytes",
-           "linattn_deltaproduct_fwd", "linattn_chunk_fwd_prep")
+           "linattn_deltaproduct_fwd", "linattn_chunk_fwd_prep",
+           "linattn_normalized_workspace_bytes", "linattn_chunk_fwd_normalized")
 QK_MAPS = {"as_is": 0, "l2": 1, "elu1": 2}
 GATE_MAPS = {"as_is": 0, "neg_softplus": 1}
 BETA_MAPS = {"as_is": 0, "sigmoid": 1}
@@ -93,6 +94,11 @@ def load(path: str = LIB_PATH):
         lib.linattn_chunk_fwd_prep.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.POINTER(PrepArgs),
                                                vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.linattn_chunk_fwd_prep.restype = ctypes.c_int
+        lib.linattn_normalized_workspace_bytes.argtypes = [ctypes.POINTER(ChunkArgs)]
+        lib.linattn_normalized_workspace_bytes.restype = sz
+        lib.linattn_chunk_fwd_normalized.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.POINTER(PrepArgs),
+                                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.linattn_chunk_fwd_normalized.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -296,3 +302,61 @@ def deltaproduct_fwd(q, k, v, g=None, beta=None, s0=None, *, gate="scalar", chun
     if st != 0:
         raise LinattnError(st, "linattn_deltaproduct_fwd")
     return out, s_final
+
+
+def normalized_workspace_bytes(B, H, T, dk, dv, *, gate="none", dtype="bf16", chunk=64) -> int:
+    a = chunk_args(B, H, T, dk, dv, rule="add", gate=gate, dtype=dtype, chunk=chunk)
+    return int(load().linattn_normalized_workspace_bytes(ctypes.byref(a)))
+
+
+def chunk_fwd_normalized(q, k, v, g=None, s0=None, z0=None, *, gate="none", chunk=64, out=None,
+                         s_final=None, z_final=None, return_state=True, workspace=None,
+                         qk_map="as_is", gate_map="as_is"):
+    """Normalised linear attention on the GPU: o_t = (q_t S_t) / (q_t . z_t), add
+    rule, z_t the decayed running key sum.  q, k [B,H,T,dk]; v [B,H,T,dv];
+    g [B,H,T] | [B,H,T,dk] | None; s0 [B,H,dk,dv] and z0 [B,H,dk] fp32 or None.
+    Returns (o, S_T, z_T).  qk_map / gate_map as for chunk_fwd."""
+    import torch
+    lib = load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    dtype = _token_dtype(q)
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    if gate == "scalar":
+        _check(g, "g", (B, H, T), dt, dev)
+    elif gate == "channel":
+        _check(g, "g", (B, H, T, dk), dt, dev)
+    elif g is not None:
+        raise ValueError("g must be None when gate='none'")
+    if s0 is not None:
+        _check(s0, "s0", (B, H, dk, dv), torch.float32, dev)
+    if z0 is not None:
+        _check(z0, "z0", (B, H, dk), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    if return_state:
+        if s_final is None:
+            s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        if z_final is None:
+            z_final = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    for t, name, shape in ((s_final, "s_final", (B, H, dk, dv)), (z_final, "z_final", (B, H, dk))):
+        if t is not None:
+            _check(t, name, shape, torch.float32, dev)
+    a = chunk_args(B, H, T, dk, dv, rule="add", gate=gate, dtype=dtype, chunk=chunk)
+    need = int(lib.linattn_normalized_workspace_bytes(ctypes.byref(a)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    pa = PrepArgs(QK_MAPS[qk_map], GATE_MAPS[gate_map], 0)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_chunk_fwd_normalized(ctypes.byref(a), ctypes.byref(pa), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(g), _ptr(s0), _ptr(z0), _ptr(out), _ptr(s_final),
+                                          _ptr(z_final), _ptr(workspace), ws_bytes, stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_chunk_fwd_normalized")
+    return out, s_final, z_final

@@ -48,6 +48,25 @@ struct DeltaProductProblem {
 hipError_t launch_dp_expand(const DeltaProductProblem& p, hipStream_t stream);
 hipError_t launch_dp_gather(const DeltaProductProblem& p, hipStream_t stream);
 
+// Normalised linear attention as two add-rule passes (values, then a block of
+// ones started at z0): the block of ones and its initial state before them;
+// o /= den (column 0 of the second pass's output) and z_T = column 0 of its
+// final state after them.
+struct NormalizedProblem {
+    int64_t rows, heads;          // B*H*T token rows, B*H heads
+    int dk, dv, dtype;
+    void* ones;                   // [rows][normalized_ones_columns()] token dtype
+    const float* z0;              // [heads][dk] or NULL
+    float* s0_den;                // [heads][dk][normalized_ones_columns()]
+    void* o;                      // [rows][dv] numerator in, output out
+    const void* den;              // [rows][normalized_ones_columns()]
+    const float* sf_den;          // [heads][dk][normalized_ones_columns()]
+    float* z_final;               // [heads][dk] or NULL
+};
+int normalized_ones_columns();
+hipError_t launch_norm_prepare(const NormalizedProblem& p, hipStream_t stream);
+hipError_t launch_norm_finish(const NormalizedProblem& p, hipStream_t stream);
+
 // Single-pass chunk kernel (gate NONE or SCALAR), three phases per chunk.
 bool chunk_fused_supported(const ChunkProblem& p);
 hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t stream);

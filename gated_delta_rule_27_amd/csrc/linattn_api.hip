@@ -155,6 +155,43 @@ DpLayout dp_layout(const linattn_chunk_args& va, const ChunkProblem& vp)
     return l;
 }
 
+// Normalised linear attention: the second (denominator) pass's problem and the
+// workspace pieces, 256-byte aligned: ones [B,H,T,64], den [B,H,T,64], its
+// initial and final states [B,H,dk,64] fp32, then the two-kernel path's
+// workspace (shared by both passes, sized for the wider one).
+struct NormLayout {
+    size_t ones, den, s0d, sfd, cws, total;
+};
+NormLayout norm_layout(const ChunkProblem& p, const ChunkProblem& pd)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t esz = p.dtype == kBF16 ? 2 : 4;
+    const size_t rows = (size_t)(p.B * p.H) * (size_t)p.T;
+    const size_t nc = (size_t)normalized_ones_columns();
+    NormLayout l{};
+    l.ones = 0;
+    l.den = up(rows * nc * esz);
+    l.s0d = l.den + up(rows * nc * esz);
+    l.sfd = l.s0d + up((size_t)(p.B * p.H) * p.dk * nc * 4);
+    l.cws = l.sfd + up((size_t)(p.B * p.H) * p.dk * nc * 4);
+    size_t w = use_split(p) ? chunk_split_workspace_bytes(p) : 0;
+    const size_t wd = use_split(pd) ? chunk_split_workspace_bytes(pd) : 0;
+    l.total = l.cws + (w > wd ? w : wd);
+    return l;
+}
+
+linattn_status validate_norm(const linattn_chunk_args* a, const linattn_prep_args* prep,
+                             linattn_chunk_args* ad, ChunkProblem* p, ChunkProblem* pd)
+{
+    if (!a) return LINATTN_ERR_NULL;
+    if (a->rule != LINATTN_RULE_ADD) return LINATTN_ERR_ARG;
+    linattn_status st = validate_chunk(a, p, prep);
+    if (st != LINATTN_OK) return st;
+    *ad = *a;
+    ad->dv = normalized_ones_columns();
+    return validate_chunk(ad, pd, prep);
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,6 +328,52 @@ linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args* a, cons
     if (st != LINATTN_OK) return st;
     if (a->T > 0 && launch_dp_gather(p, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
     return LINATTN_OK;
+}
+
+size_t linattn_normalized_workspace_bytes(const linattn_chunk_args* a)
+{
+    linattn_chunk_args ad{};
+    ChunkProblem p{}, pd{};
+    if (validate_norm(a, nullptr, &ad, &p, &pd) != LINATTN_OK) return 0;
+    return norm_layout(p, pd).total;
+}
+
+linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args* a, const linattn_prep_args* prep,
+                                            const void* q, const void* k, const void* v, const void* g,
+                                            const float* s0, const float* z0, void* o, float* s_final,
+                                            float* z_final, void* workspace, size_t workspace_bytes,
+                                            void* stream)
+{
+    linattn_chunk_args ad{};
+    ChunkProblem p{}, pd{};
+    linattn_status st = validate_norm(a, prep, &ad, &p, &pd);
+    if (st != LINATTN_OK) return st;
+    if (p.B * p.H == 0) return LINATTN_OK;
+    if (p.T > 0) {
+        st = check_pointers(LINATTN_RULE_ADD, a->gate, q, k, v, g, nullptr, q, o);
+        if (st != LINATTN_OK) return st;
+    }
+    st = check_states(p, s0, s_final);
+    if (st != LINATTN_OK) return st;
+    if ((z0 && !aligned16(z0)) || (z_final && !aligned16(z_final))) return LINATTN_ERR_UNSUPPORTED;
+    const NormLayout l = norm_layout(p, pd);
+    if (!workspace || workspace_bytes < l.total) return LINATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    NormalizedProblem np{p.B * p.H * p.T, p.B * p.H, p.dk, p.dv, p.dtype, ws + l.ones, z0,
+                         reinterpret_cast<float*>(ws + l.s0d), o, ws + l.den,
+                         reinterpret_cast<const float*>(ws + l.sfd), z_final};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_norm_prepare(np, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+    // numerator: the add rule on the values; denominator: on the block of ones
+    st = linattn_chunk_fwd_prep(a, prep, q, k, v, g, nullptr, s0, o, s_final, ws + l.cws,
+                                workspace_bytes - l.cws, stream);
+    if (st != LINATTN_OK) return st;
+    st = linattn_chunk_fwd_prep(&ad, prep, q, k, ws + l.ones, g, nullptr, reinterpret_cast<float*>(ws + l.s0d),
+                                ws + l.den, reinterpret_cast<float*>(ws + l.sfd), ws + l.cws,
+                                workspace_bytes - l.cws, stream);
+    if (st != LINATTN_OK) return st;
+    return launch_norm_finish(np, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

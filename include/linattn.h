@@ -152,6 +152,34 @@ linattn_status linattn_chunk_fwd_prep(const linattn_chunk_args *a, const linattn
                                       const float *s0, void *o, float *s_final,
                                       void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Device workspace, in bytes, that linattn_chunk_fwd_normalized needs (a block
+ * of ones, the denominator pass's output and states, and the chunk path's
+ * workspace); 0 for invalid arguments.
+ */
+size_t linattn_normalized_workspace_bytes(const linattn_chunk_args *a);
+
+/*
+ * Normalised linear attention ("All sorts of famous Attention Layers",
+ * "Linear Magic" and its normaliser): the add rule (a->rule must be
+ * LINATTN_RULE_ADD, else LINATTN_ERR_ARG) with a second state z_t = a_t
+ * z_{t-1} + k_t (the decayed running sum of the keys; Diag(a_t) for the
+ * channel gate) and the read-out o_t = (q_t S_t) / (q_t . z_t).  The
+ * denominator is only well defined for positive feature maps (elu + 1, e.g.
+ * prep->qk_map = LINATTN_QK_ELU1 on raw projections).
+ *
+ *   q, k, v, g, s0, o, s_final: as for linattn_chunk_fwd_prep (no beta)
+ *   z0       [B,H,dk] fp32 initial key sum, or NULL for zero
+ *   z_final  [B,H,dk] fp32 final key sum, or NULL
+ *   workspace: at least linattn_normalized_workspace_bytes(a) bytes,
+ *            16-byte aligned (always needed: the denominator pass writes to it)
+ */
+linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args *a, const linattn_prep_args *prep,
+                                            const void *q, const void *k, const void *v,
+                                            const void *g, const float *s0, const float *z0,
+                                            void *o, float *s_final, float *z_final,
+                                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* Gated DeltaProduct problem description: n_h delta-rule substeps per token.
  * gate holds LINATTN_GATE_NONE or LINATTN_GATE_SCALAR; dtype as above. */
 typedef struct {

@@ -255,12 +255,13 @@ int oracle_deltaproduct(int64_t B, int64_t H, int64_t T, int nh, int dk, int dv,
  * add rule with a second state z_t, the (decayed) running sum of the keys, and
  * the read-out divided by q_t . z_t:
  *
- *   a_t = exp(g_t) (scalar gate) or 1;  S_t = a_t S_{t-1} + k_t^T v_t;
+ *   a_t = exp(g_t) (scalar gate), a vector (channel gate: row r of S and
+ *   entry r of z decay by a_t[r]) or 1;  S_t = a_t S_{t-1} + k_t^T v_t;
  *   z_t = a_t z_{t-1} + k_t;  o_t = (q_t S_t) / (q_t . z_t)
  *
  * q, k are the feature-mapped queries and keys (positive for elu + 1, so the
  * denominator is positive).  Layouts: q, k [B,H,T,dk]; v, o [B,H,T,dv];
- * g [B,H,T] or NULL; s0, s_final [B,H,dk,dv]; z0, z_final [B,H,dk].
+ * g [B,H,T] | [B,H,T,dk] | NULL; s0, s_final [B,H,dk,dv]; z0, z_final [B,H,dk].
  */
 int oracle_normalized(int64_t B, int64_t H, int64_t T, int dk, int dv, int gate,
                       const double *q, const double *k, const double *v, const double *g,
@@ -268,9 +269,9 @@ int oracle_normalized(int64_t B, int64_t H, int64_t T, int dk, int dv, int gate,
                       double *z_final, int nthreads)
 {
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 2;
-    if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_SCALAR) return 3;
+    if (gate < ORACLE_GATE_NONE || gate > ORACLE_GATE_CHANNEL) return 3;
     if (B * H * T > 0 && (!q || !k || !v || !o)) return 1;
-    if (gate == ORACLE_GATE_SCALAR && B * H * T > 0 && !g) return 1;
+    if (gate != ORACLE_GATE_NONE && B * H * T > 0 && !g) return 1;
     int64_t nheads = B * H;
     size_t ss = (size_t)dk * dv;
     int64_t bh;
@@ -294,8 +295,9 @@ int oracle_normalized(int64_t B, int64_t H, int64_t T, int dk, int dv, int gate,
         for (t = 0; t < T; ++t) {
             size_t tok = (size_t)bh * (size_t)T + (size_t)t;
             const double *qt = q + tok * dk, *kt = k + tok * dk, *vt = v + tok * dv;
-            double a = gate == ORACLE_GATE_SCALAR ? exp(g[tok]) : 1.0;
             for (r = 0; r < dk; ++r) {
+                double a = gate == ORACLE_GATE_SCALAR    ? exp(g[tok])
+                         : gate == ORACLE_GATE_CHANNEL ? exp(g[tok * dk + r]) : 1.0;
                 z[r] = a * z[r] + kt[r];
                 for (c = 0; c < dv; ++c) S[(size_t)r * dv + c] = a * S[(size_t)r * dv + c] + kt[r] * vt[c];
             }

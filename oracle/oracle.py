@@ -177,7 +177,8 @@ OracleLib.deltaproduct = _deltaproduct
 
 def _normalized(self, q, k, v, g=None, s0=None, z0=None, *, gate="none", nthreads: int = 0):
     """fp64 normalised linear attention (see ``oracle.c``).  Shapes: q, k
-    [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] or None; s0 [B,H,dk,dv]; z0 [B,H,dk].
+    [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] | [B,H,T,dk] | None; s0 [B,H,dk,dv];
+    z0 [B,H,dk].
     Returns (o [B,H,T,dv], S_T [B,H,dk,dv], z_T [B,H,dk])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     g, s0, z0 = _f64(g), _f64(s0), _f64(z0)
@@ -187,8 +188,8 @@ def _normalized(self, q, k, v, g=None, s0=None, z0=None, *, gate="none", nthread
         raise ValueError("q/k/v shapes disagree")
     if gate == "scalar" and (g is None or g.shape != (B, H, T)):
         raise ValueError("scalar gate needs g of shape [B,H,T]")
-    if gate not in ("none", "scalar"):
-        raise ValueError("normalised linear attention takes no gate or a scalar gate")
+    if gate == "channel" and (g is None or g.shape != (B, H, T, dk)):
+        raise ValueError("channel gate needs g of shape [B,H,T,dk]")
     if gate == "none":
         g = None
     o = np.empty((B, H, T, dv), dtype=np.float64)

@@ -491,7 +491,11 @@ def _norm_case(rng, B, H, T, dk, dv, gate):
     q = np.abs(rng.standard_normal((B, H, T, dk))) + 0.1
     k = np.abs(rng.standard_normal((B, H, T, dk))) + 0.1
     v = rng.standard_normal((B, H, T, dv))
-    g = -_softplus(rng.standard_normal((B, H, T))) * 0.3 if gate == "scalar" else None
+    g = None
+    if gate == "scalar":
+        g = -_softplus(rng.standard_normal((B, H, T))) * 0.3
+    elif gate == "channel":
+        g = -_softplus(rng.standard_normal((B, H, T, dk))) * 0.3
     S0 = np.abs(rng.standard_normal((B, H, dk, dv)))
     z0 = np.abs(rng.standard_normal((B, H, dk))) + 0.5
     return q, k, v, g, S0, z0
@@ -500,18 +504,19 @@ def _norm_case(rng, B, H, T, dk, dv, gate):
 def pin_normalized_quadratic_form(orc):
     rng = np.random.default_rng(116)
     B, H, T, dk, dv = 1, 2, 13, 5, 3
-    for gate in ("none", "scalar"):
+    for gate in ("none", "scalar", "channel"):
         q, k, v, g, S0, z0 = _norm_case(rng, B, H, T, dk, dv, gate)
         o, S, z = orc.normalized(q, k, v, g, S0, z0, gate=gate)
         for h in range(H):
-            G = np.cumsum(g[0, h]) if gate == "scalar" else np.zeros(T)
-            W = (q[0, h] @ k[0, h].T) * np.exp(G[:, None] - G[None, :])
+            G = _Gc(g[0, h], gate, dk) if gate != "none" else np.zeros((T, dk))
+            # w_tj = sum_c q_tc k_jc exp(G_tc - G_jc), j <= t; carried states decay by exp(G_t)
+            W = np.einsum("tc,jc,tjc->tj", q[0, h], k[0, h], np.exp(G[:, None, :] - G[None, :, :]))
             W = np.tril(W)
-            lam = np.exp(G)                               # decay of the carried states
-            num = W @ v[0, h] + lam[:, None] * (q[0, h] @ S0[0, h])
-            den = W.sum(axis=1) + lam * (q[0, h] @ z0[0, h])
+            lam = np.exp(G)                                # [T, dk]
+            num = W @ v[0, h] + (q[0, h] * lam) @ S0[0, h]
+            den = W.sum(axis=1) + (q[0, h] * lam) @ z0[0, h]
             assert rel_err(o[0, h], num / den[:, None]) < TOL, f"normalised LA quadratic form ({gate})"
-            zT = lam[-1] * z0[0, h] + (np.exp(G[-1] - G)[:, None] * k[0, h]).sum(axis=0)
+            zT = lam[-1] * z0[0, h] + (np.exp(G[-1][None, :] - G) * k[0, h]).sum(axis=0)
             assert rel_err(z[0, h], zT) < TOL, f"normaliser state ({gate})"
 
 
@@ -533,6 +538,13 @@ def pin_normalized_invariants(orc):
         o1, _, _ = orc.normalized(q, k, v, g, S0, z0, gate=gate)
         o2, _, _ = orc.normalized(q * 3.7, k, v, g, S0, z0, gate=gate)
         assert rel_err(o2, o1) < TOL, f"query scale ({gate})"
+        if gate == "scalar":
+            # a channel gate with all channels equal is the scalar gate
+            gc = np.repeat(g[..., None], dk, axis=-1)
+            o3, S3, z3 = orc.normalized(q, k, v, gc, S0, z0, gate="channel")
+            a = orc.normalized(q, k, v, g, S0, z0, gate="scalar")
+            assert rel_err(o3, a[0]) < TOL and rel_err(S3, a[1]) < TOL and rel_err(z3, a[2]) < TOL, \
+                "equal-channel gate != scalar gate (normalised)"
 
 
 PINS = [

@@ -96,6 +96,23 @@ def test_prep_validation(lib):
     assert call(mk(), (1, 1, 1), q=None) == 1
 
 
+def test_normalized_validation(lib):
+    mk = lambda **kw: bd.chunk_args(**{**dict(B=1, H=1, T=64, dk=64, dv=64, rule="add",
+                                              gate="none", dtype="bf16"), **kw})
+    call = lambda a, **p: lib.linattn_chunk_fwd_normalized(
+        ctypes.byref(a), None, *[p.get(n, FAKE) for n in ("q", "k", "v")], p.get("g"), p.get("s0"),
+        p.get("z0"), p.get("o", FAKE), p.get("sf"), p.get("zf"), p.get("ws"), p.get("wsb", 0), None)
+    assert call(mk(rule="delta")) == 6                           # add rule only
+    assert call(mk(dk=96)) == 3
+    assert call(mk(), q=None) == 1
+    assert call(mk(), z0=FAKE + 4) == 3                           # misaligned z0
+    assert call(mk()) == 4                                        # workspace missing
+    assert call(mk(B=0)) == 0
+    # ones + denominator [64 x 64 bf16 each], two [64 x 64] fp32 states
+    assert lib.linattn_normalized_workspace_bytes(ctypes.byref(mk())) == 2 * 64 * 64 * 2 + 2 * 64 * 64 * 4
+    assert lib.linattn_normalized_workspace_bytes(ctypes.byref(mk(rule="delta"))) == 0
+
+
 def test_deltaproduct_validation(lib):
     mk = lambda **kw: bd.deltaproduct_args(**{**dict(B=1, H=1, T=64, nh=2, dk=64, dv=64,
                                                      gate="scalar", dtype="bf16"), **kw})

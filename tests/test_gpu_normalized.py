@@ -1,0 +1,105 @@
+"""Parity of normalised linear attention (HIP, through the C ABI: two add-rule
+passes and a division) with the fp64 oracle's normalised recurrence: positive
+features (elu + 1), every head size and dtype, no gate / scalar gate /
+per-channel gate, carried S_0 and z_0, the feature map fused from raw
+projections, empty sequences and resume."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from gpu_util import TOL, dev, dev_state, host, note, rel_l2
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def inputs(case, rng_id):
+    x = syn.chunk_inputs(case)
+    rng = np.random.default_rng([syn.SEED, rng_id])
+    z0 = np.abs(rng.standard_normal((case.B, case.H, case.dk))).astype(np.float32)
+    s0 = None if x["s0"] is None else np.abs(x["s0"]).astype(np.float32)
+    return x, s0, z0
+
+
+def check(case, x, s0, z0, **maps):
+    import gated_delta_rule_27_amd as la
+    note(f"[norm] {case.gate} {case.dtype} dk={case.dk} dv={case.dv} T={case.T} {maps}")
+    d = lambda a: dev(a, case.dtype)
+    o, s, z = la.chunk_fwd_normalized(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), dev_state(s0),
+                                      dev_state(z0), gate=case.gate, **maps)
+    torch.cuda.synchronize()
+    q, k = x["q"], x["k"]
+    if maps.get("qk_map") == "elu1":
+        q, k = oracle.prepare_qk(q, "elu1"), oracle.prepare_qk(k, "elu1")
+    oref, sref, zref = oracle.normalized(q, k, x["v"], x["g"], s0, z0, gate=case.gate)
+    eo, es, ez = rel_l2(host(o), oref), rel_l2(host(s), sref), rel_l2(host(z), zref)
+    note(f"    rel L2 o={eo:.3e} S={es:.3e} z={ez:.3e}")
+    tol = TOL[case.dtype]
+    assert np.all(np.isfinite(host(o)))
+    assert eo <= tol and es <= tol and ez <= tol
+    return o, s, z
+
+
+CASES = []
+for dtype, dims in (("bf16", ((64, 64), (128, 128), (64, 128), (128, 64))), ("fp32", ((64, 64),))):
+    for (dk, dv) in dims:
+        for gate in ("none", "scalar"):
+            CASES.append((dtype, dk, dv, gate))
+
+
+@pytest.mark.parametrize("dtype,dk,dv,gate", CASES)
+def test_small_ragged(dtype, dk, dv, gate):
+    case = syn.Case("norm", 2, 2, 200, dk, dv, "add", gate, dtype, qk="elu1", gate_scale=0.25,
+                    s0_std=0.3, case_id=140)
+    x, s0, z0 = inputs(case, 140)
+    check(case, x, s0, z0)
+
+
+def test_channel_gate():
+    case = syn.Case("norm_chan", 1, 2, 150, 128, 128, "add", "channel", "bf16", qk="elu1",
+                    gate_scale=0.1, s0_std=0.3, case_id=141)
+    x, s0, z0 = inputs(case, 141)
+    check(case, x, s0, z0)
+
+
+def test_feature_map_from_raw_projections():
+    # q, k raw Gaussian; elu + 1 applied inside the kernel
+    case = syn.Case("norm_raw", 2, 2, 130, 128, 128, "add", "scalar", "bf16", qk="gauss",
+                    gate_scale=0.25, case_id=142)
+    x, _, z0 = inputs(case, 142)
+    check(case, x, None, None, qk_map="elu1")
+
+
+def test_zero_tokens_returns_states():
+    import gated_delta_rule_27_amd as la
+    rng = np.random.default_rng(143)
+    s0 = rng.random((1, 2, 64, 64)).astype(np.float32)
+    z0 = rng.random((1, 2, 64)).astype(np.float32)
+    e = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    o, s, z = la.chunk_fwd_normalized(e(1, 2, 0, 64), e(1, 2, 0, 64), e(1, 2, 0, 64), None,
+                                      dev_state(s0), dev_state(z0))
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert np.array_equal(host(s), s0.astype(np.float64)) and np.array_equal(host(z), z0.astype(np.float64))
+
+
+def test_resume_equals_one_pass():
+    case = syn.Case("norm_resume", 1, 2, 300, 128, 128, "add", "scalar", "bf16", qk="elu1",
+                    gate_scale=0.1, case_id=144)
+    import gated_delta_rule_27_amd as la
+    x, _, _ = inputs(case, 144)
+    d = lambda a: dev(a, case.dtype)
+    o, s, z = la.chunk_fwd_normalized(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), gate="scalar")
+    cut = 131
+    part = lambda a, sl: d(np.ascontiguousarray(a[:, :, sl]))
+    o1, s1, z1 = la.chunk_fwd_normalized(part(x["q"], slice(0, cut)), part(x["k"], slice(0, cut)),
+                                         part(x["v"], slice(0, cut)), part(x["g"], slice(0, cut)),
+                                         gate="scalar")
+    o2, s2, z2 = la.chunk_fwd_normalized(part(x["q"], slice(cut, None)), part(x["k"], slice(cut, None)),
+                                         part(x["v"], slice(cut, None)), part(x["g"], slice(cut, None)),
+                                         s1, z1, gate="scalar")
+    torch.cuda.synchronize()
+    assert rel_l2(host(torch.cat([o1, o2], dim=2)), host(o)) < 1e-2
+    assert rel_l2(host(s2), host(s)) < 1e-2 and rel_l2(host(z2), host(z)) < 1e-2

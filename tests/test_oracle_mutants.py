@@ -54,6 +54,8 @@ MUTANTS = [
     ("norm_den_with_key", [("den += qt[r] * z[r];", "den += kt[r] * z[r];")]),
     ("norm_ignore_z0", [("if (z0 != NULL) memcpy(", "if (0) memcpy(")]),
     ("norm_ignore_s0", [("if (s0 != 0) memcpy(", "if (0) memcpy(")]),
+    ("norm_channel_gate_reversed", [(": gate == ORACLE_GATE_CHANNEL ? exp(g[tok * dk + r]) : 1.0;",
+                                     ": gate == ORACLE_GATE_CHANNEL ? exp(g[tok * dk + dk - 1 - r]) : 1.0;")]),
     ("norm_not_divided", [("o[tok * dv + c] = num / den;", "o[tok * dv + c] = num;")]),
 ]
 
