@@ -42,6 +42,10 @@
  * 1 x d_k, v_t is 1 x d_v, S is d_k x d_v, stored row-major (S[i*dv + j]).
  * No query scaling, no normaliser: neither appears in the read-out on [LAV].
  *
+ * oracle_recurrence_bwd differentiates the same recurrence in reverse (the
+ * gradients of a training step); oracle_deltaproduct and oracle_normalized are
+ * the Gated DeltaProduct and normalised variants, each described where defined.
+ *
  * Arithmetic: IEEE fp64, plain loops, fixed order per head.  OpenMP
  * parallelises over independent (b, h) pairs only, so the result does not
  * depend on the thread count.
@@ -313,6 +317,179 @@ int oracle_normalized(int64_t B, int64_t H, int64_t T, int dk, int dv, int gate,
         if (z_final) memcpy(z_final + (size_t)bh * dk, z, (size_t)dk * sizeof(double));
         free(S);
         free(z);
+    }
+    return failed ? 6 : 0;
+}
+
+/*
+ * Backward pass of the token recurrence above (the gradients the chunkwise
+ * form is trained with: [BA] "Chunkwise parallel" motivates the chunk form by
+ * training, and the boundary states it keeps are what a backward pass needs).
+ * Given the gradient of a loss with respect to every output o_t (do) and to the
+ * final state S_T (dsT, NULL for zero), it returns the gradients with respect
+ * to q, k, v, g, beta and s0, by reverse-mode differentiation of each step of
+ * token_update, newest token first:
+ *
+ *   H      gradient w.r.t. S_t from everything after the read-out of token t
+ *          (starts as dsT); the read-out adds q_t^T do_t:  Ht = H + q_t^T do_t
+ *   dq_t   = do_t S_t^T
+ *   write  S_t = S' + k_t^T u :   du = k_t Ht,  dk_t += Ht u^T,  dS' = Ht
+ *   delta  u = beta (v - k S') :  dbeta_t = du . (v - vhat),  dv_t = beta du,
+ *          dvhat = -beta du,  dk_t += S' dvhat^T,  dS' += k_t^T dvhat
+ *   add    u = v :                dv_t = du
+ *   decay  S' = a S_{t-1}, a = exp(g_t):  dg_t = <dS', S'>  (channel gate: one
+ *          inner product per row), and the gradient passed to S_{t-1} is a dS'
+ *          (row-wise for the channel gate).
+ *   ds0    = the gradient left after the first token.
+ *
+ * States are recomputed rather than stored: the forward keeps S at the start of
+ * every segment of SEG tokens, and the backward replays one segment at a time
+ * with the same arithmetic (so the replayed states are bit-identical).
+ * Layouts as oracle_recurrence; do, dv [B,H,T,dv]; dq, dk [B,H,T,dk];
+ * dg like g (NULL when there is no gate); dbeta like beta (NULL for the add
+ * rule); ds0 [B,H,dk,dv] or NULL.
+ */
+enum { ORACLE_BWD_SEG = 64 };
+
+int oracle_recurrence_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int rule, int gate,
+                          const double *q, const double *k, const double *v,
+                          const double *g, const double *beta, const double *s0,
+                          const double *dout, const double *dsT,
+                          double *dq, double *dk_out, double *dv_out, double *dg,
+                          double *dbeta, double *ds0, int nthreads)
+{
+    int rc = check_args(B, H, T, dk, dv, rule, gate, q, k, v, g, beta, dout);
+    if (rc) return rc;
+    if (B * H * T > 0 && (!dq || !dk_out || !dv_out)) return 1;
+    if (gate != ORACLE_GATE_NONE && B * H * T > 0 && !dg) return 1;
+    if (rule == ORACLE_RULE_DELTA && B * H * T > 0 && !dbeta) return 1;
+    int64_t nheads = B * H;
+    size_t ss = (size_t)dk * dv;
+    int64_t nseg = (T + ORACLE_BWD_SEG - 1) / ORACLE_BWD_SEG;
+    int64_t bh;
+    int failed = 0;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : failed)
+#else
+    (void)nthreads;
+#endif
+    for (bh = 0; bh < nheads; ++bh) {
+        /* segment start states, the decayed states S' of one segment, the
+         * running gradient and small vectors */
+        double *ck = (double *)malloc((size_t)(nseg + 1) * ss * sizeof(double));
+        double *Sd = (double *)malloc((size_t)ORACLE_BWD_SEG * ss * sizeof(double));
+        double *Hg = (double *)malloc(ss * sizeof(double));
+        double *St = (double *)malloc(ss * sizeof(double));
+        double *u = (double *)malloc((size_t)dv * sizeof(double));
+        double *vh = (double *)malloc((size_t)dv * sizeof(double));
+        double *du = (double *)malloc((size_t)dv * sizeof(double));
+        double *ot = (double *)malloc((size_t)dv * sizeof(double));
+        if (!ck || !Sd || !Hg || !St || !u || !vh || !du || !ot) {
+            free(ck); free(Sd); free(Hg); free(St); free(u); free(vh); free(du); free(ot);
+            failed |= 1;
+            continue;
+        }
+        int i, j;
+        int64_t t, sg;
+        /* forward: keep the state at the start of every segment */
+        if (s0 == NULL) memset(St, 0, ss * sizeof(double));
+        else memcpy(St, s0 + (size_t)bh * ss, ss * sizeof(double));
+        for (t = 0; t < T; ++t) {
+            if (t % ORACLE_BWD_SEG == 0) memcpy(ck + (size_t)(t / ORACLE_BWD_SEG) * ss, St, ss * sizeof(double));
+            size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+            const double *gt = gate == ORACLE_GATE_SCALAR ? g + tok : gate == ORACLE_GATE_CHANNEL ? g + tok * dk : NULL;
+            token_update(dk, dv, rule, gate, q + tok * dk, k + tok * dk, v + tok * dv, gt,
+                         rule == ORACLE_RULE_DELTA ? beta[tok] : 0.0, St, ot, u);
+        }
+        /* backward */
+        if (dsT) memcpy(Hg, dsT + (size_t)bh * ss, ss * sizeof(double));
+        else memset(Hg, 0, ss * sizeof(double));
+        for (sg = nseg - 1; sg >= 0; --sg) {
+            int64_t ta = sg * ORACLE_BWD_SEG;
+            int64_t tb = ta + ORACLE_BWD_SEG < T ? ta + ORACLE_BWD_SEG : T;
+            /* replay the segment, keeping Sd[t - ta] = S' of token t (the decayed S_{t-1}) */
+            memcpy(St, ck + (size_t)sg * ss, ss * sizeof(double));
+            for (t = ta; t < tb; ++t) {
+                size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+                const double *gt = gate == ORACLE_GATE_SCALAR ? g + tok : gate == ORACLE_GATE_CHANNEL ? g + tok * dk : NULL;
+                double *sd = Sd + (size_t)(t - ta) * ss;
+                for (i = 0; i < dk; ++i) {
+                    double a = gate == ORACLE_GATE_SCALAR ? exp(gt[0]) : gate == ORACLE_GATE_CHANNEL ? exp(gt[i]) : 1.0;
+                    for (j = 0; j < dv; ++j) sd[(size_t)i * dv + j] = a * St[(size_t)i * dv + j];
+                }
+                token_update(dk, dv, rule, gate, q + tok * dk, k + tok * dk, v + tok * dv, gt,
+                             rule == ORACLE_RULE_DELTA ? beta[tok] : 0.0, St, ot, u);
+            }
+            for (t = tb - 1; t >= ta; --t) {
+                size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+                const double *qt = q + tok * dk, *kt = k + tok * dk, *vt = v + tok * dv;
+                const double *dot = dout + tok * dv;
+                const double *sd = Sd + (size_t)(t - ta) * ss;
+                double bt = 0.0;
+                if (rule == ORACLE_RULE_DELTA) bt = beta[tok];
+                /* vhat and u of this token, and S_t = S' + k^T u */
+                for (j = 0; j < dv; ++j) {
+                    double p = 0.0;
+                    for (i = 0; i < dk; ++i) p += kt[i] * sd[(size_t)i * dv + j];
+                    vh[j] = p;
+                    u[j] = rule == ORACLE_RULE_DELTA ? bt * (vt[j] - p) : vt[j];
+                }
+                for (i = 0; i < dk; ++i)
+                    for (j = 0; j < dv; ++j) St[(size_t)i * dv + j] = sd[(size_t)i * dv + j] + kt[i] * u[j];
+                /* read-out o_t = q_t S_t */
+                for (i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (j = 0; j < dv; ++j) acc += dot[j] * St[(size_t)i * dv + j];
+                    dq[tok * dk + i] = acc;
+                }
+                for (i = 0; i < dk; ++i)
+                    for (j = 0; j < dv; ++j) Hg[(size_t)i * dv + j] += qt[i] * dot[j];
+                /* write S_t = S' + k^T u */
+                for (j = 0; j < dv; ++j) {
+                    double acc = 0.0;
+                    for (i = 0; i < dk; ++i) acc += kt[i] * Hg[(size_t)i * dv + j];
+                    du[j] = acc;
+                }
+                for (i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (j = 0; j < dv; ++j) acc += Hg[(size_t)i * dv + j] * u[j];
+                    dk_out[tok * dk + i] = acc;
+                }
+                if (rule == ORACLE_RULE_DELTA) {
+                    double db = 0.0;
+                    for (j = 0; j < dv; ++j) db += du[j] * (vt[j] - vh[j]);
+                    dbeta[tok] = db;
+                    for (j = 0; j < dv; ++j) dv_out[tok * dv + j] = bt * du[j];
+                    /* dvhat = -beta du, into k and into S' */
+                    for (i = 0; i < dk; ++i) {
+                        double acc = 0.0;
+                        for (j = 0; j < dv; ++j) acc += sd[(size_t)i * dv + j] * (-bt * du[j]);
+                        dk_out[tok * dk + i] += acc;
+                    }
+                    for (i = 0; i < dk; ++i)
+                        for (j = 0; j < dv; ++j) Hg[(size_t)i * dv + j] += kt[i] * (-bt * du[j]);
+                } else {
+                    for (j = 0; j < dv; ++j) dv_out[tok * dv + j] = du[j];
+                }
+                /* decay S' = a S_{t-1}; Hg now holds dS' */
+                if (gate == ORACLE_GATE_SCALAR) {
+                    double acc = 0.0, a = exp(g[tok]);
+                    for (i = 0; i < dk * dv; ++i) acc += Hg[i] * sd[i];
+                    dg[tok] = acc;
+                    for (i = 0; i < dk * dv; ++i) Hg[i] *= a;
+                } else if (gate == ORACLE_GATE_CHANNEL) {
+                    for (i = 0; i < dk; ++i) {
+                        double acc = 0.0, a = exp(g[tok * dk + i]);
+                        for (j = 0; j < dv; ++j) acc += Hg[(size_t)i * dv + j] * sd[(size_t)i * dv + j];
+                        dg[tok * dk + i] = acc;
+                        for (j = 0; j < dv; ++j) Hg[(size_t)i * dv + j] *= a;
+                    }
+                }
+            }
+        }
+        if (ds0) memcpy(ds0 + (size_t)bh * ss, Hg, ss * sizeof(double));
+        free(ck); free(Sd); free(Hg); free(St); free(u); free(vh); free(du); free(ot);
     }
     return failed ? 6 : 0;
 }

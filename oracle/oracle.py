@@ -7,7 +7,8 @@ It imports nothing from the HIP package and the HIP package never imports it.
 ``recurrence`` runs the token-by-token recurrence of causal linear attention
 (add rule, decay with a scalar or per-key-channel gate, delta rule) described
 in ``oracle.c``; ``decode_step`` runs one token per (sequence, head) in place;
-``deltaproduct`` runs the Gated DeltaProduct recurrence (n_h substeps per token).
+``deltaproduct`` runs the Gated DeltaProduct recurrence (n_h substeps per token);
+``recurrence_bwd`` returns the recurrence's gradients (reverse mode, fp64).
 Every input is widened to float64 exactly (bf16 and fp32 values are exact in
 fp64), so the oracle sees the very values a GPU kernel received.
 """
@@ -77,6 +78,9 @@ class OracleLib:
         lib.oracle_normalized.argtypes = [i64, i64, i64, i32, i32, i32, d, d, d, d, d, d, d, d, d,
                                           i32]
         lib.oracle_normalized.restype = i32
+        lib.oracle_recurrence_bwd.argtypes = [i64, i64, i64, i32, i32, i32, i32,
+                                              d, d, d, d, d, d, d, d, d, d, d, d, d, d, i32]
+        lib.oracle_recurrence_bwd.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         self.lib = lib
@@ -173,6 +177,50 @@ def _deltaproduct(self, q, k, v, g=None, beta=None, s0=None, *, gate="scalar", n
 
 
 OracleLib.deltaproduct = _deltaproduct
+
+
+def _recurrence_bwd(self, q, k, v, g=None, beta=None, s0=None, do=None, dsT=None, *, rule="delta",
+                    gate="scalar", nthreads: int = 0):
+    """fp64 gradients of the token recurrence (see ``oracle.c``) for the loss
+    sum(do * o) + sum(dsT * S_T).  Shapes as ``recurrence``; do [B,H,T,dv];
+    dsT [B,H,dk,dv] or None.  Returns a dict with dq, dk, dv, dg (None without a
+    gate), dbeta (None for the add rule) and ds0, all float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g, beta, s0, do, dsT = _f64(g), _f64(beta), _f64(s0), _f64(do), _f64(dsT)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, H, T, dk) or v.shape != (B, H, T, dv):
+        raise ValueError("q/k/v shapes disagree")
+    if do is None or do.shape != (B, H, T, dv):
+        raise ValueError("do must be [B,H,T,dv]")
+    if gate == "scalar" and (g is None or g.shape != (B, H, T)):
+        raise ValueError("scalar gate needs g of shape [B,H,T]")
+    if gate == "channel" and (g is None or g.shape != (B, H, T, dk)):
+        raise ValueError("channel gate needs g of shape [B,H,T,dk]")
+    if rule == "delta" and (beta is None or beta.shape != (B, H, T)):
+        raise ValueError("delta rule needs beta of shape [B,H,T]")
+    for name, a in (("s0", s0), ("dsT", dsT)):
+        if a is not None and a.shape != (B, H, dk, dv):
+            raise ValueError(f"{name} must be [B,H,dk,dv]")
+    if gate == "none":
+        g = None
+    if rule == "add":
+        beta = None
+    out = {"dq": np.empty((B, H, T, dk)), "dk": np.empty((B, H, T, dk)),
+           "dv": np.empty((B, H, T, dv)), "ds0": np.empty((B, H, dk, dv)),
+           "dg": None if g is None else np.empty(g.shape),
+           "dbeta": None if beta is None else np.empty((B, H, T))}
+    rc = self.lib.oracle_recurrence_bwd(B, H, T, dk, dv, RULES[rule], GATES[gate], _ptr(q), _ptr(k),
+                                        _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(do), _ptr(dsT),
+                                        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                        _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]),
+                                        int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_recurrence_bwd failed with code {rc}")
+    return out
+
+
+OracleLib.recurrence_bwd = _recurrence_bwd
 
 
 def _normalized(self, q, k, v, g=None, s0=None, z0=None, *, gate="none", nthreads: int = 0):
@@ -274,6 +322,11 @@ def decode_step(*args, **kw):
 def deltaproduct(*args, **kw):
     """See :meth:`OracleLib.deltaproduct`."""
     return default().deltaproduct(*args, **kw)
+
+
+def recurrence_bwd(*args, **kw):
+    """See :meth:`OracleLib.recurrence_bwd`."""
+    return default().recurrence_bwd(*args, **kw)
 
 
 def normalized(*args, **kw):

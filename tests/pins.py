@@ -547,6 +547,121 @@ def pin_normalized_invariants(orc):
                 "equal-channel gate != scalar gate (normalised)"
 
 
+# ---------------------------------------------------------------------------
+# Backward pass.  The gradients of loss = sum(do . o) + sum(dsT . S_T) with
+# respect to q, k, v, g, beta and s0 ([BA] "Chunkwise parallel": the chunk form
+# exists for training, whose backward pass these are).
+# ---------------------------------------------------------------------------
+BWD_NAMES = (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"), ("s0", "ds0"))
+
+
+def _bwd_case(rng, T, dk, dv, rule, gate, B=1, H=1):
+    q, k, v, g, beta, S0 = rand_case(rng, B, H, T, dk, dv, gate=gate, gate_scale=0.7,
+                                     unit_keys=False)
+    do = rng.standard_normal((B, H, T, dv))
+    dsT = rng.standard_normal((B, H, dk, dv))
+    x = {"q": q, "k": k, "v": v, "g": g if gate != "none" else None,
+         "beta": beta if rule == "delta" else None, "s0": S0}
+    return x, do, dsT
+
+
+def _loss(orc, x, do, dsT, rule, gate):
+    o, S = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], rule=rule, gate=gate)
+    return float(np.sum(o * do) + np.sum(S * dsT))
+
+
+# ---------------------------------------------------------------------------
+# V17  the backward pass against central differences of the (pinned) forward:
+#      every entry of every input on tiny cases, for each rule and gate, with
+#      d_k != d_v; and random directions on a case longer than the oracle's
+#      replay segment (64 tokens).
+# ---------------------------------------------------------------------------
+def pin_bwd_finite_differences(orc):
+    rng = np.random.default_rng(117)
+    eps = 1e-6
+    for rule in ("add", "delta"):
+        for gate in ("none", "scalar", "channel"):
+            x, do, dsT = _bwd_case(rng, 6, 3, 2, rule, gate)
+            grads = orc.recurrence_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT,
+                                       rule=rule, gate=gate)
+            for name, gname in BWD_NAMES:
+                if x[name] is None:
+                    assert grads[gname] is None, f"{gname} given for an absent input"
+                    continue
+                fd = np.zeros_like(x[name])
+                for idx in np.ndindex(x[name].shape):
+                    xp = dict(x); xp[name] = x[name].copy(); xp[name][idx] += eps
+                    xm = dict(x); xm[name] = x[name].copy(); xm[name][idx] -= eps
+                    fd[idx] = (_loss(orc, xp, do, dsT, rule, gate) - _loss(orc, xm, do, dsT, rule, gate)) / (2 * eps)
+                err = np.max(np.abs(grads[gname] - fd)) / max(1.0, np.max(np.abs(fd)))
+                assert err < 1e-7, f"{gname} vs central differences ({rule}/{gate}): {err:.2e}"
+    # 150 tokens: three replay segments; directional derivatives
+    for rule, gate in (("delta", "scalar"), ("add", "channel")):
+        x, do, dsT = _bwd_case(rng, 150, 4, 3, rule, gate)
+        x["q"] /= 2.0
+        grads = orc.recurrence_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT,
+                                   rule=rule, gate=gate)
+        for _ in range(3):
+            dirs = {n: (None if x[n] is None else rng.standard_normal(x[n].shape)) for n, _g in BWD_NAMES}
+            xp = {n: (None if x[n] is None else x[n] + eps * dirs[n]) for n in x}
+            xm = {n: (None if x[n] is None else x[n] - eps * dirs[n]) for n in x}
+            fd = (_loss(orc, xp, do, dsT, rule, gate) - _loss(orc, xm, do, dsT, rule, gate)) / (2 * eps)
+            an = sum(float(np.sum(grads[gn] * dirs[n])) for n, gn in BWD_NAMES if x[n] is not None)
+            assert abs(an - fd) < 1e-6 * max(1.0, abs(fd)), \
+                f"directional derivative ({rule}/{gate}, T=150): {an} vs {fd}"
+
+
+# ---------------------------------------------------------------------------
+# V18  the backward pass against automatic differentiation (torch, fp64) of
+#      the one-chunk parallel form: C = T, incoming state s0 (the special case
+#      of the chunkwise equations in [LAV] "Chunkwise algorithm", the GDN and
+#      KDA tables, which pin V10 ties to the recurrence).  A different formula,
+#      differentiated by a library.
+# ---------------------------------------------------------------------------
+def _one_chunk_torch(q, k, v, g, beta, s0, rule, gate):
+    import torch
+    T, dk = q.shape
+    if gate == "none":
+        G = torch.zeros((T, dk), dtype=q.dtype)
+    elif gate == "scalar":
+        G = torch.cumsum(g, 0)[:, None].expand(T, dk)
+    else:
+        G = torch.cumsum(g, 0)
+    dec = torch.exp(G[:, None, :] - G[None, :, :])               # [l, m, c]
+    incl = torch.tril(torch.ones((T, T), dtype=q.dtype))
+    A = torch.einsum("lc,lmc,mc->lm", q, dec, k) * incl
+    Qd, Kd = torch.exp(G) * q, torch.exp(G) * k
+    Kr = torch.exp(G[-1][None, :] - G) * k
+    if rule == "delta":
+        Lm = torch.einsum("lc,lmc,mc->lm", k, dec, k) * (incl - torch.eye(T, dtype=q.dtype))
+        M = torch.eye(T, dtype=q.dtype) + beta[:, None] * Lm
+        Z = torch.linalg.solve(M, beta[:, None] * (v - Kd @ s0))
+    else:
+        Z = v
+    o = Qd @ s0 + A @ Z
+    S = torch.exp(G[-1])[:, None] * s0 + Kr.T @ Z
+    return o, S
+
+
+def pin_bwd_autograd_one_chunk(orc):
+    import torch
+    rng = np.random.default_rng(118)
+    for rule in ("add", "delta"):
+        for gate in ("none", "scalar", "channel"):
+            x, do, dsT = _bwd_case(rng, 37, 5, 4, rule, gate)
+            grads = orc.recurrence_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT,
+                                       rule=rule, gate=gate)
+            tx = {n: (None if a is None else torch.tensor(a[0, 0], requires_grad=True)) for n, a in x.items()}
+            o, S = _one_chunk_torch(tx["q"], tx["k"], tx["v"], tx["g"], tx["beta"], tx["s0"], rule, gate)
+            loss = (o * torch.tensor(do[0, 0])).sum() + (S * torch.tensor(dsT[0, 0])).sum()
+            loss.backward()
+            for name, gname in BWD_NAMES:
+                if tx[name] is None:
+                    continue
+                assert rel_err(grads[gname][0, 0], tx[name].grad.numpy()) < 1e-10, \
+                    f"{gname} vs autograd of the one-chunk form ({rule}/{gate})"
+
+
 PINS = [
     pin_add_equals_masked_quadratic,
     pin_decay_equals_gamma_form,
@@ -567,4 +682,6 @@ PINS = [
     pin_deltaproduct_virtual_sequence,
     pin_normalized_quadratic_form,
     pin_normalized_invariants,
+    pin_bwd_finite_differences,
+    pin_bwd_autograd_one_chunk,
 ]

@@ -57,6 +57,21 @@ MUTANTS = [
     ("norm_channel_gate_reversed", [(": gate == ORACLE_GATE_CHANNEL ? exp(g[tok * dk + r]) : 1.0;",
                                      ": gate == ORACLE_GATE_CHANNEL ? exp(g[tok * dk + dk - 1 - r]) : 1.0;")]),
     ("norm_not_divided", [("o[tok * dv + c] = num / den;", "o[tok * dv + c] = num;")]),
+    # backward pass
+    ("bwd_dq_from_decayed_state", [("acc += dot[j] * St[(size_t)i * dv + j];",
+                                    "acc += dot[j] * sd[(size_t)i * dv + j];")]),
+    ("bwd_no_prediction_into_key", [("dk_out[tok * dk + i] += acc;", "dk_out[tok * dk + i] += 0.0 * acc;")]),
+    ("bwd_prediction_sign", [("acc += sd[(size_t)i * dv + j] * (-bt * du[j]);",
+                              "acc += sd[(size_t)i * dv + j] * (bt * du[j]);")]),
+    ("bwd_no_correction_into_state", [("Hg[(size_t)i * dv + j] += kt[i] * (-bt * du[j]);",
+                                       "Hg[(size_t)i * dv + j] += 0.0;")]),
+    ("bwd_gate_not_passed_back", [("for (i = 0; i < dk * dv; ++i) Hg[i] *= a;", "(void)a;")]),
+    ("bwd_dbeta_with_value_only", [("db += du[j] * (vt[j] - vh[j]);", "db += du[j] * vt[j];")]),
+    ("bwd_dg_with_new_state", [("acc += Hg[i] * sd[i];", "acc += Hg[i] * St[i];")]),
+    ("bwd_channel_dg_reversed", [("dg[tok * dk + i] = acc;", "dg[tok * dk + (dk - 1 - i)] = acc;")]),
+    ("bwd_ignore_initial_state", [("if (s0 == NULL) memset(St,", "if (1) memset(St,")]),
+    ("bwd_ignore_final_state_grad", [("if (dsT) memcpy(Hg,", "if (0) memcpy(Hg,")]),
+    ("bwd_readout_grad_missing", [("Hg[(size_t)i * dv + j] += qt[i] * dot[j];", "Hg[(size_t)i * dv + j] += 0.0;")]),
 ]
 
 
