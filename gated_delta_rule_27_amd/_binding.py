@@ -23,7 +23,8 @@ DTYPES = {"fp32": 0, "bf16": 1}
 EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_workspace_bytes",
            "linattn_chunk_fwd", "linattn_decode_step", "linattn_deltaproduct_workspace_bytes",
            "linattn_deltaproduct_fwd", "linattn_chunk_fwd_prep",
-           "linattn_normalized_workspace_bytes", "linattn_chunk_fwd_normalized")
+           "linattn_normalized_workspace_bytes", "linattn_chunk_fwd_normalized",
+           "linattn_chunk_fwd_save", "linattn_chunk_bwd_workspace_bytes", "linattn_chunk_bwd")
 QK_MAPS = {"as_is": 0, "l2": 1, "elu1": 2}
 GATE_MAPS = {"as_is": 0, "neg_softplus": 1}
 BETA_MAPS = {"as_is": 0, "sigmoid": 1}
@@ -99,6 +100,14 @@ def load(path: str = LIB_PATH):
         lib.linattn_chunk_fwd_normalized.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.POINTER(PrepArgs),
                                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.linattn_chunk_fwd_normalized.restype = ctypes.c_int
+        lib.linattn_chunk_fwd_save.argtypes = [ctypes.POINTER(ChunkArgs), vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp]
+        lib.linattn_chunk_fwd_save.restype = ctypes.c_int
+        lib.linattn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.c_int]
+        lib.linattn_chunk_bwd_workspace_bytes.restype = sz
+        lib.linattn_chunk_bwd.argtypes = [ctypes.POINTER(ChunkArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.linattn_chunk_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -360,3 +369,111 @@ def chunk_fwd_normalized(q, k, v, g=None, s0=None, z0=None, *, gate="none", chun
     if st != 0:
         raise LinattnError(st, "linattn_chunk_fwd_normalized")
     return out, s_final, z_final
+
+
+def _train_inputs(q, k, v, g, beta, rule, gate):
+    """Shapes, dtype and device of a training-pass problem (gate none or scalar)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    if gate == "scalar":
+        _check(g, "g", (B, H, T), dt, dev)
+    elif gate == "none":
+        if g is not None:
+            raise ValueError("g must be None when gate='none'")
+    else:
+        raise ValueError("the training passes take gate='none' or gate='scalar'")
+    if rule == "delta":
+        _check(beta, "beta", (B, H, T), dt, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None for the add rule")
+    return B, H, T, dk, dv, dev, dt
+
+
+def chunk_states_shape(B, H, T, dk, dv, chunk=64):
+    """Shape of the per-chunk states chunk_fwd_save keeps: [B,H,ceil(T/64),dk,dv]."""
+    return (B, H, (T + chunk - 1) // chunk, dk, dv)
+
+
+def chunk_fwd_save(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar", chunk=64,
+                   out=None, s_final=None, states=None, return_state=True):
+    """Chunk forward that also returns the state entering every chunk, for
+    chunk_bwd.  Returns (o, S_T or None, states [B,H,N,dk,dv] fp32)."""
+    import torch
+    lib = load()
+    B, H, T, dk, dv, dev, dt = _train_inputs(q, k, v, g, beta, rule, gate)
+    if s0 is not None:
+        _check(s0, "s0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    if s_final is None and return_state:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif s_final is not None:
+        _check(s_final, "s_final", (B, H, dk, dv), torch.float32, dev)
+    shape = chunk_states_shape(B, H, T, dk, dv, chunk)
+    if states is None:
+        states = torch.empty(shape, dtype=torch.float32, device=dev)
+    else:
+        _check(states, "states", shape, torch.float32, dev)
+    a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=_token_dtype(q), chunk=chunk)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_chunk_fwd_save(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(s0), _ptr(out), _ptr(s_final), _ptr(states), stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_chunk_fwd_save")
+    return out, s_final, states
+
+
+def chunk_bwd_workspace_bytes(B, H, T, dk, dv, *, rule, gate, dtype="bf16", states_given=False,
+                              chunk=64) -> int:
+    a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=dtype, chunk=chunk)
+    return int(load().linattn_chunk_bwd_workspace_bytes(ctypes.byref(a), int(bool(states_given))))
+
+
+def chunk_bwd(q, k, v, g, beta, dout, s0=None, dsT=None, *, states=None, rule="delta", gate="scalar",
+              chunk=64, workspace=None, grads=None):
+    """Backward pass of chunk_fwd: gradients of a loss given dL/do (dout
+    [B,H,T,dv], token dtype) and dL/dS_T (dsT [B,H,dk,dv] fp32 or None).
+    states: the per-chunk states from chunk_fwd_save, or None to recompute
+    them from q, k, v, g, beta and s0.  Returns a dict with dq, dk, dv, dg
+    (None without a gate), dbeta (None for the add rule) and ds0 (fp32).
+    ``grads`` may supply preallocated outputs under the same names."""
+    import torch
+    lib = load()
+    B, H, T, dk, dv, dev, dt = _train_inputs(q, k, v, g, beta, rule, gate)
+    _check(dout, "dout", (B, H, T, dv), dt, dev)
+    for t, name in ((s0, "s0"), (dsT, "dsT")):
+        if t is not None:
+            _check(t, name, (B, H, dk, dv), torch.float32, dev)
+    if states is not None:
+        _check(states, "states", chunk_states_shape(B, H, T, dk, dv, chunk), torch.float32, dev)
+    shapes = {"dq": ((B, H, T, dk), dt), "dk": ((B, H, T, dk), dt), "dv": ((B, H, T, dv), dt),
+              "dg": ((B, H, T), dt) if gate == "scalar" else None,
+              "dbeta": ((B, H, T), dt) if rule == "delta" else None,
+              "ds0": ((B, H, dk, dv), torch.float32)}
+    out = dict(grads or {})
+    for name, spec in shapes.items():
+        if spec is None:
+            out[name] = None
+        elif out.get(name) is None:
+            out[name] = torch.empty(spec[0], dtype=spec[1], device=dev)
+        else:
+            _check(out[name], name, spec[0], spec[1], dev)
+    a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=_token_dtype(q), chunk=chunk)
+    need = int(lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(a), int(states is not None)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_chunk_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                               _ptr(states), _ptr(dout), _ptr(dsT), _ptr(out["dq"]), _ptr(out["dk"]),
+                               _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]),
+                               _ptr(workspace), ws_bytes, stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_chunk_bwd")
+    return out

@@ -1,0 +1,896 @@
+// chunk_bwd.hip — backward pass of the chunkwise forward, gates none and
+// scalar, add and delta rules ("Linear Attention, Visualized", "Update the
+// state": the chunk form trains with one saved state per chunk; the per-chunk
+// quantities of "Chunkwise algorithm", the GDN table and "The triangular
+// correction system", differentiated; "Beyond attention", "Chunkwise parallel
+// training").
+//
+// Per chunk r (C = 64 local positions, G the in-chunk prefix of the log-gate,
+// D[l,m] = exp(G_l - G_m), <-Q = exp(G) Q, <-K = exp(G) K, ->K = exp(G_C - G) K,
+// A the causal decayed scores, L the strict decayed key scores,
+// T = (I + diag(beta) L)^-1, Tb = T diag(beta); forward R = V - <-K S_r,
+// Z = Tb R (add rule: Z = V)):
+//
+//   reverse state pass, newest chunk first (dS = gradient w.r.t. S_{r+1}):
+//     dZ = A^T dO + ->K dS ;  dR = Tb^T dZ ;  dS_r = exp(G_C) dS + <-Q^T dO - <-K^T dR
+//   per-chunk gradients, from S_r and dS_{r+1} alone:
+//     dv = dR ; d<-Q = dO S_r^T ; d<-K = -dR S_r^T ; d->K = Z dS^T
+//     dA = dO Z^T (causal) ; dTb = dZ R^T (causal)
+//     dbeta_m = sum_l T[l,m] dTb[l,m] + sum_k dM[m,k] L[m,k],  dM = -T^T dTb Tb^T
+//     dL = diag(beta) dM (strict) ; P = dA . D ; P2 = dL . D
+//     dq = exp(G) d<-Q + P K
+//     dk = exp(G) d<-K + exp(G_C - G) d->K + P^T Q + (P2 + P2^T) K
+//     dG_l = q_l.(exp(G_l) d<-Q_l) + k_l.(exp(G_l) d<-K_l) - k_l.(exp(G_C-G_l) d->K_l)
+//            + rowsum_l(dA.A) - colsum_l(dA.A) + rowsum_l(dL.L) - colsum_l(dL.L)
+//     dG_C += sum_l k_l.(exp(G_C-G_l) d->K_l) + exp(G_C) <S_r, dS>
+//     dg = reverse prefix sum of dG within the chunk.
+//
+// Three kernels: bwd_ops_kernel (per chunk, parallel) prepares the operands of
+// the reverse state pass; bwd_chain_kernel runs that pass per (head, 64 value
+// columns) and stores dS_{r+1} of every chunk; bwd_grad_kernel (per chunk,
+// parallel) forms every gradient of its chunk.  The incoming states S_r come
+// from the forward (chunk_fused_kernel with SAVE).  Padding rows of a ragged
+// last chunk are zero (q = k = v = dO = 0, g = 0, beta = 0), as in the forward.
+//
+// The 16x16 products read their operands from LDS in either orientation
+// (tile<>): a product of this pass has several operand orientations, and every
+// matrix is kept once.
+#include "device_common.h"
+#include "launch.h"
+#include "mfma.h"
+#include "prep.h"
+
+namespace linattn {
+
+namespace {
+
+constexpr int kC = 64;
+constexpr int kNT = 512;                 // 8 waves
+typedef __attribute__((__vector_size__(16))) int i4;
+
+template <typename T> using F16 = typename Frag16<T>::type;
+
+// K = 16 operand fragment of lane l at contraction offset k0: element
+// (x0 + l%16, k0 + 4(l/16) + r), r = 0..3, of a matrix whose element (x, k) is
+// stored at P[x*ld + k] (frag_xk, one vector read) or at P[k*ld + x] (frag_kx).
+// x is the output row for an A operand and the output column for a B operand.
+template <typename T>
+__device__ __forceinline__ F16<T> frag_xk(const T* P, int ld, int x0, int k0, int lane)
+{
+    return *reinterpret_cast<const F16<T>*>(P + (x0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+}
+
+template <typename T>
+__device__ __forceinline__ F16<T> frag_kx(const T* P, int ld, int x0, int k0, int lane)
+{
+    const T* p = P + (k0 + 4 * (lane >> 4)) * ld + x0 + (lane & 15);
+    F16<T> f;
+    f[0] = p[0];
+    f[1] = p[ld];
+    f[2] = p[2 * ld];
+    f[3] = p[3 * ld];
+    return f;
+}
+
+// acc += sum_{k in [kb, ke)} A(m0 + ., k) B(k, n0 + .) as a 16x16 result tile
+// (lane l holds D[4(l/16) + r][l%16]); AXK / BXK: operand stored as (x, k)
+// rows, else as (k, x) rows.
+template <typename T, bool AXK, bool BXK>
+__device__ __forceinline__ floatx4 tile(floatx4 acc, const T* A, int lda, int m0, const T* B, int ldb,
+                                        int n0, int kb, int ke, int lane)
+{
+    for (int k0 = kb; k0 < ke; k0 += 16) {
+        F16<T> a, b;
+        if constexpr (AXK) a = frag_xk(A, lda, m0, k0, lane);
+        else a = frag_kx(A, lda, m0, k0, lane);
+        if constexpr (BXK) b = frag_xk(B, ldb, n0, k0, lane);
+        else b = frag_kx(B, ldb, n0, k0, lane);
+        acc = mma16<T>(a, b, acc);
+    }
+    return acc;
+}
+
+// result tile into P[m*ld + n] (row-major)
+template <typename T>
+__device__ __forceinline__ void put(T* P, int ld, int m0, int n0, floatx4 v, int lane)
+{
+    T* p = P + (m0 + 4 * (lane >> 4)) * ld + n0 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r * ld] = from_f32<T>(v[r]);
+}
+
+// (lj, mi) of the p-th causal 16x16 tile (mi <= lj), row-major over lj
+__device__ __forceinline__ void causal_tile(int p, int& lj, int& mi)
+{
+    lj = 0;
+    while (p > lj) { p -= lj + 1; ++lj; }
+    mi = p;
+}
+
+template <typename T, int DK>
+struct BwdCfg {
+    static constexpr int PAD = 16 / sizeof(T);       // 16-byte row padding
+    static constexpr int E = 16 / sizeof(T);         // elements per 16-byte vector
+    static constexpr int LDQ = DK + PAD;             // rows of length dk
+    static constexpr int LDC = kC + PAD;             // rows of length C
+    static constexpr int J = sizeof(T) == 2 ? 32 : 16;   // value columns per step of the gradient kernel
+    static constexpr int LDJ = J + PAD;
+    static constexpr int LDF = kC + 4;               // fp32 scratch rows
+    // per-chunk operands of the reverse state pass: A^T, Tb^T [C][C],
+    // ->K [C][dk], <-Q^T, -<-K^T [dk][C] (token type, dense)
+    static constexpr int OPS = 2 * kC * kC + 3 * kC * DK;
+    static constexpr int O_AQT = 0, O_TBT = kC * kC, O_KR = 2 * kC * kC, O_QDT = O_KR + kC * DK,
+                         O_NKDT = O_QDT + DK * kC;
+};
+
+// Shared front of the two per-chunk kernels: chunk r's q and k (zero rows past
+// the end), the in-chunk gate prefix G, exp(G), beta, the causal decayed
+// scores A, the strict decayed key scores L and, for the delta rule,
+// T = (I + diag(beta) L)^-1 and Tb = T diag(beta), all in LDS.
+template <typename T, int DK>
+struct IntraLds {
+    T *Qs, *Ks, *Aq, *Lm, *Tm, *Tb;
+    float *G, *gam, *bet;
+};
+
+template <typename T, int DK, int RULE, int GATE>
+__device__ void intra_chunk(const IntraLds<T, DK>& L, const T* __restrict__ q, const T* __restrict__ k,
+                            const T* __restrict__ g, const T* __restrict__ beta, int64_t bh, int64_t Tlen,
+                            int64_t t0, int tvalid, int tid)
+{
+    using C = BwdCfg<T, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, E = C::E;
+    constexpr bool DELTA = RULE == kRuleDelta, GATED = GATE == kGateScalar;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    // A, L and T are written on their causal part only: clear them
+    {
+        constexpr int NZ = 3 * kC * LDC * (int)sizeof(T) / 16;
+        i4* z = reinterpret_cast<i4*>(L.Aq);   // Aq, Lm, Tm are contiguous
+        for (int i = tid; i < NZ; i += kNT) z[i] = i4{0, 0, 0, 0};
+    }
+    {
+        constexpr int VR = DK / E;
+        for (int i = tid; i < kC * VR; i += kNT) {
+            const int row = i / VR, c = (i % VR) * E;
+            i4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+            if (row < tvalid) {
+                a = *reinterpret_cast<const i4*>(q + (bh * Tlen + t0 + row) * DK + c);
+                b = *reinterpret_cast<const i4*>(k + (bh * Tlen + t0 + row) * DK + c);
+            }
+            *reinterpret_cast<i4*>(L.Qs + row * LDQ + c) = a;
+            *reinterpret_cast<i4*>(L.Ks + row * LDQ + c) = b;
+        }
+    }
+    if (wave == 0) {
+        float gl = 0.f, bl = 0.f;
+        if (lane < tvalid) {
+            if constexpr (GATED) gl = to_f32(g[bh * Tlen + t0 + lane]);
+            if constexpr (DELTA) bl = to_f32(beta[bh * Tlen + t0 + lane]);
+        }
+        const float G = wave_prefix_sum(gl);
+        L.G[lane] = G;
+        L.gam[lane] = GATED ? expf(G) : 1.f;
+        L.bet[lane] = bl;
+    }
+    __syncthreads();
+
+    // A (causal) and L (strict): 10 causal tiles each
+    {
+        constexpr int NJOB = DELTA ? 20 : 10;
+        for (int j = wave; j < NJOB; j += 8) {
+            const bool isL = j >= 10;
+            int lb, mb;
+            causal_tile(isL ? j - 10 : j, lb, mb);
+            floatx4 acc = tile<T, true, true>(zero4(), isL ? L.Ks : L.Qs, LDQ, 16 * lb, L.Ks, LDQ, 16 * mb, 0,
+                                              DK, lane);
+            const int m = 16 * mb + (lane & 15);
+            floatx4 val;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int l = 16 * lb + 4 * (lane >> 4) + r;
+                const float d = GATED ? expf(fminf(L.G[l] - L.G[m], 0.f)) : 1.f;
+                val[r] = (isL ? m < l : m <= l) ? acc[r] * d : 0.f;
+            }
+            put(isL ? L.Lm : L.Aq, LDC, 16 * lb, 16 * mb, val, lane);
+        }
+    }
+    __syncthreads();
+    if constexpr (DELTA) {
+        // diagonal 16x16 blocks of T by forward substitution, fp32: lane = (block
+        // b, column j); x_i = [i == j] - beta_i sum_{s < i} L_is x_s
+        if (wave == 0) {
+            const int b = lane >> 4, j = lane & 15;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = i == j ? 1.f : 0.f;
+                const T* lrow = L.Lm + (16 * b + i) * LDC + 16 * b;
+                float s = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < i; ++s2) s += to_f32(lrow[s2]) * x[s2];
+                x[i] = acc - L.bet[16 * b + i] * s;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) L.Tm[(16 * b + i) * LDC + 16 * b + j] = from_f32<T>(x[i]);
+        }
+        __syncthreads();
+        // blocks below the diagonal, one diagonal of blocks at a time:
+        // T_ij = -T_ii diag(beta_i) sum_{s=j}^{i-1} L_is T_sj
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {
+                const int i = wave + d, j = wave;
+                floatx4 y = tile<T, true, false>(zero4(), L.Lm, LDC, 16 * i, L.Tm, LDC, 16 * j, 16 * j, 16 * i, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] *= -L.bet[16 * i + 4 * (lane >> 4) + r];
+                const floatx4 t = mma16<T>(frag_xk(L.Tm, LDC, 16 * i, 16 * i, lane), frag16_acc<T>(y), zero4());
+                put(L.Tm, LDC, 16 * i, 16 * j, t, lane);
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < kC * kC; i += kNT) {
+            const int l = i / kC, m = i % kC;
+            L.Tb[l * LDC + m] = from_f32<T>(to_f32(L.Tm[l * LDC + m]) * L.bet[m]);
+        }
+        __syncthreads();
+    }
+}
+
+// ============================================================================
+// bwd_ops_kernel: per chunk, the operands of the reverse state pass.
+// ============================================================================
+template <typename T, int DK, int RULE, int GATE>
+__global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const T* __restrict__ g, const T* __restrict__ beta,
+                                                         T* __restrict__ ops, float* __restrict__ gC,
+                                                         int64_t Tlen, int64_t nchunks)
+{
+    using C = BwdCfg<T, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, E = C::E;
+    constexpr bool DELTA = RULE == kRuleDelta, GATED = GATE == kGateScalar;
+    __shared__ __align__(16) T Qs[kC * LDQ], Ks[kC * LDQ];
+    __shared__ __align__(16) T CC[4 * kC * LDC];    // Aq, Lm, Tm, Tb
+    __shared__ __align__(16) float G[kC], gam[kC], bet[kC];
+
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x / nchunks, r = blockIdx.x % nchunks;
+    const int64_t t0 = r * kC;
+    const int tvalid = (int)(Tlen - t0 < kC ? Tlen - t0 : kC);
+    IntraLds<T, DK> L{Qs, Ks, CC, CC + kC * LDC, CC + 2 * kC * LDC, CC + 3 * kC * LDC, G, gam, bet};
+    intra_chunk<T, DK, RULE, GATE>(L, q, k, g, beta, bh, Tlen, t0, tvalid, tid);
+
+    T* out = ops + (bh * nchunks + r) * (int64_t)C::OPS;
+    auto store = [&](T* dst, const float* x) {
+        T e[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) e[i] = from_f32<T>(x[i]);
+        i4 w;
+        __builtin_memcpy(&w, e, 16);
+        *reinterpret_cast<i4*>(dst) = w;
+    };
+    float x[E];
+    // A^T and Tb^T: row l holds column l of A / Tb
+    for (int v = tid; v < kC * kC / E; v += kNT) {
+        const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+#pragma unroll
+        for (int i = 0; i < E; ++i) x[i] = to_f32(L.Aq[(m0 + i) * LDC + l]);
+        store(out + C::O_AQT + l * kC + m0, x);
+        if constexpr (DELTA) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) x[i] = to_f32(L.Tb[(m0 + i) * LDC + l]);
+            store(out + C::O_TBT + l * kC + m0, x);
+        }
+    }
+    // ->K = exp(G_C - G) K
+    for (int v = tid; v < kC * DK / E; v += kNT) {
+        const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
+        const float s = GATED ? expf(G[kC - 1] - G[l]) : 1.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) x[i] = to_f32(Ks[l * LDQ + i0 + i]) * s;
+        store(out + C::O_KR + l * DK + i0, x);
+    }
+    // <-Q^T and -<-K^T: row i holds key channel i over the chunk
+    for (int v = tid; v < DK * kC / E; v += kNT) {
+        const int i = v / (kC / E), m0 = (v % (kC / E)) * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = to_f32(Qs[(m0 + e) * LDQ + i]) * gam[m0 + e];
+        store(out + C::O_QDT + i * kC + m0, x);
+        if constexpr (DELTA) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = -to_f32(Ks[(m0 + e) * LDQ + i]) * gam[m0 + e];
+            store(out + C::O_NKDT + i * kC + m0, x);
+        }
+    }
+    if (tid == 0) gC[bh * nchunks + r] = gam[kC - 1];
+}
+
+// ============================================================================
+// bwd_chain_kernel: the reverse state pass.  One workgroup per (b, h, 64 value
+// columns): waves 0-3 own 16 columns of dS each (dk/16 result tiles, kept in
+// registers for the whole sequence) and touch no global memory but their
+// dstates stores; waves 4-7 move the chunk operands from HBM to LDS.
+// Per chunk, newest first: store dS (= dS_{r+1}); phase 1 dZ = A^T dO + ->K dS,
+// dR = Tb^T dZ while the helpers stage <-Q^T, -<-K^T; phase 2
+// dS = exp(G_C) dS + <-Q^T dO - <-K^T dR while they stage the previous chunk's
+// A^T, Tb^T, ->K and dO^T (dO^T double-buffered, phase 2 reads it).
+// ============================================================================
+template <typename T, int DK, int RULE>
+__global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__ dout, const T* __restrict__ ops,
+                                                           const float* __restrict__ gC, const float* dsT,
+                                                           float* __restrict__ dstates, float* ds0,
+                                                           int64_t Tlen, int64_t nchunks, int DV)
+{
+    using C = BwdCfg<T, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, E = C::E, ND = DK / 16;
+    constexpr bool DELTA = RULE == kRuleDelta;
+    constexpr int NH = 256;                            // helper threads
+    constexpr int NA = kC * kC / E / NH;               // [C][C] vectors per helper thread
+    constexpr int NK = kC * DK / E / NH;               // [C][dk] / [dk][C]
+    constexpr int NO = kC * 64 / E / NH;               // dO block
+    static_assert(NA >= 1 && NK >= 1 && NO >= 1, "staging split");
+
+    __shared__ __align__(16) T AqT[kC * LDC];
+    __shared__ __align__(16) T TbT[DELTA ? kC * LDC : 8];
+    __shared__ __align__(16) T Kr[kC * LDQ];
+    __shared__ __align__(16) T QdT[DK * LDC];
+    __shared__ __align__(16) T NKdT[DELTA ? DK * LDC : 8];
+    __shared__ __align__(16) T dOT[2][64 * LDC];       // dO^T of the block: row j, column m
+    __shared__ float gCs[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nvb = DV / 64;
+    const int64_t bh = blockIdx.x / nvb;
+    const int vb = blockIdx.x % nvb;
+
+    if (wave < 4) {
+        const int n0 = 16 * wave;
+        const int cl = lane & 15, g4 = 4 * (lane >> 4);
+        const int64_t col = (int64_t)vb * 64 + n0 + cl;
+        floatx4 dS[ND];
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                dS[db][rr] = dsT ? dsT[(bh * DK + 16 * db + g4 + rr) * DV + col] : 0.f;
+        wait_vmem_all();
+        __syncthreads();
+        for (int64_t c = nchunks - 1; c >= 0; --c) {
+            const int ln = opaque(lane);
+            const int buf = (int)(c & 1);
+            float* dsr = dstates + ((bh * nchunks + c) * DK + g4) * DV + col;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) dsr[(16 * db + rr) * DV] = dS[db][rr];
+            // ---- phase 1: dZ = A^T dO + ->K dS ; dR = Tb^T dZ ----
+            floatx4 X[4], dR[4];
+#pragma unroll
+            for (int li = 0; li < 4; ++li) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    if (mb >= li)
+                        acc = mma16<T>(frag_xk(AqT, LDC, 16 * li, 16 * mb, ln),
+                                       frag_xk(dOT[buf], LDC, n0, 16 * mb, ln), acc);
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+                    acc = mma16<T>(frag_xk(Kr, LDQ, 16 * li, 16 * db, ln), frag16_acc<T>(dS[db]), acc);
+                X[li] = acc;
+            }
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int li = 0; li < 4; ++li) {
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        if (mb >= li)
+                            acc = mma16<T>(frag_xk(TbT, LDC, 16 * li, 16 * mb, ln), frag16_acc<T>(X[mb]), acc);
+                    dR[li] = acc;
+                }
+            }
+            lds_barrier();
+            // ---- phase 2: dS = exp(G_C) dS + <-Q^T dO - <-K^T dR ----
+            const float gc = gCs[buf];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                floatx4 acc = dS[db] * gc;
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    acc = mma16<T>(frag_xk(QdT, LDC, 16 * db, 16 * mb, ln), frag_xk(dOT[buf], LDC, n0, 16 * mb, ln),
+                                   acc);
+                if constexpr (DELTA) {
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        acc = mma16<T>(frag_xk(NKdT, LDC, 16 * db, 16 * mb, ln), frag16_acc<T>(dR[mb]), acc);
+                }
+                dS[db] = acc;
+            }
+            lds_barrier();
+        }
+        if (ds0) {
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) ds0[(bh * DK + 16 * db + g4 + rr) * DV + col] = dS[db][rr];
+        }
+    } else {
+        const int ht = tid - 256;
+        i4 ra[NA], rt[NA], rk[NK], ro[NO], rq[NK], rn[NK];
+        float rg = 0.f;
+        auto load1 = [&](int64_t c) {
+            const T* base = ops + (bh * nchunks + c) * (int64_t)C::OPS;
+#pragma unroll
+            for (int p = 0; p < NA; ++p) {
+                const int e = (p * NH + ht) * E;
+                ra[p] = *reinterpret_cast<const i4*>(base + C::O_AQT + e);
+                if constexpr (DELTA) rt[p] = *reinterpret_cast<const i4*>(base + C::O_TBT + e);
+            }
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = (p * NH + ht) * E;
+                rk[p] = *reinterpret_cast<const i4*>(base + C::O_KR + e);
+            }
+#pragma unroll
+            for (int p = 0; p < NO; ++p) {
+                const int e = (p * NH + ht) * E;
+                const int row = e / 64, cc = e % 64;
+                const int64_t t = c * kC + row;
+                ro[p] = i4{0, 0, 0, 0};
+                if (t < Tlen) ro[p] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t) * DV + vb * 64 + cc);
+            }
+            rg = gC[bh * nchunks + c];
+        };
+        auto stage1 = [&](int64_t c) {
+            const int buf = (int)(c & 1);
+#pragma unroll
+            for (int p = 0; p < NA; ++p) {
+                const int e = (p * NH + ht) * E;
+                *reinterpret_cast<i4*>(AqT + (e / kC) * LDC + e % kC) = ra[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(TbT + (e / kC) * LDC + e % kC) = rt[p];
+            }
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = (p * NH + ht) * E;
+                *reinterpret_cast<i4*>(Kr + (e / DK) * LDQ + e % DK) = rk[p];
+            }
+#pragma unroll
+            for (int p = 0; p < NO; ++p) {
+                const int e = (p * NH + ht) * E;
+                const int row = e / 64, cc = e % 64;
+                T x[E];
+                __builtin_memcpy(x, &ro[p], 16);
+#pragma unroll
+                for (int i = 0; i < E; ++i) dOT[buf][(cc + i) * LDC + row] = x[i];
+            }
+            if (ht == 0) gCs[buf] = rg;
+        };
+        auto load2 = [&](int64_t c) {
+            const T* base = ops + (bh * nchunks + c) * (int64_t)C::OPS;
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = (p * NH + ht) * E;
+                rq[p] = *reinterpret_cast<const i4*>(base + C::O_QDT + e);
+                if constexpr (DELTA) rn[p] = *reinterpret_cast<const i4*>(base + C::O_NKDT + e);
+            }
+        };
+        auto stage2 = [&]() {
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = (p * NH + ht) * E;
+                *reinterpret_cast<i4*>(QdT + (e / kC) * LDC + e % kC) = rq[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(NKdT + (e / kC) * LDC + e % kC) = rn[p];
+            }
+        };
+        if (nchunks > 0) {
+            load1(nchunks - 1);
+            stage1(nchunks - 1);
+            load2(nchunks - 1);
+        }
+        __syncthreads();
+        for (int64_t c = nchunks - 1; c >= 0; --c) {
+            const int64_t cn = c > 0 ? c - 1 : 0;
+            stage2();                       // <-Q^T, -<-K^T of chunk c (read in phase 2)
+            load1(cn);
+            lds_barrier();
+            if (c > 0) stage1(cn);          // the buffers phase 1 read are free now
+            load2(cn);
+            lds_barrier();
+        }
+        wait_vmem_all();
+    }
+}
+
+// ============================================================================
+// bwd_grad_kernel: every gradient of one chunk from S_r and dS_{r+1}.
+// ============================================================================
+template <typename T, int DK, int RULE, int GATE>
+__global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
+    const T* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ states,
+    const float* __restrict__ dstates, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    T* __restrict__ dg, T* __restrict__ dbeta, int64_t Tlen, int64_t nchunks, int DV)
+{
+    using C = BwdCfg<T, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, LDJ = C::LDJ, LDF = C::LDF, J = C::J, E = C::E;
+    constexpr bool DELTA = RULE == kRuleDelta, GATED = GATE == kGateScalar;
+    constexpr int NI = DK / 32;            // key-column tiles per wave (of dq, dk)
+    constexpr int NJT = J / 16;            // value-column tiles per step
+    // the value-block arrays of the loop, and the scratch of the final phase in
+    // the same bytes
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int LOOP_BYTES = (5 * kC * LDJ + 2 * DK * LDJ) * SZ;
+    constexpr int FIN_BYTES = 2 * kC * LDF * 4;
+    constexpr int REGION = LOOP_BYTES > FIN_BYTES ? LOOP_BYTES : FIN_BYTES;
+    static_assert(kC * LDC * SZ <= kC * LDF * 4, "scratch sizes");
+
+    __shared__ __align__(16) T Qs[kC * LDQ], Ks[kC * LDQ];
+    __shared__ __align__(16) T CC[4 * kC * LDC];    // Aq (then P), Lm (then P2), Tm, Tb
+    __shared__ __align__(16) unsigned char region[REGION];
+    __shared__ __align__(16) float G[kC], gam[kC], bet[kC];
+    __shared__ float dGs[kC], dBs[kC], rowp[2][kC], rowp2[2][kC], krp[2][kC], sdp[8];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.x / nchunks, r = blockIdx.x % nchunks;
+    const int64_t t0 = r * kC;
+    const int tvalid = (int)(Tlen - t0 < kC ? Tlen - t0 : kC);
+    T* const Aq = CC;
+    T* const Lm = CC + kC * LDC;
+    T* const Tm = CC + 2 * kC * LDC;
+    T* const Tb = CC + 3 * kC * LDC;
+    IntraLds<T, DK> L{Qs, Ks, Aq, Lm, Tm, Tb, G, gam, bet};
+    intra_chunk<T, DK, RULE, GATE>(L, q, k, g, beta, bh, Tlen, t0, tvalid, tid);
+
+    T* const dOs = reinterpret_cast<T*>(region);
+    T* const Rs = dOs + kC * LDJ;
+    T* const Zs = Rs + kC * LDJ;
+    T* const dZs = Zs + kC * LDJ;
+    T* const dRs = dZs + kC * LDJ;
+    T* const Ss = dRs + kC * LDJ;
+    T* const dSs = Ss + DK * LDJ;
+
+    const int cl = lane & 15, g4 = 4 * (lane >> 4);
+    const int lbq = wave >> 1;                       // row block of this wave's dq/dk tiles
+    const int lbt = wave >> 1;                       // row block of its dA/dTb tiles
+    floatx4 dQd[NI], dKd[NI], dKr[NI], dAq[2], dTb[2];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) dQd[u] = dKd[u] = dKr[u] = zero4();
+    dAq[0] = dAq[1] = dTb[0] = dTb[1] = zero4();
+    float sdot = 0.f;
+    const float* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
+    const float* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
+
+    for (int j0 = 0; j0 < DV; j0 += J) {
+        // ---- stage dO and V (token rows), S_r and dS_{r+1} (value columns j0..j0+J) ----
+        {
+            constexpr int VR = J / E;
+            for (int i = tid; i < kC * VR; i += kNT) {
+                const int row = i / VR, c = (i % VR) * E;
+                i4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+                if (row < tvalid) {
+                    a = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t0 + row) * DV + j0 + c);
+                    b = *reinterpret_cast<const i4*>(v + (bh * Tlen + t0 + row) * DV + j0 + c);
+                }
+                *reinterpret_cast<i4*>(dOs + row * LDJ + c) = a;
+                *reinterpret_cast<i4*>(Zs + row * LDJ + c) = b;
+            }
+            constexpr int SR = J / 4;
+            for (int i = tid; i < DK * SR; i += kNT) {
+                const int row = i / SR, c = (i % SR) * 4;
+                const floatx4 a = *reinterpret_cast<const floatx4*>(Sr + row * DV + j0 + c);
+                const floatx4 b = *reinterpret_cast<const floatx4*>(dSr + row * DV + j0 + c);
+                sdot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    Ss[row * LDJ + c + x] = from_f32<T>(a[x]);
+                    dSs[row * LDJ + c + x] = from_f32<T>(b[x]);
+                }
+            }
+        }
+        __syncthreads();
+        // ---- step A: R = V - <-K S_r ; dZ = A^T dO + ->K dS ; d<-Q += dO S_r^T ----
+        if (wave < 4 * NJT) {
+            const int lb = wave / NJT, jc = wave % NJT;
+            floatx4 a1 = tile<T, false, false>(zero4(), Aq, LDC, 16 * lb, dOs, LDJ, 16 * jc, 16 * lb, kC, lane);
+            floatx4 a2 = tile<T, true, false>(zero4(), Ks, LDQ, 16 * lb, dSs, LDJ, 16 * jc, 0, DK, lane);
+            floatx4 dz;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lb + g4 + rr;
+                dz[rr] = a1[rr] + (GATED ? expf(G[kC - 1] - G[l]) : 1.f) * a2[rr];
+            }
+            put(dZs, LDJ, 16 * lb, 16 * jc, dz, lane);
+            if constexpr (DELTA) {
+                const floatx4 ks = tile<T, true, false>(zero4(), Ks, LDQ, 16 * lb, Ss, LDJ, 16 * jc, 0, DK, lane);
+                floatx4 rv;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    rv[rr] = to_f32(Zs[l * LDJ + 16 * jc + cl]) - gam[l] * ks[rr];
+                }
+                put(Rs, LDJ, 16 * lb, 16 * jc, rv, lane);
+            } else {
+                // add rule: dv = dZ
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    if (l < tvalid) dv[(bh * Tlen + t0 + l) * DV + j0 + 16 * jc + cl] = from_f32<T>(dz[rr]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NI; ++u)
+            dQd[u] = tile<T, true, true>(dQd[u], dOs, LDJ, 16 * lbq, Ss, LDJ, 16 * (NI * (wave & 1) + u), 0, J, lane);
+        __syncthreads();
+        // ---- step B (delta): Z = Tb R ; dR = Tb^T dZ (= dv) ; dTb += dZ R^T ----
+        if constexpr (DELTA) {
+            if (wave < 4 * NJT) {
+                const int lb = wave / NJT, jc = wave % NJT;
+                const floatx4 z = tile<T, true, false>(zero4(), Tb, LDC, 16 * lb, Rs, LDJ, 16 * jc, 0, 16 * lb + 16, lane);
+                const floatx4 dr = tile<T, false, false>(zero4(), Tb, LDC, 16 * lb, dZs, LDJ, 16 * jc, 16 * lb, kC, lane);
+                put(Zs, LDJ, 16 * lb, 16 * jc, z, lane);
+                put(dRs, LDJ, 16 * lb, 16 * jc, dr, lane);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    if (l < tvalid) dv[(bh * Tlen + t0 + l) * DV + j0 + 16 * jc + cl] = from_f32<T>(dr[rr]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int mb = 2 * (wave & 1) + u;
+                if (mb <= lbt) dTb[u] = tile<T, true, true>(dTb[u], dZs, LDJ, 16 * lbt, Rs, LDJ, 16 * mb, 0, J, lane);
+            }
+            __syncthreads();
+        }
+        // ---- step C: d<-K += dR S_r^T (negated later) ; d->K += Z dS^T ; dA += dO Z^T ----
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            const int ib = NI * (wave & 1) + u;
+            if constexpr (DELTA) dKd[u] = tile<T, true, true>(dKd[u], dRs, LDJ, 16 * lbq, Ss, LDJ, 16 * ib, 0, J, lane);
+            dKr[u] = tile<T, true, true>(dKr[u], Zs, LDJ, 16 * lbq, dSs, LDJ, 16 * ib, 0, J, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            if (mb <= lbt) dAq[u] = tile<T, true, true>(dAq[u], dOs, LDJ, 16 * lbt, Zs, LDJ, 16 * mb, 0, J, lane);
+        }
+        __syncthreads();
+    }
+
+    // ============ final phase ============
+    float* const sc = reinterpret_cast<float*>(region);               // fp32 [C][LDF]
+    unsigned char* const second = region + kC * LDF * 4;
+    T* const dTbs = reinterpret_cast<T*>(second);                     // [C][LDC]
+    T* const X1s = reinterpret_cast<T*>(region);                      // [C][LDC], after sc is read
+    float* const E2 = reinterpret_cast<float*>(second);               // [C][LDF], after dTbs is read
+    {
+        const float tot = wave_last(wave_prefix_sum(sdot));
+        if (lane == 0) sdp[wave] = tot;
+    }
+    // F0: dA . A to the scratch, P = dA . D over A in place; dTb to LDS
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int mb = 2 * (wave & 1) + u;
+        const int m = 16 * mb + cl;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbt + g4 + rr;
+            const bool on = mb <= lbt && m <= l;
+            const float da = on ? dAq[u][rr] : 0.f;
+            const float a = to_f32(Aq[l * LDC + m]);
+            sc[l * LDF + m] = da * a;
+            const float d = GATED ? expf(fminf(G[l] - G[m], 0.f)) : 1.f;
+            Aq[l * LDC + m] = from_f32<T>(da * d);
+            if constexpr (DELTA) dTbs[l * LDC + m] = from_f32<T>(on ? dTb[u][rr] : 0.f);
+        }
+    }
+    __syncthreads();
+    // F1: dG from dA . A; dbeta from T . dTb; X1 = T^T dTb; the row dots of the
+    // dq/dk accumulators
+    if (wave == 0) {
+        float s1 = 0.f, s2 = 0.f;
+        for (int m = 0; m < kC; ++m) {
+            s1 += sc[lane * LDF + m];
+            s2 += sc[m * LDF + lane];
+        }
+        dGs[lane] = s1 - s2;
+    }
+    if constexpr (DELTA) {
+        if (wave == 1) {
+            float s = 0.f;
+            for (int l = 0; l < kC; ++l) s += to_f32(Tm[l * LDC + lane]) * to_f32(dTbs[l * LDC + lane]);
+            dBs[lane] = s;
+        }
+    }
+    floatx4 X1[2];
+    if constexpr (DELTA) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int sb = 2 * (wave & 1) + u;
+            X1[u] = tile<T, false, false>(zero4(), Tm, LDC, 16 * lbt, dTbs, LDC, 16 * sb,
+                                          16 * (lbt > sb ? lbt : sb), kC, lane);
+        }
+    }
+    {
+        float rd[4] = {0.f, 0.f, 0.f, 0.f}, kr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            const int i = 16 * (NI * (wave & 1) + u) + cl;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbq + g4 + rr;
+                const float qv = to_f32(Qs[l * LDQ + i]), kv = to_f32(Ks[l * LDQ + i]);
+                const float er = GATED ? expf(G[kC - 1] - G[l]) : 1.f;
+                const float t3 = kv * er * dKr[u][rr];
+                rd[rr] += qv * gam[l] * dQd[u][rr] - kv * gam[l] * dKd[u][rr] - t3;
+                kr[rr] += t3;
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float a = group_sum<16>(rd[rr]), b = group_sum<16>(kr[rr]);
+            if (cl == 0) {
+                rowp[wave & 1][16 * lbq + g4 + rr] = a;
+                krp[wave & 1][16 * lbq + g4 + rr] = b;
+            }
+        }
+    }
+    __syncthreads();
+    if constexpr (DELTA) {
+        // F2: X1 to LDS (over the first scratch)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) put(X1s, LDC, 16 * lbt, 16 * (2 * (wave & 1) + u), X1[u], lane);
+        __syncthreads();
+        // F3: dM = -X1 Tb^T (causal tiles); dL = diag(beta) dM (strict);
+        // dbeta += rowsum(dM . L); dL . L to the scratch; P2 = dL . D over L
+        float rb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            const int m = 16 * mb + cl;
+            floatx4 dm = zero4();
+            if (mb <= lbt) dm = tile<T, true, true>(zero4(), X1s, LDC, 16 * lbt, Tb, LDC, 16 * mb, 0, 16 * mb + 16, lane);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbt + g4 + rr;
+                const bool strict = mb <= lbt && m < l;
+                const float dM = -dm[rr];
+                const float lv = to_f32(Lm[l * LDC + m]);
+                rb[rr] += strict ? dM * lv : 0.f;
+                const float dl = strict ? bet[l] * dM : 0.f;
+                E2[l * LDF + m] = dl * lv;
+                if (strict) Lm[l * LDC + m] = from_f32<T>(dl * (GATED ? expf(G[l] - G[m]) : 1.f));
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float a = group_sum<16>(rb[rr]);
+            if (cl == 0) rowp2[wave & 1][16 * lbt + g4 + rr] = a;
+        }
+        __syncthreads();
+    }
+    // F4: dG and dbeta totals per row; dq = exp(G) d<-Q + P K;
+    // dk = -exp(G) (dR S^T) + exp(G_C - G) d->K + P^T Q + (P2 + P2^T) K
+    if (wave == 0) {
+        float x = dGs[lane] + rowp[0][lane] + rowp[1][lane];
+        if constexpr (DELTA) {
+            float s1 = 0.f, s2 = 0.f;
+            for (int m = 0; m < kC; ++m) {
+                s1 += E2[lane * LDF + m];
+                s2 += E2[m * LDF + lane];
+            }
+            x += s1 - s2;
+        }
+        dGs[lane] = x;
+    }
+    if constexpr (DELTA) {
+        if (wave == 1) dBs[lane] += rowp2[0][lane] + rowp2[1][lane];
+    }
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        const int ib = NI * (wave & 1) + u;
+        floatx4 aq, ak;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbq + g4 + rr;
+            aq[rr] = gam[l] * dQd[u][rr];
+            ak[rr] = -gam[l] * dKd[u][rr] + (GATED ? expf(G[kC - 1] - G[l]) : 1.f) * dKr[u][rr];
+        }
+        aq = tile<T, true, false>(aq, Aq, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, 16 * lbq + 16, lane);
+        ak = tile<T, false, false>(ak, Aq, LDC, 16 * lbq, Qs, LDQ, 16 * ib, 16 * lbq, kC, lane);
+        if constexpr (DELTA) {
+            ak = tile<T, true, false>(ak, Lm, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, 16 * lbq + 16, lane);
+            ak = tile<T, false, false>(ak, Lm, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 16 * lbq, kC, lane);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbq + g4 + rr;
+            if (l < tvalid) {
+                dq[(bh * Tlen + t0 + l) * DK + 16 * ib + cl] = from_f32<T>(aq[rr]);
+                dk[(bh * Tlen + t0 + l) * DK + 16 * ib + cl] = from_f32<T>(ak[rr]);
+            }
+        }
+    }
+    __syncthreads();
+    // F5: dG_C extras, then dg = reverse prefix sum of dG
+    if (wave == 0) {
+        if constexpr (GATED) {
+            const float krs = wave_last(wave_prefix_sum(krp[0][lane] + krp[1][lane]));
+            float sd = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) sd += sdp[w];
+            float x = dGs[kC - 1 - lane];
+            if (lane == 0) x += krs + gam[kC - 1] * sd;
+            const float dgs = wave_prefix_sum(x);      // lane L: dg at position 63 - L
+            const int s = kC - 1 - lane;
+            if (s < tvalid) dg[bh * Tlen + t0 + s] = from_f32<T>(dgs);
+        }
+    }
+    if constexpr (DELTA) {
+        if (wave == 1 && lane < tvalid) dbeta[bh * Tlen + t0 + lane] = from_f32<T>(dBs[lane]);
+    }
+}
+
+template <typename T, int DK, int RULE, int GATE>
+hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
+{
+    const int64_t bh = p.B * p.H;
+    const int64_t nchunks = (p.T + kC - 1) / kC;
+    const T* q = static_cast<const T*>(p.q);
+    const T* k = static_cast<const T*>(p.k);
+    const T* g = static_cast<const T*>(p.g);
+    const T* beta = static_cast<const T*>(p.beta);
+    if (bh * nchunks > 0) {
+        hipLaunchKernelGGL((bwd_ops_kernel<T, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s,
+                           q, k, g, beta, static_cast<T*>(p.ops), p.gC, p.T, nchunks);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0, s,
+                       static_cast<const T*>(p.dout), static_cast<const T*>(p.ops), p.gC, p.dsT, p.dstates, p.ds0,
+                       p.T, nchunks, p.dv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || bh * nchunks == 0) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<T, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s,
+                       q, k, static_cast<const T*>(p.v), g, beta, static_cast<const T*>(p.dout), p.states,
+                       p.dstates, static_cast<T*>(p.dq), static_cast<T*>(p.dk_out), static_cast<T*>(p.dv_out),
+                       static_cast<T*>(p.dg), static_cast<T*>(p.dbeta), p.T, nchunks, p.dv);
+    return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t bwd_by_rule_gate(const ChunkBwdProblem& p, hipStream_t s)
+{
+    if (p.rule == kRuleAdd)
+        return p.gate == kGateNone ? launch_bwd_t<T, DK, kRuleAdd, kGateNone>(p, s)
+                                   : launch_bwd_t<T, DK, kRuleAdd, kGateScalar>(p, s);
+    return p.gate == kGateNone ? launch_bwd_t<T, DK, kRuleDelta, kGateNone>(p, s)
+                               : launch_bwd_t<T, DK, kRuleDelta, kGateScalar>(p, s);
+}
+
+}  // namespace
+
+bool chunk_bwd_supported(int dk, int dv, int rule, int gate, int dtype)
+{
+    (void)rule;
+    if (gate == kGateChannel) return false;
+    if (dtype == kBF16) return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    return dk == 64 && (dv == 64 || dv == 128);
+}
+
+size_t chunk_bwd_ops_bytes(int dk, int dtype)
+{
+    const size_t esz = dtype == kBF16 ? 2 : 4;
+    return (size_t)(2 * kC * kC + 3 * kC * dk) * esz;
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdProblem& p, hipStream_t s)
+{
+    if (p.dtype == kBF16)
+        return p.dk == 64 ? bwd_by_rule_gate<bf16, 64>(p, s) : bwd_by_rule_gate<bf16, 128>(p, s);
+    return bwd_by_rule_gate<float, 64>(p, s);
+}
+
+}  // namespace linattn

@@ -91,11 +91,13 @@ __device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
     mi = p;
 }
 
-template <typename T, int DK, int RULE, int GATE>
+// SAVE: also write the state entering every chunk, states[b,h,r] = S_r
+// ([dk][dv] fp32 per chunk), for the backward pass.
+template <typename T, int DK, int RULE, int GATE, bool SAVE = false>
 __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const float* s0, T* __restrict__ o,
-    float* s_final, int64_t Tlen, int DV, int nblocks, int prep)
+    float* s_final, float* __restrict__ states, int64_t Tlen, int DV, int nblocks, int prep)
 {
     using Cfg = FusedCfg<T, DK, RULE, GATE>;
     using F = typename Frag16<T>::type;
@@ -375,6 +377,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 
             stage(t0);
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
+            if constexpr (SAVE) {
+                float* sr = states + ((bh * nchunks + r) * DK) * DV + vb * kDVB + n0 + cl;
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) sr[(16 * db + g4 + rr) * DV] = S[db][rr];
+            }
             lds_barrier();
 
             // ---- P2a: R = V - gamma K S_r (delta; V for add) --------------------------
@@ -647,27 +656,27 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     if (wave >= kW0 && nchunks > 0) copy_out((nchunks - 1) * kC, wave - kW0, lane);
 }
 
-template <typename T, int DK, int RULE, int GATE>
-hipError_t launch_t(const ChunkProblem& p, hipStream_t s)
+template <typename T, int DK, int RULE, int GATE, bool SAVE>
+hipError_t launch_t(const ChunkProblem& p, float* states, hipStream_t s)
 {
     const int nvb = p.dv / kDVB;
     const int64_t nblocks = p.B * p.H * nvb;
-    hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE>), dim3((unsigned)nblocks), dim3(kNT), 0,
+    hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE, SAVE>), dim3((unsigned)nblocks), dim3(kNT), 0,
                        s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
                        static_cast<const T*>(p.v), static_cast<const T*>(p.g),
-                       static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, p.T,
-                       p.dv, (int)nblocks, p.prep);
+                       static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, states,
+                       p.T, p.dv, (int)nblocks, p.prep);
     return hipGetLastError();
 }
 
-template <typename T, int DK>
-hipError_t by_rule_gate(const ChunkProblem& p, hipStream_t s)
+template <typename T, int DK, bool SAVE>
+hipError_t by_rule_gate(const ChunkProblem& p, float* states, hipStream_t s)
 {
     if (p.rule == kRuleAdd)
-        return p.gate == kGateNone ? launch_t<T, DK, kRuleAdd, kGateNone>(p, s)
-                                   : launch_t<T, DK, kRuleAdd, kGateScalar>(p, s);
-    return p.gate == kGateNone ? launch_t<T, DK, kRuleDelta, kGateNone>(p, s)
-                               : launch_t<T, DK, kRuleDelta, kGateScalar>(p, s);
+        return p.gate == kGateNone ? launch_t<T, DK, kRuleAdd, kGateNone, SAVE>(p, states, s)
+                                   : launch_t<T, DK, kRuleAdd, kGateScalar, SAVE>(p, states, s);
+    return p.gate == kGateNone ? launch_t<T, DK, kRuleDelta, kGateNone, SAVE>(p, states, s)
+                               : launch_t<T, DK, kRuleDelta, kGateScalar, SAVE>(p, states, s);
 }
 
 }  // namespace
@@ -682,8 +691,17 @@ bool chunk_fused_supported(const ChunkProblem& p)
 hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t s)
 {
     if (p.dtype == kBF16)
-        return p.dk == 64 ? by_rule_gate<bf16, 64>(p, s) : by_rule_gate<bf16, 128>(p, s);
-    return by_rule_gate<float, 64>(p, s);
+        return p.dk == 64 ? by_rule_gate<bf16, 64, false>(p, nullptr, s)
+                          : by_rule_gate<bf16, 128, false>(p, nullptr, s);
+    return by_rule_gate<float, 64, false>(p, nullptr, s);
+}
+
+hipError_t launch_chunk_fused_save(const ChunkProblem& p, float* states, hipStream_t s)
+{
+    if (p.dtype == kBF16)
+        return p.dk == 64 ? by_rule_gate<bf16, 64, true>(p, states, s)
+                          : by_rule_gate<bf16, 128, true>(p, states, s);
+    return by_rule_gate<float, 64, true>(p, states, s);
 }
 
 }  // namespace linattn

@@ -192,6 +192,53 @@ linattn_status validate_norm(const linattn_chunk_args* a, const linattn_prep_arg
     return validate_chunk(ad, pd, prep);
 }
 
+// Backward pass and the forward that keeps the chunk states: the problem (gate
+// NONE or SCALAR, chunk 64) and its sizes.
+linattn_status validate_train(const linattn_chunk_args* a, ChunkProblem* p)
+{
+    if (!a) return LINATTN_ERR_NULL;
+    if (a->B < 0 || a->H < 0 || a->T < 0 || a->dk <= 0 || a->dv <= 0 || a->chunk < 0)
+        return LINATTN_ERR_SHAPE;
+    linattn_status st = check_enums(a->rule, a->gate, a->dtype);
+    if (st != LINATTN_OK) return st;
+    int64_t bh, bht, tot;
+    if (!mul_ok(a->B, a->H, &bh) || !mul_ok(bh, a->T, &bht) ||
+        !mul_ok(bht, (int64_t)(a->dk > a->dv ? a->dk : a->dv), &tot) || bh > (int64_t)INT32_MAX)
+        return LINATTN_ERR_SHAPE;
+    if (a->chunk != 0 && a->chunk != 64) return LINATTN_ERR_UNSUPPORTED;
+    if (!chunk_bwd_supported(a->dk, a->dv, a->rule, a->gate, a->dtype)) return LINATTN_ERR_UNSUPPORTED;
+    const int64_t esz = a->dtype == LINATTN_BF16 ? 2 : 4;
+    if (a->T * a->dv * esz >= ((int64_t)1 << 31)) return LINATTN_ERR_UNSUPPORTED;
+    // every chunk-indexed launch grid stays within 2^31 workgroups
+    if (bh * ((a->T + 63) / 64) >= ((int64_t)1 << 31)) return LINATTN_ERR_SHAPE;
+    *p = ChunkProblem{};
+    p->B = a->B; p->H = a->H; p->T = a->T;
+    p->dk = a->dk; p->dv = a->dv; p->chunk = 64;
+    p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
+    return chunk_fused_supported(*p) ? LINATTN_OK : LINATTN_ERR_UNSUPPORTED;
+}
+
+// Backward workspace, 256-byte aligned pieces: chunk operands [B,H,N] blocks,
+// exp(G_C) [B,H,N], dstates [B,H,N,dk,dv] fp32, then (states not given) the
+// recomputed states [B,H,N,dk,dv] fp32 and a forward output [B,H,T,dv].
+struct BwdLayout {
+    size_t ops, gc, dst, st, o, total;
+};
+BwdLayout bwd_layout(const ChunkProblem& p, bool states_given)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t bh = (size_t)(p.B * p.H), nch = (size_t)((p.T + 63) / 64);
+    const size_t esz = p.dtype == kBF16 ? 2 : 4;
+    BwdLayout l{};
+    l.ops = 0;
+    l.gc = up(bh * nch * chunk_bwd_ops_bytes(p.dk, p.dtype));
+    l.dst = l.gc + up(bh * nch * 4);
+    l.st = l.dst + up(bh * nch * p.dk * p.dv * 4);
+    l.o = l.st + (states_given ? 0 : up(bh * nch * p.dk * p.dv * 4));
+    l.total = l.o + (states_given ? 0 : up(bh * (size_t)p.T * p.dv * esz));
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +421,88 @@ linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args* a, const l
                                 workspace_bytes - l.cws, stream);
     if (st != LINATTN_OK) return st;
     return launch_norm_finish(np, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+linattn_status linattn_chunk_fwd_save(const linattn_chunk_args* a, const void* q, const void* k,
+                                      const void* v, const void* g, const void* beta, const float* s0,
+                                      void* o, float* s_final, float* states, void* stream)
+{
+    ChunkProblem p{};
+    linattn_status st = validate_train(a, &p);
+    if (st != LINATTN_OK) return st;
+    if (p.B * p.H == 0) return LINATTN_OK;
+    if (p.T > 0) {
+        st = check_pointers(p.rule, p.gate, q, k, v, g, beta, q, o);
+        if (st != LINATTN_OK) return st;
+        if (!states) return LINATTN_ERR_NULL;
+        if (!aligned16(states)) return LINATTN_ERR_UNSUPPORTED;
+    }
+    st = check_states(p, s0, s_final);
+    if (st != LINATTN_OK) return st;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s0 = s0; p.o = o; p.s_final = s_final;
+    return launch_chunk_fused_save(p, states, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+}
+
+size_t linattn_chunk_bwd_workspace_bytes(const linattn_chunk_args* a, int states_given)
+{
+    ChunkProblem p{};
+    if (validate_train(a, &p) != LINATTN_OK) return 0;
+    return bwd_layout(p, states_given != 0).total;
+}
+
+linattn_status linattn_chunk_bwd(const linattn_chunk_args* a, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* s0, const float* states,
+                                 const void* dout, const float* dsT, void* dq, void* dk, void* dv, void* dg,
+                                 void* dbeta, float* ds0, void* workspace, size_t workspace_bytes,
+                                 void* stream)
+{
+    ChunkProblem p{};
+    linattn_status st = validate_train(a, &p);
+    if (st != LINATTN_OK) return st;
+    if (p.B * p.H == 0) return LINATTN_OK;
+    if (p.T > 0) {
+        st = check_pointers(p.rule, p.gate, q, k, v, g, beta, q, dout);
+        if (st != LINATTN_OK) return st;
+        // gradient outputs: dg exactly for the scalar gate, dbeta for the delta rule
+        if (!dq || !dk || !dv) return LINATTN_ERR_NULL;
+        if ((p.gate == kGateScalar) != (dg != nullptr)) return dg ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
+        if ((p.rule == kRuleDelta) != (dbeta != nullptr)) return dbeta ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
+        const void* outs[] = {dq, dk, dv, dg, dbeta, states};
+        for (const void* x : outs)
+            if (x && !aligned16(x)) return LINATTN_ERR_UNSUPPORTED;
+    }
+    const void* st_ptrs[] = {s0, dsT, ds0};
+    for (const void* x : st_ptrs)
+        if (x && !aligned16(x)) return LINATTN_ERR_UNSUPPORTED;
+    const bool given = states != nullptr;
+    const BwdLayout l = bwd_layout(p, given);
+    if (p.T > 0) {
+        if (!workspace || workspace_bytes < l.total) return LINATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const float* sts = states;
+    if (p.T > 0 && !given) {
+        ChunkProblem fp = p;
+        fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta;
+        fp.s0 = s0; fp.o = ws + l.o; fp.s_final = nullptr;
+        float* rec = reinterpret_cast<float*>(ws + l.st);
+        if (launch_chunk_fused_save(fp, rec, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+        sts = rec;
+    }
+    ChunkBwdProblem b{p.B, p.H, p.T, p.dk, p.dv, p.rule, p.gate, p.dtype,
+                      q, k, v, g, beta, dout, sts, dsT, dq, dk, dv, dg, dbeta, ds0,
+                      p.T > 0 ? ws + l.ops : nullptr,
+                      p.T > 0 ? reinterpret_cast<float*>(ws + l.gc) : nullptr,
+                      p.T > 0 ? reinterpret_cast<float*>(ws + l.dst) : nullptr};
+    return launch_chunk_bwd(b, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

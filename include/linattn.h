@@ -225,6 +225,68 @@ linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args *a,
                                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Chunk forward that also keeps, for the backward pass, the state entering
+ * every chunk ("Linear Attention, Visualized", "Update the state": in the
+ * chunkwise form autograd keeps one boundary state per chunk instead of one
+ * state per token).  Same arguments and results as
+ * linattn_chunk_fwd, plus
+ *   states   [B,H,N,dk,dv] fp32, N = ceil(T / 64): states[b,h,r] is the state
+ *            before chunk r (states[b,h,0] = s0, or zero); caller-owned.
+ * Supported: gate NONE or SCALAR, chunk 64, bf16 tokens with dk, dv in
+ * {64, 128}, fp32 tokens with dk = 64 (LINATTN_ERR_UNSUPPORTED otherwise);
+ * the same 2 GiB limit.  No workspace.
+ */
+linattn_status linattn_chunk_fwd_save(const linattn_chunk_args *a,
+                                      const void *q, const void *k, const void *v,
+                                      const void *g, const void *beta,
+                                      const float *s0, void *o, float *s_final,
+                                      float *states, void *stream);
+
+/*
+ * Device workspace, in bytes, of linattn_chunk_bwd: the per-chunk operands of
+ * its reverse state pass and the gradients of every chunk's outgoing state,
+ * plus, when states_given is 0, room for the recomputed chunk states and a
+ * forward output.  0 for invalid or unsupported arguments.
+ */
+size_t linattn_chunk_bwd_workspace_bytes(const linattn_chunk_args *a, int states_given);
+
+/*
+ * Backward pass of the chunkwise forward: the gradients of a loss with
+ * respect to q, k, v, g, beta and s0, given its gradients with respect to
+ * every output (dout) and the final state (dsT).  "Linear Attention,
+ * Visualized", "Update the state" (the chunk form is how these layers train,
+ * saving one state per chunk for the backward pass) and "Beyond attention",
+ * "Chunkwise parallel training", with the per-chunk quantities of "Linear Attention, Visualized", "Chunkwise
+ * algorithm", the GDN table and "The triangular correction system"
+ * differentiated: a reverse pass over the chunks carries the gradient of the
+ * state, and every chunk's gradients then follow from its incoming state and
+ * the gradient of its outgoing state.
+ *
+ *   q, k, v, g, beta, s0: the forward's inputs (as linattn_chunk_fwd)
+ *   states   [B,H,N,dk,dv] fp32 from linattn_chunk_fwd_save, or NULL to
+ *            recompute them (then s0 is read; with states given it is not)
+ *   dout     [B,H,T,dv] token dtype
+ *   dsT      [B,H,dk,dv] fp32, or NULL for zero
+ *   dq, dk   [B,H,T,dk] token dtype (written)
+ *   dv       [B,H,T,dv] token dtype (written)
+ *   dg       [B,H,T] token dtype for the SCALAR gate, NULL for NONE (written)
+ *   dbeta    [B,H,T] token dtype for DELTA, NULL for ADD (written)
+ *   ds0      [B,H,dk,dv] fp32, or NULL (written)
+ *   workspace: at least linattn_chunk_bwd_workspace_bytes(a, states != NULL)
+ *            bytes, 16-byte aligned
+ * Supported: as linattn_chunk_fwd_save.  Accumulation is fp32; matrix-core
+ * operands are in the token dtype.  Inputs are not normalised or mapped here:
+ * these are the gradients with respect to the values the kernels received.
+ */
+linattn_status linattn_chunk_bwd(const linattn_chunk_args *a,
+                                 const void *q, const void *k, const void *v,
+                                 const void *g, const void *beta, const float *s0,
+                                 const float *states, const void *dout, const float *dsT,
+                                 void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                                 float *ds0, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * One recurrent decode step for N sequences x H heads, updating the state in
  * place ("Linear Attention, Visualized", "Optional: Linear attention as an
  * RNN" and the DeltaNet recurrent form; "All sorts of famous Attention

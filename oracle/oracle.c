@@ -322,9 +322,10 @@ int oracle_normalized(int64_t B, int64_t H, int64_t T, int dk, int dv, int gate,
 }
 
 /*
- * Backward pass of the token recurrence above (the gradients the chunkwise
- * form is trained with: [BA] "Chunkwise parallel" motivates the chunk form by
- * training, and the boundary states it keeps are what a backward pass needs).
+ * Backward pass of the token recurrence above: the gradients a training step
+ * needs ([LAV] "Optional: Linear attention as an RNN" and "Update the state":
+ * autograd of the recurrent form keeps every state for the backward pass, the
+ * chunk form one per chunk; [BA] "Chunkwise parallel training").
  * Given the gradient of a loss with respect to every output o_t (do) and to the
  * final state S_T (dsT, NULL for zero), it returns the gradients with respect
  * to q, k, v, g, beta and s0, by reverse-mode differentiation of each step of

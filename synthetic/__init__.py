@@ -216,6 +216,29 @@ def raw_inputs(case: Case, seed: int = SEED) -> dict:
     return out
 
 
+def grad_head_inputs(case: Case, b: int, h: int, seed: int = SEED) -> dict:
+    """Upstream gradients of one head for the backward pass: do [T,dv] N(0,1)
+    in the token dtype, dsT [dk,dv] N(0, 0.5^2) fp32 (its own stream,
+    [seed, case_id, b, h, 1])."""
+    rng = np.random.default_rng([seed, case.case_id, b, h, 1])
+    do = to_dtype(rng.standard_normal((case.T, case.dv), dtype=np.float32), case.dtype)
+    dsT = (rng.standard_normal((case.dk, case.dv), dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+    return {"do": do, "dsT": dsT}
+
+
+def grad_inputs(case: Case, heads: Optional[Sequence[tuple]] = None, seed: int = SEED) -> dict:
+    """All heads ([B,H,...]) or the listed (b,h) heads ([n,...]) of grad_head_inputs."""
+    idx = [(b, h) for b in range(case.B) for h in range(case.H)] if heads is None else list(heads)
+    parts = [grad_head_inputs(case, b, h, seed) for (b, h) in idx]
+    out = {}
+    for key in ("do", "dsT"):
+        arr = np.stack([p[key] for p in parts])
+        if heads is None:
+            arr = arr.reshape((case.B, case.H) + arr.shape[1:])
+        out[key] = arr
+    return out
+
+
 def iter_heads(case: Case, seed: int = SEED) -> Iterable[tuple]:
     """Yield ((b,h), inputs) one head at a time (for workloads too big to hold twice)."""
     for b in range(case.B):
@@ -363,6 +386,16 @@ def chunk_inputs_torch(case: Case, device, seed: int = SEED) -> dict:
     out["g"] = None if case.gate == "none" else g.to(dt)
     out["s0"] = None
     return out
+
+
+def grad_inputs_torch(case: Case, device, seed: int = SEED) -> dict:
+    """Upstream gradients drawn on the device: do [B,H,T,dv] N(0,1), dsT None."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000 + 500 + (case.case_id if isinstance(case.case_id, int) else 0))
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    do = torch.randn(case.B, case.H, case.T, case.dv, generator=gen, device=device, dtype=torch.float32)
+    return {"do": do.to(dt), "dsT": None}
 
 
 def decode_tokens_torch(case: DecodeCase, steps: int, device, seed: int = SEED) -> dict:

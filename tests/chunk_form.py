@@ -61,3 +61,110 @@ def chunk_forward(q, k, v, g, beta, s0, *, rule, gate, C):
         o[c0:c1] = Qd @ S + A @ Z
         S = np.exp(G[-1])[:, None] * S + Kr.T @ Z
     return o, S
+
+
+def chunk_backward(q, k, v, g, beta, s0, do, dsT, *, rule, gate, C):
+    """Gradients of sum(do . o) + sum(dsT . S_T) in the chunk form, one head,
+    gate "none" or "scalar", written as the three passes the HIP backward runs:
+
+      1. forward over the chunks, keeping the incoming state S_r of every chunk;
+      2. backward over the chunks, newest first, carrying dS (the gradient with
+         respect to the state leaving the chunk):
+           dZ = A^T dO + ->K dS_{r+1};  dR = Tb^T dZ (delta; dR = dZ for add)
+           dS_r = exp(G_C) dS_{r+1} + <-Q^T dO - <-K^T dR (the last term: delta only)
+      3. per chunk, from S_r and dS_{r+1} alone, with Tb = T diag(beta),
+         R = V - <-K S_r, Z = Tb R:
+           dv = dR;  d<-Q = dO S_r^T;  d<-K = -dR S_r^T;  d->K = Z dS_{r+1}^T
+           dA = (dO Z^T) masked;  dTb = dZ R^T;  dbeta_m = sum_l T[l,m] dTb[l,m]
+           dM = -T^T dTb Tb^T (M = I + diag(beta) L);  dL = diag(beta) dM masked;
+           dbeta_l += sum_m dM[l,m] L[l,m]
+           P = dA . D, P2 = dL . D (D[l,m] = exp(G_l - G_m))
+           dq = exp(G) d<-Q + P K;  dk = exp(G) d<-K + exp(G_C - G) d->K + P^T Q + (P2 + P2^T) K
+           dG_l = q_l.(exp(G_l) d<-Q_l) + k_l.(exp(G_l) d<-K_l) - k_l.(exp(G_C-G_l) d->K_l)
+                  + rowsum(dA.A)_l - colsum(dA.A)_l + rowsum(dL.L)_l - colsum(dL.L)_l
+           dG_C += sum_l k_l.(exp(G_C-G_l) d->K_l) + exp(G_C) <S_r, dS_{r+1}>
+           dg = reverse prefix sum of dG within the chunk.
+    Returns dq, dk, dv, dg (None without a gate), dbeta (None for add), ds0."""
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    T, dk = q.shape
+    dv = v.shape[1]
+    gg = np.zeros(T) if gate == "none" else np.asarray(g, np.float64)
+    bb = np.asarray(beta, np.float64) if rule == "delta" else None
+    starts = list(range(0, T, C))
+
+    def local(c0):
+        c1 = min(T, c0 + C)
+        n = c1 - c0
+        G = np.cumsum(gg[c0:c1])
+        D = np.exp(G[:, None] - G[None, :])
+        Q, K, V = q[c0:c1], k[c0:c1], v[c0:c1]
+        A = (Q @ K.T) * D * np.tril(np.ones((n, n)))
+        out = dict(n=n, G=G, D=D, Q=Q, K=K, V=V, A=A, Qd=np.exp(G)[:, None] * Q,
+                   Kd=np.exp(G)[:, None] * K, Kr=np.exp(G[-1] - G)[:, None] * K, gC=np.exp(G[-1]))
+        if rule == "delta":
+            b = bb[c0:c1]
+            L = (K @ K.T) * D * np.tril(np.ones((n, n)), -1)
+            Tm = np.linalg.inv(np.eye(n) + b[:, None] * L)
+            out.update(b=b, L=L, T=Tm, Tb=Tm * b[None, :])
+        return out
+
+    # pass 1: incoming states
+    S = np.zeros((dk, dv)) if s0 is None else np.array(s0, np.float64)
+    Sin = []
+    for c0 in starts:
+        x = local(c0)
+        Sin.append(S.copy())
+        Z = x["Tb"] @ (x["V"] - x["Kd"] @ S) if rule == "delta" else x["V"]
+        S = x["gC"] * S + x["Kr"].T @ Z
+    # pass 2: gradients of the outgoing states
+    dS = np.zeros((dk, dv)) if dsT is None else np.array(dsT, np.float64)
+    dSout = [None] * len(starts)
+    for r in range(len(starts) - 1, -1, -1):
+        x = local(starts[r])
+        dSout[r] = dS.copy()
+        dO = do[starts[r]:starts[r] + x["n"]]
+        dZ = x["A"].T @ dO + x["Kr"] @ dS
+        dS = x["gC"] * dS + x["Qd"].T @ dO
+        if rule == "delta":
+            dS = dS - x["Kd"].T @ (x["Tb"].T @ dZ)
+    ds0 = dS
+    # pass 3: per chunk
+    gq, gk, gv, gg_out = np.zeros((T, dk)), np.zeros((T, dk)), np.zeros((T, dv)), np.zeros(T)
+    gb = np.zeros(T) if rule == "delta" else None
+    for r, c0 in enumerate(starts):
+        x = local(c0)
+        n = x["n"]
+        Sr, dSn = Sin[r], dSout[r]
+        dO = do[c0:c0 + n]
+        if rule == "delta":
+            R = x["V"] - x["Kd"] @ Sr
+            Z = x["Tb"] @ R
+        else:
+            Z = x["V"]
+        dZ = x["A"].T @ dO + x["Kr"] @ dSn
+        dR = x["Tb"].T @ dZ if rule == "delta" else dZ
+        gv[c0:c0 + n] = dR
+        dQd = dO @ Sr.T
+        dKr = Z @ dSn.T
+        dKd = -dR @ Sr.T if rule == "delta" else np.zeros((n, dk))
+        dA = (dO @ Z.T) * np.tril(np.ones((n, n)))
+        P = dA * x["D"]
+        eG, eR = np.exp(x["G"])[:, None], np.exp(x["G"][-1] - x["G"])[:, None]
+        dq = eG * dQd + P @ x["K"]
+        dkk = eG * dKd + eR * dKr + P.T @ x["Q"]
+        dG = (np.sum(x["Q"] * eG * dQd, 1) + np.sum(x["K"] * eG * dKd, 1) - np.sum(x["K"] * eR * dKr, 1)
+              + np.sum(dA * x["A"], 1) - np.sum(dA * x["A"], 0))
+        dG[-1] += np.sum(x["K"] * eR * dKr) + x["gC"] * np.sum(Sr * dSn)
+        if rule == "delta":
+            dTb = (dZ @ R.T) * np.tril(np.ones((n, n)))
+            db = np.sum(x["T"] * dTb, 0)
+            dM = -x["T"].T @ dTb @ x["Tb"].T
+            dL = x["b"][:, None] * dM * np.tril(np.ones((n, n)), -1)
+            db = db + np.sum(dM * x["L"], 1)
+            P2 = dL * x["D"]
+            dkk = dkk + (P2 + P2.T) @ x["K"]
+            dG = dG + np.sum(dL * x["L"], 1) - np.sum(dL * x["L"], 0)
+            gb[c0:c0 + n] = db
+        gq[c0:c0 + n], gk[c0:c0 + n] = dq, dkk
+        gg_out[c0:c0 + n] = np.cumsum(dG[::-1])[::-1]
+    return gq, gk, gv, (gg_out if gate != "none" else None), gb, ds0

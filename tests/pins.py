@@ -549,8 +549,9 @@ def pin_normalized_invariants(orc):
 
 # ---------------------------------------------------------------------------
 # Backward pass.  The gradients of loss = sum(do . o) + sum(dsT . S_T) with
-# respect to q, k, v, g, beta and s0 ([BA] "Chunkwise parallel": the chunk form
-# exists for training, whose backward pass these are).
+# respect to q, k, v, g, beta and s0 ([LAV] "Optional: Linear attention as an
+# RNN" and "Update the state": the states autograd keeps for the backward pass
+# of the recurrent and the chunk form).
 # ---------------------------------------------------------------------------
 BWD_NAMES = (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"), ("s0", "ds0"))
 

@@ -1,0 +1,166 @@
+"""Parity of the chunkwise backward pass (HIP, through the C ABI) with the
+fp64 oracle's reverse-mode recurrence: every rule, gate none/scalar, both
+dtypes and head sizes, ragged lengths, initial state and final-state gradient,
+the forward that keeps the chunk states, and a sampled full-size workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from gpu_util import TOL, dev, dev_state, host, note, rel_l2
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "ds0")
+
+
+def run_bwd(case, x, gr, use_states=False):
+    import gated_delta_rule_27_amd as la
+    d = lambda a: dev(a, case.dtype)
+    args = (d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]))
+    states = None
+    if use_states:
+        _, _, states = la.chunk_fwd_save(*args, dev_state(x["s0"]), rule=case.rule, gate=case.gate)
+    out = la.chunk_bwd(*args, d(gr["do"]), dev_state(x["s0"]), dev_state(gr["dsT"]), states=states,
+                       rule=case.rule, gate=case.gate)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_bwd(case, use_states=False, tol=None):
+    tol = TOL[case.dtype] if tol is None else tol
+    note(f"[bwd] {case.name} rule={case.rule} gate={case.gate} dtype={case.dtype} B={case.B} H={case.H} "
+         f"T={case.T} dk={case.dk} dv={case.dv} states={'saved' if use_states else 'recomputed'}")
+    x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
+    out = run_bwd(case, x, gr, use_states)
+    ref = oracle.recurrence_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], gr["do"], gr["dsT"],
+                                rule=case.rule, gate=case.gate)
+    errs = {}
+    for n in NAMES:
+        if ref[n] is None:
+            assert out[n] is None
+            continue
+        a = host(out[n])
+        assert np.all(np.isfinite(a)), f"non-finite {n}"
+        errs[n] = rel_l2(a, ref[n])
+    note("    rel L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > tol}
+    assert not bad, f"above {tol}: {bad}"
+    return out
+
+
+SMALL = []
+for dtype, dims in (("bf16", ((128, 128), (64, 64), (64, 128), (128, 64))), ("fp32", ((64, 64), (64, 128)))):
+    for (dk, dv) in dims:
+        for rule in ("add", "delta"):
+            for gate in ("none", "scalar"):
+                SMALL.append((dtype, dk, dv, rule, gate))
+
+
+@pytest.mark.parametrize("dtype,dk,dv,rule,gate", SMALL)
+def test_small_ragged(dtype, dk, dv, rule, gate):
+    # T = 200: three full chunks and a ragged tail of 8; s0 and dS_T nonzero;
+    # gates weak enough that the carried state matters
+    case = syn.Case("bwd_small", 2, 2, 200, dk, dv, rule, gate, dtype, gate_scale=0.1, s0_std=0.3,
+                    case_id=140)
+    check_bwd(case)
+
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 128, 130])
+def test_lengths(T):
+    case = syn.Case("bwd_len", 1, 2, T, 128, 128, "delta", "scalar", "bf16", gate_scale=0.2, s0_std=0.2,
+                    case_id=141)
+    check_bwd(case)
+
+
+@pytest.mark.parametrize("beta_mode", ["zero", "one"])
+def test_beta_extremes(beta_mode):
+    case = syn.Case("bwd_beta", 1, 2, 150, 128, 128, "delta", "scalar", "bf16", gate_scale=0.1,
+                    beta_mode=beta_mode, s0_std=0.2, case_id=142)
+    check_bwd(case)
+
+
+def test_strong_decay():
+    # the workloads' own gate law (a chunk decays by ~e^-40): the carried
+    # state barely reaches the next chunk, the in-chunk decays dominate dg
+    case = syn.Case("bwd_strong", 2, 2, 192, 128, 128, "delta", "scalar", "bf16", s0_std=0.3,
+                    case_id=143)
+    check_bwd(case)
+
+
+def test_saved_states_equal_recomputed():
+    import gated_delta_rule_27_amd as la
+    case = syn.Case("bwd_saved", 2, 3, 333, 128, 128, "delta", "scalar", "bf16", gate_scale=0.1,
+                    s0_std=0.3, case_id=144)
+    a = check_bwd(case, use_states=True)
+    x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
+    b = run_bwd(case, x, gr, use_states=False)
+    for n in NAMES:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), f"{n}: saved and recomputed states differ"
+    # the states themselves: chunk r starts from the oracle's state after 64 r tokens
+    d = lambda t: dev(t, case.dtype)
+    _, _, states = la.chunk_fwd_save(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]),
+                                     dev_state(x["s0"]), rule=case.rule, gate=case.gate)
+    torch.cuda.synchronize()
+    st = host(states)
+    assert np.array_equal(st[:, :, 0], x["s0"].astype(np.float64))
+    for r in (1, 3, 5):
+        cut = 64 * r
+        sub = {k2: (None if v2 is None else np.ascontiguousarray(v2[:, :, :cut])) for k2, v2 in x.items()
+               if k2 != "s0"}
+        _, sref = oracle.recurrence(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], x["s0"],
+                                    rule=case.rule, gate=case.gate)
+        assert rel_l2(st[:, :, r], sref) <= TOL["bf16"], f"state entering chunk {r}"
+
+
+def test_zero_tokens():
+    import gated_delta_rule_27_amd as la
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    dsT = torch.randn(1, 2, 64, 64, device="cuda")
+    out = la.chunk_bwd(e(1, 2, 0, 64), e(1, 2, 0, 64), e(1, 2, 0, 64), e(1, 2, 0), e(1, 2, 0),
+                       e(1, 2, 0, 64), None, dsT, rule="delta", gate="scalar")
+    torch.cuda.synchronize()
+    assert torch.equal(out["ds0"], dsT)
+    out = la.chunk_bwd(e(1, 2, 0, 64), e(1, 2, 0, 64), e(1, 2, 0, 64), None, None, e(1, 2, 0, 64),
+                       rule="add", gate="none")
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out["ds0"]) == 0
+
+
+def test_deterministic():
+    case = syn.Case("bwd_det", 1, 4, 300, 128, 128, "delta", "scalar", "bf16", gate_scale=0.2,
+                    s0_std=0.2, case_id=145)
+    x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
+    a, b = run_bwd(case, x, gr), run_bwd(case, x, gr)
+    for n in NAMES:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), f"{n} differs between runs"
+
+
+def test_gdn_full_size_sampled():
+    # the GDN workload's shape (B8 H16 T8192 d128), every head on the GPU;
+    # the oracle checks two heads
+    import gated_delta_rule_27_amd as la
+    case = syn.CFG3
+    heads = [(0, 0), (7, 15)]
+    xs = syn.chunk_inputs(case, heads=heads)
+    gs = syn.grad_inputs(case, heads=heads)
+    full = syn.chunk_inputs_torch(case, "cuda")
+    gfull = syn.grad_inputs_torch(case, "cuda")
+    for i, (b, h) in enumerate(heads):
+        for key in ("q", "k", "v", "g", "beta"):
+            full[key][b, h] = dev(xs[key][i], case.dtype)
+        gfull["do"][b, h] = dev(gs["do"][i], case.dtype)
+    out = la.chunk_bwd(full["q"], full["k"], full["v"], full["g"], full["beta"], gfull["do"],
+                       rule=case.rule, gate=case.gate)
+    torch.cuda.synchronize()
+    sub = lambda a: None if a is None else a[:, None]
+    ref = oracle.recurrence_bwd(sub(xs["q"]), sub(xs["k"]), sub(xs["v"]), sub(xs["g"]), sub(xs["beta"]),
+                                None, sub(gs["do"]), None, rule=case.rule, gate=case.gate)
+    for i, (b, h) in enumerate(heads):
+        errs = {n: rel_l2(host(out[n][b, h]), ref[n][i, 0]) for n in NAMES}
+        note(f"    head ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        assert all(e <= TOL["bf16"] for e in errs.values()), errs

@@ -59,3 +59,28 @@ def test_input_preparation_maps():
     assert np.allclose(b, scipy.special.expit(x), rtol=1e-14, atol=1e-16)
     assert oracle.prepare_beta(np.zeros(1), "sigmoid")[0] == 0.5
     assert oracle.prepare_qk(x, "identity") is not None and np.array_equal(oracle.prepare_qk(x, "identity"), x)
+
+
+def test_chunk_backward_equals_oracle(orc):
+    # the chunk-level backward equations the HIP backward runs (three passes:
+    # incoming states, gradients of the outgoing states newest first, then
+    # per-chunk gradients) equal the oracle's reverse-mode recurrence at any C
+    import numpy as np
+    from chunk_form import chunk_backward
+    from pins import rand_case, rel_err
+    rng = np.random.default_rng(19)
+    B, H, T, dk, dv = 1, 1, 45, 6, 5
+    for rule in ("add", "delta"):
+        for gate in ("none", "scalar"):
+            q, k, v, g, beta, S0 = rand_case(rng, B, H, T, dk, dv, gate=gate, gate_scale=0.5)
+            do = rng.standard_normal((B, H, T, dv))
+            dsT = rng.standard_normal((B, H, dk, dv))
+            ref = orc.recurrence_bwd(q, k, v, g, beta, S0, do, dsT, rule=rule, gate=gate)
+            for C in (1, 7, 16, 45):
+                out = chunk_backward(q[0, 0], k[0, 0], v[0, 0], None if g is None else g[0, 0],
+                                     beta[0, 0], S0[0, 0], do[0, 0], dsT[0, 0], rule=rule, gate=gate, C=C)
+                for name, a in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), out):
+                    if ref[name] is None:
+                        assert a is None
+                        continue
+                    assert rel_err(a, ref[name][0, 0]) < 1e-12, f"{name} ({rule}/{gate}, C={C})"
