@@ -259,6 +259,80 @@ def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
             "path": "expand + pipe + gather", "steps": steps}
 
 
+def bwd_alg_bytes(B, H, T, dk, dv, s, rule, gate, states):
+    """Bytes the backward pass must move at minimum: q, k, v, dO (and g, beta)
+    in, dq, dk, dv (and dg, dbeta) out, plus the saved chunk states when they
+    are read (fp32, one per chunk)."""
+    per_tok = (2 * dk + 2 * dv) * s + (2 * dk + dv) * s
+    if gate == "scalar":
+        per_tok += 2 * s
+    if rule == "delta":
+        per_tok += 2 * s
+    nch = (T + 63) // 64
+    return B * H * T * per_tok + (B * H * nch * dk * dv * 4 if states else 0)
+
+
+def bwd_nominal_flops(B, H, T, dk, dv, C=64):
+    """Nominal FLOPs per head-token of the delta-rule backward as built: the
+    operand pass (A, L), the reverse state pass (A^T dO, ->K dS, Tb^T dZ,
+    <-Q^T dO, <-K^T dR) and the gradient pass (A, L, R, Z, dZ, dR, d<-Q, d<-K,
+    d->K, dA, dTb, T^T dTb, dM, P K, P^T Q, P2 K, P2^T K)."""
+    macs = 8 * C * dk + 7 * C * dv + 8 * dk * dv + 2 * C * C
+    return B * H * T * 2 * macs
+
+
+def time_backward(la, syn, case, dev, steps, warmup=2):
+    """Event-timed training passes at the shape and laws of ``case``: the
+    forward that keeps the chunk states, the backward from those states, and
+    the backward that recomputes them."""
+    import torch
+    B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
+    x = syn.chunk_inputs_torch(case, dev)
+    do = syn.grad_inputs_torch(case, dev)["do"]
+    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    states = torch.empty(la.chunk_states_shape(B, H, T, dk, dv), dtype=torch.float32, device=dev)
+    grads = {"dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
+             "dg": torch.empty_like(x["g"]), "dbeta": torch.empty_like(x["beta"]),
+             "ds0": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)}
+    ws = torch.empty(la.chunk_bwd_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate,
+                                                  states_given=False), dtype=torch.uint8, device=dev)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"])
+
+    def fwd():
+        la.chunk_fwd_save(*args, rule=case.rule, gate=case.gate, out=out, states=states, return_state=False)
+
+    def bwd_saved():
+        la.chunk_bwd(*args, do, states=states, rule=case.rule, gate=case.gate, workspace=ws, grads=grads)
+
+    def bwd_recompute():
+        la.chunk_bwd(*args, do, rule=case.rule, gate=case.gate, workspace=ws, grads=grads)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_f, ms_b, ms_r = timed(fwd), timed(bwd_saved), timed(bwd_recompute)
+    abytes = bwd_alg_bytes(B, H, T, dk, dv, 2, case.rule, case.gate, True)
+    aflops = bwd_nominal_flops(B, H, T, dk, dv)
+    return {"workload": f"gdn training passes B={B} H={H} T={T} dk={dk} dv={dv} bf16 (backward "
+                        f"from dO, chunk states saved by the forward)",
+            "fwd_save_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4), "bwd_recompute_ms": round(ms_r, 4),
+            "ms_per_step": round(ms_f + ms_b, 4),
+            "tokens_per_s": round(B * T / ((ms_f + ms_b) * 1e-3), 1),
+            "bwd_hbm_frac": round(abytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "bwd_mfma_frac": round(aflops / (ms_b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bwd_alg_bytes": abytes, "bwd_nominal_flops": aflops,
+            "path": "fused+save; bwd_ops + bwd_chain + bwd_grad", "steps": steps}
+
+
 def chunk_path(case, wsb):
     """Which chunk kernel the library runs for this case (its dispatch rule)."""
     if wsb:
@@ -285,9 +359,9 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm",
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm,cfg3bwd",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm, cfg3bwd), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -363,6 +437,8 @@ def main():
             others.append(time_prep(la, syn.CFG3, dev, steps=10))
         elif name == "cfg2norm":
             others.append(time_normalized(la, syn, syn.CFG2, dev, steps=10))
+        elif name == "cfg3bwd":
+            others.append(time_backward(la, syn, syn.CFG3, dev, steps=5))
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
             others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))

@@ -90,6 +90,33 @@ __device__ __forceinline__ floatx4 tile(floatx4 acc, const T* A, int lda, int m0
     return acc;
 }
 
+// The same product over a fixed range [k0, k0 + K), every fragment read before
+// the first matrix-core op and pairs of K = 16 steps issued as one K = 32 op.
+// Causal operands are zero outside their triangle, so a product over the full
+// range equals the one over the causal part.
+template <typename T, bool AXK, bool BXK, int K>
+__device__ __forceinline__ floatx4 tilek(floatx4 acc, const T* A, int lda, int m0, const T* B, int ldb,
+                                         int n0, int k0, int lane)
+{
+    constexpr int NS = K / 16;
+    static_assert(NS % 2 == 0 || sizeof(T) == 4 || NS == 1, "one matrix-core shape per chain");
+    F16<T> a[NS], b[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if constexpr (AXK) a[s] = frag_xk(A, lda, m0, k0 + 16 * s, lane);
+        else a[s] = frag_kx(A, lda, m0, k0 + 16 * s, lane);
+        if constexpr (BXK) b[s] = frag_xk(B, ldb, n0, k0 + 16 * s, lane);
+        else b[s] = frag_kx(B, ldb, n0, k0 + 16 * s, lane);
+    }
+    if constexpr (NS == 1) {
+        acc = mma16<T>(a[0], b[0], acc);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NS; s += 2) acc = mma16x2<T>(a[s], a[s + 1], b[s], b[s + 1], acc);
+    }
+    return acc;
+}
+
 // result tile into P[m*ld + n] (row-major)
 template <typename T>
 __device__ __forceinline__ void put(T* P, int ld, int m0, int n0, floatx4 v, int lane)
@@ -182,8 +209,8 @@ __device__ void intra_chunk(const IntraLds<T, DK>& L, const T* __restrict__ q, c
             const bool isL = j >= 10;
             int lb, mb;
             causal_tile(isL ? j - 10 : j, lb, mb);
-            floatx4 acc = tile<T, true, true>(zero4(), isL ? L.Ks : L.Qs, LDQ, 16 * lb, L.Ks, LDQ, 16 * mb, 0,
-                                              DK, lane);
+            floatx4 acc = tilek<T, true, true, DK>(zero4(), isL ? L.Ks : L.Qs, LDQ, 16 * lb, L.Ks, LDQ,
+                                                   16 * mb, 0, lane);
             const int m = 16 * mb + (lane & 15);
             floatx4 val;
 #pragma unroll
@@ -540,6 +567,37 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     T* const Tm = CC + 2 * kC * LDC;
     T* const Tb = CC + 3 * kC * LDC;
     IntraLds<T, DK> L{Qs, Ks, Aq, Lm, Tm, Tb, G, gam, bet};
+    const float* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
+    const float* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
+
+    // the value block's dO and V rows and its S_r and dS_{r+1} columns go
+    // through registers: the next block's loads are issued before this block's
+    // products (the first block's before the intra-chunk work)
+    constexpr int VR = J / E, NVJ = (kC * VR + kNT - 1) / kNT;
+    constexpr int SR = J / 4, NSJ = (DK * SR + kNT - 1) / kNT;
+    i4 pdo[NVJ], pv[NVJ];
+    floatx4 ps[NSJ], pds[NSJ];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < NVJ; ++u) {
+            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            pdo[u] = pv[u] = i4{0, 0, 0, 0};
+            if (i < kC * VR && row < tvalid) {
+                pdo[u] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t0 + row) * DV + j0 + c);
+                pv[u] = *reinterpret_cast<const i4*>(v + (bh * Tlen + t0 + row) * DV + j0 + c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NSJ; ++u) {
+            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * 4;
+            ps[u] = pds[u] = zero4();
+            if (i < DK * SR) {
+                ps[u] = *reinterpret_cast<const floatx4*>(Sr + row * DV + j0 + c);
+                pds[u] = *reinterpret_cast<const floatx4*>(dSr + row * DV + j0 + c);
+            }
+        }
+    };
+    fetch(0);
     intra_chunk<T, DK, RULE, GATE>(L, q, k, g, beta, bh, Tlen, t0, tvalid, tid);
 
     T* const dOs = reinterpret_cast<T*>(region);
@@ -558,28 +616,22 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     for (int u = 0; u < NI; ++u) dQd[u] = dKd[u] = dKr[u] = zero4();
     dAq[0] = dAq[1] = dTb[0] = dTb[1] = zero4();
     float sdot = 0.f;
-    const float* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
-    const float* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
 
     for (int j0 = 0; j0 < DV; j0 += J) {
         // ---- stage dO and V (token rows), S_r and dS_{r+1} (value columns j0..j0+J) ----
-        {
-            constexpr int VR = J / E;
-            for (int i = tid; i < kC * VR; i += kNT) {
-                const int row = i / VR, c = (i % VR) * E;
-                i4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-                if (row < tvalid) {
-                    a = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t0 + row) * DV + j0 + c);
-                    b = *reinterpret_cast<const i4*>(v + (bh * Tlen + t0 + row) * DV + j0 + c);
-                }
-                *reinterpret_cast<i4*>(dOs + row * LDJ + c) = a;
-                *reinterpret_cast<i4*>(Zs + row * LDJ + c) = b;
+#pragma unroll
+        for (int u = 0; u < NVJ; ++u) {
+            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            if (i < kC * VR) {
+                *reinterpret_cast<i4*>(dOs + row * LDJ + c) = pdo[u];
+                *reinterpret_cast<i4*>(Zs + row * LDJ + c) = pv[u];
             }
-            constexpr int SR = J / 4;
-            for (int i = tid; i < DK * SR; i += kNT) {
-                const int row = i / SR, c = (i % SR) * 4;
-                const floatx4 a = *reinterpret_cast<const floatx4*>(Sr + row * DV + j0 + c);
-                const floatx4 b = *reinterpret_cast<const floatx4*>(dSr + row * DV + j0 + c);
+        }
+#pragma unroll
+        for (int u = 0; u < NSJ; ++u) {
+            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * 4;
+            if (i < DK * SR) {
+                const floatx4 a = ps[u], b = pds[u];
                 sdot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
@@ -589,11 +641,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
             }
         }
         __syncthreads();
+        if (j0 + J < DV) fetch(j0 + J);
         // ---- step A: R = V - <-K S_r ; dZ = A^T dO + ->K dS ; d<-Q += dO S_r^T ----
         if (wave < 4 * NJT) {
             const int lb = wave / NJT, jc = wave % NJT;
-            floatx4 a1 = tile<T, false, false>(zero4(), Aq, LDC, 16 * lb, dOs, LDJ, 16 * jc, 16 * lb, kC, lane);
-            floatx4 a2 = tile<T, true, false>(zero4(), Ks, LDQ, 16 * lb, dSs, LDJ, 16 * jc, 0, DK, lane);
+            floatx4 a1 = tilek<T, false, false, kC>(zero4(), Aq, LDC, 16 * lb, dOs, LDJ, 16 * jc, 0, lane);
+            floatx4 a2 = tilek<T, true, false, DK>(zero4(), Ks, LDQ, 16 * lb, dSs, LDJ, 16 * jc, 0, lane);
             floatx4 dz;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -602,7 +655,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
             }
             put(dZs, LDJ, 16 * lb, 16 * jc, dz, lane);
             if constexpr (DELTA) {
-                const floatx4 ks = tile<T, true, false>(zero4(), Ks, LDQ, 16 * lb, Ss, LDJ, 16 * jc, 0, DK, lane);
+                const floatx4 ks = tilek<T, true, false, DK>(zero4(), Ks, LDQ, 16 * lb, Ss, LDJ, 16 * jc, 0, lane);
                 floatx4 rv;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -621,14 +674,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
         }
 #pragma unroll
         for (int u = 0; u < NI; ++u)
-            dQd[u] = tile<T, true, true>(dQd[u], dOs, LDJ, 16 * lbq, Ss, LDJ, 16 * (NI * (wave & 1) + u), 0, J, lane);
+            dQd[u] = tilek<T, true, true, J>(dQd[u], dOs, LDJ, 16 * lbq, Ss, LDJ, 16 * (NI * (wave & 1) + u), 0, lane);
         __syncthreads();
         // ---- step B (delta): Z = Tb R ; dR = Tb^T dZ (= dv) ; dTb += dZ R^T ----
         if constexpr (DELTA) {
             if (wave < 4 * NJT) {
                 const int lb = wave / NJT, jc = wave % NJT;
-                const floatx4 z = tile<T, true, false>(zero4(), Tb, LDC, 16 * lb, Rs, LDJ, 16 * jc, 0, 16 * lb + 16, lane);
-                const floatx4 dr = tile<T, false, false>(zero4(), Tb, LDC, 16 * lb, dZs, LDJ, 16 * jc, 16 * lb, kC, lane);
+                const floatx4 z = tilek<T, true, false, kC>(zero4(), Tb, LDC, 16 * lb, Rs, LDJ, 16 * jc, 0, lane);
+                const floatx4 dr = tilek<T, false, false, kC>(zero4(), Tb, LDC, 16 * lb, dZs, LDJ, 16 * jc, 0, lane);
                 put(Zs, LDJ, 16 * lb, 16 * jc, z, lane);
                 put(dRs, LDJ, 16 * lb, 16 * jc, dr, lane);
 #pragma unroll
@@ -640,7 +693,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int mb = 2 * (wave & 1) + u;
-                if (mb <= lbt) dTb[u] = tile<T, true, true>(dTb[u], dZs, LDJ, 16 * lbt, Rs, LDJ, 16 * mb, 0, J, lane);
+                if (mb <= lbt) dTb[u] = tilek<T, true, true, J>(dTb[u], dZs, LDJ, 16 * lbt, Rs, LDJ, 16 * mb, 0, lane);
             }
             __syncthreads();
         }
@@ -648,13 +701,13 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
             const int ib = NI * (wave & 1) + u;
-            if constexpr (DELTA) dKd[u] = tile<T, true, true>(dKd[u], dRs, LDJ, 16 * lbq, Ss, LDJ, 16 * ib, 0, J, lane);
-            dKr[u] = tile<T, true, true>(dKr[u], Zs, LDJ, 16 * lbq, dSs, LDJ, 16 * ib, 0, J, lane);
+            if constexpr (DELTA) dKd[u] = tilek<T, true, true, J>(dKd[u], dRs, LDJ, 16 * lbq, Ss, LDJ, 16 * ib, 0, lane);
+            dKr[u] = tilek<T, true, true, J>(dKr[u], Zs, LDJ, 16 * lbq, dSs, LDJ, 16 * ib, 0, lane);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int mb = 2 * (wave & 1) + u;
-            if (mb <= lbt) dAq[u] = tile<T, true, true>(dAq[u], dOs, LDJ, 16 * lbt, Zs, LDJ, 16 * mb, 0, J, lane);
+            if (mb <= lbt) dAq[u] = tilek<T, true, true, J>(dAq[u], dOs, LDJ, 16 * lbt, Zs, LDJ, 16 * mb, 0, lane);
         }
         __syncthreads();
     }
@@ -689,19 +742,24 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     __syncthreads();
     // F1: dG from dA . A; dbeta from T . dTb; X1 = T^T dTb; the row dots of the
     // dq/dk accumulators
-    if (wave == 0) {
-        float s1 = 0.f, s2 = 0.f;
-        for (int m = 0; m < kC; ++m) {
-            s1 += sc[lane * LDF + m];
-            s2 += sc[m * LDF + lane];
+    // row and column sums of the 64x64 matrices: thread t takes index t/8 and
+    // eight of its elements, then the 8 lanes of the index add up in DPP
+    const int sx = tid >> 3, sp = tid & 7;
+    {
+        float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int m = 8 * sp + u;
+            s1 += sc[sx * LDF + m];
+            s2 += sc[m * LDF + sx];
+            if constexpr (DELTA) s3 += to_f32(Tm[m * LDC + sx]) * to_f32(dTbs[m * LDC + sx]);
         }
-        dGs[lane] = s1 - s2;
-    }
-    if constexpr (DELTA) {
-        if (wave == 1) {
-            float s = 0.f;
-            for (int l = 0; l < kC; ++l) s += to_f32(Tm[l * LDC + lane]) * to_f32(dTbs[l * LDC + lane]);
-            dBs[lane] = s;
+        s1 = group_sum<8>(s1);
+        s2 = group_sum<8>(s2);
+        s3 = group_sum<8>(s3);
+        if (sp == 0) {
+            dGs[sx] = s1 - s2;
+            dBs[sx] = s3;
         }
     }
     floatx4 X1[2];
@@ -709,8 +767,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int sb = 2 * (wave & 1) + u;
-            X1[u] = tile<T, false, false>(zero4(), Tm, LDC, 16 * lbt, dTbs, LDC, 16 * sb,
-                                          16 * (lbt > sb ? lbt : sb), kC, lane);
+            X1[u] = tilek<T, false, false, kC>(zero4(), Tm, LDC, 16 * lbt, dTbs, LDC, 16 * sb, 0, lane);
         }
     }
     {
@@ -751,7 +808,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
             const int mb = 2 * (wave & 1) + u;
             const int m = 16 * mb + cl;
             floatx4 dm = zero4();
-            if (mb <= lbt) dm = tile<T, true, true>(zero4(), X1s, LDC, 16 * lbt, Tb, LDC, 16 * mb, 0, 16 * mb + 16, lane);
+            if (mb <= lbt) dm = tilek<T, true, true, kC>(zero4(), X1s, LDC, 16 * lbt, Tb, LDC, 16 * mb, 0, lane);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int l = 16 * lbt + g4 + rr;
@@ -773,20 +830,22 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     }
     // F4: dG and dbeta totals per row; dq = exp(G) d<-Q + P K;
     // dk = -exp(G) (dR S^T) + exp(G_C - G) d->K + P^T Q + (P2 + P2^T) K
-    if (wave == 0) {
-        float x = dGs[lane] + rowp[0][lane] + rowp[1][lane];
+    {
+        float s1 = 0.f, s2 = 0.f;
         if constexpr (DELTA) {
-            float s1 = 0.f, s2 = 0.f;
-            for (int m = 0; m < kC; ++m) {
-                s1 += E2[lane * LDF + m];
-                s2 += E2[m * LDF + lane];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int m = 8 * sp + u;
+                s1 += E2[sx * LDF + m];
+                s2 += E2[m * LDF + sx];
             }
-            x += s1 - s2;
+            s1 = group_sum<8>(s1);
+            s2 = group_sum<8>(s2);
         }
-        dGs[lane] = x;
-    }
-    if constexpr (DELTA) {
-        if (wave == 1) dBs[lane] += rowp2[0][lane] + rowp2[1][lane];
+        if (sp == 0) {
+            dGs[sx] += rowp[0][sx] + rowp[1][sx] + (s1 - s2);
+            if constexpr (DELTA) dBs[sx] += rowp2[0][sx] + rowp2[1][sx];
+        }
     }
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
@@ -798,11 +857,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
             aq[rr] = gam[l] * dQd[u][rr];
             ak[rr] = -gam[l] * dKd[u][rr] + (GATED ? expf(G[kC - 1] - G[l]) : 1.f) * dKr[u][rr];
         }
-        aq = tile<T, true, false>(aq, Aq, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, 16 * lbq + 16, lane);
-        ak = tile<T, false, false>(ak, Aq, LDC, 16 * lbq, Qs, LDQ, 16 * ib, 16 * lbq, kC, lane);
+        aq = tilek<T, true, false, kC>(aq, Aq, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, lane);
+        ak = tilek<T, false, false, kC>(ak, Aq, LDC, 16 * lbq, Qs, LDQ, 16 * ib, 0, lane);
         if constexpr (DELTA) {
-            ak = tile<T, true, false>(ak, Lm, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, 16 * lbq + 16, lane);
-            ak = tile<T, false, false>(ak, Lm, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 16 * lbq, kC, lane);
+            ak = tilek<T, true, false, kC>(ak, Lm, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, lane);
+            ak = tilek<T, false, false, kC>(ak, Lm, LDC, 16 * lbq, Ks, LDQ, 16 * ib, 0, lane);
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
