@@ -262,14 +262,14 @@ def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
 def bwd_alg_bytes(B, H, T, dk, dv, s, rule, gate, states):
     """Bytes the backward pass must move at minimum: q, k, v, dO (and g, beta)
     in, dq, dk, dv (and dg, dbeta) out, plus the saved chunk states when they
-    are read (fp32, one per chunk)."""
+    are read (one per chunk, token dtype)."""
     per_tok = (2 * dk + 2 * dv) * s + (2 * dk + dv) * s
     if gate == "scalar":
         per_tok += 2 * s
     if rule == "delta":
         per_tok += 2 * s
     nch = (T + 63) // 64
-    return B * H * T * per_tok + (B * H * nch * dk * dv * 4 if states else 0)
+    return B * H * T * per_tok + (B * H * nch * dk * dv * s if states else 0)
 
 
 def bwd_nominal_flops(B, H, T, dk, dv, C=64):
@@ -290,7 +290,7 @@ def time_backward(la, syn, case, dev, steps, warmup=2):
     x = syn.chunk_inputs_torch(case, dev)
     do = syn.grad_inputs_torch(case, dev)["do"]
     out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
-    states = torch.empty(la.chunk_states_shape(B, H, T, dk, dv), dtype=torch.float32, device=dev)
+    states = torch.empty(la.chunk_states_shape(B, H, T, dk, dv), dtype=torch.bfloat16, device=dev)
     grads = {"dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
              "dg": torch.empty_like(x["g"]), "dbeta": torch.empty_like(x["beta"]),
              "ds0": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)}

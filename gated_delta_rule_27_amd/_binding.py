@@ -394,14 +394,16 @@ def _train_inputs(q, k, v, g, beta, rule, gate):
 
 
 def chunk_states_shape(B, H, T, dk, dv, chunk=64):
-    """Shape of the per-chunk states chunk_fwd_save keeps: [B,H,ceil(T/64),dk,dv]."""
+    """Shape of the per-chunk states chunk_fwd_save keeps: [B,H,ceil(T/64),dk,dv]
+    (in the token dtype)."""
     return (B, H, (T + chunk - 1) // chunk, dk, dv)
 
 
 def chunk_fwd_save(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar", chunk=64,
                    out=None, s_final=None, states=None, return_state=True):
     """Chunk forward that also returns the state entering every chunk, for
-    chunk_bwd.  Returns (o, S_T or None, states [B,H,N,dk,dv] fp32)."""
+    chunk_bwd.  Returns (o, S_T or None, states [B,H,N,dk,dv] in the token
+    dtype)."""
     import torch
     lib = load()
     B, H, T, dk, dv, dev, dt = _train_inputs(q, k, v, g, beta, rule, gate)
@@ -417,9 +419,9 @@ def chunk_fwd_save(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="s
         _check(s_final, "s_final", (B, H, dk, dv), torch.float32, dev)
     shape = chunk_states_shape(B, H, T, dk, dv, chunk)
     if states is None:
-        states = torch.empty(shape, dtype=torch.float32, device=dev)
+        states = torch.empty(shape, dtype=dt, device=dev)
     else:
-        _check(states, "states", shape, torch.float32, dev)
+        _check(states, "states", shape, dt, dev)
     a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=_token_dtype(q), chunk=chunk)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib.linattn_chunk_fwd_save(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -451,7 +453,7 @@ def chunk_bwd(q, k, v, g, beta, dout, s0=None, dsT=None, *, states=None, rule="d
         if t is not None:
             _check(t, name, (B, H, dk, dv), torch.float32, dev)
     if states is not None:
-        _check(states, "states", chunk_states_shape(B, H, T, dk, dv, chunk), torch.float32, dev)
+        _check(states, "states", chunk_states_shape(B, H, T, dk, dv, chunk), dt, dev)
     shapes = {"dq": ((B, H, T, dk), dt), "dk": ((B, H, T, dk), dt), "dv": ((B, H, T, dv), dt),
               "dg": ((B, H, T), dt) if gate == "scalar" else None,
               "dbeta": ((B, H, T), dt) if rule == "delta" else None,

@@ -143,11 +143,12 @@ struct BwdCfg {
     static constexpr int J = sizeof(T) == 2 ? 32 : 16;   // value columns per step of the gradient kernel
     static constexpr int LDJ = J + PAD;
     static constexpr int LDF = kC + 4;               // fp32 scratch rows
-    // per-chunk operands of the reverse state pass: A^T, Tb^T [C][C],
-    // ->K [C][dk], <-Q^T, -<-K^T [dk][C] (token type, dense)
-    static constexpr int OPS = 2 * kC * kC + 3 * kC * DK;
-    static constexpr int O_AQT = 0, O_TBT = kC * kC, O_KR = 2 * kC * kC, O_QDT = O_KR + kC * DK,
-                         O_NKDT = O_QDT + DK * kC;
+    // per-chunk operands (token type, dense): of the reverse state pass A^T,
+    // Tb^T [C][C], ->K [C][dk], <-Q^T, -<-K^T [dk][C]; and Tb [C][C] for the
+    // gradient pass
+    static constexpr int OPS = 3 * kC * kC + 3 * kC * DK;
+    static constexpr int O_AQT = 0, O_TBT = kC * kC, O_TB = 2 * kC * kC, O_KR = 3 * kC * kC,
+                         O_QDT = O_KR + kC * DK, O_NKDT = O_QDT + DK * kC;
 };
 
 // Shared front of the two per-chunk kernels: chunk r's q and k (zero rows past
@@ -308,6 +309,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q
             store(out + C::O_TBT + l * kC + m0, x);
         }
     }
+    if constexpr (DELTA) {
+        for (int v = tid; v < kC * kC / E; v += kNT) {
+            const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+            *reinterpret_cast<i4*>(out + C::O_TB + l * kC + m0) = *reinterpret_cast<const i4*>(L.Tb + l * LDC + m0);
+        }
+    }
     // ->K = exp(G_C - G) K
     for (int v = tid; v < kC * DK / E; v += kNT) {
         const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q
 template <typename T, int DK, int RULE>
 __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__ dout, const T* __restrict__ ops,
                                                            const float* __restrict__ gC, const float* dsT,
-                                                           float* __restrict__ dstates, float* ds0,
+                                                           T* __restrict__ dstates, float* ds0,
                                                            int64_t Tlen, int64_t nchunks, int DV)
 {
     using C = BwdCfg<T, DK>;
@@ -367,8 +374,13 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nvb = DV / 64;
-    const int64_t bh = blockIdx.x / nvb;
-    const int vb = blockIdx.x % nvb;
+    // the value blocks of one head read the same chunk operands: dispatch puts
+    // workgroup i on XCD i mod 8, so consecutive logical blocks are spread to
+    // land on one XCD (and its L2)
+    int blk = blockIdx.x;
+    if ((gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+    const int64_t bh = blk / nvb;
+    const int vb = blk % nvb;
 
     if (wave < 4) {
         const int n0 = 16 * wave;
@@ -385,11 +397,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
         for (int64_t c = nchunks - 1; c >= 0; --c) {
             const int ln = opaque(lane);
             const int buf = (int)(c & 1);
-            float* dsr = dstates + ((bh * nchunks + c) * DK + g4) * DV + col;
+            T* dsr = dstates + ((bh * nchunks + c) * DK + g4) * DV + col;
 #pragma unroll
             for (int db = 0; db < ND; ++db)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) dsr[(16 * db + rr) * DV] = dS[db][rr];
+                for (int rr = 0; rr < 4; ++rr) dsr[(16 * db + rr) * DV] = from_f32<T>(dS[db][rr]);
             // ---- phase 1: dZ = A^T dO + ->K dS ; dR = Tb^T dZ ----
             floatx4 X[4], dR[4];
 #pragma unroll
@@ -534,8 +546,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
 template <typename T, int DK, int RULE, int GATE>
 __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
-    const T* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ states,
-    const float* __restrict__ dstates, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    const T* __restrict__ beta, const T* __restrict__ dout, const T* __restrict__ states,
+    const T* __restrict__ dstates, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
     T* __restrict__ dg, T* __restrict__ dbeta, int64_t Tlen, int64_t nchunks, int DV)
 {
     using C = BwdCfg<T, DK>;
@@ -567,16 +579,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     T* const Tm = CC + 2 * kC * LDC;
     T* const Tb = CC + 3 * kC * LDC;
     IntraLds<T, DK> L{Qs, Ks, Aq, Lm, Tm, Tb, G, gam, bet};
-    const float* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
-    const float* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
+    const T* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
+    const T* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
 
     // the value block's dO and V rows and its S_r and dS_{r+1} columns go
     // through registers: the next block's loads are issued before this block's
     // products (the first block's before the intra-chunk work)
     constexpr int VR = J / E, NVJ = (kC * VR + kNT - 1) / kNT;
-    constexpr int SR = J / 4, NSJ = (DK * SR + kNT - 1) / kNT;
-    i4 pdo[NVJ], pv[NVJ];
-    floatx4 ps[NSJ], pds[NSJ];
+    constexpr int SR = J / E, NSJ = (DK * SR + kNT - 1) / kNT;
+    i4 pdo[NVJ], pv[NVJ], ps[NSJ], pds[NSJ];
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < NVJ; ++u) {
@@ -589,11 +600,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
         }
 #pragma unroll
         for (int u = 0; u < NSJ; ++u) {
-            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * 4;
-            ps[u] = pds[u] = zero4();
+            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * E;
+            ps[u] = pds[u] = i4{0, 0, 0, 0};
             if (i < DK * SR) {
-                ps[u] = *reinterpret_cast<const floatx4*>(Sr + row * DV + j0 + c);
-                pds[u] = *reinterpret_cast<const floatx4*>(dSr + row * DV + j0 + c);
+                ps[u] = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
+                pds[u] = *reinterpret_cast<const i4*>(dSr + row * DV + j0 + c);
             }
         }
     };
@@ -629,15 +640,15 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
         }
 #pragma unroll
         for (int u = 0; u < NSJ; ++u) {
-            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * 4;
+            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * E;
             if (i < DK * SR) {
-                const floatx4 a = ps[u], b = pds[u];
-                sdot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+                T a[E], b[E];
+                __builtin_memcpy(a, &ps[u], 16);
+                __builtin_memcpy(b, &pds[u], 16);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    Ss[row * LDJ + c + x] = from_f32<T>(a[x]);
-                    dSs[row * LDJ + c + x] = from_f32<T>(b[x]);
-                }
+                for (int x = 0; x < E; ++x) sdot += to_f32(a[x]) * to_f32(b[x]);
+                *reinterpret_cast<i4*>(Ss + row * LDJ + c) = ps[u];
+                *reinterpret_cast<i4*>(dSs + row * LDJ + c) = pds[u];
             }
         }
         __syncthreads();
@@ -892,6 +903,483 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
     }
 }
 
+// ============================================================================
+// bwd_grad_bf16_kernel: the gradient pass for bf16 tokens.  Same equations as
+// bwd_grad_kernel; every matrix-core operand is one contiguous vector read:
+// each matrix is kept in LDS in the orientation its products contract over
+// (transposed copies are written while staging or from result tiles), A^T, Tb
+// and Tb^T come from the operand pass, and the row and column sums of the
+// final phase are reduced in registers (DPP rows, lane shuffles).
+// ============================================================================
+// result tile transposed into P[n*ld + m] (four contiguous values per lane)
+__device__ __forceinline__ void put_t(bf16* P, int ld, int m0, int n0, floatx4 v, int lane)
+{
+    store_tile_t(P + n0 * ld + m0, ld, v, lane);
+}
+
+// column sums of a result tile: every lane gets the sum over the 16 rows of its
+// column l%16
+__device__ __forceinline__ float tile_colsum(floatx4 x)
+{
+    float s = x[0] + x[1] + x[2] + x[3];
+    s += __shfl_xor(s, 16, kWave);
+    s += __shfl_xor(s, 32, kWave);
+    return s;
+}
+
+template <int DK, int RULE, int GATE>
+__global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
+    const bf16* __restrict__ ops, const bf16* __restrict__ states, const bf16* __restrict__ dstates,
+    bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ dg,
+    bf16* __restrict__ dbeta, int64_t Tlen, int64_t nchunks, int DV)
+{
+    using T = bf16;
+    using C = BwdCfg<T, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, E = 8, J = 32, LDJ = J + 8;
+    constexpr bool DELTA = RULE == kRuleDelta, GATED = GATE == kGateScalar;
+    constexpr int NI = DK / 32;            // key-column tiles per wave (of dq, dk)
+    // value-block arrays of the loop (row-major and transposed copies), and the
+    // matrices of the final phase, in the same bytes
+    constexpr int LOOP_ELEMS = 5 * kC * LDJ + 2 * DK * LDJ + 3 * J * LDC + 2 * J * LDQ;
+    constexpr int FIN_ELEMS = 5 * kC * LDC + 2 * DK * LDC;
+    constexpr int REGION = 2 * (LOOP_ELEMS > FIN_ELEMS ? LOOP_ELEMS : FIN_ELEMS);
+
+    __shared__ __align__(16) T Ks[kC * LDQ];
+    __shared__ __align__(16) T AqT[kC * LDC];
+    __shared__ __align__(16) T Tb[DELTA ? kC * LDC : 8];
+    __shared__ __align__(16) T TbT[DELTA ? kC * LDC : 8];
+    __shared__ __align__(16) unsigned char region[REGION];
+    __shared__ float G[kC], gam[kC], bet[kC];
+    __shared__ float rowE[2][kC], colE[4][kC], rowB[2][kC], colB[4][kC], rdp[2][kC], krp[2][kC], sdp[8];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.x / nchunks, r = blockIdx.x % nchunks;
+    const int64_t t0 = r * kC;
+    const int tvalid = (int)(Tlen - t0 < kC ? Tlen - t0 : kC);
+    const int cl = lane & 15, g4 = 4 * (lane >> 4);
+    const int lbq = wave >> 1, lbt = wave >> 1;    // row block of this wave's tiles
+
+    // loop arrays
+    T* const dOs = reinterpret_cast<T*>(region);   // [C][LDJ]
+    T* const Rs = dOs + kC * LDJ;
+    T* const Zs = Rs + kC * LDJ;
+    T* const dZs = Zs + kC * LDJ;
+    T* const dRs = dZs + kC * LDJ;
+    T* const Ss = dRs + kC * LDJ;                   // [DK][LDJ]
+    T* const dSs = Ss + DK * LDJ;
+    T* const dOT = dSs + DK * LDJ;                  // [J][LDC]
+    T* const RT = dOT + J * LDC;
+    T* const dZT = RT + J * LDC;
+    T* const ST = dZT + J * LDC;                    // [J][LDQ]
+    T* const dSnT = ST + J * LDQ;
+    // final-phase arrays
+    T* const Pm = reinterpret_cast<T*>(region);    // [C][LDC]
+    T* const PT = Pm + kC * LDC;
+    T* const dTbT = PT + kC * LDC;                  // then P2
+    T* const LT = dTbT + kC * LDC;                  // then P2^T
+    T* const TT = LT + kC * LDC;                    // then X1
+    T* const KT = TT + kC * LDC;                    // [DK][LDC]
+    T* const QT = KT + DK * LDC;
+
+    // ---- prologue: k, A^T, Tb, Tb^T to LDS; q to registers; gate prefix ----
+    constexpr int NKV = kC * DK / E / kNT;          // k / q vectors per thread
+    i4 rq[NKV];
+    {
+        const T* base = ops + (bh * nchunks + r) * (int64_t)C::OPS;
+        i4 rk[NKV], ra, rt = {0, 0, 0, 0}, rb = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < NKV; ++u) {
+            const int i = tid + u * kNT, row = i / (DK / E), c = (i % (DK / E)) * E;
+            rk[u] = rq[u] = i4{0, 0, 0, 0};
+            if (row < tvalid) {
+                rk[u] = *reinterpret_cast<const i4*>(k + (bh * Tlen + t0 + row) * DK + c);
+                rq[u] = *reinterpret_cast<const i4*>(q + (bh * Tlen + t0 + row) * DK + c);
+            }
+        }
+        ra = *reinterpret_cast<const i4*>(base + C::O_AQT + tid * E);
+        if constexpr (DELTA) {
+            rt = *reinterpret_cast<const i4*>(base + C::O_TBT + tid * E);
+            rb = *reinterpret_cast<const i4*>(base + C::O_TB + tid * E);
+        }
+#pragma unroll
+        for (int u = 0; u < NKV; ++u) {
+            const int i = tid + u * kNT, row = i / (DK / E), c = (i % (DK / E)) * E;
+            *reinterpret_cast<i4*>(Ks + row * LDQ + c) = rk[u];
+        }
+        const int row = tid / (kC / E), c = (tid % (kC / E)) * E;
+        *reinterpret_cast<i4*>(AqT + row * LDC + c) = ra;
+        if constexpr (DELTA) {
+            *reinterpret_cast<i4*>(TbT + row * LDC + c) = rt;
+            *reinterpret_cast<i4*>(Tb + row * LDC + c) = rb;
+        }
+    }
+    if (wave == 0) {
+        float gl = 0.f, bl = 0.f;
+        if (lane < tvalid) {
+            if constexpr (GATED) gl = to_f32(g[bh * Tlen + t0 + lane]);
+            if constexpr (DELTA) bl = to_f32(beta[bh * Tlen + t0 + lane]);
+        }
+        const float Gl = wave_prefix_sum(gl);
+        G[lane] = Gl;
+        gam[lane] = GATED ? expf(Gl) : 1.f;
+        bet[lane] = bl;
+    }
+
+    // ---- value blocks: dO, V, S_r, dS_{r+1} through registers, next block prefetched ----
+    const T* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
+    const T* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
+    constexpr int VR = J / E, NVJ = (kC * VR + kNT - 1) / kNT;
+    constexpr int SR = J / E, NSJ = (DK * SR + kNT - 1) / kNT;
+    i4 pdo[NVJ], pv[NVJ], ps[NSJ], pds[NSJ];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < NVJ; ++u) {
+            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            pdo[u] = pv[u] = i4{0, 0, 0, 0};
+            if (i < kC * VR && row < tvalid) {
+                pdo[u] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t0 + row) * DV + j0 + c);
+                pv[u] = *reinterpret_cast<const i4*>(v + (bh * Tlen + t0 + row) * DV + j0 + c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NSJ; ++u) {
+            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * E;
+            ps[u] = pds[u] = i4{0, 0, 0, 0};
+            if (i < DK * SR) {
+                ps[u] = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
+                pds[u] = *reinterpret_cast<const i4*>(dSr + row * DV + j0 + c);
+            }
+        }
+    };
+    fetch(0);
+
+    floatx4 dQd[NI], dKd[NI], dKr[NI], dAq[2], dTb[2];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) dQd[u] = dKd[u] = dKr[u] = zero4();
+    dAq[0] = dAq[1] = dTb[0] = dTb[1] = zero4();
+    float sdot = 0.f;
+
+    for (int j0 = 0; j0 < DV; j0 += J) {
+        __syncthreads();       // the previous block's arrays are free (and the prologue's LDS is written)
+#pragma unroll
+        for (int u = 0; u < NVJ; ++u) {
+            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            if (i < kC * VR) {
+                *reinterpret_cast<i4*>(dOs + row * LDJ + c) = pdo[u];
+                *reinterpret_cast<i4*>(Zs + row * LDJ + c) = pv[u];
+                T x[E];
+                __builtin_memcpy(x, &pdo[u], 16);
+#pragma unroll
+                for (int e = 0; e < E; ++e) dOT[(c + e) * LDC + row] = x[e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NSJ; ++u) {
+            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * E;
+            if (i < DK * SR) {
+                T a[E], b[E];
+                __builtin_memcpy(a, &ps[u], 16);
+                __builtin_memcpy(b, &pds[u], 16);
+#pragma unroll
+                for (int x = 0; x < E; ++x) {
+                    sdot += to_f32(a[x]) * to_f32(b[x]);
+                    ST[(c + x) * LDQ + row] = a[x];
+                    dSnT[(c + x) * LDQ + row] = b[x];
+                }
+                *reinterpret_cast<i4*>(Ss + row * LDJ + c) = ps[u];
+                *reinterpret_cast<i4*>(dSs + row * LDJ + c) = pds[u];
+            }
+        }
+        __syncthreads();
+        if (j0 + J < DV) fetch(j0 + J);
+        // ---- step A: dZ = A^T dO + ->K dS ; R = V - <-K S_r ; d<-Q += dO S_r^T ----
+        {
+            const int lb = wave >> 1, jc = wave & 1;
+            const floatx4 a1 = tilek<T, true, true, kC>(zero4(), AqT, LDC, 16 * lb, dOT, LDC, 16 * jc, 0, lane);
+            floatx4 a2 = tilek<T, true, true, 64>(zero4(), Ks, LDQ, 16 * lb, dSnT, LDQ, 16 * jc, 0, lane);
+            if constexpr (DK > 64) a2 = tilek<T, true, true, 64>(a2, Ks, LDQ, 16 * lb, dSnT, LDQ, 16 * jc, 64, lane);
+            floatx4 dz;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lb + g4 + rr;
+                dz[rr] = a1[rr] + (GATED ? expf(G[kC - 1] - G[l]) : 1.f) * a2[rr];
+            }
+            put(dZs, LDJ, 16 * lb, 16 * jc, dz, lane);
+            put_t(dZT, LDC, 16 * lb, 16 * jc, dz, lane);
+            if constexpr (DELTA) {
+                floatx4 ks = tilek<T, true, true, 64>(zero4(), Ks, LDQ, 16 * lb, ST, LDQ, 16 * jc, 0, lane);
+                if constexpr (DK > 64) ks = tilek<T, true, true, 64>(ks, Ks, LDQ, 16 * lb, ST, LDQ, 16 * jc, 64, lane);
+                floatx4 rv;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    rv[rr] = to_f32(Zs[l * LDJ + 16 * jc + cl]) - gam[l] * ks[rr];
+                }
+                put(Rs, LDJ, 16 * lb, 16 * jc, rv, lane);
+                put_t(RT, LDC, 16 * lb, 16 * jc, rv, lane);
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    if (l < tvalid) dv[(bh * Tlen + t0 + l) * DV + j0 + 16 * jc + cl] = from_f32<T>(dz[rr]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NI; ++u)
+            dQd[u] = tilek<T, true, true, J>(dQd[u], dOs, LDJ, 16 * lbq, Ss, LDJ, 16 * (NI * (wave & 1) + u), 0, lane);
+        __syncthreads();
+        // ---- step B (delta): Z = Tb R ; dR = Tb^T dZ (= dv) ; dTb += dZ R^T ----
+        if constexpr (DELTA) {
+            const int lb = wave >> 1, jc = wave & 1;
+            const floatx4 z = tilek<T, true, true, kC>(zero4(), Tb, LDC, 16 * lb, RT, LDC, 16 * jc, 0, lane);
+            const floatx4 dr = tilek<T, true, true, kC>(zero4(), TbT, LDC, 16 * lb, dZT, LDC, 16 * jc, 0, lane);
+            put(Zs, LDJ, 16 * lb, 16 * jc, z, lane);
+            put(dRs, LDJ, 16 * lb, 16 * jc, dr, lane);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lb + g4 + rr;
+                if (l < tvalid) dv[(bh * Tlen + t0 + l) * DV + j0 + 16 * jc + cl] = from_f32<T>(dr[rr]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int mb = 2 * (wave & 1) + u;
+                if (mb <= lbt) dTb[u] = tilek<T, true, true, J>(dTb[u], dZs, LDJ, 16 * lbt, Rs, LDJ, 16 * mb, 0, lane);
+            }
+            __syncthreads();
+        }
+        // ---- step C: d<-K += dR S_r^T (negated later) ; d->K += Z dS^T ; dA += dO Z^T ----
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            const int ib = NI * (wave & 1) + u;
+            if constexpr (DELTA) dKd[u] = tilek<T, true, true, J>(dKd[u], dRs, LDJ, 16 * lbq, Ss, LDJ, 16 * ib, 0, lane);
+            dKr[u] = tilek<T, true, true, J>(dKr[u], Zs, LDJ, 16 * lbq, dSs, LDJ, 16 * ib, 0, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            if (mb <= lbt) dAq[u] = tilek<T, true, true, J>(dAq[u], dOs, LDJ, 16 * lbt, Zs, LDJ, 16 * mb, 0, lane);
+        }
+    }
+    __syncthreads();
+
+    // ============ final phase ============
+    {
+        const float tot = wave_last(wave_prefix_sum(sdot));
+        if (lane == 0) sdp[wave] = tot;
+    }
+    // F0: P = dA . D (and P^T), dA . A kept in registers; dTb^T; L in registers
+    // and L^T; K^T and Q^T
+    floatx4 Ev[2], Lr[2], Bt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int mb = 2 * (wave & 1) + u;
+        const int m = 16 * mb + cl;
+        floatx4 pv2, dt, lv = zero4();
+        if constexpr (DELTA) {
+            if (mb <= lbt) {
+                lv = tilek<T, true, true, 64>(zero4(), Ks, LDQ, 16 * lbt, Ks, LDQ, 16 * mb, 0, lane);
+                if constexpr (DK > 64) lv = tilek<T, true, true, 64>(lv, Ks, LDQ, 16 * lbt, Ks, LDQ, 16 * mb, 64, lane);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbt + g4 + rr;
+            const bool on = mb <= lbt && m <= l;
+            const float d = GATED ? expf(fminf(G[l] - G[m], 0.f)) : 1.f;
+            const float da = on ? dAq[u][rr] : 0.f;
+            Ev[u][rr] = da * to_f32(AqT[m * LDC + l]);
+            pv2[rr] = da * d;
+            dt[rr] = on ? dTb[u][rr] : 0.f;
+            Lr[u][rr] = (mb <= lbt && m < l) ? lv[rr] * d : 0.f;
+        }
+        put(Pm, LDC, 16 * lbt, 16 * mb, pv2, lane);
+        put_t(PT, LDC, 16 * lbt, 16 * mb, pv2, lane);
+        if constexpr (DELTA) {
+            Bt[u] = dt;
+            put_t(dTbT, LDC, 16 * lbt, 16 * mb, dt, lane);
+            put_t(LT, LDC, 16 * lbt, 16 * mb, Lr[u], lane);
+        }
+    }
+    {
+        // K^T from LDS, Q^T from the registers loaded in the prologue
+        for (int i = tid; i < kC * DK / 4; i += kNT) {
+            const int m = i / (DK / 4), c = (i % (DK / 4)) * 4;
+            const bf16x4 x = *reinterpret_cast<const bf16x4*>(Ks + m * LDQ + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) KT[(c + e) * LDC + m] = x[e];
+        }
+#pragma unroll
+        for (int u = 0; u < NKV; ++u) {
+            const int i = tid + u * kNT, row = i / (DK / E), c = (i % (DK / E)) * E;
+            T x[E];
+            __builtin_memcpy(x, &rq[u], 16);
+#pragma unroll
+            for (int e = 0; e < E; ++e) QT[(c + e) * LDC + row] = x[e];
+        }
+    }
+    __syncthreads();
+    // F1: T^T = I - L^T Tb^T (upper tiles); the row dots of the dq/dk accumulators
+    floatx4 X1[2];
+    if constexpr (DELTA) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kb = 2 * (wave & 1) + u;
+            floatx4 tt = zero4();
+            if (kb >= lbt) tt = tilek<T, true, true, kC>(zero4(), LT, LDC, 16 * lbt, Tb, LDC, 16 * kb, 0, lane);
+            X1[u] = tt;                             // held until T^T is stored
+        }
+    }
+    {
+        float rd[4] = {0.f, 0.f, 0.f, 0.f}, kr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            const int i = 16 * (NI * (wave & 1) + u) + cl;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbq + g4 + rr;
+                const float qv = to_f32(QT[i * LDC + l]), kv = to_f32(Ks[l * LDQ + i]);
+                const float er = GATED ? expf(G[kC - 1] - G[l]) : 1.f;
+                const float t3 = kv * er * dKr[u][rr];
+                rd[rr] += qv * gam[l] * dQd[u][rr] - kv * gam[l] * dKd[u][rr] - t3;
+                kr[rr] += t3;
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float a = group_sum<16>(rd[rr]), b = group_sum<16>(kr[rr]);
+            if (cl == 0) {
+                rdp[wave & 1][16 * lbq + g4 + rr] = a;
+                krp[wave & 1][16 * lbq + g4 + rr] = b;
+            }
+        }
+    }
+    if constexpr (DELTA) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kb = 2 * (wave & 1) + u;
+            floatx4 t;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbt + g4 + rr, kk = 16 * kb + cl;
+                t[rr] = kb < lbt ? 0.f : (kk == l ? 1.f : 0.f) - (kk > l ? X1[u][rr] : 0.f);
+            }
+            put(TT, LDC, 16 * lbt, 16 * kb, t, lane);
+        }
+        __syncthreads();
+        // F2: dbeta (part 1) = column sums of T . dTb; X1 = T^T dTb
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            const int m = 16 * mb + cl;
+            floatx4 f;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbt + g4 + rr;
+                f[rr] = Bt[u][rr] * to_f32(TT[m * LDC + l]);
+            }
+            const float cs = tile_colsum(f);
+            if (g4 == 0) colB[lbt][m] = cs;
+            X1[u] = tilek<T, true, true, kC>(zero4(), TT, LDC, 16 * lbt, dTbT, LDC, 16 * mb, 0, lane);
+        }
+        __syncthreads();
+        // F3: X1 over T^T; then dM = -X1 Tb^T, dL = diag(beta) dM (strict),
+        // P2 = dL . D and its transpose, dbeta part 2, dL . L into the sums
+#pragma unroll
+        for (int u = 0; u < 2; ++u) put(TT, LDC, 16 * lbt, 16 * (2 * (wave & 1) + u), X1[u], lane);
+        __syncthreads();
+        float rb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            const int m = 16 * mb + cl;
+            floatx4 dm = zero4(), p2;
+            if (mb <= lbt) dm = tilek<T, true, true, kC>(zero4(), TT, LDC, 16 * lbt, Tb, LDC, 16 * mb, 0, lane);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbt + g4 + rr;
+                const bool strict = mb <= lbt && m < l;
+                const float dM = -dm[rr];
+                rb[rr] += strict ? dM * Lr[u][rr] : 0.f;
+                const float dl = strict ? bet[l] * dM : 0.f;
+                Ev[u][rr] += dl * Lr[u][rr];
+                p2[rr] = dl * (GATED ? expf(fminf(G[l] - G[m], 0.f)) : 1.f);
+            }
+            put(dTbT, LDC, 16 * lbt, 16 * mb, p2, lane);    // P2
+            put_t(LT, LDC, 16 * lbt, 16 * mb, p2, lane);    // P2^T
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float a = group_sum<16>(rb[rr]);
+            if (cl == 0) rowB[wave & 1][16 * lbt + g4 + rr] = a;
+        }
+    }
+    // row and column sums of dA . A + dL . L
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int mb = 2 * (wave & 1) + u;
+        const float cs = tile_colsum(Ev[u]);
+        if (g4 == 0) colE[lbt][16 * mb + cl] = cs;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const float a = group_sum<16>(Ev[0][rr] + Ev[1][rr]);
+        if (cl == 0) rowE[wave & 1][16 * lbt + g4 + rr] = a;
+    }
+    __syncthreads();
+    // F4: dq = exp(G) d<-Q + P K;  dk = -exp(G) (dR S^T) + exp(G_C - G) d->K + P^T Q + P2 K + P2^T K
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        const int ib = NI * (wave & 1) + u;
+        floatx4 aq, ak;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbq + g4 + rr;
+            aq[rr] = gam[l] * dQd[u][rr];
+            ak[rr] = -gam[l] * dKd[u][rr] + (GATED ? expf(G[kC - 1] - G[l]) : 1.f) * dKr[u][rr];
+        }
+        aq = tilek<T, true, true, kC>(aq, Pm, LDC, 16 * lbq, KT, LDC, 16 * ib, 0, lane);
+        ak = tilek<T, true, true, kC>(ak, PT, LDC, 16 * lbq, QT, LDC, 16 * ib, 0, lane);
+        if constexpr (DELTA) {
+            ak = tilek<T, true, true, kC>(ak, dTbT, LDC, 16 * lbq, KT, LDC, 16 * ib, 0, lane);
+            ak = tilek<T, true, true, kC>(ak, LT, LDC, 16 * lbq, KT, LDC, 16 * ib, 0, lane);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbq + g4 + rr;
+            if (l < tvalid) {
+                dq[(bh * Tlen + t0 + l) * DK + 16 * ib + cl] = from_f32<T>(aq[rr]);
+                dk[(bh * Tlen + t0 + l) * DK + 16 * ib + cl] = from_f32<T>(ak[rr]);
+            }
+        }
+    }
+    // F5: dG per row, its chunk-end extras, dg = reverse prefix sum; dbeta
+    if (wave == 0) {
+        const int l = kC - 1 - lane;                 // reversed: lane 0 holds the last row
+        float x = rowE[0][l] + rowE[1][l] - (colE[0][l] + colE[1][l] + colE[2][l] + colE[3][l]) + rdp[0][l] +
+                  rdp[1][l];
+        if constexpr (GATED) {
+            const float krs = wave_last(wave_prefix_sum(krp[0][lane] + krp[1][lane]));
+            float sd = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) sd += sdp[w];
+            if (lane == 0) x += krs + gam[kC - 1] * sd;
+            const float dgs = wave_prefix_sum(x);
+            if (l < tvalid) dg[bh * Tlen + t0 + l] = from_f32<T>(dgs);
+        }
+    }
+    if constexpr (DELTA) {
+        if (wave == 1 && lane < tvalid) {
+            const float b = colB[0][lane] + colB[1][lane] + colB[2][lane] + colB[3][lane] + rowB[0][lane] +
+                            rowB[1][lane];
+            dbeta[bh * Tlen + t0 + lane] = from_f32<T>(b);
+        }
+    }
+}
+
 template <typename T, int DK, int RULE, int GATE>
 hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
 {
@@ -908,14 +1396,25 @@ hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0, s,
-                       static_cast<const T*>(p.dout), static_cast<const T*>(p.ops), p.gC, p.dsT, p.dstates, p.ds0,
+                       static_cast<const T*>(p.dout), static_cast<const T*>(p.ops), p.gC, p.dsT,
+                       static_cast<T*>(p.dstates), p.ds0,
                        p.T, nchunks, p.dv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || bh * nchunks == 0) return e;
-    hipLaunchKernelGGL((bwd_grad_kernel<T, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s,
-                       q, k, static_cast<const T*>(p.v), g, beta, static_cast<const T*>(p.dout), p.states,
-                       p.dstates, static_cast<T*>(p.dq), static_cast<T*>(p.dk_out), static_cast<T*>(p.dv_out),
-                       static_cast<T*>(p.dg), static_cast<T*>(p.dbeta), p.T, nchunks, p.dv);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((bwd_grad_bf16_kernel<DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0,
+                           s, q, k, static_cast<const T*>(p.v), g, beta, static_cast<const T*>(p.dout),
+                           static_cast<const T*>(p.ops), static_cast<const T*>(p.states),
+                           static_cast<const T*>(p.dstates), static_cast<T*>(p.dq),
+                           static_cast<T*>(p.dk_out), static_cast<T*>(p.dv_out), static_cast<T*>(p.dg),
+                           static_cast<T*>(p.dbeta), p.T, nchunks, p.dv);
+    else
+        hipLaunchKernelGGL((bwd_grad_kernel<T, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s,
+                           q, k, static_cast<const T*>(p.v), g, beta, static_cast<const T*>(p.dout),
+                           static_cast<const T*>(p.states), static_cast<const T*>(p.dstates),
+                           static_cast<T*>(p.dq), static_cast<T*>(p.dk_out),
+                           static_cast<T*>(p.dv_out), static_cast<T*>(p.dg), static_cast<T*>(p.dbeta), p.T,
+                           nchunks, p.dv);
     return hipGetLastError();
 }
 
@@ -942,7 +1441,7 @@ bool chunk_bwd_supported(int dk, int dv, int rule, int gate, int dtype)
 size_t chunk_bwd_ops_bytes(int dk, int dtype)
 {
     const size_t esz = dtype == kBF16 ? 2 : 4;
-    return (size_t)(2 * kC * kC + 3 * kC * dk) * esz;
+    return (size_t)(3 * kC * kC + 3 * kC * dk) * esz;
 }
 
 hipError_t launch_chunk_bwd(const ChunkBwdProblem& p, hipStream_t s)

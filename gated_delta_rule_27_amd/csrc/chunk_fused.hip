@@ -92,12 +92,12 @@ __device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
 }
 
 // SAVE: also write the state entering every chunk, states[b,h,r] = S_r
-// ([dk][dv] fp32 per chunk), for the backward pass.
+// ([dk][dv] per chunk, rounded to the token type once), for the backward pass.
 template <typename T, int DK, int RULE, int GATE, bool SAVE = false>
 __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const float* s0, T* __restrict__ o,
-    float* s_final, float* __restrict__ states, int64_t Tlen, int DV, int nblocks, int prep)
+    float* s_final, T* __restrict__ states, int64_t Tlen, int DV, int nblocks, int prep)
 {
     using Cfg = FusedCfg<T, DK, RULE, GATE>;
     using F = typename Frag16<T>::type;
@@ -378,11 +378,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             stage(t0);
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
             if constexpr (SAVE) {
-                float* sr = states + ((bh * nchunks + r) * DK) * DV + vb * kDVB + n0 + cl;
+                T* sr = states + ((bh * nchunks + r) * DK) * DV + vb * kDVB + n0 + cl;
 #pragma unroll
                 for (int db = 0; db < ND; ++db)
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) sr[(16 * db + g4 + rr) * DV] = S[db][rr];
+                    for (int rr = 0; rr < 4; ++rr) sr[(16 * db + g4 + rr) * DV] = from_f32<T>(S[db][rr]);
             }
             lds_barrier();
 
@@ -657,20 +657,20 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 }
 
 template <typename T, int DK, int RULE, int GATE, bool SAVE>
-hipError_t launch_t(const ChunkProblem& p, float* states, hipStream_t s)
+hipError_t launch_t(const ChunkProblem& p, void* states, hipStream_t s)
 {
     const int nvb = p.dv / kDVB;
     const int64_t nblocks = p.B * p.H * nvb;
     hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE, SAVE>), dim3((unsigned)nblocks), dim3(kNT), 0,
                        s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
                        static_cast<const T*>(p.v), static_cast<const T*>(p.g),
-                       static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, states,
+                       static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, static_cast<T*>(states),
                        p.T, p.dv, (int)nblocks, p.prep);
     return hipGetLastError();
 }
 
 template <typename T, int DK, bool SAVE>
-hipError_t by_rule_gate(const ChunkProblem& p, float* states, hipStream_t s)
+hipError_t by_rule_gate(const ChunkProblem& p, void* states, hipStream_t s)
 {
     if (p.rule == kRuleAdd)
         return p.gate == kGateNone ? launch_t<T, DK, kRuleAdd, kGateNone, SAVE>(p, states, s)
@@ -696,7 +696,7 @@ hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t s)
     return by_rule_gate<float, 64, false>(p, nullptr, s);
 }
 
-hipError_t launch_chunk_fused_save(const ChunkProblem& p, float* states, hipStream_t s)
+hipError_t launch_chunk_fused_save(const ChunkProblem& p, void* states, hipStream_t s)
 {
     if (p.dtype == kBF16)
         return p.dk == 64 ? by_rule_gate<bf16, 64, true>(p, states, s)

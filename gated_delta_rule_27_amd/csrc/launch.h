@@ -71,8 +71,8 @@ hipError_t launch_norm_finish(const NormalizedProblem& p, hipStream_t stream);
 bool chunk_fused_supported(const ChunkProblem& p);
 hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t stream);
 // The same kernel also writing the state entering every chunk,
-// states [B,H,nchunks,dk,dv] fp32 (for the backward pass).
-hipError_t launch_chunk_fused_save(const ChunkProblem& p, float* states, hipStream_t stream);
+// states [B,H,nchunks,dk,dv] in the token type (for the backward pass).
+hipError_t launch_chunk_fused_save(const ChunkProblem& p, void* states, hipStream_t stream);
 // Single-pass chunk kernel for bf16 tokens (gate NONE or SCALAR), pipelined:
 // chunk r+1's intra-chunk work beside chunk r's state pass.
 bool chunk_pipe_supported(const ChunkProblem& p);
@@ -93,13 +93,13 @@ struct ChunkBwdProblem {
     int64_t B, H, T;
     int dk, dv, rule, gate, dtype;
     const void *q, *k, *v, *g, *beta, *dout;
-    const float* states;          // [B,H,N,dk,dv] fp32, S entering chunk r
+    const void* states;           // [B,H,N,dk,dv] token type, S entering chunk r
     const float* dsT;             // [B,H,dk,dv] or NULL
     void *dq, *dk_out, *dv_out, *dg, *dbeta;
     float* ds0;                   // [B,H,dk,dv] or NULL
     void* ops;                    // [B,H,N] chunk operand blocks (chunk_bwd_ops_bytes each)
     float* gC;                    // [B,H,N] exp of the chunk's total log-gate
-    float* dstates;               // [B,H,N,dk,dv] gradient w.r.t. S leaving chunk r
+    void* dstates;                // [B,H,N,dk,dv] token type, gradient w.r.t. S leaving chunk r
 };
 bool chunk_bwd_supported(int dk, int dv, int rule, int gate, int dtype);
 size_t chunk_bwd_ops_bytes(int dk, int dtype);

@@ -219,8 +219,9 @@ linattn_status validate_train(const linattn_chunk_args* a, ChunkProblem* p)
 }
 
 // Backward workspace, 256-byte aligned pieces: chunk operands [B,H,N] blocks,
-// exp(G_C) [B,H,N], dstates [B,H,N,dk,dv] fp32, then (states not given) the
-// recomputed states [B,H,N,dk,dv] fp32 and a forward output [B,H,T,dv].
+// exp(G_C) [B,H,N], dstates [B,H,N,dk,dv], then (states not given) the
+// recomputed states [B,H,N,dk,dv] and a forward output [B,H,T,dv], all in the
+// token type except exp(G_C).
 struct BwdLayout {
     size_t ops, gc, dst, st, o, total;
 };
@@ -233,8 +234,8 @@ BwdLayout bwd_layout(const ChunkProblem& p, bool states_given)
     l.ops = 0;
     l.gc = up(bh * nch * chunk_bwd_ops_bytes(p.dk, p.dtype));
     l.dst = l.gc + up(bh * nch * 4);
-    l.st = l.dst + up(bh * nch * p.dk * p.dv * 4);
-    l.o = l.st + (states_given ? 0 : up(bh * nch * p.dk * p.dv * 4));
+    l.st = l.dst + up(bh * nch * p.dk * p.dv * esz);
+    l.o = l.st + (states_given ? 0 : up(bh * nch * p.dk * p.dv * esz));
     l.total = l.o + (states_given ? 0 : up(bh * (size_t)p.T * p.dv * esz));
     return l;
 }
@@ -429,7 +430,7 @@ extern "C" {
 
 linattn_status linattn_chunk_fwd_save(const linattn_chunk_args* a, const void* q, const void* k,
                                       const void* v, const void* g, const void* beta, const float* s0,
-                                      void* o, float* s_final, float* states, void* stream)
+                                      void* o, float* s_final, void* states, void* stream)
 {
     ChunkProblem p{};
     linattn_status st = validate_train(a, &p);
@@ -457,7 +458,7 @@ size_t linattn_chunk_bwd_workspace_bytes(const linattn_chunk_args* a, int states
 }
 
 linattn_status linattn_chunk_bwd(const linattn_chunk_args* a, const void* q, const void* k, const void* v,
-                                 const void* g, const void* beta, const float* s0, const float* states,
+                                 const void* g, const void* beta, const float* s0, const void* states,
                                  const void* dout, const float* dsT, void* dq, void* dk, void* dv, void* dg,
                                  void* dbeta, float* ds0, void* workspace, size_t workspace_bytes,
                                  void* stream)
@@ -488,20 +489,19 @@ linattn_status linattn_chunk_bwd(const linattn_chunk_args* a, const void* q, con
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const float* sts = states;
+    const void* sts = states;
     if (p.T > 0 && !given) {
         ChunkProblem fp = p;
         fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta;
         fp.s0 = s0; fp.o = ws + l.o; fp.s_final = nullptr;
-        float* rec = reinterpret_cast<float*>(ws + l.st);
-        if (launch_chunk_fused_save(fp, rec, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
-        sts = rec;
+        if (launch_chunk_fused_save(fp, ws + l.st, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+        sts = ws + l.st;
     }
     ChunkBwdProblem b{p.B, p.H, p.T, p.dk, p.dv, p.rule, p.gate, p.dtype,
                       q, k, v, g, beta, dout, sts, dsT, dq, dk, dv, dg, dbeta, ds0,
                       p.T > 0 ? ws + l.ops : nullptr,
                       p.T > 0 ? reinterpret_cast<float*>(ws + l.gc) : nullptr,
-                      p.T > 0 ? reinterpret_cast<float*>(ws + l.dst) : nullptr};
+                      p.T > 0 ? ws + l.dst : nullptr};
     return launch_chunk_bwd(b, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
 }
 

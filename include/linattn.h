@@ -230,8 +230,11 @@ linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args *a,
  * chunkwise form autograd keeps one boundary state per chunk instead of one
  * state per token).  Same arguments and results as
  * linattn_chunk_fwd, plus
- *   states   [B,H,N,dk,dv] fp32, N = ceil(T / 64): states[b,h,r] is the state
- *            before chunk r (states[b,h,0] = s0, or zero); caller-owned.
+ *   states   [B,H,N,dk,dv] in the token dtype, N = ceil(T / 64):
+ *            states[b,h,r] is the state before chunk r (states[b,h,0] = s0,
+ *            or zero), rounded once from the fp32 state the forward carries
+ *            (the backward uses it as matrix-core operands of that dtype);
+ *            caller-owned.
  * Supported: gate NONE or SCALAR, chunk 64, bf16 tokens with dk, dv in
  * {64, 128}, fp32 tokens with dk = 64 (LINATTN_ERR_UNSUPPORTED otherwise);
  * the same 2 GiB limit.  No workspace.
@@ -240,7 +243,7 @@ linattn_status linattn_chunk_fwd_save(const linattn_chunk_args *a,
                                       const void *q, const void *k, const void *v,
                                       const void *g, const void *beta,
                                       const float *s0, void *o, float *s_final,
-                                      float *states, void *stream);
+                                      void *states, void *stream);
 
 /*
  * Device workspace, in bytes, of linattn_chunk_bwd: the per-chunk operands of
@@ -263,7 +266,7 @@ size_t linattn_chunk_bwd_workspace_bytes(const linattn_chunk_args *a, int states
  * the gradient of its outgoing state.
  *
  *   q, k, v, g, beta, s0: the forward's inputs (as linattn_chunk_fwd)
- *   states   [B,H,N,dk,dv] fp32 from linattn_chunk_fwd_save, or NULL to
+ *   states   [B,H,N,dk,dv] from linattn_chunk_fwd_save, or NULL to
  *            recompute them (then s0 is read; with states given it is not)
  *   dout     [B,H,T,dv] token dtype
  *   dsT      [B,H,dk,dv] fp32, or NULL for zero
@@ -281,7 +284,7 @@ size_t linattn_chunk_bwd_workspace_bytes(const linattn_chunk_args *a, int states
 linattn_status linattn_chunk_bwd(const linattn_chunk_args *a,
                                  const void *q, const void *k, const void *v,
                                  const void *g, const void *beta, const float *s0,
-                                 const float *states, const void *dout, const float *dsT,
+                                 const void *states, const void *dout, const float *dsT,
                                  void *dq, void *dk, void *dv, void *dg, void *dbeta,
                                  float *ds0, void *workspace, size_t workspace_bytes,
                                  void *stream);

@@ -106,7 +106,7 @@ def test_saved_states_equal_recomputed():
                                      dev_state(x["s0"]), rule=case.rule, gate=case.gate)
     torch.cuda.synchronize()
     st = host(states)
-    assert np.array_equal(st[:, :, 0], x["s0"].astype(np.float64))
+    assert np.array_equal(st[:, :, 0], syn.to_dtype(x["s0"], case.dtype).astype(np.float64))
     for r in (1, 3, 5):
         cut = 64 * r
         sub = {k2: (None if v2 is None else np.ascontiguousarray(v2[:, :, :cut])) for k2, v2 in x.items()
