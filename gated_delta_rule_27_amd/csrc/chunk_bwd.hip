@@ -403,45 +403,56 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) dsr[(16 * db + rr) * DV] = from_f32<T>(dS[db][rr]);
             // ---- phase 1: dZ = A^T dO + ->K dS ; dR = Tb^T dZ ----
+            // every product as K = 32 pairs of K = 16 steps; the blocks of A^T and
+            // Tb^T left of the diagonal are zero, so the full range is exact
             floatx4 X[4], dR[4];
+            F16<T> dof[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) dof[mb] = frag_xk(dOT[buf], LDC, n0, 16 * mb, ln);
 #pragma unroll
             for (int li = 0; li < 4; ++li) {
                 floatx4 acc = zero4();
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    if (mb >= li)
-                        acc = mma16<T>(frag_xk(AqT, LDC, 16 * li, 16 * mb, ln),
-                                       frag_xk(dOT[buf], LDC, n0, 16 * mb, ln), acc);
+                for (int mb = 0; mb < 4; mb += 2)
+                    acc = mma16x2<T>(frag_xk(AqT, LDC, 16 * li, 16 * mb, ln), frag_xk(AqT, LDC, 16 * li, 16 * mb + 16, ln),
+                                     dof[mb], dof[mb + 1], acc);
 #pragma unroll
-                for (int db = 0; db < ND; ++db)
-                    acc = mma16<T>(frag_xk(Kr, LDQ, 16 * li, 16 * db, ln), frag16_acc<T>(dS[db]), acc);
+                for (int db = 0; db < ND; db += 2)
+                    acc = mma16x2<T>(frag_xk(Kr, LDQ, 16 * li, 16 * db, ln), frag_xk(Kr, LDQ, 16 * li, 16 * db + 16, ln),
+                                     frag16_acc<T>(dS[db]), frag16_acc<T>(dS[db + 1]), acc);
                 X[li] = acc;
             }
             if constexpr (DELTA) {
+                const F16<T> x0 = frag16_acc<T>(X[0]), x1 = frag16_acc<T>(X[1]), x2 = frag16_acc<T>(X[2]),
+                             x3 = frag16_acc<T>(X[3]);
 #pragma unroll
                 for (int li = 0; li < 4; ++li) {
-                    floatx4 acc = zero4();
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        if (mb >= li)
-                            acc = mma16<T>(frag_xk(TbT, LDC, 16 * li, 16 * mb, ln), frag16_acc<T>(X[mb]), acc);
-                    dR[li] = acc;
+                    floatx4 acc = mma16x2<T>(frag_xk(TbT, LDC, 16 * li, 0, ln), frag_xk(TbT, LDC, 16 * li, 16, ln),
+                                             x0, x1, zero4());
+                    dR[li] = mma16x2<T>(frag_xk(TbT, LDC, 16 * li, 32, ln), frag_xk(TbT, LDC, 16 * li, 48, ln),
+                                        x2, x3, acc);
                 }
             }
             lds_barrier();
             // ---- phase 2: dS = exp(G_C) dS + <-Q^T dO - <-K^T dR ----
             const float gc = gCs[buf];
+            F16<T> drf[4];
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) drf[mb] = frag16_acc<T>(dR[mb]);
+            }
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
                 floatx4 acc = dS[db] * gc;
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc = mma16<T>(frag_xk(QdT, LDC, 16 * db, 16 * mb, ln), frag_xk(dOT[buf], LDC, n0, 16 * mb, ln),
-                                   acc);
+                for (int mb = 0; mb < 4; mb += 2)
+                    acc = mma16x2<T>(frag_xk(QdT, LDC, 16 * db, 16 * mb, ln), frag_xk(QdT, LDC, 16 * db, 16 * mb + 16, ln),
+                                     dof[mb], dof[mb + 1], acc);
                 if constexpr (DELTA) {
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        acc = mma16<T>(frag_xk(NKdT, LDC, 16 * db, 16 * mb, ln), frag16_acc<T>(dR[mb]), acc);
+                    for (int mb = 0; mb < 4; mb += 2)
+                        acc = mma16x2<T>(frag_xk(NKdT, LDC, 16 * db, 16 * mb, ln),
+                                         frag_xk(NKdT, LDC, 16 * db, 16 * mb + 16, ln), drf[mb], drf[mb + 1], acc);
                 }
                 dS[db] = acc;
             }
@@ -472,8 +483,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             }
 #pragma unroll
             for (int p = 0; p < NO; ++p) {
-                const int e = (p * NH + ht) * E;
-                const int row = e / 64, cc = e % 64;
+                const int e = p * NH + ht;                 // lane-consecutive rows
+                const int row = e % kC, cc = (e / kC) * E;
                 const int64_t t = c * kC + row;
                 ro[p] = i4{0, 0, 0, 0};
                 if (t < Tlen) ro[p] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t) * DV + vb * 64 + cc);
@@ -495,8 +506,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             }
 #pragma unroll
             for (int p = 0; p < NO; ++p) {
-                const int e = (p * NH + ht) * E;
-                const int row = e / 64, cc = e % 64;
+                const int e = p * NH + ht;
+                const int row = e % kC, cc = (e / kC) * E;
                 T x[E];
                 __builtin_memcpy(x, &ro[p], 16);
 #pragma unroll
@@ -993,11 +1004,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
 #pragma unroll
         for (int u = 0; u < NKV; ++u) {
             const int i = tid + u * kNT, row = i / (DK / E), c = (i % (DK / E)) * E;
+            // q: lane-consecutive rows (its transposed copy is written from these)
+            const int qrow = i % kC, qc = (i / kC) * E;
             rk[u] = rq[u] = i4{0, 0, 0, 0};
-            if (row < tvalid) {
-                rk[u] = *reinterpret_cast<const i4*>(k + (bh * Tlen + t0 + row) * DK + c);
-                rq[u] = *reinterpret_cast<const i4*>(q + (bh * Tlen + t0 + row) * DK + c);
-            }
+            if (row < tvalid) rk[u] = *reinterpret_cast<const i4*>(k + (bh * Tlen + t0 + row) * DK + c);
+            if (qrow < tvalid) rq[u] = *reinterpret_cast<const i4*>(q + (bh * Tlen + t0 + qrow) * DK + qc);
         }
         ra = *reinterpret_cast<const i4*>(base + C::O_AQT + tid * E);
         if constexpr (DELTA) {
@@ -1034,10 +1045,12 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
     constexpr int VR = J / E, NVJ = (kC * VR + kNT - 1) / kNT;
     constexpr int SR = J / E, NSJ = (DK * SR + kNT - 1) / kNT;
     i4 pdo[NVJ], pv[NVJ], ps[NSJ], pds[NSJ];
+    // lane i holds row i % rows of its vector: the transposed copies written from
+    // these registers then go to consecutive LDS addresses
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < NVJ; ++u) {
-            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            const int i = tid + u * kNT, row = i % kC, c = (i / kC) * E;
             pdo[u] = pv[u] = i4{0, 0, 0, 0};
             if (i < kC * VR && row < tvalid) {
                 pdo[u] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t0 + row) * DV + j0 + c);
@@ -1046,7 +1059,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
         }
 #pragma unroll
         for (int u = 0; u < NSJ; ++u) {
-            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * E;
+            const int i = tid + u * kNT, row = i % DK, c = (i / DK) * E;
             ps[u] = pds[u] = i4{0, 0, 0, 0};
             if (i < DK * SR) {
                 ps[u] = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
@@ -1066,7 +1079,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
         __syncthreads();       // the previous block's arrays are free (and the prologue's LDS is written)
 #pragma unroll
         for (int u = 0; u < NVJ; ++u) {
-            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            const int i = tid + u * kNT, row = i % kC, c = (i / kC) * E;
             if (i < kC * VR) {
                 *reinterpret_cast<i4*>(dOs + row * LDJ + c) = pdo[u];
                 *reinterpret_cast<i4*>(Zs + row * LDJ + c) = pv[u];
@@ -1078,7 +1091,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
         }
 #pragma unroll
         for (int u = 0; u < NSJ; ++u) {
-            const int i = tid + u * kNT, row = i / SR, c = (i % SR) * E;
+            const int i = tid + u * kNT, row = i % DK, c = (i / DK) * E;
             if (i < DK * SR) {
                 T a[E], b[E];
                 __builtin_memcpy(a, &ps[u], 16);
@@ -1099,8 +1112,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
         {
             const int lb = wave >> 1, jc = wave & 1;
             const floatx4 a1 = tilek<T, true, true, kC>(zero4(), AqT, LDC, 16 * lb, dOT, LDC, 16 * jc, 0, lane);
-            floatx4 a2 = tilek<T, true, true, 64>(zero4(), Ks, LDQ, 16 * lb, dSnT, LDQ, 16 * jc, 0, lane);
-            if constexpr (DK > 64) a2 = tilek<T, true, true, 64>(a2, Ks, LDQ, 16 * lb, dSnT, LDQ, 16 * jc, 64, lane);
+            // K dS and K S_r share their K fragments
+            floatx4 a2 = zero4(), ks = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32) {
+                const F16<T> a0 = frag_xk(Ks, LDQ, 16 * lb, k0, lane), a1f = frag_xk(Ks, LDQ, 16 * lb, k0 + 16, lane);
+                a2 = mma16x2<T>(a0, a1f, frag_xk(dSnT, LDQ, 16 * jc, k0, lane),
+                                frag_xk(dSnT, LDQ, 16 * jc, k0 + 16, lane), a2);
+                if constexpr (DELTA)
+                    ks = mma16x2<T>(a0, a1f, frag_xk(ST, LDQ, 16 * jc, k0, lane),
+                                    frag_xk(ST, LDQ, 16 * jc, k0 + 16, lane), ks);
+            }
             floatx4 dz;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -1110,8 +1132,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
             put(dZs, LDJ, 16 * lb, 16 * jc, dz, lane);
             put_t(dZT, LDC, 16 * lb, 16 * jc, dz, lane);
             if constexpr (DELTA) {
-                floatx4 ks = tilek<T, true, true, 64>(zero4(), Ks, LDQ, 16 * lb, ST, LDQ, 16 * jc, 0, lane);
-                if constexpr (DK > 64) ks = tilek<T, true, true, 64>(ks, Ks, LDQ, 16 * lb, ST, LDQ, 16 * jc, 64, lane);
                 floatx4 rv;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -1207,14 +1227,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
     {
         // K^T from LDS, Q^T from the registers loaded in the prologue
         for (int i = tid; i < kC * DK / 4; i += kNT) {
-            const int m = i / (DK / 4), c = (i % (DK / 4)) * 4;
+            const int m = i % kC, c = (i / kC) * 4;
             const bf16x4 x = *reinterpret_cast<const bf16x4*>(Ks + m * LDQ + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) KT[(c + e) * LDC + m] = x[e];
         }
 #pragma unroll
         for (int u = 0; u < NKV; ++u) {
-            const int i = tid + u * kNT, row = i / (DK / E), c = (i % (DK / E)) * E;
+            const int i = tid + u * kNT, row = i % kC, c = (i / kC) * E;
             T x[E];
             __builtin_memcpy(x, &rq[u], 16);
 #pragma unroll
