@@ -29,8 +29,8 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_27_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources each measured kernel is built from: counter figures in profiles/
 # are valid only while these hash to the value recorded with them
-CHUNK_SOURCES = ("chunk_pipe.hip", "mfma.h", "tsolve.h", "device_common.h", "launch.h")
-DECODE_SOURCES = ("decode_step.hip", "device_common.h", "launch.h")
+CHUNK_SOURCES = ("chunk_pipe.hip", "mfma.h", "tsolve.h", "device_common.h", "prep.h")
+DECODE_SOURCES = ("decode_step.hip", "device_common.h")
 CHUNK_PROFILE = "chunk_pipe_gdn_B8_H16_T8192_d128.md"
 DECODE_PROFILE = "decode_step_gdn_N256_H32_d128.md"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
