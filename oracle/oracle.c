@@ -43,8 +43,9 @@
  * No query scaling, no normaliser: neither appears in the read-out on [LAV].
  *
  * oracle_recurrence_bwd differentiates the same recurrence in reverse (the
- * gradients of a training step); oracle_deltaproduct and oracle_normalized are
- * the Gated DeltaProduct and normalised variants, each described where defined.
+ * gradients of a training step); oracle_deltaproduct (and its backward) and
+ * oracle_normalized are the Gated DeltaProduct and normalised variants, each
+ * described where defined.
  *
  * Arithmetic: IEEE fp64, plain loops, fixed order per head.  OpenMP
  * parallelises over independent (b, h) pairs only, so the result does not
@@ -491,6 +492,162 @@ int oracle_recurrence_bwd(int64_t B, int64_t H, int64_t T, int dk, int dv, int r
         }
         if (ds0) memcpy(ds0 + (size_t)bh * ss, Hg, ss * sizeof(double));
         free(ck); free(Sd); free(Hg); free(St); free(u); free(vh); free(du); free(ot);
+    }
+    return failed ? 6 : 0;
+}
+
+/*
+ * Backward pass of Gated DeltaProduct (oracle_deltaproduct above): the
+ * gradients of sum(dout . o) + sum(dsT . S_T) with respect to q, k, v, g,
+ * beta and s0.  Per token, newest first: the read-out adds q_t^T dout_t to the
+ * running gradient H and gives dq_t = dout_t S_t^T; the substeps are undone
+ * last first, each exactly as the delta step in oracle_recurrence_bwd (without
+ * a decay of its own); then the token's decay, a_t = exp(g_t) applied once
+ * before the first substep, gives dg_t = <H, a_t S_{t-1}> and H <- a_t H.
+ * States are recomputed per segment of SEG tokens from checkpoints, and each
+ * token's substep states from the state before the token.  Layouts as
+ * oracle_deltaproduct; dq [B,H,T,dk], dk [B,H,T,nh,dk], dv [B,H,T,nh,dv],
+ * dg [B,H,T] or NULL (no gate), dbeta [B,H,T,nh], ds0 [B,H,dk,dv] or NULL.
+ */
+int oracle_deltaproduct_bwd(int64_t B, int64_t H, int64_t T, int nh, int dk, int dv, int gate,
+                            const double *q, const double *k, const double *v,
+                            const double *g, const double *beta, const double *s0,
+                            const double *dout, const double *dsT,
+                            double *dq, double *dk_out, double *dv_out, double *dg,
+                            double *dbeta, double *ds0, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || nh <= 0 || dk <= 0 || dv <= 0) return 2;
+    if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_SCALAR) return 3;
+    if (B * H * T > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk_out || !dv_out || !dbeta)) return 1;
+    if (gate == ORACLE_GATE_SCALAR && B * H * T > 0 && (!g || !dg)) return 1;
+    int64_t nheads = B * H;
+    size_t ss = (size_t)dk * dv;
+    int64_t nseg = (T + ORACLE_BWD_SEG - 1) / ORACLE_BWD_SEG;
+    int64_t bh;
+    int failed = 0;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : failed)
+#else
+    (void)nthreads;
+#endif
+    for (bh = 0; bh < nheads; ++bh) {
+        /* checkpoints, the state before each token of a segment, the substep
+         * states of one token, the running gradient, small vectors */
+        double *ck = (double *)malloc((size_t)(nseg + 1) * ss * sizeof(double));
+        double *Sp = (double *)malloc((size_t)ORACLE_BWD_SEG * ss * sizeof(double));
+        double *Sj = (double *)malloc((size_t)(nh + 1) * ss * sizeof(double));
+        double *Hg = (double *)malloc(ss * sizeof(double));
+        double *St = (double *)malloc(ss * sizeof(double));
+        double *w = (double *)malloc((size_t)dv * sizeof(double));
+        double *vh = (double *)malloc((size_t)dv * sizeof(double));
+        double *du = (double *)malloc((size_t)dv * sizeof(double));
+        if (!ck || !Sp || !Sj || !Hg || !St || !w || !vh || !du) {
+            free(ck); free(Sp); free(Sj); free(Hg); free(St); free(w); free(vh); free(du);
+            failed |= 1;
+            continue;
+        }
+        int64_t t, sg;
+        int i, j, c;
+        /* one token forward from St (in place), keeping its substep states in Sj:
+         * Sj[0] = a S_{t-1}, Sj[j+1] after substep j */
+#define GDP_TOKEN_FWD(tok_)                                                                    \
+        do {                                                                                   \
+            double a_ = gate == ORACLE_GATE_SCALAR ? exp(g[tok_]) : 1.0;                      \
+            for (i = 0; i < dk * dv; ++i) Sj[i] = a_ * St[i];                                  \
+            for (j = 0; nh > j; ++j) {                                                         \
+                const double *kj = k + ((tok_) * nh + j) * dk;                                 \
+                const double *vj = v + ((tok_) * nh + j) * dv;                                 \
+                double bj = beta[(tok_) * nh + j];                                             \
+                const double *Sa = Sj + (size_t)j * ss;                                        \
+                double *Sb = Sj + (size_t)(j + 1) * ss;                                        \
+                for (c = 0; c < dv; ++c) {                                                     \
+                    double p_ = 0.0;                                                           \
+                    for (i = 0; i < dk; ++i) p_ += kj[i] * Sa[(size_t)i * dv + c];             \
+                    w[c] = bj * (vj[c] - p_);                                                  \
+                }                                                                              \
+                for (i = 0; i < dk; ++i)                                                       \
+                    for (c = 0; c < dv; ++c) Sb[(size_t)i * dv + c] = Sa[(size_t)i * dv + c] + kj[i] * w[c]; \
+            }                                                                                  \
+            memcpy(St, Sj + (size_t)nh * ss, ss * sizeof(double));                              \
+        } while (0)
+        if (NULL != s0) memcpy(St, s0 + (size_t)bh * ss, ss * sizeof(double));
+        else memset(St, 0, ss * sizeof(double));
+        for (t = 0; t < T; ++t) {
+            size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+            if (t % ORACLE_BWD_SEG == 0) memcpy(ck + (size_t)(t / ORACLE_BWD_SEG) * ss, St, ss * sizeof(double));
+            GDP_TOKEN_FWD(tok);
+        }
+        if (dsT != NULL) memcpy(Hg, dsT + (size_t)bh * ss, ss * sizeof(double));
+        else memset(Hg, 0, ss * sizeof(double));
+        for (sg = nseg - 1; sg >= 0; --sg) {
+            int64_t ta = sg * ORACLE_BWD_SEG;
+            int64_t tb = ta + ORACLE_BWD_SEG < T ? ta + ORACLE_BWD_SEG : T;
+            memcpy(St, ck + (size_t)sg * ss, ss * sizeof(double));
+            for (t = ta; t < tb; ++t) {
+                size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+                memcpy(Sp + (size_t)(t - ta) * ss, St, ss * sizeof(double));
+                GDP_TOKEN_FWD(tok);
+            }
+            for (t = tb - 1; t >= ta; --t) {
+                size_t tok = (size_t)bh * (size_t)T + (size_t)t;
+                memcpy(St, Sp + (size_t)(t - ta) * ss, ss * sizeof(double));
+                GDP_TOKEN_FWD(tok);                   /* Sj now holds this token's states */
+                const double *qt = q + tok * dk, *dot = dout + tok * dv;
+                const double *Sl = Sj + (size_t)nh * ss;
+                for (i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (c = 0; c < dv; ++c) acc += dot[c] * Sl[(size_t)i * dv + c];
+                    dq[tok * dk + i] = acc;
+                }
+                for (i = 0; i < dk; ++i)
+                    for (c = 0; c < dv; ++c) Hg[(size_t)i * dv + c] += qt[i] * dot[c];
+                for (j = nh - 1; j >= 0; --j) {
+                    const double *kj = k + (j + tok * nh) * dk;
+                    const double *vj = v + (j + tok * nh) * dv;
+                    double bj = beta[j + tok * nh];
+                    const double *Sa = Sj + (size_t)j * ss;
+                    double *dkj = dk_out + (tok * nh + j) * dk;
+                    for (c = 0; c < dv; ++c) {
+                        double p_ = 0.0, d_ = 0.0;
+                        for (i = 0; i < dk; ++i) {
+                            p_ += kj[i] * Sa[(size_t)i * dv + c];
+                            d_ += kj[i] * Hg[(size_t)i * dv + c];
+                        }
+                        vh[c] = p_;
+                        w[c] = bj * (vj[c] - p_);
+                        du[c] = d_;
+                    }
+                    /* write S_{j+1} = S_j + k^T w */
+                    for (i = 0; i < dk; ++i) {
+                        double acc = 0.0;
+                        for (c = 0; c < dv; ++c) acc += Hg[(size_t)i * dv + c] * w[c];
+                        dkj[i] = acc;
+                    }
+                    double db = 0.0;
+                    for (c = 0; c < dv; ++c) db += du[c] * (vj[c] - vh[c]);
+                    dbeta[tok * nh + j] = db;
+                    for (c = 0; c < dv; ++c) dv_out[(tok * nh + j) * dv + c] = bj * du[c];
+                    /* the prediction k S_j, into k and into S_j */
+                    for (i = 0; i < dk; ++i) {
+                        double acc = 0.0;
+                        for (c = 0; c < dv; ++c) acc += Sa[(size_t)i * dv + c] * (-bj * du[c]);
+                        dkj[i] += acc;
+                    }
+                    for (i = 0; i < dk; ++i)
+                        for (c = 0; c < dv; ++c) Hg[(size_t)i * dv + c] -= kj[i] * bj * du[c];
+                }
+                if (gate == ORACLE_GATE_SCALAR) {
+                    double acc = 0.0, a = exp(g[tok]);
+                    for (i = 0; i < dk * dv; ++i) acc += Hg[i] * Sj[i];
+                    dg[tok] = acc;
+                    for (i = 0; i < dk * dv; ++i) Hg[i] = a * Hg[i];
+                }
+            }
+        }
+#undef GDP_TOKEN_FWD
+        if (ds0) memcpy(ds0 + (size_t)bh * ss, Hg, ss * sizeof(double));
+        free(ck); free(Sp); free(Sj); free(Hg); free(St); free(w); free(vh); free(du);
     }
     return failed ? 6 : 0;
 }

@@ -81,6 +81,9 @@ class OracleLib:
         lib.oracle_recurrence_bwd.argtypes = [i64, i64, i64, i32, i32, i32, i32,
                                               d, d, d, d, d, d, d, d, d, d, d, d, d, d, i32]
         lib.oracle_recurrence_bwd.restype = i32
+        lib.oracle_deltaproduct_bwd.argtypes = [i64, i64, i64, i32, i32, i32, i32,
+                                                d, d, d, d, d, d, d, d, d, d, d, d, d, d, i32]
+        lib.oracle_deltaproduct_bwd.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         self.lib = lib
@@ -177,6 +180,44 @@ def _deltaproduct(self, q, k, v, g=None, beta=None, s0=None, *, gate="scalar", n
 
 
 OracleLib.deltaproduct = _deltaproduct
+
+
+def _deltaproduct_bwd(self, q, k, v, g=None, beta=None, s0=None, do=None, dsT=None, *, gate="scalar",
+                      nthreads: int = 0):
+    """fp64 gradients of the Gated DeltaProduct recurrence for the loss
+    sum(do * o) + sum(dsT * S_T).  Shapes as ``deltaproduct``; do [B,H,T,dv].
+    Returns dq [B,H,T,dk], dk [B,H,T,nh,dk], dv [B,H,T,nh,dv], dg [B,H,T] (None
+    without a gate), dbeta [B,H,T,nh], ds0 [B,H,dk,dv]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g, beta, s0, do, dsT = _f64(g), _f64(beta), _f64(s0), _f64(do), _f64(dsT)
+    B, H, T, dk = q.shape
+    nh, dv = k.shape[3], v.shape[-1]
+    if k.shape != (B, H, T, nh, dk) or v.shape != (B, H, T, nh, dv):
+        raise ValueError("k/v must be [B,H,T,nh,d]")
+    if beta is None or beta.shape != (B, H, T, nh):
+        raise ValueError("beta must be [B,H,T,nh]")
+    if do is None or do.shape != (B, H, T, dv):
+        raise ValueError("do must be [B,H,T,dv]")
+    if gate == "scalar" and (g is None or g.shape != (B, H, T)):
+        raise ValueError("scalar gate needs g of shape [B,H,T]")
+    if gate not in ("none", "scalar"):
+        raise ValueError("Gated DeltaProduct takes no gate or a scalar gate")
+    if gate == "none":
+        g = None
+    out = {"dq": np.empty((B, H, T, dk)), "dk": np.empty((B, H, T, nh, dk)),
+           "dv": np.empty((B, H, T, nh, dv)), "dbeta": np.empty((B, H, T, nh)),
+           "dg": None if g is None else np.empty((B, H, T)), "ds0": np.empty((B, H, dk, dv))}
+    rc = self.lib.oracle_deltaproduct_bwd(B, H, T, nh, dk, dv, GATES[gate], _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(g), _ptr(beta), _ptr(s0), _ptr(do), _ptr(dsT),
+                                          _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                          _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]),
+                                          int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_deltaproduct_bwd failed with code {rc}")
+    return out
+
+
+OracleLib.deltaproduct_bwd = _deltaproduct_bwd
 
 
 def _recurrence_bwd(self, q, k, v, g=None, beta=None, s0=None, do=None, dsT=None, *, rule="delta",
@@ -322,6 +363,11 @@ def decode_step(*args, **kw):
 def deltaproduct(*args, **kw):
     """See :meth:`OracleLib.deltaproduct`."""
     return default().deltaproduct(*args, **kw)
+
+
+def deltaproduct_bwd(*args, **kw):
+    """See :meth:`OracleLib.deltaproduct_bwd`."""
+    return default().deltaproduct_bwd(*args, **kw)
 
 
 def recurrence_bwd(*args, **kw):

@@ -663,6 +663,87 @@ def pin_bwd_autograd_one_chunk(orc):
                     f"{gname} vs autograd of the one-chunk form ({rule}/{gate})"
 
 
+# ---------------------------------------------------------------------------
+# V19  the Gated DeltaProduct backward against central differences of the
+#      pinned GDP forward: every entry on tiny cases, n_h in {1, 2, 3}, gate
+#      none and scalar; directional derivatives over 70 tokens (two replay
+#      segments).  ([LAV] "Gated Delta Product (GDP)")
+# ---------------------------------------------------------------------------
+def _gdp_bwd_case(rng, T, nh, dk, dv, gate):
+    q = rng.standard_normal((1, 1, T, dk))
+    k = rng.standard_normal((1, 1, T, nh, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((1, 1, T, nh, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((1, 1, T, nh))))
+    g = -_softplus(rng.standard_normal((1, 1, T))) * 0.5 if gate == "scalar" else None
+    s0 = rng.standard_normal((1, 1, dk, dv)) * 0.5
+    do = rng.standard_normal((1, 1, T, dv))
+    dsT = rng.standard_normal((1, 1, dk, dv))
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "s0": s0}, do, dsT
+
+
+def _gdp_loss(orc, x, do, dsT, gate):
+    o, S = orc.deltaproduct(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], gate=gate)
+    return float(np.sum(o * do) + np.sum(S * dsT))
+
+
+def pin_deltaproduct_bwd_finite_differences(orc):
+    rng = np.random.default_rng(119)
+    eps = 1e-6
+    for nh in (1, 2, 3):
+        for gate in ("none", "scalar"):
+            x, do, dsT = _gdp_bwd_case(rng, 5, nh, 3, 2, gate)
+            gr = orc.deltaproduct_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT, gate=gate)
+            for name, gname in BWD_NAMES:
+                if x[name] is None:
+                    assert gr[gname] is None
+                    continue
+                fd = np.zeros_like(x[name])
+                for idx in np.ndindex(x[name].shape):
+                    xp = dict(x); xp[name] = x[name].copy(); xp[name][idx] += eps
+                    xm = dict(x); xm[name] = x[name].copy(); xm[name][idx] -= eps
+                    fd[idx] = (_gdp_loss(orc, xp, do, dsT, gate) - _gdp_loss(orc, xm, do, dsT, gate)) / (2 * eps)
+                err = np.max(np.abs(gr[gname] - fd)) / max(1.0, np.max(np.abs(fd)))
+                assert err < 1e-7, f"GDP {gname} vs central differences (nh={nh}, {gate}): {err:.2e}"
+    x, do, dsT = _gdp_bwd_case(rng, 70, 2, 4, 3, "scalar")
+    gr = orc.deltaproduct_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT, gate="scalar")
+    for _ in range(3):
+        dirs = {n: rng.standard_normal(a.shape) for n, a in x.items()}
+        xp = {n: a + eps * dirs[n] for n, a in x.items()}
+        xm = {n: a - eps * dirs[n] for n, a in x.items()}
+        fd = (_gdp_loss(orc, xp, do, dsT, "scalar") - _gdp_loss(orc, xm, do, dsT, "scalar")) / (2 * eps)
+        an = sum(float(np.sum(gr[gn] * dirs[n])) for n, gn in BWD_NAMES)
+        assert abs(an - fd) < 1e-6 * max(1.0, abs(fd)), f"GDP directional derivative: {an} vs {fd}"
+
+
+# ---------------------------------------------------------------------------
+# V20  the Gated DeltaProduct backward equals the Gated DeltaNet backward over
+#      the virtual sequence of n_h T steps ([LAV] "GDP as GDN over a virtual
+#      sequence"): the query sits on the last substep and the gate on the first,
+#      so dq and dg are the virtual ones there; dk, dv, dbeta share the layout.
+# ---------------------------------------------------------------------------
+def pin_deltaproduct_bwd_virtual_sequence(orc):
+    rng = np.random.default_rng(120)
+    for nh, gate in ((1, "scalar"), (2, "scalar"), (3, "none")):
+        T, dk, dv = 23, 5, 4
+        x, do, dsT = _gdp_bwd_case(rng, T, nh, dk, dv, gate)
+        gr = orc.deltaproduct_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT, gate=gate)
+        Tv = T * nh
+        qv = np.zeros((1, 1, Tv, dk)); qv[0, 0, nh - 1::nh] = x["q"][0, 0]
+        dov = np.zeros((1, 1, Tv, dv)); dov[0, 0, nh - 1::nh] = do[0, 0]
+        gv = None
+        if gate == "scalar":
+            gv = np.zeros((1, 1, Tv)); gv[0, 0, 0::nh] = x["g"][0, 0]
+        ref = orc.recurrence_bwd(qv, x["k"].reshape(1, 1, Tv, dk), x["v"].reshape(1, 1, Tv, dv), gv,
+                                 x["beta"].reshape(1, 1, Tv), x["s0"], dov, dsT, rule="delta", gate=gate)
+        assert rel_err(gr["dq"][0, 0], ref["dq"][0, 0, nh - 1::nh]) < 1e-10, f"GDP dq (nh={nh})"
+        assert rel_err(gr["dk"].reshape(Tv, dk), ref["dk"][0, 0]) < 1e-10, f"GDP dk (nh={nh})"
+        assert rel_err(gr["dv"].reshape(Tv, dv), ref["dv"][0, 0]) < 1e-10, f"GDP dv (nh={nh})"
+        assert rel_err(gr["dbeta"].reshape(Tv), ref["dbeta"][0, 0]) < 1e-10, f"GDP dbeta (nh={nh})"
+        assert rel_err(gr["ds0"], ref["ds0"]) < 1e-10, f"GDP ds0 (nh={nh})"
+        if gate == "scalar":
+            assert rel_err(gr["dg"][0, 0], ref["dg"][0, 0, 0::nh]) < 1e-10, f"GDP dg (nh={nh})"
+
+
 PINS = [
     pin_add_equals_masked_quadratic,
     pin_decay_equals_gamma_form,
@@ -685,4 +766,6 @@ PINS = [
     pin_normalized_invariants,
     pin_bwd_finite_differences,
     pin_bwd_autograd_one_chunk,
+    pin_deltaproduct_bwd_finite_differences,
+    pin_deltaproduct_bwd_virtual_sequence,
 ]

@@ -71,6 +71,17 @@ MUTANTS = [
     ("bwd_channel_dg_reversed", [("dg[tok * dk + i] = acc;", "dg[tok * dk + (dk - 1 - i)] = acc;")]),
     ("bwd_ignore_initial_state", [("if (s0 == NULL) memset(St,", "if (1) memset(St,")]),
     ("bwd_ignore_final_state_grad", [("if (dsT) memcpy(Hg,", "if (0) memcpy(Hg,")]),
+    ("gdp_bwd_substeps_in_forward_order", [("for (j = nh - 1; j >= 0; --j) {", "for (j = 0; j < nh; ++j) {")]),
+    ("gdp_bwd_dbeta_value_only", [("db += du[c] * (vj[c] - vh[c]);", "db += du[c] * vj[c];")]),
+    ("gdp_bwd_no_prediction_into_state", [("Hg[(size_t)i * dv + c] -= kj[i] * bj * du[c];",
+                                           "Hg[(size_t)i * dv + c] -= 0.0 * kj[i] * bj * du[c];")]),
+    ("gdp_bwd_dg_with_token_end_state", [("for (i = 0; i < dk * dv; ++i) acc += Hg[i] * Sj[i];",
+                                          "for (i = 0; i < dk * dv; ++i) acc += Hg[i] * St[i];")]),
+    ("gdp_bwd_gate_not_passed_back", [("for (i = 0; i < dk * dv; ++i) Hg[i] = a * Hg[i];", "(void)a;")]),
+    ("gdp_bwd_ignore_final_state_grad", [("if (dsT != NULL) memcpy(Hg,", "if (0) memcpy(Hg,")]),
+    ("gdp_bwd_ignore_initial_state", [("if (NULL != s0) memcpy(St,", "if (0) memcpy(St,")]),
+    ("gdp_bwd_dq_from_first_substep", [("acc += dot[c] * Sl[(size_t)i * dv + c];",
+                                        "acc += dot[c] * Sj[(size_t)i * dv + c];")]),
     ("bwd_readout_grad_missing", [("Hg[(size_t)i * dv + j] += qt[i] * dot[j];", "Hg[(size_t)i * dv + j] += 0.0;")]),
 ]
 
