@@ -333,6 +333,42 @@ def time_backward(la, syn, case, dev, steps, warmup=2):
             "path": "fused+save; bwd_ops + bwd_chain + bwd_grad", "steps": steps}
 
 
+def time_deltaproduct_bwd(la, syn, case, dev, steps, warmup=2):
+    """Event-timed Gated DeltaProduct backward (GDN backward over the virtual
+    sequence, its states recomputed) at the shape and laws of ``case``."""
+    import torch
+    B, H, T, nh, dk, dv = case.B, case.H, case.T, case.nh, case.dk, case.dv
+    x = syn.deltaproduct_inputs_torch(case, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(syn.SEED * 1000 + 600)
+    do = torch.randn(B, H, T, dv, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    grads = {"dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
+             "dg": torch.empty_like(x["g"]), "dbeta": torch.empty_like(x["beta"]),
+             "ds0": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)}
+    ws = torch.empty(la.deltaproduct_bwd_workspace_bytes(B, H, T, nh, dk, dv, gate=case.gate, dtype=case.dtype),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        la.deltaproduct_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, gate=case.gate, workspace=ws,
+                            grads=grads)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": f"gated deltaproduct backward n_h={nh} B={B} H={H} T={T} dk={dk} dv={dv} bf16 "
+                        f"(states recomputed)",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "path": "expand + fused+save + bwd_ops + bwd_chain + bwd_grad over the virtual sequence + picks",
+            "steps": steps}
+
+
 def chunk_path(case, wsb):
     """Which chunk kernel the library runs for this case (its dispatch rule)."""
     if wsb:
@@ -359,9 +395,9 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm,cfg3bwd",
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm,cfg3bwd,gdp2bwd",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm, cfg3bwd), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm, cfg3bwd, gdp2bwd), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -439,6 +475,8 @@ def main():
             others.append(time_normalized(la, syn, syn.CFG2, dev, steps=10))
         elif name == "cfg3bwd":
             others.append(time_backward(la, syn, syn.CFG3, dev, steps=5))
+        elif name == "gdp2bwd":
+            others.append(time_deltaproduct_bwd(la, syn, syn.GDP2, dev, steps=5))
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
             others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))

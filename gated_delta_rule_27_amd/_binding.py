@@ -24,7 +24,8 @@ EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_worksp
            "linattn_chunk_fwd", "linattn_decode_step", "linattn_deltaproduct_workspace_bytes",
            "linattn_deltaproduct_fwd", "linattn_chunk_fwd_prep",
            "linattn_normalized_workspace_bytes", "linattn_chunk_fwd_normalized",
-           "linattn_chunk_fwd_save", "linattn_chunk_bwd_workspace_bytes", "linattn_chunk_bwd")
+           "linattn_chunk_fwd_save", "linattn_chunk_bwd_workspace_bytes", "linattn_chunk_bwd",
+           "linattn_deltaproduct_bwd_workspace_bytes", "linattn_deltaproduct_bwd")
 QK_MAPS = {"as_is": 0, "l2": 1, "elu1": 2}
 GATE_MAPS = {"as_is": 0, "neg_softplus": 1}
 BETA_MAPS = {"as_is": 0, "sigmoid": 1}
@@ -108,6 +109,11 @@ def load(path: str = LIB_PATH):
         lib.linattn_chunk_bwd.argtypes = [ctypes.POINTER(ChunkArgs), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.linattn_chunk_bwd.restype = ctypes.c_int
+        lib.linattn_deltaproduct_bwd_workspace_bytes.argtypes = [ctypes.POINTER(DeltaProductArgs)]
+        lib.linattn_deltaproduct_bwd_workspace_bytes.restype = sz
+        lib.linattn_deltaproduct_bwd.argtypes = [ctypes.POINTER(DeltaProductArgs), vp, vp, vp, vp, vp, vp, vp,
+                                                 vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.linattn_deltaproduct_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -478,4 +484,58 @@ def chunk_bwd(q, k, v, g, beta, dout, s0=None, dsT=None, *, states=None, rule="d
                                _ptr(workspace), ws_bytes, stream)
     if st != 0:
         raise LinattnError(st, "linattn_chunk_bwd")
+    return out
+
+
+def deltaproduct_bwd_workspace_bytes(B, H, T, nh, dk, dv, *, gate="scalar", dtype="bf16", chunk=64) -> int:
+    a = deltaproduct_args(B, H, T, nh, dk, dv, gate=gate, dtype=dtype, chunk=chunk)
+    return int(load().linattn_deltaproduct_bwd_workspace_bytes(ctypes.byref(a)))
+
+
+def deltaproduct_bwd(q, k, v, g, beta, dout, s0=None, dsT=None, *, gate="scalar", chunk=64, workspace=None,
+                     grads=None):
+    """Backward pass of deltaproduct_fwd on the GPU: gradients given dL/do
+    (dout [B,H,T,dv]) and dL/dS_T (dsT [B,H,dk,dv] fp32 or None).  Returns a
+    dict with dq [B,H,T,dk], dk [B,H,T,nh,dk], dv [B,H,T,nh,dv], dg [B,H,T] (None
+    without a gate), dbeta [B,H,T,nh] and ds0 (fp32)."""
+    import torch
+    lib = load()
+    B, H, T, dk = q.shape
+    nh, dv = k.shape[3], v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, nh, dk), dt, dev)
+    _check(v, "v", (B, H, T, nh, dv), dt, dev)
+    _check(beta, "beta", (B, H, T, nh), dt, dev)
+    _check(dout, "dout", (B, H, T, dv), dt, dev)
+    if gate == "scalar":
+        _check(g, "g", (B, H, T), dt, dev)
+    elif gate != "none" or g is not None:
+        raise ValueError("Gated DeltaProduct takes gate='scalar' with g, or gate='none'")
+    for t, name in ((s0, "s0"), (dsT, "dsT")):
+        if t is not None:
+            _check(t, name, (B, H, dk, dv), torch.float32, dev)
+    shapes = {"dq": ((B, H, T, dk), dt), "dk": ((B, H, T, nh, dk), dt), "dv": ((B, H, T, nh, dv), dt),
+              "dg": ((B, H, T), dt) if gate == "scalar" else None, "dbeta": ((B, H, T, nh), dt),
+              "ds0": ((B, H, dk, dv), torch.float32)}
+    out = dict(grads or {})
+    for name, spec in shapes.items():
+        if spec is None:
+            out[name] = None
+        elif out.get(name) is None:
+            out[name] = torch.empty(spec[0], dtype=spec[1], device=dev)
+        else:
+            _check(out[name], name, spec[0], spec[1], dev)
+    a = deltaproduct_args(B, H, T, nh, dk, dv, gate=gate, dtype=_token_dtype(q), chunk=chunk)
+    need = int(lib.linattn_deltaproduct_bwd_workspace_bytes(ctypes.byref(a)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.linattn_deltaproduct_bwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                                      _ptr(dout), _ptr(dsT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                      _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]), _ptr(workspace),
+                                      ws_bytes, stream)
+    if st != 0:
+        raise LinattnError(st, "linattn_deltaproduct_bwd")
     return out

@@ -47,6 +47,12 @@ struct DeltaProductProblem {
 };
 hipError_t launch_dp_expand(const DeltaProductProblem& p, hipStream_t stream);
 hipError_t launch_dp_gather(const DeltaProductProblem& p, hipStream_t stream);
+// backward: dO of the virtual outputs (do at every nh-th step, zero between),
+// and the pick of row j of every group of nh virtual rows (width w; w = 1 for
+// one value per row)
+hipError_t launch_dp_scatter(const DeltaProductProblem& p, const void* dout, void* dov, hipStream_t stream);
+hipError_t launch_dp_pick(const void* src, void* dst, int64_t rows, int nh, int j, int w, int dtype,
+                          hipStream_t stream);
 
 // Normalised linear attention as two add-rule passes (values, then a block of
 // ones started at z0): the block of ones and its initial state before them;

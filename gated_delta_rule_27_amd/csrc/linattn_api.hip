@@ -240,6 +240,29 @@ BwdLayout bwd_layout(const ChunkProblem& p, bool states_given)
     return l;
 }
 
+// Gated DeltaProduct backward workspace, 256-byte aligned pieces: expanded
+// queries and log-gates, the virtual dO, dq and dg, then the chunk backward's
+// own workspace for the virtual problem (its states recomputed).
+struct DpBwdLayout {
+    size_t qv, gv, dov, dqv, dgv, cws, total;
+};
+DpBwdLayout dp_bwd_layout(const linattn_chunk_args& va, const ChunkProblem& vp)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t esz = va.dtype == LINATTN_BF16 ? 2 : 4;
+    const size_t steps = (size_t)(va.B * va.H) * (size_t)va.T;
+    const bool gated = va.gate == LINATTN_GATE_SCALAR;
+    DpBwdLayout l{};
+    l.qv = 0;
+    l.gv = up(steps * va.dk * esz);
+    l.dov = l.gv + (gated ? up(steps * esz) : 0);
+    l.dqv = l.dov + up(steps * va.dv * esz);
+    l.dgv = l.dqv + up(steps * va.dk * esz);
+    l.cws = l.dgv + (gated ? up(steps * esz) : 0);
+    l.total = l.cws + bwd_layout(vp, false).total;
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -503,6 +526,69 @@ linattn_status linattn_chunk_bwd(const linattn_chunk_args* a, const void* q, con
                       p.T > 0 ? reinterpret_cast<float*>(ws + l.gc) : nullptr,
                       p.T > 0 ? ws + l.dst : nullptr};
     return launch_chunk_bwd(b, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t linattn_deltaproduct_bwd_workspace_bytes(const linattn_deltaproduct_args* a)
+{
+    linattn_chunk_args va{};
+    ChunkProblem vp{};
+    if (validate_dp(a, &va, &vp) != LINATTN_OK || validate_train(&va, &vp) != LINATTN_OK) return 0;
+    if (a->nh == 1) return bwd_layout(vp, false).total;
+    return dp_bwd_layout(va, vp).total;
+}
+
+linattn_status linattn_deltaproduct_bwd(const linattn_deltaproduct_args* a, const void* q, const void* k,
+                                        const void* v, const void* g, const void* beta, const float* s0,
+                                        const void* dout, const float* dsT, void* dq, void* dk, void* dv,
+                                        void* dg, void* dbeta, float* ds0, void* workspace,
+                                        size_t workspace_bytes, void* stream)
+{
+    linattn_chunk_args va{};
+    ChunkProblem vp{};
+    linattn_status st = validate_dp(a, &va, &vp);
+    if (st != LINATTN_OK) return st;
+    st = validate_train(&va, &vp);
+    if (st != LINATTN_OK) return st;
+    // one substep per token: the virtual sequence is the sequence itself
+    if (a->nh == 1)
+        return linattn_chunk_bwd(&va, q, k, v, g, beta, s0, nullptr, dout, dsT, dq, dk, dv, dg, dbeta, ds0,
+                                 workspace, workspace_bytes, stream);
+    if (vp.B * vp.H == 0) return LINATTN_OK;
+    if (a->T == 0)
+        return linattn_chunk_bwd(&va, q, k, v, g, beta, s0, nullptr, dout, dsT, dq, dk, dv, dg, dbeta, ds0,
+                                 workspace, workspace_bytes, stream);
+    st = check_pointers(LINATTN_RULE_DELTA, a->gate, q, k, v, g, beta, q, dout);
+    if (st != LINATTN_OK) return st;
+    if (!dq || !dk || !dv || !dbeta) return LINATTN_ERR_NULL;
+    if ((a->gate == LINATTN_GATE_SCALAR) != (dg != nullptr)) return dg ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
+    const void* outs[] = {dq, dk, dv, dg, dbeta, s0, dsT, ds0};
+    for (const void* x : outs)
+        if (x && !aligned16(x)) return LINATTN_ERR_UNSUPPORTED;
+    const DpBwdLayout l = dp_bwd_layout(va, vp);
+    if (!workspace || workspace_bytes < l.total) return LINATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const bool gated = a->gate == LINATTN_GATE_SCALAR;
+    DeltaProductProblem p{a->B, a->H, a->T, a->nh, a->dk, a->dv, a->dtype, q, g, ws + l.qv,
+                          gated ? ws + l.gv : nullptr, nullptr, nullptr};
+    if (launch_dp_expand(p, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+    if (launch_dp_scatter(p, dout, ws + l.dov, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+    st = linattn_chunk_bwd(&va, ws + l.qv, k, v, gated ? ws + l.gv : nullptr, beta, s0, nullptr, ws + l.dov, dsT,
+                           ws + l.dqv, dk, dv, gated ? ws + l.dgv : nullptr, dbeta, ds0, ws + l.cws,
+                           workspace_bytes - l.cws, stream);
+    if (st != LINATTN_OK) return st;
+    const int64_t rows = a->B * a->H * a->T;
+    // the query sits on the last substep, the gate on the first
+    if (launch_dp_pick(ws + l.dqv, dq, rows, a->nh, a->nh - 1, a->dk, a->dtype, s) != hipSuccess)
+        return LINATTN_ERR_LAUNCH;
+    if (gated && launch_dp_pick(ws + l.dgv, dg, rows, a->nh, 0, 1, a->dtype, s) != hipSuccess)
+        return LINATTN_ERR_LAUNCH;
+    return LINATTN_OK;
 }
 
 }  // extern "C"

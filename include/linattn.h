@@ -290,6 +290,38 @@ linattn_status linattn_chunk_bwd(const linattn_chunk_args *a,
                                  void *stream);
 
 /*
+ * Device workspace, in bytes, of linattn_deltaproduct_bwd (the expanded
+ * queries and gates, the virtual dO, dq and dg, and linattn_chunk_bwd's
+ * workspace for the virtual sequence); 0 for invalid or unsupported arguments.
+ */
+size_t linattn_deltaproduct_bwd_workspace_bytes(const linattn_deltaproduct_args *a);
+
+/*
+ * Backward pass of Gated DeltaProduct ("Linear Attention, Visualized", "Gated
+ * Delta Product (GDP)"): the gradients with respect to q, k, v, g, beta and s0
+ * given dout and dsT, computed as the Gated DeltaNet backward over the
+ * virtual sequence ("GDP as GDN over a virtual sequence": the query on the
+ * last substep of each token, the gate on the first), so dk, dv and dbeta come
+ * out in the [B,H,T,nh,...] layout and dq, dg are the virtual ones at those
+ * substeps.  The forward's states are recomputed.
+ *
+ *   q, k, v, g, beta, s0: as linattn_deltaproduct_fwd
+ *   dout     [B,H,T,dv] token dtype;  dsT [B,H,dk,dv] fp32 or NULL
+ *   dq [B,H,T,dk], dk [B,H,T,nh,dk], dv [B,H,T,nh,dv], dg [B,H,T] (SCALAR gate,
+ *   else NULL), dbeta [B,H,T,nh]: token dtype;  ds0 [B,H,dk,dv] fp32 or NULL
+ *   workspace: at least linattn_deltaproduct_bwd_workspace_bytes(a) bytes,
+ *            16-byte aligned
+ * Supported: as linattn_chunk_bwd for the virtual length n_h T.
+ */
+linattn_status linattn_deltaproduct_bwd(const linattn_deltaproduct_args *a,
+                                        const void *q, const void *k, const void *v,
+                                        const void *g, const void *beta, const float *s0,
+                                        const void *dout, const float *dsT,
+                                        void *dq, void *dk, void *dv, void *dg, void *dbeta,
+                                        float *ds0, void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
+/*
  * One recurrent decode step for N sequences x H heads, updating the state in
  * place ("Linear Attention, Visualized", "Optional: Linear attention as an
  * RNN" and the DeltaNet recurrent form; "All sorts of famous Attention

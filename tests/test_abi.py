@@ -139,6 +139,48 @@ def test_deltaproduct_validation(lib):
     assert lib.linattn_deltaproduct_workspace_bytes(ctypes.byref(mk(nh=1))) == 0
 
 
+def test_backward_validation(lib):
+    mk = lambda **kw: bd.chunk_args(**{**dict(B=1, H=1, T=64, dk=64, dv=64, rule="delta",
+                                              gate="scalar", dtype="bf16"), **kw})
+    F = FAKE
+
+    def bwd(a, g=F, beta=F, dg=F, dbeta=F, states=None, dq=F, ws=None, wsb=0):
+        return lib.linattn_chunk_bwd(ctypes.byref(a), F, F, F, g, beta, None, states, F, None, dq, F, F, dg,
+                                     dbeta, None, ws, wsb, None)
+
+    assert lib.linattn_chunk_bwd(None, *([None] * 16), 0, None) == 1
+    assert bwd(mk(gate="channel")) == 3                     # the per-channel gate has no backward
+    assert bwd(mk(chunk=32)) == 3
+    assert bwd(mk(dtype="fp32", dk=128)) == 3
+    assert bwd(mk(), dg=None) == 1                           # scalar gate needs dg
+    assert bwd(mk(gate="none"), g=None) == 6                 # dg given without a gate
+    assert bwd(mk(rule="add"), beta=None) == 6               # dbeta given for the add rule
+    assert bwd(mk(), dq=None) == 1
+    assert bwd(mk(), dq=F + 8) == 3                          # misaligned
+    assert bwd(mk()) == 4                                    # no workspace
+    need = lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk()), 0)
+    given = lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk()), 1)
+    assert need > given > 0
+    assert bwd(mk(), ws=F, wsb=need - 1) == 4
+    assert lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk(gate="channel")), 0) == 0
+    assert bwd(mk(B=0)) == 0                                 # nothing to do
+    # forward keeping the chunk states
+    fs = lambda a, states=F: lib.linattn_chunk_fwd_save(ctypes.byref(a), F, F, F, F, F, None, F, None, states, None)
+    assert fs(mk(), states=None) == 1
+    assert fs(mk(gate="channel")) == 3
+    assert fs(mk(), states=F + 4) == 3
+    # Gated DeltaProduct backward
+    da = lambda **kw: bd.deltaproduct_args(**{**dict(B=1, H=1, T=32, nh=2, dk=64, dv=64, gate="scalar",
+                                                     dtype="bf16"), **kw})
+    dpb = lambda a, dg=F, ws=None, wsb=0: lib.linattn_deltaproduct_bwd(
+        ctypes.byref(a), F, F, F, F, F, None, F, None, F, F, F, dg, F, None, ws, wsb, None)
+    assert dpb(da(gate="channel")) == 3
+    assert dpb(da(nh=0)) == 2
+    assert dpb(da(), dg=None) == 1
+    assert dpb(da()) == 4
+    assert lib.linattn_deltaproduct_bwd_workspace_bytes(ctypes.byref(da())) > 0
+
+
 def test_decode_validation(lib):
     mk = lambda **kw: bd.DecodeArgs(*[{**dict(N=2, H=2, dk=64, dv=64, rule=1, gate=1, dtype=1),
                                         **kw}[f] for f in ("N", "H", "dk", "dv", "rule", "gate",

@@ -111,3 +111,64 @@ def test_gdp2_full_size_sampled():
         es = rel_l2(host(s[b, h]), sref[i, 0])
         note(f"    head ({b},{h}): rel L2 o={eo:.3e} S={es:.3e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# ---- backward ----------------------------------------------------------------
+BWD_NAMES = ("dq", "dk", "dv", "dg", "dbeta", "ds0")
+
+
+def check_gdp_bwd(case, tol=None):
+    import gated_delta_rule_27_amd as la
+    tol = TOL[case.dtype] if tol is None else tol
+    note(f"[gdp bwd] {case.name} nh={case.nh} gate={case.gate} dtype={case.dtype} B={case.B} H={case.H} "
+         f"T={case.T} dk={case.dk} dv={case.dv}")
+    x, gr = syn.deltaproduct_inputs(case), syn.grad_inputs(case)
+    d = lambda a: dev(a, case.dtype)
+    out = la.deltaproduct_bwd(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]), d(gr["do"]),
+                              dev_state(x["s0"]), dev_state(gr["dsT"]), gate=case.gate)
+    torch.cuda.synchronize()
+    ref = oracle.deltaproduct_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], gr["do"], gr["dsT"],
+                                  gate=case.gate)
+    errs = {}
+    for n in BWD_NAMES:
+        if ref[n] is None:
+            assert out[n] is None
+            continue
+        a = host(out[n])
+        assert np.all(np.isfinite(a)), f"non-finite {n}"
+        errs[n] = rel_l2(a, ref[n])
+    note("    rel L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if e > tol}
+    assert not bad, f"above {tol}: {bad}"
+
+
+BWD_SMALL = []
+for dtype, dims in (("bf16", ((128, 128), (64, 64), (64, 128))), ("fp32", ((64, 64),))):
+    for (dk, dv) in dims:
+        for nh in (1, 2, 3):
+            for gate in ("none", "scalar"):
+                BWD_SMALL.append((dtype, dk, dv, nh, gate))
+
+
+@pytest.mark.parametrize("dtype,dk,dv,nh,gate", BWD_SMALL)
+def test_bwd_small_ragged(dtype, dk, dv, nh, gate):
+    case = syn.DeltaProductCase("gdp_bwd", 2, 2, 70, nh, dk, dv, gate, dtype, gate_scale=0.25,
+                                s0_std=0.3, case_id=150)
+    check_gdp_bwd(case)
+
+
+@pytest.mark.parametrize("T", [1, 32, 33, 97])
+def test_bwd_lengths(T):
+    case = syn.DeltaProductCase("gdp_bwd_len", 1, 2, T, 2, 128, 128, "scalar", "bf16", gate_scale=0.25,
+                                s0_std=0.2, case_id=151)
+    check_gdp_bwd(case)
+
+
+def test_bwd_zero_tokens():
+    import gated_delta_rule_27_amd as la
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    dsT = torch.randn(1, 2, 64, 64, device="cuda")
+    out = la.deltaproduct_bwd(e(1, 2, 0, 64), e(1, 2, 0, 3, 64), e(1, 2, 0, 3, 64), e(1, 2, 0), e(1, 2, 0, 3),
+                              e(1, 2, 0, 64), None, dsT)
+    torch.cuda.synchronize()
+    assert torch.equal(out["ds0"], dsT)
