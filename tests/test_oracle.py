@@ -71,7 +71,7 @@ def test_chunk_backward_equals_oracle(orc):
     rng = np.random.default_rng(19)
     B, H, T, dk, dv = 1, 1, 45, 6, 5
     for rule in ("add", "delta"):
-        for gate in ("none", "scalar"):
+        for gate in ("none", "scalar", "channel"):
             q, k, v, g, beta, S0 = rand_case(rng, B, H, T, dk, dv, gate=gate, gate_scale=0.5)
             do = rng.standard_normal((B, H, T, dv))
             dsT = rng.standard_normal((B, H, dk, dv))
