@@ -102,7 +102,7 @@ def load(path: str = LIB_PATH):
                                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.linattn_chunk_fwd_normalized.restype = ctypes.c_int
         lib.linattn_chunk_fwd_save.argtypes = [ctypes.POINTER(ChunkArgs), vp, vp, vp, vp, vp, vp, vp,
-                                               vp, vp, vp]
+                                               vp, vp, vp, sz, vp]
         lib.linattn_chunk_fwd_save.restype = ctypes.c_int
         lib.linattn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.c_int]
         lib.linattn_chunk_bwd_workspace_bytes.restype = sz
@@ -378,7 +378,7 @@ def chunk_fwd_normalized(q, k, v, g=None, s0=None, z0=None, *, gate="none", chun
 
 
 def _train_inputs(q, k, v, g, beta, rule, gate):
-    """Shapes, dtype and device of a training-pass problem (gate none or scalar)."""
+    """Shapes, dtype and device of a training-pass problem."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -387,11 +387,13 @@ def _train_inputs(q, k, v, g, beta, rule, gate):
     _check(v, "v", (B, H, T, dv), dt, dev)
     if gate == "scalar":
         _check(g, "g", (B, H, T), dt, dev)
+    elif gate == "channel":
+        _check(g, "g", (B, H, T, dk), dt, dev)
     elif gate == "none":
         if g is not None:
             raise ValueError("g must be None when gate='none'")
     else:
-        raise ValueError("the training passes take gate='none' or gate='scalar'")
+        raise ValueError(f"unknown gate {gate!r}")
     if rule == "delta":
         _check(beta, "beta", (B, H, T), dt, dev)
     elif beta is not None:
@@ -406,10 +408,11 @@ def chunk_states_shape(B, H, T, dk, dv, chunk=64):
 
 
 def chunk_fwd_save(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar", chunk=64,
-                   out=None, s_final=None, states=None, return_state=True):
+                   out=None, s_final=None, states=None, return_state=True, workspace=None):
     """Chunk forward that also returns the state entering every chunk, for
     chunk_bwd.  Returns (o, S_T or None, states [B,H,N,dk,dv] in the token
-    dtype)."""
+    dtype).  The per-channel gate needs a workspace (allocated here unless
+    given, at least chunk_workspace_bytes)."""
     import torch
     lib = load()
     B, H, T, dk, dv, dev, dt = _train_inputs(q, k, v, g, beta, rule, gate)
@@ -429,9 +432,14 @@ def chunk_fwd_save(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="s
     else:
         _check(states, "states", shape, dt, dev)
     a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=_token_dtype(q), chunk=chunk)
+    need = int(lib.linattn_chunk_workspace_bytes(ctypes.byref(a))) if gate == "channel" else 0
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib.linattn_chunk_fwd_save(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                    _ptr(s0), _ptr(out), _ptr(s_final), _ptr(states), stream)
+                                    _ptr(s0), _ptr(out), _ptr(s_final), _ptr(states), _ptr(workspace),
+                                    ws_bytes, stream)
     if st != 0:
         raise LinattnError(st, "linattn_chunk_fwd_save")
     return out, s_final, states
@@ -449,7 +457,8 @@ def chunk_bwd(q, k, v, g, beta, dout, s0=None, dsT=None, *, states=None, rule="d
     [B,H,T,dv], token dtype) and dL/dS_T (dsT [B,H,dk,dv] fp32 or None).
     states: the per-chunk states from chunk_fwd_save, or None to recompute
     them from q, k, v, g, beta and s0.  Returns a dict with dq, dk, dv, dg
-    (None without a gate), dbeta (None for the add rule) and ds0 (fp32).
+    (None without a gate; [B,H,T,dk] for the per-channel gate), dbeta (None
+    for the add rule) and ds0 (fp32).
     ``grads`` may supply preallocated outputs under the same names."""
     import torch
     lib = load()
@@ -461,7 +470,7 @@ def chunk_bwd(q, k, v, g, beta, dout, s0=None, dsT=None, *, states=None, rule="d
     if states is not None:
         _check(states, "states", chunk_states_shape(B, H, T, dk, dv, chunk), dt, dev)
     shapes = {"dq": ((B, H, T, dk), dt), "dk": ((B, H, T, dk), dt), "dv": ((B, H, T, dv), dt),
-              "dg": ((B, H, T), dt) if gate == "scalar" else None,
+              "dg": {"scalar": ((B, H, T), dt), "channel": ((B, H, T, dk), dt)}.get(gate),
               "dbeta": ((B, H, T), dt) if rule == "delta" else None,
               "ds0": ((B, H, dk, dv), torch.float32)}
     out = dict(grads or {})

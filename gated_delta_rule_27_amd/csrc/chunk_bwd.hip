@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kC = 64;
 constexpr int kNT = 512;                 // 8 waves
+constexpr float kLog2eB = 1.4426950408889634f;   // log2(e): channel gates are kept in base 2
 typedef __attribute__((__vector_size__(16))) int i4;
 
 template <typename T> using F16 = typename Frag16<T>::type;
@@ -151,6 +152,53 @@ struct BwdCfg {
                          O_QDT = O_KR + kC * DK, O_NKDT = O_QDT + DK * kC;
 };
 
+// T = (I + diag(beta) L)^-1 and Tb = T diag(beta) from the strict lower
+// triangular L in LDS (Tm must hold zeros above its diagonal blocks); every
+// thread of the workgroup calls this, the results are in LDS on return.
+template <typename T>
+__device__ void tri_inverse(const T* Lm, T* Tm, T* Tb, const float* bet, int tid)
+{
+    using C = BwdCfg<T, 64>;
+    constexpr int LDC = C::LDC;
+    const int lane = tid & 63, wave = tid >> 6;
+    // diagonal 16x16 blocks of T by forward substitution, fp32: lane = (block
+    // b, column j); x_i = [i == j] - beta_i sum_{s < i} L_is x_s
+    if (wave == 0) {
+        const int b = lane >> 4, j = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = i == j ? 1.f : 0.f;
+            const T* lrow = Lm + (16 * b + i) * LDC + 16 * b;
+            float s = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < i; ++s2) s += to_f32(lrow[s2]) * x[s2];
+            x[i] = acc - bet[16 * b + i] * s;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tm[(16 * b + i) * LDC + 16 * b + j] = from_f32<T>(x[i]);
+    }
+    __syncthreads();
+    // blocks below the diagonal, one diagonal of blocks at a time:
+    // T_ij = -T_ii diag(beta_i) sum_{s=j}^{i-1} L_is T_sj
+    for (int d = 1; d < 4; ++d) {
+        if (wave < 4 - d) {
+            const int i = wave + d, j = wave;
+            floatx4 y = tile<T, true, false>(zero4(), Lm, LDC, 16 * i, Tm, LDC, 16 * j, 16 * j, 16 * i, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] *= -bet[16 * i + 4 * (lane >> 4) + r];
+            const floatx4 t = mma16<T>(frag_xk(Tm, LDC, 16 * i, 16 * i, lane), frag16_acc<T>(y), zero4());
+            put(Tm, LDC, 16 * i, 16 * j, t, lane);
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < kC * kC; i += kNT) {
+        const int l = i / kC, m = i % kC;
+        Tb[l * LDC + m] = from_f32<T>(to_f32(Tm[l * LDC + m]) * bet[m]);
+    }
+    __syncthreads();
+}
+
 // Shared front of the two per-chunk kernels: chunk r's q and k (zero rows past
 // the end), the in-chunk gate prefix G, exp(G), beta, the causal decayed
 // scores A, the strict decayed key scores L and, for the delta rule,
@@ -224,44 +272,7 @@ __device__ void intra_chunk(const IntraLds<T, DK>& L, const T* __restrict__ q, c
         }
     }
     __syncthreads();
-    if constexpr (DELTA) {
-        // diagonal 16x16 blocks of T by forward substitution, fp32: lane = (block
-        // b, column j); x_i = [i == j] - beta_i sum_{s < i} L_is x_s
-        if (wave == 0) {
-            const int b = lane >> 4, j = lane & 15;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = i == j ? 1.f : 0.f;
-                const T* lrow = L.Lm + (16 * b + i) * LDC + 16 * b;
-                float s = 0.f;
-#pragma unroll
-                for (int s2 = 0; s2 < i; ++s2) s += to_f32(lrow[s2]) * x[s2];
-                x[i] = acc - L.bet[16 * b + i] * s;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) L.Tm[(16 * b + i) * LDC + 16 * b + j] = from_f32<T>(x[i]);
-        }
-        __syncthreads();
-        // blocks below the diagonal, one diagonal of blocks at a time:
-        // T_ij = -T_ii diag(beta_i) sum_{s=j}^{i-1} L_is T_sj
-        for (int d = 1; d < 4; ++d) {
-            if (wave < 4 - d) {
-                const int i = wave + d, j = wave;
-                floatx4 y = tile<T, true, false>(zero4(), L.Lm, LDC, 16 * i, L.Tm, LDC, 16 * j, 16 * j, 16 * i, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] *= -L.bet[16 * i + 4 * (lane >> 4) + r];
-                const floatx4 t = mma16<T>(frag_xk(L.Tm, LDC, 16 * i, 16 * i, lane), frag16_acc<T>(y), zero4());
-                put(L.Tm, LDC, 16 * i, 16 * j, t, lane);
-            }
-            __syncthreads();
-        }
-        for (int i = tid; i < kC * kC; i += kNT) {
-            const int l = i / kC, m = i % kC;
-            L.Tb[l * LDC + m] = from_f32<T>(to_f32(L.Tm[l * LDC + m]) * L.bet[m]);
-        }
-        __syncthreads();
-    }
+    if constexpr (DELTA) tri_inverse<T>(L.Lm, L.Tm, L.Tb, L.bet, tid);
 }
 
 // ============================================================================
@@ -339,6 +350,208 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q
 }
 
 // ============================================================================
+// bwd_ops_channel_kernel: per chunk, the operands of the reverse state pass and
+// of the gradient pass for the per-key-channel gate (bf16 tokens; "Linear
+// Attention, Visualized", "Gated Linear Attention (GLA)" and "Kimi Delta
+// Attention (KDA)": the decay is a diagonal matrix, so every score keeps the
+// decay inside its sum over key channels).  With G[l][c] the in-chunk prefix
+// of channel c's log-gate (kept in base 2: log2(e) g, so each factor is one
+// hardware exp2):
+//   A[l][m] = sum_c q_lc 2^(G_lc - G_mc) k_mc (m <= l),  L[l][m] the same with
+//   k_l in place of q_l (m < l).
+// Off the diagonal 16x16 blocks (row l in block i, key m in block j < i) the
+// factor splits at row s = 16 i - 1 into 2^(G_l - G_s) 2^(G_s - G_m), both at
+// most 1 for decays, applied to the operands of one matrix-core product; the
+// diagonal blocks are summed element by element with the exact factor.
+// Stored per chunk: A^T, Tb^T, Tb, ->K, <-Q^T, -<-K^T (the reverse state pass,
+// as bwd_ops_kernel), T and L (the gradient pass), and 2^(G_C) per channel.
+// ============================================================================
+template <int DK, int RULE>
+__global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __restrict__ q,
+                                                                 const bf16* __restrict__ k,
+                                                                 const bf16* __restrict__ g,
+                                                                 const bf16* __restrict__ beta,
+                                                                 bf16* __restrict__ ops, float* __restrict__ gC,
+                                                                 int64_t Tlen, int64_t nchunks)
+{
+    using C = BwdCfg<bf16, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, E = C::E, LDG = DK + 4;
+    constexpr bool DELTA = RULE == kRuleDelta;
+    constexpr int OSTRIDE = C::OPS + 2 * kC * kC;
+    __shared__ __align__(16) bf16 Qs[kC * LDQ], Ks[kC * LDQ];
+    __shared__ __align__(16) bf16 CC[4 * kC * LDC];    // Aq, Lm, Tm, Tb
+    __shared__ __align__(16) float Gf[kC * LDG];        // G, base 2
+    __shared__ __align__(16) float tot[4][DK];
+    __shared__ float bet[kC];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.x / nchunks, r = blockIdx.x % nchunks;
+    const int64_t t0 = r * kC;
+    const int tvalid = (int)(Tlen - t0 < kC ? Tlen - t0 : kC);
+    bf16* const Aq = CC;
+    bf16* const Lm = CC + kC * LDC;
+    bf16* const Tm = CC + 2 * kC * LDC;
+    bf16* const Tb = CC + 3 * kC * LDC;
+
+    {
+        constexpr int NZ = 3 * kC * LDC * 2 / 16;      // Aq, Lm, Tm
+        i4* z = reinterpret_cast<i4*>(CC);
+        for (int i = tid; i < NZ; i += kNT) z[i] = i4{0, 0, 0, 0};
+    }
+    {
+        constexpr int VR = DK / E;
+        for (int i = tid; i < kC * VR; i += kNT) {
+            const int row = i / VR, c = (i % VR) * E;
+            i4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+            if (row < tvalid) {
+                a = *reinterpret_cast<const i4*>(q + (bh * Tlen + t0 + row) * DK + c);
+                b = *reinterpret_cast<const i4*>(k + (bh * Tlen + t0 + row) * DK + c);
+            }
+            *reinterpret_cast<i4*>(Qs + row * LDQ + c) = a;
+            *reinterpret_cast<i4*>(Ks + row * LDQ + c) = b;
+        }
+    }
+    if (tid < kC) bet[tid] = (DELTA && tid < tvalid) ? to_f32(beta[bh * Tlen + t0 + tid]) : 0.f;
+    // prefix: thread (block pb, channel pc) walks its block's 16 rows
+    const int pc = tid % DK, pb = tid / DK;
+    const bool pre = tid < 4 * DK;
+    float Gl[16];
+    if (pre) {
+        float acc = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 16 * pb + rr;
+            if (row < tvalid) acc += to_f32(g[(bh * Tlen + t0 + row) * DK + pc]) * kLog2eB;
+            Gl[rr] = acc;
+        }
+        tot[pb][pc] = acc;
+    }
+    __syncthreads();
+    if (pre) {
+        float off = 0.f;
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+            if (b < pb) off += tot[b][pc];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) Gf[(16 * pb + rr) * LDG + pc] = off + Gl[rr];
+    }
+    __syncthreads();
+
+    // off-diagonal score tiles: wave p takes pair p of (1,0)(2,0)(2,1)(3,0)(3,1)(3,2),
+    // A and L together (their query-side factors are the same)
+    if (wave < 6) {
+        const int i = wave < 1 ? 1 : (wave < 3 ? 2 : 3);
+        const int j = wave - i * (i - 1) / 2;
+        const int s = 16 * i - 1;
+        const int xa = 16 * i + (lane & 15), xb = 16 * j + (lane & 15);
+        floatx4 accA = zero4(), accL = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 16) {
+            const int c0 = k0 + 4 * (lane >> 4);
+            const floatx4 gs = *reinterpret_cast<const floatx4*>(&Gf[s * LDG + c0]);
+            const floatx4 ga = *reinterpret_cast<const floatx4*>(&Gf[xa * LDG + c0]);
+            const floatx4 gb = *reinterpret_cast<const floatx4*>(&Gf[xb * LDG + c0]);
+            const bf16x4 qa = *reinterpret_cast<const bf16x4*>(&Qs[xa * LDQ + c0]);
+            const bf16x4 ka = *reinterpret_cast<const bf16x4*>(&Ks[xa * LDQ + c0]);
+            const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&Ks[xb * LDQ + c0]);
+            bf16x4 fq, fk, fb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ua = fast_exp2(ga[e] - gs[e]), wb = fast_exp2(gs[e] - gb[e]);
+                fq[e] = from_f32<bf16>(to_f32(qa[e]) * ua);
+                fk[e] = from_f32<bf16>(to_f32(ka[e]) * ua);
+                fb[e] = from_f32<bf16>(to_f32(kb[e]) * wb);
+            }
+            accA = mma16<bf16>(fq, fb, accA);
+            if constexpr (DELTA) accL = mma16<bf16>(fk, fb, accL);
+        }
+        put(Aq, LDC, 16 * i, 16 * j, accA, lane);
+        if constexpr (DELTA) put(Lm, LDC, 16 * i, 16 * j, accL, lane);
+    }
+    // diagonal blocks element by element: item = (block b, l >= m inside it)
+    for (int it = tid; it < 4 * 136; it += kNT) {
+        const int b = it / 136;
+        int li = 0, p = it % 136;
+        while (p > li) { p -= li + 1; ++li; }
+        const int l = 16 * b + li, m = 16 * b + p;
+        float a = 0.f, n = 0.f;
+        for (int c0 = 0; c0 < DK; c0 += 4) {
+            const floatx4 gl = *reinterpret_cast<const floatx4*>(&Gf[l * LDG + c0]);
+            const floatx4 gm = *reinterpret_cast<const floatx4*>(&Gf[m * LDG + c0]);
+            const bf16x4 ql = *reinterpret_cast<const bf16x4*>(&Qs[l * LDQ + c0]);
+            const bf16x4 kl = *reinterpret_cast<const bf16x4*>(&Ks[l * LDQ + c0]);
+            const bf16x4 km = *reinterpret_cast<const bf16x4*>(&Ks[m * LDQ + c0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dk_ = to_f32(km[e]) * fast_exp2(gl[e] - gm[e]);
+                a = fmaf(to_f32(ql[e]), dk_, a);
+                n = fmaf(to_f32(kl[e]), dk_, n);
+            }
+        }
+        Aq[l * LDC + m] = from_f32<bf16>(a);
+        if constexpr (DELTA) Lm[l * LDC + m] = from_f32<bf16>(m < l ? n : 0.f);
+    }
+    __syncthreads();
+    if constexpr (DELTA) tri_inverse<bf16>(Lm, Tm, Tb, bet, tid);
+
+    bf16* out = ops + (bh * nchunks + r) * (int64_t)OSTRIDE;
+    auto store = [&](bf16* dst, const float* x) {
+        bf16 e[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) e[i] = from_f32<bf16>(x[i]);
+        i4 w;
+        __builtin_memcpy(&w, e, 16);
+        *reinterpret_cast<i4*>(dst) = w;
+    };
+    auto copy_rows = [&](bf16* dst, const bf16* src) {
+        for (int v = tid; v < kC * kC / E; v += kNT) {
+            const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+            *reinterpret_cast<i4*>(dst + l * kC + m0) = *reinterpret_cast<const i4*>(src + l * LDC + m0);
+        }
+    };
+    float x[E];
+    // A^T and Tb^T: row l holds column l of A / Tb
+    for (int v = tid; v < kC * kC / E; v += kNT) {
+        const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+#pragma unroll
+        for (int i = 0; i < E; ++i) x[i] = to_f32(Aq[(m0 + i) * LDC + l]);
+        store(out + C::O_AQT + l * kC + m0, x);
+        if constexpr (DELTA) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) x[i] = to_f32(Tb[(m0 + i) * LDC + l]);
+            store(out + C::O_TBT + l * kC + m0, x);
+        }
+    }
+    if constexpr (DELTA) {
+        copy_rows(out + C::O_TB, Tb);
+        copy_rows(out + C::OPS, Tm);
+        copy_rows(out + C::OPS + kC * kC, Lm);
+    }
+    // ->K = 2^(G_C - G) . K, per channel
+    for (int v = tid; v < kC * DK / E; v += kNT) {
+        const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            x[i] = to_f32(Ks[l * LDQ + i0 + i]) * fast_exp2(Gf[(kC - 1) * LDG + i0 + i] - Gf[l * LDG + i0 + i]);
+        store(out + C::O_KR + l * DK + i0, x);
+    }
+    // <-Q^T and -<-K^T: row i holds key channel i over the chunk
+    for (int v = tid; v < DK * kC / E; v += kNT) {
+        const int i = v / (kC / E), m0 = (v % (kC / E)) * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = to_f32(Qs[(m0 + e) * LDQ + i]) * fast_exp2(Gf[(m0 + e) * LDG + i]);
+        store(out + C::O_QDT + i * kC + m0, x);
+        if constexpr (DELTA) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = -to_f32(Ks[(m0 + e) * LDQ + i]) * fast_exp2(Gf[(m0 + e) * LDG + i]);
+            store(out + C::O_NKDT + i * kC + m0, x);
+        }
+    }
+    if (tid < DK) gC[(bh * nchunks + r) * DK + tid] = fast_exp2(Gf[(kC - 1) * LDG + tid]);
+}
+
+// ============================================================================
 // bwd_chain_kernel: the reverse state pass.  One workgroup per (b, h, 64 value
 // columns): waves 0-3 own 16 columns of dS each (dk/16 result tiles, kept in
 // registers for the whole sequence) and touch no global memory but their
@@ -348,10 +561,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q
 // dS = exp(G_C) dS + <-Q^T dO - <-K^T dR while they stage the previous chunk's
 // A^T, Tb^T, ->K and dO^T (dO^T double-buffered, phase 2 reads it).
 // ============================================================================
-template <typename T, int DK, int RULE>
+template <typename T, int DK, int RULE, bool CHAN>
 __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__ dout, const T* __restrict__ ops,
-                                                           const float* __restrict__ gC, const float* dsT,
-                                                           T* __restrict__ dstates, float* ds0,
+                                                           int64_t ostride, const float* __restrict__ gC,
+                                                           const float* dsT, T* __restrict__ dstates, float* ds0,
                                                            int64_t Tlen, int64_t nchunks, int DV)
 {
     using C = BwdCfg<T, DK>;
@@ -369,7 +582,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
     __shared__ __align__(16) T QdT[DK * LDC];
     __shared__ __align__(16) T NKdT[DELTA ? DK * LDC : 8];
     __shared__ __align__(16) T dOT[2][64 * LDC];       // dO^T of the block: row j, column m
-    __shared__ float gCs[2];
+    __shared__ __align__(16) float gCs[2][CHAN ? DK : 1];   // exp(G_C), per key channel with CHAN
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -435,7 +648,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             }
             lds_barrier();
             // ---- phase 2: dS = exp(G_C) dS + <-Q^T dO - <-K^T dR ----
-            const float gc = gCs[buf];
             F16<T> drf[4];
             if constexpr (DELTA) {
 #pragma unroll
@@ -443,7 +655,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             }
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
-                floatx4 acc = dS[db] * gc;
+                floatx4 acc;
+                if constexpr (CHAN) acc = dS[db] * *reinterpret_cast<const floatx4*>(&gCs[buf][16 * db + g4]);
+                else acc = dS[db] * gCs[buf][0];
 #pragma unroll
                 for (int mb = 0; mb < 4; mb += 2)
                     acc = mma16x2<T>(frag_xk(QdT, LDC, 16 * db, 16 * mb, ln), frag_xk(QdT, LDC, 16 * db, 16 * mb + 16, ln),
@@ -468,8 +682,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
         const int ht = tid - 256;
         i4 ra[NA], rt[NA], rk[NK], ro[NO], rq[NK], rn[NK];
         float rg = 0.f;
+        i4 rgv = {0, 0, 0, 0};
         auto load1 = [&](int64_t c) {
-            const T* base = ops + (bh * nchunks + c) * (int64_t)C::OPS;
+            const T* base = ops + (bh * nchunks + c) * ostride;
 #pragma unroll
             for (int p = 0; p < NA; ++p) {
                 const int e = (p * NH + ht) * E;
@@ -489,7 +704,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
                 ro[p] = i4{0, 0, 0, 0};
                 if (t < Tlen) ro[p] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t) * DV + vb * 64 + cc);
             }
-            rg = gC[bh * nchunks + c];
+            if constexpr (CHAN) {
+                if (ht < DK / 4) rgv = *reinterpret_cast<const i4*>(gC + (bh * nchunks + c) * DK + 4 * ht);
+            } else {
+                rg = gC[bh * nchunks + c];
+            }
         };
         auto stage1 = [&](int64_t c) {
             const int buf = (int)(c & 1);
@@ -513,10 +732,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
 #pragma unroll
                 for (int i = 0; i < E; ++i) dOT[buf][(cc + i) * LDC + row] = x[i];
             }
-            if (ht == 0) gCs[buf] = rg;
+            if constexpr (CHAN) {
+                if (ht < DK / 4) *reinterpret_cast<i4*>(&gCs[buf][4 * ht]) = rgv;
+            } else {
+                if (ht == 0) gCs[buf][0] = rg;
+            }
         };
         auto load2 = [&](int64_t c) {
-            const T* base = ops + (bh * nchunks + c) * (int64_t)C::OPS;
+            const T* base = ops + (bh * nchunks + c) * ostride;
 #pragma unroll
             for (int p = 0; p < NK; ++p) {
                 const int e = (p * NH + ht) * E;
@@ -1400,6 +1623,520 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
     }
 }
 
+// ============================================================================
+// bwd_grad_channel_kernel: every gradient of one chunk for the per-key-channel
+// gate (bf16 tokens).  The value loop is that of bwd_grad_kernel with the
+// decayed keys as explicit operands (<-K = 2^G . K and ->K = 2^(G_C - G) . K
+// per channel, built in LDS).  The score gradients then keep the decay per
+// channel c, D_c[l][m] = 2^(G_lc - G_mc):
+//   dq_A[l][c] = sum_m dA[l][m] D_c[l][m] k_mc        dk_L1[l][c] likewise with dL
+//   dk_A[m][c] = sum_l dA[l][m] D_c[l][m] q_lc        dk_L2[m][c] = sum_l dL[l][m] D_c[l][m] k_lc
+// Off the diagonal 16x16 blocks each is one matrix-core product over the other
+// block's rows, the decay split at a block boundary into two factors of at most
+// 1 (one on the operand, one on the result); the diagonal blocks are summed
+// element by element by thread (block, channel) and handed to the result tiles
+// through LDS.  Per element then
+//   dq = 2^G d<-Q + dq_A ; dk = 2^G d<-K + 2^(G_C - G) d->K + dk_A + dk_L1 + dk_L2
+//   dG = q 2^G d<-Q + k 2^G d<-K - k 2^(G_C-G) d->K + q dq_A - k dk_A + k dk_L1 - k dk_L2
+//   dG_C += sum_l k_l 2^(G_C-G_l) d->K_l + 2^(G_C) sum_j S_r[c][j] dS[c][j]
+// and dg is the reverse prefix sum of dG over the chunk, per channel.
+// ============================================================================
+template <int DK, int RULE>
+__global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ g, const bf16* __restrict__ beta, const bf16* __restrict__ dout,
+    const bf16* __restrict__ ops, const bf16* __restrict__ states, const bf16* __restrict__ dstates,
+    bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv, bf16* __restrict__ dg,
+    bf16* __restrict__ dbeta, int64_t Tlen, int64_t nchunks, int DV)
+{
+    using C = BwdCfg<bf16, DK>;
+    constexpr int LDQ = C::LDQ, LDC = C::LDC, LDJ = C::LDJ, J = C::J, E = C::E, LDG = DK + 4;
+    constexpr bool DELTA = RULE == kRuleDelta;
+    constexpr int NI = DK / 32;            // key-channel tiles per wave (of dq, dk)
+    constexpr int NJT = J / 16;            // value-column tiles per step
+    constexpr int OSTRIDE = C::OPS + 2 * kC * kC;
+    static_assert(4 * NJT == 8, "one step-A tile per wave");
+    // the value loop's arrays, and in the same bytes the final phase's
+    // X (fp32 [C][LDG]: dTb and X1 first, then the hand-over buffer), G (fp32
+    // [C][LDG], base 2), dA and dL (bf16 [C][LDC])
+    constexpr int LOOP_BYTES = (5 * kC * LDJ + 2 * DK * LDJ) * 2;
+    constexpr int XB = kC * LDG * 4, CB = kC * LDC * 2;
+    constexpr int XS = XB > 2 * CB ? XB : 2 * CB;                 // X holds dTb and X1 first
+    constexpr int FIN_BYTES = XS + XB + 2 * CB;
+    constexpr int REGION = LOOP_BYTES > FIN_BYTES ? LOOP_BYTES : FIN_BYTES;
+
+    __shared__ __align__(16) bf16 KA[kC * LDQ];                // <-K in the loop, then q
+    __shared__ __align__(16) bf16 KB[kC * LDQ];                // ->K in the loop, then k
+    __shared__ __align__(16) bf16 AqT[kC * LDC];               // A^T in the loop, then T
+    __shared__ __align__(16) bf16 TbT[DELTA ? kC * LDC : 8];   // Tb^T in the loop, then L
+    __shared__ __align__(16) bf16 Tb[DELTA ? kC * LDC : 8];
+    __shared__ __align__(16) unsigned char region[REGION];
+    __shared__ __align__(16) float tot[4][DK], tsum[4][DK];
+    __shared__ float sdc[DK], bet[kC], colB[kC], rowB[2][kC];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.x / nchunks, r = blockIdx.x % nchunks;
+    const int64_t t0 = r * kC;
+    const int tvalid = (int)(Tlen - t0 < kC ? Tlen - t0 : kC);
+    const bf16* Sr = states + (bh * nchunks + r) * (int64_t)DK * DV;
+    const bf16* dSr = dstates + (bh * nchunks + r) * (int64_t)DK * DV;
+    const bf16* opc = ops + (bh * nchunks + r) * (int64_t)OSTRIDE;
+    const int pc = tid % DK, pb = tid / DK;
+    const bool pre = tid < 4 * DK;          // thread (block pb, channel pc)
+
+    // in-chunk prefix of the gate, thread (pb, pc): G of its 16 rows (base 2);
+    // every thread calls this (it holds a barrier)
+    auto prefix = [&](float* Gl) {
+        if (pre) {
+            float acc = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 16 * pb + rr;
+                if (row < tvalid) acc += to_f32(g[(bh * Tlen + t0 + row) * DK + pc]) * kLog2eB;
+                Gl[rr] = acc;
+            }
+            tot[pb][pc] = acc;
+        }
+        __syncthreads();
+        if (pre) {
+            float off = 0.f;
+#pragma unroll
+            for (int b = 0; b < 3; ++b)
+                if (b < pb) off += tot[b][pc];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) Gl[rr] += off;
+        }
+    };
+
+    // ---- front: A^T, Tb, Tb^T and the decayed keys ----
+    for (int vv = tid; vv < kC * kC / E; vv += kNT) {
+        const int l = vv / (kC / E), m0 = (vv % (kC / E)) * E;
+        *reinterpret_cast<i4*>(AqT + l * LDC + m0) = *reinterpret_cast<const i4*>(opc + C::O_AQT + l * kC + m0);
+        if constexpr (DELTA) {
+            *reinterpret_cast<i4*>(Tb + l * LDC + m0) = *reinterpret_cast<const i4*>(opc + C::O_TB + l * kC + m0);
+            *reinterpret_cast<i4*>(TbT + l * LDC + m0) = *reinterpret_cast<const i4*>(opc + C::O_TBT + l * kC + m0);
+        }
+    }
+    if (tid < kC) bet[tid] = (DELTA && tid < tvalid) ? to_f32(beta[bh * Tlen + t0 + tid]) : 0.f;
+    {
+        float Gl[16];
+        prefix(Gl);
+        if (pre) {
+            // 2^(G_C) of this channel: the last row's prefix, read back from the
+            // block totals
+            const float gl = tot[0][pc] + tot[1][pc] + tot[2][pc] + tot[3][pc];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 16 * pb + rr;
+                const float kv = row < tvalid ? to_f32(k[(bh * Tlen + t0 + row) * DK + pc]) : 0.f;
+                KA[row * LDQ + pc] = from_f32<bf16>(kv * fast_exp2(Gl[rr]));
+                KB[row * LDQ + pc] = from_f32<bf16>(kv * fast_exp2(gl - Gl[rr]));
+            }
+        }
+    }
+
+    // the value block's dO and V rows and its S_r and dS_{r+1} columns go
+    // through registers, the next block's loads issued before this block's products
+    constexpr int VR = J / E, NVJ = (kC * VR + kNT - 1) / kNT;
+    constexpr int SR = J / E, NSJ = (DK * SR + kNT - 1) / kNT;
+    static_assert(NSJ == 1, "one state row piece per thread");
+    i4 pdo[NVJ], pv[NVJ], ps, pds;
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < NVJ; ++u) {
+            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            pdo[u] = pv[u] = i4{0, 0, 0, 0};
+            if (i < kC * VR && row < tvalid) {
+                pdo[u] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t0 + row) * DV + j0 + c);
+                pv[u] = *reinterpret_cast<const i4*>(v + (bh * Tlen + t0 + row) * DV + j0 + c);
+            }
+        }
+        const int row = tid / SR, c = (tid % SR) * E;
+        ps = pds = i4{0, 0, 0, 0};
+        if (tid < DK * SR) {
+            ps = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
+            pds = *reinterpret_cast<const i4*>(dSr + row * DV + j0 + c);
+        }
+    };
+    fetch(0);
+
+    bf16* const dOs = reinterpret_cast<bf16*>(region);
+    bf16* const Rs = dOs + kC * LDJ;
+    bf16* const Zs = Rs + kC * LDJ;
+    bf16* const dZs = Zs + kC * LDJ;
+    bf16* const dRs = dZs + kC * LDJ;
+    bf16* const Ss = dRs + kC * LDJ;
+    bf16* const dSs = Ss + DK * LDJ;
+
+    const int cl = lane & 15, g4 = 4 * (lane >> 4);
+    const int lbq = wave >> 1;                       // row block of this wave's dq/dk tiles
+    const int lbt = wave >> 1;                       // row block of its dA/dTb tiles
+    floatx4 dQd[NI], dKd[NI], dKr[NI], dAq[2], dTb[2];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) dQd[u] = dKd[u] = dKr[u] = zero4();
+    dAq[0] = dAq[1] = dTb[0] = dTb[1] = zero4();
+    float sdot = 0.f;
+
+    for (int j0 = 0; j0 < DV; j0 += J) {
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NVJ; ++u) {
+            const int i = tid + u * kNT, row = i / VR, c = (i % VR) * E;
+            if (i < kC * VR) {
+                *reinterpret_cast<i4*>(dOs + row * LDJ + c) = pdo[u];
+                *reinterpret_cast<i4*>(Zs + row * LDJ + c) = pv[u];
+            }
+        }
+        if (tid < DK * SR) {
+            const int row = tid / SR, c = (tid % SR) * E;
+            bf16 a[E], b[E];
+            __builtin_memcpy(a, &ps, 16);
+            __builtin_memcpy(b, &pds, 16);
+#pragma unroll
+            for (int x = 0; x < E; ++x) sdot += to_f32(a[x]) * to_f32(b[x]);
+            *reinterpret_cast<i4*>(Ss + row * LDJ + c) = ps;
+            *reinterpret_cast<i4*>(dSs + row * LDJ + c) = pds;
+        }
+        __syncthreads();
+        if (j0 + J < DV) fetch(j0 + J);
+        // ---- step A: R = V - <-K S_r ; dZ = A^T dO + ->K dS ; d<-Q += dO S_r^T ----
+        {
+            const int lb = wave / NJT, jc = wave % NJT;
+            floatx4 dz = tilek<bf16, true, false, kC>(zero4(), AqT, LDC, 16 * lb, dOs, LDJ, 16 * jc, 0, lane);
+            dz = tilek<bf16, true, false, DK>(dz, KB, LDQ, 16 * lb, dSs, LDJ, 16 * jc, 0, lane);
+            put(dZs, LDJ, 16 * lb, 16 * jc, dz, lane);
+            if constexpr (DELTA) {
+                const floatx4 ks = tilek<bf16, true, false, DK>(zero4(), KA, LDQ, 16 * lb, Ss, LDJ, 16 * jc, 0, lane);
+                floatx4 rv;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) rv[rr] = to_f32(Zs[(16 * lb + g4 + rr) * LDJ + 16 * jc + cl]) - ks[rr];
+                put(Rs, LDJ, 16 * lb, 16 * jc, rv, lane);
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    if (l < tvalid) dv[(bh * Tlen + t0 + l) * DV + j0 + 16 * jc + cl] = from_f32<bf16>(dz[rr]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NI; ++u)
+            dQd[u] = tilek<bf16, true, true, J>(dQd[u], dOs, LDJ, 16 * lbq, Ss, LDJ, 16 * (NI * (wave & 1) + u), 0, lane);
+        __syncthreads();
+        // ---- step B (delta): Z = Tb R ; dR = Tb^T dZ (= dv) ; dTb += dZ R^T ----
+        if constexpr (DELTA) {
+            {
+                const int lb = wave / NJT, jc = wave % NJT;
+                const floatx4 z = tilek<bf16, true, false, kC>(zero4(), Tb, LDC, 16 * lb, Rs, LDJ, 16 * jc, 0, lane);
+                const floatx4 dr = tilek<bf16, true, false, kC>(zero4(), TbT, LDC, 16 * lb, dZs, LDJ, 16 * jc, 0, lane);
+                put(Zs, LDJ, 16 * lb, 16 * jc, z, lane);
+                put(dRs, LDJ, 16 * lb, 16 * jc, dr, lane);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int l = 16 * lb + g4 + rr;
+                    if (l < tvalid) dv[(bh * Tlen + t0 + l) * DV + j0 + 16 * jc + cl] = from_f32<bf16>(dr[rr]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int mb = 2 * (wave & 1) + u;
+                if (mb <= lbt) dTb[u] = tilek<bf16, true, true, J>(dTb[u], dZs, LDJ, 16 * lbt, Rs, LDJ, 16 * mb, 0, lane);
+            }
+            __syncthreads();
+        }
+        // ---- step C: d<-K += dR S_r^T (negated later) ; d->K += Z dS^T ; dA += dO Z^T ----
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            const int ib = NI * (wave & 1) + u;
+            if constexpr (DELTA) dKd[u] = tilek<bf16, true, true, J>(dKd[u], dRs, LDJ, 16 * lbq, Ss, LDJ, 16 * ib, 0, lane);
+            dKr[u] = tilek<bf16, true, true, J>(dKr[u], Zs, LDJ, 16 * lbq, dSs, LDJ, 16 * ib, 0, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            if (mb <= lbt) dAq[u] = tilek<bf16, true, true, J>(dAq[u], dOs, LDJ, 16 * lbt, Zs, LDJ, 16 * mb, 0, lane);
+        }
+    }
+    __syncthreads();
+
+    // ============ final phase ============
+    float* const X = reinterpret_cast<float*>(region);
+    float* const Gf = reinterpret_cast<float*>(region + XS);
+    bf16* const dAs = reinterpret_cast<bf16*>(region + XS + XB);
+    bf16* const dLs = reinterpret_cast<bf16*>(region + XS + XB + CB);
+    bf16* const dTbs = reinterpret_cast<bf16*>(region);           // in X
+    bf16* const X1s = reinterpret_cast<bf16*>(region + CB);       // in X
+    bf16* const Tm = AqT;
+    bf16* const Lm = TbT;
+    {
+        const float s = group_sum<4>(sdot);
+        if (tid < DK * SR && tid % SR == 0) sdc[tid / SR] = s;
+    }
+    // F0: dA and dTb (causal) to LDS; T, L over A^T, Tb^T; raw q, k over the
+    // decayed keys; G to LDS
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int mb = 2 * (wave & 1) + u;
+        floatx4 a = dAq[u], t = dTb[u];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const bool on = mb < lbt || (mb == lbt && cl <= g4 + rr);
+            a[rr] = on ? a[rr] : 0.f;
+            t[rr] = on ? t[rr] : 0.f;
+        }
+        put(dAs, LDC, 16 * lbt, 16 * mb, a, lane);
+        if constexpr (DELTA) put(dTbs, LDC, 16 * lbt, 16 * mb, t, lane);
+    }
+    for (int vv = tid; vv < kC * kC / E; vv += kNT) {
+        const int l = vv / (kC / E), m0 = (vv % (kC / E)) * E;
+        if constexpr (DELTA) {
+            *reinterpret_cast<i4*>(Tm + l * LDC + m0) = *reinterpret_cast<const i4*>(opc + C::OPS + l * kC + m0);
+            *reinterpret_cast<i4*>(Lm + l * LDC + m0) =
+                *reinterpret_cast<const i4*>(opc + C::OPS + kC * kC + l * kC + m0);
+        }
+    }
+    {
+        constexpr int VQ = DK / E;
+        for (int i = tid; i < kC * VQ; i += kNT) {
+            const int row = i / VQ, c = (i % VQ) * E;
+            i4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+            if (row < tvalid) {
+                a = *reinterpret_cast<const i4*>(q + (bh * Tlen + t0 + row) * DK + c);
+                b = *reinterpret_cast<const i4*>(k + (bh * Tlen + t0 + row) * DK + c);
+            }
+            *reinterpret_cast<i4*>(KA + row * LDQ + c) = a;
+            *reinterpret_cast<i4*>(KB + row * LDQ + c) = b;
+        }
+    }
+    {
+        float Gl[16];
+        prefix(Gl);
+        if (pre) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) Gf[(16 * pb + rr) * LDG + pc] = Gl[rr];
+        }
+    }
+    __syncthreads();
+    bf16* const Qr = KA;
+    bf16* const Kr = KB;
+
+    if constexpr (DELTA) {
+        // F1: dbeta from T . dTb (column sums); X1 = T^T dTb
+        const int sx = tid >> 3, sp = tid & 7;
+        {
+            float s3 = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int m = 8 * sp + u;
+                s3 += to_f32(Tm[m * LDC + sx]) * to_f32(dTbs[m * LDC + sx]);
+            }
+            s3 = group_sum<8>(s3);
+            if (sp == 0) colB[sx] = s3;
+        }
+        floatx4 X1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int sb = 2 * (wave & 1) + u;
+            X1[u] = tilek<bf16, false, false, kC>(zero4(), Tm, LDC, 16 * lbt, dTbs, LDC, 16 * sb, 0, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) put(X1s, LDC, 16 * lbt, 16 * (2 * (wave & 1) + u), X1[u], lane);
+        __syncthreads();
+        // F3: dM = -X1 Tb^T ; dL = diag(beta) dM (strict) ; dbeta += rowsum(dM . L)
+        float rb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mb = 2 * (wave & 1) + u;
+            const int m = 16 * mb + cl;
+            floatx4 dm = zero4();
+            if (mb <= lbt) dm = tilek<bf16, true, true, kC>(zero4(), X1s, LDC, 16 * lbt, Tb, LDC, 16 * mb, 0, lane);
+            floatx4 dl;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int l = 16 * lbt + g4 + rr;
+                const bool strict = mb <= lbt && m < l;
+                const float dM = -dm[rr];
+                rb[rr] += strict ? dM * to_f32(Lm[l * LDC + m]) : 0.f;
+                dl[rr] = strict ? bet[l] * dM : 0.f;
+            }
+            put(dLs, LDC, 16 * lbt, 16 * mb, dl, lane);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float a = group_sum<16>(rb[rr]);
+            if (cl == 0) rowB[wave & 1][16 * lbt + g4 + rr] = a;
+        }
+        __syncthreads();
+    }
+
+    // F4: the off-diagonal blocks of dq_A, dk_L1 (rows of block lbq against
+    // keys of earlier blocks, decay split at s = 16 lbq - 1) and of
+    // dk_A + dk_L2 (keys of block lbq against rows of later blocks, split at
+    // e = 16 lbq + 15)
+    floatx4 DQ[NI], KP[NI], KM[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        DQ[u] = KP[u] = KM[u] = zero4();
+        const int c = 16 * (NI * (wave & 1) + u) + cl;   // this lane's channel in the tiles
+        if (lbq > 0) {
+            const int s = 16 * lbq - 1;
+            const float gs = Gf[s * LDG + c];
+            for (int j = 0; j < lbq; ++j) {
+                const int m0 = 16 * j + g4;
+                bf16x4 b;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    b[e] = from_f32<bf16>(to_f32(Kr[(m0 + e) * LDQ + c]) * fast_exp2(gs - Gf[(m0 + e) * LDG + c]));
+                DQ[u] = mma16<bf16>(frag_xk(dAs, LDC, 16 * lbq, 16 * j, lane), b, DQ[u]);
+                if constexpr (DELTA) KP[u] = mma16<bf16>(frag_xk(dLs, LDC, 16 * lbq, 16 * j, lane), b, KP[u]);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float f = fast_exp2(Gf[(16 * lbq + g4 + rr) * LDG + c] - gs);
+                DQ[u][rr] *= f;
+                KP[u][rr] *= f;
+            }
+        }
+        if (lbq < 3) {
+            const int e = 16 * lbq + 15;
+            const float ge = Gf[e * LDG + c];
+            for (int i = lbq + 1; i < 4; ++i) {
+                const int l0 = 16 * i + g4;
+                bf16x4 bq, bk;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float f = fast_exp2(Gf[(l0 + x) * LDG + c] - ge);
+                    bq[x] = from_f32<bf16>(to_f32(Qr[(l0 + x) * LDQ + c]) * f);
+                    bk[x] = from_f32<bf16>(to_f32(Kr[(l0 + x) * LDQ + c]) * f);
+                }
+                KM[u] = mma16<bf16>(frag_kx(dAs, LDC, 16 * lbq, 16 * i, lane), bq, KM[u]);
+                if constexpr (DELTA) KM[u] = mma16<bf16>(frag_kx(dLs, LDC, 16 * lbq, 16 * i, lane), bk, KM[u]);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) KM[u][rr] *= fast_exp2(ge - Gf[(16 * lbq + g4 + rr) * LDG + c]);
+        }
+    }
+    // F5: the diagonal blocks, thread (pb, pc) over its block's 16 rows, exact
+    // factors; handed to the tiles through X in three rounds
+    float aq[16], ap[16], am[16];
+    if (pre) {
+        float gd[16], qd[16], kd[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 16 * pb + rr;
+            gd[rr] = Gf[row * LDG + pc];
+            qd[rr] = to_f32(Qr[row * LDQ + pc]);
+            kd[rr] = to_f32(Kr[row * LDQ + pc]);
+            aq[rr] = ap[rr] = am[rr] = 0.f;
+        }
+#pragma unroll
+        for (int li = 0; li < 16; ++li) {
+            const int l = 16 * pb + li;
+            bf16 ra[16], rl[16];
+            {
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(dAs + l * LDC + 16 * pb);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dAs + l * LDC + 16 * pb + 8);
+                __builtin_memcpy(ra, &a0, 16);
+                __builtin_memcpy(ra + 8, &a1, 16);
+            }
+            if constexpr (DELTA) {
+                const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(dLs + l * LDC + 16 * pb);
+                const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(dLs + l * LDC + 16 * pb + 8);
+                __builtin_memcpy(rl, &b0, 16);
+                __builtin_memcpy(rl + 8, &b1, 16);
+            }
+#pragma unroll
+            for (int mi = 0; mi <= li; ++mi) {
+                const float d = fast_exp2(gd[li] - gd[mi]);
+                const float a = to_f32(ra[mi]) * d;
+                aq[li] = fmaf(a, kd[mi], aq[li]);
+                am[mi] = fmaf(a, qd[li], am[mi]);
+                if constexpr (DELTA) {
+                    if (mi < li) {
+                        const float b = to_f32(rl[mi]) * d;
+                        ap[li] = fmaf(b, kd[mi], ap[li]);
+                        am[mi] = fmaf(b, kd[li], am[mi]);
+                    }
+                }
+            }
+        }
+    }
+    auto hand_over = [&](const float* part, floatx4* acc) {
+        if (pre) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) X[(16 * pb + rr) * LDG + pc] = part[rr];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            const int c = 16 * (NI * (wave & 1) + u) + cl;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[u][rr] += X[(16 * lbq + g4 + rr) * LDG + c];
+        }
+        __syncthreads();
+    };
+    hand_over(aq, DQ);
+    if constexpr (DELTA) hand_over(ap, KP);
+    hand_over(am, KM);
+
+    // F6: dq, dk; dG per element to X; column sums of k 2^(G_C - G) d->K
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        const int c = 16 * (NI * (wave & 1) + u) + cl;
+        const float gC_ = Gf[(kC - 1) * LDG + c];
+        floatx4 tk;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * lbq + g4 + rr;
+            const float G = Gf[l * LDG + c];
+            const float eG = fast_exp2(G), eR = fast_exp2(gC_ - G);
+            const float qv = to_f32(Qr[l * LDQ + c]), kv = to_f32(Kr[l * LDQ + c]);
+            const float a = eG * dQd[u][rr], b = eG * dKd[u][rr], t = eR * dKr[u][rr];
+            const float dqv = a + DQ[u][rr];
+            const float dkv = t - b + KP[u][rr] + KM[u][rr];
+            X[l * LDG + c] = qv * (a + DQ[u][rr]) - kv * (b + t - KP[u][rr] + KM[u][rr]);
+            tk[rr] = kv * t;
+            if (l < tvalid) {
+                dq[(bh * Tlen + t0 + l) * DK + c] = from_f32<bf16>(dqv);
+                dk[(bh * Tlen + t0 + l) * DK + c] = from_f32<bf16>(dkv);
+            }
+        }
+        const float ts = tile_colsum(tk);
+        if (lane < 16) tsum[lbq][c] = ts;
+    }
+    __syncthreads();
+    // F7: dg = reverse prefix sum of dG per channel, plus the chunk-end terms
+    {
+        float suf[16], acc = 0.f;
+        if (pre) {
+#pragma unroll
+            for (int rr = 15; rr >= 0; --rr) {
+                acc += X[(16 * pb + rr) * LDG + pc];
+                suf[rr] = acc;
+            }
+            tot[pb][pc] = acc;
+        }
+        __syncthreads();
+        if (pre) {
+        float later = tsum[0][pc] + tsum[1][pc] + tsum[2][pc] + tsum[3][pc] +
+                      fast_exp2(Gf[(kC - 1) * LDG + pc]) * sdc[pc];
+#pragma unroll
+        for (int b = 1; b < 4; ++b)
+            if (b > pb) later += tot[b][pc];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 16 * pb + rr;
+            if (row < tvalid) dg[(bh * Tlen + t0 + row) * DK + pc] = from_f32<bf16>(suf[rr] + later);
+        }
+        }
+    }
+    if constexpr (DELTA) {
+        if (wave == 7 && lane < tvalid)
+            dbeta[bh * Tlen + t0 + lane] = from_f32<bf16>(colB[lane] + rowB[0][lane] + rowB[1][lane]);
+    }
+}
+
 template <typename T, int DK, int RULE, int GATE>
 hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
 {
@@ -1415,8 +2152,9 @@ hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0, s,
-                       static_cast<const T*>(p.dout), static_cast<const T*>(p.ops), p.gC, p.dsT,
+    hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE, false>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0, s,
+                       static_cast<const T*>(p.dout), static_cast<const T*>(p.ops),
+                       (int64_t)BwdCfg<T, DK>::OPS, p.gC, p.dsT,
                        static_cast<T*>(p.dstates), p.ds0,
                        p.T, nchunks, p.dv);
     hipError_t e = hipGetLastError();
@@ -1438,9 +2176,44 @@ hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int DK, int RULE>
+hipError_t launch_bwd_channel(const ChunkBwdProblem& p, hipStream_t s)
+{
+    using C = BwdCfg<bf16, DK>;
+    const int64_t bh = p.B * p.H;
+    const int64_t nchunks = (p.T + kC - 1) / kC;
+    const bf16* q = static_cast<const bf16*>(p.q);
+    const bf16* k = static_cast<const bf16*>(p.k);
+    const bf16* g = static_cast<const bf16*>(p.g);
+    const bf16* beta = static_cast<const bf16*>(p.beta);
+    if (bh * nchunks > 0) {
+        hipLaunchKernelGGL((bwd_ops_channel_kernel<DK, RULE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s,
+                           q, k, g, beta, static_cast<bf16*>(p.ops), p.gC, p.T, nchunks);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_chain_kernel<bf16, DK, RULE, true>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0,
+                       s, static_cast<const bf16*>(p.dout), static_cast<const bf16*>(p.ops),
+                       (int64_t)(C::OPS + 2 * kC * kC), p.gC, p.dsT, static_cast<bf16*>(p.dstates), p.ds0, p.T,
+                       nchunks, p.dv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || bh * nchunks == 0) return e;
+    hipLaunchKernelGGL((bwd_grad_channel_kernel<DK, RULE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s, q, k,
+                       static_cast<const bf16*>(p.v), g, beta, static_cast<const bf16*>(p.dout),
+                       static_cast<const bf16*>(p.ops), static_cast<const bf16*>(p.states),
+                       static_cast<const bf16*>(p.dstates), static_cast<bf16*>(p.dq), static_cast<bf16*>(p.dk_out),
+                       static_cast<bf16*>(p.dv_out), static_cast<bf16*>(p.dg), static_cast<bf16*>(p.dbeta), p.T,
+                       nchunks, p.dv);
+    return hipGetLastError();
+}
+
 template <typename T, int DK>
 hipError_t bwd_by_rule_gate(const ChunkBwdProblem& p, hipStream_t s)
 {
+    if constexpr (sizeof(T) == 2) {
+        if (p.gate == kGateChannel)
+            return p.rule == kRuleAdd ? launch_bwd_channel<DK, kRuleAdd>(p, s) : launch_bwd_channel<DK, kRuleDelta>(p, s);
+    }
     if (p.rule == kRuleAdd)
         return p.gate == kGateNone ? launch_bwd_t<T, DK, kRuleAdd, kGateNone>(p, s)
                                    : launch_bwd_t<T, DK, kRuleAdd, kGateScalar>(p, s);
@@ -1453,15 +2226,14 @@ hipError_t bwd_by_rule_gate(const ChunkBwdProblem& p, hipStream_t s)
 bool chunk_bwd_supported(int dk, int dv, int rule, int gate, int dtype)
 {
     (void)rule;
-    if (gate == kGateChannel) return false;
     if (dtype == kBF16) return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
-    return dk == 64 && (dv == 64 || dv == 128);
+    return gate != kGateChannel && dk == 64 && (dv == 64 || dv == 128);
 }
 
-size_t chunk_bwd_ops_bytes(int dk, int dtype)
+size_t chunk_bwd_ops_bytes(int dk, int gate, int dtype)
 {
     const size_t esz = dtype == kBF16 ? 2 : 4;
-    return (size_t)(3 * kC * kC + 3 * kC * dk) * esz;
+    return (size_t)(3 * kC * kC + 3 * kC * dk + (gate == kGateChannel ? 2 * kC * kC : 0)) * esz;
 }
 
 hipError_t launch_chunk_bwd(const ChunkBwdProblem& p, hipStream_t s)

@@ -399,10 +399,14 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 //            chunk
 // so each LDS region is refilled while the other phase runs.
 // ===========================================================================
-template <int DK, int RULE, int DVB>
+//
+// With SAVE the state waves also store S_r, the state entering chunk r, to
+// states[b, h, r] ([dk][dv], bf16) at the top of every chunk.
+template <int DK, int RULE, int DVB, bool SAVE>
 __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const bf16* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0,
-    bf16* __restrict__ o, float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks)
+    bf16* __restrict__ o, float* s_final, bf16* __restrict__ states, int64_t Tlen, int64_t nchunks, int DV,
+    int nblocks)
 {
     using W = SplitWs<DK>;
     constexpr int NSW = DVB / 16;                // state waves, 16 value columns each
@@ -450,6 +454,13 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
         for (int64_t c = 0; c < nchunks; ++c) {
             const int ln = opaque(lane);
             const int cl = ln & 15, g4 = 4 * (ln >> 4);
+            if constexpr (SAVE) {
+                bf16* sr = states + ((bh * nchunks + c) * DK + g4) * DV + vb * DVB + n0 + cl;
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) sr[(16 * db + rr) * DV] = from_f32<bf16>(S[db][rr]);
+            }
             // ---- phase 1: R = V - Kd S_r ; Z = Tb R ; O^T = S_r^T Qd^T ----------------
             floatx4 R[NL], Z[NL], Ot[NL];
 #pragma unroll
@@ -642,7 +653,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
 }
 
 template <int DK, int RULE, int GATE>
-hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
+hipError_t launch_split(const ChunkProblem& p, bf16* states, hipStream_t s)
 {
     const int64_t nchunks = (p.T + kC - 1) / kC;
     const int64_t bh = p.B * p.H;
@@ -666,17 +677,23 @@ hipError_t launch_split(const ChunkProblem& p, hipStream_t s)
     // (fewer 64-column blocks than CUs) the blocks are 32 columns wide, which
     // doubles the number of independent chains; each staged tile is then read
     // by twice as many workgroups (mostly from L2).
-    if (bh * (p.dv / 64) < ncu) {
-        const int nblocks = (int)(bh * (p.dv / 32));
-        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 32>), dim3((unsigned)nblocks), dim3(6 * 64), 0, s,
-                           static_cast<const bf16*>(p.v), ws, p.s0, static_cast<bf16*>(p.o), p.s_final,
-                           p.T, nchunks, p.dv, nblocks);
-    } else {
-        const int nblocks = (int)(bh * (p.dv / 64));
-        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 64>), dim3((unsigned)nblocks), dim3(8 * 64), 0, s,
-                           static_cast<const bf16*>(p.v), ws, p.s0, static_cast<bf16*>(p.o), p.s_final,
-                           p.T, nchunks, p.dv, nblocks);
-    }
+    const bool narrow = bh * (p.dv / 64) < ncu;
+    const int nblocks = (int)(bh * (p.dv / (narrow ? 32 : 64)));
+    const dim3 grid((unsigned)nblocks);
+    const bf16* v = static_cast<const bf16*>(p.v);
+    bf16* o = static_cast<bf16*>(p.o);
+    if (narrow && states)
+        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 32, true>), grid, dim3(6 * 64), 0, s, v, ws, p.s0, o,
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+    else if (narrow)
+        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 32, false>), grid, dim3(6 * 64), 0, s, v, ws, p.s0, o,
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+    else if (states)
+        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 64, true>), grid, dim3(8 * 64), 0, s, v, ws, p.s0, o,
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+    else
+        hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 64, false>), grid, dim3(8 * 64), 0, s, v, ws, p.s0, o,
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
     return hipGetLastError();
 }
 
@@ -696,18 +713,24 @@ size_t chunk_split_workspace_bytes(const ChunkProblem& p)
 }
 
 template <int DK>
-hipError_t split_by_rule_gate(const ChunkProblem& p, hipStream_t s)
+hipError_t split_by_rule_gate(const ChunkProblem& p, bf16* states, hipStream_t s)
 {
     if (p.gate == kGateChannel)
-        return p.rule == kRuleDelta ? launch_split<DK, kRuleDelta, kGateChannel>(p, s)
-                                    : launch_split<DK, kRuleAdd, kGateChannel>(p, s);
-    return p.rule == kRuleDelta ? launch_split<DK, kRuleDelta, kGateScalar>(p, s)
-                                : launch_split<DK, kRuleAdd, kGateScalar>(p, s);
+        return p.rule == kRuleDelta ? launch_split<DK, kRuleDelta, kGateChannel>(p, states, s)
+                                    : launch_split<DK, kRuleAdd, kGateChannel>(p, states, s);
+    return p.rule == kRuleDelta ? launch_split<DK, kRuleDelta, kGateScalar>(p, states, s)
+                                : launch_split<DK, kRuleAdd, kGateScalar>(p, states, s);
 }
 
 hipError_t launch_chunk_split(const ChunkProblem& p, hipStream_t s)
 {
-    return p.dk == 64 ? split_by_rule_gate<64>(p, s) : split_by_rule_gate<128>(p, s);
+    return p.dk == 64 ? split_by_rule_gate<64>(p, nullptr, s) : split_by_rule_gate<128>(p, nullptr, s);
+}
+
+hipError_t launch_chunk_split_save(const ChunkProblem& p, void* states, hipStream_t s)
+{
+    bf16* st = static_cast<bf16*>(states);
+    return p.dk == 64 ? split_by_rule_gate<64>(p, st, s) : split_by_rule_gate<128>(p, st, s);
 }
 
 }  // namespace linattn

@@ -89,12 +89,15 @@ hipError_t launch_chunk_pipe(const ChunkProblem& p, hipStream_t stream);
 bool chunk_split_supported(const ChunkProblem& p);
 size_t chunk_split_workspace_bytes(const ChunkProblem& p);
 hipError_t launch_chunk_split(const ChunkProblem& p, hipStream_t stream);
+// The same, also writing the state entering every chunk, states
+// [B,H,nchunks,dk,dv] bf16 (for the backward pass).
+hipError_t launch_chunk_split_save(const ChunkProblem& p, void* states, hipStream_t stream);
 
-// Backward pass of the chunk form (gate NONE or SCALAR, chunk 64): given the
-// incoming state of every chunk (states), the per-chunk operands of the
-// reverse state pass are prepared, the gradients of the outgoing states are
-// carried newest chunk first (dstates, ds0), and every chunk's gradients are
-// then formed independently.
+// Backward pass of the chunk form (chunk 64; the per-channel gate with bf16
+// tokens): given the incoming state of every chunk (states), the per-chunk
+// operands of the reverse state pass are prepared, the gradients of the
+// outgoing states are carried newest chunk first (dstates, ds0), and every
+// chunk's gradients are then formed independently.
 struct ChunkBwdProblem {
     int64_t B, H, T;
     int dk, dv, rule, gate, dtype;
@@ -104,11 +107,11 @@ struct ChunkBwdProblem {
     void *dq, *dk_out, *dv_out, *dg, *dbeta;
     float* ds0;                   // [B,H,dk,dv] or NULL
     void* ops;                    // [B,H,N] chunk operand blocks (chunk_bwd_ops_bytes each)
-    float* gC;                    // [B,H,N] exp of the chunk's total log-gate
+    float* gC;                    // [B,H,N] exp of the chunk's total log-gate ([B,H,N,dk] per channel)
     void* dstates;                // [B,H,N,dk,dv] token type, gradient w.r.t. S leaving chunk r
 };
 bool chunk_bwd_supported(int dk, int dv, int rule, int gate, int dtype);
-size_t chunk_bwd_ops_bytes(int dk, int dtype);
+size_t chunk_bwd_ops_bytes(int dk, int gate, int dtype);
 hipError_t launch_chunk_bwd(const ChunkBwdProblem& p, hipStream_t stream);
 
 }  // namespace linattn

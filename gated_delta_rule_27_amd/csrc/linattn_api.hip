@@ -215,15 +215,31 @@ linattn_status validate_train(const linattn_chunk_args* a, ChunkProblem* p)
     p->B = a->B; p->H = a->H; p->T = a->T;
     p->dk = a->dk; p->dv = a->dv; p->chunk = 64;
     p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
+    if (p->gate == kGateChannel) return chunk_split_supported(*p) ? LINATTN_OK : LINATTN_ERR_UNSUPPORTED;
     return chunk_fused_supported(*p) ? LINATTN_OK : LINATTN_ERR_UNSUPPORTED;
 }
 
+// The state-saving forward: the two-kernel path for the per-channel gate (its
+// staged operands in the workspace), the single-pass kernel otherwise.
+size_t fwd_save_workspace_bytes(const ChunkProblem& p)
+{
+    return p.gate == kGateChannel ? chunk_split_workspace_bytes(p) : 0;
+}
+hipError_t launch_fwd_save(ChunkProblem p, void* states, void* ws, size_t wsb, hipStream_t s)
+{
+    if (p.gate != kGateChannel) return launch_chunk_fused_save(p, states, s);
+    p.workspace = ws;
+    p.workspace_bytes = wsb;
+    return launch_chunk_split_save(p, states, s);
+}
+
 // Backward workspace, 256-byte aligned pieces: chunk operands [B,H,N] blocks,
-// exp(G_C) [B,H,N], dstates [B,H,N,dk,dv], then (states not given) the
-// recomputed states [B,H,N,dk,dv] and a forward output [B,H,T,dv], all in the
-// token type except exp(G_C).
+// exp(G_C) [B,H,N] (per channel: [B,H,N,dk]), dstates [B,H,N,dk,dv], then
+// (states not given) the recomputed states [B,H,N,dk,dv], a forward output
+// [B,H,T,dv] and the forward's own workspace, all in the token type except
+// exp(G_C).
 struct BwdLayout {
-    size_t ops, gc, dst, st, o, total;
+    size_t ops, gc, dst, st, o, fws, total;
 };
 BwdLayout bwd_layout(const ChunkProblem& p, bool states_given)
 {
@@ -232,11 +248,12 @@ BwdLayout bwd_layout(const ChunkProblem& p, bool states_given)
     const size_t esz = p.dtype == kBF16 ? 2 : 4;
     BwdLayout l{};
     l.ops = 0;
-    l.gc = up(bh * nch * chunk_bwd_ops_bytes(p.dk, p.dtype));
-    l.dst = l.gc + up(bh * nch * 4);
+    l.gc = up(bh * nch * chunk_bwd_ops_bytes(p.dk, p.gate, p.dtype));
+    l.dst = l.gc + up(bh * nch * (p.gate == kGateChannel ? (size_t)p.dk : 1) * 4);
     l.st = l.dst + up(bh * nch * p.dk * p.dv * esz);
     l.o = l.st + (states_given ? 0 : up(bh * nch * p.dk * p.dv * esz));
-    l.total = l.o + (states_given ? 0 : up(bh * (size_t)p.T * p.dv * esz));
+    l.fws = l.o + (states_given ? 0 : up(bh * (size_t)p.T * p.dv * esz));
+    l.total = l.fws + (states_given ? 0 : up(fwd_save_workspace_bytes(p)));
     return l;
 }
 
@@ -453,7 +470,8 @@ extern "C" {
 
 linattn_status linattn_chunk_fwd_save(const linattn_chunk_args* a, const void* q, const void* k,
                                       const void* v, const void* g, const void* beta, const float* s0,
-                                      void* o, float* s_final, void* states, void* stream)
+                                      void* o, float* s_final, void* states, void* workspace,
+                                      size_t workspace_bytes, void* stream)
 {
     ChunkProblem p{};
     linattn_status st = validate_train(a, &p);
@@ -467,9 +485,14 @@ linattn_status linattn_chunk_fwd_save(const linattn_chunk_args* a, const void* q
     }
     st = check_states(p, s0, s_final);
     if (st != LINATTN_OK) return st;
+    const size_t need = fwd_save_workspace_bytes(p);
+    if (p.T > 0 && need > 0) {
+        if (!workspace || workspace_bytes < need) return LINATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+    }
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = s0; p.o = o; p.s_final = s_final;
-    return launch_chunk_fused_save(p, states, static_cast<hipStream_t>(stream)) == hipSuccess
+    return launch_fwd_save(p, states, workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
                ? LINATTN_OK : LINATTN_ERR_LAUNCH;
 }
 
@@ -493,9 +516,9 @@ linattn_status linattn_chunk_bwd(const linattn_chunk_args* a, const void* q, con
     if (p.T > 0) {
         st = check_pointers(p.rule, p.gate, q, k, v, g, beta, q, dout);
         if (st != LINATTN_OK) return st;
-        // gradient outputs: dg exactly for the scalar gate, dbeta for the delta rule
+        // gradient outputs: dg exactly for a gate, dbeta for the delta rule
         if (!dq || !dk || !dv) return LINATTN_ERR_NULL;
-        if ((p.gate == kGateScalar) != (dg != nullptr)) return dg ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
+        if ((p.gate != kGateNone) != (dg != nullptr)) return dg ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
         if ((p.rule == kRuleDelta) != (dbeta != nullptr)) return dbeta ? LINATTN_ERR_ARG : LINATTN_ERR_NULL;
         const void* outs[] = {dq, dk, dv, dg, dbeta, states};
         for (const void* x : outs)
@@ -517,7 +540,7 @@ linattn_status linattn_chunk_bwd(const linattn_chunk_args* a, const void* q, con
         ChunkProblem fp = p;
         fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta;
         fp.s0 = s0; fp.o = ws + l.o; fp.s_final = nullptr;
-        if (launch_chunk_fused_save(fp, ws + l.st, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
+        if (launch_fwd_save(fp, ws + l.st, ws + l.fws, l.total - l.fws, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
         sts = ws + l.st;
     }
     ChunkBwdProblem b{p.B, p.H, p.T, p.dk, p.dv, p.rule, p.gate, p.dtype,

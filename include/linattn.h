@@ -235,15 +235,19 @@ linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args *a,
  *            or zero), rounded once from the fp32 state the forward carries
  *            (the backward uses it as matrix-core operands of that dtype);
  *            caller-owned.
- * Supported: gate NONE or SCALAR, chunk 64, bf16 tokens with dk, dv in
- * {64, 128}, fp32 tokens with dk = 64 (LINATTN_ERR_UNSUPPORTED otherwise);
- * the same 2 GiB limit.  No workspace.
+ *   workspace: at least linattn_chunk_workspace_bytes(a) bytes, 16-byte
+ *            aligned, for the per-channel gate (the two-kernel path's staged
+ *            chunk operands); not read otherwise (NULL allowed).
+ * Supported: chunk 64; bf16 tokens with dk, dv in {64, 128} (every gate);
+ * fp32 tokens with dk = 64 and dv in {64, 128}, gate NONE or SCALAR
+ * (LINATTN_ERR_UNSUPPORTED otherwise); the same 2 GiB limit.
  */
 linattn_status linattn_chunk_fwd_save(const linattn_chunk_args *a,
                                       const void *q, const void *k, const void *v,
                                       const void *g, const void *beta,
                                       const float *s0, void *o, float *s_final,
-                                      void *states, void *stream);
+                                      void *states, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /*
  * Device workspace, in bytes, of linattn_chunk_bwd: the per-chunk operands of
@@ -272,13 +276,17 @@ size_t linattn_chunk_bwd_workspace_bytes(const linattn_chunk_args *a, int states
  *   dsT      [B,H,dk,dv] fp32, or NULL for zero
  *   dq, dk   [B,H,T,dk] token dtype (written)
  *   dv       [B,H,T,dv] token dtype (written)
- *   dg       [B,H,T] token dtype for the SCALAR gate, NULL for NONE (written)
+ *   dg       [B,H,T] token dtype for the SCALAR gate, [B,H,T,dk] for the
+ *            CHANNEL gate, NULL for NONE (written)
  *   dbeta    [B,H,T] token dtype for DELTA, NULL for ADD (written)
  *   ds0      [B,H,dk,dv] fp32, or NULL (written)
  *   workspace: at least linattn_chunk_bwd_workspace_bytes(a, states != NULL)
  *            bytes, 16-byte aligned
- * Supported: as linattn_chunk_fwd_save.  Accumulation is fp32; matrix-core
- * operands are in the token dtype.  Inputs are not normalised or mapped here:
+ * Supported: as linattn_chunk_fwd_save.  For the CHANNEL gate ("Gated
+ * Linear Attention (GLA)" and "Kimi Delta Attention (KDA)" on the same page:
+ * the decay is diagonal, one factor per key channel) the per-channel decay
+ * stays inside every score's sum over key channels, and dg is per channel.
+ * Accumulation is fp32; matrix-core operands are in the token dtype.  Inputs are not normalised or mapped here:
  * these are the gradients with respect to the values the kernels received.
  */
 linattn_status linattn_chunk_bwd(const linattn_chunk_args *a,

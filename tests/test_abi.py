@@ -149,7 +149,8 @@ def test_backward_validation(lib):
                                      dbeta, None, ws, wsb, None)
 
     assert lib.linattn_chunk_bwd(None, *([None] * 16), 0, None) == 1
-    assert bwd(mk(gate="channel")) == 3                     # the per-channel gate has no backward
+    assert bwd(mk(gate="channel", dtype="fp32")) == 3       # the per-channel gate: bf16 tokens only
+    assert bwd(mk(gate="channel"), dg=None) == 1             # the per-channel gate needs dg
     assert bwd(mk(chunk=32)) == 3
     assert bwd(mk(dtype="fp32", dk=128)) == 3
     assert bwd(mk(), dg=None) == 1                           # scalar gate needs dg
@@ -162,12 +163,19 @@ def test_backward_validation(lib):
     given = lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk()), 1)
     assert need > given > 0
     assert bwd(mk(), ws=F, wsb=need - 1) == 4
-    assert lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk(gate="channel")), 0) == 0
+    ch_need = lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk(gate="channel")), 0)
+    ch_given = lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk(gate="channel")), 1)
+    assert ch_need > ch_given > given                        # wider operand blocks, the forward's workspace
+    assert lib.linattn_chunk_bwd_workspace_bytes(ctypes.byref(mk(gate="channel", dtype="fp32")), 0) == 0
     assert bwd(mk(B=0)) == 0                                 # nothing to do
     # forward keeping the chunk states
-    fs = lambda a, states=F: lib.linattn_chunk_fwd_save(ctypes.byref(a), F, F, F, F, F, None, F, None, states, None)
+    fs = lambda a, states=F, ws=None, wsb=0: lib.linattn_chunk_fwd_save(ctypes.byref(a), F, F, F, F, F, None, F,
+                                                                         None, states, ws, wsb, None)
     assert fs(mk(), states=None) == 1
-    assert fs(mk(gate="channel")) == 3
+    assert fs(mk(gate="channel", dtype="fp32")) == 3
+    assert fs(mk(gate="channel")) == 4                       # the per-channel gate needs a workspace
+    ch_fws = lib.linattn_chunk_workspace_bytes(ctypes.byref(mk(gate="channel")))
+    assert ch_fws > 0 and fs(mk(gate="channel"), ws=F, wsb=ch_fws - 1) == 4
     assert fs(mk(), states=F + 4) == 3
     # Gated DeltaProduct backward
     da = lambda **kw: bd.deltaproduct_args(**{**dict(B=1, H=1, T=32, nh=2, dk=64, dv=64, gate="scalar",

@@ -164,3 +164,77 @@ def test_gdn_full_size_sampled():
         errs = {n: rel_l2(host(out[n][b, h]), ref[n][i, 0]) for n in NAMES}
         note(f"    head ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+# ---- per-key-channel gate (GLA decay with the add rule, KDA with the delta rule) ----
+CHANNEL = [(dk, dv, rule) for (dk, dv) in ((128, 128), (64, 64), (64, 128), (128, 64))
+           for rule in ("add", "delta")]
+
+
+@pytest.mark.parametrize("dk,dv,rule", CHANNEL)
+def test_channel_small_ragged(dk, dv, rule):
+    case = syn.Case("bwd_chan", 2, 2, 200, dk, dv, rule, "channel", "bf16", gate_scale=1 / 16, s0_std=0.3,
+                    case_id=146)
+    check_bwd(case)
+
+
+@pytest.mark.parametrize("T", [1, 16, 63, 65, 130])
+def test_channel_lengths(T):
+    case = syn.Case("bwd_chan_len", 1, 2, T, 128, 128, "delta", "channel", "bf16", gate_scale=0.25,
+                    s0_std=0.2, case_id=147)
+    check_bwd(case)
+
+
+@pytest.mark.parametrize("gate_scale", [1.0, 12.0])
+def test_channel_decay_laws(gate_scale):
+    # gate_scale 1: the workloads' law per channel; 12: per-token log-decays
+    # near -10, so whole 16-row blocks decay past the fp32 range
+    case = syn.Case("bwd_chan_law", 1, 2, 192, 128, 128, "delta", "channel", "bf16", gate_scale=gate_scale,
+                    s0_std=0.3, case_id=148)
+    check_bwd(case)
+
+
+def test_channel_saved_states_equal_recomputed():
+    case = syn.Case("bwd_chan_saved", 1, 3, 150, 128, 128, "delta", "channel", "bf16", gate_scale=0.25,
+                    s0_std=0.3, case_id=149)
+    a = check_bwd(case, use_states=True)
+    x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
+    b = run_bwd(case, x, gr, use_states=False)
+    for n in NAMES:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), f"{n}: saved and recomputed states differ"
+
+
+def test_channel_equal_channels_match_scalar_gate():
+    # every channel with the same log-gate is the scalar gate: the same dq, dk,
+    # dv, dbeta, ds0, and the channel gradients of dg sum to the scalar one
+    import gated_delta_rule_27_amd as la
+    case = syn.Case("bwd_chan_eq", 1, 2, 140, 128, 128, "delta", "scalar", "bf16", gate_scale=0.3, s0_std=0.3,
+                    case_id=150)
+    x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
+    d = lambda a: dev(a, case.dtype)
+    gs = d(x["g"])
+    gc = gs[..., None].expand(*gs.shape, case.dk).contiguous()
+    common = (d(x["q"]), d(x["k"]), d(x["v"]))
+    a = la.chunk_bwd(*common, gs, d(x["beta"]), d(gr["do"]), dev_state(x["s0"]), dev_state(gr["dsT"]),
+                     rule="delta", gate="scalar")
+    b = la.chunk_bwd(*common, gc, d(x["beta"]), d(gr["do"]), dev_state(x["s0"]), dev_state(gr["dsT"]),
+                     rule="delta", gate="channel")
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dbeta", "ds0"):
+        e = rel_l2(host(b[n]), host(a[n]))
+        note(f"    {n} rel L2 {e:.2e}")
+        assert e <= TOL["bf16"], n
+    e = rel_l2(host(b["dg"]).sum(axis=-1), host(a["dg"]))
+    note(f"    dg (summed over channels) rel L2 {e:.2e}")
+    assert e <= TOL["bf16"]
+
+
+def test_channel_deterministic():
+    case = syn.Case("bwd_chan_det", 1, 4, 300, 128, 128, "delta", "channel", "bf16", gate_scale=0.2,
+                    s0_std=0.2, case_id=151)
+    x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
+    a, b = run_bwd(case, x, gr), run_bwd(case, x, gr)
+    for n in NAMES:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), f"{n} differs between runs"
