@@ -266,6 +266,8 @@ def bwd_alg_bytes(B, H, T, dk, dv, s, rule, gate, states):
     per_tok = (2 * dk + 2 * dv) * s + (2 * dk + dv) * s
     if gate == "scalar":
         per_tok += 2 * s
+    elif gate == "channel":
+        per_tok += 2 * dk * s
     if rule == "delta":
         per_tok += 2 * s
     nch = (T + 63) // 64
@@ -296,10 +298,15 @@ def time_backward(la, syn, case, dev, steps, warmup=2):
              "ds0": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)}
     ws = torch.empty(la.chunk_bwd_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate,
                                                   states_given=False), dtype=torch.uint8, device=dev)
+    fws = None
+    if case.gate == "channel":
+        fws = torch.empty(la.chunk_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate),
+                          dtype=torch.uint8, device=dev)
     args = (x["q"], x["k"], x["v"], x["g"], x["beta"])
 
     def fwd():
-        la.chunk_fwd_save(*args, rule=case.rule, gate=case.gate, out=out, states=states, return_state=False)
+        la.chunk_fwd_save(*args, rule=case.rule, gate=case.gate, out=out, states=states, return_state=False,
+                          workspace=fws)
 
     def bwd_saved():
         la.chunk_bwd(*args, do, states=states, rule=case.rule, gate=case.gate, workspace=ws, grads=grads)
@@ -322,7 +329,11 @@ def time_backward(la, syn, case, dev, steps, warmup=2):
     ms_f, ms_b, ms_r = timed(fwd), timed(bwd_saved), timed(bwd_recompute)
     abytes = bwd_alg_bytes(B, H, T, dk, dv, 2, case.rule, case.gate, True)
     aflops = bwd_nominal_flops(B, H, T, dk, dv)
-    return {"workload": f"gdn training passes B={B} H={H} T={T} dk={dk} dv={dv} bf16 (backward "
+    kind = {("delta", "scalar"): "gdn", ("delta", "channel"): "kda", ("add", "channel"): "gla"}.get(
+        (case.rule, case.gate), f"{case.rule}/{case.gate}")
+    path = ("split+save; bwd_ops_channel + bwd_chain + bwd_grad_channel" if case.gate == "channel"
+            else "fused+save; bwd_ops + bwd_chain + bwd_grad")
+    return {"workload": f"{kind} training passes B={B} H={H} T={T} dk={dk} dv={dv} bf16 (backward "
                         f"from dO, chunk states saved by the forward)",
             "fwd_save_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4), "bwd_recompute_ms": round(ms_r, 4),
             "ms_per_step": round(ms_f + ms_b, 4),
@@ -330,7 +341,7 @@ def time_backward(la, syn, case, dev, steps, warmup=2):
             "bwd_hbm_frac": round(abytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "bwd_mfma_frac": round(aflops / (ms_b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "bwd_alg_bytes": abytes, "bwd_nominal_flops": aflops,
-            "path": "fused+save; bwd_ops + bwd_chain + bwd_grad", "steps": steps}
+            "path": path, "steps": steps}
 
 
 def time_deltaproduct_bwd(la, syn, case, dev, steps, warmup=2):
@@ -395,9 +406,9 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm,cfg3bwd,gdp2bwd",
+    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm,cfg3bwd,gdp2bwd,cfg4bwd",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm, cfg3bwd, gdp2bwd), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm, cfg3bwd, gdp2bwd, cfg4bwd), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -475,6 +486,8 @@ def main():
             others.append(time_normalized(la, syn, syn.CFG2, dev, steps=10))
         elif name == "cfg3bwd":
             others.append(time_backward(la, syn, syn.CFG3, dev, steps=5))
+        elif name == "cfg4bwd":
+            others.append(time_backward(la, syn, syn.CFG4, dev, steps=3))
         elif name == "gdp2bwd":
             others.append(time_deltaproduct_bwd(la, syn, syn.GDP2, dev, steps=5))
         else:

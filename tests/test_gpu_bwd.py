@@ -1,7 +1,8 @@
 """Parity of the chunkwise backward pass (HIP, through the C ABI) with the
-fp64 oracle's reverse-mode recurrence: every rule, gate none/scalar, both
-dtypes and head sizes, ragged lengths, initial state and final-state gradient,
-the forward that keeps the chunk states, and a sampled full-size workload."""
+fp64 oracle's reverse-mode recurrence: every rule and gate (the per-channel
+gate with bf16 tokens), both dtypes and head sizes, ragged lengths, initial
+state and final-state gradient, the forward that keeps the chunk states, and
+sampled full-size workloads (GDN and KDA)."""
 import numpy as np
 import pytest
 import torch
@@ -238,3 +239,46 @@ def test_channel_deterministic():
     for n in NAMES:
         if a[n] is not None:
             assert torch.equal(a[n], b[n]), f"{n} differs between runs"
+
+
+@pytest.mark.timeout(900)
+def test_kda_full_size_sampled():
+    # the KDA workload's shape (B1 H32 T262144 d128), every head on the GPU.
+    # The gradients of the last n tokens depend on the earlier ones only
+    # through the state entering them, so the oracle checks them exactly: its
+    # forward over the first T - n tokens gives that state, its backward over
+    # the last n tokens the gradients (the loss has no dS_T term).
+    import gated_delta_rule_27_amd as la
+    case = syn.CFG4
+    n = 300
+    heads = [(0, 0), (0, 31)]
+    note(f"[bwd full] {case.name}: inputs on the GPU, heads {heads} from the host generator")
+    xs = syn.chunk_inputs(case, heads=heads)
+    gs = syn.grad_inputs(case, heads=heads)
+    full = syn.chunk_inputs_torch(case, "cuda")
+    gfull = syn.grad_inputs_torch(case, "cuda")
+    for i, (b, h) in enumerate(heads):
+        for key in ("q", "k", "v", "g", "beta"):
+            full[key][b, h] = dev(xs[key][i], case.dtype)
+        gfull["do"][b, h] = dev(gs["do"][i], case.dtype)
+    note(f"[bwd full] {case.name}: GPU backward (states recomputed)")
+    out = la.chunk_bwd(full["q"], full["k"], full["v"], full["g"], full["beta"], gfull["do"],
+                       rule=case.rule, gate=case.gate)
+    torch.cuda.synchronize()
+    for nm in NAMES:
+        if out[nm] is not None:
+            assert torch.isfinite(out[nm]).all(), nm
+    cut = case.T - n
+    head = lambda a, sl: None if a is None else np.ascontiguousarray(a[:, None, sl])
+    note(f"[bwd full] {case.name}: oracle forward over {cut} tokens, backward over the last {n}")
+    _, s_cut = oracle.recurrence(head(xs["q"], slice(0, cut)), head(xs["k"], slice(0, cut)),
+                                 head(xs["v"], slice(0, cut)), head(xs["g"], slice(0, cut)),
+                                 head(xs["beta"], slice(0, cut)), None, rule=case.rule, gate=case.gate)
+    tail = slice(cut, None)
+    ref = oracle.recurrence_bwd(head(xs["q"], tail), head(xs["k"], tail), head(xs["v"], tail),
+                                head(xs["g"], tail), head(xs["beta"], tail), s_cut, head(gs["do"], tail), None,
+                                rule=case.rule, gate=case.gate)
+    for i, (b, h) in enumerate(heads):
+        errs = {nm: rel_l2(host(out[nm][b, h, cut:]), ref[nm][i, 0]) for nm in NAMES if nm != "ds0"}
+        note(f"    head ({b},{h}) last {n} tokens: " + " ".join(f"{nm}={e:.2e}" for nm, e in errs.items()))
+        assert all(e <= TOL["bf16"] for e in errs.values()), errs
