@@ -47,6 +47,11 @@ namespace {
 constexpr int kC = 64;
 constexpr int kNT = 512;                 // 8 waves
 constexpr float kLog2eB = 1.4426950408889634f;   // log2(e): channel gates are kept in base 2
+// A diagonal 16x16 block of a per-channel decay splits at its middle row m7,
+// 2^(G_l - G_m) = 2^(G_l - G_m7) 2^(G_m7 - G_m), each factor within 2^(+-kSpanMax)
+// when every |G_l - G_m7| of the block is: then the block is one matrix-core
+// product like the others; past that it is summed element by element.
+constexpr float kSpanMax = 120.f;
 typedef __attribute__((__vector_size__(16))) int i4;
 
 template <typename T> using F16 = typename Frag16<T>::type;
@@ -151,6 +156,21 @@ struct BwdCfg {
     static constexpr int O_AQT = 0, O_TBT = kC * kC, O_TB = 2 * kC * kC, O_KR = 3 * kC * kC,
                          O_QDT = O_KR + kC * DK, O_NKDT = O_QDT + DK * kC;
 };
+
+// 16 consecutive rows of one column of a [rows][ld] bf16 matrix, rows from
+// row0; rows at or past nvalid read as 0.  The addresses are clamped instead
+// of branched around, so the 16 loads issue back to back.
+__device__ __forceinline__ void load_col16(float* x, const bf16* base, int ld, int row0, int nvalid)
+{
+    bf16 raw[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int row = row0 + rr < nvalid ? row0 + rr : nvalid - 1;
+        raw[rr] = base[(int64_t)row * ld];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) x[rr] = row0 + rr < nvalid ? to_f32(raw[rr]) : 0.f;
+}
 
 // T = (I + diag(beta) L)^-1 and Tb = T diag(beta) from the strict lower
 // triangular L in LDS (Tm must hold zeros above its diagonal blocks); every
@@ -361,8 +381,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q
 //   k_l in place of q_l (m < l).
 // Off the diagonal 16x16 blocks (row l in block i, key m in block j < i) the
 // factor splits at row s = 16 i - 1 into 2^(G_l - G_s) 2^(G_s - G_m), both at
-// most 1 for decays, applied to the operands of one matrix-core product; the
-// diagonal blocks are summed element by element with the exact factor.
+// most 1 for decays, applied to the operands of one matrix-core product; a
+// diagonal block splits at its middle row when both factors stay within
+// 2^(+-kSpanMax), else it is summed element by element with the exact factor.
 // Stored per chunk: A^T, Tb^T, Tb, ->K, <-Q^T, -<-K^T (the reverse state pass,
 // as bwd_ops_kernel), T and L (the gradient pass), and 2^(G_C) per channel.
 // ============================================================================
@@ -382,7 +403,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __r
     __shared__ __align__(16) bf16 CC[4 * kC * LDC];    // Aq, Lm, Tm, Tb
     __shared__ __align__(16) float Gf[kC * LDG];        // G, base 2
     __shared__ __align__(16) float tot[4][DK];
-    __shared__ float bet[kC];
+    __shared__ float bet[kC], spanw[8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -418,32 +439,50 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __r
     const bool pre = tid < 4 * DK;
     float Gl[16];
     if (pre) {
+        load_col16(Gl, g + (bh * Tlen + t0) * DK + pc, DK, 16 * pb, tvalid);
         float acc = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            const int row = 16 * pb + rr;
-            if (row < tvalid) acc += to_f32(g[(bh * Tlen + t0 + row) * DK + pc]) * kLog2eB;
+            acc += Gl[rr] * kLog2eB;
             Gl[rr] = acc;
         }
         tot[pb][pc] = acc;
     }
     __syncthreads();
+    float span = 0.f;
     if (pre) {
         float off = 0.f;
 #pragma unroll
         for (int b = 0; b < 3; ++b)
             if (b < pb) off += tot[b][pc];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) Gf[(16 * pb + rr) * LDG + pc] = off + Gl[rr];
+        for (int rr = 0; rr < 16; ++rr) {
+            Gf[(16 * pb + rr) * LDG + pc] = off + Gl[rr];
+            span = fmaxf(span, fabsf(Gl[rr] - Gl[7]));
+        }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) span = fmaxf(span, shfl_xor(span, o));
+    if (lane == 0) spanw[wave] = span;
     __syncthreads();
+    bool safe[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float sp = spanw[b * (DK / 64)];
+        if constexpr (DK == 128) sp = fmaxf(sp, spanw[2 * b + 1]);
+        safe[b] = sp <= kSpanMax;
+    }
 
-    // off-diagonal score tiles: wave p takes pair p of (1,0)(2,0)(2,1)(3,0)(3,1)(3,2),
-    // A and L together (their query-side factors are the same)
-    if (wave < 6) {
-        const int i = wave < 1 ? 1 : (wave < 3 ? 2 : 3);
-        const int j = wave - i * (i - 1) / 2;
-        const int s = 16 * i - 1;
+    // score tiles, A and L together (their query-side factors are the same):
+    // jobs 0-5 the off-diagonal pairs (1,0)(2,0)(2,1)(3,0)(3,1)(3,2), split at
+    // the row before the query block; jobs 6-9 the diagonal blocks, split at
+    // their middle row
+    for (int job = wave; job < 10; job += 8) {
+        const bool diag = job >= 6;
+        const int i = diag ? job - 6 : (job < 1 ? 1 : (job < 3 ? 2 : 3));
+        const int j = diag ? i : job - i * (i - 1) / 2;
+        if (diag && !safe[i]) continue;
+        const int s = diag ? 16 * i + 7 : 16 * i - 1;
         const int xa = 16 * i + (lane & 15), xb = 16 * j + (lane & 15);
         floatx4 accA = zero4(), accL = zero4();
 #pragma unroll
@@ -466,12 +505,23 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __r
             accA = mma16<bf16>(fq, fb, accA);
             if constexpr (DELTA) accL = mma16<bf16>(fk, fb, accL);
         }
+        if (diag) {
+            // result (l = 16 i + 4(lane/16) + rr, m = 16 i + lane%16): causal / strict
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int lo = 4 * (lane >> 4) + rr, mo = lane & 15;
+                accA[rr] = mo <= lo ? accA[rr] : 0.f;
+                accL[rr] = mo < lo ? accL[rr] : 0.f;
+            }
+        }
         put(Aq, LDC, 16 * i, 16 * j, accA, lane);
         if constexpr (DELTA) put(Lm, LDC, 16 * i, 16 * j, accL, lane);
     }
-    // diagonal blocks element by element: item = (block b, l >= m inside it)
+    // diagonal blocks past the split's range, element by element with the
+    // exact factor: item = (block b, l >= m inside it)
     for (int it = tid; it < 4 * 136; it += kNT) {
         const int b = it / 136;
+        if (safe[b]) continue;
         int li = 0, p = it % 136;
         while (p > li) { p -= li + 1; ++li; }
         const int l = 16 * b + li, m = 16 * b + p;
@@ -1633,9 +1683,9 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
 //   dk_A[m][c] = sum_l dA[l][m] D_c[l][m] q_lc        dk_L2[m][c] = sum_l dL[l][m] D_c[l][m] k_lc
 // Off the diagonal 16x16 blocks each is one matrix-core product over the other
 // block's rows, the decay split at a block boundary into two factors of at most
-// 1 (one on the operand, one on the result); the diagonal blocks are summed
-// element by element by thread (block, channel) and handed to the result tiles
-// through LDS.  Per element then
+// 1 for decays (one on the operand, one on the result); the diagonal blocks
+// are summed element by element by thread (block, channel) with the exact
+// factors and handed to the result tiles through LDS.  Per element then
 //   dq = 2^G d<-Q + dq_A ; dk = 2^G d<-K + 2^(G_C - G) d->K + dk_A + dk_L1 + dk_L2
 //   dG = q 2^G d<-Q + k 2^G d<-K - k 2^(G_C-G) d->K + q dq_A - k dk_A + k dk_L1 - k dk_L2
 //   dG_C += sum_l k_l 2^(G_C-G_l) d->K_l + 2^(G_C) sum_j S_r[c][j] dS[c][j]
@@ -1689,11 +1739,11 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
     // every thread calls this (it holds a barrier)
     auto prefix = [&](float* Gl) {
         if (pre) {
+            load_col16(Gl, g + (bh * Tlen + t0) * DK + pc, DK, 16 * pb, tvalid);
             float acc = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const int row = 16 * pb + rr;
-                if (row < tvalid) acc += to_f32(g[(bh * Tlen + t0 + row) * DK + pc]) * kLog2eB;
+                acc += Gl[rr] * kLog2eB;
                 Gl[rr] = acc;
             }
             tot[pb][pc] = acc;
@@ -1720,7 +1770,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
     }
     if (tid < kC) bet[tid] = (DELTA && tid < tvalid) ? to_f32(beta[bh * Tlen + t0 + tid]) : 0.f;
     {
-        float Gl[16];
+        float Gl[16], kv[16];
+        if (pre) load_col16(kv, k + (bh * Tlen + t0) * DK + pc, DK, 16 * pb, tvalid);
         prefix(Gl);
         if (pre) {
             // 2^(G_C) of this channel: the last row's prefix, read back from the
@@ -1729,9 +1780,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int row = 16 * pb + rr;
-                const float kv = row < tvalid ? to_f32(k[(bh * Tlen + t0 + row) * DK + pc]) : 0.f;
-                KA[row * LDQ + pc] = from_f32<bf16>(kv * fast_exp2(Gl[rr]));
-                KB[row * LDQ + pc] = from_f32<bf16>(kv * fast_exp2(gl - Gl[rr]));
+                KA[row * LDQ + pc] = from_f32<bf16>(kv[rr] * fast_exp2(Gl[rr]));
+                KB[row * LDQ + pc] = from_f32<bf16>(kv[rr] * fast_exp2(gl - Gl[rr]));
             }
         }
     }
@@ -1982,25 +2032,27 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
         if (lbq > 0) {
             const int s = 16 * lbq - 1;
             const float gs = Gf[s * LDG + c];
+            floatx4 dq_ = zero4(), kp_ = zero4();
             for (int j = 0; j < lbq; ++j) {
                 const int m0 = 16 * j + g4;
                 bf16x4 b;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     b[e] = from_f32<bf16>(to_f32(Kr[(m0 + e) * LDQ + c]) * fast_exp2(gs - Gf[(m0 + e) * LDG + c]));
-                DQ[u] = mma16<bf16>(frag_xk(dAs, LDC, 16 * lbq, 16 * j, lane), b, DQ[u]);
-                if constexpr (DELTA) KP[u] = mma16<bf16>(frag_xk(dLs, LDC, 16 * lbq, 16 * j, lane), b, KP[u]);
+                dq_ = mma16<bf16>(frag_xk(dAs, LDC, 16 * lbq, 16 * j, lane), b, dq_);
+                if constexpr (DELTA) kp_ = mma16<bf16>(frag_xk(dLs, LDC, 16 * lbq, 16 * j, lane), b, kp_);
             }
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const float f = fast_exp2(Gf[(16 * lbq + g4 + rr) * LDG + c] - gs);
-                DQ[u][rr] *= f;
-                KP[u][rr] *= f;
+                DQ[u][rr] += dq_[rr] * f;
+                KP[u][rr] += kp_[rr] * f;
             }
         }
         if (lbq < 3) {
             const int e = 16 * lbq + 15;
             const float ge = Gf[e * LDG + c];
+            floatx4 km_ = zero4();
             for (int i = lbq + 1; i < 4; ++i) {
                 const int l0 = 16 * i + g4;
                 bf16x4 bq, bk;
@@ -2010,25 +2062,30 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
                     bq[x] = from_f32<bf16>(to_f32(Qr[(l0 + x) * LDQ + c]) * f);
                     bk[x] = from_f32<bf16>(to_f32(Kr[(l0 + x) * LDQ + c]) * f);
                 }
-                KM[u] = mma16<bf16>(frag_kx(dAs, LDC, 16 * lbq, 16 * i, lane), bq, KM[u]);
-                if constexpr (DELTA) KM[u] = mma16<bf16>(frag_kx(dLs, LDC, 16 * lbq, 16 * i, lane), bk, KM[u]);
+                km_ = mma16<bf16>(frag_kx(dAs, LDC, 16 * lbq, 16 * i, lane), bq, km_);
+                if constexpr (DELTA) km_ = mma16<bf16>(frag_kx(dLs, LDC, 16 * lbq, 16 * i, lane), bk, km_);
             }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) KM[u][rr] *= fast_exp2(ge - Gf[(16 * lbq + g4 + rr) * LDG + c]);
+            for (int rr = 0; rr < 4; ++rr) KM[u][rr] += km_[rr] * fast_exp2(ge - Gf[(16 * lbq + g4 + rr) * LDG + c]);
         }
     }
-    // F5: the diagonal blocks, thread (pb, pc) over its block's 16 rows, exact
-    // factors; handed to the tiles through X in three rounds
+    // F5: the diagonal blocks, thread (pb, pc) over its block's 16 rows with
+    // the exact factors, handed to the tiles through X in three rounds.  The
+    // terms of a pair (l, m) enter row l of q dq_A and row m of k dk_A with one
+    // and the same fp32 product, so they cancel in the suffix sums of dg as
+    // they do in the exact gradient (a rounded split of the decay would not).
+    // 2^(G_l - G_m) = prod_{s=m+1..l} 2^(G_s - G_{s-1}): one exp per row.
     float aq[16], ap[16], am[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) aq[rr] = ap[rr] = am[rr] = 0.f;
     if (pre) {
-        float gd[16], qd[16], kd[16];
+        float es[16], qd[16], kd[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int row = 16 * pb + rr;
-            gd[rr] = Gf[row * LDG + pc];
+            es[rr] = rr > 0 ? fast_exp2(Gf[row * LDG + pc] - Gf[(row - 1) * LDG + pc]) : 1.f;
             qd[rr] = to_f32(Qr[row * LDQ + pc]);
             kd[rr] = to_f32(Kr[row * LDQ + pc]);
-            aq[rr] = ap[rr] = am[rr] = 0.f;
         }
 #pragma unroll
         for (int li = 0; li < 16; ++li) {
@@ -2046,9 +2103,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
                 __builtin_memcpy(rl, &b0, 16);
                 __builtin_memcpy(rl + 8, &b1, 16);
             }
+            float d = 1.f;                       // 2^(G_l - G_m), m from l down
 #pragma unroll
-            for (int mi = 0; mi <= li; ++mi) {
-                const float d = fast_exp2(gd[li] - gd[mi]);
+            for (int mi = li; mi >= 0; --mi) {
+                if (mi < li) d *= es[mi + 1];
                 const float a = to_f32(ra[mi]) * d;
                 aq[li] = fmaf(a, kd[mi], aq[li]);
                 am[mi] = fmaf(a, qd[li], am[mi]);
