@@ -601,6 +601,45 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __r
     if (tid < DK) gC[(bh * nchunks + r) * DK + tid] = fast_exp2(Gf[(kC - 1) * LDG + tid]);
 }
 
+// The gradients of the chunk-leaving states (dstates) are kept in blocks of
+// 16 value columns, [B,H,N][dv/16][dk][16], so that the reverse state pass
+// writes each wave's 16 columns as one contiguous block: offset of element
+// (key row i, value column j) inside one chunk's [dk][dv] state.
+__device__ __forceinline__ int dstate_offset(int i, int j, int dk)
+{
+    return ((j >> 4) * dk + i) * 16 + (j & 15);
+}
+
+// Row store of a 16x16 result tile in the token type: lane l holds rows
+// 4(l/16)..+3 of column l%16; a 4x4 transpose inside each quad of lanes (two
+// DPP exchanges) leaves lane l with row 4(l/16) + l%4 over columns
+// 4(l%16 / 4)..+3, stored as one 8-byte (bf16) or 16-byte (fp32) write.
+template <typename T>
+__device__ __forceinline__ void store_tile_rows(T* P, int64_t ld, floatx4 v, int lane)
+{
+    const int s = lane & 3;
+    float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+    {
+        // lanes s, s^1: afterwards lane s holds rows (s&1, s&1 + 2), columns (s&2, s&2 + 1)
+        const bool odd = s & 1;
+        const float a = dpp_move<0xB1, 0xf>(odd ? v0 : v1), b = dpp_move<0xB1, 0xf>(odd ? v2 : v3);
+        if (odd) { v0 = a; v2 = b; } else { v1 = a; v3 = b; }
+    }
+    {
+        // lanes s, s^2: afterwards lane s holds row s, columns 0..3
+        const bool hi = s & 2;
+        const float a = dpp_move<0x4E, 0xf>(hi ? v0 : v2), b = dpp_move<0x4E, 0xf>(hi ? v1 : v3);
+        if (hi) { v0 = a; v1 = b; } else { v2 = a; v3 = b; }
+    }
+    T* p = P + (int64_t)(4 * (lane >> 4) + s) * ld + 4 * ((lane & 15) >> 2);
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 w = {from_f32<bf16>(v0), from_f32<bf16>(v1), from_f32<bf16>(v2), from_f32<bf16>(v3)};
+        *reinterpret_cast<bf16x4*>(p) = w;
+    } else {
+        *reinterpret_cast<floatx4*>(p) = floatx4{v0, v1, v2, v3};
+    }
+}
+
 // ============================================================================
 // bwd_chain_kernel: the reverse state pass.  One workgroup per (b, h, 64 value
 // columns): waves 0-3 own 16 columns of dS each (dk/16 result tiles, kept in
@@ -660,41 +699,70 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
         for (int64_t c = nchunks - 1; c >= 0; --c) {
             const int ln = opaque(lane);
             const int buf = (int)(c & 1);
-            T* dsr = dstates + ((bh * nchunks + c) * DK + g4) * DV + col;
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) dsr[(16 * db + rr) * DV] = from_f32<T>(dS[db][rr]);
+            // Fragments are read from LDS two row blocks ahead of the products
+            // that use them; the scheduling barriers keep the compiler from
+            // sinking each read down to its product, which would make every
+            // matrix-core op wait for one LDS round trip.
             // ---- phase 1: dZ = A^T dO + ->K dS ; dR = Tb^T dZ ----
             // every product as K = 32 pairs of K = 16 steps; the blocks of A^T and
             // Tb^T left of the diagonal are zero, so the full range is exact
+            constexpr int NF1 = 4 + ND;                // A^T and ->K fragments of one row block
             floatx4 X[4], dR[4];
-            F16<T> dof[4];
+            F16<T> dof[4], fa[NF1], fb[NF1], tb[DELTA ? 16 : 1];
+            auto load1 = [&](int li, F16<T>* f) {
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) f[mb] = frag_xk(AqT, LDC, 16 * li, 16 * mb, ln);
+#pragma unroll
+                for (int db = 0; db < ND; ++db) f[4 + db] = frag_xk(Kr, LDQ, 16 * li, 16 * db, ln);
+            };
+            auto prod1x2 = [&](const F16<T>* f, const F16<T>* h, floatx4& xf, floatx4& xh) {
+                floatx4 a = zero4(), b = zero4();
+#pragma unroll
+                for (int mb = 0; mb < 4; mb += 2) {
+                    a = mma16x2<T>(f[mb], f[mb + 1], dof[mb], dof[mb + 1], a);
+                    b = mma16x2<T>(h[mb], h[mb + 1], dof[mb], dof[mb + 1], b);
+                }
+#pragma unroll
+                for (int db = 0; db < ND; db += 2) {
+                    const F16<T> s0 = frag16_acc<T>(dS[db]), s1 = frag16_acc<T>(dS[db + 1]);
+                    a = mma16x2<T>(f[4 + db], f[5 + db], s0, s1, a);
+                    b = mma16x2<T>(h[4 + db], h[5 + db], s0, s1, b);
+                }
+                xf = a;
+                xh = b;
+            };
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) dof[mb] = frag_xk(dOT[buf], LDC, n0, 16 * mb, ln);
+            load1(0, fa);
+            load1(1, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                // dS_{r+1} of this chunk to HBM while the reads are in flight:
+                // this wave's 16 columns are one contiguous [dk][16] block
+                T* dsr = dstates + (bh * nchunks + c) * DK * DV + dstate_offset(0, vb * 64 + n0, DK);
 #pragma unroll
-            for (int li = 0; li < 4; ++li) {
-                floatx4 acc = zero4();
-#pragma unroll
-                for (int mb = 0; mb < 4; mb += 2)
-                    acc = mma16x2<T>(frag_xk(AqT, LDC, 16 * li, 16 * mb, ln), frag_xk(AqT, LDC, 16 * li, 16 * mb + 16, ln),
-                                     dof[mb], dof[mb + 1], acc);
-#pragma unroll
-                for (int db = 0; db < ND; db += 2)
-                    acc = mma16x2<T>(frag_xk(Kr, LDQ, 16 * li, 16 * db, ln), frag_xk(Kr, LDQ, 16 * li, 16 * db + 16, ln),
-                                     frag16_acc<T>(dS[db]), frag16_acc<T>(dS[db + 1]), acc);
-                X[li] = acc;
+                for (int db = 0; db < ND; ++db) store_tile_rows(dsr + 16 * db * 16, 16, dS[db], ln);
             }
+            // two row blocks at a time, their products interleaved (two
+            // independent accumulation chains for the matrix cores)
+            prod1x2(fa, fb, X[0], X[1]);
+            load1(2, fa);
+            load1(3, fb);
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int li = 0; li < 4; ++li)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) tb[4 * li + kb] = frag_xk(TbT, LDC, 16 * li, 16 * kb, ln);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            prod1x2(fa, fb, X[2], X[3]);
             if constexpr (DELTA) {
                 const F16<T> x0 = frag16_acc<T>(X[0]), x1 = frag16_acc<T>(X[1]), x2 = frag16_acc<T>(X[2]),
                              x3 = frag16_acc<T>(X[3]);
 #pragma unroll
-                for (int li = 0; li < 4; ++li) {
-                    floatx4 acc = mma16x2<T>(frag_xk(TbT, LDC, 16 * li, 0, ln), frag_xk(TbT, LDC, 16 * li, 16, ln),
-                                             x0, x1, zero4());
-                    dR[li] = mma16x2<T>(frag_xk(TbT, LDC, 16 * li, 32, ln), frag_xk(TbT, LDC, 16 * li, 48, ln),
-                                        x2, x3, acc);
-                }
+                for (int li = 0; li < 4; ++li)
+                    dR[li] = mma16x2<T>(tb[4 * li + 2], tb[4 * li + 3], x2, x3,
+                                        mma16x2<T>(tb[4 * li], tb[4 * li + 1], x0, x1, zero4()));
             }
             lds_barrier();
             // ---- phase 2: dS = exp(G_C) dS + <-Q^T dO - <-K^T dR ----
@@ -703,22 +771,51 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) drf[mb] = frag16_acc<T>(dR[mb]);
             }
+            constexpr int NF2 = DELTA ? 8 : 4;         // <-Q^T and -<-K^T fragments of one row block
+            F16<T> fq[2][NF2];
+            auto load2 = [&](int db, F16<T>* f) {
 #pragma unroll
-            for (int db = 0; db < ND; ++db) {
-                floatx4 acc;
-                if constexpr (CHAN) acc = dS[db] * *reinterpret_cast<const floatx4*>(&gCs[buf][16 * db + g4]);
-                else acc = dS[db] * gCs[buf][0];
+                for (int mb = 0; mb < 4; ++mb) {
+                    f[mb] = frag_xk(QdT, LDC, 16 * db, 16 * mb, ln);
+                    if constexpr (DELTA) f[4 + mb] = frag_xk(NKdT, LDC, 16 * db, 16 * mb, ln);
+                }
+            };
+            load2(0, fq[0]);
+            load2(1, fq[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // two row blocks of dS at a time, their products interleaved; the
+            // next pair's fragments are read meanwhile
 #pragma unroll
-                for (int mb = 0; mb < 4; mb += 2)
-                    acc = mma16x2<T>(frag_xk(QdT, LDC, 16 * db, 16 * mb, ln), frag_xk(QdT, LDC, 16 * db, 16 * mb + 16, ln),
-                                     dof[mb], dof[mb + 1], acc);
+            for (int db = 0; db < ND; db += 2) {
+                floatx4 a, b;
+                if constexpr (CHAN) {
+                    a = dS[db] * *reinterpret_cast<const floatx4*>(&gCs[buf][16 * db + g4]);
+                    b = dS[db + 1] * *reinterpret_cast<const floatx4*>(&gCs[buf][16 * db + 16 + g4]);
+                } else {
+                    a = dS[db] * gCs[buf][0];
+                    b = dS[db + 1] * gCs[buf][0];
+                }
+                const F16<T>* f = fq[0];
+                const F16<T>* h = fq[1];
+#pragma unroll
+                for (int mb = 0; mb < 4; mb += 2) {
+                    a = mma16x2<T>(f[mb], f[mb + 1], dof[mb], dof[mb + 1], a);
+                    b = mma16x2<T>(h[mb], h[mb + 1], dof[mb], dof[mb + 1], b);
+                }
                 if constexpr (DELTA) {
 #pragma unroll
-                    for (int mb = 0; mb < 4; mb += 2)
-                        acc = mma16x2<T>(frag_xk(NKdT, LDC, 16 * db, 16 * mb, ln),
-                                         frag_xk(NKdT, LDC, 16 * db, 16 * mb + 16, ln), drf[mb], drf[mb + 1], acc);
+                    for (int mb = 0; mb < 4; mb += 2) {
+                        a = mma16x2<T>(f[4 + mb], f[5 + mb], drf[mb], drf[mb + 1], a);
+                        b = mma16x2<T>(h[4 + mb], h[5 + mb], drf[mb], drf[mb + 1], b);
+                    }
                 }
-                dS[db] = acc;
+                dS[db] = a;
+                dS[db + 1] = b;
+                if (db + 2 < ND) {
+                    load2(db + 2, fq[0]);
+                    load2(db + 3, fq[1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             lds_barrier();
         }
@@ -730,96 +827,106 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
         }
     } else {
         const int ht = tid - 256;
-        i4 ra[NA], rt[NA], rk[NK], ro[NO], rq[NK], rn[NK];
-        float rg = 0.f;
-        i4 rgv = {0, 0, 0, 0};
-        auto load1 = [&](int64_t c) {
+        // The operands of one chunk in registers: group 1 (A^T, Tb^T, ->K, dO
+        // and the chunk decay, read in phase 1) and group 2 (<-Q^T, -<-K^T, read
+        // in phase 2).  Two sets, the chunk being staged and the next one, so
+        // each load is issued about one chunk period before it is staged: the
+        // HBM round trip, not the products, would otherwise set the pace.
+        struct Regs {
+            i4 ra[NA], rt[NA], rk[NK], ro[NO], rq[NK], rn[NK], rgv;
+            float rg;
+        };
+        Regs A, B;
+        auto load = [&](int64_t c, Regs& R) {
             const T* base = ops + (bh * nchunks + c) * ostride;
 #pragma unroll
             for (int p = 0; p < NA; ++p) {
                 const int e = (p * NH + ht) * E;
-                ra[p] = *reinterpret_cast<const i4*>(base + C::O_AQT + e);
-                if constexpr (DELTA) rt[p] = *reinterpret_cast<const i4*>(base + C::O_TBT + e);
+                R.ra[p] = *reinterpret_cast<const i4*>(base + C::O_AQT + e);
+                if constexpr (DELTA) R.rt[p] = *reinterpret_cast<const i4*>(base + C::O_TBT + e);
             }
 #pragma unroll
             for (int p = 0; p < NK; ++p) {
                 const int e = (p * NH + ht) * E;
-                rk[p] = *reinterpret_cast<const i4*>(base + C::O_KR + e);
+                R.rk[p] = *reinterpret_cast<const i4*>(base + C::O_KR + e);
+                R.rq[p] = *reinterpret_cast<const i4*>(base + C::O_QDT + e);
+                if constexpr (DELTA) R.rn[p] = *reinterpret_cast<const i4*>(base + C::O_NKDT + e);
             }
 #pragma unroll
             for (int p = 0; p < NO; ++p) {
-                const int e = p * NH + ht;                 // lane-consecutive rows
+                // lane-consecutive rows; rows past the end read the last row and
+                // are zeroed, so every chunk issues the same loads
+                const int e = p * NH + ht;
                 const int row = e % kC, cc = (e / kC) * E;
                 const int64_t t = c * kC + row;
-                ro[p] = i4{0, 0, 0, 0};
-                if (t < Tlen) ro[p] = *reinterpret_cast<const i4*>(dout + (bh * Tlen + t) * DV + vb * 64 + cc);
+                const int64_t tr = t < Tlen ? t : Tlen - 1;
+                const i4 x = *reinterpret_cast<const i4*>(dout + (bh * Tlen + tr) * DV + vb * 64 + cc);
+                R.ro[p] = t < Tlen ? x : i4{0, 0, 0, 0};
             }
             if constexpr (CHAN) {
-                if (ht < DK / 4) rgv = *reinterpret_cast<const i4*>(gC + (bh * nchunks + c) * DK + 4 * ht);
+                if (ht < DK / 4) R.rgv = *reinterpret_cast<const i4*>(gC + (bh * nchunks + c) * DK + 4 * ht);
             } else {
-                rg = gC[bh * nchunks + c];
+                R.rg = gC[bh * nchunks + c];
             }
         };
-        auto stage1 = [&](int64_t c) {
+        auto stage1 = [&](int64_t c, const Regs& R) {
             const int buf = (int)(c & 1);
 #pragma unroll
             for (int p = 0; p < NA; ++p) {
                 const int e = (p * NH + ht) * E;
-                *reinterpret_cast<i4*>(AqT + (e / kC) * LDC + e % kC) = ra[p];
-                if constexpr (DELTA) *reinterpret_cast<i4*>(TbT + (e / kC) * LDC + e % kC) = rt[p];
+                *reinterpret_cast<i4*>(AqT + (e / kC) * LDC + e % kC) = R.ra[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(TbT + (e / kC) * LDC + e % kC) = R.rt[p];
             }
 #pragma unroll
             for (int p = 0; p < NK; ++p) {
                 const int e = (p * NH + ht) * E;
-                *reinterpret_cast<i4*>(Kr + (e / DK) * LDQ + e % DK) = rk[p];
+                *reinterpret_cast<i4*>(Kr + (e / DK) * LDQ + e % DK) = R.rk[p];
             }
 #pragma unroll
             for (int p = 0; p < NO; ++p) {
                 const int e = p * NH + ht;
                 const int row = e % kC, cc = (e / kC) * E;
                 T x[E];
-                __builtin_memcpy(x, &ro[p], 16);
+                __builtin_memcpy(x, &R.ro[p], 16);
 #pragma unroll
                 for (int i = 0; i < E; ++i) dOT[buf][(cc + i) * LDC + row] = x[i];
             }
             if constexpr (CHAN) {
-                if (ht < DK / 4) *reinterpret_cast<i4*>(&gCs[buf][4 * ht]) = rgv;
+                if (ht < DK / 4) *reinterpret_cast<i4*>(&gCs[buf][4 * ht]) = R.rgv;
             } else {
-                if (ht == 0) gCs[buf][0] = rg;
+                if (ht == 0) gCs[buf][0] = R.rg;
             }
         };
-        auto load2 = [&](int64_t c) {
-            const T* base = ops + (bh * nchunks + c) * ostride;
+        auto stage2 = [&](const Regs& R) {
 #pragma unroll
             for (int p = 0; p < NK; ++p) {
                 const int e = (p * NH + ht) * E;
-                rq[p] = *reinterpret_cast<const i4*>(base + C::O_QDT + e);
-                if constexpr (DELTA) rn[p] = *reinterpret_cast<const i4*>(base + C::O_NKDT + e);
+                *reinterpret_cast<i4*>(QdT + (e / kC) * LDC + e % kC) = R.rq[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(NKdT + (e / kC) * LDC + e % kC) = R.rn[p];
             }
         };
-        auto stage2 = [&]() {
-#pragma unroll
-            for (int p = 0; p < NK; ++p) {
-                const int e = (p * NH + ht) * E;
-                *reinterpret_cast<i4*>(QdT + (e / kC) * LDC + e % kC) = rq[p];
-                if constexpr (DELTA) *reinterpret_cast<i4*>(NKdT + (e / kC) * LDC + e % kC) = rn[p];
-            }
+        // one chunk of the state waves' loop: X holds chunk c (its group 1
+        // already staged), Y chunk c - 1; X is refilled with chunk c - 2 (the
+        // last chunk again past the start, never staged)
+        auto step = [&](int64_t c, Regs& X, Regs& Y) {
+            stage2(X);                      // <-Q^T, -<-K^T of chunk c (read in phase 2)
+            load(c >= 2 ? c - 2 : 0, X);
+            lds_barrier();
+            if (c > 0) stage1(c - 1, Y);    // the buffers phase 1 read are free now
+            lds_barrier();
         };
         if (nchunks > 0) {
-            load1(nchunks - 1);
-            stage1(nchunks - 1);
-            load2(nchunks - 1);
+            load(nchunks - 1, A);
+            stage1(nchunks - 1, A);
+            load(nchunks >= 2 ? nchunks - 2 : 0, B);
         }
         __syncthreads();
-        for (int64_t c = nchunks - 1; c >= 0; --c) {
-            const int64_t cn = c > 0 ? c - 1 : 0;
-            stage2();                       // <-Q^T, -<-K^T of chunk c (read in phase 2)
-            load1(cn);
-            lds_barrier();
-            if (c > 0) stage1(cn);          // the buffers phase 1 read are free now
-            load2(cn);
-            lds_barrier();
+        int64_t c = nchunks - 1;
+        for (; c >= 1; c -= 2) {
+            step(c, A, B);
+            step(c - 1, B, A);
         }
+        if (c == 0) step(0, A, B);
         wait_vmem_all();
     }
 }
@@ -888,7 +995,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_kernel(
             ps[u] = pds[u] = i4{0, 0, 0, 0};
             if (i < DK * SR) {
                 ps[u] = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
-                pds[u] = *reinterpret_cast<const i4*>(dSr + row * DV + j0 + c);
+                pds[u] = *reinterpret_cast<const i4*>(dSr + dstate_offset(row, j0 + c, DK));
             }
         }
     };
@@ -1336,7 +1443,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
             ps[u] = pds[u] = i4{0, 0, 0, 0};
             if (i < DK * SR) {
                 ps[u] = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
-                pds[u] = *reinterpret_cast<const i4*>(dSr + row * DV + j0 + c);
+                pds[u] = *reinterpret_cast<const i4*>(dSr + dstate_offset(row, j0 + c, DK));
             }
         }
     };
@@ -1806,7 +1913,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
         ps = pds = i4{0, 0, 0, 0};
         if (tid < DK * SR) {
             ps = *reinterpret_cast<const i4*>(Sr + row * DV + j0 + c);
-            pds = *reinterpret_cast<const i4*>(dSr + row * DV + j0 + c);
+            pds = *reinterpret_cast<const i4*>(dSr + dstate_offset(row, j0 + c, DK));
         }
     };
     fetch(0);

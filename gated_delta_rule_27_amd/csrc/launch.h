@@ -108,7 +108,7 @@ struct ChunkBwdProblem {
     float* ds0;                   // [B,H,dk,dv] or NULL
     void* ops;                    // [B,H,N] chunk operand blocks (chunk_bwd_ops_bytes each)
     float* gC;                    // [B,H,N] exp of the chunk's total log-gate ([B,H,N,dk] per channel)
-    void* dstates;                // [B,H,N,dk,dv] token type, gradient w.r.t. S leaving chunk r
+    void* dstates;                // [B,H,N,dv/16,dk,16] token type, gradient w.r.t. S leaving chunk r
 };
 bool chunk_bwd_supported(int dk, int dv, int rule, int gate, int dtype);
 size_t chunk_bwd_ops_bytes(int dk, int gate, int dtype);

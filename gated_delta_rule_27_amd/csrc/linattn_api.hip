@@ -234,7 +234,7 @@ hipError_t launch_fwd_save(ChunkProblem p, void* states, void* ws, size_t wsb, h
 }
 
 // Backward workspace, 256-byte aligned pieces: chunk operands [B,H,N] blocks,
-// exp(G_C) [B,H,N] (per channel: [B,H,N,dk]), dstates [B,H,N,dk,dv], then
+// exp(G_C) [B,H,N] (per channel: [B,H,N,dk]), dstates [B,H,N,dv/16,dk,16], then
 // (states not given) the recomputed states [B,H,N,dk,dv], a forward output
 // [B,H,T,dv] and the forward's own workspace, all in the token type except
 // exp(G_C).
