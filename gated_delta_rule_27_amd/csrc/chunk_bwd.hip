@@ -39,6 +39,7 @@
 #include "launch.h"
 #include "mfma.h"
 #include "prep.h"
+#include "tile_rows.h"
 
 namespace linattn {
 
@@ -610,36 +611,6 @@ __device__ __forceinline__ int dstate_offset(int i, int j, int dk)
     return ((j >> 4) * dk + i) * 16 + (j & 15);
 }
 
-// Row store of a 16x16 result tile in the token type: lane l holds rows
-// 4(l/16)..+3 of column l%16; a 4x4 transpose inside each quad of lanes (two
-// DPP exchanges) leaves lane l with row 4(l/16) + l%4 over columns
-// 4(l%16 / 4)..+3, stored as one 8-byte (bf16) or 16-byte (fp32) write.
-template <typename T>
-__device__ __forceinline__ void store_tile_rows(T* P, int64_t ld, floatx4 v, int lane)
-{
-    const int s = lane & 3;
-    float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-    {
-        // lanes s, s^1: afterwards lane s holds rows (s&1, s&1 + 2), columns (s&2, s&2 + 1)
-        const bool odd = s & 1;
-        const float a = dpp_move<0xB1, 0xf>(odd ? v0 : v1), b = dpp_move<0xB1, 0xf>(odd ? v2 : v3);
-        if (odd) { v0 = a; v2 = b; } else { v1 = a; v3 = b; }
-    }
-    {
-        // lanes s, s^2: afterwards lane s holds row s, columns 0..3
-        const bool hi = s & 2;
-        const float a = dpp_move<0x4E, 0xf>(hi ? v0 : v2), b = dpp_move<0x4E, 0xf>(hi ? v1 : v3);
-        if (hi) { v0 = a; v1 = b; } else { v2 = a; v3 = b; }
-    }
-    T* p = P + (int64_t)(4 * (lane >> 4) + s) * ld + 4 * ((lane & 15) >> 2);
-    if constexpr (sizeof(T) == 2) {
-        bf16x4 w = {from_f32<bf16>(v0), from_f32<bf16>(v1), from_f32<bf16>(v2), from_f32<bf16>(v3)};
-        *reinterpret_cast<bf16x4*>(p) = w;
-    } else {
-        *reinterpret_cast<floatx4*>(p) = floatx4{v0, v1, v2, v3};
-    }
-}
-
 // ============================================================================
 // bwd_chain_kernel: the reverse state pass.  One workgroup per (b, h, 64 value
 // columns): waves 0-3 own 16 columns of dS each (dk/16 result tiles, kept in
@@ -671,6 +642,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
     __shared__ __align__(16) T QdT[DK * LDC];
     __shared__ __align__(16) T NKdT[DELTA ? DK * LDC : 8];
     __shared__ __align__(16) T dOT[2][64 * LDC];       // dO^T of the block: row j, column m
+    __shared__ __align__(16) T dSs[DK * LDC];          // dS of the block, handed to the helpers
     __shared__ __align__(16) float gCs[2][CHAN ? DK : 1];   // exp(G_C), per key channel with CHAN
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -736,13 +708,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             load1(0, fa);
             load1(1, fb);
             __builtin_amdgcn_sched_barrier(0);
-            {
-                // dS_{r+1} of this chunk to HBM while the reads are in flight:
-                // this wave's 16 columns are one contiguous [dk][16] block
-                T* dsr = dstates + (bh * nchunks + c) * DK * DV + dstate_offset(0, vb * 64 + n0, DK);
+            // dS_{r+1} of this chunk to LDS while the reads are in flight; the
+            // helper waves write it to HBM in phase 2
 #pragma unroll
-                for (int db = 0; db < ND; ++db) store_tile_rows(dsr + 16 * db * 16, 16, dS[db], ln);
-            }
+            for (int db = 0; db < ND; ++db) store_tile_rows(dSs + 16 * db * LDC + n0, LDC, dS[db], ln);
             // two row blocks at a time, their products interleaved (two
             // independent accumulation chains for the matrix cores)
             prod1x2(fa, fb, X[0], X[1]);
@@ -905,6 +874,19 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
                 if constexpr (DELTA) *reinterpret_cast<i4*>(NKdT + (e / kC) * LDC + e % kC) = R.rn[p];
             }
         };
+        // dS of chunk c from LDS to HBM, in the 16-column blocked layout
+        auto copy_ds = [&](int64_t c) {
+            constexpr int VR = 64 / E, ND2 = DK * VR / NH;
+            static_assert(ND2 * NH == DK * VR, "dS copy split");
+            T* base = dstates + (bh * nchunks + c) * DK * DV;
+#pragma unroll
+            for (int p = 0; p < ND2; ++p) {
+                const int e = p * NH + ht;
+                const int row = e / VR, col = (e % VR) * E;
+                *reinterpret_cast<i4*>(base + dstate_offset(row, vb * 64 + col, DK)) =
+                    *reinterpret_cast<const i4*>(dSs + row * LDC + col);
+            }
+        };
         // one chunk of the state waves' loop: X holds chunk c (its group 1
         // already staged), Y chunk c - 1; X is refilled with chunk c - 2 (the
         // last chunk again past the start, never staged)
@@ -913,6 +895,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             load(c >= 2 ? c - 2 : 0, X);
             lds_barrier();
             if (c > 0) stage1(c - 1, Y);    // the buffers phase 1 read are free now
+            copy_ds(c);                     // written by the state waves in phase 1
             lds_barrier();
         };
         if (nchunks > 0) {

@@ -31,6 +31,7 @@
 #include "launch.h"
 #include "mfma.h"
 #include "tsolve.h"
+#include "tile_rows.h"
 
 namespace linattn {
 
@@ -400,8 +401,9 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 // so each LDS region is refilled while the other phase runs.
 // ===========================================================================
 //
-// With SAVE the state waves also store S_r, the state entering chunk r, to
-// states[b, h, r] ([dk][dv], bf16) at the top of every chunk.
+// With SAVE the state waves also write S_r, the state entering chunk r, to an
+// LDS tile at the top of every chunk, and the helper waves copy it to
+// states[b, h, r] ([dk][dv], bf16) during phase 2 with 16-byte stores.
 template <int DK, int RULE, int DVB, bool SAVE>
 __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const bf16* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0,
@@ -426,6 +428,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     __shared__ __align__(16) bf16 Tb[DELTA ? kC * LDC : 8];
     __shared__ __align__(16) bf16 Vs[kC * LDV];
     __shared__ __align__(16) bf16 Os[kC * LDV];
+    __shared__ __align__(16) bf16 Sst[SAVE ? DK * LDV : 8];
     __shared__ __align__(16) float gC[DK];
 
     const int tid = threadIdx.x;
@@ -455,11 +458,8 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             const int ln = opaque(lane);
             const int cl = ln & 15, g4 = 4 * (ln >> 4);
             if constexpr (SAVE) {
-                bf16* sr = states + ((bh * nchunks + c) * DK + g4) * DV + vb * DVB + n0 + cl;
 #pragma unroll
-                for (int db = 0; db < ND; ++db)
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) sr[(16 * db + rr) * DV] = from_f32<bf16>(S[db][rr]);
+                for (int db = 0; db < ND; ++db) store_tile_rows(Sst + 16 * db * LDV + n0, LDV, S[db], ln);
             }
             // ---- phase 1: R = V - Kd S_r ; Z = Tb R ; O^T = S_r^T Qd^T ----------------
             floatx4 R[NL], Z[NL], Ot[NL];
@@ -628,6 +628,19 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                                                        off, 0, 0);
             }
         };
+        // S_r of chunk c from LDS to HBM (written by the state waves at the top
+        // of the chunk, stable until its second barrier)
+        auto copy_state = [&](int64_t c) {
+            constexpr int VR = DVB / 8, NS = DK * VR / NH;
+            static_assert(NS * NH == DK * VR, "state copy split");
+#pragma unroll
+            for (int p = 0; p < NS; ++p) {
+                const int e = p * NH + ht;
+                const int row = e / VR, col = (e % VR) * 8;
+                *reinterpret_cast<i4*>(states + ((bh * nchunks + c) * DK + row) * DV + vb * DVB + col) =
+                    *reinterpret_cast<const i4*>(&Sst[row * LDV + col]);
+            }
+        };
         const int64_t last = nchunks - 1;
         if (nchunks > 0) {
             load1(0);
@@ -645,6 +658,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             // ---- phase 2 ----
             if (c + 1 < nchunks) stage1(c + 1);
             load1(c + 2 < last ? c + 2 : last);
+            if constexpr (SAVE) copy_state(c);
             lds_barrier();
         }
         __syncthreads();                          // the last output is in Os
