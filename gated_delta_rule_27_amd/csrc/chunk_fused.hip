@@ -559,7 +559,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         for (int64_t r = 0; r < nchunks; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
-            const int cl = ln & 15, g4 = 4 * (ln >> 4);
+            const int g4 = 4 * (ln >> 4);
             float* const Gs = Gsb[r & 1];
             float* const bet = betb[r & 1];
 
@@ -631,7 +631,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         for (int64_t r = 0; r < nchunks; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
-            const int cl = ln & 15, g4 = 4 * (ln >> 4);
             const float* const Gs = Gsb[r & 1];
             const float* const bet = betb[r & 1];
             stage(t0);

@@ -112,7 +112,6 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int cl = lane & 15, g4 = 4 * (lane >> 4);
-    using Fr = typename Mfma<bf16>::frag;
 
     // the causal blocks above the diagonal stay zero
     for (int i = tid; i < kC * LDC; i += NT) Aq[i] = from_f32<bf16>(0.f);
@@ -142,8 +141,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     if (blockIdx.x < ntasks) fetch(blockIdx.x);
 
     for (int64_t task = blockIdx.x; task < ntasks; task += gridDim.x) {
-        const int64_t bh = task / nchunks, r = task % nchunks, t0 = r * kC;
-        unsigned char* wc = ws + task * W::BYTES;     // task = bh * nchunks + r
+        const int64_t t0 = (task % nchunks) * kC;
+        unsigned char* wc = ws + task * W::BYTES;     // task = (b, h) * nchunks + chunk
 
         // ---- stage the chunk; issue the next chunk-head's loads ---------------------
         __syncthreads();
