@@ -283,6 +283,27 @@ def bwd_nominal_flops(B, H, T, dk, dv, C=64):
     return B * H * T * 2 * macs
 
 
+def rmw_ceiling(dev, mib=1024, reps=20):
+    """Read-modify-write bandwidth a plain streaming kernel reaches on this
+    device: torch's in-place scale of a ``mib`` MiB fp32 buffer (every byte
+    read once and written once, like the decode step's state), HIP events; 23
+    halvings of ones stay normal fp32."""
+    import torch
+    x = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        x.mul_(0.5)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        x.mul_(0.5)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x
+    return {"kernel": f"torch in-place scale of {mib} MiB fp32", "GBps": round(2 * mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)}
+
+
 def time_backward(la, syn, case, dev, steps, warmup=2):
     """Event-timed training passes at the shape and laws of ``case``: the
     forward that keeps the chunk states, the backward from those states, and
@@ -529,7 +550,9 @@ def main():
             "hbm_frac": round(dgbps / HBM_PEAK_GBPS, 4),
             "alg_bytes_per_step": dbytes,
             "traffic": counter_traffic(DECODE_PROFILE, DECODE_SOURCES),
+            "rmw_ceiling": rmw_ceiling(dev),
         }
+        decode["frac_of_rmw_ceiling"] = round(dgbps / decode["rmw_ceiling"]["GBps"], 4)
         del tok, state
 
     # ---------------- CPU oracle baseline ------------------------------------

@@ -806,7 +806,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             float rg;
         };
         Regs A, B;
-        auto load = [&](int64_t c, Regs& R) {
+        auto load_g1 = [&](int64_t c, Regs& R) {
             const T* base = ops + (bh * nchunks + c) * ostride;
 #pragma unroll
             for (int p = 0; p < NA; ++p) {
@@ -818,8 +818,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             for (int p = 0; p < NK; ++p) {
                 const int e = (p * NH + ht) * E;
                 R.rk[p] = *reinterpret_cast<const i4*>(base + C::O_KR + e);
-                R.rq[p] = *reinterpret_cast<const i4*>(base + C::O_QDT + e);
-                if constexpr (DELTA) R.rn[p] = *reinterpret_cast<const i4*>(base + C::O_NKDT + e);
             }
 #pragma unroll
             for (int p = 0; p < NO; ++p) {
@@ -837,6 +835,19 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             } else {
                 R.rg = gC[bh * nchunks + c];
             }
+        };
+        auto load_g2 = [&](int64_t c, Regs& R) {
+            const T* base = ops + (bh * nchunks + c) * ostride;
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = (p * NH + ht) * E;
+                R.rq[p] = *reinterpret_cast<const i4*>(base + C::O_QDT + e);
+                if constexpr (DELTA) R.rn[p] = *reinterpret_cast<const i4*>(base + C::O_NKDT + e);
+            }
+        };
+        auto load = [&](int64_t c, Regs& R) {
+            load_g1(c, R);
+            load_g2(c, R);
         };
         auto stage1 = [&](int64_t c, const Regs& R) {
             const int buf = (int)(c & 1);
@@ -898,18 +909,39 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
             copy_ds(c);                     // written by the state waves in phase 1
             lds_barrier();
         };
-        if (nchunks > 0) {
-            load(nchunks - 1, A);
-            stage1(nchunks - 1, A);
-            load(nchunks >= 2 ? nchunks - 2 : 0, B);
+        if constexpr (sizeof(T) == 2) {
+            if (nchunks > 0) {
+                load(nchunks - 1, A);
+                stage1(nchunks - 1, A);
+                load(nchunks >= 2 ? nchunks - 2 : 0, B);
+            }
+            __syncthreads();
+            int64_t c = nchunks - 1;
+            for (; c >= 1; c -= 2) {
+                step(c, A, B);
+                step(c - 1, B, A);
+            }
+            if (c == 0) step(0, A, B);
+        } else {
+            // fp32 operands take twice the registers: one set, each group
+            // loaded one phase ahead of its staging
+            if (nchunks > 0) {
+                load_g1(nchunks - 1, A);
+                stage1(nchunks - 1, A);
+                load_g2(nchunks - 1, A);
+            }
+            __syncthreads();
+            for (int64_t c = nchunks - 1; c >= 0; --c) {
+                const int64_t cn = c > 0 ? c - 1 : 0;
+                stage2(A);
+                load_g1(cn, A);
+                lds_barrier();
+                if (c > 0) stage1(cn, A);
+                copy_ds(c);
+                load_g2(cn, A);
+                lds_barrier();
+            }
         }
-        __syncthreads();
-        int64_t c = nchunks - 1;
-        for (; c >= 1; c -= 2) {
-            step(c, A, B);
-            step(c - 1, B, A);
-        }
-        if (c == 0) step(0, A, B);
         wait_vmem_all();
     }
 }
