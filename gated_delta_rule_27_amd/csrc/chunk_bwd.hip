@@ -1567,16 +1567,34 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
             __syncthreads();
         }
         // ---- step C: d<-K += dR S_r^T (negated later) ; d->K += Z dS^T ; dA += dO Z^T ----
+        // every fragment of the step is read before its first product (the
+        // scheduling barrier keeps the reads together), so the products do not
+        // wait for LDS one tile at a time; the row-side fragments are shared
+        {
+            F16<T> aR[2], aZ[2], aO[2], bS[NI][2], bD[NI][2], bZ[2][2];
 #pragma unroll
-        for (int u = 0; u < NI; ++u) {
-            const int ib = NI * (wave & 1) + u;
-            if constexpr (DELTA) dKd[u] = tilek<T, true, true, J>(dKd[u], dRs, LDJ, 16 * lbq, Ss, LDJ, 16 * ib, 0, lane);
-            dKr[u] = tilek<T, true, true, J>(dKr[u], Zs, LDJ, 16 * lbq, dSs, LDJ, 16 * ib, 0, lane);
-        }
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if constexpr (DELTA) aR[s2] = frag_xk(dRs, LDJ, 16 * lbq, 16 * s2, lane);
+                aZ[s2] = frag_xk(Zs, LDJ, 16 * lbq, 16 * s2, lane);
+                aO[s2] = frag_xk(dOs, LDJ, 16 * lbt, 16 * s2, lane);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int mb = 2 * (wave & 1) + u;
-            if (mb <= lbt) dAq[u] = tilek<T, true, true, J>(dAq[u], dOs, LDJ, 16 * lbt, Zs, LDJ, 16 * mb, 0, lane);
+                for (int u = 0; u < NI; ++u) {
+                    const int ib = NI * (wave & 1) + u;
+                    if constexpr (DELTA) bS[u][s2] = frag_xk(Ss, LDJ, 16 * ib, 16 * s2, lane);
+                    bD[u][s2] = frag_xk(dSs, LDJ, 16 * ib, 16 * s2, lane);
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) bZ[u][s2] = frag_xk(Zs, LDJ, 16 * (2 * (wave & 1) + u), 16 * s2, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < NI; ++u) {
+                if constexpr (DELTA) dKd[u] = mma16x2<T>(aR[0], aR[1], bS[u][0], bS[u][1], dKd[u]);
+                dKr[u] = mma16x2<T>(aZ[0], aZ[1], bD[u][0], bD[u][1], dKr[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (2 * (wave & 1) + u <= lbt) dAq[u] = mma16x2<T>(aO[0], aO[1], bZ[u][0], bZ[u][1], dAq[u]);
         }
     }
     __syncthreads();
