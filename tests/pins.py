@@ -597,7 +597,7 @@ def pin_bwd_finite_differences(orc):
                 err = np.max(np.abs(grads[gname] - fd)) / max(1.0, np.max(np.abs(fd)))
                 assert err < 1e-7, f"{gname} vs central differences ({rule}/{gate}): {err:.2e}"
     # 150 tokens: three replay segments; directional derivatives
-    for rule, gate in (("delta", "scalar"), ("add", "channel")):
+    for rule, gate in (("delta", "scalar"), ("add", "channel"), ("delta", "channel")):
         x, do, dsT = _bwd_case(rng, 150, 4, 3, rule, gate)
         x["q"] /= 2.0
         grads = orc.recurrence_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], do, dsT,
