@@ -418,8 +418,11 @@ CHUNK_KERNELS = {"pipe": "chunk_pipe_kernel", "fused": "chunk_fused_kernel",
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 100 warm-up steps: from idle the GPU's clocks ramp for ~60 steps of this
+    # workload (per-step times fall from ~580 to ~400 us); the timed steps are
+    # the steady state
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128,
