@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tokens/s chunk fwd (H=16,d=128,T=8192) + decode state GB/s vs peak"
+SETTLE_STEPS = 100    # untimed headline steps before timing, warm-up included
 CSRC = os.path.join(ROOT, "gated_delta_rule_27_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources each measured kernel is built from: counter figures in profiles/
@@ -480,7 +481,11 @@ def main():
         la.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, rule=case.rule,
                      gate=case.gate, out=out, s_final=s_fin, workspace=ws)
 
-    for _ in range(args.warmup):
+    # at least SETTLE_STEPS untimed steps before the timed ones, whatever
+    # --warmup asks for: from idle the GPU's clocks take ~60 steps of this
+    # workload to settle, and the timed steps measure the steady state
+    settle = max(0, SETTLE_STEPS - args.warmup)
+    for _ in range(settle + args.warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -590,6 +595,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
