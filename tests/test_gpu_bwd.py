@@ -233,12 +233,14 @@ def test_channel_equal_channels_match_scalar_gate():
     assert e <= TOL["bf16"]
 
 
-def test_channel_many_heads_wide_blocks():
-    # 256 heads: the forward's state pass takes 64-column value blocks (the
-    # narrow 32-column blocks serve fewer heads than CUs), so its saved states
-    # go through the wide copy path; saved and recomputed states agree and the
-    # gradients match the oracle on every head
-    case = syn.Case("bwd_chan_wide", 2, 128, 130, 128, 128, "delta", "channel", "bf16", gate_scale=0.25,
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_channel_many_heads_wide_blocks(dk, dv):
+    # 256 heads (512 with d_v = 64 counted in 64-column blocks): the forward's
+    # state pass takes 64-column value blocks (the narrow 32-column blocks
+    # serve fewer blocks than CUs), so its saved states go through the wide
+    # copy path; saved and recomputed states agree and the gradients match the
+    # oracle on every head
+    case = syn.Case("bwd_chan_wide", 2, 128, 130, dk, dv, "delta", "channel", "bf16", gate_scale=0.25,
                     s0_std=0.2, case_id=152)
     a = check_bwd(case, use_states=True)
     x, gr = syn.chunk_inputs(case), syn.grad_inputs(case)
