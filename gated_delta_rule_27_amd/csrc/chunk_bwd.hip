@@ -614,12 +614,14 @@ __device__ __forceinline__ int dstate_offset(int i, int j, int dk)
 // ============================================================================
 // bwd_chain_kernel: the reverse state pass.  One workgroup per (b, h, 64 value
 // columns): waves 0-3 own 16 columns of dS each (dk/16 result tiles, kept in
-// registers for the whole sequence) and touch no global memory but their
-// dstates stores; waves 4-7 move the chunk operands from HBM to LDS.
-// Per chunk, newest first: store dS (= dS_{r+1}); phase 1 dZ = A^T dO + ->K dS,
+// registers for the whole sequence; with CHAN the chunk decay is a vector over
+// the key rows) and touch no global memory inside the loop; waves 4-7 move the
+// chunk operands from HBM to LDS, two chunks ahead (bf16), and dS to HBM.
+// Per chunk, newest first: dS (= dS_{r+1}) to LDS; phase 1 dZ = A^T dO + ->K dS,
 // dR = Tb^T dZ while the helpers stage <-Q^T, -<-K^T; phase 2
 // dS = exp(G_C) dS + <-Q^T dO - <-K^T dR while they stage the previous chunk's
-// A^T, Tb^T, ->K and dO^T (dO^T double-buffered, phase 2 reads it).
+// A^T, Tb^T, ->K and dO^T (dO^T double-buffered, phase 2 reads it) and copy
+// the dS of phase 1 to dstates.
 // ============================================================================
 template <typename T, int DK, int RULE, bool CHAN>
 __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__ dout, const T* __restrict__ ops,
