@@ -110,7 +110,7 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-def time_chunk(la, syn, case, dev, steps, warmup=2):
+def time_chunk(la, syn, case, dev, steps, warmup=20):
     """Event-timed chunk forward of one workload (inputs resident in HBM); the
     figures of a secondary line beside the headline one."""
     import torch
@@ -146,7 +146,7 @@ def time_chunk(la, syn, case, dev, steps, warmup=2):
             "path": chunk_path(case, wsb), "steps": steps}
 
 
-def time_prep(la, case, dev, steps, warmup=2):
+def time_prep(la, case, dev, steps, warmup=20):
     """Event-timed chunk forward from raw projections with the input
     preparation fused into the kernel (q, k L2-normalised, log-gate
     -softplus, beta sigmoid), at the shape of ``case``; raw inputs drawn on the
@@ -185,7 +185,7 @@ def time_prep(la, case, dev, steps, warmup=2):
             "path": "pipe with input preparation", "steps": steps}
 
 
-def time_normalized(la, syn, case, dev, steps, warmup=2):
+def time_normalized(la, syn, case, dev, steps, warmup=20):
     """Event-timed normalised linear attention (two add-rule passes and the
     division) at the shape and input laws of ``case``; minimal bytes as for the
     add rule plus the fp32 key sum."""
@@ -222,7 +222,7 @@ def time_normalized(la, syn, case, dev, steps, warmup=2):
             "path": "fused (values) + fused (ones) + divide", "steps": steps}
 
 
-def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
+def time_deltaproduct(la, syn, case, dev, steps, warmup=20):
     """Event-timed Gated DeltaProduct forward (inputs resident in HBM).  Minimal
     bytes: q and o once, k, v and beta per substep, the gate and the final
     state; nominal FLOPs: the GDN count over the n_h T virtual steps."""
@@ -257,7 +257,7 @@ def time_deltaproduct(la, syn, case, dev, steps, warmup=2):
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "path": "expand + pipe + gather", "steps": steps}
+            "path": "pipe over the virtual sequence in place (no expand or gather)", "steps": steps}
 
 
 def bwd_alg_bytes(B, H, T, dk, dv, s, rule, gate, states):

@@ -88,11 +88,17 @@ __device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
     mi = p;
 }
 
-template <int DK, int RULE, int GATE>
+// VIRT: Gated DeltaProduct read in place ("Linear Attention, Visualized",
+// "GDP as GDN over a virtual sequence"): the chunks walk the virtual sequence
+// of Tlen = T nh substeps (k, v, beta already in that layout), the query of
+// real token t sits on its last substep and its log-gate on its first, both
+// read from the real [B,H,T] layout, and only the last substep's output of each
+// token is written, to the real o [B,H,T,dv].
+template <int DK, int RULE, int GATE, bool VIRT>
 __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const float* s0, bf16* __restrict__ o,
-    float* s_final, int64_t Tlen, int DV, int nblocks, int prep)
+    float* s_final, int64_t Tlen, int DV, int nblocks, int prep, int nh)
 {
     using T = bf16;
     using Cfg = PipeCfg<DK, RULE, GATE>;
@@ -130,7 +136,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
     const int64_t bh = blk / nvb;
     const int vb = blk % nvb;
-    const T* qh = q + bh * Tlen * DK;
+    const int64_t Treal = VIRT ? Tlen / nh : Tlen;   // rows of q, g and o
+    const T* qh = q + bh * Treal * DK;
     const T* kh = k + bh * Tlen * DK;
     const T* vh = v + bh * Tlen * DV + vb * kDVB;
     const int64_t nchunks = (Tlen + kC - 1) / kC;
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             const int idx = (p * kNS + st) * E;
             const int row = idx / DK, col = idx % DK;
             const int64_t tr = t0 + row < Tlen ? t0 + row : Tlen - 1;
-            P.q[p] = *reinterpret_cast<const i4*>(qh + tr * DK + col);
+            P.q[p] = *reinterpret_cast<const i4*>(qh + (VIRT ? (int64_t)((int)tr / nh) : tr) * DK + col);
             P.k[p] = *reinterpret_cast<const i4*>(kh + tr * DK + col);
         }
     };
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     // loads them so that all its global accesses are unconditional)
     auto fetch_gate = [&](Pref& P, int64_t t0) {
         const int64_t tr = t0 + lane < Tlen ? t0 + lane : Tlen - 1;
-        P.g = GATED ? g[bh * Tlen + tr] : from_f32<T>(0.f);
+        P.g = GATED ? g[bh * Treal + (VIRT ? (int64_t)((int)tr / nh) : tr)] : from_f32<T>(0.f);
         P.b = DELTA ? beta[bh * Tlen + tr] : from_f32<T>(0.f);
     };
     // Q and K rows go to LDS with their columns in pcol order (mfma.h), four
@@ -191,10 +198,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             const int idx = (p * kNS + st) * E;
             const int row = idx / DK, col = idx % DK;
             const bool ok = t0 + row < Tlen;
+            // (virtual sequence: the query only on a token's last substep)
+            const bool okq = ok && (!VIRT || (int)(t0 + row) % nh == nh - 1);
             // every lane maps its vector (the L2 norm is reduced across lanes)
             const i4 qp = prep_qk<T, DK / E>(P.q[p], qk_map);
             const i4 kp = prep_qk<T, DK / E>(P.k[p], qk_map);
-            const i4 qv = ok ? qp : i4{0, 0, 0, 0};
+            const i4 qv = okq ? qp : i4{0, 0, 0, 0};
             const i4 kv = ok ? kp : i4{0, 0, 0, 0};
             *reinterpret_cast<i2*>(&Qb[row * LDQ + pcol(col)]) = i2{qv[0], qv[1]};
             *reinterpret_cast<i2*>(&Qb[row * LDQ + pcol(col + 4)]) = i2{qv[2], qv[3]};
@@ -215,7 +224,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     // (log2 e * prefix sum) so every decay factor is one hardware exp2.
     auto scan = [&](const Pref& P, int64_t t0, int sl) {
         const bool ok = t0 + lane < Tlen;
-        const float G = wave_prefix_sum((GATED && ok) ? prep_gate(to_f32(P.g), prep) * kLog2e : 0.f);
+        // (virtual sequence: the log-gate only on a token's first substep)
+        const bool okg = ok && (!VIRT || (int)(t0 + lane) % nh == 0);
+        const float G = wave_prefix_sum((GATED && okg) ? prep_gate(to_f32(P.g), prep) * kLog2e : 0.f);
         const float Glast = wave_last(G);
         Gsb[sl][lane] = G;
         gamb[sl][lane] = GATED ? fast_exp2(G) : 1.f;
@@ -230,14 +241,19 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     // hardware drops them, so no branch hides a store from the compiler's wait
     // counts (loads and stores share one vector-memory counter).
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        o + bh * Tlen * DV, (short)0, (int)(Tlen * DV * (int64_t)sizeof(T)), 0x00020000);
+        o + bh * Treal * DV, (short)0, (int)(Treal * DV * (int64_t)sizeof(T)), 0x00020000);
     auto copy_out = [&](int64_t tb, bool valid, int cw, int ln) {
         constexpr int NCW = 4, NCOPY = kC * kDVB / E, NROUND = NCOPY / (NCW * kWave);
 #pragma unroll
         for (int p = 0; p < NROUND; ++p) {
             const int idx = (p * NCW + cw) * kWave + ln;
             const int row = idx / (kDVB / E), col = (idx % (kDVB / E)) * E;
-            const int off = valid ? (int)(((tb + row) * DV + vb * kDVB + col) * (int64_t)sizeof(T)) : 0x7fffffff;
+            // virtual sequence: a token's last substep goes to its real row, the
+            // other substeps are dropped like rows past the end
+            const int64_t vr = tb + row;
+            const bool keep = valid && (!VIRT || (int)vr % nh == nh - 1);
+            const int off = keep ? (int)(((VIRT ? (int64_t)((int)vr / nh) : vr) * DV + vb * kDVB + col) * (int64_t)sizeof(T))
+                                 : 0x7fffffff;
             __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i4*>(&Os[row * LDV + col]), orsrc, off,
                                                    0, 0);
         }
@@ -640,16 +656,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     copy_out(tlast, true, wave - 4, lane);
 }
 
-template <int DK, int RULE, int GATE>
-hipError_t launch_t(const ChunkProblem& p, hipStream_t s)
+template <int DK, int RULE, int GATE, bool VIRT>
+hipError_t launch_t(const ChunkProblem& p, int nh, hipStream_t s)
 {
     const int nvb = p.dv / kDVB;
     const int64_t nblocks = p.B * p.H * nvb;
-    hipLaunchKernelGGL((chunk_pipe_kernel<DK, RULE, GATE>), dim3((unsigned)nblocks), dim3(kNT), 0, s,
+    hipLaunchKernelGGL((chunk_pipe_kernel<DK, RULE, GATE, VIRT>), dim3((unsigned)nblocks), dim3(kNT), 0, s,
                        static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                        static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.g),
                        static_cast<const bf16*>(p.beta), p.s0, static_cast<bf16*>(p.o), p.s_final, p.T,
-                       p.dv, (int)nblocks, p.prep);
+                       p.dv, (int)nblocks, p.prep, nh);
     return hipGetLastError();
 }
 
@@ -657,10 +673,10 @@ template <int DK>
 hipError_t by_rule_gate(const ChunkProblem& p, hipStream_t s)
 {
     if (p.rule == kRuleAdd)
-        return p.gate == kGateNone ? launch_t<DK, kRuleAdd, kGateNone>(p, s)
-                                   : launch_t<DK, kRuleAdd, kGateScalar>(p, s);
-    return p.gate == kGateNone ? launch_t<DK, kRuleDelta, kGateNone>(p, s)
-                               : launch_t<DK, kRuleDelta, kGateScalar>(p, s);
+        return p.gate == kGateNone ? launch_t<DK, kRuleAdd, kGateNone, false>(p, 1, s)
+                                   : launch_t<DK, kRuleAdd, kGateScalar, false>(p, 1, s);
+    return p.gate == kGateNone ? launch_t<DK, kRuleDelta, kGateNone, false>(p, 1, s)
+                               : launch_t<DK, kRuleDelta, kGateScalar, false>(p, 1, s);
 }
 
 }  // namespace
@@ -674,6 +690,15 @@ bool chunk_pipe_supported(const ChunkProblem& p)
 hipError_t launch_chunk_pipe(const ChunkProblem& p, hipStream_t s)
 {
     return p.dk == 64 ? by_rule_gate<64>(p, s) : by_rule_gate<128>(p, s);
+}
+
+hipError_t launch_chunk_pipe_virtual(const ChunkProblem& p, int nh, hipStream_t s)
+{
+    if (p.dk == 64)
+        return p.gate == kGateNone ? launch_t<64, kRuleDelta, kGateNone, true>(p, nh, s)
+                                   : launch_t<64, kRuleDelta, kGateScalar, true>(p, nh, s);
+    return p.gate == kGateNone ? launch_t<128, kRuleDelta, kGateNone, true>(p, nh, s)
+                               : launch_t<128, kRuleDelta, kGateScalar, true>(p, nh, s);
 }
 
 }  // namespace linattn

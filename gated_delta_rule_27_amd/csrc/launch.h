@@ -83,6 +83,10 @@ hipError_t launch_chunk_fused_save(const ChunkProblem& p, void* states, hipStrea
 // chunk r+1's intra-chunk work beside chunk r's state pass.
 bool chunk_pipe_supported(const ChunkProblem& p);
 hipError_t launch_chunk_pipe(const ChunkProblem& p, hipStream_t stream);
+// The same kernel over the virtual sequence of Gated DeltaProduct (delta rule,
+// p.T = T nh substeps): q, g and o in the real [B,H,T] layout, k, v and beta in
+// the virtual one; no expand or gather pass.
+hipError_t launch_chunk_pipe_virtual(const ChunkProblem& p, int nh, hipStream_t stream);
 
 // Two-kernel chunk path (intra-chunk precompute, then the state pass with the
 // output); used for the per-channel gate.

@@ -405,6 +405,13 @@ linattn_status linattn_deltaproduct_fwd(const linattn_deltaproduct_args* a, cons
         if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // the pipelined kernel reads q and g and writes o in the real token layout
+    // itself; the workspace stays part of the contract for the other paths
+    if (chunk_path(vp) == kPathPipe) {
+        vp.q = q; vp.k = k; vp.v = v; vp.g = g; vp.beta = beta;
+        vp.s0 = s0; vp.o = o; vp.s_final = s_final;
+        return launch_chunk_pipe_virtual(vp, a->nh, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+    }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     DeltaProductProblem p{a->B, a->H, a->T, a->nh, a->dk, a->dv, a->dtype, q, g,
                           a->T > 0 ? ws + l.qv : nullptr,

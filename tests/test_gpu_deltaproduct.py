@@ -60,6 +60,18 @@ def test_lengths(T):
     check_gdp(case, x, s0=x["s0"])
 
 
+@pytest.mark.parametrize("path,nh", [("fused", 2), ("fused", 3), ("pipe", 4), ("pipe", 5)])
+def test_both_routes(monkeypatch, path, nh):
+    # bf16 runs the pipelined kernel over the virtual sequence in place (q, g
+    # and o in the token layout); the fused path keeps the expand and gather
+    # passes around the chunk kernel: both against the oracle
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", path)
+    case = syn.DeltaProductCase("gdp_route", 1, 3, 83, nh, 128, 128, "scalar", "bf16",
+                                gate_scale=0.25, s0_std=0.3, case_id=124)
+    x = syn.deltaproduct_inputs(case)
+    check_gdp(case, x, s0=x["s0"])
+
+
 def test_zero_tokens_returns_initial_state():
     case = syn.DeltaProductCase("gdp_empty", 1, 2, 0, 3, 64, 64, "scalar", "bf16", s0_std=0.5,
                                 case_id=122)
