@@ -186,9 +186,9 @@ def time_prep(la, case, dev, steps, warmup=20):
 
 
 def time_normalized(la, syn, case, dev, steps, warmup=20):
-    """Event-timed normalised linear attention (two add-rule passes and the
-    division) at the shape and input laws of ``case``; minimal bytes as for the
-    add rule plus the fp32 key sum."""
+    """Event-timed normalised linear attention (no gate or a scalar gate: one
+    fused pass that carries the key sum beside the state) at the shape and input
+    laws of ``case``; minimal bytes as for the add rule plus the fp32 key sum."""
     import torch
     B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
     x = syn.chunk_inputs_torch(case, dev)
@@ -219,7 +219,7 @@ def time_normalized(la, syn, case, dev, steps, warmup=20):
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "path": "fused (values) + fused (ones) + divide", "steps": steps}
+            "path": "fused, one pass with the key sum", "steps": steps}
 
 
 def time_deltaproduct(la, syn, case, dev, steps, warmup=20):

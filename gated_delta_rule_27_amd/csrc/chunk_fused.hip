@@ -91,14 +91,48 @@ __device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
     mi = p;
 }
 
+// the E = 16 / sizeof(T) elements of a 16-byte vector, as floats and back
+template <typename T, typename V>
+__device__ __forceinline__ void vec_f32(V x, float (&f)[16 / sizeof(T)])
+{
+    T e[16 / sizeof(T)];
+    __builtin_memcpy(e, &x, 16);
+#pragma unroll
+    for (int j = 0; j < 16 / (int)sizeof(T); ++j) f[j] = to_f32(e[j]);
+}
+template <typename T, typename V>
+__device__ __forceinline__ V f32_vec(const float (&f)[16 / sizeof(T)])
+{
+    T e[16 / sizeof(T)];
+#pragma unroll
+    for (int j = 0; j < 16 / (int)sizeof(T); ++j) e[j] = from_f32<T>(f[j]);
+    V x;
+    __builtin_memcpy(&x, e, 16);
+    return x;
+}
+
 // SAVE: also write the state entering every chunk, states[b,h,r] = S_r
 // ([dk][dv] per chunk, rounded to the token type once), for the backward pass.
-template <typename T, int DK, int RULE, int GATE, bool SAVE = false>
+// NORM (add rule): normalised linear attention ("All sorts of famous Attention
+// Layers", "Linear Magic" and its normaliser) in the same pass.  The key sum
+// z_t = a_t z_{t-1} + k_t is one more state, a d_k vector; per chunk, with the
+// notation below,
+//   den_l   = gamma_l (q_l . z_r) + sum_m Aq[l][m]
+//   z_{r+1} = gamma_{C-1} z_r + sum_m rho_m k_m
+// and each output row leaves multiplied by 1 / den_l.  The state waves carry
+// z as one more value column: gamma_l (q_l . z_r) beside their Q S_r products
+// (phase P2a), z_{r+1} beside their state update (P4), each wave a quarter of
+// z's key blocks, with rho as that column of Z; in the next chunk's P1, while
+// the state waves finish this chunk, waves 4..7 each add the Aq row sums of
+// one 16-row block.
+template <typename T, int DK, int RULE, int GATE, bool SAVE = false, bool NORM = false>
 __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const float* s0, T* __restrict__ o,
-    float* s_final, T* __restrict__ states, int64_t Tlen, int DV, int nblocks, int prep)
+    float* s_final, T* __restrict__ states, int64_t Tlen, int DV, int nblocks, int prep,
+    const float* z0, float* z_final)
 {
+    static_assert(!NORM || RULE == kRuleAdd, "the normaliser belongs to the add rule");
     using Cfg = FusedCfg<T, DK, RULE, GATE>;
     using F = typename Frag16<T>::type;
     constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDV = Cfg::LDV;
@@ -123,6 +157,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     // gate values alternate between two buffers: the state waves still read the
     // previous chunk's while wave 4 writes this chunk's
     __shared__ __align__(16) float Gsb[2][kC], gamb[2][kC], rhob[2][kC], betb[2][kC];
+    // NORM: z_r and z_{r+1}, gamma_l (q_l . z_r), and the reciprocal
+    // denominators of two chunks (the one formed, the one copied out)
+    __shared__ __align__(16) float zSb[2][NORM ? DK : 4], denb[2][NORM ? kC : 4], qzs[2][NORM ? kC : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -147,6 +184,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 
     typedef __attribute__((__vector_size__(16))) int i4;
     const int64_t nchunks = (Tlen + kC - 1) / kC;
+    if constexpr (NORM)
+        for (int i = tid; i < DK; i += kNT) zSb[0][i] = z0 ? z0[bh * DK + i] : 0.f;
 
     // ---- P1 of every role: this thread's share of the chunk from registers
     // into LDS, then the next chunk's loads into the same registers.  Loads never
@@ -226,8 +265,16 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const int off = idx < NCOPY ? (int)(((tb + row) * DV + vb * kDVB + col) * (int64_t)sizeof(T))
                                         : 0x7fffffff;
             const int ro = idx < NCOPY ? row : 0;
-            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i4*>(&Os[ro * LDV + col]), orsrc, off,
-                                                   0, 0);
+            i4 x = *reinterpret_cast<const i4*>(&Os[ro * LDV + col]);
+            if constexpr (NORM) {
+                const float rd = denb[(int)(tb / kC) & 1][ro];   // 1 / den
+                float f[E];
+                vec_f32<T>(x, f);
+#pragma unroll
+                for (int j = 0; j < E; ++j) f[j] *= rd;
+                x = f32_vec<T, i4>(f);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, 0);
         }
     };
     const int64_t tlast = (nchunks - 1) * kC;     // start of the last chunk
@@ -245,6 +292,56 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
         for (int i = 0; i < NK; ++i) x = Mfma<T>::mma(fa[i], fb[i], x);
         return x;
+    };
+    // ---- NORM.  z is kept in natural key order; Qs columns, and the token
+    // columns of KsT and Aq, are stored in pcol order, whose position s holds
+    // logical column pcol_first(s & ~7) + (s & 4 ? 16 : 0) + (s & 3).
+    // Matrix-core right factor: a 16-row block whose row 0 is x (logical
+    // order, at the fragment's stored positions; x == nullptr: all ones) and
+    // whose other rows are zero, so lanes 0, 16, 32, 48 (result column 0)
+    // receive the products with x.  The loads are unconditional (in bounds for
+    // every lane) and the selection follows, so no lane mask guards them.
+    auto row0_frag = [&](const float* x, int k0, int ln) {
+        const bool r0 = (ln & 15) == 0;
+        if constexpr (sizeof(T) == 4) {
+            const int sp = k0 + (ln >> 4);
+            const float xv = x ? x[pcol_first(sp & ~7) + ((sp & 4) ? 16 : 0) + (sp & 3)] : 1.f;
+            return r0 ? xv : 0.f;
+        } else {
+            float f[E];
+            if (x) {
+                const int c0 = pcol_first(k0 + E * (ln >> 4));
+                const floatx4 a = *reinterpret_cast<const floatx4*>(&x[c0]);
+                const floatx4 b = *reinterpret_cast<const floatx4*>(&x[c0 + 16]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[j] = r0 ? a[j] : 0.f;
+                    f[j + 4] = r0 ? b[j] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < E; ++j) f[j] = r0 ? 1.f : 0.f;
+            }
+            return f32_vec<T, Fr>(f);
+        }
+    };
+    // Waves 4..7 (part = wave - 4) once chunk rp's state pass is under way
+    // (Aq and qz of chunk rp stay in place until the next chunk's P2a):
+    // 1 / den for row block part.
+    auto norm_tail = [&](int64_t rp, int part, int ln) {
+        constexpr int kS = Mfma<T>::kStep, NA = kC / kS;
+        const int cl = ln & 15, g4 = 4 * (ln >> 4);
+        const Fr f1 = row0_frag(nullptr, 0, ln);
+        floatx4 xa = zero4();
+#pragma unroll
+        for (int i = 0; i < NA; ++i) xa = Mfma<T>::mma(Mfma<T>::load(&Aq[part * 16 * LDC], LDC, i * kS, ln), f1, xa);
+        if (cl == 0) {
+            const floatx4 qz = *reinterpret_cast<const floatx4*>(&qzs[rp & 1][16 * part + g4]);
+            floatx4 d;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) d[rr] = 1.f / (qz[rr] + xa[rr]);
+            *reinterpret_cast<floatx4*>(&denb[rp & 1][16 * part + g4]) = d;
+        }
     };
     auto dot_tile = [&](const T* A, const T* B, int mi, int lj, int ln) {
         Fr fa[NK], fb[NK];
@@ -428,6 +525,24 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) Ot[li][rr] *= gl;
                 }
+                if constexpr (NORM) {
+                    // qz[l] = gamma_l (q_l . z_r) for this wave's row block l = 16 wave + cl:
+                    // z_r as value column 0 of a state-shaped tile (zero elsewhere)
+                    floatx4 oz = zero4();
+#pragma unroll
+                    for (int db = 0; db < ND; db += 2) {
+                        const floatx4 z0v = *reinterpret_cast<const floatx4*>(&zSb[r & 1][16 * db + g4]);
+                        const floatx4 z1v = *reinterpret_cast<const floatx4*>(&zSb[r & 1][16 * db + 16 + g4]);
+                        floatx4 za, zb;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            za[rr] = cl == 0 ? z0v[rr] : 0.f;
+                            zb[rr] = cl == 0 ? z1v[rr] : 0.f;
+                        }
+                        oz = mma_pair<T>(pair_regs<T>(za, zb), pair_lds(&Qs[16 * wave * LDQ + 16 * db], LDQ, ln), oz);
+                    }
+                    if (g4 == 0) qzs[r & 1][16 * wave + cl] = gam[16 * wave + cl] * oz[0];
+                }
             };
             // K^T through the matrix core (this wave's quarter of the tiles)
             auto ksT = [&]() {
@@ -538,6 +653,29 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 S[db] = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
                                     mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
             }
+            if constexpr (NORM) {
+                // z_{r+1} = gamma_{C-1} z_r + K^T rho for this wave's key blocks: rho
+                // as value column 0 of Z, z as value column 0 of the state (lanes
+                // with cl = 0 hold and store it)
+                floatx4 rz[NL];
+#pragma unroll
+                for (int lj = 0; lj < NL; ++lj) {
+                    const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) rz[lj][rr] = cl == 0 ? rh[rr] : 0.f;
+                }
+                const auto rz01 = pair_regs<T>(rz[0], rz[1]), rz23 = pair_regs<T>(rz[2], rz[3]);
+#pragma unroll
+                for (int d2 = 0; d2 < ND / 4; ++d2) {
+                    const int db = (ND / 4) * wave + d2;
+                    floatx4 zt = *reinterpret_cast<const floatx4*>(&zSb[r & 1][16 * db + g4]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) zt[rr] *= gC;
+                    zt = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), rz23,
+                                     mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), rz01, zt));
+                    if (cl == 0) *reinterpret_cast<floatx4*>(&zSb[(r + 1) & 1][16 * db + g4]) = zt;
+                }
+            }
         }
         if (s_final) {
             const int cl = lane & 15, g4 = 4 * (lane >> 4);
@@ -577,6 +715,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
             fetch_gate(t0 + kC < tlast ? t0 + kC : tlast);
+            if constexpr (NORM)
+                if (r > 0) norm_tail(r - 1, 0, ln);
             lds_barrier();
 
             if constexpr (DELTA) {
@@ -635,6 +775,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const float* const bet = betb[r & 1];
             stage(t0);
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
+            if constexpr (NORM)
+                if (r > 0) norm_tail(r - 1, iw, ln);
             lds_barrier();
             // ---- P2a ----
             if constexpr (DELTA) {
@@ -652,20 +794,35 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 
     // the last chunk's output, once every state wave has staged it
     __syncthreads();
+    if constexpr (NORM) {
+        if (wave >= 4 && nchunks > 0) norm_tail(nchunks - 1, wave - 4, lane);
+        __syncthreads();
+    }
     if (wave >= kW0 && nchunks > 0) copy_out((nchunks - 1) * kC, wave - kW0, lane);
+    if constexpr (NORM)
+        if (z_final && vb == 0)
+            for (int i = tid; i < DK; i += kNT) z_final[bh * DK + i] = zSb[nchunks & 1][i];
 }
 
-template <typename T, int DK, int RULE, int GATE, bool SAVE>
-hipError_t launch_t(const ChunkProblem& p, void* states, hipStream_t s)
+template <typename T, int DK, int RULE, int GATE, bool SAVE, bool NORM = false>
+hipError_t launch_t(const ChunkProblem& p, void* states, hipStream_t s, const float* z0 = nullptr,
+                    float* z_final = nullptr)
 {
     const int nvb = p.dv / kDVB;
     const int64_t nblocks = p.B * p.H * nvb;
-    hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE, SAVE>), dim3((unsigned)nblocks), dim3(kNT), 0,
-                       s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
+    hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE, SAVE, NORM>), dim3((unsigned)nblocks), dim3(kNT),
+                       0, s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
                        static_cast<const T*>(p.v), static_cast<const T*>(p.g),
                        static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, static_cast<T*>(states),
-                       p.T, p.dv, (int)nblocks, p.prep);
+                       p.T, p.dv, (int)nblocks, p.prep, z0, z_final);
     return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t norm_by_gate(const ChunkProblem& p, const float* z0, float* z_final, hipStream_t s)
+{
+    return p.gate == kGateNone ? launch_t<T, DK, kRuleAdd, kGateNone, false, true>(p, nullptr, s, z0, z_final)
+                               : launch_t<T, DK, kRuleAdd, kGateScalar, false, true>(p, nullptr, s, z0, z_final);
 }
 
 template <typename T, int DK, bool SAVE>
@@ -693,6 +850,14 @@ hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t s)
         return p.dk == 64 ? by_rule_gate<bf16, 64, false>(p, nullptr, s)
                           : by_rule_gate<bf16, 128, false>(p, nullptr, s);
     return by_rule_gate<float, 64, false>(p, nullptr, s);
+}
+
+hipError_t launch_chunk_fused_normalized(const ChunkProblem& p, const float* z0, float* z_final, hipStream_t s)
+{
+    if (p.rule != kRuleAdd) return hipErrorInvalidValue;
+    if (p.dtype == kBF16)
+        return p.dk == 64 ? norm_by_gate<bf16, 64>(p, z0, z_final, s) : norm_by_gate<bf16, 128>(p, z0, z_final, s);
+    return norm_by_gate<float, 64>(p, z0, z_final, s);
 }
 
 hipError_t launch_chunk_fused_save(const ChunkProblem& p, void* states, hipStream_t s)

@@ -79,6 +79,11 @@ hipError_t launch_chunk_fused(const ChunkProblem& p, hipStream_t stream);
 // The same kernel also writing the state entering every chunk,
 // states [B,H,nchunks,dk,dv] in the token type (for the backward pass).
 hipError_t launch_chunk_fused_save(const ChunkProblem& p, void* states, hipStream_t stream);
+// The same kernel for normalised linear attention (add rule, gate NONE or
+// SCALAR): it also carries the key sum z (z0, z_final [B,H,dk] fp32, either
+// may be NULL for zero / not wanted) and writes o_t = (q_t S_t) / (q_t . z_t).
+hipError_t launch_chunk_fused_normalized(const ChunkProblem& p, const float* z0, float* z_final,
+                                         hipStream_t stream);
 // Single-pass chunk kernel for bf16 tokens (gate NONE or SCALAR), pipelined:
 // chunk r+1's intra-chunk work beside chunk r's state pass.
 bool chunk_pipe_supported(const ChunkProblem& p);

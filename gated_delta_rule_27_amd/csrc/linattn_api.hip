@@ -454,11 +454,18 @@ linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args* a, const l
     const NormLayout l = norm_layout(p, pd);
     if (!workspace || workspace_bytes < l.total) return LINATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // gate NONE or SCALAR on the fused path: one pass carries z beside S; the
+    // workspace stays part of the contract for the two-pass route
+    if (chunk_path(p) == kPathFused) {
+        p.q = q; p.k = k; p.v = v; p.g = g; p.beta = nullptr;
+        p.s0 = s0; p.o = o; p.s_final = s_final;
+        return launch_chunk_fused_normalized(p, z0, z_final, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+    }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     NormalizedProblem np{p.B * p.H * p.T, p.B * p.H, p.dk, p.dv, p.dtype, ws + l.ones, z0,
                          reinterpret_cast<float*>(ws + l.s0d), o, ws + l.den,
                          reinterpret_cast<const float*>(ws + l.sfd), z_final};
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_norm_prepare(np, s) != hipSuccess) return LINATTN_ERR_LAUNCH;
     // numerator: the add rule on the values; denominator: on the block of ones
     st = linattn_chunk_fwd_prep(a, prep, q, k, v, g, nullptr, s0, o, s_final, ws + l.cws,

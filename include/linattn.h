@@ -172,7 +172,10 @@ size_t linattn_normalized_workspace_bytes(const linattn_chunk_args *a);
  *   z0       [B,H,dk] fp32 initial key sum, or NULL for zero
  *   z_final  [B,H,dk] fp32 final key sum, or NULL
  *   workspace: at least linattn_normalized_workspace_bytes(a) bytes,
- *            16-byte aligned (always needed: the denominator pass writes to it)
+ *            16-byte aligned; always required (the per-channel gate runs a
+ *            second, denominator pass that writes to it; no gate and the
+ *            scalar gate run one pass that carries z beside S and leave it
+ *            untouched)
  */
 linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args *a, const linattn_prep_args *prep,
                                             const void *q, const void *k, const void *v,

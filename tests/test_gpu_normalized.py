@@ -1,5 +1,7 @@
-"""Parity of normalised linear attention (HIP, through the C ABI: two add-rule
-passes and a division) with the fp64 oracle's normalised recurrence: positive
+"""Parity of normalised linear attention (HIP, through the C ABI: one fused pass
+carrying the key sum for no gate and the scalar gate, two add-rule passes and a
+division for the per-channel gate or when another chunk path is selected) with
+the fp64 oracle's normalised recurrence: positive
 features (elu + 1), every head size and dtype, no gate / scalar gate /
 per-channel gate, carried S_0 and z_0, the feature map fused from raw
 projections, empty sequences and resume."""
@@ -55,6 +57,25 @@ def test_small_ragged(dtype, dk, dv, gate):
                     s0_std=0.3, case_id=140)
     x, s0, z0 = inputs(case, 140)
     check(case, x, s0, z0)
+
+
+@pytest.mark.parametrize("path,gate", [("pipe", "none"), ("split", "scalar"), ("pipe", "scalar")])
+def test_two_pass_route(monkeypatch, path, gate):
+    # another chunk path selected: the two add-rule passes and the division
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", path)
+    case = syn.Case("norm_route", 1, 3, 170, 128, 128, "add", gate, "bf16", qk="elu1", gate_scale=0.25,
+                    s0_std=0.3, case_id=145)
+    x, s0, z0 = inputs(case, 145)
+    check(case, x, s0, z0)
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar"])
+def test_long_sequence(gate):
+    # 63 chunks and a ragged tail through the one-pass kernel, no initial states
+    case = syn.Case("norm_long", 1, 2, 4001, 128, 128, "add", gate, "bf16", qk="elu1", gate_scale=0.05,
+                    case_id=146)
+    x, _, _ = inputs(case, 146)
+    check(case, x, None, None)
 
 
 def test_channel_gate():
