@@ -71,6 +71,7 @@ def test_chunk_validation(lib):
     assert call_chunk(lib, mk(), s0=FAKE, sf=FAKE + 16) == 6     # partial overlap
     assert call_chunk(lib, mk(B=0)) == 0                         # nothing to do
     assert call_chunk(lib, mk(T=1 << 24, dv=128)) == 3           # one head's output >= 2 GiB
+    assert call_chunk(lib, mk(T=1 << 23, dv=128)) == 3           # exactly 2 GiB: one token too many
     assert call_chunk(lib, mk(T=1 << 23, dv=128, gate="channel", dk=128), g=FAKE) == 3
     assert lib.linattn_chunk_workspace_bytes(ctypes.byref(mk())) == 0
     # the per-channel gate runs the two-kernel path, which stages per-chunk tiles
@@ -130,6 +131,7 @@ def test_deltaproduct_validation(lib):
     assert call(mk(), s0=FAKE, sf=FAKE + 16) == 6                 # partial state overlap
     assert call(mk()) == 4                                        # workspace missing
     assert call(mk(T=1 << 22, nh=4, dv=128)) == 3                 # virtual output >= 2 GiB
+    assert call(mk(T=1 << 22, nh=2, dv=128)) == 3                 # virtual output exactly 2 GiB
     assert call(mk(B=0)) == 0
     # expanded queries + expanded gates + virtual outputs, 256-byte pieces
     assert lib.linattn_deltaproduct_workspace_bytes(ctypes.byref(mk())) == \
