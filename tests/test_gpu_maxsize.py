@@ -3,7 +3,7 @@ under 2^31 for bf16 tokens, so T = 8,388,607 at d_v = 128 (one head; the
 32-bit offsets of the kernels' buffer stores are at their limit).  Covered:
 the pipelined GDN kernel, the single-pass add-rule kernel, the two-kernel KDA
 path, the one-pass normalised kernel and Gated DeltaProduct over its virtual
-sequence read in place.
+sequence read in place; and one decode step over a state of 2^32 elements.
 
 The decay is strong (a_t <= e^-0.7 < 0.5 per token, per channel for KDA), and
 with unit-norm keys and beta in (0, 1) the delta-rule factor (I - beta k k^T)
@@ -144,3 +144,30 @@ def test_deltaproduct_in_place_max_length():
         w = piece(x, sl)
         return oracle.deltaproduct(w["q"], w["k"], w["v"], w["g"], w["beta"], None, gate="scalar")
     check_ends(f"gated deltaproduct n_h={nh} in place", T, (o, s), ref)
+
+
+@pytest.mark.timeout(600)
+def test_decode_state_past_2g_elements():
+    # 8192 sequences x 32 heads x 128 x 128 fp32: 2^32 state elements (16 GiB),
+    # so the second half of the heads starts past element 2^31 (byte offsets
+    # past 2^33); sampled heads at both ends and on each side of that boundary
+    # against the oracle's step
+    import gated_delta_rule_27_amd as la
+    N, H, d = 8192, 32, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(406)
+    state = torch.randn((N, H, d, d), generator=gen, device="cuda") * 0.1
+    x = draw({"q": (N, H, d), "k": (N, H, d), "v": (N, H, d), "g": (N, H), "beta": (N, H)},
+             seed=407, unit=("q", "k"))
+    picks = [(0, 0), (4095, 31), (4096, 0), (8191, 30), (8191, 31)]
+    before = [host(state[n, h]) for n, h in picks]
+    o = la.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], state, rule="delta", gate="scalar")
+    torch.cuda.synchronize()
+    for i, (n, h) in enumerate(picks):
+        one = {k2: host(t[n, h])[None, None] for k2, t in x.items()}
+        o_ref, s_ref = oracle.decode_step(one["q"], one["k"], one["v"], one["g"], one["beta"],
+                                          before[i][None, None], rule="delta", gate="scalar")
+        eo = rel_l2(host(o[n, h]), o_ref[0, 0])
+        es = rel_l2(host(state[n, h]), s_ref[0, 0])
+        note(f"[max] decode head ({n},{h}): rel L2 o {eo:.3e} state {es:.3e}")
+        assert eo <= TOL["bf16"] and es <= 1e-5
