@@ -94,12 +94,14 @@ __device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
 // real token t sits on its last substep and its log-gate on its first, both
 // read from the real [B,H,T] layout, and only the last substep's output of each
 // token is written, to the real o [B,H,T,dv].
-template <int DK, int RULE, int GATE, bool VIRT>
+// NHC > 0 fixes n_h at compile time (its divisions become shifts for 2).
+template <int DK, int RULE, int GATE, bool VIRT, int NHC = 0>
 __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ g, const bf16* __restrict__ beta, const float* s0, bf16* __restrict__ o,
-    float* s_final, int64_t Tlen, int DV, int nblocks, int prep, int nh)
+    float* s_final, int64_t Tlen, int DV, int nblocks, int prep, int nh_arg)
 {
+    const int nh = NHC > 0 ? NHC : nh_arg;
     using T = bf16;
     using Cfg = PipeCfg<DK, RULE, GATE>;
     using F = typename Frag16<T>::type;
@@ -656,12 +658,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     copy_out(tlast, true, wave - 4, lane);
 }
 
-template <int DK, int RULE, int GATE, bool VIRT>
+template <int DK, int RULE, int GATE, bool VIRT, int NHC = 0>
 hipError_t launch_t(const ChunkProblem& p, int nh, hipStream_t s)
 {
     const int nvb = p.dv / kDVB;
     const int64_t nblocks = p.B * p.H * nvb;
-    hipLaunchKernelGGL((chunk_pipe_kernel<DK, RULE, GATE, VIRT>), dim3((unsigned)nblocks), dim3(kNT), 0, s,
+    hipLaunchKernelGGL((chunk_pipe_kernel<DK, RULE, GATE, VIRT, NHC>), dim3((unsigned)nblocks), dim3(kNT), 0, s,
                        static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                        static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.g),
                        static_cast<const bf16*>(p.beta), p.s0, static_cast<bf16*>(p.o), p.s_final, p.T,
@@ -677,6 +679,18 @@ hipError_t by_rule_gate(const ChunkProblem& p, hipStream_t s)
                                    : launch_t<DK, kRuleAdd, kGateScalar, false>(p, 1, s);
     return p.gate == kGateNone ? launch_t<DK, kRuleDelta, kGateNone, false>(p, 1, s)
                                : launch_t<DK, kRuleDelta, kGateScalar, false>(p, 1, s);
+}
+
+// the virtual sequence with n_h fixed at compile time for 2, 3 and 4
+template <int DK, int GATE>
+hipError_t virtual_by_nh(const ChunkProblem& p, int nh, hipStream_t s)
+{
+    switch (nh) {
+    case 2: return launch_t<DK, kRuleDelta, GATE, true, 2>(p, nh, s);
+    case 3: return launch_t<DK, kRuleDelta, GATE, true, 3>(p, nh, s);
+    case 4: return launch_t<DK, kRuleDelta, GATE, true, 4>(p, nh, s);
+    default: return launch_t<DK, kRuleDelta, GATE, true>(p, nh, s);
+    }
 }
 
 }  // namespace
@@ -695,10 +709,8 @@ hipError_t launch_chunk_pipe(const ChunkProblem& p, hipStream_t s)
 hipError_t launch_chunk_pipe_virtual(const ChunkProblem& p, int nh, hipStream_t s)
 {
     if (p.dk == 64)
-        return p.gate == kGateNone ? launch_t<64, kRuleDelta, kGateNone, true>(p, nh, s)
-                                   : launch_t<64, kRuleDelta, kGateScalar, true>(p, nh, s);
-    return p.gate == kGateNone ? launch_t<128, kRuleDelta, kGateNone, true>(p, nh, s)
-                               : launch_t<128, kRuleDelta, kGateScalar, true>(p, nh, s);
+        return p.gate == kGateNone ? virtual_by_nh<64, kGateNone>(p, nh, s) : virtual_by_nh<64, kGateScalar>(p, nh, s);
+    return p.gate == kGateNone ? virtual_by_nh<128, kGateNone>(p, nh, s) : virtual_by_nh<128, kGateScalar>(p, nh, s);
 }
 
 }  // namespace linattn
