@@ -449,7 +449,7 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
               "multi-GPU path; each head's recurrence is independent, so a multi-GPU run "
               "would shard heads with no communication", file=sys.stderr)
         sys.exit(2)
