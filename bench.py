@@ -305,6 +305,41 @@ def rmw_ceiling(dev, mib=1024, reps=20):
     return {"kernel": f"torch in-place scale of {mib} MiB fp32", "GBps": round(2 * mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)}
 
 
+def mfma_achievable(dev, grid=2048, iters=20000, reps=5):
+    """Dense bf16 matrix-core throughput a register-only MFMA loop reaches on
+    this device (``peak/mfma_peak.hip``: 8 independent accumulation chains per
+    wave, 4 waves per workgroup, no memory traffic in the loop), for the two
+    bf16 shapes; the best of ``reps`` event-timed launches of each."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_delta_rule_27_amd", "libmfmapeak.so"))
+    lib.mfma_peak_threads.restype = ctypes.c_int
+    lib.mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.mfma_peak_flops.restype = ctypes.c_double
+    lib.mfma_peak_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_peak_launch.restype = ctypes.c_int
+    out = torch.empty(grid * lib.mfma_peak_threads(), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {"kernel": f"register-only MFMA loop, {grid} workgroups x 4 waves x {iters} rounds of 8 chains"}
+    for shape, name in ((0, "16x16x32_bf16"), (1, "32x32x16_bf16")):
+        best = None
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = lib.mfma_peak_launch(shape, grid, iters, ctypes.c_void_p(out.data_ptr()), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"mfma_peak_launch failed ({rc})")
+            ms = e0.elapsed_time(e1)
+            if r > 0 and (best is None or ms < best):
+                best = ms
+        res[f"TFLOPs_{name}"] = round(lib.mfma_peak_flops(shape, grid, iters) / (best * 1e-3) / 1e12, 1)
+    del out
+    return res
+
+
 def time_backward(la, syn, case, dev, steps, warmup=2):
     """Event-timed training passes at the shape and laws of ``case``: the
     forward that keeps the chunk states, the backward from those states, and
@@ -426,6 +461,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the register-only MFMA loop that measures the achievable matrix-core rate")
     ap.add_argument("--cpu-heads", type=int, default=128,
                     help="heads of the workload the CPU oracle runs for its baseline")
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
@@ -500,6 +537,9 @@ def main():
     aflops = chunk_nominal_flops(B, H, T, dk, dv, case.rule)
     gbps = abytes / (ms * 1e-3) / 1e9
     tflops = aflops / (ms * 1e-3) / 1e12
+
+    # ---------------- measured matrix-core ceiling -------------------------------
+    peak = None if args.no_peak_probe else mfma_achievable(dev)
 
     # ---------------- secondary chunk workloads (reported beside the headline) ----
     others = []
@@ -577,6 +617,13 @@ def main():
         oracle.recurrence(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], None, rule=case.rule,
                           gate=case.gate, nthreads=cores)
         wall = time.perf_counter() - t0
+        # one thread on a subset of the same heads, to show how the oracle scales
+        n1 = min(8, nh)
+        xs1 = {n: v[:, :n1] for n, v in xs.items()}
+        t1 = time.perf_counter()
+        oracle.recurrence(xs1["q"], xs1["k"], xs1["v"], xs1["g"], xs1["beta"], None, rule=case.rule,
+                          gate=case.gate, nthreads=1)
+        wall1 = time.perf_counter() - t1
         cpu = {
             "value": round(nh * T / H / wall, 1),
             "unit": "tokens/s",
@@ -586,6 +633,9 @@ def main():
                       f"token recurrence, OpenMP over heads), {wall:.2f} s wall; tokens/s = "
                       f"head-tokens / {H} heads / wall",
             "cpu_model": cpu_model(),
+            "one_thread": {"value": round(n1 * T / H / wall1, 1), "unit": "tokens/s", "cores": 1,
+                           "sample": f"{n1} heads x {T} tokens, {wall1:.2f} s wall",
+                           "speedup_all_cores": round((nh / wall) / (n1 / wall1), 2)},
         }
 
     line = {
@@ -607,15 +657,19 @@ def main():
                    "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": 64,
                    "rule": case.rule, "gate": case.gate, "parallelism": "single GPU",
                    "path": path},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+        # the chunk forward is a dense contraction judged by its matrix-core
+        # fraction; its HBM fraction (minimal bytes) stands beside it
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": counter_traffic(CHUNK_PROFILE, CHUNK_SOURCES) if path == "pipe" else None,
                      "kernel": CHUNK_KERNELS[path],
-                     "alg_bytes_per_launch": abytes},
-        "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 2),
-                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                          "nominal_flops_per_launch": aflops},
+                     "nominal_flops_per_launch": aflops,
+                     "frac_of_measured_peak": (round(tflops / peak["TFLOPs_16x16x32_bf16"], 4)
+                                               if peak else None)},
+        "roofline_hbm": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "alg_bytes_per_launch": abytes},
+        "mfma_achievable": peak,
         "decode": decode,
         "other_chunk_workloads": others,
         "cpu_baseline": cpu,

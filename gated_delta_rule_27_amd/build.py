@@ -1,7 +1,9 @@
 """Build the HIP library ``liblinattn.so`` for gfx950 with hipcc.
 
 Every ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
-parallel) and linked into ``gated_delta_rule_27_amd/liblinattn.so``.
+parallel) and linked into ``gated_delta_rule_27_amd/liblinattn.so``.  The
+matrix-core throughput probe that bench.py reports beside the datasheet peak
+(``peak/mfma_peak.hip``) is built on its own into ``libmfmapeak.so``.
 """
 from __future__ import annotations
 
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
+PEAK_SRC = os.path.join(HERE, "peak", "mfma_peak.hip")
+PEAK_LIB = os.path.join(HERE, "libmfmapeak.so")
 ARCH = os.environ.get("LINATTN_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,8 +54,13 @@ def build(verbose: bool = True) -> str:
     subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                    check=True)
     os.replace(tmp, LIB)
+    ptmp = PEAK_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", ptmp, PEAK_SRC], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAK_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(ptmp, PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 
