@@ -451,18 +451,34 @@ linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args* a, const l
     st = check_states(p, s0, s_final);
     if (st != LINATTN_OK) return st;
     if ((z0 && !aligned16(z0)) || (z_final && !aligned16(z_final))) return LINATTN_ERR_UNSUPPORTED;
+    // z_final may alias z0 exactly (the key sum carried in place), but must not
+    // partially overlap it
+    const size_t zbytes = (size_t)(p.B * p.H) * p.dk * sizeof(float);
+    if (z0 && z_final && z0 != z_final) {
+        const char* a0 = reinterpret_cast<const char*>(z0);
+        const char* a1 = reinterpret_cast<const char*>(z_final);
+        if (a0 < a1 + zbytes && a1 < a0 + zbytes) return LINATTN_ERR_ARG;
+    }
     const NormLayout l = norm_layout(p, pd);
     if (!workspace || workspace_bytes < l.total) return LINATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // gate NONE or SCALAR on the fused path: one pass carries z beside S; the
-    // workspace stays part of the contract for the two-pass route
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    // gate NONE or SCALAR on the fused path: one pass carries z beside S.
+    // Every value block of a head reads z0 when it starts, but only the first
+    // writes z_final, so an in-place z0 is read from a copy in the workspace
+    // (the denominator pass's state region, unused on this route)
     if (chunk_path(p) == kPathFused) {
+        const float* zin = z0;
+        if (z0 && z0 == z_final) {
+            if (hipMemcpyAsync(ws + l.s0d, z0, zbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+                return LINATTN_ERR_LAUNCH;
+            zin = reinterpret_cast<const float*>(ws + l.s0d);
+        }
         p.q = q; p.k = k; p.v = v; p.g = g; p.beta = nullptr;
         p.s0 = s0; p.o = o; p.s_final = s_final;
-        return launch_chunk_fused_normalized(p, z0, z_final, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
+        return launch_chunk_fused_normalized(p, zin, z_final, s) == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
     }
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
     NormalizedProblem np{p.B * p.H * p.T, p.B * p.H, p.dk, p.dv, p.dtype, ws + l.ones, z0,
                          reinterpret_cast<float*>(ws + l.s0d), o, ws + l.den,
                          reinterpret_cast<const float*>(ws + l.sfd), z_final};

@@ -170,12 +170,13 @@ size_t linattn_normalized_workspace_bytes(const linattn_chunk_args *a);
  *
  *   q, k, v, g, s0, o, s_final: as for linattn_chunk_fwd_prep (no beta)
  *   z0       [B,H,dk] fp32 initial key sum, or NULL for zero
- *   z_final  [B,H,dk] fp32 final key sum, or NULL
+ *   z_final  [B,H,dk] fp32 final key sum, or NULL; may alias z0 exactly (the
+ *            key sum carried in place), a partial overlap is LINATTN_ERR_ARG
  *   workspace: at least linattn_normalized_workspace_bytes(a) bytes,
  *            16-byte aligned; always required (the per-channel gate runs a
  *            second, denominator pass that writes to it; no gate and the
- *            scalar gate run one pass that carries z beside S and leave it
- *            untouched)
+ *            scalar gate run one pass that carries z beside S and use it only
+ *            to hold a copy of z0 when z_final aliases it)
  */
 linattn_status linattn_chunk_fwd_normalized(const linattn_chunk_args *a, const linattn_prep_args *prep,
                                             const void *q, const void *k, const void *v,

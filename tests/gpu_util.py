@@ -50,6 +50,20 @@ def worst_head(x, ref):
                                            ref.reshape(-1, *ref.shape[-2:])))
 
 
+def worst_block(x, ref, block=64):
+    """Largest relative L2 error over consecutive blocks of ``block`` tokens
+    (axis 0 = tokens) and the first token of that block: one wrong token moves
+    a whole head's relative L2 by only ~1/sqrt(T), a block's by ~1/sqrt(block)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    worst, at = 0.0, 0
+    for t0 in range(0, ref.shape[0], block):
+        e = rel_l2(x[t0:t0 + block], ref[t0:t0 + block])
+        if e > worst:
+            worst, at = e, t0
+    return worst, at
+
+
 def run_chunk(case, x, s0=None):
     import gated_delta_rule_27_amd as la
     o, s = la.chunk_fwd(dev(x["q"], case.dtype), dev(x["k"], case.dtype), dev(x["v"], case.dtype),

@@ -8,7 +8,7 @@ import torch
 
 import synthetic as syn
 from gpu_util import (TOL, check_chunk, dev, dev_state, host, note, oracle_chunk, rel_l2,
-                      run_chunk, worst_head)
+                      run_chunk, worst_block, worst_head)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -29,12 +29,16 @@ def sampled_full_size(case, heads):
     for (b, h) in heads:
         xs = {kk: (None if vv is None else vv[b:b + 1, h:h + 1]) for kk, vv in x.items()}
         oref, sref = oracle_chunk(case, xs)
-        eo = rel_l2(host(o[b, h]), oref[0, 0])
+        oh = host(o[b, h])
+        eo = rel_l2(oh, oref[0, 0])
         es = rel_l2(host(s[b, h]), sref[0, 0])
-        note(f"    head ({b},{h}): rel L2 o={eo:.3e} S={es:.3e}")
-        errs.append((eo, es))
+        wb, at = worst_block(oh, oref[0, 0])
+        note(f"    head ({b},{h}): rel L2 o={eo:.3e} S={es:.3e}; worst 64-token block {wb:.3e} at t={at}")
+        errs.append((eo, es, wb))
     tol = TOL[case.dtype]
+    # the bound holds for each head and for each 64-token block of it
     assert max(e[0] for e in errs) <= tol and max(e[1] for e in errs) <= tol
+    assert max(e[2] for e in errs) <= tol
 
 
 def test_cfg1_gdn_fp32_full():
@@ -113,6 +117,32 @@ def test_add_rule_unnormalised_keys_long():
     case = syn.Case("addlong", 1, 2, 4096, 128, 128, "add", "none", "bf16", qk="elu1",
                     case_id=104)
     check_chunk(case, syn.chunk_inputs(case))
+
+
+UNDERFLOW = [(rule, path, dtype, dk, scale)
+             for scale in (12.0, 30.0)
+             for (rule, path, dtype, dk) in (("delta", "pipe", "bf16", 128), ("delta", "fused", "bf16", 128),
+                                             ("add", "fused", "bf16", 128), ("add", "pipe", "bf16", 64),
+                                             ("delta", "fused", "fp32", 64), ("add", "fused", "fp32", 64))]
+
+
+@pytest.mark.parametrize("rule,path,dtype,dk,scale", UNDERFLOW)
+def test_scalar_gate_underflow_in_chunk(monkeypatch, rule, path, dtype, dk, scale):
+    # log-gates ~ -10 (scale 12) and ~ -24 (scale 30) per token: exp(G) of a
+    # chunk's prefix underflows fp32 within a few tokens, so every decay
+    # factor must come from differences G_l - G_m, never from exp(G_l) and
+    # exp(-G_m) separately.  Both single-pass kernels, both token dtypes.
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", path)
+    case = syn.Case("underflow", 2, 2, 200, dk, 128, rule, "scalar", dtype, gate_scale=scale,
+                    s0_std=0.3, case_id=117)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
+    o, _ = run_chunk(case, x, x["s0"])
+    oref, _ = oracle_chunk(case, x, x["s0"])
+    oh = host(o)
+    wb = max(worst_block(oh[b, h], oref[b, h])[0] for b in range(case.B) for h in range(case.H))
+    note(f"    worst 64-token block {wb:.3e}")
+    assert wb <= TOL[dtype]
 
 
 def test_zero_tokens_copies_state():
@@ -246,10 +276,12 @@ def test_cfg4_kda_bf16_full_size_sampled():
     xs = {kk: (None if vv is None else vv[:, None]) for kk, vv in xs.items()}
     oref, sref = oracle_chunk(case, xs)
     for i, (b, h) in enumerate(heads):
-        eo = rel_l2(host(o[b, h]), oref[i, 0])
+        oh = host(o[b, h])
+        eo = rel_l2(oh, oref[i, 0])
         es = rel_l2(host(s[b, h]), sref[i, 0])
-        note(f"    head ({b},{h}): rel L2 o={eo:.3e} S={es:.3e}")
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+        wb, at = worst_block(oh, oref[i, 0])
+        note(f"    head ({b},{h}): rel L2 o={eo:.3e} S={es:.3e}; worst 64-token block {wb:.3e} at t={at}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"] and wb <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("rule", ["add", "delta"])

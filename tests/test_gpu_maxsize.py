@@ -9,9 +9,10 @@ The decay is strong (a_t <= e^-0.7 < 0.5 per token, per channel for KDA), and
 with unit-norm keys and beta in (0, 1) the delta-rule factor (I - beta k k^T)
 does not grow the state, so a token's output and the final state depend on
 what lies more than W tokens back only up to 0.5^W of their size.  The oracle
-therefore checks the first tokens from the start and the last ones from a
-window of W earlier tokens started at the zero state (W = 160: 0.5^160 is
-far below the bf16 tolerance)."""
+therefore checks the first tokens from the start, and the last ones and two
+runs in the middle (one across the output row at byte offset 2^30) each from a
+window of W earlier tokens started at the zero state (W = 160: 0.5^160 is far
+below the bf16 tolerance)."""
 import numpy as np
 import pytest
 import torch
@@ -63,9 +64,17 @@ def check_ends(name, T, outs, ref):
     tail = ref(slice(T - WIN - TAIL, T))
     e_tail = rel_l2(host(o[:, :, T - TAIL:]), tail[0][:, :, WIN:])
     e_states = [rel_l2(host(s), sr) for s, sr in zip(outs[1:], tail[1:])]
+    # windows inside the sequence: one a third of the way in, and one whose
+    # checked tokens straddle the output row where the byte offset passes 2^30
+    e_mid = []
+    for c in (T // 3, (1 << 30) // (DV * 2)):
+        t0 = c - TAIL // 2
+        win = ref(slice(t0 - WIN, t0 + TAIL))
+        e_mid.append(rel_l2(host(o[:, :, t0:t0 + TAIL]), win[0][:, :, WIN:]))
     note(f"[max] {name} T={T}: rel L2 first {HEAD} {e_head:.3e}, last {TAIL} {e_tail:.3e}, "
+         f"middle windows {', '.join(f'{e:.3e}' for e in e_mid)}, "
          f"final states {', '.join(f'{e:.3e}' for e in e_states)}")
-    assert max([e_head, e_tail] + e_states) <= TOL["bf16"]
+    assert max([e_head, e_tail] + e_mid + e_states) <= TOL["bf16"]
 
 
 @pytest.mark.timeout(600)

@@ -124,3 +124,42 @@ def test_resume_equals_one_pass():
     torch.cuda.synchronize()
     assert rel_l2(host(torch.cat([o1, o2], dim=2)), host(o)) < 1e-2
     assert rel_l2(host(s2), host(s)) < 1e-2 and rel_l2(host(z2), host(z)) < 1e-2
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar"])
+def test_key_sum_in_place(gate):
+    # z_final aliasing z0 (and s_final aliasing s0): the key sum carried in
+    # place.  d_v = 128 gives every head two value-block workgroups that read
+    # z0, and 256 heads put them in more than one wave of workgroups, so a
+    # block that started after its partner finished would read the advanced
+    # key sum if the entry point did not read z0 from a copy.
+    import gated_delta_rule_27_amd as la
+    case = syn.Case("norm_inplace", 4, 64, 150, 128, 128, "add", gate, "bf16", qk="elu1",
+                    gate_scale=0.25, s0_std=0.3, case_id=147)
+    x, s0, z0 = inputs(case, 147)
+    d = lambda a: dev(a, case.dtype)
+    ref_o, ref_s, ref_z = la.chunk_fwd_normalized(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), dev_state(s0),
+                                                  dev_state(z0), gate=gate)
+    s_io, z_io = dev_state(s0), dev_state(z0)
+    o, s, z = la.chunk_fwd_normalized(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), s_io, z_io, gate=gate,
+                                      s_final=s_io, z_final=z_io)
+    torch.cuda.synchronize()
+    assert z.data_ptr() == z_io.data_ptr() and s.data_ptr() == s_io.data_ptr()
+    assert torch.equal(o, ref_o), "in-place key sum changed the output"
+    assert torch.equal(s, ref_s) and torch.equal(z, ref_z)
+    oref, sref, zref = oracle.normalized(x["q"], x["k"], x["v"], x["g"], s0, z0, gate=gate)
+    eo, ez = rel_l2(host(o), oref), rel_l2(host(z), zref)
+    note(f"[norm in place] {gate}: rel L2 o={eo:.3e} z={ez:.3e}")
+    assert eo <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+def test_key_sum_partial_overlap_rejected():
+    import gated_delta_rule_27_amd as la
+    e = lambda *shape: torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    zbuf = torch.zeros(2 * 2 * 64 + 4, dtype=torch.float32, device="cuda")
+    z0 = zbuf[:256].view(1, 2, 128)
+    zf = zbuf[4:260].view(1, 2, 128)
+    with pytest.raises(la.LinattnError) as ei:
+        la.chunk_fwd_normalized(e(1, 2, 10, 128), e(1, 2, 10, 128), e(1, 2, 10, 64), None, None, z0,
+                                z_final=zf)
+    assert ei.value.status == 6
