@@ -204,11 +204,11 @@ def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar
     elif s_final is not None:
         _check(s_final, "s_final", (B, H, dk, dv), torch.float32, dev)
     a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=dtype, chunk=chunk)
+    stream = torch.cuda.current_stream(dev).cuda_stream
     need = int(lib.linattn_chunk_workspace_bytes(ctypes.byref(a)))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    stream = torch.cuda.current_stream(dev).cuda_stream
     if (qk_map, gate_map, beta_map) == ("as_is", "as_is", "as_is"):
         st = lib.linattn_chunk_fwd(ctypes.byref(a), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(s0), _ptr(out), _ptr(s_final), _ptr(workspace), ws_bytes,

@@ -1,0 +1,578 @@
+// chunk_gen.hip — chunkwise forward for every supported chunk size
+// C in {16, 32, 64, 128}, fp32 or bf16 tokens, dk, dv in {64, 128}, the add
+// or delta rule and no / scalar / per-key-channel gate.  It serves what the
+// tuned single-pass and two-kernel paths (chunk 64) do not: other chunk sizes,
+// fp32 tokens at dk = 128 and fp32 tokens with the per-channel gate.
+//
+// Sources: "Linear Attention, Visualized" — "Chunkwise algorithm" and "Cost"
+// (any chunk size gives the exact result; the size only trades the C x C
+// intra-chunk work against the n / C state steps), "Gated Linear Attention
+// (GLA)" and "Kimi Delta Attention (KDA)" (channelwise decay inside the
+// scores, decayed query <-Q and right-boundary key ->K), "The triangular
+// correction system", "Optional: Use UT to share the triangular transform"
+// (W = T B <-K, U = T B V) and "Correct the incoming state" (Z = U - W S_r),
+// and the GDN row of the chunkwise table.
+//
+// Two kernels, the first over all chunks in parallel, the second walking each
+// head's chunks in order:
+//
+//   gen_intra_kernel   one workgroup per (b, h, chunk), 4 waves; stages q, k
+//     (and the per-channel gate) 32 key channels at a time in fp32 LDS and
+//     writes to the workspace, in the token type:
+//       a1  G = prefix of the log-gate (base 2; per channel or scalar)
+//       a2  Aq[l][m] = sum_c q_lc 2^(G_lc - G_mc) k_mc   (m <= l)
+//           scalar gate / no gate: a matrix-core product, decay applied after;
+//           per-channel gate: element-wise fp32 sums with the decay of every
+//           (l, m, c) formed from the difference G_lc - G_mc <= 0, so no
+//           factor can overflow whatever the gate
+//       a3  T = (I + diag(beta) L)^-1, L[l][m] = as Aq with k for q, m < l
+//           (fp32: 16 x 16 diagonal blocks by forward substitution, one lane
+//           per column; the blocks below by block substitution on the fp32
+//           matrix cores)
+//       a4  W = T diag(beta) <-K,  U = T diag(beta) V   (fp32 matrix cores)
+//       and the operands of the state pass: <-Q = 2^G . Q, ->K^T with
+//       ->k_l = 2^(G_{C-1} - G_l) . k_l, and 2^(G_{C-1})
+//   gen_chain_kernel   one workgroup per (b, h, 64 value columns), 4 waves of
+//     16 columns each, S (fp32) in matrix-core result registers; per chunk and
+//     per 16-row block li of the chunk:
+//       b1  Z_li = U_li - W_li S_r   (add rule: Z = V)
+//       c1  O_li = <-Q_li S_r + sum_{mj <= li} Aq(li, mj) Z_mj
+//           dS  += ->K_li^T Z_li
+//     then S_{r+1} = Diag(2^(G_{C-1})) S_r + dS.  Operands are read as
+//     matrix-core fragments straight from the workspace (L2-resident).
+//
+// Rows past the end of the sequence are staged as zeros (k = v = 0, g = 0,
+// beta = 0), which leaves the state unchanged; their outputs are not written.
+#include "device_common.h"
+#include "launch.h"
+#include "mfma.h"
+#include "prep.h"
+
+namespace linattn {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kGT = 256;          // threads of the intra-chunk kernel (4 waves)
+constexpr int kKS = 32;           // key / value channels per staged slice
+constexpr int kLDS = kKS + 4;     // row stride of a staged fp32 slice
+
+// Workspace of one chunk of one head: byte offsets of its pieces (256-byte
+// aligned), operands in the token type (element size esz), 2^(G_{C-1}) fp32.
+struct GenWs {
+    size_t qd, krt, aq, gc, w, u, bytes;
+};
+__host__ __device__ inline GenWs gen_ws(int C, int DK, int DV, int esz, bool delta)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    GenWs l{};
+    l.qd = 0;                                           // <-Q   [C][DK]
+    l.krt = l.qd + up((size_t)C * DK * esz);            // ->K^T [DK][C]
+    l.aq = l.krt + up((size_t)DK * C * esz);            // Aq    [C][C] (causal blocks)
+    l.gc = l.aq + up((size_t)C * C * esz);              // 2^(G_{C-1}) [DK] fp32
+    l.w = l.gc + up((size_t)DK * 4);                    // W     [C][DK]  (delta)
+    l.u = l.w + (delta ? up((size_t)C * DK * esz) : 0); // U     [C][DV]  (delta)
+    l.bytes = l.u + (delta ? up((size_t)C * DV * esz) : 0);
+    return l;
+}
+
+// four consecutive token values as fp32
+__device__ __forceinline__ floatx4 load4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+__device__ __forceinline__ floatx4 load4(const bf16* p)
+{
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return floatx4{to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
+}
+
+// K = 16 fragment of a row-major block in global memory (lane: row l % 16,
+// columns 4 (l / 16) .. +3), as frag16_lds reads one from LDS
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type frag16_g(const T* M, int ld, int lane)
+{
+    return *reinterpret_cast<const typename Frag16<T>::type*>(M + (lane & 15) * ld + 4 * (lane >> 4));
+}
+
+// (i, j) of the p-th causal 16 x 16 tile, j <= i, row-major over i
+__device__ __forceinline__ void tile_ij(int p, int& i, int& j)
+{
+    i = 0;
+    while (p > i) { p -= i + 1; ++i; }
+    j = p;
+}
+
+// ===========================================================================
+// Intra-chunk kernel
+// ===========================================================================
+template <typename T, int C, int DK, int RULE, int GATE>
+__global__ __launch_bounds__(kGT) void gen_intra_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
+    const T* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks, int DV,
+    int prep)
+{
+    constexpr int NB = C / 16;
+    constexpr bool DELTA = RULE == kRuleDelta;
+    constexpr bool CHAN = GATE == kGateChannel;
+    constexpr bool GATED = GATE != kGateNone;
+    constexpr int NTILE = NB * (NB + 1) / 2;
+    constexpr int MS = (NTILE + 3) / 4;          // causal tiles per wave
+    constexpr int LDL = C + 4;                   // row stride of L and T
+    constexpr int NSL = DK / kKS;                // key-channel slices
+    static_assert(NB >= 1 && NB <= 8 && DK % kKS == 0, "chunk and head sizes");
+
+    __shared__ __align__(16) float xs[C * kLDS];                  // q slice, later beta <-K or beta V
+    __shared__ __align__(16) float ys[C * kLDS];                  // k slice
+    __shared__ __align__(16) float gs[CHAN ? C * kLDS : 4];       // per-channel prefix (base 2)
+    __shared__ __align__(16) float Lm[DELTA ? C * LDL : 4];       // beta L, then T
+    __shared__ __align__(16) float Gsc[C];                        // scalar prefix (base 2)
+    __shared__ __align__(16) float bet[C];
+    __shared__ __align__(16) float rq[C], rk[C];                  // 1 / |q_l|, 1 / |k_l| (L2 map)
+    __shared__ __align__(16) float gtot[CHAN ? NB * kKS : 4];     // block totals of a channel slice
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t task = blockIdx.x;
+    const int64_t bh = task / nchunks, t0 = (task % nchunks) * C;
+    const int nrow = (int)(Tlen - t0 < C ? Tlen - t0 : C);      // rows of this chunk in the sequence
+    const int qkm = prep_qk_map(prep);
+    const GenWs L = gen_ws(C, DK, DV, (int)sizeof(T), DELTA);
+    unsigned char* wc = ws + task * L.bytes;
+    T* const Qd = reinterpret_cast<T*>(wc + L.qd);
+    T* const KrT = reinterpret_cast<T*>(wc + L.krt);
+    T* const Aqw = reinterpret_cast<T*>(wc + L.aq);
+    float* const gCw = reinterpret_cast<float*>(wc + L.gc);
+    T* const Ww = reinterpret_cast<T*>(wc + L.w);
+    T* const Uw = reinterpret_cast<T*>(wc + L.u);
+    const int64_t rowbase = bh * Tlen + t0;
+
+    // ---- a1 (scalar gate) and beta: one wave, 64 rows at a time ------------------
+    if (wave == 0) {
+        float carry = 0.f;
+        for (int h = 0; h < C; h += 64) {
+            const int l = h + lane;
+            const bool ok = l < nrow;
+            float gv = 0.f;
+            if constexpr (GATED && !CHAN)
+                if (ok) gv = prep_gate(to_f32(g[rowbase + l]), prep) * kLog2e;
+            const float G = wave_prefix_sum(gv) + carry;
+            carry = wave_last(G);
+            if (l < C) {
+                Gsc[l] = G;
+                float b = 0.f;
+                if constexpr (DELTA)
+                    if (ok) b = prep_beta(to_f32(beta[rowbase + l]), prep);
+                bet[l] = b;
+            }
+        }
+    }
+    // ---- inverse L2 norms of the raw rows (q/k map L2): one thread per row -------
+    if (qkm == kQkL2 && tid < 2 * C) {
+        const int l = tid % C;
+        const T* src = (tid < C ? q : k) + (rowbase + (l < nrow ? l : 0)) * DK;
+        float ss = 0.f;
+        for (int c = 0; c < DK; c += 4) {
+            const floatx4 x = load4(src + c);
+            ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        }
+        (tid < C ? rq : rk)[l] = rsqrtf(fmaxf(ss, 1e-12f));
+    }
+    __syncthreads();
+
+    // prepared q / k value (the map, then one rounding to the token type)
+    auto mapqk = [&](float x, float rn) {
+        float y = x;
+        if (qkm == kQkL2) y = x * rn;
+        else if (qkm == kQkElu1) y = x > 0.f ? x + 1.f : __expf(x);
+        return to_f32(from_f32<T>(y));
+    };
+
+    // Stage key channels c0 .. c0 + kKS - 1 of q and k (and the per-channel
+    // log-gate as its prefix within the chunk) into xs, ys (gs), fp32.
+    auto stage_qk = [&](int c0) {
+        __syncthreads();
+        for (int e = tid; e < C * kKS / 4; e += kGT) {
+            const int row = e / (kKS / 4), cq = 4 * (e % (kKS / 4));
+            const bool ok = row < nrow;
+            const int64_t off = (rowbase + (ok ? row : 0)) * DK + c0 + cq;
+            const floatx4 qv = load4(q + off), kv = load4(k + off);
+            floatx4 gv = zero4();
+            if constexpr (CHAN) gv = load4(g + off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xs[row * kLDS + cq + i] = ok ? mapqk(qv[i], rq[row]) : 0.f;
+                ys[row * kLDS + cq + i] = ok ? mapqk(kv[i], rk[row]) : 0.f;
+                if constexpr (CHAN) gs[row * kLDS + cq + i] = ok ? prep_gate(gv[i], prep) * kLog2e : 0.f;
+            }
+        }
+        if constexpr (CHAN) {
+            // prefix along the rows of each channel: 16-row blocks in parallel,
+            // then the block totals carried
+            __syncthreads();
+            const int c = tid % kKS, b = tid / kKS;
+            float acc = 0.f;
+            if (b < NB) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc += gs[(16 * b + r) * kLDS + c];
+                    gs[(16 * b + r) * kLDS + c] = acc;
+                }
+                gtot[b * kKS + c] = acc;
+            }
+            __syncthreads();
+            if (b < NB && b > 0) {
+                float off = 0.f;
+                for (int bb = 0; bb < b; ++bb) off += gtot[bb * kKS + c];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) gs[(16 * b + r) * kLDS + c] += off;
+            }
+        }
+        __syncthreads();
+    };
+
+    // ---- a2: score tiles, accumulated over the key-channel slices ---------------
+    floatx4 xa[MS], xn[MS];
+#pragma unroll
+    for (int s = 0; s < MS; ++s) { xa[s] = zero4(); xn[s] = zero4(); }
+    for (int sl = 0; sl < NSL; ++sl) {
+        stage_qk(sl * kKS);
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+            const int p = wave + 4 * s;
+            if (p >= NTILE) continue;
+            int i, j;
+            tile_ij(p, i, j);
+            if constexpr (!CHAN) {
+                // x[rr] = q_l . k_m (and k_l . k_m), l = 16 i + g4 + rr, m = 16 j + cl
+#pragma unroll
+                for (int kk = 0; kk < kKS / 16; ++kk) {
+                    const floatx4 bk = load4(&ys[(16 * j + (lane & 15)) * kLDS + 16 * kk + 4 * (lane >> 4)]);
+                    xa[s] = mm16<T>(&xs[16 * i * kLDS + 16 * kk], kLDS, bk, xa[s], lane);
+                    if constexpr (DELTA) xn[s] = mm16<T>(&ys[16 * i * kLDS + 16 * kk], kLDS, bk, xn[s], lane);
+                }
+            } else {
+                // exact per-channel decay of every pair: 2^(G_lc - G_mc), m <= l
+                const int m = 16 * j + (lane & 15), lb = 16 * i + 4 * (lane >> 4);
+#pragma unroll 2
+                for (int c4 = 0; c4 < kKS; c4 += 4) {
+                    const floatx4 km = load4(&ys[m * kLDS + c4]);
+                    const floatx4 Gm = load4(&gs[m * kLDS + c4]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int l = lb + rr;
+                        const floatx4 qv = load4(&xs[l * kLDS + c4]);
+                        const floatx4 Gl = load4(&gs[l * kLDS + c4]);
+                        floatx4 kv = zero4();
+                        if constexpr (DELTA) kv = load4(&ys[l * kLDS + c4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float t = m <= l ? km[e] * fast_exp2(Gl[e] - Gm[e]) : 0.f;
+                            xa[s][rr] = fmaf(qv[e], t, xa[s][rr]);
+                            if constexpr (DELTA) xn[s][rr] = fmaf(kv[e], t, xn[s][rr]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    mfma_settle();
+    // Aq to the workspace, beta L to LDS (rows l = 16 i + g4 + rr, column m)
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+        const int p = wave + 4 * s;
+        if (p >= NTILE) continue;
+        int i, j;
+        tile_ij(p, i, j);
+        const int m = 16 * j + (lane & 15);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int l = 16 * i + 4 * (lane >> 4) + rr;
+            float dec = 1.f;
+            if constexpr (GATED && !CHAN) dec = m <= l ? fast_exp2(Gsc[l] - Gsc[m]) : 0.f;
+            Aqw[l * C + m] = from_f32<T>(m <= l ? xa[s][rr] * dec : 0.f);
+            if constexpr (DELTA) Lm[l * LDL + m] = m < l ? bet[l] * xn[s][rr] * dec : 0.f;
+        }
+    }
+    __syncthreads();
+
+    if constexpr (DELTA) {
+        // ---- a3: T = (I + beta L)^-1.  Diagonal block i: wave i % 4, lane group
+        // i / 4, lane column jj; rows by forward substitution --------------------
+        {
+            const int jj = lane & 15, i = wave + 4 * (lane >> 4);
+            if (i < NB) {
+                float x[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    float acc = t == jj ? 1.f : 0.f;
+#pragma unroll
+                    for (int s2 = 0; s2 < t; ++s2) acc = fmaf(-Lm[(16 * i + t) * LDL + 16 * i + s2], x[s2], acc);
+                    x[t] = acc;
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) Lm[(16 * i + t) * LDL + 16 * i + jj] = x[t];
+            }
+        }
+        __syncthreads();
+        // blocks below the diagonal, one block row at a time:
+        // T(i, j) = -T(i, i) sum_{kb = j}^{i - 1} L(i, kb) T(kb, j)
+        for (int i = 1; i < NB; ++i) {
+            floatx4 X[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int j = wave + 4 * s2;
+                X[s2] = zero4();
+                if (j < i)
+                    for (int kb = j; kb < i; ++kb)
+                        X[s2] = mm16<float>(&Lm[16 * i * LDL + 16 * kb], LDL,
+                                            load_tile_rl(&Lm[16 * kb * LDL + 16 * j], LDL, lane), X[s2], lane);
+            }
+            mfma_settle();
+            __syncthreads();
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int j = wave + 4 * s2;
+                if (j < i) {
+                    const floatx4 t = mm16<float>(&Lm[16 * i * LDL + 16 * i], LDL, X[s2], zero4(), lane);
+                    mfma_settle();
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        Lm[(16 * i + 4 * (lane >> 4) + rr) * LDL + 16 * j + (lane & 15)] = -t[rr];
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- products T (beta X) for the staged slice in xs: tiles (lb, cb) of a
+    // [C][kKS] block, written to dst (row stride ld) at column c0 --------------
+    auto tb_product = [&](T* dst, int ld, int c0) {
+        for (int p = wave; p < NB * (kKS / 16); p += 4) {
+            const int lb = p / (kKS / 16), cb = p % (kKS / 16);
+            floatx4 acc = zero4();
+            for (int mb = 0; mb <= lb; ++mb)
+                acc = mm16<float>(&Lm[16 * lb * LDL + 16 * mb], LDL, load_tile_rl(&xs[16 * mb * kLDS + 16 * cb], kLDS, lane),
+                                  acc, lane);
+            mfma_settle();
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                dst[(16 * lb + 4 * (lane >> 4) + rr) * ld + c0 + 16 * cb + (lane & 15)] = from_f32<T>(acc[rr]);
+        }
+    };
+
+    // ---- operands of the state pass, slice by slice -----------------------------
+    for (int sl = 0; sl < NSL; ++sl) {
+        const int c0 = sl * kKS;
+        stage_qk(c0);
+        for (int e = tid; e < C * kKS; e += kGT) {
+            const int row = e / kKS, c = e % kKS;
+            const float G = CHAN ? gs[row * kLDS + c] : Gsc[row];
+            Qd[row * DK + c0 + c] = from_f32<T>(GATED ? xs[row * kLDS + c] * fast_exp2(G) : xs[row * kLDS + c]);
+        }
+        for (int e = tid; e < C * kKS; e += kGT) {
+            const int c = e / C, row = e % C;
+            const float G = CHAN ? gs[row * kLDS + c] : Gsc[row];
+            const float Ge = CHAN ? gs[(C - 1) * kLDS + c] : Gsc[C - 1];
+            KrT[(c0 + c) * C + row] = from_f32<T>(GATED ? ys[row * kLDS + c] * fast_exp2(Ge - G) : ys[row * kLDS + c]);
+        }
+        if (tid < kKS) gCw[c0 + tid] = GATED ? fast_exp2(CHAN ? gs[(C - 1) * kLDS + tid] : Gsc[C - 1]) : 1.f;
+        if constexpr (DELTA) {
+            // W = T (beta <-K): xs <- beta_m 2^(G_m) k_m
+            __syncthreads();
+            for (int e = tid; e < C * kKS; e += kGT) {
+                const int row = e / kKS, c = e % kKS;
+                const float G = CHAN ? gs[row * kLDS + c] : Gsc[row];
+                xs[row * kLDS + c] = bet[row] * (GATED ? fast_exp2(G) : 1.f) * ys[row * kLDS + c];
+            }
+            __syncthreads();
+            tb_product(Ww, DK, c0);
+        }
+    }
+    if constexpr (DELTA) {
+        // U = T (beta V), kKS value columns at a time
+        for (int n0 = 0; n0 < DV; n0 += kKS) {
+            __syncthreads();
+            for (int e = tid; e < C * kKS / 4; e += kGT) {
+                const int row = e / (kKS / 4), cq = 4 * (e % (kKS / 4));
+                const bool ok = row < nrow;
+                const floatx4 vv = load4(v + (rowbase + (ok ? row : 0)) * DV + n0 + cq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xs[row * kLDS + cq + i] = ok ? bet[row] * vv[i] : 0.f;
+            }
+            __syncthreads();
+            tb_product(Uw, DV, n0);
+        }
+    }
+}
+
+// ===========================================================================
+// State pass + output
+// ===========================================================================
+template <typename T, int C, int DK, int RULE>
+__global__ __launch_bounds__(256) void gen_chain_kernel(
+    const T* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0, T* __restrict__ o,
+    float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks)
+{
+    using F = typename Frag16<T>::type;
+    constexpr int NB = C / 16, ND = DK / 16;
+    constexpr bool DELTA = RULE == kRuleDelta;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nvb = DV / 64;
+    // the value blocks of a head on one XCD (dispatch is round-robin over 8)
+    int blk = blockIdx.x;
+    if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
+    const int64_t bh = blk / nvb;
+    const int n0 = (blk % nvb) * 64 + 16 * wave;
+    const int cl = lane & 15, g4 = 4 * (lane >> 4);
+    const GenWs L = gen_ws(C, DK, DV, (int)sizeof(T), DELTA);
+
+    floatx4 S[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const unsigned char* wc = ws + (bh * nchunks + c) * L.bytes;
+        const T* const Qd = reinterpret_cast<const T*>(wc + L.qd);
+        const T* const KrT = reinterpret_cast<const T*>(wc + L.krt);
+        const T* const Aq = reinterpret_cast<const T*>(wc + L.aq);
+        const float* const gC = reinterpret_cast<const float*>(wc + L.gc);
+        const T* const Ww = reinterpret_cast<const T*>(wc + L.w);
+        const T* const Uw = reinterpret_cast<const T*>(wc + L.u);
+        const int64_t t0 = c * C;
+        F Sf[ND];
+#pragma unroll
+        for (int db = 0; db < ND; ++db) Sf[db] = frag16_acc<T>(S[db]);
+        floatx4 dS[ND];
+#pragma unroll
+        for (int db = 0; db < ND; ++db) dS[db] = zero4();
+        F Zf[NB];
+#pragma unroll
+        for (int li = 0; li < NB; ++li) {
+            // b1: Z = U - W S_r (delta) | V (add)
+            floatx4 Z;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 16 * li + g4 + rr;
+                if constexpr (DELTA) {
+                    Z[rr] = to_f32(Uw[row * DV + n0 + cl]);
+                } else {
+                    const bool ok = t0 + row < Tlen;
+                    Z[rr] = ok ? to_f32(v[(bh * Tlen + t0 + row) * DV + n0 + cl]) : 0.f;
+                }
+            }
+            floatx4 O = zero4();
+            if constexpr (DELTA) {
+                floatx4 P = zero4();
+#pragma unroll
+                for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_g(Ww + 16 * li * DK + 16 * db, DK, lane), Sf[db], P);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
+            }
+            Zf[li] = frag16_acc<T>(Z);
+            // c1: O = <-Q S_r + sum_{mj <= li} Aq(li, mj) Z_mj
+#pragma unroll
+            for (int db = 0; db < ND; ++db) O = mma16<T>(frag16_g(Qd + 16 * li * DK + 16 * db, DK, lane), Sf[db], O);
+#pragma unroll
+            for (int mj = 0; mj <= li; ++mj) O = mma16<T>(frag16_g(Aq + 16 * li * C + 16 * mj, C, lane), Zf[mj], O);
+            mfma_settle();   // O is read inside the row-bounds branches below
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int64_t row = t0 + 16 * li + g4 + rr;
+                if (row < Tlen) o[(bh * Tlen + row) * DV + n0 + cl] = from_f32<T>(O[rr]);
+            }
+            // ->K_li^T Z_li
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+                dS[db] = mma16<T>(frag16_g(KrT + 16 * db * C + 16 * li, C, lane), Zf[li], dS[db]);
+        }
+        // S_{r+1} = Diag(2^(G_{C-1})) S_r + ->K^T Z
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            const floatx4 gd = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) S[db][rr] = gd[rr] * S[db][rr] + dS[db][rr];
+        }
+    }
+    if (s_final) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s_final[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] = S[db][rr];
+    }
+}
+
+template <typename T, int C, int DK, int RULE, int GATE>
+hipError_t launch_gen_t(const ChunkProblem& p, hipStream_t s)
+{
+    const int64_t nchunks = (p.T + C - 1) / C;
+    const int64_t bh = p.B * p.H;
+    unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+    if (nchunks > 0) {
+        hipLaunchKernelGGL((gen_intra_kernel<T, C, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kGT), 0, s,
+                           static_cast<const T*>(p.q), static_cast<const T*>(p.k), static_cast<const T*>(p.v),
+                           static_cast<const T*>(p.g), static_cast<const T*>(p.beta), ws, p.T, nchunks, p.dv,
+                           p.prep);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int nblocks = (int)(bh * (p.dv / 64));
+    hipLaunchKernelGGL((gen_chain_kernel<T, C, DK, RULE>), dim3((unsigned)nblocks), dim3(256), 0, s,
+                       static_cast<const T*>(p.v), ws, p.s0, static_cast<T*>(p.o), p.s_final, p.T, nchunks, p.dv,
+                       nblocks);
+    return hipGetLastError();
+}
+
+template <typename T, int C, int DK>
+hipError_t gen_by_rule_gate(const ChunkProblem& p, hipStream_t s)
+{
+    if (p.rule == kRuleDelta) {
+        if (p.gate == kGateNone) return launch_gen_t<T, C, DK, kRuleDelta, kGateNone>(p, s);
+        if (p.gate == kGateScalar) return launch_gen_t<T, C, DK, kRuleDelta, kGateScalar>(p, s);
+        return launch_gen_t<T, C, DK, kRuleDelta, kGateChannel>(p, s);
+    }
+    if (p.gate == kGateNone) return launch_gen_t<T, C, DK, kRuleAdd, kGateNone>(p, s);
+    if (p.gate == kGateScalar) return launch_gen_t<T, C, DK, kRuleAdd, kGateScalar>(p, s);
+    return launch_gen_t<T, C, DK, kRuleAdd, kGateChannel>(p, s);
+}
+
+template <typename T, int C>
+hipError_t gen_by_dk(const ChunkProblem& p, hipStream_t s)
+{
+    return p.dk == 64 ? gen_by_rule_gate<T, C, 64>(p, s) : gen_by_rule_gate<T, C, 128>(p, s);
+}
+
+template <typename T>
+hipError_t gen_by_chunk(const ChunkProblem& p, hipStream_t s)
+{
+    switch (p.chunk) {
+    case 16: return gen_by_dk<T, 16>(p, s);
+    case 32: return gen_by_dk<T, 32>(p, s);
+    case 64: return gen_by_dk<T, 64>(p, s);
+    default: return gen_by_dk<T, 128>(p, s);
+    }
+}
+
+}  // namespace
+
+bool chunk_gen_supported(const ChunkProblem& p)
+{
+    return (p.chunk == 16 || p.chunk == 32 || p.chunk == 64 || p.chunk == 128) && (p.dk == 64 || p.dk == 128) &&
+           (p.dv == 64 || p.dv == 128) && (p.dtype == kF32 || p.dtype == kBF16);
+}
+
+size_t chunk_gen_workspace_bytes(const ChunkProblem& p)
+{
+    const size_t nchunks = (size_t)((p.T + p.chunk - 1) / p.chunk);
+    const GenWs l = gen_ws(p.chunk, p.dk, p.dv, p.dtype == kBF16 ? 2 : 4, p.rule == kRuleDelta);
+    return (size_t)(p.B * p.H) * nchunks * l.bytes;
+}
+
+hipError_t launch_chunk_gen(const ChunkProblem& p, hipStream_t s)
+{
+    return p.dtype == kBF16 ? gen_by_chunk<bf16>(p, s) : gen_by_chunk<float>(p, s);
+}
+
+}  // namespace linattn

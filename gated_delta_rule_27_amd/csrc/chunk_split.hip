@@ -30,6 +30,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
+#include "prep.h"
 #include "tsolve.h"
 #include "tile_rows.h"
 
@@ -81,7 +82,7 @@ template <int DK, int RULE, int GATE>
 __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ g,
     const bf16* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks,
-    int64_t ntasks)
+    int64_t ntasks, int prep)
 {
     using W = SplitWs<DK>;
     constexpr int NT = 512;
@@ -145,21 +146,28 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
         unsigned char* wc = ws + task * W::BYTES;     // task = (b, h) * nchunks + chunk
 
         // ---- stage the chunk; issue the next chunk-head's loads ---------------------
+        // (raw projections first go through the maps of prep.h: q/k here, the
+        // DK / 8 lanes holding a row reducing its L2 norm; the log-gate map where
+        // the gate is read in fp32; beta below)
         __syncthreads();
+        const int qk_map = prep_qk_map(prep);
 #pragma unroll
         for (int p = 0; p < NV; ++p) {
             const int idx = (p * NT + tid) * 8;
             const int row = idx / DK, col = idx % DK;
             const bool ok = t0 + row < Tlen;
             const i4 z = {0, 0, 0, 0};
-            *reinterpret_cast<i4*>(&qs[row * LDQ + col]) = ok ? qreg[p] : z;
-            *reinterpret_cast<i4*>(&ks[row * LDQ + col]) = ok ? kreg[p] : z;
+            const i4 qp = prep_qk<bf16, DK / 8>(qreg[p], qk_map);
+            const i4 kp = prep_qk<bf16, DK / 8>(kreg[p], qk_map);
+            *reinterpret_cast<i4*>(&qs[row * LDQ + col]) = ok ? qp : z;
+            *reinterpret_cast<i4*>(&ks[row * LDQ + col]) = ok ? kp : z;
             if constexpr (GATE == kGateChannel) *reinterpret_cast<i4*>(&gs[row * LDQ + col]) = ok ? greg[p] : z;
         }
         if (tid < kC) {
             // a scalar gate is the channel gate with every channel equal
-            if constexpr (GATE != kGateChannel) gsc[tid] = (t0 + tid < Tlen) ? to_f32(gsreg) * kLog2e : 0.f;
-            bet[tid] = (DELTA && t0 + tid < Tlen) ? to_f32(breg) : 0.f;
+            if constexpr (GATE != kGateChannel)
+                gsc[tid] = (t0 + tid < Tlen) ? prep_gate(to_f32(gsreg), prep) * kLog2e : 0.f;
+            bet[tid] = (DELTA && t0 + tid < Tlen) ? prep_beta(to_f32(breg), prep) : 0.f;
         }
         if (task + gridDim.x < ntasks) fetch(task + gridDim.x);
         __syncthreads();
@@ -174,7 +182,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 float gv;
-                if constexpr (GATE == kGateChannel) gv = to_f32(gs[(16 * pb + rr) * LDQ + pc]) * kLog2e;
+                if constexpr (GATE == kGateChannel)
+                    gv = t0 + 16 * pb + rr < Tlen ? prep_gate(to_f32(gs[(16 * pb + rr) * LDQ + pc]), prep) * kLog2e : 0.f;
                 else gv = gsc[16 * pb + rr];
                 acc += gv;
                 Gl[rr] = acc;                          // G_l - G_s(b)
@@ -228,7 +237,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
                     for (int c = 0; c < DK; ++c) {
                         float dG = 0.f;                // G_l - G_m, base 2
                         for (int s2 = m + 1; s2 <= l; ++s2) {
-                            if constexpr (GATE == kGateChannel) dG += to_f32(gs[s2 * LDQ + c]) * kLog2e;
+                            if constexpr (GATE == kGateChannel)
+                                dG += t0 + s2 < Tlen ? prep_gate(to_f32(gs[s2 * LDQ + c]), prep) * kLog2e : 0.f;
                             else dG += gsc[s2];
                         }
                         const float km = to_f32(ks[m * LDQ + c]) * fast_exp2(dG);
@@ -682,7 +692,7 @@ hipError_t launch_split(const ChunkProblem& p, bf16* states, hipStream_t s)
         hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE>), dim3((unsigned)grid), dim3(512), 0, s,
                            static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                            static_cast<const bf16*>(p.g), static_cast<const bf16*>(p.beta), ws, p.T,
-                           nchunks, ntasks);
+                           nchunks, ntasks, p.prep);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -102,6 +102,13 @@ hipError_t launch_chunk_split(const ChunkProblem& p, hipStream_t stream);
 // [B,H,nchunks,dk,dv] bf16 (for the backward pass).
 hipError_t launch_chunk_split_save(const ChunkProblem& p, void* states, hipStream_t stream);
 
+// Generic two-kernel chunk path (intra-chunk operands to the workspace, then
+// the state pass): every chunk size 16, 32, 64, 128, fp32 or bf16 tokens,
+// every rule and gate, input maps of prep.h.
+bool chunk_gen_supported(const ChunkProblem& p);
+size_t chunk_gen_workspace_bytes(const ChunkProblem& p);
+hipError_t launch_chunk_gen(const ChunkProblem& p, hipStream_t stream);
+
 // Backward pass of the chunk form (chunk 64; the per-channel gate with bf16
 // tokens): given the incoming state of every chunk (states), the per-chunk
 // operands of the reverse state pass are prepared, the gradients of the

@@ -18,23 +18,38 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
-// Which chunk path serves a problem: the per-channel gate always takes the
-// two-kernel path.  Otherwise the delta rule with bf16 tokens takes the
+// Which chunk path serves a problem.  Chunk 64 (the default) with bf16 tokens,
+// or fp32 tokens at dk = 64 with gate NONE or SCALAR, takes a tuned path: the
+// per-channel gate the two-kernel path, the delta rule with bf16 tokens the
 // pipelined single-pass kernel (its intra-chunk work is large enough to pay
-// for the pipelining), everything else the three-phase one.
-// LINATTN_CHUNK_PATH=split, =fused or =pipe selects that path instead (for A/B
-// measurement) where it supports the problem.
-enum ChunkPath { kPathSplit, kPathFused, kPathPipe };
+// for the pipelining), everything else the three-phase one.  Every other
+// chunk size, fp32 tokens at dk = 128 and fp32 tokens with the per-channel
+// gate take the generic two-kernel path.  LINATTN_CHUNK_PATH=split, =fused,
+// =pipe or =gen selects that path instead (for A/B measurement) where it
+// supports the problem.
+enum ChunkPath { kPathSplit, kPathFused, kPathPipe, kPathGen };
 ChunkPath chunk_path(const ChunkProblem& p)
 {
-    if (p.gate == kGateChannel) return kPathSplit;
     const char* e = getenv("LINATTN_CHUNK_PATH");
-    if (e && strcmp(e, "split") == 0 && p.prep == 0 && chunk_split_supported(p)) return kPathSplit;
+    if (e && strcmp(e, "gen") == 0 && chunk_gen_supported(p)) return kPathGen;
+    if (p.chunk != 64 || (p.dtype == kF32 && (p.dk != 64 || p.gate == kGateChannel))) return kPathGen;
+    if (p.gate == kGateChannel) return kPathSplit;
+    if (e && strcmp(e, "split") == 0 && chunk_split_supported(p)) return kPathSplit;
     if (e && strcmp(e, "fused") == 0 && chunk_fused_supported(p)) return kPathFused;
     if (e && strcmp(e, "pipe") == 0 && chunk_pipe_supported(p)) return kPathPipe;
     return p.dtype == kBF16 && p.rule == kRuleDelta ? kPathPipe : kPathFused;
 }
-bool use_split(const ChunkProblem& p) { return chunk_path(p) == kPathSplit; }
+
+// Workspace the chosen path needs (the two-kernel paths stage per-chunk
+// operands in it; the single-pass kernels need none).
+size_t path_workspace_bytes(const ChunkProblem& p)
+{
+    switch (chunk_path(p)) {
+    case kPathSplit: return chunk_split_workspace_bytes(p);
+    case kPathGen: return chunk_gen_workspace_bytes(p);
+    default: return 0;
+    }
+}
 
 linattn_status check_enums(int rule, int gate, int dtype)
 {
@@ -95,13 +110,15 @@ linattn_status validate_chunk(const linattn_chunk_args* a, ChunkProblem* p,
     p->rule = a->rule; p->gate = a->gate; p->dtype = a->dtype;
     st = prep_flags(prep, a->rule, a->gate, &p->prep);
     if (st != LINATTN_OK) return st;
+    if (p->chunk != 16 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128) return LINATTN_ERR_UNSUPPORTED;
     const ChunkPath path = chunk_path(*p);
-    // the two-kernel path stages prepared operands already; it takes no maps
-    if (path == kPathSplit && p->prep != 0) return LINATTN_ERR_UNSUPPORTED;
     const bool ok = path == kPathSplit ? chunk_split_supported(*p)
                   : path == kPathPipe  ? chunk_pipe_supported(*p)
+                  : path == kPathGen   ? chunk_gen_supported(*p)
                                        : chunk_fused_supported(*p);
     if (!ok) return LINATTN_ERR_UNSUPPORTED;
+    // the generic path launches one workgroup per chunk of every head
+    if (path == kPathGen && bh * ((a->T + p->chunk - 1) / p->chunk) >= ((int64_t)1 << 31)) return LINATTN_ERR_SHAPE;
     // every chunk kernel addresses one head's output through a buffer resource
     // with a 31-bit byte range
     const int64_t esz = a->dtype == LINATTN_BF16 ? 2 : 4;
@@ -151,7 +168,7 @@ DpLayout dp_layout(const linattn_chunk_args& va, const ChunkProblem& vp)
     l.gv = up(steps * va.dk * esz);
     l.ov = l.gv + (va.gate == LINATTN_GATE_SCALAR ? up(steps * esz) : 0);
     l.cws = l.ov + up(steps * va.dv * esz);
-    l.total = l.cws + (use_split(vp) ? chunk_split_workspace_bytes(vp) : 0);
+    l.total = l.cws + path_workspace_bytes(vp);
     return l;
 }
 
@@ -174,8 +191,8 @@ NormLayout norm_layout(const ChunkProblem& p, const ChunkProblem& pd)
     l.s0d = l.den + up(rows * nc * esz);
     l.sfd = l.s0d + up((size_t)(p.B * p.H) * p.dk * nc * 4);
     l.cws = l.sfd + up((size_t)(p.B * p.H) * p.dk * nc * 4);
-    size_t w = use_split(p) ? chunk_split_workspace_bytes(p) : 0;
-    const size_t wd = use_split(pd) ? chunk_split_workspace_bytes(pd) : 0;
+    const size_t w = path_workspace_bytes(p);
+    const size_t wd = path_workspace_bytes(pd);
     l.total = l.cws + (w > wd ? w : wd);
     return l;
 }
@@ -304,7 +321,7 @@ size_t linattn_chunk_workspace_bytes(const linattn_chunk_args* a)
 {
     ChunkProblem p{};
     if (validate_chunk(a, &p) != LINATTN_OK) return 0;
-    return use_split(p) ? chunk_split_workspace_bytes(p) : 0;
+    return path_workspace_bytes(p);
 }
 
 linattn_status linattn_chunk_fwd(const linattn_chunk_args* a, const void* q, const void* k,
@@ -338,15 +355,16 @@ linattn_status linattn_chunk_fwd_prep(const linattn_chunk_args* a, const linattn
     p.workspace = workspace; p.workspace_bytes = workspace_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
-    if (chunk_path(p) == kPathPipe) {
+    const ChunkPath path = chunk_path(p);
+    if (path == kPathPipe) {
         err = launch_chunk_pipe(p, s);
-    } else if (chunk_path(p) == kPathFused) {
+    } else if (path == kPathFused) {
         err = launch_chunk_fused(p, s);
     } else {
-        const size_t need = chunk_split_workspace_bytes(p);
+        const size_t need = path_workspace_bytes(p);
         if (need > 0 && (!workspace || workspace_bytes < need)) return LINATTN_ERR_WORKSPACE;
         if (workspace && !aligned16(workspace)) return LINATTN_ERR_UNSUPPORTED;
-        err = launch_chunk_split(p, s);
+        err = path == kPathSplit ? launch_chunk_split(p, s) : launch_chunk_gen(p, s);
     }
     return err == hipSuccess ? LINATTN_OK : LINATTN_ERR_LAUNCH;
 }
@@ -645,3 +663,4 @@ linattn_status linattn_deltaproduct_bwd(const linattn_deltaproduct_args* a, cons
 }
 
 }  // extern "C"
+

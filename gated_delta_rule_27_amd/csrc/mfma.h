@@ -77,6 +77,19 @@ __device__ __forceinline__ floatx4 mma_nt_k(floatx4 acc, const T* A, int lda, co
     return acc;
 }
 
+// Twenty wait states, with nothing scheduled across them: placed after a chain
+// of matrix-core ops whose results are next read past a branch (a loop exit,
+// a skipped block).  Measured on gfx950: with the wait states the compiler
+// inserted on the branch-taken path alone (a branch and s_nop 3), the last
+// result register of a v_mfma_f32_16x16x4_f32 chain read its value from
+// before the last op.  Twenty cover the longest (16-pass) op.
+__device__ __forceinline__ void mfma_settle()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
 // then s_barrier.  Global loads in flight (prefetch of the next chunk) stay in
 // flight across it; no kernel here communicates through global memory inside
@@ -305,6 +318,55 @@ template <typename T>
 __device__ __forceinline__ void store_tile_t_pc(T* M, int ld, int kb, floatx4 v, int lane)
 {
     store_tile_t(M + 32 * (kb >> 1) + 4 * (kb & 1) + 4 * (lane >> 4), ld, v, lane);
+}
+
+// ---- swizzled pcol tiles ----------------------------------------------------
+// The same column order with, in rows 4..11 of every 16-row block, the
+// 16-byte units 2u and 2u + 1 of the row trading places (element offset XOR 8
+// for 2-byte types; swz_x gives the XOR of row r).  Measured on gfx950: a
+// ds_read_b128 serves 16 lanes per clock over 64 four-byte banks, lane 0
+// together with lanes 1-3, 12-15 and 20-27 (the quads of equal bit parity),
+// and a paired-operand read (16 rows, four 16-byte units each, at row strides
+// of 17 or 9 units) puts two lanes on one bank in every group: 8 clocks
+// instead of 4.  With the swap every group covers 64 distinct banks.  Every
+// access to such a tile (reads, transposed stores, staging writes) applies
+// the XOR of its row; base pointers sit at a 16-row block and at a multiple
+// of 16 columns, so the XOR touches only the in-block offset.
+__host__ __device__ constexpr int swz_x(int r) { return ((((r & 15) + 4) >> 3) & 1) << 3; }
+
+template <typename T>
+__device__ __forceinline__ typename Pair<T>::type pair_lds_sw(const T* M, int ld, int lane)
+{
+    static_assert(sizeof(T) == 2, "16-byte units of 2-byte elements");
+    return *reinterpret_cast<const bf16x8*>(M + (lane & 15) * ld + ((8 * (lane >> 4)) ^ swz_x(lane & 15)));
+}
+
+// Mfma<T>::load of a swizzled tile (k0 a multiple of 32)
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag mfma_load_sw(const T* row0, int ld, int k0, int lane)
+{
+    static_assert(sizeof(T) == 2, "16-byte units of 2-byte elements");
+    return *reinterpret_cast<const typename Mfma<T>::frag*>(
+        row0 + (lane & 15) * ld + ((k0 + 8 * (lane >> 4)) ^ swz_x(lane & 15)));
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type frag16_lds_pc_sw(const T* M, int ld, int kb, int lane)
+{
+    static_assert(sizeof(T) == 2, "16-byte units of 2-byte elements");
+    return *reinterpret_cast<const typename Frag16<T>::type*>(
+        M + (lane & 15) * ld + ((32 * (kb >> 1) + 4 * (kb & 1) + 8 * (lane >> 4)) ^ swz_x(lane & 15)));
+}
+
+template <typename T>
+__device__ __forceinline__ void store_tile_t_pc_sw(T* M, int ld, int kb, floatx4 v, int lane)
+{
+    static_assert(sizeof(T) == 2, "16-byte units of 2-byte elements");
+    T* p = M + (lane & 15) * ld + ((32 * (kb >> 1) + 4 * (kb & 1) + 8 * (lane >> 4)) ^ swz_x(lane & 15));
+    bf16x4 w;
+    w[0] = from_f32<bf16>(v[0]); w[1] = from_f32<bf16>(v[1]);
+    w[2] = from_f32<bf16>(v[2]); w[3] = from_f32<bf16>(v[3]);
+    *reinterpret_cast<bf16x4*>(p) = w;
 }
 
 // Identity as a K = 16 right factor (lane holds I[4(l/16)+r][l%16]): mma16

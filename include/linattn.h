@@ -110,10 +110,14 @@ size_t linattn_chunk_workspace_bytes(const linattn_chunk_args *a);
  *   workspace, workspace_bytes: device scratch of at least
  *            linattn_chunk_workspace_bytes(a) bytes (may be NULL when that is 0)
  *   stream   hipStream_t
- * Supported: dk, dv in {64, 128}; chunk 64; bf16 tokens for any gate; fp32
- * tokens for dk = 64 with gate NONE or SCALAR; one head's output under 2 GiB
+ * Supported: dk, dv in {64, 128}; chunk in {16, 32, 64, 128} (0 = 64); bf16
+ * or fp32 tokens; every rule and gate; one head's output under 2 GiB
  * (T * dv * element size < 2^31, else LINATTN_ERR_UNSUPPORTED).  T need not
- * be a multiple of the chunk size.
+ * be a multiple of the chunk size.  Chunk 64 with bf16 tokens (and fp32
+ * tokens at dk = 64 without the per-channel gate) runs the tuned kernels;
+ * other chunk sizes, fp32 tokens at dk = 128 and fp32 tokens with the
+ * per-channel gate run a generic two-kernel path; both need the workspace
+ * linattn_chunk_workspace_bytes reports (0 for the single-pass kernels).
  */
 linattn_status linattn_chunk_fwd(const linattn_chunk_args *a,
                                  const void *q, const void *k, const void *v,
@@ -134,7 +138,7 @@ typedef enum { LINATTN_GMAP_AS_IS = 0, LINATTN_GMAP_NEG_SOFTPLUS = 1 } linattn_g
 typedef enum { LINATTN_BMAP_AS_IS = 0, LINATTN_BMAP_SIGMOID = 1 } linattn_beta_map;
 typedef struct {
     int32_t qk_map;     /* applied to q and to k (linattn_qk_map) */
-    int32_t gate_map;   /* linattn_gate_map; needs a scalar gate */
+    int32_t gate_map;   /* linattn_gate_map; needs a gate (scalar or per channel) */
     int32_t beta_map;   /* linattn_beta_map; needs the delta rule */
 } linattn_prep_args;
 
@@ -143,8 +147,9 @@ typedef struct {
  * inside the kernel as prep says (NULL prep: no maps, same as
  * linattn_chunk_fwd).  A map the problem has no operand for (a gate map without
  * a gate, a beta map for the add rule) or an unknown map value is
- * LINATTN_ERR_ARG; the per-channel gate takes no maps (LINATTN_ERR_UNSUPPORTED).
- * Same arguments, layouts and workspace as linattn_chunk_fwd otherwise.
+ * LINATTN_ERR_ARG.  Every path applies the maps (the per-channel gate map
+ * element by element, -softplus of each key channel's logit).  Same
+ * arguments, layouts and workspace as linattn_chunk_fwd otherwise.
  */
 linattn_status linattn_chunk_fwd_prep(const linattn_chunk_args *a, const linattn_prep_args *prep,
                                       const void *q, const void *k, const void *v,

@@ -190,8 +190,8 @@ def chunk_inputs(case: Case, heads: Optional[Sequence[tuple]] = None, seed: int 
 def raw_inputs(case: Case, seed: int = SEED) -> dict:
     """Raw projections for the fused input preparation, all heads: q, k
     N(0,1) * 2 (not normalised), v N(0,1), beta logits N(0,1), gate logits
-    N(0,1) * gate_scale ([B,H,T] scalar gate), initial state as in
-    ``head_inputs``; same draw order per (b,h) head."""
+    N(0,1) * gate_scale ([B,H,T] scalar gate, [B,H,T,dk] per-channel gate),
+    initial state as in ``head_inputs``; same draw order per (b,h) head."""
     parts = []
     for b in range(case.B):
         for h in range(case.H):
@@ -201,7 +201,8 @@ def raw_inputs(case: Case, seed: int = SEED) -> dict:
             k = to_dtype(rng.standard_normal((T, dk), dtype=np.float32) * np.float32(2), case.dtype)
             v = to_dtype(rng.standard_normal((T, dv), dtype=np.float32), case.dtype)
             beta = to_dtype(rng.standard_normal((T,), dtype=np.float32), case.dtype)
-            g = to_dtype(rng.standard_normal((T,), dtype=np.float32) * np.float32(case.gate_scale),
+            gshape = (T, dk) if case.gate == "channel" else (T,)
+            g = to_dtype(rng.standard_normal(gshape, dtype=np.float32) * np.float32(case.gate_scale),
                          case.dtype)
             s0 = None
             if case.s0_std > 0:

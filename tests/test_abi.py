@@ -64,7 +64,16 @@ def test_chunk_validation(lib):
     assert call_chunk(lib, mk(gate="scalar")) == 1               # scalar gate needs g
     assert call_chunk(lib, mk(), g=FAKE) == 6                    # g given without a gate
     assert call_chunk(lib, mk(), q=FAKE + 8) == 3                # misaligned
-    assert call_chunk(lib, mk(dtype="fp32", dk=128)) == 3        # fp32 needs dk = 64
+    # fp32 tokens at dk = 128, chunk sizes other than 64: the generic two-kernel
+    # path, which stages per-chunk operands in the workspace
+    assert call_chunk(lib, mk(dtype="fp32", dk=128)) == 4        # workspace missing
+    for c in (16, 32, 128):
+        assert call_chunk(lib, mk(chunk=c)) == 4
+    # chunk 32, dk = dv = 64, bf16, delta rule, two chunks of T = 64: <-Q, ->K^T,
+    # Aq, 2^G (fp32, 256-byte piece), W and U per chunk
+    per = 32 * 64 * 2 + 32 * 64 * 2 + 32 * 32 * 2 + 256 + 32 * 64 * 2 + 32 * 64 * 2
+    assert lib.linattn_chunk_workspace_bytes(ctypes.byref(mk(chunk=32))) == 2 * per
+    assert lib.linattn_chunk_workspace_bytes(ctypes.byref(mk(chunk=48))) == 0
     a = mk()
     a.rule = 7
     assert call_chunk(lib, a) == 6
@@ -78,7 +87,7 @@ def test_chunk_validation(lib):
     wa = mk(gate="channel", dk=128, dv=128, T=130)
     assert lib.linattn_chunk_workspace_bytes(ctypes.byref(wa)) == 3 * 66048
     assert call_chunk(lib, wa, g=FAKE) == 4                      # workspace missing
-    assert call_chunk(lib, mk(gate="channel", dtype="fp32"), g=FAKE) == 3
+    assert call_chunk(lib, mk(gate="channel", dtype="fp32"), g=FAKE) == 4   # generic path
 
 
 def test_prep_validation(lib):
@@ -92,7 +101,7 @@ def test_prep_validation(lib):
     assert call(mk(), (0, 0, -1)) == 6
     assert call(mk(gate="none"), (0, 1, 0), g=None) == 6          # gate map without a gate
     assert call(mk(rule="add"), (0, 0, 1), beta=None) == 6        # beta map for the add rule
-    assert call(mk(gate="channel", dk=128, dv=128), (1, 0, 0)) == 3   # the channel path takes no maps
+    assert call(mk(gate="channel", dk=128, dv=128), (1, 1, 1)) == 4   # maps on the channel path: needs its workspace
     assert call(mk(dk=96), (1, 0, 0)) == 3
     assert call(mk(), (1, 1, 1), q=None) == 1
 
