@@ -188,8 +188,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
         P.g = GATED ? g[bh * Treal + (VIRT ? (int64_t)((int)tr / nh) : tr)] : from_f32<T>(0.f);
         P.b = DELTA ? beta[bh * Tlen + tr] : from_f32<T>(0.f);
     };
-    // Q and K rows go to LDS with their columns in pcol order (mfma.h), four
-    // columns (8 bytes) at a time
+    // Q and K rows go to LDS with their columns in swizzled pcol order
+    // (mfma.h), four columns (8 bytes) at a time.  At dk = 128 the threads of
+    // the second 64 columns of a row write their upper four columns first, so
+    // each 16-lane group of a write instruction covers 32 distinct banks.
     // (raw projections first go through the q/k map of prep.h; rows past the
     // end are zeroed after it)
     auto stage_qk = [&](const Pref& P, int64_t t0, T* Qb, T* Kb) {
@@ -207,10 +209,14 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             const i4 kp = prep_qk<T, DK / E>(P.k[p], qk_map);
             const i4 qv = okq ? qp : i4{0, 0, 0, 0};
             const i4 kv = ok ? kp : i4{0, 0, 0, 0};
-            *reinterpret_cast<i2*>(&Qb[row * LDQ + pcol(col)]) = i2{qv[0], qv[1]};
-            *reinterpret_cast<i2*>(&Qb[row * LDQ + pcol(col + 4)]) = i2{qv[2], qv[3]};
-            *reinterpret_cast<i2*>(&Kb[row * LDQ + pcol(col)]) = i2{kv[0], kv[1]};
-            *reinterpret_cast<i2*>(&Kb[row * LDQ + pcol(col + 4)]) = i2{kv[2], kv[3]};
+            const int sw = swz_x(row);
+            const bool hi = DK == 128 && (col & 64);
+            const int c0 = row * LDQ + (pcol(col + (hi ? 4 : 0)) ^ sw);
+            const int c1 = row * LDQ + (pcol(col + (hi ? 0 : 4)) ^ sw);
+            *reinterpret_cast<i2*>(&Qb[c0]) = hi ? i2{qv[2], qv[3]} : i2{qv[0], qv[1]};
+            *reinterpret_cast<i2*>(&Kb[c0]) = hi ? i2{kv[2], kv[3]} : i2{kv[0], kv[1]};
+            *reinterpret_cast<i2*>(&Qb[c1]) = hi ? i2{qv[0], qv[1]} : i2{qv[2], qv[3]};
+            *reinterpret_cast<i2*>(&Kb[c1]) = hi ? i2{kv[0], kv[1]} : i2{kv[2], kv[3]};
         }
     };
     auto stage_v = [&](const Pref& P, int64_t t0) {
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     // Ks); a wave loads each block it needs once per chunk.
     auto block_frags = [&](const T* A, int b, int ln, Fr (&f)[NK]) {
 #pragma unroll
-        for (int i = 0; i < NK; ++i) f[i] = Mfma<T>::load(&A[b * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
+        for (int i = 0; i < NK; ++i) f[i] = mfma_load_sw(&A[b * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
     };
     // x[rr] = sum_c A[16 mi + g4 + rr][c] B[16 lj + cl][c] from the blocks' fragments
     auto tile_dot = [&](const Fr (&fa)[NK], const Fr (&fb)[NK]) {
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             const float dec = GATED ? fast_exp2(Gl - Gm[rr]) : 1.f;
             va[rr] = (mi < lj || g4 + rr <= cl) ? xa[rr] * dec : 0.f;
         }
-        store_tile_t_pc(&Aqb[lj * 16 * LDC], LDC, mi, va, ln);
+        store_tile_t_pc_sw(&Aqb[lj * 16 * LDC], LDC, mi, va, ln);
     };
     // a2 diagonal N block b in registers.  x = K_b K_b^T is symmetric, so one
     // product gives N_bb both as tile(N_bb^T) (lane value N[l][m], l = 16 b + cl)
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
         floatx4 nd[1], nt[1], br[1], Xa[1], Xta[1];
         Fr kb[NK], k2[NK];
         diag_block(Kb, Gs, bet, b, ln, nd[0], nt[0], br[0], kb);
-        tsolve_diag<T, true, 1>(nd, nt, Xa, Xta, Tbb, LDC, br, ln, b);
+        tsolve_diag<T, 2, 1>(nd, nt, Xa, Xta, Tbb, LDC, br, ln, b);
         const floatx4 X = Xa[0], Xt = Xta[0];
         if (b == 0) {
             block_frags(Kb, 1, ln, k2);
@@ -367,11 +373,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
         const floatx4* nl = Nlo + ln;
         const floatx4* xx = Xx + ln;
         if (h == 0)
-            tsolve_offdiag_a<T, true>(xx[4 * kWave], xx[0 * kWave], xx[2 * kWave], xx[3 * kWave], nl[0 * kWave],
+            tsolve_offdiag_a<T, 2>(xx[4 * kWave], xx[0 * kWave], xx[2 * kWave], xx[3 * kWave], nl[0 * kWave],
                                       nl[1 * kWave], nl[2 * kWave], nl[3 * kWave], nl[4 * kWave], nl[5 * kWave],
                                       Tbb, LDC, brow, ln);
         else
-            tsolve_offdiag_b<T, true>(xx[5 * kWave], xx[1 * kWave], xx[2 * kWave], xx[3 * kWave], nl[2 * kWave],
+            tsolve_offdiag_b<T, 2>(xx[5 * kWave], xx[1 * kWave], xx[2 * kWave], xx[3 * kWave], nl[2 * kWave],
                                       nl[4 * kWave], nl[5 * kWave], Tbb, LDC, brow, ln);
     };
 
@@ -461,7 +467,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                     const auto sp = pair_regs<T>(S[db], S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        P[li] = mma_pair<T>(pair_lds(&Kc[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
+                        P[li] = mma_pair<T>(pair_lds_sw(&Kc[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
                 }
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                 const auto sp = pair_regs<T>(S[db], S[db + 1]);
 #pragma unroll
                 for (int li = 0; li < NL; ++li)
-                    Ot[li] = mma_pair<T>(sp, pair_lds(&Qc[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
+                    Ot[li] = mma_pair<T>(sp, pair_lds_sw(&Qc[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
             }
 #pragma unroll
             for (int li = 0; li < NL; ++li) {
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
 #pragma unroll
                 for (int i = 0; i < NKT; ++i) {
                     const int t = wave + 4 * i;
-                    af[i] = frag16_lds_pc(&Kc[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
+                    af[i] = frag16_lds_pc_sw(&Kc[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
                 }
                 const F id = ident_frag<T>(ln);
                 floatx4 d[NKT];
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
 #pragma unroll
                 for (int i = 0; i < NKT; ++i) {
                     const int t = wave + 4 * i;
-                    store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
+                    store_tile_t_pc_sw(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
                 }
             }
             if constexpr (DELTA)
@@ -522,8 +528,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                 const auto r01 = pair_regs<T>(R[0], R[1]), r23 = pair_regs<T>(R[2], R[3]);
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
-                    Z[li] = mma_pair<T>(pair_lds(&Tbc[16 * li * LDC], LDC, ln), r01, zero4());
-                    if (li >= 2) Z[li] = mma_pair<T>(pair_lds(&Tbc[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                    Z[li] = mma_pair<T>(pair_lds_sw(&Tbc[16 * li * LDC], LDC, ln), r01, zero4());
+                    if (li >= 2) Z[li] = mma_pair<T>(pair_lds_sw(&Tbc[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
                 }
             } else {
 #pragma unroll
@@ -534,8 +540,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                 const auto z01 = pair_regs<T>(Z[0], Z[1]), z23 = pair_regs<T>(Z[2], Z[3]);
 #pragma unroll
                 for (int lj = 0; lj < NL; ++lj) {
-                    Ot[lj] = mma_pair<T>(z01, pair_lds(&Aqc[16 * lj * LDC], LDC, ln), Ot[lj]);
-                    if (lj >= 2) Ot[lj] = mma_pair<T>(z23, pair_lds(&Aqc[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
+                    Ot[lj] = mma_pair<T>(z01, pair_lds_sw(&Aqc[16 * lj * LDC], LDC, ln), Ot[lj]);
+                    if (lj >= 2) Ot[lj] = mma_pair<T>(z23, pair_lds_sw(&Aqc[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
                 }
             }
             // O^T tile -> Os[token][column]
@@ -558,8 +564,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             for (int db = 0; db < ND; ++db) {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gC;
-                S[db] = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
-                                    mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
+                S[db] = mma_pair<T>(pair_lds_sw(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
+                                    mma_pair<T>(pair_lds_sw(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
             }
             if constexpr (DELTA)
                 if (wave < 2 && r + 1 < nchunks) offdiag(wave, betb[(r + 1) % 3], Tb[(r + 1) & 1], ln);

@@ -31,12 +31,13 @@
 
 namespace linattn {
 
-// Tb block (rb, qb) from -tile(C^T)-style data: with PC the columns of Tb are
-// stored in pcol order (mfma.h).
-template <typename T, bool PC>
+// Tb block (rb, qb) from -tile(C^T)-style data: with PC = 1 the columns of Tb
+// are stored in pcol order, with PC = 2 in swizzled pcol order (mfma.h).
+template <typename T, int PC>
 __device__ __forceinline__ void store_tb(T* Tb, int ldt, int rb, int qb, floatx4 v, int lane)
 {
-    if constexpr (PC) store_tile_t_pc(&Tb[(rb * 16) * ldt], ldt, qb, v, lane);
+    if constexpr (PC == 2) store_tile_t_pc_sw(&Tb[(rb * 16) * ldt], ldt, qb, v, lane);
+    else if constexpr (PC == 1) store_tile_t_pc(&Tb[(rb * 16) * ldt], ldt, qb, v, lane);
     else store_tile_t(&Tb[(rb * 16) * ldt + qb * 16], ldt, v, lane);
 }
 
@@ -45,7 +46,7 @@ __device__ __forceinline__ void store_tb(T* Tb, int ldt, int rb, int qb, floatx4
 // nd[i] = tile(N_bb), nt[i] = tile(N_bb^T).  Returns X[i] = tile(X_bb) and
 // Xt[i] = tile(X_bb^T) (fp32) and stores those diagonal blocks of
 // Tb = T diag(beta); brow[i][r] = beta[16 b + 4(l/16) + r].
-template <typename T, bool PC = false, int NB = 4, int B0 = 0>
+template <typename T, int PC = 0, int NB = 4, int B0 = 0>
 __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[NB], const floatx4 (&nt)[NB],
                                             floatx4 (&X)[NB], floatx4 (&Xt)[NB], T* Tb, int ldt,
                                             const floatx4 (&brow)[NB], int lane, int b0 = B0)
@@ -113,7 +114,7 @@ __device__ __forceinline__ void tsolve_diag(const floatx4 (&nd)[NB], const float
 //           Y0 = N21 X11, Y1 = N31 X11, T21 = -X22 Y0, T31 = -X33 (N32 T21 + Y1)
 // Arguments are fp32 tiles: x_bb = tile(X_bb), xt_bb = tile(X_bb^T) and
 // n_ij = tile(N_ij^T); brow as for tsolve_diag (all four blocks).
-template <typename T, bool PC>
+template <typename T, int PC>
 __device__ __forceinline__ void tb_store_neg(T* Tb, int ldt, floatx4 ct, int rb, int qb,
                                              const floatx4 (&brow)[4], int lane)
 {
@@ -123,7 +124,7 @@ __device__ __forceinline__ void tb_store_neg(T* Tb, int ldt, floatx4 ct, int rb,
     store_tb<T, PC>(Tb, ldt, rb, qb, ct, lane);
 }
 
-template <typename T, bool PC = false>
+template <typename T, int PC = 0>
 __device__ __forceinline__ void tsolve_offdiag_a(floatx4 x00, floatx4 xt11, floatx4 xt22, floatx4 xt33,
                                                  floatx4 n10, floatx4 n20, floatx4 n21, floatx4 n30,
                                                  floatx4 n31, floatx4 n32, T* Tb, int ldt,
@@ -149,7 +150,7 @@ __device__ __forceinline__ void tsolve_offdiag_a(floatx4 x00, floatx4 xt11, floa
     tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu, fx33r, zero4()), 3, 0, brow, lane);
 }
 
-template <typename T, bool PC = false>
+template <typename T, int PC = 0>
 __device__ __forceinline__ void tsolve_offdiag_b(floatx4 x11, floatx4 x22, floatx4 xt22, floatx4 xt33,
                                                  floatx4 n21, floatx4 n31, floatx4 n32, T* Tb, int ldt,
                                                  const floatx4 (&brow)[4], int lane)
@@ -172,7 +173,7 @@ __device__ __forceinline__ void tsolve_offdiag_b(floatx4 x11, floatx4 x22, float
 }
 
 // Both halves on one wave, from X, Xt of tsolve_diag.
-template <typename T, bool PC = false>
+template <typename T, int PC = 0>
 __device__ __forceinline__ void tsolve_offdiag(const floatx4 (&X)[4], const floatx4 (&Xt)[4],
                                                floatx4 n10, floatx4 n20, floatx4 n21, floatx4 n30,
                                                floatx4 n31, floatx4 n32, T* Tb, int ldt,
