@@ -25,7 +25,8 @@ EXPORTS = ("linattn_abi_version", "linattn_status_string", "linattn_chunk_worksp
            "linattn_deltaproduct_fwd", "linattn_chunk_fwd_prep",
            "linattn_normalized_workspace_bytes", "linattn_chunk_fwd_normalized",
            "linattn_chunk_fwd_save", "linattn_chunk_bwd_workspace_bytes", "linattn_chunk_bwd",
-           "linattn_deltaproduct_bwd_workspace_bytes", "linattn_deltaproduct_bwd")
+           "linattn_deltaproduct_bwd_workspace_bytes", "linattn_deltaproduct_bwd",
+           "linattn_chunk_fwd_noalloc")
 QK_MAPS = {"as_is": 0, "l2": 1, "elu1": 2}
 GATE_MAPS = {"as_is": 0, "neg_softplus": 1}
 BETA_MAPS = {"as_is": 0, "sigmoid": 1}
@@ -114,6 +115,9 @@ def load(path: str = LIB_PATH):
         lib.linattn_deltaproduct_bwd.argtypes = [ctypes.POINTER(DeltaProductArgs), vp, vp, vp, vp, vp, vp, vp,
                                                  vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.linattn_deltaproduct_bwd.restype = ctypes.c_int
+        lib.linattn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkArgs), ctypes.POINTER(PrepArgs), vp, vp, vp,
+                                                  vp, vp, vp, vp, vp, vp]
+        lib.linattn_chunk_fwd_noalloc.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -163,7 +167,7 @@ def chunk_workspace_bytes(B, H, T, dk, dv, *, rule, gate, dtype="bf16", chunk=64
 
 def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar", chunk=64,
               out=None, s_final=None, return_state=True, workspace=None, qk_map="as_is",
-              gate_map="as_is", beta_map="as_is"):
+              gate_map="as_is", beta_map="as_is", no_alloc=False):
     """Chunkwise forward over whole sequences on the GPU.
 
     q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] (scalar gate) or [B,H,T,dk]
@@ -172,7 +176,9 @@ def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar
     None).  Runs on torch's current stream of q's device, asynchronously.
     qk_map ("as_is" | "l2" | "elu1"), gate_map ("as_is" | "neg_softplus") and
     beta_map ("as_is" | "sigmoid") treat q/k, g and beta as raw projections
-    mapped inside the kernel (linattn_chunk_fwd_prep).
+    mapped inside the kernel (linattn_chunk_fwd_prep).  no_alloc=True calls
+    linattn_chunk_fwd_noalloc: the library's static device scratch replaces the
+    workspace (pass out and s_final to allocate nothing at all).
     """
     import torch
     lib = load()
@@ -205,6 +211,13 @@ def chunk_fwd(q, k, v, g=None, beta=None, s0=None, *, rule="delta", gate="scalar
         _check(s_final, "s_final", (B, H, dk, dv), torch.float32, dev)
     a = chunk_args(B, H, T, dk, dv, rule=rule, gate=gate, dtype=dtype, chunk=chunk)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if no_alloc:
+        pa = PrepArgs(QK_MAPS[qk_map], GATE_MAPS[gate_map], BETA_MAPS[beta_map])
+        st = lib.linattn_chunk_fwd_noalloc(ctypes.byref(a), ctypes.byref(pa), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           _ptr(beta), _ptr(s0), _ptr(out), _ptr(s_final), stream)
+        if st != 0:
+            raise LinattnError(st, "linattn_chunk_fwd_noalloc")
+        return out, s_final
     need = int(lib.linattn_chunk_workspace_bytes(ctypes.byref(a)))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

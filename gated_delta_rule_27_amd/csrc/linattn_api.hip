@@ -7,6 +7,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 using namespace linattn;
 
@@ -664,3 +665,49 @@ linattn_status linattn_deltaproduct_bwd(const linattn_deltaproduct_args* a, cons
 
 }  // extern "C"
 
+// ---- the chunk forward that allocates nothing ------------------------------
+// Scratch of linattn_chunk_fwd_noalloc: a static device array, one per GPU.  In
+// host code `scratch` names a host-side stand-in; kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[LINATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// This device's scratch address, looked up once per device with it current.
+hipError_t device_scratch(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" linattn_status linattn_chunk_fwd_noalloc(const linattn_chunk_args* a, const linattn_prep_args* prep,
+                                                    const void* q, const void* k, const void* v, const void* g,
+                                                    const void* beta, const float* s0, void* o, float* s_final,
+                                                    void* stream)
+{
+    ChunkProblem p{};
+    const linattn_status st = validate_chunk(a, &p, prep);
+    if (st != LINATTN_OK) return st;
+    const size_t need = path_workspace_bytes(p);
+    if (need > LINATTN_NOALLOC_SCRATCH_BYTES) return LINATTN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0 && p.B * p.H > 0 && p.T > 0 && device_scratch(&ws) != hipSuccess) return LINATTN_ERR_LAUNCH;
+    return linattn_chunk_fwd_prep(a, prep, q, k, v, g, beta, s0, o, s_final, ws, ws ? need : 0, stream);
+}

@@ -339,6 +339,29 @@ linattn_status linattn_deltaproduct_bwd(const linattn_deltaproduct_args *a,
                                         void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * linattn_chunk_fwd_prep without a workspace argument.  Where the chosen path
+ * stages per-chunk operands (the per-channel gate, chunk sizes other than 64,
+ * fp32 tokens at dk = 128 or with the per-channel gate) they go to a static
+ * device array of LINATTN_NOALLOC_SCRATCH_BYTES owned by the library, one per
+ * GPU, held until the process ends; its address is looked up once per device
+ * (the device current at the call, which must own `stream`).  The call makes
+ * no allocation.  Problems whose workspace (linattn_chunk_workspace_bytes)
+ * exceeds the array return LINATTN_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or threads) race and must be serialised by the
+ * caller.  The array needs no clearing between calls (every byte a call reads
+ * was written by the same call).  Arguments otherwise as
+ * linattn_chunk_fwd_prep (prep may be NULL).
+ */
+#define LINATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+linattn_status linattn_chunk_fwd_noalloc(const linattn_chunk_args *a, const linattn_prep_args *prep,
+                                         const void *q, const void *k, const void *v,
+                                         const void *g, const void *beta,
+                                         const float *s0, void *o, float *s_final, void *stream);
+
+/*
  * One recurrent decode step for N sequences x H heads, updating the state in
  * place ("Linear Attention, Visualized", "Optional: Linear attention as an
  * RNN" and the DeltaNet recurrent form; "All sorts of famous Attention
