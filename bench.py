@@ -116,14 +116,16 @@ def time_chunk(la, syn, case, dev, steps, warmup=20):
     import torch
     B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
     x = syn.chunk_inputs_torch(case, dev)
-    out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    out = torch.empty((B, H, T, dv), dtype=tdt, device=dev)
     s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    wsb = la.chunk_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate)
+    wsb = la.chunk_workspace_bytes(B, H, T, dk, dv, rule=case.rule, gate=case.gate, dtype=case.dtype,
+                                   chunk=case.chunk)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
     def step():
         la.chunk_fwd(x["q"], x["k"], x["v"], x.get("g"), x.get("beta"), None, rule=case.rule,
-                     gate=case.gate, out=out, s_final=s_fin, workspace=ws)
+                     gate=case.gate, chunk=case.chunk, out=out, s_final=s_fin, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -139,7 +141,7 @@ def time_chunk(la, syn, case, dev, steps, warmup=20):
     abytes = chunk_alg_bytes(B, H, T, dk, dv, s, case.rule, case.gate)
     aflops = chunk_nominal_flops(B, H, T, dk, dv, case.rule)
     return {"workload": f"{case.rule}/{case.gate} chunk_fwd B={B} H={H} T={T} dk={dk} dv={dv} "
-                        f"{case.dtype} tokens fp32 state",
+                        f"chunk={case.chunk} {case.dtype} tokens fp32 state",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -149,21 +151,25 @@ def time_chunk(la, syn, case, dev, steps, warmup=20):
 def time_prep(la, case, dev, steps, warmup=20):
     """Event-timed chunk forward from raw projections with the input
     preparation fused into the kernel (q, k L2-normalised, log-gate
-    -softplus, beta sigmoid), at the shape of ``case``; raw inputs drawn on the
-    device (q, k N(0,1) * 2, gate and beta logits N(0,1))."""
+    -softplus per token or per key channel, beta sigmoid), at the shape and
+    gate of ``case``; raw inputs drawn on the device (q, k N(0,1) * 2, gate and
+    beta logits N(0,1))."""
     import torch
     B, H, T, dk, dv = case.B, case.H, case.T, case.dk, case.dv
     gen = torch.Generator(device=dev)
     gen.manual_seed(27 * 1000 + 77)
     rn = lambda *sh: torch.randn(*sh, generator=gen, device=dev, dtype=torch.float32)
     q, k = (rn(B, H, T, dk) * 2).bfloat16(), (rn(B, H, T, dk) * 2).bfloat16()
-    v, g, beta = rn(B, H, T, dv).bfloat16(), rn(B, H, T).bfloat16(), rn(B, H, T).bfloat16()
+    gshape = (B, H, T, dk) if case.gate == "channel" else (B, H, T)
+    v, g, beta = rn(B, H, T, dv).bfloat16(), rn(*gshape).bfloat16(), rn(B, H, T).bfloat16()
     out = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
     s_fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    wsb = la.chunk_workspace_bytes(B, H, T, dk, dv, rule="delta", gate=case.gate)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
     def step():
-        la.chunk_fwd(q, k, v, g, beta, None, rule="delta", gate="scalar", out=out, s_final=s_fin,
-                     qk_map="l2", gate_map="neg_softplus", beta_map="sigmoid")
+        la.chunk_fwd(q, k, v, g, beta, None, rule="delta", gate=case.gate, out=out, s_final=s_fin,
+                     workspace=ws, qk_map="l2", gate_map="neg_softplus", beta_map="sigmoid")
 
     for _ in range(warmup):
         step()
@@ -175,14 +181,15 @@ def time_prep(la, case, dev, steps, warmup=20):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    abytes = chunk_alg_bytes(B, H, T, dk, dv, 2, "delta", "scalar")
+    abytes = chunk_alg_bytes(B, H, T, dk, dv, 2, "delta", case.gate)
     aflops = chunk_nominal_flops(B, H, T, dk, dv, "delta")
-    return {"workload": f"gdn chunk_fwd from raw projections (fused L2 q/k, -softplus gate, "
+    kind = "kda" if case.gate == "channel" else "gdn"
+    return {"workload": f"{kind} chunk_fwd from raw projections (fused L2 q/k, -softplus gate, "
                         f"sigmoid beta) B={B} H={H} T={T} dk={dk} dv={dv} bf16",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "path": "pipe with input preparation", "steps": steps}
+            "path": ("split" if case.gate == "channel" else "pipe") + " with input preparation", "steps": steps}
 
 
 def time_normalized(la, syn, case, dev, steps, warmup=20):
@@ -439,6 +446,9 @@ def time_deltaproduct_bwd(la, syn, case, dev, steps, warmup=2):
 
 def chunk_path(case, wsb):
     """Which chunk kernel the library runs for this case (its dispatch rule)."""
+    if case.chunk != 64 or (case.dtype == "fp32" and (case.dk != 64 or case.gate == "channel")) \
+            or os.environ.get("LINATTN_CHUNK_PATH") == "gen":
+        return "gen"
     if wsb:
         return "split"
     env = os.environ.get("LINATTN_CHUNK_PATH")
@@ -448,7 +458,8 @@ def chunk_path(case, wsb):
 
 
 CHUNK_KERNELS = {"pipe": "chunk_pipe_kernel", "fused": "chunk_fused_kernel",
-                 "split": "chunk_intra_channel_kernel + chunk_chain_kernel"}
+                 "split": "chunk_intra_channel_kernel + chunk_chain_kernel",
+                 "gen": "gen_intra_kernel + gen_chain_kernel"}
 
 
 def main():
@@ -468,9 +479,13 @@ def main():
     ap.add_argument("--path", choices=["pipe", "fused", "split"], default=None,
                     help="chunk path for the scalar gate (default: the library's choice: the "
                          "pipelined single-pass kernel for the delta rule with bf16 tokens)")
-    ap.add_argument("--other-configs", default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg2norm,cfg3bwd,gdp2bwd,cfg4bwd",
+    ap.add_argument("--other-configs",
+                    default="cfg2,cfg3b,cfg4,gdp2,cfg3prep,cfg4prep,cfg2norm,cfg3bwd,gdp2bwd,cfg4bwd,"
+                            "cfg3c16,cfg3c32,cfg3c128,cfg3fp32",
                     help="comma-separated secondary chunk workloads to time after the headline "
-                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg2norm, cfg3bwd, gdp2bwd, cfg4bwd), or 'none'")
+                         "one (cfg2, cfg3b, cfg4, gdp2, cfg3prep, cfg4prep, cfg2norm, cfg3bwd, gdp2bwd, "
+                         "cfg4bwd, cfg3c16/cfg3c32/cfg3c128 (the GDN workload at other chunk sizes), "
+                         "cfg3fp32 (fp32 tokens), cfg4fp32 (KDA with fp32 tokens, T = 65536)), or 'none'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "for scaling HBM byte counters")
@@ -551,6 +566,14 @@ def main():
             others.append(time_deltaproduct(la, syn, syn.GDP2, dev, steps=10))
         elif name == "cfg3prep":
             others.append(time_prep(la, syn.CFG3, dev, steps=10))
+        elif name == "cfg4prep":
+            others.append(time_prep(la, syn.CFG4, dev, steps=3, warmup=2))
+        elif name in ("cfg3c16", "cfg3c32", "cfg3c128"):
+            others.append(time_chunk(la, syn, syn.CFG3.with_(chunk=int(name[5:])), dev, steps=5, warmup=3))
+        elif name == "cfg3fp32":
+            others.append(time_chunk(la, syn, syn.CFG3.with_(dtype="fp32"), dev, steps=5, warmup=3))
+        elif name == "cfg4fp32":
+            others.append(time_chunk(la, syn, syn.CFG4.with_(dtype="fp32", T=65536), dev, steps=3, warmup=2))
         elif name == "cfg2norm":
             others.append(time_normalized(la, syn, syn.CFG2, dev, steps=10))
         elif name == "cfg3bwd":
@@ -562,6 +585,7 @@ def main():
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
             others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))
+        print(f"bench: {name} done ({others[-1]['ms_per_step']} ms per step)", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     # ---------------- decode step --------------------------------------------

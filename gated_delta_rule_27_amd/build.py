@@ -3,7 +3,9 @@
 Every ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
 parallel) and linked into ``gated_delta_rule_27_amd/liblinattn.so``.  The
 matrix-core throughput probe that bench.py reports beside the datasheet peak
-(``peak/mfma_peak.hip``) is built on its own into ``libmfmapeak.so``.
+(``peak/mfma_peak.hip``) is built on its own into ``libmfmapeak.so``, and the
+LDS lane-group probe (``peak/lds_banks.hip``) into the executable
+``peak/lds_banks``.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
 PEAK_SRC = os.path.join(HERE, "peak", "mfma_peak.hip")
 PEAK_LIB = os.path.join(HERE, "libmfmapeak.so")
+LDS_SRC = os.path.join(HERE, "peak", "lds_banks.hip")
+LDS_BIN = os.path.join(HERE, "peak", "lds_banks")
 ARCH = os.environ.get("LINATTN_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -59,8 +63,13 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {PEAK_SRC}:\n{r.stdout}{r.stderr}")
     os.replace(ptmp, PEAK_LIB)
+    ltmp = LDS_BIN + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-o", ltmp, LDS_SRC], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {LDS_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(ltmp, LDS_BIN)
     if verbose:
-        print(f"built {LIB} and {PEAK_LIB}")
+        print(f"built {LIB}, {PEAK_LIB} and {LDS_BIN}")
     return LIB
 
 
