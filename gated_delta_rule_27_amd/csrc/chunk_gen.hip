@@ -29,7 +29,8 @@
 //           (fp32: 16 x 16 diagonal blocks by forward substitution, one lane
 //           per column; the blocks below by block substitution on the fp32
 //           matrix cores)
-//       a4  W = T diag(beta) <-K,  U = T diag(beta) V   (fp32 matrix cores)
+//       a4  W = T diag(beta) <-K,  U = T diag(beta) V   (matrix cores with
+//           operands of the token type: T rounded once, like every operand)
 //       and the operands of the state pass: <-Q = 2^G . Q, ->K^T with
 //       ->k_l = 2^(G_{C-1} - G_l) . k_l, and 2^(G_{C-1})
 //   gen_chain_kernel   one workgroup per (b, h, 64 value columns), 4 waves of
@@ -39,7 +40,8 @@
 //       c1  O_li = <-Q_li S_r + sum_{mj <= li} Aq(li, mj) Z_mj
 //           dS  += ->K_li^T Z_li
 //     then S_{r+1} = Diag(2^(G_{C-1})) S_r + dS.  Operands are read as
-//     matrix-core fragments straight from the workspace (L2-resident).
+//     matrix-core fragments straight from the workspace (L2-resident), each
+//     16-row block's while the block before it is computed.
 //
 // Rows past the end of the sequence are staged as zeros (k = v = 0, g = 0,
 // beta = 0), which leaves the state unchanged; their outputs are not written.
@@ -350,8 +352,8 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
             const int lb = p / (kKS / 16), cb = p % (kKS / 16);
             floatx4 acc = zero4();
             for (int mb = 0; mb <= lb; ++mb)
-                acc = mm16<float>(&Lm[16 * lb * LDL + 16 * mb], LDL, load_tile_rl(&xs[16 * mb * kLDS + 16 * cb], kLDS, lane),
-                                  acc, lane);
+                acc = mm16<T>(&Lm[16 * lb * LDL + 16 * mb], LDL, load_tile_rl(&xs[16 * mb * kLDS + 16 * cb], kLDS, lane),
+                              acc, lane);
             mfma_settle();
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
@@ -407,6 +409,17 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
 // ===========================================================================
 // State pass + output
 // ===========================================================================
+// Operands of one 16-row block of a chunk as this wave uses them: fragments of
+// W, <-Q and ->K^T, the causal Aq fragments of the block's row, and U (the
+// values for the add rule) at the wave's columns.  Each block's operands are
+// fetched while the previous block is computed (the next chunk's first block
+// during the last one), so the loads are off the state recurrence.
+template <typename T, int ND, int NB, bool DELTA>
+struct GenBlk {
+    typename Frag16<T>::type w[DELTA ? ND : 1], q[ND], kr[ND], a[NB];
+    floatx4 u;
+};
+
 template <typename T, int C, int DK, int RULE>
 __global__ __launch_bounds__(256) void gen_chain_kernel(
     const T* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0, T* __restrict__ o,
@@ -415,6 +428,7 @@ __global__ __launch_bounds__(256) void gen_chain_kernel(
     using F = typename Frag16<T>::type;
     constexpr int NB = C / 16, ND = DK / 16;
     constexpr bool DELTA = RULE == kRuleDelta;
+    using Blk = GenBlk<T, ND, NB, DELTA>;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvb = DV / 64;
@@ -426,6 +440,35 @@ __global__ __launch_bounds__(256) void gen_chain_kernel(
     const int cl = lane & 15, g4 = 4 * (lane >> 4);
     const GenWs L = gen_ws(C, DK, DV, (int)sizeof(T), DELTA);
 
+    // operands of block li of chunk c (rows past the end of the sequence read
+    // the last row for the add rule's values; they are zeroed where used)
+    auto fetch = [&](Blk& b, int64_t c, int li) {
+        const unsigned char* wc = ws + (bh * nchunks + c) * L.bytes;
+        const T* const Qd = reinterpret_cast<const T*>(wc + L.qd);
+        const T* const KrT = reinterpret_cast<const T*>(wc + L.krt);
+        const T* const Aq = reinterpret_cast<const T*>(wc + L.aq);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            if constexpr (DELTA)
+                b.w[db] = frag16_g(reinterpret_cast<const T*>(wc + L.w) + 16 * li * DK + 16 * db, DK, lane);
+            b.q[db] = frag16_g(Qd + 16 * li * DK + 16 * db, DK, lane);
+            b.kr[db] = frag16_g(KrT + 16 * db * C + 16 * li, C, lane);
+        }
+#pragma unroll
+        for (int mj = 0; mj < NB; ++mj)
+            if (mj <= li) b.a[mj] = frag16_g(Aq + 16 * li * C + 16 * mj, C, lane);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = 16 * li + g4 + rr;
+            if constexpr (DELTA) {
+                b.u[rr] = to_f32(reinterpret_cast<const T*>(wc + L.u)[row * DV + n0 + cl]);
+            } else {
+                const int64_t t = c * C + row < Tlen ? c * C + row : Tlen - 1;
+                b.u[rr] = to_f32(v[(bh * Tlen + t) * DV + n0 + cl]);
+            }
+        }
+    };
+
     floatx4 S[ND];
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -433,14 +476,13 @@ __global__ __launch_bounds__(256) void gen_chain_kernel(
         for (int rr = 0; rr < 4; ++rr)
             S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
 
+    Blk cur, nxt;
+    if (nchunks > 0) fetch(cur, 0, 0);
     for (int64_t c = 0; c < nchunks; ++c) {
-        const unsigned char* wc = ws + (bh * nchunks + c) * L.bytes;
-        const T* const Qd = reinterpret_cast<const T*>(wc + L.qd);
-        const T* const KrT = reinterpret_cast<const T*>(wc + L.krt);
-        const T* const Aq = reinterpret_cast<const T*>(wc + L.aq);
-        const float* const gC = reinterpret_cast<const float*>(wc + L.gc);
-        const T* const Ww = reinterpret_cast<const T*>(wc + L.w);
-        const T* const Uw = reinterpret_cast<const T*>(wc + L.u);
+        const float* const gC = reinterpret_cast<const float*>(ws + (bh * nchunks + c) * L.bytes + L.gc);
+        floatx4 gd[ND];
+#pragma unroll
+        for (int db = 0; db < ND; ++db) gd[db] = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
         const int64_t t0 = c * C;
         F Sf[ND];
 #pragma unroll
@@ -451,50 +493,44 @@ __global__ __launch_bounds__(256) void gen_chain_kernel(
         F Zf[NB];
 #pragma unroll
         for (int li = 0; li < NB; ++li) {
+            if (li + 1 < NB) fetch(nxt, c, li + 1);
+            else fetch(nxt, c + 1 < nchunks ? c + 1 : c, 0);
             // b1: Z = U - W S_r (delta) | V (add)
-            floatx4 Z;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = 16 * li + g4 + rr;
-                if constexpr (DELTA) {
-                    Z[rr] = to_f32(Uw[row * DV + n0 + cl]);
-                } else {
-                    const bool ok = t0 + row < Tlen;
-                    Z[rr] = ok ? to_f32(v[(bh * Tlen + t0 + row) * DV + n0 + cl]) : 0.f;
-                }
-            }
-            floatx4 O = zero4();
+            floatx4 Z = cur.u;
             if constexpr (DELTA) {
                 floatx4 P = zero4();
 #pragma unroll
-                for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_g(Ww + 16 * li * DK + 16 * db, DK, lane), Sf[db], P);
+                for (int db = 0; db < ND; ++db) P = mma16<T>(cur.w[db], Sf[db], P);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    if (t0 + 16 * li + g4 + rr >= Tlen) Z[rr] = 0.f;
             }
             Zf[li] = frag16_acc<T>(Z);
             // c1: O = <-Q S_r + sum_{mj <= li} Aq(li, mj) Z_mj
+            floatx4 O = zero4();
 #pragma unroll
-            for (int db = 0; db < ND; ++db) O = mma16<T>(frag16_g(Qd + 16 * li * DK + 16 * db, DK, lane), Sf[db], O);
+            for (int db = 0; db < ND; ++db) O = mma16<T>(cur.q[db], Sf[db], O);
 #pragma unroll
-            for (int mj = 0; mj <= li; ++mj) O = mma16<T>(frag16_g(Aq + 16 * li * C + 16 * mj, C, lane), Zf[mj], O);
+            for (int mj = 0; mj <= li; ++mj) O = mma16<T>(cur.a[mj], Zf[mj], O);
+            // ->K_li^T Z_li
+#pragma unroll
+            for (int db = 0; db < ND; ++db) dS[db] = mma16<T>(cur.kr[db], Zf[li], dS[db]);
             mfma_settle();   // O is read inside the row-bounds branches below
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int64_t row = t0 + 16 * li + g4 + rr;
                 if (row < Tlen) o[(bh * Tlen + row) * DV + n0 + cl] = from_f32<T>(O[rr]);
             }
-            // ->K_li^T Z_li
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-                dS[db] = mma16<T>(frag16_g(KrT + 16 * db * C + 16 * li, C, lane), Zf[li], dS[db]);
+            cur = nxt;
         }
         // S_{r+1} = Diag(2^(G_{C-1})) S_r + ->K^T Z
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            const floatx4 gd = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) S[db][rr] = gd[rr] * S[db][rr] + dS[db][rr];
-        }
+            for (int rr = 0; rr < 4; ++rr) S[db][rr] = gd[db][rr] * S[db][rr] + dS[db][rr];
     }
     if (s_final) {
 #pragma unroll

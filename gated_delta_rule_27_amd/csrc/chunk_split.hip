@@ -78,7 +78,9 @@ typedef __attribute__((__vector_size__(16))) int i4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSpan2Max = 120.f;   // 2^60 per factor, far inside bf16 / fp32 range
 
-template <int DK, int RULE, int GATE>
+// PREP: the input maps of prep.h (flags in prep) applied while staging; a
+// separate instantiation, so the kernel without maps is the plain one.
+template <int DK, int RULE, int GATE, bool PREP>
 __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ g,
     const bf16* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks,
@@ -150,15 +152,15 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
         // DK / 8 lanes holding a row reducing its L2 norm; the log-gate map where
         // the gate is read in fp32; beta below)
         __syncthreads();
-        const int qk_map = prep_qk_map(prep);
+        const int qk_map = PREP ? prep_qk_map(prep) : 0;
 #pragma unroll
         for (int p = 0; p < NV; ++p) {
             const int idx = (p * NT + tid) * 8;
             const int row = idx / DK, col = idx % DK;
             const bool ok = t0 + row < Tlen;
             const i4 z = {0, 0, 0, 0};
-            const i4 qp = prep_qk<bf16, DK / 8>(qreg[p], qk_map);
-            const i4 kp = prep_qk<bf16, DK / 8>(kreg[p], qk_map);
+            const i4 qp = PREP ? prep_qk<bf16, DK / 8>(qreg[p], qk_map) : qreg[p];
+            const i4 kp = PREP ? prep_qk<bf16, DK / 8>(kreg[p], qk_map) : kreg[p];
             *reinterpret_cast<i4*>(&qs[row * LDQ + col]) = ok ? qp : z;
             *reinterpret_cast<i4*>(&ks[row * LDQ + col]) = ok ? kp : z;
             if constexpr (GATE == kGateChannel) *reinterpret_cast<i4*>(&gs[row * LDQ + col]) = ok ? greg[p] : z;
@@ -166,8 +168,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
         if (tid < kC) {
             // a scalar gate is the channel gate with every channel equal
             if constexpr (GATE != kGateChannel)
-                gsc[tid] = (t0 + tid < Tlen) ? prep_gate(to_f32(gsreg), prep) * kLog2e : 0.f;
-            bet[tid] = (DELTA && t0 + tid < Tlen) ? prep_beta(to_f32(breg), prep) : 0.f;
+                gsc[tid] = (t0 + tid < Tlen) ? (PREP ? prep_gate(to_f32(gsreg), prep) : to_f32(gsreg)) * kLog2e : 0.f;
+            bet[tid] = (DELTA && t0 + tid < Tlen) ? (PREP ? prep_beta(to_f32(breg), prep) : to_f32(breg)) : 0.f;
         }
         if (task + gridDim.x < ntasks) fetch(task + gridDim.x);
         __syncthreads();
@@ -183,7 +185,9 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
             for (int rr = 0; rr < 16; ++rr) {
                 float gv;
                 if constexpr (GATE == kGateChannel)
-                    gv = t0 + 16 * pb + rr < Tlen ? prep_gate(to_f32(gs[(16 * pb + rr) * LDQ + pc]), prep) * kLog2e : 0.f;
+                    gv = !PREP ? to_f32(gs[(16 * pb + rr) * LDQ + pc]) * kLog2e
+                       : t0 + 16 * pb + rr < Tlen ? prep_gate(to_f32(gs[(16 * pb + rr) * LDQ + pc]), prep) * kLog2e
+                                                   : 0.f;
                 else gv = gsc[16 * pb + rr];
                 acc += gv;
                 Gl[rr] = acc;                          // G_l - G_s(b)
@@ -238,7 +242,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
                         float dG = 0.f;                // G_l - G_m, base 2
                         for (int s2 = m + 1; s2 <= l; ++s2) {
                             if constexpr (GATE == kGateChannel)
-                                dG += t0 + s2 < Tlen ? prep_gate(to_f32(gs[s2 * LDQ + c]), prep) * kLog2e : 0.f;
+                                dG += !PREP ? to_f32(gs[s2 * LDQ + c]) * kLog2e
+                                    : t0 + s2 < Tlen ? prep_gate(to_f32(gs[s2 * LDQ + c]), prep) * kLog2e : 0.f;
                             else dG += gsc[s2];
                         }
                         const float km = to_f32(ks[m * LDQ + c]) * fast_exp2(dG);
@@ -689,10 +694,16 @@ hipError_t launch_split(const ChunkProblem& p, bf16* states, hipStream_t s)
         // persistent: one workgroup per CU (its LDS use allows no second one)
         const int64_t ntasks = bh * nchunks;
         const int64_t grid = ntasks < ncu ? ntasks : ncu;
-        hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE>), dim3((unsigned)grid), dim3(512), 0, s,
-                           static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
-                           static_cast<const bf16*>(p.g), static_cast<const bf16*>(p.beta), ws, p.T,
-                           nchunks, ntasks, p.prep);
+        if (p.prep != 0)
+            hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE, true>), dim3((unsigned)grid), dim3(512), 0,
+                               s, static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
+                               static_cast<const bf16*>(p.g), static_cast<const bf16*>(p.beta), ws, p.T,
+                               nchunks, ntasks, p.prep);
+        else
+            hipLaunchKernelGGL((chunk_intra_channel_kernel<DK, RULE, GATE, false>), dim3((unsigned)grid), dim3(512), 0,
+                               s, static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
+                               static_cast<const bf16*>(p.g), static_cast<const bf16*>(p.beta), ws, p.T,
+                               nchunks, ntasks, 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
