@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = ok ? P.v[p] : i4{0, 0, 0, 0};
         }
     };
-    // wave 4's gate scan of one chunk into slot sl.  G is kept in base 2
+    // wave 7's gate scan of one chunk into slot sl.  G is kept in base 2
     // (log2 e * prefix sum) so every decay factor is one hardware exp2.
     auto scan = [&](const Pref& P, int64_t t0, int sl) {
         const bool ok = t0 + lane < Tlen;
@@ -339,27 +339,30 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
         diag_block(Kb, Gs, bet, b, ln, nd[0], nt[0], br[0], kb);
         tsolve_diag<T, 2, 1>(nd, nt, Xa, Xta, Tbb, LDC, br, ln, b);
         const floatx4 X = Xa[0], Xt = Xta[0];
+        // the six blocks below the diagonal, 1-2 per wave: blocks 0 and 1 also
+        // hold the off-diagonal transform's longest inputs (X00, X11), so the
+        // waves of blocks 2 and 3 take two N blocks each
         if (b == 0) {
             block_frags(Kb, 1, ln, k2);
             n_block(Gs, bet, 1, 0, kb, k2, ln);
-            block_frags(Kb, 2, ln, k2);
-            n_block(Gs, bet, 2, 0, kb, k2, ln);
             Xx[4 * kWave + ln] = X;
         } else if (b == 1) {
             block_frags(Kb, 2, ln, k2);
             n_block(Gs, bet, 2, 1, kb, k2, ln);
-            block_frags(Kb, 3, ln, k2);
-            n_block(Gs, bet, 3, 1, kb, k2, ln);
             Xx[0 * kWave + ln] = Xt;
             Xx[5 * kWave + ln] = X;
         } else if (b == 2) {
             block_frags(Kb, 3, ln, k2);
             n_block(Gs, bet, 3, 2, kb, k2, ln);
+            block_frags(Kb, 0, ln, k2);
+            n_block(Gs, bet, 2, 0, k2, kb, ln);
             Xx[1 * kWave + ln] = X;
             Xx[2 * kWave + ln] = Xt;
         } else {
             block_frags(Kb, 0, ln, k2);
             n_block(Gs, bet, 3, 0, k2, kb, ln);
+            block_frags(Kb, 1, ln, k2);
+            n_block(Gs, bet, 3, 1, k2, kb, ln);
             Xx[3 * kWave + ln] = Xt;
         }
     };
@@ -376,9 +379,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             tsolve_offdiag_a<T, 2>(xx[4 * kWave], xx[0 * kWave], xx[2 * kWave], xx[3 * kWave], nl[0 * kWave],
                                       nl[1 * kWave], nl[2 * kWave], nl[3 * kWave], nl[4 * kWave], nl[5 * kWave],
                                       Tbb, LDC, brow, ln);
+        else if (h == 1)
+            tsolve_offdiag_b1<T, 2>(xx[5 * kWave], xx[2 * kWave], xx[3 * kWave], nl[2 * kWave], nl[4 * kWave],
+                                    nl[5 * kWave], Tbb, LDC, brow, ln);
         else
-            tsolve_offdiag_b<T, 2>(xx[5 * kWave], xx[1 * kWave], xx[2 * kWave], xx[3 * kWave], nl[2 * kWave],
-                                      nl[4 * kWave], nl[5 * kWave], Tbb, LDC, brow, ln);
+            tsolve_t32<T, 2>(xx[1 * kWave], xx[3 * kWave], nl[5 * kWave], Tbb, LDC, brow, ln);
     };
 
     if (wave < 4) {
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             if constexpr (DELTA) aq_state(0, opaque(lane));
             lds_barrier();
             if constexpr (DELTA)
-                if (wave < 2) offdiag(wave, betb[0], Tb[0], opaque(lane));
+                if (wave < 3) offdiag(wave, betb[0], Tb[0], opaque(lane));
             lds_barrier();
         }
         for (int64_t r = 0; r < nchunks; ++r) {
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                                     mma_pair<T>(pair_lds_sw(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
             }
             if constexpr (DELTA)
-                if (wave < 2 && r + 1 < nchunks) offdiag(wave, betb[(r + 1) % 3], Tb[(r + 1) & 1], ln);
+                if (wave < 3 && r + 1 < nchunks) offdiag(wave, betb[(r + 1) % 3], Tb[(r + 1) & 1], ln);
             lds_barrier();
         }
         // waves 4..7 run an even number of steps; the spare one has no work here
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     fetch_qk(P0, 0);
     fetch_gate(P0, 0);
     stage_qk(P0, 0, Qs[0], Ks[0]);
-    if (wave == 4) scan(P0, 0, 0);
+    if (wave == 7) scan(P0, 0, 0);
     fetch_qk(P1, clampc(kC));
     fetch_v(P1, 0);
     fetch_gate(P1, clampc(kC));
@@ -609,7 +614,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     auto stage_and_fetch = [&](Pref& P, int64_t r) {
         stage_qk(P, (r + 2) * kC, Qs[r & 1], Ks[r & 1]);
         stage_v(P, (r + 1) * kC);
-        if (wave == 4) scan(P, (r + 2) * kC, (int)((r + 2) % 3));
+        if (wave == 7) scan(P, (r + 2) * kC, (int)((r + 2) % 3));
         fetch_qk(P, clampc((r + 4) * kC));
         fetch_v(P, clampc((r + 3) * kC));
         fetch_gate(P, clampc((r + 4) * kC));

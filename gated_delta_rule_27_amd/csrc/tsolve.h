@@ -172,6 +172,38 @@ __device__ __forceinline__ void tsolve_offdiag_b(floatx4 x11, floatx4 x22, float
     tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu, fx33r, zero4()), 3, 1, brow, lane);
 }
 
+// Half B without T32 (tsolve_t32), so the two can run on different waves:
+// T21 = -X22 N21 X11, T31 = -X33 (N32 T21 + N31 X11).
+template <typename T, int PC = 0>
+__device__ __forceinline__ void tsolve_offdiag_b1(floatx4 x11, floatx4 xt22, floatx4 xt33, floatx4 n21,
+                                                  floatx4 n31, floatx4 n32, T* Tb, int ldt,
+                                                  const floatx4 (&brow)[4], int lane)
+{
+    using F = typename Frag16<T>::type;
+    const F fx11 = frag16_acc<T>(x11);
+    const F fx22r = frag16_acc<T>(xt22), fx33r = frag16_acc<T>(xt33);
+    const F fn32 = frag16_acc<T>(n32);
+    const floatx4 y0 = mma16<T>(frag16_acc<T>(n21), fx11, zero4());
+    const floatx4 y1 = mma16<T>(frag16_acc<T>(n31), fx11, zero4());
+    const F fy0 = frag16_acc<T>(y0);
+    floatx4 t2 = mma16<T>(fx22r, fy0, zero4());                                   // -T21
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t2[r] = -t2[r];
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fy0, fx22r, zero4()), 2, 1, brow, lane);
+    const F fu = frag16_acc<T>(mma16<T>(fn32, frag16_acc<T>(t2), y1));
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu, fx33r, zero4()), 3, 1, brow, lane);
+}
+
+// T32 = -X33 N32 X22 alone.
+template <typename T, int PC = 0>
+__device__ __forceinline__ void tsolve_t32(floatx4 x22, floatx4 xt33, floatx4 n32, T* Tb, int ldt,
+                                           const floatx4 (&brow)[4], int lane)
+{
+    using F = typename Frag16<T>::type;
+    const F fu32 = frag16_acc<T>(mma16<T>(frag16_acc<T>(n32), frag16_acc<T>(x22), zero4()));   // N32 X22
+    tb_store_neg<T, PC>(Tb, ldt, mma16<T>(fu32, frag16_acc<T>(xt33), zero4()), 3, 2, brow, lane);
+}
+
 // Both halves on one wave, from X, Xt of tsolve_diag.
 template <typename T, int PC = 0>
 __device__ __forceinline__ void tsolve_offdiag(const floatx4 (&X)[4], const floatx4 (&Xt)[4],
