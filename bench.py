@@ -584,7 +584,7 @@ def main():
             others.append(time_deltaproduct_bwd(la, syn, syn.GDP2, dev, steps=5))
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
-            others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 10))
+            others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 50))
         print(f"bench: {name} done ({others[-1]['ms_per_step']} ms per step)", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 

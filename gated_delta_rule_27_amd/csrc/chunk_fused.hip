@@ -9,7 +9,8 @@
 // state") and the GDN row of the chunkwise table.
 //
 // One workgroup owns one (batch, head, 64 value columns) and walks its chunks
-// in order.  Per chunk r (positions l, m = 0..C-1, G = prefix sum of the
+// in order (add rule with fewer such workgroups than compute units: one
+// segment of the chunks, see seg_split).  Per chunk r (positions l, m = 0..C-1, G = prefix sum of the
 // log-gate, gamma_l = exp(G_l), rho_l = exp(G_{C-1} - G_l)):
 //   a1  G, gamma, rho (one wave, shuffle scan)
 //   a2  Aq[l][m] = (q_l . k_m) exp(G_l - G_m)            (m <= l)
@@ -50,6 +51,8 @@
 //        (the other waves go on with the next chunk's P1)
 // Operands are bf16 (fp32 for fp32 tokens), accumulation is fp32; the state
 // stays fp32 and is rounded to the operand type only as an operand.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -91,6 +94,19 @@ __device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
     mi = p;
 }
 
+// Add rule: each head's chunks split into segments run by separate workgroups.
+// Segment s covers chunks [c[s], c[s+1]); n = 1 is the whole sequence.
+constexpr int kMaxSeg = 4;
+struct SegSplit {
+    int n;
+    int c[kMaxSeg + 1];
+};
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
 // the E = 16 / sizeof(T) elements of a 16-byte vector, as floats and back
 template <typename T, typename V>
 __device__ __forceinline__ void vec_f32(V x, float (&f)[16 / sizeof(T)])
@@ -130,7 +146,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, const float* s0, T* __restrict__ o,
     float* s_final, T* __restrict__ states, int64_t Tlen, int DV, int nblocks, int prep,
-    const float* z0, float* z_final)
+    const float* z0, float* z_final, SegSplit seg)
 {
     static_assert(!NORM || RULE == kRuleAdd, "the normaliser belongs to the add rule");
     using Cfg = FusedCfg<T, DK, RULE, GATE>;
@@ -170,8 +186,14 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     // over the 8 XCDs), so its value blocks share q/k reads in that XCD's L2.
     int blk = blockIdx.x;
     if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
-    const int64_t bh = blk / nvb;
-    const int vb = blk % nvb;
+    const int nunit = nvb * seg.n;
+    const int64_t bh = blk / nunit;
+    const int vb = (blk % nunit) % nvb;
+    const int sg = (blk % nunit) / nvb;
+    // this workgroup's chunks [rb, re); the add rule's later segments first form
+    // the state entering chunk rb from the chunks before it (prefix pass below)
+    const int64_t rb = DELTA ? 0 : seg.c[sg], re = DELTA ? (Tlen + kC - 1) / kC : seg.c[sg + 1];
+    const bool last_seg = DELTA || sg == seg.n - 1;
 
     const T* qh = q + bh * Tlen * DK;
     const T* kh = k + bh * Tlen * DK;
@@ -243,7 +265,64 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = ok ? vreg[p] : i4{0, 0, 0, 0};
         }
     };
-    if (nchunks > 0) fetch(0);
+    // Prefix pass (later segments of the add rule): K and V only, loaded two
+    // chunks ahead into two register sets (kreg, vreg and qreg, vreg2), since
+    // its chunks take far less time than one load's latency.  Loads are
+    // unconditional (chunk index clamped), as in the main loop.
+    i4 vreg2[NV];
+    auto fetch_kv = [&](int64_t t0, i4 (&kr)[NQ], i4 (&vr)[NV]) {
+#pragma unroll
+        for (int p = 0; p < NQ; ++p) {
+            const int idx = (p * kNT + tid) * E;
+            const int row = idx / DK, col = idx % DK;
+            const int64_t tr = t0 + row < Tlen ? t0 + row : Tlen - 1;
+            kr[p] = *reinterpret_cast<const i4*>(kh + tr * DK + col);
+        }
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = (p * kNT + tid) * E;
+            const int row = idx / kDVB, col = idx % kDVB;
+            const int64_t tr = t0 + row < Tlen ? t0 + row : Tlen - 1;
+            vr[p] = *reinterpret_cast<const i4*>(vh + tr * DV + col);
+        }
+    };
+    auto stage_kv = [&](int64_t t0, const i4 (&kr)[NQ], const i4 (&vr)[NV]) {
+        const int qk_map = prep_qk_map(prep);
+#pragma unroll
+        for (int p = 0; p < NQ; ++p) {
+            const int idx = (p * kNT + tid) * E;
+            const int row = idx / DK, col = idx % DK;
+            const bool ok = t0 + row < Tlen;
+            const i4 kp = prep_qk<T, DK / E>(kr[p], qk_map);
+            const i4 kv = ok ? kp : i4{0, 0, 0, 0};
+            if constexpr (E == 8) {
+                typedef __attribute__((__vector_size__(8))) int i2;
+                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col)]) = i2{kv[0], kv[1]};
+                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col + 4)]) = i2{kv[2], kv[3]};
+            } else {
+                *reinterpret_cast<i4*>(&Ks[row * LDQ + pcol(col)]) = kv;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = (p * kNT + tid) * E;
+            const int row = idx / kDVB, col = idx % kDVB;
+            const bool ok = t0 + row < Tlen;
+            *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = ok ? vr[p] : i4{0, 0, 0, 0};
+        }
+    };
+    // prefix chunk r: stage it from its register set and refill the set with
+    // chunk r + 2 (clamped to the last prefix chunk)
+    auto prefix_stage = [&](int64_t r, i4 (&kr)[NQ], i4 (&vr)[NV]) {
+        stage_kv(r * kC, kr, vr);
+        fetch_kv((r + 2 < rb ? r + 2 : rb - 1) * kC, kr, vr);
+    };
+    if (rb > 0) {
+        fetch_kv(0, kreg, vreg);
+        fetch_kv(rb > 1 ? kC : 0, qreg, vreg2);
+    } else if (re > 0) {
+        fetch(0);
+    }
 
     // The output of a chunk is staged in LDS (Os) by the state waves and written
     // to HBM by waves kW0..7 during the next chunk, after that chunk's loads were
@@ -277,7 +356,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, 0);
         }
     };
-    const int64_t tlast = (nchunks - 1) * kC;     // start of the last chunk
+    const int64_t tlast = (re - 1) * kC;          // start of the segment's last chunk
     // All matrix-core fragments (every k step) of the 16-row block b of a [C][DK]
     // tile (Qs or Ks); a wave loads each block it needs once per chunk and forms
     // its tiles from the registers.
@@ -445,6 +524,84 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
     };
 
+    // K^T through the matrix core: tiles iw, iw + NW, ... of the NL x ND tiles
+    // of Ks (transposed into KsT) for wave iw of NW
+    auto kt_share = [&](auto nwc, int iw, int ln) {
+        constexpr int NW = decltype(nwc)::value, NKT = NL * ND / NW;
+        F af[NKT];
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+            const int t = iw + NW * i;
+            af[i] = frag16_lds_pc(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
+        }
+        const F id = ident_frag<T>(ln);
+        floatx4 d[NKT];
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) d[i] = mma16<T>(af[i], id, zero4());
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+            const int t = iw + NW * i;
+            store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
+        }
+    };
+    // b1 of state wave w: S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z (NORM: and
+    // z_{r+1} for the wave's quarter of the key blocks)
+    auto state_update = [&](floatx4 (&S)[ND], const floatx4 (&Z)[NL], const float* gam, const float* rho,
+                            int64_t r, int ln) {
+        const int cl = ln & 15, g4 = 4 * (ln >> 4);
+        const float gC = gam[kC - 1];
+        floatx4 zr[NL];
+#pragma unroll
+        for (int lj = 0; lj < NL; ++lj) {
+            zr[lj] = Z[lj];
+            if constexpr (GATED) {
+                const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) zr[lj][rr] *= rh[rr];
+            }
+        }
+        const auto zr01 = pair_regs<T>(zr[0], zr[1]), zr23 = pair_regs<T>(zr[2], zr[3]);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gC;
+            S[db] = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
+                                mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
+        }
+        if constexpr (NORM) {
+            // z_{r+1} = gamma_{C-1} z_r + K^T rho for this wave's key blocks: rho
+            // as value column 0 of Z, z as value column 0 of the state (lanes
+            // with cl = 0 hold and store it)
+            floatx4 rz[NL];
+#pragma unroll
+            for (int lj = 0; lj < NL; ++lj) {
+                const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) rz[lj][rr] = cl == 0 ? rh[rr] : 0.f;
+            }
+            const auto rz01 = pair_regs<T>(rz[0], rz[1]), rz23 = pair_regs<T>(rz[2], rz[3]);
+#pragma unroll
+            for (int d2 = 0; d2 < ND / 4; ++d2) {
+                const int db = (ND / 4) * wave + d2;
+                floatx4 zt = *reinterpret_cast<const floatx4*>(&zSb[r & 1][16 * db + g4]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) zt[rr] *= gC;
+                zt = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), rz23,
+                                 mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), rz01, zt));
+                if (cl == 0) *reinterpret_cast<floatx4*>(&zSb[(r + 1) & 1][16 * db + g4]) = zt;
+            }
+        }
+    };
+    // Prefix pass, per chunk r < rb: K and V to LDS (wave 4: the gate scan) and
+    // the next loads; K^T on all eight waves, the state waves also take their V
+    // columns into registers; then the state waves update S while the others
+    // stage the next chunk.  Two barriers per chunk; the other waves' part:
+    auto prefix_other = [&](int64_t r, int ln) {
+        lds_barrier();
+        kt_share(IntC<kNW>{}, wave, ln);
+        lds_barrier();
+    };
+
     if (wave < 4) {
         // ======== state waves: wave w owns value columns n0..n0+15 of the block and
         // keeps S[:, those columns] as ND result tiles S[db][rr] = S[16 db + g4 + rr][n0 + cl]
@@ -463,7 +620,28 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
         }
         wait_vmem_all();
-        for (int64_t r = 0; r < nchunks; ++r) {
+        if constexpr (!DELTA) {
+            auto pchunk = [&](int64_t r, i4 (&kr)[NQ], i4 (&vr)[NV]) {
+                const int ln = opaque(lane);
+                const int cl = ln & 15, g4 = 4 * (ln >> 4);
+                prefix_stage(r, kr, vr);
+                lds_barrier();
+                kt_share(IntC<kNW>{}, wave, ln);
+                floatx4 Zv[NL];
+#pragma unroll
+                for (int li = 0; li < NL; ++li)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) Zv[li][rr] = to_f32(Vs[(16 * li + g4 + rr) * LDV + n0 + cl]);
+                lds_barrier();
+                state_update(S, Zv, gamb[r & 1], rhob[r & 1], r, ln);
+            };
+            for (int64_t r = 0; r < rb; r += 2) {
+                pchunk(r, kreg, vreg);
+                if (r + 1 < rb) pchunk(r + 1, qreg, vreg2);
+            }
+            if (rb > 0) fetch(rb * kC);
+        }
+        for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
             // lane indices recomputed per chunk so the LDS addresses derived from
             // them are not held in registers across the loop
@@ -544,25 +722,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     if (g4 == 0) qzs[r & 1][16 * wave + cl] = gam[16 * wave + cl] * oz[0];
                 }
             };
-            // K^T through the matrix core (this wave's quarter of the tiles)
-            auto ksT = [&]() {
-                constexpr int NKT = NL * ND / 4;             // transposes per state wave
-                F af[NKT];
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) {
-                    const int t = wave + 4 * i;
-                    af[i] = frag16_lds_pc(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
-                }
-                const F id = ident_frag<T>(ln);
-                floatx4 d[NKT];
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) d[i] = mma16<T>(af[i], id, zero4());
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) {
-                    const int t = wave + 4 * i;
-                    store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
-                }
-            };
+            auto ksT = [&]() { kt_share(IntC<4>{}, wave, ln); };
             if constexpr (!DELTA) {
                 ohist();
             } else {
@@ -633,51 +793,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             // O^T tile -> Os[token][column]
 #pragma unroll
             for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
-            // S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z
-            const float gC = gam[kC - 1];
-            floatx4 zr[NL];
-#pragma unroll
-            for (int lj = 0; lj < NL; ++lj) {
-                zr[lj] = Z[lj];
-                if constexpr (GATED) {
-                    const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) zr[lj][rr] *= rh[rr];
-                }
-            }
-            const auto zr01 = pair_regs<T>(zr[0], zr[1]), zr23 = pair_regs<T>(zr[2], zr[3]);
-#pragma unroll
-            for (int db = 0; db < ND; ++db) {
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gC;
-                S[db] = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
-                                    mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
-            }
-            if constexpr (NORM) {
-                // z_{r+1} = gamma_{C-1} z_r + K^T rho for this wave's key blocks: rho
-                // as value column 0 of Z, z as value column 0 of the state (lanes
-                // with cl = 0 hold and store it)
-                floatx4 rz[NL];
-#pragma unroll
-                for (int lj = 0; lj < NL; ++lj) {
-                    const floatx4 rh = *reinterpret_cast<const floatx4*>(&rho[16 * lj + g4]);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) rz[lj][rr] = cl == 0 ? rh[rr] : 0.f;
-                }
-                const auto rz01 = pair_regs<T>(rz[0], rz[1]), rz23 = pair_regs<T>(rz[2], rz[3]);
-#pragma unroll
-                for (int d2 = 0; d2 < ND / 4; ++d2) {
-                    const int db = (ND / 4) * wave + d2;
-                    floatx4 zt = *reinterpret_cast<const floatx4*>(&zSb[r & 1][16 * db + g4]);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) zt[rr] *= gC;
-                    zt = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), rz23,
-                                     mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), rz01, zt));
-                    if (cl == 0) *reinterpret_cast<floatx4*>(&zSb[(r + 1) & 1][16 * db + g4]) = zt;
-                }
-            }
+            state_update(S, Z, gam, rho, r, ln);
         }
-        if (s_final) {
+        if (s_final && last_seg) {
             const int cl = lane & 15, g4 = 4 * (lane >> 4);
 #pragma unroll
             for (int db = 0; db < ND; ++db)
@@ -693,8 +811,43 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             if constexpr (GATED) greg = g[bh * Tlen + tr];
             if constexpr (DELTA) breg = beta[bh * Tlen + tr];
         };
-        if (nchunks > 0) fetch_gate(0);
-        for (int64_t r = 0; r < nchunks; ++r) {
+        // a1 of chunk r: G is kept in base 2 (log2 e * prefix sum) so every decay
+        // factor is one hardware exp2
+        auto gate_scan = [&](int64_t r, T gv) {
+            const bool ok = r * kC + lane < Tlen;
+            const float G = wave_prefix_sum((GATED && ok) ? prep_gate(to_f32(gv), prep) * kLog2e : 0.f);
+            const float Glast = wave_last(G);
+            Gsb[r & 1][lane] = G;
+            gamb[r & 1][lane] = GATED ? fast_exp2(G) : 1.f;
+            rhob[r & 1][lane] = GATED ? fast_exp2(Glast - G) : 1.f;
+            betb[r & 1][lane] = (DELTA && ok) ? prep_beta(to_f32(breg), prep) : 0.f;
+        };
+        if constexpr (!DELTA) {
+            // the prefix's gate values, two chunks ahead like its tokens
+            T ga = from_f32<T>(0.f), gb = from_f32<T>(0.f);
+            auto load_gate = [&](int64_t r, T& gv) {
+                const int64_t t = (r < rb ? r : rb - 1) * kC + lane;
+                if constexpr (GATED) gv = g[bh * Tlen + (t < Tlen ? t : Tlen - 1)];
+            };
+            auto pchunk = [&](int64_t r, i4 (&kr)[NQ], i4 (&vr)[NV], T& gv) {
+                const int ln = opaque(lane);
+                prefix_stage(r, kr, vr);
+                gate_scan(r, gv);
+                load_gate(r + 2, gv);
+                prefix_other(r, ln);
+            };
+            if (rb > 0) {
+                load_gate(0, ga);
+                load_gate(1, gb);
+            }
+            for (int64_t r = 0; r < rb; r += 2) {
+                pchunk(r, kreg, vreg, ga);
+                if (r + 1 < rb) pchunk(r + 1, qreg, vreg2, gb);
+            }
+            if (rb > 0) fetch(rb * kC);
+        }
+        if (re > rb) fetch_gate(rb * kC);
+        for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
             const int g4 = 4 * (ln >> 4);
@@ -702,21 +855,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             float* const bet = betb[r & 1];
 
             stage(t0);
-            {
-                // G is kept in base 2 (log2 e * prefix sum) so every decay factor
-                // is one hardware exp2
-                const bool ok = t0 + lane < Tlen;
-                const float G = wave_prefix_sum((GATED && ok) ? prep_gate(to_f32(greg), prep) * kLog2e : 0.f);
-                const float Glast = wave_last(G);
-                Gs[lane] = G;
-                gamb[r & 1][lane] = GATED ? fast_exp2(G) : 1.f;
-                rhob[r & 1][lane] = GATED ? fast_exp2(Glast - G) : 1.f;
-                bet[lane] = (DELTA && ok) ? prep_beta(to_f32(breg), prep) : 0.f;
-            }
+            gate_scan(r, greg);
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
             fetch_gate(t0 + kC < tlast ? t0 + kC : tlast);
             if constexpr (NORM)
-                if (r > 0) norm_tail(r - 1, 0, ln);
+                if (r > rb) norm_tail(r - 1, 0, ln);
             lds_barrier();
 
             if constexpr (DELTA) {
@@ -735,14 +878,14 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             } else {
                 aq_share(Gs, 0, kNIW, ln);
                 lds_barrier();
-                if (r > 0) copy_out(t0 - kC, 0, ln);
+                if (r > rb) copy_out(t0 - kC, 0, ln);
             }
             lds_barrier();
         }
     } else if (DELTA && wave == 5) {
         // ======== wave 5 (delta): a2 diagonal block 1, its inverse, N(2,1); half B
         // of the off-diagonal blocks -------------------------------------------------
-        for (int64_t r = 0; r < nchunks; ++r) {
+        for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
             const int g4 = 4 * (ln >> 4);
@@ -768,7 +911,18 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         // ======== waves 6, 7 (delta): N blocks below the diagonal; waves 4..7
         // (add): Aq tiles.  Both: output copy ----------------------------------------
         const int iw = wave - kW0;
-        for (int64_t r = 0; r < nchunks; ++r) {
+        if constexpr (!DELTA) {
+            for (int64_t r = 0; r < rb; r += 2) {
+                prefix_stage(r, kreg, vreg);
+                prefix_other(r, opaque(lane));
+                if (r + 1 < rb) {
+                    prefix_stage(r + 1, qreg, vreg2);
+                    prefix_other(r + 1, opaque(lane));
+                }
+            }
+            if (rb > 0) fetch(rb * kC);
+        }
+        for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
             const int ln = opaque(lane);
             const float* const Gs = Gsb[r & 1];
@@ -776,7 +930,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             stage(t0);
             fetch(t0 + kC < tlast ? t0 + kC : tlast);
             if constexpr (NORM)
-                if (r > 0) norm_tail(r - 1, iw, ln);
+                if (r > rb) norm_tail(r - 1, iw, ln);
             lds_barrier();
             // ---- P2a ----
             if constexpr (DELTA) {
@@ -787,7 +941,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
             lds_barrier();
             // ---- P2b ----
-            if (r > 0) copy_out(t0 - kC, iw, ln);
+            if (r > rb) copy_out(t0 - kC, iw, ln);
             lds_barrier();
         }
     }
@@ -795,13 +949,69 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     // the last chunk's output, once every state wave has staged it
     __syncthreads();
     if constexpr (NORM) {
-        if (wave >= 4 && nchunks > 0) norm_tail(nchunks - 1, wave - 4, lane);
+        if (wave >= 4 && re > rb) norm_tail(re - 1, wave - 4, lane);
         __syncthreads();
     }
-    if (wave >= kW0 && nchunks > 0) copy_out((nchunks - 1) * kC, wave - kW0, lane);
+    if (wave >= kW0 && re > rb) copy_out((re - 1) * kC, wave - kW0, lane);
     if constexpr (NORM)
-        if (z_final && vb == 0)
-            for (int i = tid; i < DK; i += kNT) z_final[bh * DK + i] = zSb[nchunks & 1][i];
+        if (z_final && vb == 0 && last_seg)
+            for (int i = tid; i < DK; i += kNT) z_final[bh * DK + i] = zSb[re & 1][i];
+}
+
+// A prefix chunk (state update only) costs about this fraction of a full chunk
+// step of the add rule (cycle probe at d_k = d_v = 128: 2.3 K against 5.0 K
+// cycles; a sweep of the split at B4 H16 T4096 has its minimum near 0.45).
+constexpr double kPrefixCost = 0.45;
+
+// Segments per (head, value block) for the add rule.  When the plain grid leaves
+// compute units idle, later segments run beside the first, each starting with a
+// state-only pass over the chunks before it; their lengths shrink geometrically
+// (ratio 1 - kPrefixCost) so that every workgroup's prefix plus its own chunks
+// take about as long as the first segment.  Every segment reads s0 and only the
+// last writes s_final, so a state updated in place keeps one segment.
+// LINATTN_SEGMENTS=n (1..4) fixes the count where the rule allows segments.
+SegSplit seg_split(const ChunkProblem& p, int64_t nblocks, bool allow)
+{
+    const int64_t nchunks = (p.T + kC - 1) / kC;
+    SegSplit sp{};
+    sp.n = 1;
+    sp.c[0] = 0;
+    sp.c[1] = (int)nchunks;
+    if (!allow || nchunks < 2 || nblocks <= 0) return sp;
+    if (p.s0 && p.s_final) {
+        const size_t bytes = (size_t)(p.B * p.H) * p.dk * p.dv * sizeof(float);
+        const char* a0 = reinterpret_cast<const char*>(p.s0);
+        const char* a1 = reinterpret_cast<const char*>(p.s_final);
+        if (a0 < a1 + bytes && a1 < a0 + bytes) return sp;
+    }
+    int64_t n = 0;
+    if (const char* e = getenv("LINATTN_SEGMENTS")) {
+        n = atoi(e);
+        if (n < 1 || n > kMaxSeg) n = 0;
+    }
+    if (n == 0) {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+            return sp;
+        n = ncu / nblocks;
+        if (n > kMaxSeg) n = kMaxSeg;
+        if (n > nchunks / 4) n = nchunks / 4;
+    }
+    if (n > nchunks) n = nchunks;
+    if (n < 2) return sp;
+    double w[kMaxSeg], tot = 0.0, f = 1.0;
+    for (int i = 0; i < n; ++i, f *= 1.0 - kPrefixCost) tot += (w[i] = f);
+    sp.n = (int)n;
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i) {
+        acc += w[i];
+        int64_t c = i + 1 == n ? nchunks : (int64_t)(nchunks * acc / tot + 0.5);
+        if (c < sp.c[i] + 1) c = sp.c[i] + 1;
+        if (c > nchunks - (n - 1 - i)) c = nchunks - (n - 1 - i);
+        sp.c[i + 1] = (int)c;
+    }
+    return sp;
 }
 
 template <typename T, int DK, int RULE, int GATE, bool SAVE, bool NORM = false>
@@ -809,12 +1019,13 @@ hipError_t launch_t(const ChunkProblem& p, void* states, hipStream_t s, const fl
                     float* z_final = nullptr)
 {
     const int nvb = p.dv / kDVB;
-    const int64_t nblocks = p.B * p.H * nvb;
+    const SegSplit sp = seg_split(p, p.B * p.H * nvb, RULE == kRuleAdd && !SAVE);
+    const int64_t nblocks = p.B * p.H * nvb * sp.n;
     hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE, SAVE, NORM>), dim3((unsigned)nblocks), dim3(kNT),
                        0, s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),
                        static_cast<const T*>(p.v), static_cast<const T*>(p.g),
                        static_cast<const T*>(p.beta), p.s0, static_cast<T*>(p.o), p.s_final, static_cast<T*>(states),
-                       p.T, p.dv, (int)nblocks, p.prep, z0, z_final);
+                       p.T, p.dv, (int)nblocks, p.prep, z0, z_final, sp);
     return hipGetLastError();
 }
 
