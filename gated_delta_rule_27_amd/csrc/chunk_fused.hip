@@ -25,7 +25,8 @@
 //
 // Eight waves in three roles, each running its own copy of the chunk loop (so
 // the register allocation of one role does not burden another); all of them
-// meet at the same three LDS barriers per chunk:
+// meet at the same LDS barriers, three per chunk for the delta rule and two for
+// the add rule:
 //   * state waves 0..3: wave w owns value columns 16w..16w+15 and keeps
 //     S[:, those columns] (fp32) as dk/16 MFMA result tiles for the whole
 //     sequence.  S, R and Z never leave registers: a result tile is directly a
@@ -33,22 +34,30 @@
 //     LDS only supplies Q, K, K^T, V, Aq, Tb.
 //   * wave 4: the gate scan; for the delta rule the diagonal N blocks (in
 //     registers) and the triangular transform.
-//   * waves 5..7 (4..7 for the add rule): the N blocks below the diagonal, the
-//     Aq tiles and the copy of the previous chunk's output to HBM.
-// Schedule of one chunk (the next chunk's tokens are loaded into registers
-// during the whole chunk):
+//   * waves 5..7, delta rule: the N blocks below the diagonal and the copy of
+//     the previous chunk's output to HBM; waves 4..7, add rule: the Aq tiles
+//     and that copy.
+// Schedule of one chunk, delta rule (the next chunk's tokens are loaded into
+// registers during the whole chunk):
 //   P1   all: registers -> LDS; issue next chunk's loads; wave 4: gate scan
 //   ---  barrier
-//   P2a  state waves: R = V - gamma K S_r (add rule: also gamma Q S_r)
-//        wave 4: diagonal N blocks, their inverses, diagonal blocks of Tb
-//        waves 5..7: N blocks below the diagonal (to LDS), Aq tiles
+//   P2a  state waves: R = V - gamma K S_r, Aq tiles, K^T by matrix-core
+//        transposes; wave 4: diagonal N blocks, their inverses, diagonal
+//        blocks of Tb; waves 5..7: N blocks below the diagonal (to LDS)
 //   ---  barrier
-//   P2b  state waves: (delta) gamma Q S_r; K^T by matrix-core transposes
-//        wave 4: off-diagonal blocks of Tb                          [delta]
-//        waves 5..7: previous chunk's output to HBM
+//   P2b  state waves: gamma Q S_r; wave 4: off-diagonal blocks of Tb;
+//        waves 6, 7: previous chunk's output to HBM
 //   ---  barrier
 //   P4   state waves: Z = Tb R, O = gamma Q S_r + Aq Z (to LDS), S_{r+1}
 //        (the other waves go on with the next chunk's P1)
+// Add rule, two barriers:
+//   P1   all: registers -> LDS; issue next chunk's loads; wave 4: gate scan
+//   ---  barrier
+//   P2   state waves: R = V, gamma Q S_r, K^T; waves 4..7: Aq tiles
+//   ---  barrier
+//   P4   state waves: O = gamma Q S_r + Aq V (to one of two LDS buffers),
+//        S_{r+1}; waves 4..7: previous chunk's output to HBM, then the next
+//        chunk's P1
 // Operands are bf16 (fp32 for fp32 tokens), accumulation is fp32; the state
 // stays fp32 and is rounded to the operand type only as an operand.
 #include <cstdlib>
@@ -82,17 +91,8 @@ struct FusedCfg {
     static constexpr int E = 16 / sizeof(T);                 // elements per 16-byte load
     static constexpr int NQ = kC * DK / (E * kNT);           // Q/K vectors per thread
     static constexpr int NV = kC * kDVB / (E * kNT);         // V vectors per thread
-    static constexpr int NPAIR = NL * (NL + 1) / 2;          // causal 16x16 tiles
     static_assert(NQ >= 1 && NV >= 1, "load split");
 };
-
-// (lj, mi) of the p-th causal tile, mi <= lj, row-major over lj
-__device__ __forceinline__ void causal_pair(int p, int& lj, int& mi)
-{
-    lj = 0;
-    while (p > lj) { p -= lj + 1; ++lj; }
-    mi = p;
-}
 
 // Add rule: each head's chunks split into segments run by separate workgroups.
 // Segment s covers chunks [c[s], c[s+1]); n = 1 is the whole sequence.
@@ -163,7 +163,9 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     __shared__ __align__(16) T KsT[DK * LDC];
     __shared__ __align__(16) T Vs[kC * LDV];
     __shared__ __align__(16) T Aq[kC * LDC];
-    __shared__ __align__(16) T Os[kC * LDV];
+    // output of a chunk, staged for the copy to HBM; the add rule alternates two
+    // buffers (its copy runs beside the next chunk's staging)
+    __shared__ __align__(16) T Os[DELTA ? 1 : 2][kC * LDV];
     __shared__ __align__(16) T Tb[DELTA ? kC * LDC : 8];
     // the six N blocks below the diagonal as row fragments, lane by lane, and the
     // X tiles the two halves of the off-diagonal transform need from the other
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const int off = idx < NCOPY ? (int)(((tb + row) * DV + vb * kDVB + col) * (int64_t)sizeof(T))
                                         : 0x7fffffff;
             const int ro = idx < NCOPY ? row : 0;
-            i4 x = *reinterpret_cast<const i4*>(&Os[ro * LDV + col]);
+            i4 x = *reinterpret_cast<const i4*>(&Os[DELTA ? 0 : (int)(tb / kC) & 1][ro * LDV + col]);
             if constexpr (NORM) {
                 const float rd = denb[(int)(tb / kC) & 1][ro];   // 1 / den
                 float f[E];
@@ -422,12 +424,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             *reinterpret_cast<floatx4*>(&denb[rp & 1][16 * part + g4]) = d;
         }
     };
-    auto dot_tile = [&](const T* A, const T* B, int mi, int lj, int ln) {
-        Fr fa[NK], fb[NK];
-        block_frags(A, mi, ln, fa);
-        block_frags(B, lj, ln, fb);
-        return tile_dot(fa, fb);
-    };
     // a2 Aq tile (lj, mi), mi <= lj, from xa[rr] = k_m . q_l:
     // Aq[l][m] = (q_l . k_m) exp(G_l - G_m), m <= l
     auto aq_store = [&](const float* Gs, int lj, int mi, floatx4 xa, int ln) {
@@ -442,18 +438,33 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
         store_tile_t_pc(&Aq[lj * 16 * LDC], LDC, mi, va, ln);
     };
-    auto aq_tile = [&](const float* Gs, int lj, int mi, int ln) {
-        aq_store(Gs, lj, mi, dot_tile(Ks, Qs, mi, lj, ln), ln);
-    };
-    // this wave's share (iw of nw) of the ten causal Aq tiles
-    auto aq_share = [&](const float* Gs, int iw, int nw, int ln) {
+    // add rule: the ten causal Aq tiles (lj, mi) on waves 4..7, grouped by query
+    // block so each wave loads three or four blocks once:
+    // (3,0) (3,1) | (3,2) (3,3) | (2,0) (2,1) (2,2) | (0,0) (1,0) (1,1)
+    auto aq_add = [&](const float* Gs, int iw, int ln) {
+        Fr fq[NK], fk[NK];
+        if (iw < 2) {
+            block_frags(Qs, 3, ln, fq);
 #pragma unroll
-        for (int p = 0; p < Cfg::NPAIR; ++p) {
-            if (p % nw == iw) {
-                int lj, mi;
-                causal_pair(p, lj, mi);
-                aq_tile(Gs, lj, mi, ln);
+            for (int j = 0; j < 2; ++j) {
+                block_frags(Ks, 2 * iw + j, ln, fk);
+                aq_store(Gs, 3, 2 * iw + j, tile_dot(fk, fq), ln);
             }
+        } else if (iw == 2) {
+            block_frags(Qs, 2, ln, fq);
+#pragma unroll
+            for (int mi = 0; mi < 3; ++mi) {
+                block_frags(Ks, mi, ln, fk);
+                aq_store(Gs, 2, mi, tile_dot(fk, fq), ln);
+            }
+        } else {
+            block_frags(Ks, 0, ln, fk);
+            block_frags(Qs, 0, ln, fq);
+            aq_store(Gs, 0, 0, tile_dot(fk, fq), ln);
+            block_frags(Qs, 1, ln, fq);
+            aq_store(Gs, 1, 0, tile_dot(fk, fq), ln);
+            block_frags(Ks, 1, ln, fk);
+            aq_store(Gs, 1, 1, tile_dot(fk, fq), ln);
         }
     };
 
@@ -725,6 +736,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             auto ksT = [&]() { kt_share(IntC<4>{}, wave, ln); };
             if constexpr (!DELTA) {
                 ohist();
+                ksT();
             } else {
                 // a2 Aq tiles, grouped so each wave loads few blocks: wave 0 the
                 // query blocks 0-1, wave 1 block 2, waves 2-3 block 3
@@ -758,10 +770,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
             lds_barrier();
 
-            // ---- P2b: (delta) O^T history; (add) K^T through the matrix core -------
-            if constexpr (DELTA) ohist();
-            else ksT();
-            lds_barrier();
+            // ---- P2b (delta): O^T history ---------------------------------------------
+            if constexpr (DELTA) {
+                ohist();
+                lds_barrier();
+            }
 
             // ---- P4: b1 Z = Tb R ; c1 O^T += Z^T Aq^T ; S_{r+1} -----------------------
             // Products over token blocks run in pairs (blocks 0,1 and 2,3); the
@@ -792,7 +805,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             }
             // O^T tile -> Os[token][column]
 #pragma unroll
-            for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
+            for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[DELTA ? 0 : r & 1][16 * lj * LDV + n0], LDV, Ot[lj], ln);
             state_update(S, Z, gam, rho, r, ln);
         }
         if (s_final && last_seg) {
@@ -875,12 +888,14 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 tsolve_offdiag_a<T, true>(X0, Xx[0 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
                                           nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
                                           nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
+                lds_barrier();
             } else {
-                aq_share(Gs, 0, kNIW, ln);
+                // the previous chunk's output goes out while the state waves
+                // finish this chunk
+                aq_add(Gs, 0, ln);
                 lds_barrier();
                 if (r > rb) copy_out(t0 - kC, 0, ln);
             }
-            lds_barrier();
         }
     } else if (DELTA && wave == 5) {
         // ======== wave 5 (delta): a2 diagonal block 1, its inverse, N(2,1); half B
@@ -936,13 +951,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             if constexpr (DELTA) {
                 floatx4 X, Xt;
                 intra_p2a(Gs, bet, wave - 4, ln, X, Xt);
+                lds_barrier();
+                // ---- P2b ----
+                if (r > rb) copy_out(t0 - kC, iw, ln);
+                lds_barrier();
             } else {
-                aq_share(Gs, iw, kNIW, ln);
+                aq_add(Gs, iw, ln);
+                lds_barrier();
+                if (r > rb) copy_out(t0 - kC, iw, ln);
             }
-            lds_barrier();
-            // ---- P2b ----
-            if (r > rb) copy_out(t0 - kC, iw, ln);
-            lds_barrier();
         }
     }
 
