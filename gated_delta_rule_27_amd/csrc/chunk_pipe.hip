@@ -116,7 +116,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     __shared__ __align__(16) T KsT[DK * LDC];
     __shared__ __align__(16) T Vs[kC * LDV];
     __shared__ __align__(16) T Aq[2][kC * LDC];
-    __shared__ __align__(16) T Os[kC * LDV];
     __shared__ __align__(16) T Tb[DELTA ? 2 : 1][DELTA ? kC * LDC : 8];
     // the six N blocks below the diagonal as row fragments, lane by lane, and the
     // X tiles (diagonal-block inverses) the two halves of the off-diagonal
@@ -242,30 +241,13 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
         betb[sl][lane] = (DELTA && ok) ? prep_beta(to_f32(P.b), prep) : 0.f;
     };
 
-    // The output of chunk r is staged in LDS (Os) by the state waves and written
-    // to HBM by waves 4..7 during the next step.  The stores go through a buffer
-    // resource over this head's rows: rows past the end, the spare lanes of the
-    // last round and the steps with no output yet fall outside it and the
-    // hardware drops them, so no branch hides a store from the compiler's wait
-    // counts (loads and stores share one vector-memory counter).
+    // The state waves store their output tiles straight to HBM, through a buffer
+    // resource over this head's rows: rows past the end (and, on the virtual
+    // sequence, the substeps that are not a token's last) fall outside it and
+    // the hardware drops them.  The state waves issue no global loads inside
+    // the loop, so the stores never enter a wait count there.
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         o + bh * Treal * DV, (short)0, (int)(Treal * DV * (int64_t)sizeof(T)), 0x00020000);
-    auto copy_out = [&](int64_t tb, bool valid, int cw, int ln) {
-        constexpr int NCW = 4, NCOPY = kC * kDVB / E, NROUND = NCOPY / (NCW * kWave);
-#pragma unroll
-        for (int p = 0; p < NROUND; ++p) {
-            const int idx = (p * NCW + cw) * kWave + ln;
-            const int row = idx / (kDVB / E), col = (idx % (kDVB / E)) * E;
-            // virtual sequence: a token's last substep goes to its real row, the
-            // other substeps are dropped like rows past the end
-            const int64_t vr = tb + row;
-            const bool keep = valid && (!VIRT || (int)vr % nh == nh - 1);
-            const int off = keep ? (int)(((VIRT ? (int64_t)((int)vr / nh) : vr) * DV + vb * kDVB + col) * (int64_t)sizeof(T))
-                                 : 0x7fffffff;
-            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i4*>(&Os[row * LDV + col]), orsrc, off,
-                                                   0, 0);
-        }
-    };
 
     // ---- matrix-core helpers over LDS tiles
     // All fragments (every k step) of the 16-row block b of a [C][DK] tile (Qs or
@@ -549,9 +531,23 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                     if (lj >= 2) Ot[lj] = mma_pair<T>(z23, pair_lds_sw(&Aqc[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
                 }
             }
-            // O^T tile -> Os[token][column]
+            // O^T tiles to HBM: lane (cl, g4) holds token 16 lj + cl of the chunk and
+            // value columns n0 + g4 .. n0 + g4 + 3, one 8-byte store
 #pragma unroll
-            for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
+            for (int lj = 0; lj < NL; ++lj) {
+                const int64_t vr = r * kC + 16 * lj + cl;
+                const bool keep = !VIRT || (int)vr % nh == nh - 1;
+                const int off = keep ? (int)(((VIRT ? (int64_t)((int)vr / nh) : vr) * DV + vb * kDVB + n0 + g4) *
+                                             (int64_t)sizeof(T))
+                                     : 0x7fffffff;
+                typedef __attribute__((__vector_size__(8))) int i2;
+                T e[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) e[rr] = from_f32<T>(Ot[lj][rr]);
+                i2 x;
+                __builtin_memcpy(&x, e, 8);
+                __builtin_amdgcn_raw_buffer_store_b64(x, orsrc, off, 0, 0);
+            }
             // S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z
             const float gC = gam[kC - 1];
             floatx4 zr[NL];
@@ -634,7 +630,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             T* const Tbn = Tb[c & 1];
             // ---- phase 1: diagonal block iw, its inverse, lower N blocks
             if (go) intra_p1(Ks[c & 1], Gs, bet, Tbn, iw, ln);
-            copy_out((r - 1) * kC, r >= 1, iw, ln);
             lds_barrier();
         } else {
             // ---- phase 1: this wave's share of chunk c's Aq tiles
@@ -654,7 +649,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
                     }
                 }
             }
-            copy_out((r - 1) * kC, r >= 1, iw, ln);
             lds_barrier();
         }
         stage_and_fetch(P, r);
@@ -665,8 +659,6 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
         step(r, P1);
         step(r + 1, P0);
     }
-    // the last chunk's output (staged by the state waves before the last barrier)
-    copy_out(tlast, true, wave - 4, lane);
 }
 
 template <int DK, int RULE, int GATE, bool VIRT, int NHC = 0>
