@@ -60,12 +60,11 @@
 //        chunk's P1
 // Operands are bf16 (fp32 for fp32 tokens), accumulation is fp32; the state
 // stays fp32 and is rounded to the operand type only as an operand.
-#include <cstdlib>
-
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
 #include "prep.h"
+#include "segments.h"
 #include "tsolve.h"
 
 namespace linattn {
@@ -92,19 +91,6 @@ struct FusedCfg {
     static constexpr int NQ = kC * DK / (E * kNT);           // Q/K vectors per thread
     static constexpr int NV = kC * kDVB / (E * kNT);         // V vectors per thread
     static_assert(NQ >= 1 && NV >= 1, "load split");
-};
-
-// Add rule: each head's chunks split into segments run by separate workgroups.
-// Segment s covers chunks [c[s], c[s+1]); n = 1 is the whole sequence.
-constexpr int kMaxSeg = 4;
-struct SegSplit {
-    int n;
-    int c[kMaxSeg + 1];
-};
-
-template <int N>
-struct IntC {
-    static constexpr int value = N;
 };
 
 // the E = 16 / sizeof(T) elements of a 16-byte vector, as floats and back
@@ -980,63 +966,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 // cycles; a sweep of the split at B4 H16 T4096 has its minimum near 0.45).
 constexpr double kPrefixCost = 0.45;
 
-// Segments per (head, value block) for the add rule.  When the plain grid leaves
-// compute units idle, later segments run beside the first, each starting with a
-// state-only pass over the chunks before it; their lengths shrink geometrically
-// (ratio 1 - kPrefixCost) so that every workgroup's prefix plus its own chunks
-// take about as long as the first segment.  Every segment reads s0 and only the
-// last writes s_final, so a state updated in place keeps one segment.
-// LINATTN_SEGMENTS=n (1..4) fixes the count where the rule allows segments.
-SegSplit seg_split(const ChunkProblem& p, int64_t nblocks, bool allow)
-{
-    const int64_t nchunks = (p.T + kC - 1) / kC;
-    SegSplit sp{};
-    sp.n = 1;
-    sp.c[0] = 0;
-    sp.c[1] = (int)nchunks;
-    if (!allow || nchunks < 2 || nblocks <= 0) return sp;
-    if (p.s0 && p.s_final) {
-        const size_t bytes = (size_t)(p.B * p.H) * p.dk * p.dv * sizeof(float);
-        const char* a0 = reinterpret_cast<const char*>(p.s0);
-        const char* a1 = reinterpret_cast<const char*>(p.s_final);
-        if (a0 < a1 + bytes && a1 < a0 + bytes) return sp;
-    }
-    int64_t n = 0;
-    if (const char* e = getenv("LINATTN_SEGMENTS")) {
-        n = atoi(e);
-        if (n < 1 || n > kMaxSeg) n = 0;
-    }
-    if (n == 0) {
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-            return sp;
-        n = ncu / nblocks;
-        if (n > kMaxSeg) n = kMaxSeg;
-        if (n > nchunks / 4) n = nchunks / 4;
-    }
-    if (n > nchunks) n = nchunks;
-    if (n < 2) return sp;
-    double w[kMaxSeg], tot = 0.0, f = 1.0;
-    for (int i = 0; i < n; ++i, f *= 1.0 - kPrefixCost) tot += (w[i] = f);
-    sp.n = (int)n;
-    double acc = 0.0;
-    for (int i = 0; i < n; ++i) {
-        acc += w[i];
-        int64_t c = i + 1 == n ? nchunks : (int64_t)(nchunks * acc / tot + 0.5);
-        if (c < sp.c[i] + 1) c = sp.c[i] + 1;
-        if (c > nchunks - (n - 1 - i)) c = nchunks - (n - 1 - i);
-        sp.c[i + 1] = (int)c;
-    }
-    return sp;
-}
-
 template <typename T, int DK, int RULE, int GATE, bool SAVE, bool NORM = false>
 hipError_t launch_t(const ChunkProblem& p, void* states, hipStream_t s, const float* z0 = nullptr,
                     float* z_final = nullptr)
 {
     const int nvb = p.dv / kDVB;
-    const SegSplit sp = seg_split(p, p.B * p.H * nvb, RULE == kRuleAdd && !SAVE);
+    // add rule: segments of a head's chunks when the grid leaves compute units idle
+    // (segments.h); the state-keeping forward keeps one
+    const SegSplit sp = seg_split((p.T + kC - 1) / kC, p.B * p.H * nvb, RULE == kRuleAdd && !SAVE, p.s0,
+                                  p.s_final, (size_t)(p.B * p.H) * p.dk * p.dv * sizeof(float), kPrefixCost);
     const int64_t nblocks = p.B * p.H * nvb * sp.n;
     hipLaunchKernelGGL((chunk_fused_kernel<T, DK, RULE, GATE, SAVE, NORM>), dim3((unsigned)nblocks), dim3(kNT),
                        0, s, static_cast<const T*>(p.q), static_cast<const T*>(p.k),

@@ -31,6 +31,7 @@
 #include "launch.h"
 #include "mfma.h"
 #include "prep.h"
+#include "segments.h"
 #include "tsolve.h"
 #include "tile_rows.h"
 
@@ -418,11 +419,16 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 // With SAVE the state waves also write S_r, the state entering chunk r, to an
 // LDS tile at the top of every chunk, and the helper waves copy it to
 // states[b, h, r] ([dk][dv], bf16) during phase 2 with 16-byte stores.
+//
+// Segments (segments.h, not with SAVE): a workgroup may own chunks [rb, re) of
+// its head; it first runs the state update alone over chunks [0, rb) (phase 1
+// without O, phase 2 without O; the helpers stage neither Qd nor Aq), then its
+// own chunks as usual.
 template <int DK, int RULE, int DVB, bool SAVE>
 __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const bf16* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0,
     bf16* __restrict__ o, float* s_final, bf16* __restrict__ states, int64_t Tlen, int64_t nchunks, int DV,
-    int nblocks)
+    int nblocks, SegSplit seg)
 {
     using W = SplitWs<DK>;
     constexpr int NSW = DVB / 16;                // state waves, 16 value columns each
@@ -451,8 +457,12 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const int nvb = DV / DVB;
     int blk = blockIdx.x;
     if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
-    const int64_t bh = blk / nvb;
-    const int vb = blk % nvb;
+    const int nunit = nvb * seg.n;
+    const int64_t bh = blk / nunit;
+    const int vb = (blk % nunit) % nvb;
+    const int sg = (blk % nunit) / nvb;
+    const int64_t rb = SAVE ? 0 : seg.c[sg], re = SAVE ? nchunks : seg.c[sg + 1];
+    const bool last_seg = SAVE || sg == seg.n - 1;
 
     if (wave < NSW) {
         // ======== state waves ============================================================
@@ -467,8 +477,57 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                     S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + vb * DVB + n0 + cl] : 0.f;
         }
         wait_vmem_all();
-        __syncthreads();                          // group 1 of chunk 0 staged
-        for (int64_t c = 0; c < nchunks; ++c) {
+        __syncthreads();                          // group 1 of the first chunk staged
+        if constexpr (!SAVE) {
+            // prefix pass: S_{r+1} = Diag(gC) S_r + Kr^T Tb (V - Kd S_r) over chunks [0, rb)
+            for (int64_t c = 0; c < rb; ++c) {
+                const int ln = opaque(lane);
+                const int cl = ln & 15, g4 = 4 * (ln >> 4);
+                floatx4 R[NL], Z[NL];
+#pragma unroll
+                for (int li = 0; li < NL; ++li)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) R[li][rr] = to_f32(Vs[(16 * li + g4 + rr) * LDV + n0 + cl]);
+                if constexpr (DELTA) {
+                    floatx4 P[NL];
+#pragma unroll
+                    for (int li = 0; li < NL; ++li) P[li] = zero4();
+#pragma unroll
+                    for (int db = 0; db < ND; db += 2) {
+                        const auto sp = pair_regs<bf16>(S[db], S[db + 1]);
+#pragma unroll
+                        for (int li = 0; li < NL; ++li)
+                            P[li] = mma_pair<bf16>(pair_lds(&Kd[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
+                    }
+#pragma unroll
+                    for (int li = 0; li < NL; ++li)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) R[li][rr] -= P[li][rr];
+                    const auto r01 = pair_regs<bf16>(R[0], R[1]), r23 = pair_regs<bf16>(R[2], R[3]);
+#pragma unroll
+                    for (int li = 0; li < NL; ++li) {
+                        Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
+                        if (li >= 2) Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                    }
+                } else {
+#pragma unroll
+                    for (int li = 0; li < NL; ++li) Z[li] = R[li];
+                }
+                lds_barrier();
+                const auto z01 = pair_regs<bf16>(Z[0], Z[1]), z23 = pair_regs<bf16>(Z[2], Z[3]);
+#pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    const floatx4 gd = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gd[rr];
+                    S[db] = mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC + 32], LDC, ln), z23,
+                                           mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC], LDC, ln), z01, S[db]));
+                }
+                lds_barrier();
+            }
+            if (rb > 0) __syncthreads();          // group 1 of chunk rb staged
+        }
+        for (int64_t c = rb; c < re; ++c) {
             const int ln = opaque(lane);
             const int cl = ln & 15, g4 = 4 * (ln >> 4);
             if constexpr (SAVE) {
@@ -537,7 +596,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             }
             lds_barrier();
         }
-        if (s_final) {
+        if (s_final && last_seg) {
             const int cl = lane & 15, g4 = 4 * (lane >> 4);
 #pragma unroll
             for (int db = 0; db < ND; ++db)
@@ -552,12 +611,15 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
         // group 1: Kd, Qd, V, Tb ; group 2: Aq, Kr^T, gC
         i4 rkd[VQ], rqd[VQ], rv[VV], rtb[VA];
         i4 raq[VA], rkr[VK], rg = {0, 0, 0, 0};
-        auto load1 = [&](int64_t c) {
+        // the loads and staging of the two groups; with full = IntC<false> (prefix
+        // pass) without Qd and Aq
+        auto load1 = [&](int64_t c, auto full) {
+            constexpr bool FULL = decltype(full)::value;
             const unsigned char* wc = ws + (bh * nchunks + c) * W::BYTES;
 #pragma unroll
             for (int p = 0; p < VQ; ++p) {
                 const int e = (p * NH + ht) * 8;
-                rqd[p] = *reinterpret_cast<const i4*>(wc + W::QD + 2 * e);
+                if constexpr (FULL) rqd[p] = *reinterpret_cast<const i4*>(wc + W::QD + 2 * e);
                 if constexpr (DELTA) rkd[p] = *reinterpret_cast<const i4*>(wc + W::KD + 2 * e);
             }
 #pragma unroll
@@ -573,12 +635,13 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                 rv[p] = *reinterpret_cast<const i4*>(v + (bh * Tlen + tr) * DV + vb * DVB + col);
             }
         };
-        auto stage1 = [&](int64_t c) {
+        auto stage1 = [&](int64_t c, auto full) {
+            constexpr bool FULL = decltype(full)::value;
 #pragma unroll
             for (int p = 0; p < VQ; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / DK, col = e % DK;
-                *reinterpret_cast<i4*>(&Qd[row * LDQ + col]) = rqd[p];
+                if constexpr (FULL) *reinterpret_cast<i4*>(&Qd[row * LDQ + col]) = rqd[p];
                 if constexpr (DELTA) *reinterpret_cast<i4*>(&Kd[row * LDQ + col]) = rkd[p];
             }
 #pragma unroll
@@ -595,12 +658,13 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                 *reinterpret_cast<i4*>(&Vs[row * LDV + col]) = (c * kC + row < Tlen) ? rv[p] : z;
             }
         };
-        auto load2 = [&](int64_t c) {
+        auto load2 = [&](int64_t c, auto full) {
+            constexpr bool FULL = decltype(full)::value;
             const unsigned char* wc = ws + (bh * nchunks + c) * W::BYTES;
 #pragma unroll
             for (int p = 0; p < VA; ++p) {
                 const int e = (p * NH + ht) * 8;
-                raq[p] = *reinterpret_cast<const i4*>(wc + W::AQ + 2 * e);
+                if constexpr (FULL) raq[p] = *reinterpret_cast<const i4*>(wc + W::AQ + 2 * e);
             }
 #pragma unroll
             for (int p = 0; p < VK; ++p) {
@@ -609,12 +673,13 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             }
             if (ht < DK / 4) rg = *reinterpret_cast<const i4*>(wc + W::GC + 16 * ht);
         };
-        auto stage2 = [&]() {
+        auto stage2 = [&](auto full) {
+            constexpr bool FULL = decltype(full)::value;
 #pragma unroll
             for (int p = 0; p < VA; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / kC, col = e % kC;
-                *reinterpret_cast<i4*>(&Aq[row * LDC + col]) = raq[p];
+                if constexpr (FULL) *reinterpret_cast<i4*>(&Aq[row * LDC + col]) = raq[p];
             }
 #pragma unroll
             for (int p = 0; p < VK; ++p) {
@@ -655,30 +720,60 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                     *reinterpret_cast<const i4*>(&Sst[row * LDV + col]);
             }
         };
-        const int64_t last = nchunks - 1;
-        if (nchunks > 0) {
-            load1(0);
-            load2(0);
-            stage1(0);
-            load1(1 < last ? 1 : last);
+        constexpr IntC<true> kFull{};
+        constexpr IntC<false> kPrefix{};
+        const int64_t last = re - 1, plast = rb - 1;
+        if (rb > 0) {
+            load1(0, kPrefix);
+            load2(0, kPrefix);
+            stage1(0, kPrefix);
+            load1(1 < plast ? 1 : plast, kPrefix);
+        } else if (re > rb) {
+            load1(rb, kFull);
+            load2(rb, kFull);
+            stage1(rb, kFull);
+            load1(rb + 1 < last ? rb + 1 : last, kFull);
         }
-        __syncthreads();                          // group 1 of chunk 0 staged
-        for (int64_t c = 0; c < nchunks; ++c) {
+        __syncthreads();                          // group 1 of the first chunk staged
+        if constexpr (!SAVE) {
+            for (int64_t c = 0; c < rb; ++c) {
+                stage2(kPrefix);
+                load2(c + 1 < plast ? c + 1 : plast, kPrefix);
+                lds_barrier();
+                if (c + 1 < rb) stage1(c + 1, kPrefix);
+                load1(c + 2 < plast ? c + 2 : plast, kPrefix);
+                lds_barrier();
+            }
+            if (rb > 0) {
+                load1(rb, kFull);
+                load2(rb, kFull);
+                stage1(rb, kFull);
+                load1(rb + 1 < last ? rb + 1 : last, kFull);
+                __syncthreads();                  // group 1 of chunk rb staged
+            }
+        }
+        for (int64_t c = rb; c < re; ++c) {
             // ---- phase 1 ----
-            stage2();
-            load2(c + 1 < last ? c + 1 : last);
-            if (c > 0) copy_out(c - 1);
+            stage2(kFull);
+            load2(c + 1 < last ? c + 1 : last, kFull);
+            if (c > rb) copy_out(c - 1);
             lds_barrier();
             // ---- phase 2 ----
-            if (c + 1 < nchunks) stage1(c + 1);
-            load1(c + 2 < last ? c + 2 : last);
+            if (c + 1 < re) stage1(c + 1, kFull);
+            load1(c + 2 < last ? c + 2 : last, kFull);
             if constexpr (SAVE) copy_state(c);
             lds_barrier();
         }
         __syncthreads();                          // the last output is in Os
-        if (nchunks > 0) copy_out(nchunks - 1);
+        if (re > rb) copy_out(re - 1);
     }
 }
+
+// A prefix chunk of the state pass (no Qd, Aq, output) costs about this
+// fraction of a full chunk: it moves 65 % of the bytes, and the pass is bound
+// by the memory system rather than by its own latency (KDA B1 H32 T262144,
+// two segments: 0.5, 0.65, 0.8 gave 9.24, 9.23, 9.20 ms per forward).
+constexpr double kChainPrefixCost = 0.8;
 
 template <int DK, int RULE, int GATE>
 hipError_t launch_split(const ChunkProblem& p, bf16* states, hipStream_t s)
@@ -711,23 +806,28 @@ hipError_t launch_split(const ChunkProblem& p, bf16* states, hipStream_t s)
     // (fewer 64-column blocks than CUs) the blocks are 32 columns wide, which
     // doubles the number of independent chains; each staged tile is then read
     // by twice as many workgroups (mostly from L2).
+    // Without saved states, a grid that still leaves CUs idle splits each
+    // head's chunks into segments (segments.h).
     const bool narrow = bh * (p.dv / 64) < ncu;
-    const int nblocks = (int)(bh * (p.dv / (narrow ? 32 : 64)));
+    const int64_t nblocks1 = bh * (p.dv / (narrow ? 32 : 64));
+    const SegSplit sp = seg_split(nchunks, nblocks1, states == nullptr, p.s0, p.s_final,
+                                  (size_t)bh * p.dk * p.dv * sizeof(float), kChainPrefixCost);
+    const int nblocks = (int)(nblocks1 * sp.n);
     const dim3 grid((unsigned)nblocks);
     const bf16* v = static_cast<const bf16*>(p.v);
     bf16* o = static_cast<bf16*>(p.o);
     if (narrow && states)
         hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 32, true>), grid, dim3(6 * 64), 0, s, v, ws, p.s0, o,
-                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks, sp);
     else if (narrow)
         hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 32, false>), grid, dim3(6 * 64), 0, s, v, ws, p.s0, o,
-                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks, sp);
     else if (states)
         hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 64, true>), grid, dim3(8 * 64), 0, s, v, ws, p.s0, o,
-                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks, sp);
     else
         hipLaunchKernelGGL((chunk_chain_kernel<DK, RULE, 64, false>), grid, dim3(8 * 64), 0, s, v, ws, p.s0, o,
-                           p.s_final, states, p.T, nchunks, p.dv, nblocks);
+                           p.s_final, states, p.T, nchunks, p.dv, nblocks, sp);
     return hipGetLastError();
 }
 

@@ -1,5 +1,10 @@
-"""Parity of the add rule's segmented chunk forward with the fp64 oracle and
-with the unsegmented run.
+"""Parity of the segmented chunk forwards (the add rule's single-pass kernel
+and the two-kernel path's state pass) with the fp64 oracle and with the
+unsegmented run.
+
+The two-kernel path's state pass (per-channel gate, or any gate on request)
+splits the same way for every rule: its prefix pass runs the main loop's state
+update, S <- Diag(gamma_C) S + Kr^T Tb (V - Kd S), without the output.
 
 For the add rule (no gate or a scalar gate) the chunk transition is a scalar
 times the identity ("Linear Attention, Visualized", "Chunkwise algorithm":
@@ -153,3 +158,84 @@ def test_segments_raw_projections(monkeypatch):
     eo, es = rel_l2(host(o), oref), rel_l2(host(s), sref)
     note(f"[segments prep] rel L2 o={eo:.3e} S={es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# ---- the two-kernel path's state pass (per-channel gate; any gate on request) ----
+
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("rule", ["add", "delta"])
+def test_chain_segments_channel_gate(monkeypatch, rule, dk):
+    # one batch of two heads at d_v = 128: the state pass runs 32-column blocks,
+    # 16 workgroups, and splits every head into four segments
+    case = syn.Case("segchan", 1, 2, 1500, dk, 128, rule, "channel", "bf16", gate_scale=1 / 16, s0_std=0.3,
+                    case_id=168)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
+    o, s = run_chunk(case, x, x["s0"])
+    oref, _ = oracle_chunk(case, x, x["s0"])
+    wb = worst_block_all(case, o, oref)
+    note(f"    worst 64-token block {wb:.3e}")
+    assert wb <= TOL["bf16"]
+    monkeypatch.setenv("LINATTN_SEGMENTS", "1")
+    o1, s1 = run_chunk(case, x, x["s0"])
+    assert torch.equal(o, o1) and torch.equal(s, s1)
+
+
+@pytest.mark.parametrize("nseg", [2, 3])
+@pytest.mark.parametrize("gate", ["none", "scalar"])
+def test_chain_segments_split_path(monkeypatch, gate, nseg):
+    monkeypatch.setenv("LINATTN_CHUNK_PATH", "split")
+    case = syn.Case("segsplit", 2, 1, 1300, 128, 128, "delta", gate, "bf16", gate_scale=1 / 16, s0_std=0.3,
+                    case_id=169)
+    x = syn.chunk_inputs(case)
+    monkeypatch.setenv("LINATTN_SEGMENTS", str(nseg))
+    check_chunk(case, x, s0=x["s0"])
+    on, sn = run_chunk(case, x, x["s0"])
+    monkeypatch.setenv("LINATTN_SEGMENTS", "1")
+    o1, s1 = run_chunk(case, x, x["s0"])
+    assert torch.equal(on, o1) and torch.equal(sn, s1)
+
+
+def test_chain_segments_short(monkeypatch):
+    # forced segments of one or two chunks, a ragged last chunk
+    monkeypatch.setenv("LINATTN_SEGMENTS", "4")
+    case = syn.Case("segchshort", 1, 3, 250, 128, 128, "delta", "channel", "bf16", gate_scale=0.25, s0_std=0.3,
+                    case_id=170)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
+
+
+def test_chain_segments_raw_projections(monkeypatch):
+    # KDA from raw projections: L2 q/k, -softplus per key channel, sigmoid beta
+    import gated_delta_rule_27_amd as la
+    monkeypatch.setenv("LINATTN_SEGMENTS", "3")
+    case = syn.Case("segchprep", 1, 2, 1100, 128, 128, "delta", "channel", "bf16", gate_scale=1.0, s0_std=0.3,
+                    case_id=171)
+    x = syn.raw_inputs(case)
+    d = lambda a: dev(a, case.dtype)
+    o, s = la.chunk_fwd(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]), dev_state(x["s0"]),
+                        rule="delta", gate="channel", qk_map="l2", gate_map="neg_softplus", beta_map="sigmoid")
+    torch.cuda.synchronize()
+    q, k = oracle.prepare_qk(x["q"], "l2"), oracle.prepare_qk(x["k"], "l2")
+    g = oracle.prepare_gate(x["g"], "neg_softplus")
+    b = oracle.prepare_beta(x["beta"], "sigmoid")
+    oref, sref = oracle.recurrence(q, k, x["v"], g, b, x["s0"], rule="delta", gate="channel")
+    eo, es = rel_l2(host(o), oref), rel_l2(host(s), sref)
+    note(f"[chain segments prep] rel L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_chain_segments_state_in_place():
+    import gated_delta_rule_27_amd as la
+    case = syn.Case("segchinplace", 1, 2, 1200, 128, 128, "delta", "channel", "bf16", gate_scale=1 / 16,
+                    s0_std=0.3, case_id=172)
+    x = syn.chunk_inputs(case)
+    d = lambda a: dev(a, case.dtype)
+    o_ref, s_ref = la.chunk_fwd(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]), dev_state(x["s0"]),
+                                rule="delta", gate="channel")
+    s_io = dev_state(x["s0"])
+    o, s = la.chunk_fwd(d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]), s_io, rule="delta",
+                        gate="channel", s_final=s_io)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == s_io.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
