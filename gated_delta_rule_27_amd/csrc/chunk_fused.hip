@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     // the next loads; K^T on all eight waves, the state waves also take their V
     // columns into registers; then the state waves update S while the others
     // stage the next chunk.  Two barriers per chunk; the other waves' part:
-    auto prefix_other = [&](int64_t r, int ln) {
+    auto prefix_other = [&](int ln) {
         lds_barrier();
         kt_share(IntC<kNW>{}, wave, ln);
         lds_barrier();
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 prefix_stage(r, kr, vr);
                 gate_scan(r, gv);
                 load_gate(r + 2, gv);
-                prefix_other(r, ln);
+                prefix_other(ln);
             };
             if (rb > 0) {
                 load_gate(0, ga);
@@ -915,10 +915,10 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         if constexpr (!DELTA) {
             for (int64_t r = 0; r < rb; r += 2) {
                 prefix_stage(r, kreg, vreg);
-                prefix_other(r, opaque(lane));
+                prefix_other(opaque(lane));
                 if (r + 1 < rb) {
                     prefix_stage(r + 1, qreg, vreg2);
-                    prefix_other(r + 1, opaque(lane));
+                    prefix_other(opaque(lane));
                 }
             }
             if (rb > 0) fetch(rb * kC);
