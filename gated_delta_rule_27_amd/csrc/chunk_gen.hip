@@ -33,15 +33,14 @@
 //           operands of the token type: T rounded once, like every operand)
 //       and the operands of the state pass: <-Q = 2^G . Q, ->K^T with
 //       ->k_l = 2^(G_{C-1} - G_l) . k_l, and 2^(G_{C-1})
-//   gen_chain_kernel   one workgroup per (b, h, 64 value columns), 4 waves of
-//     16 columns each, S (fp32) in matrix-core result registers; per chunk and
+//   gen_chain_kernel   one workgroup per (b, h, 64 value columns): 4 state
+//     waves of 16 columns each, S (fp32) in matrix-core result registers, and
+//     4 helper waves staging each 16-row block's operands in LDS; per chunk and
 //     per 16-row block li of the chunk:
 //       b1  Z_li = U_li - W_li S_r   (add rule: Z = V)
 //       c1  O_li = <-Q_li S_r + sum_{mj <= li} Aq(li, mj) Z_mj
 //           dS  += ->K_li^T Z_li
-//     then S_{r+1} = Diag(2^(G_{C-1})) S_r + dS.  Operands are read as
-//     matrix-core fragments straight from the workspace (L2-resident), each
-//     16-row block's while the block before it is computed.
+//     then S_{r+1} = Diag(2^(G_{C-1})) S_r + dS.
 //
 // Rows past the end of the sequence are staged as zeros (k = v = 0, g = 0,
 // beta = 0), which leaves the state unchanged; their outputs are not written.
@@ -84,14 +83,6 @@ __device__ __forceinline__ floatx4 load4(const bf16* p)
 {
     const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
     return floatx4{to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
-}
-
-// K = 16 fragment of a row-major block in global memory (lane: row l % 16,
-// columns 4 (l / 16) .. +3), as frag16_lds reads one from LDS
-template <typename T>
-__device__ __forceinline__ typename Frag16<T>::type frag16_g(const T* M, int ld, int lane)
-{
-    return *reinterpret_cast<const typename Frag16<T>::type*>(M + (lane & 15) * ld + 4 * (lane >> 4));
 }
 
 // (i, j) of the p-th causal 16 x 16 tile, j <= i, row-major over i
@@ -409,26 +400,55 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
 // ===========================================================================
 // State pass + output
 // ===========================================================================
-// Operands of one 16-row block of a chunk as this wave uses them: fragments of
-// W, <-Q and ->K^T, the causal Aq fragments of the block's row, and U (the
-// values for the add rule) at the wave's columns.  Each block's operands are
-// fetched while the previous block is computed (the next chunk's first block
-// during the last one), so the loads are off the state recurrence.
-template <typename T, int ND, int NB, bool DELTA>
-struct GenBlk {
-    typename Frag16<T>::type w[DELTA ? ND : 1], q[ND], kr[ND], a[NB];
-    floatx4 u;
+// One workgroup per (b, h, 64 value columns), 8 waves.  Waves 0..3 each own 16
+// value columns of S (fp32 result tiles, for the whole sequence); waves 4..7
+// copy each 16-row block's operands from the workspace into LDS: W and <-Q
+// rows, the block's 16 columns of ->K^T, the block's row of Aq, U (the values
+// for the add rule) at the workgroup's columns, and 2^(G_{C-1}) of its chunk.
+// A block's operands are loaded into registers three blocks ahead (three
+// register sets, so a load has two blocks' time to arrive) and written into
+// one of two LDS buffers while the state waves compute from the other; one
+// barrier per block.  Every load is issued unconditionally (indices clamped),
+// and the helpers run a multiple of three blocks (spare ones copy nothing), so
+// the compiler's wait counts stay exact.
+template <typename T, int C, int DK>
+struct GenStage {
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte vector
+    static constexpr int LDK = DK + PAD;            // W, <-Q rows: [16][DK]
+    static constexpr int LDT = 16 + PAD;            // ->K^T block: [DK][16]
+    static constexpr int LDA = C + PAD;             // Aq row block: [16][C]
+    static constexpr int LDU = 64 + PAD;            // U / V: [16][64]
+    static constexpr int W = 0, Q = W + 16 * LDK, KR = Q + 16 * LDK, A = KR + DK * LDT, U = A + 16 * LDA;
+    static constexpr int ELEMS = U + 16 * LDU;
+    // 16-byte vectors of each piece, and per helper thread (256 threads)
+    static constexpr int VW = 16 * DK / E, VKR = DK * 16 / E, VA = 16 * C / E, VU = 16 * 64 / E, VG = DK / 4;
+    static constexpr int NW = (VW + 255) / 256, NKR = (VKR + 255) / 256, NA = (VA + 255) / 256,
+                         NU = (VU + 255) / 256;
+};
+
+template <typename T, int C, int DK>
+struct GenRegs {
+    using G = GenStage<T, C, DK>;
+    typedef __attribute__((__vector_size__(16))) int i4;
+    i4 w[G::NW], q[G::NW], kr[G::NKR], a[G::NA], u[G::NU], g;
 };
 
 template <typename T, int C, int DK, int RULE>
-__global__ __launch_bounds__(256) void gen_chain_kernel(
+__global__ __launch_bounds__(512, 1) void gen_chain_kernel(
     const T* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0, T* __restrict__ o,
     float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks)
 {
     using F = typename Frag16<T>::type;
-    constexpr int NB = C / 16, ND = DK / 16;
+    using G = GenStage<T, C, DK>;
+    using Regs = GenRegs<T, C, DK>;
+    typedef __attribute__((__vector_size__(16))) int i4;
+    constexpr int NB = C / 16, ND = DK / 16, E = G::E;
     constexpr bool DELTA = RULE == kRuleDelta;
-    using Blk = GenBlk<T, ND, NB, DELTA>;
+
+    __shared__ __align__(16) T stage[2][G::ELEMS];
+    __shared__ __align__(16) float gcs[2][DK];
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvb = DV / 64;
@@ -436,107 +456,194 @@ __global__ __launch_bounds__(256) void gen_chain_kernel(
     int blk = blockIdx.x;
     if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
     const int64_t bh = blk / nvb;
-    const int n0 = (blk % nvb) * 64 + 16 * wave;
-    const int cl = lane & 15, g4 = 4 * (lane >> 4);
+    const int vb = blk % nvb;
     const GenWs L = gen_ws(C, DK, DV, (int)sizeof(T), DELTA);
+    const int64_t nsteps = nchunks * NB;           // 16-row blocks
+    const int64_t nspad = (nsteps + 2) / 3 * 3;     // the helpers' count, a multiple of 3
 
-    // operands of block li of chunk c (rows past the end of the sequence read
-    // the last row for the add rule's values; they are zeroed where used)
-    auto fetch = [&](Blk& b, int64_t c, int li) {
-        const unsigned char* wc = ws + (bh * nchunks + c) * L.bytes;
-        const T* const Qd = reinterpret_cast<const T*>(wc + L.qd);
-        const T* const KrT = reinterpret_cast<const T*>(wc + L.krt);
-        const T* const Aq = reinterpret_cast<const T*>(wc + L.aq);
+    if (wave < 4) {
+        // ======== state waves: columns n0..n0+15 of the block ==========================
+        const int n0 = vb * 64 + 16 * wave;
+        const int cl = lane & 15, g4 = 4 * (lane >> 4);
+        floatx4 S[ND];
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            if constexpr (DELTA)
-                b.w[db] = frag16_g(reinterpret_cast<const T*>(wc + L.w) + 16 * li * DK + 16 * db, DK, lane);
-            b.q[db] = frag16_g(Qd + 16 * li * DK + 16 * db, DK, lane);
-            b.kr[db] = frag16_g(KrT + 16 * db * C + 16 * li, C, lane);
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
+        lds_barrier();                               // block 0 staged
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int64_t t0 = c * C;
+            F Sf[ND];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) Sf[db] = frag16_acc<T>(S[db]);
+            floatx4 dS[ND];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) dS[db] = zero4();
+            F Zf[NB];
+#pragma unroll
+            for (int li = 0; li < NB; ++li) {
+                const int ln = opaque(lane);
+                const int b = (int)((c * NB + li) & 1);
+                const T* const st = stage[b];
+                // b1: Z = U - W S_r (delta) | V (add; rows past the end staged as zeros)
+                floatx4 Z;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Z[rr] = to_f32(st[G::U + (g4 + rr) * G::LDU + 16 * wave + cl]);
+                if constexpr (DELTA) {
+                    floatx4 P = zero4();
+#pragma unroll
+                    for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_lds(st + G::W + 16 * db, G::LDK, ln), Sf[db], P);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
+                }
+                Zf[li] = frag16_acc<T>(Z);
+                // c1: O = <-Q S_r + sum_{mj <= li} Aq(li, mj) Z_mj
+                floatx4 O = zero4();
+#pragma unroll
+                for (int db = 0; db < ND; ++db) O = mma16<T>(frag16_lds(st + G::Q + 16 * db, G::LDK, ln), Sf[db], O);
+#pragma unroll
+                for (int mj = 0; mj <= li; ++mj) O = mma16<T>(frag16_lds(st + G::A + 16 * mj, G::LDA, ln), Zf[mj], O);
+                // ->K_li^T Z_li
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+                    dS[db] = mma16<T>(frag16_lds(st + G::KR + 16 * db * G::LDT, G::LDT, ln), Zf[li], dS[db]);
+                if (li == NB - 1) {
+                    // S_{r+1} = Diag(2^(G_{C-1})) S_r + ->K^T Z
+#pragma unroll
+                    for (int db = 0; db < ND; ++db) {
+                        const floatx4 gd = *reinterpret_cast<const floatx4*>(&gcs[b][16 * db + g4]);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) S[db][rr] = gd[rr] * S[db][rr] + dS[db][rr];
+                    }
+                }
+                mfma_settle();   // O is read inside the row-bounds branches below
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int64_t row = t0 + 16 * li + g4 + rr;
+                    if (row < Tlen) o[(bh * Tlen + row) * DV + n0 + cl] = from_f32<T>(O[rr]);
+                }
+                lds_barrier();
+            }
+        }
+        for (int64_t s = nsteps; s < nspad; ++s) lds_barrier();
+        if (s_final) {
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) s_final[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] = S[db][rr];
+        }
+        return;
+    }
+
+    // ======== helper waves: thread ht of 256 ==========================================
+    const int ht = threadIdx.x - 256;
+    const int64_t lastb = nsteps > 0 ? nsteps - 1 : 0;
+    // the operands of block s into R (s clamped to the last block)
+    auto hload = [&](Regs& R, int64_t s) {
+        s = s < lastb ? s : lastb;
+        const int64_t c = s / NB;
+        const int li = (int)(s % NB);
+        const unsigned char* wc = ws + (bh * nchunks + c) * L.bytes;
+#pragma unroll
+        for (int p = 0; p < G::NW; ++p) {
+            int i = p * 256 + ht;
+            i = i < G::VW ? i : G::VW - 1;
+            const int row = i / (DK / E), col = (i % (DK / E)) * E;
+            const size_t off = ((size_t)(16 * li + row) * DK + col) * sizeof(T);
+            if constexpr (DELTA) R.w[p] = *reinterpret_cast<const i4*>(wc + L.w + off);
+            R.q[p] = *reinterpret_cast<const i4*>(wc + L.qd + off);
         }
 #pragma unroll
-        for (int mj = 0; mj < NB; ++mj)
-            if (mj <= li) b.a[mj] = frag16_g(Aq + 16 * li * C + 16 * mj, C, lane);
+        for (int p = 0; p < G::NKR; ++p) {
+            int i = p * 256 + ht;
+            i = i < G::VKR ? i : G::VKR - 1;
+            const int row = i / (16 / E), col = (i % (16 / E)) * E;
+            R.kr[p] = *reinterpret_cast<const i4*>(wc + L.krt + ((size_t)row * C + 16 * li + col) * sizeof(T));
+        }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = 16 * li + g4 + rr;
+        for (int p = 0; p < G::NA; ++p) {
+            int i = p * 256 + ht;
+            i = i < G::VA ? i : G::VA - 1;
+            const int row = i / (C / E), col = (i % (C / E)) * E;
+            R.a[p] = *reinterpret_cast<const i4*>(wc + L.aq + ((size_t)(16 * li + row) * C + col) * sizeof(T));
+        }
+#pragma unroll
+        for (int p = 0; p < G::NU; ++p) {
+            int i = p * 256 + ht;
+            i = i < G::VU ? i : G::VU - 1;
+            const int row = i / (64 / E), col = vb * 64 + (i % (64 / E)) * E;
             if constexpr (DELTA) {
-                b.u[rr] = to_f32(reinterpret_cast<const T*>(wc + L.u)[row * DV + n0 + cl]);
+                R.u[p] = *reinterpret_cast<const i4*>(wc + L.u + ((size_t)(16 * li + row) * DV + col) * sizeof(T));
             } else {
-                const int64_t t = c * C + row < Tlen ? c * C + row : Tlen - 1;
-                b.u[rr] = to_f32(v[(bh * Tlen + t) * DV + n0 + cl]);
+                const int64_t t = c * C + 16 * li + row;
+                R.u[p] = *reinterpret_cast<const i4*>(v + (bh * Tlen + (t < Tlen ? t : Tlen - 1)) * DV + col);
             }
+        }
+        {
+            const int i = ht < G::VG ? ht : G::VG - 1;
+            R.g = *reinterpret_cast<const i4*>(wc + L.gc + 16 * i);
         }
     };
-
-    floatx4 S[ND];
+    // R (the operands of block s) into LDS buffer s & 1
+    auto hstore = [&](const Regs& R, int64_t s) {
+        const int64_t c = s / NB;
+        const int li = (int)(s % NB);
+        T* const st = stage[s & 1];
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
-
-    Blk cur, nxt;
-    if (nchunks > 0) fetch(cur, 0, 0);
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const float* const gC = reinterpret_cast<const float*>(ws + (bh * nchunks + c) * L.bytes + L.gc);
-        floatx4 gd[ND];
-#pragma unroll
-        for (int db = 0; db < ND; ++db) gd[db] = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
-        const int64_t t0 = c * C;
-        F Sf[ND];
-#pragma unroll
-        for (int db = 0; db < ND; ++db) Sf[db] = frag16_acc<T>(S[db]);
-        floatx4 dS[ND];
-#pragma unroll
-        for (int db = 0; db < ND; ++db) dS[db] = zero4();
-        F Zf[NB];
-#pragma unroll
-        for (int li = 0; li < NB; ++li) {
-            if (li + 1 < NB) fetch(nxt, c, li + 1);
-            else fetch(nxt, c + 1 < nchunks ? c + 1 : c, 0);
-            // b1: Z = U - W S_r (delta) | V (add)
-            floatx4 Z = cur.u;
-            if constexpr (DELTA) {
-                floatx4 P = zero4();
-#pragma unroll
-                for (int db = 0; db < ND; ++db) P = mma16<T>(cur.w[db], Sf[db], P);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
-            } else {
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    if (t0 + 16 * li + g4 + rr >= Tlen) Z[rr] = 0.f;
+        for (int p = 0; p < G::NW; ++p) {
+            const int i = p * 256 + ht;
+            if (i < G::VW) {
+                const int row = i / (DK / E), col = (i % (DK / E)) * E;
+                if constexpr (DELTA) *reinterpret_cast<i4*>(st + G::W + row * G::LDK + col) = R.w[p];
+                *reinterpret_cast<i4*>(st + G::Q + row * G::LDK + col) = R.q[p];
             }
-            Zf[li] = frag16_acc<T>(Z);
-            // c1: O = <-Q S_r + sum_{mj <= li} Aq(li, mj) Z_mj
-            floatx4 O = zero4();
-#pragma unroll
-            for (int db = 0; db < ND; ++db) O = mma16<T>(cur.q[db], Sf[db], O);
-#pragma unroll
-            for (int mj = 0; mj <= li; ++mj) O = mma16<T>(cur.a[mj], Zf[mj], O);
-            // ->K_li^T Z_li
-#pragma unroll
-            for (int db = 0; db < ND; ++db) dS[db] = mma16<T>(cur.kr[db], Zf[li], dS[db]);
-            mfma_settle();   // O is read inside the row-bounds branches below
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int64_t row = t0 + 16 * li + g4 + rr;
-                if (row < Tlen) o[(bh * Tlen + row) * DV + n0 + cl] = from_f32<T>(O[rr]);
-            }
-            cur = nxt;
         }
-        // S_{r+1} = Diag(2^(G_{C-1})) S_r + ->K^T Z
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
+        for (int p = 0; p < G::NKR; ++p) {
+            const int i = p * 256 + ht;
+            if (i < G::VKR) {
+                const int row = i / (16 / E), col = (i % (16 / E)) * E;
+                *reinterpret_cast<i4*>(st + G::KR + row * G::LDT + col) = R.kr[p];
+            }
+        }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) S[db][rr] = gd[db][rr] * S[db][rr] + dS[db][rr];
+        for (int p = 0; p < G::NA; ++p) {
+            const int i = p * 256 + ht;
+            if (i < G::VA) {
+                const int row = i / (C / E), col = (i % (C / E)) * E;
+                *reinterpret_cast<i4*>(st + G::A + row * G::LDA + col) = R.a[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < G::NU; ++p) {
+            const int i = p * 256 + ht;
+            if (i < G::VU) {
+                const int row = i / (64 / E), col = (i % (64 / E)) * E;
+                const bool past = !DELTA && c * C + 16 * li + row >= Tlen;
+                *reinterpret_cast<i4*>(st + G::U + row * G::LDU + col) = past ? i4{0, 0, 0, 0} : R.u[p];
+            }
+        }
+        if (ht < G::VG) *reinterpret_cast<i4*>(&gcs[s & 1][4 * ht]) = R.g;
+    };
+    // block s: stage block s + 1 (held in Rw), load block s + 3 into Rl
+    auto hstep = [&](int64_t s, const Regs& Rw, Regs& Rl) {
+        if (s + 1 < nsteps) hstore(Rw, s + 1);
+        hload(Rl, s + 3);
+        lds_barrier();
+    };
+    Regs R0, R1, R2;
+    if (nsteps > 0) {
+        hload(R0, 0);
+        hload(R1, 1);
+        hload(R2, 2);
+        hstore(R0, 0);
     }
-    if (s_final) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) s_final[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] = S[db][rr];
+    lds_barrier();
+    for (int64_t s = 0; s < nspad; s += 3) {
+        hstep(s, R1, R0);
+        hstep(s + 1, R2, R1);
+        hstep(s + 2, R0, R2);
     }
 }
 
@@ -555,7 +662,7 @@ hipError_t launch_gen_t(const ChunkProblem& p, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     const int nblocks = (int)(bh * (p.dv / 64));
-    hipLaunchKernelGGL((gen_chain_kernel<T, C, DK, RULE>), dim3((unsigned)nblocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((gen_chain_kernel<T, C, DK, RULE>), dim3((unsigned)nblocks), dim3(512), 0, s,
                        static_cast<const T*>(p.v), ws, p.s0, static_cast<T*>(p.o), p.s_final, p.T, nchunks, p.dv,
                        nblocks);
     return hipGetLastError();
