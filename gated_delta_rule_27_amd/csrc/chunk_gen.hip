@@ -54,7 +54,9 @@ namespace linattn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kGT = 256;          // threads of the intra-chunk kernel (4 waves)
+// waves of the intra-chunk kernel: 8 at C = 128, whose LDS leaves one
+// workgroup per CU, else 4
+__host__ __device__ constexpr int gen_waves(int C) { return C == 128 ? 8 : 4; }
 constexpr int kKS = 32;           // key / value channels per staged slice
 constexpr int kLDS = kKS + 4;     // row stride of a staged fp32 slice
 
@@ -97,7 +99,7 @@ __device__ __forceinline__ void tile_ij(int p, int& i, int& j)
 // Intra-chunk kernel
 // ===========================================================================
 template <typename T, int C, int DK, int RULE, int GATE>
-__global__ __launch_bounds__(kGT) void gen_intra_kernel(
+__global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
     const T* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks, int DV,
     int prep)
@@ -106,8 +108,9 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
     constexpr bool DELTA = RULE == kRuleDelta;
     constexpr bool CHAN = GATE == kGateChannel;
     constexpr bool GATED = GATE != kGateNone;
+    constexpr int NW = gen_waves(C), kGT = 64 * NW;
     constexpr int NTILE = NB * (NB + 1) / 2;
-    constexpr int MS = (NTILE + 3) / 4;          // causal tiles per wave
+    constexpr int MS = (NTILE + NW - 1) / NW;    // causal tiles per wave
     constexpr int LDL = C + 4;                   // row stride of L and T
     constexpr int NSL = DK / kKS;                // key-channel slices
     static_assert(NB >= 1 && NB <= 8 && DK % kKS == 0, "chunk and head sizes");
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
         stage_qk(sl * kKS);
 #pragma unroll
         for (int s = 0; s < MS; ++s) {
-            const int p = wave + 4 * s;
+            const int p = wave + NW * s;
             if (p >= NTILE) continue;
             int i, j;
             tile_ij(p, i, j);
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
     // Aq to the workspace, beta L to LDS (rows l = 16 i + g4 + rr, column m)
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
-        const int p = wave + 4 * s;
+        const int p = wave + NW * s;
         if (p >= NTILE) continue;
         int i, j;
         tile_ij(p, i, j);
@@ -288,10 +291,10 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
     __syncthreads();
 
     if constexpr (DELTA) {
-        // ---- a3: T = (I + beta L)^-1.  Diagonal block i: wave i % 4, lane group
-        // i / 4, lane column jj; rows by forward substitution --------------------
+        // ---- a3: T = (I + beta L)^-1.  Diagonal block i: wave i % NW, lane group
+        // i / NW, lane column jj; rows by forward substitution -------------------
         {
-            const int jj = lane & 15, i = wave + 4 * (lane >> 4);
+            const int jj = lane & 15, i = wave + NW * (lane >> 4);
             if (i < NB) {
                 float x[16];
 #pragma unroll
@@ -309,10 +312,11 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
         // blocks below the diagonal, one block row at a time:
         // T(i, j) = -T(i, i) sum_{kb = j}^{i - 1} L(i, kb) T(kb, j)
         for (int i = 1; i < NB; ++i) {
-            floatx4 X[2];
+            constexpr int NJ = (8 + NW - 1) / NW;   // column blocks per wave
+            floatx4 X[NJ];
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int j = wave + 4 * s2;
+            for (int s2 = 0; s2 < NJ; ++s2) {
+                const int j = wave + NW * s2;
                 X[s2] = zero4();
                 if (j < i)
                     for (int kb = j; kb < i; ++kb)
@@ -322,8 +326,8 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
             mfma_settle();
             __syncthreads();
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int j = wave + 4 * s2;
+            for (int s2 = 0; s2 < NJ; ++s2) {
+                const int j = wave + NW * s2;
                 if (j < i) {
                     const floatx4 t = mm16<float>(&Lm[16 * i * LDL + 16 * i], LDL, X[s2], zero4(), lane);
                     mfma_settle();
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(kGT) void gen_intra_kernel(
     // ---- products T (beta X) for the staged slice in xs: tiles (lb, cb) of a
     // [C][kKS] block, written to dst (row stride ld) at column c0 --------------
     auto tb_product = [&](T* dst, int ld, int c0) {
-        for (int p = wave; p < NB * (kKS / 16); p += 4) {
+        for (int p = wave; p < NB * (kKS / 16); p += NW) {
             const int lb = p / (kKS / 16), cb = p % (kKS / 16);
             floatx4 acc = zero4();
             for (int mb = 0; mb <= lb; ++mb)
@@ -654,7 +658,8 @@ hipError_t launch_gen_t(const ChunkProblem& p, hipStream_t s)
     const int64_t bh = p.B * p.H;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((gen_intra_kernel<T, C, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)), dim3(kGT), 0, s,
+        hipLaunchKernelGGL((gen_intra_kernel<T, C, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)),
+                           dim3(64 * gen_waves(C)), 0, s,
                            static_cast<const T*>(p.q), static_cast<const T*>(p.k), static_cast<const T*>(p.v),
                            static_cast<const T*>(p.g), static_cast<const T*>(p.beta), ws, p.T, nchunks, p.dv,
                            p.prep);
