@@ -36,6 +36,7 @@ CHUNK_PROFILE = "chunk_pipe_gdn_B8_H16_T8192_d128.md"
 DECODE_PROFILE = "decode_step_gdn_N256_H32_d128.md"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix peak (fp32 tokens: fp32 operands)
 
 
 def chunk_alg_bytes(B, H, T, dk, dv, s, rule, gate, with_state=True):
@@ -139,12 +140,14 @@ def time_chunk(la, syn, case, dev, steps, warmup=20):
     ms = e0.elapsed_time(e1) / steps
     s = 2 if case.dtype == "bf16" else 4
     abytes = chunk_alg_bytes(B, H, T, dk, dv, s, case.rule, case.gate)
-    aflops = chunk_nominal_flops(B, H, T, dk, dv, case.rule)
+    aflops = chunk_nominal_flops(B, H, T, dk, dv, case.rule, case.chunk)
     return {"workload": f"{case.rule}/{case.gate} chunk_fwd B={B} H={H} T={T} dk={dk} dv={dv} "
                         f"chunk={case.chunk} {case.dtype} tokens fp32 state",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "hbm_frac": round(abytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac": round(aflops / (ms * 1e-3) / 1e12 / (MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16"
+                                                             else MFMA_FP32_PEAK_TFLOPS), 4),
+            "mfma_peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS if case.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS,
             "path": chunk_path(case, wsb), "steps": steps}
 
 
