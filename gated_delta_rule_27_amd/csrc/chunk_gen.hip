@@ -48,6 +48,7 @@
 #include "launch.h"
 #include "mfma.h"
 #include "prep.h"
+#include "segments.h"
 
 namespace linattn {
 
@@ -441,7 +442,7 @@ struct GenRegs {
 template <typename T, int C, int DK, int RULE>
 __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
     const T* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0, T* __restrict__ o,
-    float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks)
+    float* s_final, int64_t Tlen, int64_t nchunks, int DV, int nblocks, SegSplit seg)
 {
     using F = typename Frag16<T>::type;
     using G = GenStage<T, C, DK>;
@@ -459,10 +460,15 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
     // the value blocks of a head on one XCD (dispatch is round-robin over 8)
     int blk = blockIdx.x;
     if ((nblocks & 7) == 0) blk = (blk & 7) * (nblocks >> 3) + (blk >> 3);
-    const int64_t bh = blk / nvb;
-    const int vb = blk % nvb;
+    const int nunit = nvb * seg.n;
+    const int64_t bh = blk / nunit;
+    const int vb = (blk % nunit) % nvb;
+    const int sg = (blk % nunit) / nvb;
+    // this workgroup's chunks [rb, re) (segments.h); chunks [0, rb) run the state
+    // update alone first
+    const int64_t rb = seg.c[sg], re = seg.c[sg + 1];
     const GenWs L = gen_ws(C, DK, DV, (int)sizeof(T), DELTA);
-    const int64_t nsteps = nchunks * NB;           // 16-row blocks
+    const int64_t nsteps = re * NB;                // 16-row blocks staged, prefix included
     const int64_t nspad = (nsteps + 2) / 3 * 3;     // the helpers' count, a multiple of 3
 
     if (wave < 4) {
@@ -476,7 +482,46 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
             for (int rr = 0; rr < 4; ++rr)
                 S[db][rr] = s0 ? s0[(bh * DK + 16 * db + g4 + rr) * DV + n0 + cl] : 0.f;
         lds_barrier();                               // block 0 staged
-        for (int64_t c = 0; c < nchunks; ++c) {
+        // prefix pass over chunks [0, rb): Z and the state update, no output
+        for (int64_t c = 0; c < rb; ++c) {
+            F Sf[ND];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) Sf[db] = frag16_acc<T>(S[db]);
+            floatx4 dS[ND];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) dS[db] = zero4();
+#pragma unroll
+            for (int li = 0; li < NB; ++li) {
+                const int ln = opaque(lane);
+                const int b = (int)((c * NB + li) & 1);
+                const T* const st = stage[b];
+                floatx4 Z;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Z[rr] = to_f32(st[G::U + (g4 + rr) * G::LDU + 16 * wave + cl]);
+                if constexpr (DELTA) {
+                    floatx4 P = zero4();
+#pragma unroll
+                    for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_lds(st + G::W + 16 * db, G::LDK, ln), Sf[db], P);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
+                }
+                const F zf = frag16_acc<T>(Z);
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+                    dS[db] = mma16<T>(frag16_lds(st + G::KR + 16 * db * G::LDT, G::LDT, ln), zf, dS[db]);
+                if (li == NB - 1) {
+#pragma unroll
+                    for (int db = 0; db < ND; ++db) {
+                        const floatx4 gd = *reinterpret_cast<const floatx4*>(&gcs[b][16 * db + g4]);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) S[db][rr] = gd[rr] * S[db][rr] + dS[db][rr];
+                    }
+                }
+                mfma_settle();
+                lds_barrier();
+            }
+        }
+        for (int64_t c = rb; c < re; ++c) {
             const int64_t t0 = c * C;
             F Sf[ND];
 #pragma unroll
@@ -531,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
             }
         }
         for (int64_t s = nsteps; s < nspad; ++s) lds_barrier();
-        if (s_final) {
+        if (s_final && sg == seg.n - 1) {
 #pragma unroll
             for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -651,6 +696,10 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
     }
 }
 
+// A prefix block of the state pass (Z and the state update, no output) costs
+// about this fraction of a full block.
+constexpr double kGenPrefixCost = 0.6;
+
 template <typename T, int C, int DK, int RULE, int GATE>
 hipError_t launch_gen_t(const ChunkProblem& p, hipStream_t s)
 {
@@ -666,10 +715,14 @@ hipError_t launch_gen_t(const ChunkProblem& p, hipStream_t s)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int nblocks = (int)(bh * (p.dv / 64));
+    // segments of each head's chunks when the grid leaves CUs idle (segments.h)
+    const int64_t nblocks1 = bh * (p.dv / 64);
+    const SegSplit sp = seg_split(nchunks, nblocks1, true, p.s0, p.s_final,
+                                  (size_t)bh * p.dk * p.dv * sizeof(float), kGenPrefixCost);
+    const int nblocks = (int)(nblocks1 * sp.n);
     hipLaunchKernelGGL((gen_chain_kernel<T, C, DK, RULE>), dim3((unsigned)nblocks), dim3(512), 0, s,
                        static_cast<const T*>(p.v), ws, p.s0, static_cast<T*>(p.o), p.s_final, p.T, nchunks, p.dv,
-                       nblocks);
+                       nblocks, sp);
     return hipGetLastError();
 }
 

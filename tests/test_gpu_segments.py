@@ -239,3 +239,28 @@ def test_chain_segments_state_in_place():
     torch.cuda.synchronize()
     assert s.data_ptr() == s_io.data_ptr()
     assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
+
+
+# ---- the generic path's state pass (chunk 16, 32, 128; fp32 at d_k = 128) ----
+
+@pytest.mark.parametrize("chunk", [16, 32, 128])
+@pytest.mark.parametrize("rule,gate", [("delta", "scalar"), ("delta", "channel"), ("add", "none"), ("add", "channel")])
+def test_gen_segments(monkeypatch, rule, gate, chunk):
+    # one head at d_v = 128: two state-pass workgroups, split into the most
+    # segments; compared with the oracle and bit for bit with one segment
+    case = syn.Case("seggen", 1, 1, 1300, 128, 128, rule, gate, "bf16", chunk=chunk, gate_scale=1 / 16,
+                    s0_std=0.3, case_id=173)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
+    o, s = run_chunk(case, x, x["s0"])
+    monkeypatch.setenv("LINATTN_SEGMENTS", "1")
+    o1, s1 = run_chunk(case, x, x["s0"])
+    assert torch.equal(o, o1) and torch.equal(s, s1)
+
+
+def test_gen_segments_fp32(monkeypatch):
+    monkeypatch.setenv("LINATTN_SEGMENTS", "3")
+    case = syn.Case("seggen32", 1, 2, 700, 128, 64, "delta", "scalar", "fp32", gate_scale=1 / 16, s0_std=0.3,
+                    case_id=174)
+    x = syn.chunk_inputs(case)
+    check_chunk(case, x, s0=x["s0"])
