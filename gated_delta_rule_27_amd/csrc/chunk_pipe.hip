@@ -31,21 +31,21 @@
 //   phase 1  R = V - gamma K S_r,                 delta: diagonal N blocks, their
 //            gamma Q S_r, K^T (matrix-core        inverses, N blocks below the
 //            transposes); delta: Aq of chunk      diagonal (chunk r+1); add: Aq
-//            r+1                                  of chunk r+1; all: output of
-//                                                 chunk r-1 from LDS to HBM
+//            r+1                                  of chunk r+1
 //   ---- barrier
 //   phase 2  Z = Tb R, O = gamma Q S_r + Aq Z     chunk r+2's Q, K and chunk r+1's
-//            (to LDS), S_{r+1}; delta, waves      V from registers to LDS, chunk
-//            0 and 1: off-diagonal blocks of      r+2's gate scan; loads for the
-//            T (chunk r+1)                        step after next
+//            (straight to HBM), S_{r+1}; delta,   V from registers to LDS, chunk
+//            waves 0, 1, 2: off-diagonal blocks   r+2's gate scan; loads for the
+//            of T (chunk r+1)                     step after next
 //   ---- barrier
 //
 // Q and K are double-buffered in LDS (chunk parity), and so are Aq and Tb; the
 // gate arrays rotate through three slots (chunk mod 3).  The state waves own
 // 16 value columns each and keep S[:, those columns] (fp32) as dk/16 MFMA
-// result tiles for the whole sequence; S, R and Z never leave registers.  They
-// touch no global memory inside the loop.  Operands are bf16, accumulation is
-// fp32; the state is rounded to bf16 only as an operand.
+// result tiles for the whole sequence; S, R and Z never leave registers.
+// Inside the loop their only global accesses are the output stores.  Operands
+// are bf16, accumulation is fp32; the state is rounded to bf16 only as an
+// operand.
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
