@@ -113,6 +113,41 @@ __device__ __forceinline__ V f32_vec(const float (&f)[16 / sizeof(T)])
     return x;
 }
 
+// Qs, Ks, KsT, Aq and Tb hold their columns in swizzled pcol order (mfma.h)
+// for 2-byte tokens and in plain pcol order for fp32; every access goes
+// through these, which pick the matching form.
+template <typename T>
+constexpr int kTilePc = sizeof(T) == 2 ? 2 : 1;
+template <typename T>
+__device__ __forceinline__ int tile_sw(int row)
+{
+    return sizeof(T) == 2 ? swz_x(row) : 0;
+}
+template <typename T>
+__device__ __forceinline__ typename Pair<T>::type tile_pair(const T* M, int ld, int lane)
+{
+    if constexpr (sizeof(T) == 2) return pair_lds_sw(M, ld, lane);
+    else return pair_lds(M, ld, lane);
+}
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag tile_load(const T* row0, int ld, int k0, int lane)
+{
+    if constexpr (sizeof(T) == 2) return mfma_load_sw(row0, ld, k0, lane);
+    else return Mfma<T>::load(row0, ld, k0, lane);
+}
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type tile_frag16(const T* M, int ld, int kb, int lane)
+{
+    if constexpr (sizeof(T) == 2) return frag16_lds_pc_sw(M, ld, kb, lane);
+    else return frag16_lds_pc(M, ld, kb, lane);
+}
+template <typename T>
+__device__ __forceinline__ void tile_store_t(T* M, int ld, int kb, floatx4 v, int lane)
+{
+    if constexpr (sizeof(T) == 2) store_tile_t_pc_sw(M, ld, kb, v, lane);
+    else store_tile_t_pc(M, ld, kb, v, lane);
+}
+
 // SAVE: also write the state entering every chunk, states[b,h,r] = S_r
 // ([dk][dv] per chunk, rounded to the token type once), for the backward pass.
 // NORM (add rule): normalised linear attention ("All sorts of famous Attention
@@ -219,9 +254,11 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             vreg[p] = *reinterpret_cast<const i4*>(vh + tr * DV + col);
         }
     };
-    // Q and K rows go to LDS with their columns in pcol order (mfma.h), 8 bytes
-    // (four columns) at a time for bf16; raw projections first go through the
-    // q/k map of prep.h, and rows past the end are zeroed after it
+    // Q and K rows go to LDS with their columns in (swizzled) pcol order, 8
+    // bytes (four columns) at a time for bf16; at dk = 128 the threads of the
+    // second 64 columns of a row write their upper four columns first, so each
+    // 16-lane group of a write covers 32 distinct banks.  Raw projections first
+    // go through the q/k map of prep.h, and rows past the end are zeroed after it
     auto stage = [&](int64_t t0) {
         const int qk_map = prep_qk_map(prep);
 #pragma unroll
@@ -236,10 +273,14 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const i4 kv = ok ? kp : i4{0, 0, 0, 0};
             if constexpr (E == 8) {
                 typedef __attribute__((__vector_size__(8))) int i2;
-                *reinterpret_cast<i2*>(&Qs[row * LDQ + pcol(col)]) = i2{qv[0], qv[1]};
-                *reinterpret_cast<i2*>(&Qs[row * LDQ + pcol(col + 4)]) = i2{qv[2], qv[3]};
-                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col)]) = i2{kv[0], kv[1]};
-                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col + 4)]) = i2{kv[2], kv[3]};
+                const int sw = tile_sw<T>(row);
+                const bool hi = DK == 128 && (col & 64);
+                const int c0 = row * LDQ + (pcol(col + (hi ? 4 : 0)) ^ sw);
+                const int c1 = row * LDQ + (pcol(col + (hi ? 0 : 4)) ^ sw);
+                *reinterpret_cast<i2*>(&Qs[c0]) = hi ? i2{qv[2], qv[3]} : i2{qv[0], qv[1]};
+                *reinterpret_cast<i2*>(&Ks[c0]) = hi ? i2{kv[2], kv[3]} : i2{kv[0], kv[1]};
+                *reinterpret_cast<i2*>(&Qs[c1]) = hi ? i2{qv[0], qv[1]} : i2{qv[2], qv[3]};
+                *reinterpret_cast<i2*>(&Ks[c1]) = hi ? i2{kv[0], kv[1]} : i2{kv[2], kv[3]};
             } else {
                 *reinterpret_cast<i4*>(&Qs[row * LDQ + pcol(col)]) = qv;
                 *reinterpret_cast<i4*>(&Ks[row * LDQ + pcol(col)]) = kv;
@@ -285,8 +326,12 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const i4 kv = ok ? kp : i4{0, 0, 0, 0};
             if constexpr (E == 8) {
                 typedef __attribute__((__vector_size__(8))) int i2;
-                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col)]) = i2{kv[0], kv[1]};
-                *reinterpret_cast<i2*>(&Ks[row * LDQ + pcol(col + 4)]) = i2{kv[2], kv[3]};
+                const int sw = tile_sw<T>(row);
+                const bool hi = DK == 128 && (col & 64);
+                const int c0 = row * LDQ + (pcol(col + (hi ? 4 : 0)) ^ sw);
+                const int c1 = row * LDQ + (pcol(col + (hi ? 0 : 4)) ^ sw);
+                *reinterpret_cast<i2*>(&Ks[c0]) = hi ? i2{kv[2], kv[3]} : i2{kv[0], kv[1]};
+                *reinterpret_cast<i2*>(&Ks[c1]) = hi ? i2{kv[0], kv[1]} : i2{kv[2], kv[3]};
             } else {
                 *reinterpret_cast<i4*>(&Ks[row * LDQ + pcol(col)]) = kv;
             }
@@ -351,7 +396,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
     using Fr = typename Mfma<T>::frag;
     auto block_frags = [&](const T* A, int b, int ln, Fr (&f)[NK]) {
 #pragma unroll
-        for (int i = 0; i < NK; ++i) f[i] = Mfma<T>::load(&A[b * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
+        for (int i = 0; i < NK; ++i) f[i] = tile_load(&A[b * 16 * LDQ], LDQ, i * Mfma<T>::kStep, ln);
     };
     // x[rr] = sum_c A[16 mi + g4 + rr][c] B[16 lj + cl][c] from the blocks' fragments
     auto tile_dot = [&](const Fr (&fa)[NK], const Fr (&fb)[NK]) {
@@ -361,7 +406,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         return x;
     };
     // ---- NORM.  z is kept in natural key order; Qs columns, and the token
-    // columns of KsT and Aq, are stored in pcol order, whose position s holds
+    // columns of KsT and Aq, are stored in pcol order (swizzled for 2-byte
+    // tokens, which the fragment loads undo), so position s of a fragment holds
     // logical column pcol_first(s & ~7) + (s & 4 ? 16 : 0) + (s & 3).
     // Matrix-core right factor: a 16-row block whose row 0 is x (logical
     // order, at the fragment's stored positions; x == nullptr: all ones) and
@@ -401,7 +447,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         const Fr f1 = row0_frag(nullptr, 0, ln);
         floatx4 xa = zero4();
 #pragma unroll
-        for (int i = 0; i < NA; ++i) xa = Mfma<T>::mma(Mfma<T>::load(&Aq[part * 16 * LDC], LDC, i * kS, ln), f1, xa);
+        for (int i = 0; i < NA; ++i) xa = Mfma<T>::mma(tile_load(&Aq[part * 16 * LDC], LDC, i * kS, ln), f1, xa);
         if (cl == 0) {
             const floatx4 qz = *reinterpret_cast<const floatx4*>(&qzs[rp & 1][16 * part + g4]);
             floatx4 d;
@@ -422,7 +468,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
             const float dec = GATED ? fast_exp2(Gl - Gm[rr]) : 1.f;
             va[rr] = (mi < lj || g4 + rr <= cl) ? xa[rr] * dec : 0.f;
         }
-        store_tile_t_pc(&Aq[lj * 16 * LDC], LDC, mi, va, ln);
+        tile_store_t(&Aq[lj * 16 * LDC], LDC, mi, va, ln);
     };
     // add rule: the ten causal Aq tiles (lj, mi) on waves 4..7, grouped by query
     // block so each wave loads three or four blocks once:
@@ -495,7 +541,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         floatx4 nd[1], nt[1], br[1], Xa[1], Xta[1];
         Fr kb[NK], k2[NK];
         diag_block(Gs, bet, b, ln, nd[0], nt[0], br[0], kb);
-        tsolve_diag<T, true, 1>(nd, nt, Xa, Xta, Tb, LDC, br, ln, b);
+        tsolve_diag<T, kTilePc<T>, 1>(nd, nt, Xa, Xta, Tb, LDC, br, ln, b);
         X = Xa[0];
         Xt = Xta[0];
         if (b == 0) {                                  // N(1,0)
@@ -529,7 +575,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
         for (int i = 0; i < NKT; ++i) {
             const int t = iw + NW * i;
-            af[i] = frag16_lds_pc(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
+            af[i] = tile_frag16(&Ks[(t / ND) * 16 * LDQ], LDQ, t % ND, ln);
         }
         const F id = ident_frag<T>(ln);
         floatx4 d[NKT];
@@ -538,7 +584,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
         for (int i = 0; i < NKT; ++i) {
             const int t = iw + NW * i;
-            store_tile_t_pc(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
+            tile_store_t(&KsT[(t % ND) * 16 * LDC], LDC, t / ND, d[i], ln);
         }
     };
     // b1 of state wave w: S_{r+1} = gamma_{C-1} S_r + K^T diag(rho) Z (NORM: and
@@ -562,8 +608,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         for (int db = 0; db < ND; ++db) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gC;
-            S[db] = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
-                                mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
+            S[db] = mma_pair<T>(tile_pair(&KsT[16 * db * LDC + 32], LDC, ln), zr23,
+                                mma_pair<T>(tile_pair(&KsT[16 * db * LDC], LDC, ln), zr01, S[db]));
         }
         if constexpr (NORM) {
             // z_{r+1} = gamma_{C-1} z_r + K^T rho for this wave's key blocks: rho
@@ -583,8 +629,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 floatx4 zt = *reinterpret_cast<const floatx4*>(&zSb[r & 1][16 * db + g4]);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) zt[rr] *= gC;
-                zt = mma_pair<T>(pair_lds(&KsT[16 * db * LDC + 32], LDC, ln), rz23,
-                                 mma_pair<T>(pair_lds(&KsT[16 * db * LDC], LDC, ln), rz01, zt));
+                zt = mma_pair<T>(tile_pair(&KsT[16 * db * LDC + 32], LDC, ln), rz23,
+                                 mma_pair<T>(tile_pair(&KsT[16 * db * LDC], LDC, ln), rz01, zt));
                 if (cl == 0) *reinterpret_cast<floatx4*>(&zSb[(r + 1) & 1][16 * db + g4]) = zt;
             }
         }
@@ -673,7 +719,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     const auto sp = pair_regs<T>(S[db], S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        P[li] = mma_pair<T>(pair_lds(&Ks[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
+                        P[li] = mma_pair<T>(tile_pair(&Ks[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
                 }
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
@@ -692,7 +738,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                     const auto sp = pair_regs<T>(S[db], S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        Ot[li] = mma_pair<T>(sp, pair_lds(&Qs[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
+                        Ot[li] = mma_pair<T>(sp, tile_pair(&Qs[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
                 }
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
@@ -714,7 +760,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                             za[rr] = cl == 0 ? z0v[rr] : 0.f;
                             zb[rr] = cl == 0 ? z1v[rr] : 0.f;
                         }
-                        oz = mma_pair<T>(pair_regs<T>(za, zb), pair_lds(&Qs[16 * wave * LDQ + 16 * db], LDQ, ln), oz);
+                        oz = mma_pair<T>(pair_regs<T>(za, zb), tile_pair(&Qs[16 * wave * LDQ + 16 * db], LDQ, ln), oz);
                     }
                     if (g4 == 0) qzs[r & 1][16 * wave + cl] = gam[16 * wave + cl] * oz[0];
                 }
@@ -773,8 +819,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 const auto r01 = pair_regs<T>(R[0], R[1]), r23 = pair_regs<T>(R[2], R[3]);
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
-                    Z[li] = mma_pair<T>(pair_lds(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
-                    if (li >= 2) Z[li] = mma_pair<T>(pair_lds(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                    Z[li] = mma_pair<T>(tile_pair(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
+                    if (li >= 2) Z[li] = mma_pair<T>(tile_pair(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
                 }
             } else {
 #pragma unroll
@@ -785,8 +831,8 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 const auto z01 = pair_regs<T>(Z[0], Z[1]), z23 = pair_regs<T>(Z[2], Z[3]);
 #pragma unroll
                 for (int lj = 0; lj < NL; ++lj) {
-                    Ot[lj] = mma_pair<T>(z01, pair_lds(&Aq[16 * lj * LDC], LDC, ln), Ot[lj]);
-                    if (lj >= 2) Ot[lj] = mma_pair<T>(z23, pair_lds(&Aq[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
+                    Ot[lj] = mma_pair<T>(z01, tile_pair(&Aq[16 * lj * LDC], LDC, ln), Ot[lj]);
+                    if (lj >= 2) Ot[lj] = mma_pair<T>(z23, tile_pair(&Aq[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
                 }
             }
             // O^T tile -> Os[token][column]
@@ -871,7 +917,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
                 for (int b = 0; b < NL; ++b) brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
                 const floatx4* nl = Nlo + ln;
-                tsolve_offdiag_a<T, true>(X0, Xx[0 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
+                tsolve_offdiag_a<T, kTilePc<T>>(X0, Xx[0 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
                                           nl[0 * kWave], nl[1 * kWave], nl[2 * kWave], nl[3 * kWave],
                                           nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
                 lds_barrier();
@@ -904,7 +950,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
 #pragma unroll
             for (int b = 0; b < NL; ++b) brow[b] = *reinterpret_cast<const floatx4*>(&bet[16 * b + g4]);
             const floatx4* nl = Nlo + ln;
-            tsolve_offdiag_b<T, true>(X1, Xx[1 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
+            tsolve_offdiag_b<T, kTilePc<T>>(X1, Xx[1 * kWave + ln], Xx[2 * kWave + ln], Xx[3 * kWave + ln],
                                       nl[2 * kWave], nl[4 * kWave], nl[5 * kWave], Tb, LDC, brow, ln);
             lds_barrier();
         }
