@@ -328,43 +328,106 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_kernel(const T* __restrict__ q
         __builtin_memcpy(&w, e, 16);
         *reinterpret_cast<i4*>(dst) = w;
     };
-    float x[E];
-    // A^T and Tb^T: row l holds column l of A / Tb
-    for (int v = tid; v < kC * kC / E; v += kNT) {
-        const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+    if constexpr (sizeof(T) == 2) {
+        // 2-byte tokens: every transposed operand goes out in 8x8 blocks, one
+        // per thread: eight 16-byte rows read from LDS, transposed (and scaled)
+        // in registers, eight 16-byte rows written.  Within a wave, lane =
+        // column block + 8 x row block of the source, so each 16-lane group of
+        // a row read covers 64 distinct banks and the eight lanes of a row
+        // block write 128 contiguous bytes.
+        // Blocks: A^T (64), Tb^T (64, delta), <-Q^T and -<-K^T (delta), 8 dk/8
+        // each; every part is a whole number of waves.
+        constexpr int NQB = 8 * (DK / 8);
+        constexpr int NB = 64 + (DELTA ? 64 : 0) + NQB + (DELTA ? NQB : 0);
+        for (int job = tid; job < NB; job += kNT) {
+            const T* M;
+            T* dst;
+            int ldm, b = job;
+            bool scaled = false;
+            float sgn = 1.f;
+            if (b < 64) {
+                M = L.Aq; ldm = LDC; dst = out + C::O_AQT;
+            } else if (DELTA && b < 128) {
+                M = L.Tb; ldm = LDC; dst = out + C::O_TBT; b -= 64;
+            } else {
+                b -= DELTA ? 128 : 64;
+                ldm = LDQ; scaled = GATED;
+                if (b < NQB) {
+                    M = Qs; dst = out + C::O_QDT;
+                } else {
+                    M = Ks; dst = out + C::O_NKDT; b -= NQB; sgn = -1.f; scaled = true;
+                }
+            }
+            const int bc = 8 * (b >> 6) + (b & 7), br = (b & 63) >> 3;
+            bf16x8 rw[8];
 #pragma unroll
-        for (int i = 0; i < E; ++i) x[i] = to_f32(L.Aq[(m0 + i) * LDC + l]);
-        store(out + C::O_AQT + l * kC + m0, x);
-        if constexpr (DELTA) {
+            for (int i = 0; i < 8; ++i) rw[i] = *reinterpret_cast<const bf16x8*>(M + (8 * br + i) * ldm + 8 * bc);
+            float sc[8];
 #pragma unroll
-            for (int i = 0; i < E; ++i) x[i] = to_f32(L.Tb[(m0 + i) * LDC + l]);
-            store(out + C::O_TBT + l * kC + m0, x);
+            for (int i = 0; i < 8; ++i) sc[i] = sgn * gam[8 * br + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                bf16x8 w;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = scaled ? from_f32<T>(to_f32(rw[i][j]) * sc[i]) : rw[i][j];
+                *reinterpret_cast<bf16x8*>(dst + (8 * bc + j) * kC + 8 * br) = w;
+            }
         }
-    }
-    if constexpr (DELTA) {
+        if constexpr (DELTA) {
+            for (int v = tid; v < kC * kC / E; v += kNT) {
+                const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+                *reinterpret_cast<i4*>(out + C::O_TB + l * kC + m0) = *reinterpret_cast<const i4*>(L.Tb + l * LDC + m0);
+            }
+        }
+        // ->K = exp(G_C - G) K
+        for (int v = tid; v < kC * DK / E; v += kNT) {
+            const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
+            const float sv = GATED ? expf(G[kC - 1] - G[l]) : 1.f;
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Ks + l * LDQ + i0);
+            bf16x8 w;
+#pragma unroll
+            for (int i = 0; i < E; ++i) w[i] = from_f32<T>(to_f32(kr[i]) * sv);
+            *reinterpret_cast<bf16x8*>(out + C::O_KR + l * DK + i0) = w;
+        }
+    } else {
+        float x[E];
+        // A^T and Tb^T: row l holds column l of A / Tb
         for (int v = tid; v < kC * kC / E; v += kNT) {
             const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
-            *reinterpret_cast<i4*>(out + C::O_TB + l * kC + m0) = *reinterpret_cast<const i4*>(L.Tb + l * LDC + m0);
+    #pragma unroll
+            for (int i = 0; i < E; ++i) x[i] = to_f32(L.Aq[(m0 + i) * LDC + l]);
+            store(out + C::O_AQT + l * kC + m0, x);
+            if constexpr (DELTA) {
+    #pragma unroll
+                for (int i = 0; i < E; ++i) x[i] = to_f32(L.Tb[(m0 + i) * LDC + l]);
+                store(out + C::O_TBT + l * kC + m0, x);
+            }
         }
-    }
-    // ->K = exp(G_C - G) K
-    for (int v = tid; v < kC * DK / E; v += kNT) {
-        const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
-        const float s = GATED ? expf(G[kC - 1] - G[l]) : 1.f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) x[i] = to_f32(Ks[l * LDQ + i0 + i]) * s;
-        store(out + C::O_KR + l * DK + i0, x);
-    }
-    // <-Q^T and -<-K^T: row i holds key channel i over the chunk
-    for (int v = tid; v < DK * kC / E; v += kNT) {
-        const int i = v / (kC / E), m0 = (v % (kC / E)) * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = to_f32(Qs[(m0 + e) * LDQ + i]) * gam[m0 + e];
-        store(out + C::O_QDT + i * kC + m0, x);
         if constexpr (DELTA) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = -to_f32(Ks[(m0 + e) * LDQ + i]) * gam[m0 + e];
-            store(out + C::O_NKDT + i * kC + m0, x);
+            for (int v = tid; v < kC * kC / E; v += kNT) {
+                const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+                *reinterpret_cast<i4*>(out + C::O_TB + l * kC + m0) = *reinterpret_cast<const i4*>(L.Tb + l * LDC + m0);
+            }
+        }
+        // ->K = exp(G_C - G) K
+        for (int v = tid; v < kC * DK / E; v += kNT) {
+            const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
+            const float s = GATED ? expf(G[kC - 1] - G[l]) : 1.f;
+    #pragma unroll
+            for (int i = 0; i < E; ++i) x[i] = to_f32(Ks[l * LDQ + i0 + i]) * s;
+            store(out + C::O_KR + l * DK + i0, x);
+        }
+        // <-Q^T and -<-K^T: row i holds key channel i over the chunk
+        for (int v = tid; v < DK * kC / E; v += kNT) {
+            const int i = v / (kC / E), m0 = (v % (kC / E)) * E;
+    #pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = to_f32(Qs[(m0 + e) * LDQ + i]) * gam[m0 + e];
+            store(out + C::O_QDT + i * kC + m0, x);
+            if constexpr (DELTA) {
+    #pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = -to_f32(Ks[(m0 + e) * LDQ + i]) * gam[m0 + e];
+                store(out + C::O_NKDT + i * kC + m0, x);
+            }
         }
     }
     if (tid == 0) gC[bh * nchunks + r] = gam[kC - 1];
