@@ -429,9 +429,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
             lds_barrier();
         }
         for (int64_t r = 0; r < nchunks; ++r) {
-            // lane indices recomputed per step so the LDS addresses derived from
-            // them are not held in registers across the loop
-            const int ln = opaque(lane);
+            const int ln = lane;
             const int cl = ln & 15, g4 = 4 * (ln >> 4);
             const int sl = (int)(r % 3);
             const float* const gam = gamb[sl];
@@ -619,7 +617,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_pipe_kernel(
     // one step r (chunk r+1 prepared; a step past the last chunk does no work
     // but keeps the loop's accesses unconditional)
     auto step = [&](int64_t r, Pref& P) {
-        const int ln = opaque(lane);
+        const int ln = lane;
         const int64_t c = r + 1;
         const bool go = c < nchunks;
         const int iw = wave - 4;
