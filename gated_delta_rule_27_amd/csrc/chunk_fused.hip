@@ -645,6 +645,15 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         lds_barrier();
     };
 
+    // The lane index each role's chunk loop derives its LDS addresses from:
+    // the addresses stay in registers across chunks, except with the delta
+    // rule's state saving at dk = 128, whose registers are full (an opaque copy
+    // per chunk makes the compiler recompute them instead of spilling).
+    auto lane_id = [&]() {
+        if constexpr (DELTA && SAVE && DK == 128) return opaque(lane);
+        else return lane;
+    };
+
     if (wave < 4) {
         // ======== state waves: wave w owns value columns n0..n0+15 of the block and
         // keeps S[:, those columns] as ND result tiles S[db][rr] = S[16 db + g4 + rr][n0 + cl]
@@ -665,7 +674,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         wait_vmem_all();
         if constexpr (!DELTA) {
             auto pchunk = [&](int64_t r, i4 (&kr)[NQ], i4 (&vr)[NV]) {
-                const int ln = opaque(lane);
+                const int ln = lane_id();
                 const int cl = ln & 15, g4 = 4 * (ln >> 4);
                 prefix_stage(r, kr, vr);
                 lds_barrier();
@@ -686,9 +695,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         }
         for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
-            // lane indices recomputed per chunk so the LDS addresses derived from
-            // them are not held in registers across the loop
-            const int ln = opaque(lane);
+            const int ln = lane_id();
             const int cl = ln & 15, g4 = 4 * (ln >> 4);
             const float* const gam = gamb[r & 1];
             const float* const rho = rhob[r & 1];
@@ -875,7 +882,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
                 if constexpr (GATED) gv = g[bh * Tlen + (t < Tlen ? t : Tlen - 1)];
             };
             auto pchunk = [&](int64_t r, i4 (&kr)[NQ], i4 (&vr)[NV], T& gv) {
-                const int ln = opaque(lane);
+                const int ln = lane_id();
                 prefix_stage(r, kr, vr);
                 gate_scan(r, gv);
                 load_gate(r + 2, gv);
@@ -894,7 +901,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         if (re > rb) fetch_gate(rb * kC);
         for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
-            const int ln = opaque(lane);
+            const int ln = lane_id();
             const int g4 = 4 * (ln >> 4);
             float* const Gs = Gsb[r & 1];
             float* const bet = betb[r & 1];
@@ -934,7 +941,7 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         // of the off-diagonal blocks -------------------------------------------------
         for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
-            const int ln = opaque(lane);
+            const int ln = lane_id();
             const int g4 = 4 * (ln >> 4);
             const float* const Gs = Gsb[r & 1];
             const float* const bet = betb[r & 1];
@@ -961,17 +968,17 @@ __global__ __launch_bounds__(kNT, 1) void chunk_fused_kernel(
         if constexpr (!DELTA) {
             for (int64_t r = 0; r < rb; r += 2) {
                 prefix_stage(r, kreg, vreg);
-                prefix_other(opaque(lane));
+                prefix_other(lane_id());
                 if (r + 1 < rb) {
                     prefix_stage(r + 1, qreg, vreg2);
-                    prefix_other(opaque(lane));
+                    prefix_other(lane_id());
                 }
             }
             if (rb > 0) fetch(rb * kC);
         }
         for (int64_t r = rb; r < re; ++r) {
             const int64_t t0 = r * kC;
-            const int ln = opaque(lane);
+            const int ln = lane_id();
             const float* const Gs = Gsb[r & 1];
             const float* const bet = betb[r & 1];
             stage(t0);
