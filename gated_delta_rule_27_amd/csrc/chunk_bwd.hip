@@ -610,31 +610,74 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __r
     if constexpr (DELTA) tri_inverse<bf16>(Lm, Tm, Tb, bet, tid);
 
     bf16* out = ops + (bh * nchunks + r) * (int64_t)OSTRIDE;
-    auto store = [&](bf16* dst, const float* x) {
-        bf16 e[E];
-#pragma unroll
-        for (int i = 0; i < E; ++i) e[i] = from_f32<bf16>(x[i]);
-        i4 w;
-        __builtin_memcpy(&w, e, 16);
-        *reinterpret_cast<i4*>(dst) = w;
-    };
     auto copy_rows = [&](bf16* dst, const bf16* src) {
         for (int v = tid; v < kC * kC / E; v += kNT) {
             const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
             *reinterpret_cast<i4*>(dst + l * kC + m0) = *reinterpret_cast<const i4*>(src + l * LDC + m0);
         }
     };
-    float x[E];
-    // A^T and Tb^T: row l holds column l of A / Tb
-    for (int v = tid; v < kC * kC / E; v += kNT) {
-        const int l = v / (kC / E), m0 = (v % (kC / E)) * E;
+    // The transposed operands go out in 8x8 blocks, one per thread: eight
+    // 16-byte rows read from LDS, transposed (and scaled) in registers, eight
+    // 16-byte rows written.  Within a wave, lane = column block + 8 x row
+    // block of the source, so each 16-lane group of a row read covers 64
+    // distinct banks.  Blocks: A^T (64), Tb^T (64, delta), then <-Q^T with
+    // -<-K^T (8 dk/8; the two share their factors 2^(G[m][c])).
+    {
+        constexpr int NQB = 8 * (DK / 8);
+        constexpr int NB = 64 + (DELTA ? 64 : 0) + NQB;
+        for (int job = tid; job < NB; job += kNT) {
+            int b = job;
+            const bool qk = b >= (DELTA ? 128 : 64);
+            const bf16* M = Aq;
+            int ldm = LDC;
+            if (qk) {
+                b -= DELTA ? 128 : 64;
+                M = Qs;
+                ldm = LDQ;
+            } else if (b >= 64) {
+                b -= 64;
+                M = Tb;
+            }
+            const int bc = 8 * (b >> 6) + (b & 7), br = (b & 63) >> 3;
+            bf16x8 rw[8], kw[8];
 #pragma unroll
-        for (int i = 0; i < E; ++i) x[i] = to_f32(Aq[(m0 + i) * LDC + l]);
-        store(out + C::O_AQT + l * kC + m0, x);
-        if constexpr (DELTA) {
+            for (int i = 0; i < 8; ++i) rw[i] = *reinterpret_cast<const bf16x8*>(M + (8 * br + i) * ldm + 8 * bc);
+            if (!qk) {
+                bf16* dst = out + (M == Aq ? C::O_AQT : C::O_TBT);
 #pragma unroll
-            for (int i = 0; i < E; ++i) x[i] = to_f32(Tb[(m0 + i) * LDC + l]);
-            store(out + C::O_TBT + l * kC + m0, x);
+                for (int j = 0; j < 8; ++j) {
+                    bf16x8 w;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) w[i] = rw[i][j];
+                    *reinterpret_cast<bf16x8*>(dst + (8 * bc + j) * kC + 8 * br) = w;
+                }
+            } else {
+                float ef[8][8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float* gr = &Gf[(8 * br + i) * LDG + 8 * bc];
+                    const floatx4 a = *reinterpret_cast<const floatx4*>(gr);
+                    const floatx4 c = *reinterpret_cast<const floatx4*>(gr + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ef[i][j] = fast_exp2(a[j]);
+                        ef[i][j + 4] = fast_exp2(c[j]);
+                    }
+                    if constexpr (DELTA) kw[i] = *reinterpret_cast<const bf16x8*>(Ks + (8 * br + i) * LDQ + 8 * bc);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    bf16x8 w, wk;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        w[i] = from_f32<bf16>(to_f32(rw[i][j]) * ef[i][j]);
+                        if constexpr (DELTA) wk[i] = from_f32<bf16>(-to_f32(kw[i][j]) * ef[i][j]);
+                    }
+                    *reinterpret_cast<bf16x8*>(out + C::O_QDT + (8 * bc + j) * kC + 8 * br) = w;
+                    if constexpr (DELTA)
+                        *reinterpret_cast<bf16x8*>(out + C::O_NKDT + (8 * bc + j) * kC + 8 * br) = wk;
+                }
+            }
         }
     }
     if constexpr (DELTA) {
@@ -645,22 +688,18 @@ __global__ __launch_bounds__(kNT, 1) void bwd_ops_channel_kernel(const bf16* __r
     // ->K = 2^(G_C - G) . K, per channel
     for (int v = tid; v < kC * DK / E; v += kNT) {
         const int l = v / (DK / E), i0 = (v % (DK / E)) * E;
+        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Ks + l * LDQ + i0);
+        const float* gl = &Gf[l * LDG + i0];
+        const float* gc = &Gf[(kC - 1) * LDG + i0];
+        float gv[8], cv[8];
+        *reinterpret_cast<floatx4*>(gv) = *reinterpret_cast<const floatx4*>(gl);
+        *reinterpret_cast<floatx4*>(gv + 4) = *reinterpret_cast<const floatx4*>(gl + 4);
+        *reinterpret_cast<floatx4*>(cv) = *reinterpret_cast<const floatx4*>(gc);
+        *reinterpret_cast<floatx4*>(cv + 4) = *reinterpret_cast<const floatx4*>(gc + 4);
+        bf16x8 w;
 #pragma unroll
-        for (int i = 0; i < E; ++i)
-            x[i] = to_f32(Ks[l * LDQ + i0 + i]) * fast_exp2(Gf[(kC - 1) * LDG + i0 + i] - Gf[l * LDG + i0 + i]);
-        store(out + C::O_KR + l * DK + i0, x);
-    }
-    // <-Q^T and -<-K^T: row i holds key channel i over the chunk
-    for (int v = tid; v < DK * kC / E; v += kNT) {
-        const int i = v / (kC / E), m0 = (v % (kC / E)) * E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = to_f32(Qs[(m0 + e) * LDQ + i]) * fast_exp2(Gf[(m0 + e) * LDG + i]);
-        store(out + C::O_QDT + i * kC + m0, x);
-        if constexpr (DELTA) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = -to_f32(Ks[(m0 + e) * LDQ + i]) * fast_exp2(Gf[(m0 + e) * LDG + i]);
-            store(out + C::O_NKDT + i * kC + m0, x);
-        }
+        for (int i = 0; i < E; ++i) w[i] = from_f32<bf16>(to_f32(kr[i]) * fast_exp2(cv[i] - gv[i]));
+        *reinterpret_cast<bf16x8*>(out + C::O_KR + l * DK + i0) = w;
     }
     if (tid < DK) gC[(bh * nchunks + r) * DK + tid] = fast_exp2(Gf[(kC - 1) * LDG + tid]);
 }
