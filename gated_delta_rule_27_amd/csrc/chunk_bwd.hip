@@ -61,10 +61,15 @@ template <typename T> using F16 = typename Frag16<T>::type;
 // (x0 + l%16, k0 + 4(l/16) + r), r = 0..3, of a matrix whose element (x, k) is
 // stored at P[x*ld + k] (frag_xk, one vector read) or at P[k*ld + x] (frag_kx).
 // x is the output row for an A operand and the output column for a B operand.
+// frag_xk reads through a volatile pointer of the LDS address space so that
+// each read stays one ds_read_b64: the compiler would otherwise merge two reads
+// from one base into a ds_read2_b64, which on gfx950 serves 16 lanes per clock
+// over 32 banks and takes four times the LDS cycles of one ds_read_b64.
 template <typename T>
 __device__ __forceinline__ F16<T> frag_xk(const T* P, int ld, int x0, int k0, int lane)
 {
-    return *reinterpret_cast<const F16<T>*>(P + (x0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+    typedef const volatile __attribute__((address_space(3))) F16<T>* LP;
+    return *(LP)(P + (x0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
 }
 
 template <typename T>

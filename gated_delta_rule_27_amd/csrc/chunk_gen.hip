@@ -54,6 +54,19 @@ namespace linattn {
 
 namespace {
 
+// A K = 16 fragment read as frag16_lds (mfma.h), through a volatile pointer of
+// the LDS address space, so that every 8-byte read stays one ds_read_b64: two
+// reads from one base register would otherwise be merged into a ds_read2_b64,
+// which on gfx950 serves 16 lanes per clock over 32 banks and takes 8 LDS
+// cycles, against 2 cycles (32 lanes per clock over 64 banks) for each
+// ds_read_b64 (lane-group probe, peak/lds_banks.hip).
+template <typename T>
+__device__ __forceinline__ typename Frag16<T>::type frag16_lds_sep(const T* M, int ld, int lane)
+{
+    typedef const volatile __attribute__((address_space(3))) typename Frag16<T>::type* LP;
+    return *(LP)(M + (lane & 15) * ld + 4 * (lane >> 4));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 // waves of the intra-chunk kernel: 8 at C = 128, whose LDS leaves one
 // workgroup per CU, else 4
@@ -501,14 +514,14 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
                 if constexpr (DELTA) {
                     floatx4 P = zero4();
 #pragma unroll
-                    for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_lds(st + G::W + 16 * db, G::LDK, ln), Sf[db], P);
+                    for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_lds_sep(st + G::W + 16 * db, G::LDK, ln), Sf[db], P);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
                 }
                 const F zf = frag16_acc<T>(Z);
 #pragma unroll
                 for (int db = 0; db < ND; ++db)
-                    dS[db] = mma16<T>(frag16_lds(st + G::KR + 16 * db * G::LDT, G::LDT, ln), zf, dS[db]);
+                    dS[db] = mma16<T>(frag16_lds_sep(st + G::KR + 16 * db * G::LDT, G::LDT, ln), zf, dS[db]);
                 if (li == NB - 1) {
 #pragma unroll
                     for (int db = 0; db < ND; ++db) {
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
                 if constexpr (DELTA) {
                     floatx4 P = zero4();
 #pragma unroll
-                    for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_lds(st + G::W + 16 * db, G::LDK, ln), Sf[db], P);
+                    for (int db = 0; db < ND; ++db) P = mma16<T>(frag16_lds_sep(st + G::W + 16 * db, G::LDK, ln), Sf[db], P);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) Z[rr] -= P[rr];
                 }
@@ -550,13 +563,13 @@ __global__ __launch_bounds__(512, 1) void gen_chain_kernel(
                 // c1: O = <-Q S_r + sum_{mj <= li} Aq(li, mj) Z_mj
                 floatx4 O = zero4();
 #pragma unroll
-                for (int db = 0; db < ND; ++db) O = mma16<T>(frag16_lds(st + G::Q + 16 * db, G::LDK, ln), Sf[db], O);
+                for (int db = 0; db < ND; ++db) O = mma16<T>(frag16_lds_sep(st + G::Q + 16 * db, G::LDK, ln), Sf[db], O);
 #pragma unroll
-                for (int mj = 0; mj <= li; ++mj) O = mma16<T>(frag16_lds(st + G::A + 16 * mj, G::LDA, ln), Zf[mj], O);
+                for (int mj = 0; mj <= li; ++mj) O = mma16<T>(frag16_lds_sep(st + G::A + 16 * mj, G::LDA, ln), Zf[mj], O);
                 // ->K_li^T Z_li
 #pragma unroll
                 for (int db = 0; db < ND; ++db)
-                    dS[db] = mma16<T>(frag16_lds(st + G::KR + 16 * db * G::LDT, G::LDT, ln), Zf[li], dS[db]);
+                    dS[db] = mma16<T>(frag16_lds_sep(st + G::KR + 16 * db * G::LDT, G::LDT, ln), Zf[li], dS[db]);
                 if (li == NB - 1) {
                     // S_{r+1} = Diag(2^(G_{C-1})) S_r + ->K^T Z
 #pragma unroll
