@@ -578,7 +578,7 @@ def main():
         elif name == "cfg4fp32":
             others.append(time_chunk(la, syn, syn.CFG4.with_(dtype="fp32", T=65536), dev, steps=3, warmup=2))
         elif name == "cfg2norm":
-            others.append(time_normalized(la, syn, syn.CFG2, dev, steps=10))
+            others.append(time_normalized(la, syn, syn.CFG2, dev, steps=50, warmup=100))
         elif name == "cfg3bwd":
             others.append(time_backward(la, syn, syn.CFG3, dev, steps=5))
         elif name == "cfg4bwd":
@@ -587,7 +587,9 @@ def main():
             others.append(time_deltaproduct_bwd(la, syn, syn.GDP2, dev, steps=5))
         else:
             oc = {"cfg2": syn.CFG2, "cfg3b": syn.CFG3B, "cfg4": syn.CFG4}[name]
-            others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 50))
+            # the short workloads get 100 untimed steps, so the clocks have ramped
+            others.append(time_chunk(la, syn, oc, dev, steps=3 if name == "cfg4" else 50,
+                                     warmup=20 if name == "cfg4" else 100))
         print(f"bench: {name} done ({others[-1]['ms_per_step']} ms per step)", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
