@@ -35,6 +35,8 @@
 // The 16x16 products read their operands from LDS in either orientation
 // (tile<>): a product of this pass has several operand orientations, and every
 // matrix is kept once.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -730,7 +732,7 @@ __device__ __forceinline__ int dstate_offset(int i, int j, int dk)
 // A^T, Tb^T, ->K and dO^T (dO^T double-buffered, phase 2 reads it) and copy
 // the dS of phase 1 to dstates.
 // ============================================================================
-template <typename T, int DK, int RULE, bool CHAN>
+template <typename T, int DK, int RULE, bool CHAN, int VB = 64>
 __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__ dout, const T* __restrict__ ops,
                                                            int64_t ostride, const float* __restrict__ gC,
                                                            const float* dsT, T* __restrict__ dstates, float* ds0,
@@ -742,7 +744,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
     constexpr int NH = 256;                            // helper threads
     constexpr int NA = kC * kC / E / NH;               // [C][C] vectors per helper thread
     constexpr int NK = kC * DK / E / NH;               // [C][dk] / [dk][C]
-    constexpr int NO = kC * 64 / E / NH;               // dO block
+    constexpr int NO = kC * VB / E / NH;               // dO block
+    static_assert(VB == 64 || VB == 32, "value block of 64 or 32 columns");
     static_assert(NA >= 1 && NK >= 1 && NO >= 1, "staging split");
 
     __shared__ __align__(16) T AqT[kC * LDC];
@@ -756,7 +759,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nvb = DV / 64;
+    const int nvb = DV / VB;
     // the value blocks of one head read the same chunk operands: dispatch puts
     // workgroup i on XCD i mod 8, so consecutive logical blocks are spread to
     // land on one XCD (and its L2)
@@ -765,10 +768,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
     const int64_t bh = blk / nvb;
     const int vb = blk % nvb;
 
-    if (wave < 4) {
+    if (wave < VB / 16) {
         const int n0 = 16 * wave;
         const int cl = lane & 15, g4 = 4 * (lane >> 4);
-        const int64_t col = (int64_t)vb * 64 + n0 + cl;
+        const int64_t col = (int64_t)vb * VB + n0 + cl;
         floatx4 dS[ND];
 #pragma unroll
         for (int db = 0; db < ND; ++db)
@@ -903,6 +906,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) ds0[(bh * DK + 16 * db + g4 + rr) * DV + col] = dS[db][rr];
         }
+    } else if (wave < 4) {
+        // a 32-column block has two state waves: waves 2 and 3 keep the
+        // barrier schedule of the state waves' loop (two per chunk) and idle
+        __syncthreads();
+        for (int64_t c = nchunks - 1; c >= 0; --c) {
+            lds_barrier();
+            lds_barrier();
+        }
     } else {
         const int ht = tid - 256;
         // The operands of one chunk in registers: group 1 (A^T, Tb^T, ->K, dO
@@ -936,7 +947,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
                 const int row = e % kC, cc = (e / kC) * E;
                 const int64_t t = c * kC + row;
                 const int64_t tr = t < Tlen ? t : Tlen - 1;
-                const i4 x = *reinterpret_cast<const i4*>(dout + (bh * Tlen + tr) * DV + vb * 64 + cc);
+                const i4 x = *reinterpret_cast<const i4*>(dout + (bh * Tlen + tr) * DV + vb * VB + cc);
                 R.ro[p] = t < Tlen ? x : i4{0, 0, 0, 0};
             }
             if constexpr (CHAN) {
@@ -996,14 +1007,14 @@ __global__ __launch_bounds__(kNT, 1) void bwd_chain_kernel(const T* __restrict__
         };
         // dS of chunk c from LDS to HBM, in the 16-column blocked layout
         auto copy_ds = [&](int64_t c) {
-            constexpr int VR = 64 / E, ND2 = DK * VR / NH;
+            constexpr int VR = VB / E, ND2 = DK * VR / NH;
             static_assert(ND2 * NH == DK * VR, "dS copy split");
             T* base = dstates + (bh * nchunks + c) * DK * DV;
 #pragma unroll
             for (int p = 0; p < ND2; ++p) {
                 const int e = p * NH + ht;
                 const int row = e / VR, col = (e % VR) * E;
-                *reinterpret_cast<i4*>(base + dstate_offset(row, vb * 64 + col, DK)) =
+                *reinterpret_cast<i4*>(base + dstate_offset(row, vb * VB + col, DK)) =
                     *reinterpret_cast<const i4*>(dSs + row * LDC + col);
             }
         };
@@ -2444,6 +2455,20 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_channel_kernel(
     }
 }
 
+// The reverse state pass runs one workgroup per (b, h, value block); blocks of
+// 32 value columns (two state waves) instead of 64 when the 64-column blocks
+// would leave compute units idle (bf16 tokens; LINATTN_CHAIN_VB=32 or 64 fixes
+// the width for tests).
+inline bool chain_vb32(int64_t bh, int dv)
+{
+    if (const char* e = getenv("LINATTN_CHAIN_VB")) return atoi(e) == 32;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    return bh * (dv / 64) < ncu;
+}
+
 template <typename T, int DK, int RULE, int GATE>
 hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
 {
@@ -2459,11 +2484,20 @@ hipError_t launch_bwd_t(const ChunkBwdProblem& p, hipStream_t s)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE, false>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0, s,
-                       static_cast<const T*>(p.dout), static_cast<const T*>(p.ops),
-                       (int64_t)BwdCfg<T, DK>::OPS, p.gC, p.dsT,
-                       static_cast<T*>(p.dstates), p.ds0,
-                       p.T, nchunks, p.dv);
+    bool vb32 = false;
+    if constexpr (sizeof(T) == 2) {
+        vb32 = chain_vb32(bh, p.dv);
+        if (vb32)
+            hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE, false, 32>), dim3((unsigned)(bh * (p.dv / 32))),
+                               dim3(kNT), 0, s, static_cast<const T*>(p.dout), static_cast<const T*>(p.ops),
+                               (int64_t)BwdCfg<T, DK>::OPS, p.gC, p.dsT, static_cast<T*>(p.dstates), p.ds0, p.T,
+                               nchunks, p.dv);
+    }
+    if (!vb32)
+        hipLaunchKernelGGL((bwd_chain_kernel<T, DK, RULE, false>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0,
+                           s, static_cast<const T*>(p.dout), static_cast<const T*>(p.ops),
+                           (int64_t)BwdCfg<T, DK>::OPS, p.gC, p.dsT, static_cast<T*>(p.dstates), p.ds0, p.T,
+                           nchunks, p.dv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || bh * nchunks == 0) return e;
     if constexpr (sizeof(T) == 2)
@@ -2499,10 +2533,16 @@ hipError_t launch_bwd_channel(const ChunkBwdProblem& p, hipStream_t s)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_chain_kernel<bf16, DK, RULE, true>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT), 0,
-                       s, static_cast<const bf16*>(p.dout), static_cast<const bf16*>(p.ops),
-                       (int64_t)(C::OPS + 2 * kC * kC), p.gC, p.dsT, static_cast<bf16*>(p.dstates), p.ds0, p.T,
-                       nchunks, p.dv);
+    if (chain_vb32(bh, p.dv))
+        hipLaunchKernelGGL((bwd_chain_kernel<bf16, DK, RULE, true, 32>), dim3((unsigned)(bh * (p.dv / 32))),
+                           dim3(kNT), 0, s, static_cast<const bf16*>(p.dout), static_cast<const bf16*>(p.ops),
+                           (int64_t)(C::OPS + 2 * kC * kC), p.gC, p.dsT, static_cast<bf16*>(p.dstates), p.ds0,
+                           p.T, nchunks, p.dv);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<bf16, DK, RULE, true>), dim3((unsigned)(bh * (p.dv / 64))), dim3(kNT),
+                           0, s, static_cast<const bf16*>(p.dout), static_cast<const bf16*>(p.ops),
+                           (int64_t)(C::OPS + 2 * kC * kC), p.gC, p.dsT, static_cast<bf16*>(p.dstates), p.ds0,
+                           p.T, nchunks, p.dv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || bh * nchunks == 0) return e;
     hipLaunchKernelGGL((bwd_grad_channel_kernel<DK, RULE>), dim3((unsigned)(bh * nchunks)), dim3(kNT), 0, s, q, k,

@@ -262,6 +262,23 @@ def test_channel_many_heads_wide_blocks(dk, dv):
             assert torch.equal(a[n], b[n]), f"{n}: saved and recomputed states differ"
 
 
+@pytest.mark.parametrize("gate,dk,dv,rule", [("scalar", 128, 128, "delta"), ("none", 64, 128, "add"),
+                                             ("channel", 128, 128, "delta"), ("channel", 64, 64, "add")])
+def test_chain_value_block_widths_agree(monkeypatch, gate, dk, dv, rule):
+    # the reverse state pass in 32-column value blocks (two state waves; chosen
+    # when 64-column blocks leave CUs idle) gives the same bits as in 64-column
+    # blocks, and both match the oracle
+    case = syn.Case("bwd_vb", 1, 3, 200, dk, dv, rule, gate, "bf16", gate_scale=0.25, s0_std=0.2,
+                    case_id=160)
+    monkeypatch.setenv("LINATTN_CHAIN_VB", "64")
+    a = check_bwd(case)
+    monkeypatch.setenv("LINATTN_CHAIN_VB", "32")
+    b = check_bwd(case)
+    for n in NAMES:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), f"{n}: 32- and 64-column value blocks differ"
+
+
 def test_channel_deterministic():
     case = syn.Case("bwd_chan_det", 1, 4, 300, 128, 128, "delta", "channel", "bf16", gate_scale=0.2,
                     s0_std=0.2, case_id=151)
