@@ -420,10 +420,11 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 // LDS tile at the top of every chunk, and the helper waves copy it to
 // states[b, h, r] ([dk][dv], bf16) during phase 2 with 16-byte stores.
 //
-// Segments (segments.h, not with SAVE): a workgroup may own chunks [rb, re) of
-// its head; it first runs the state update alone over chunks [0, rb) (phase 1
-// without O, phase 2 without O; the helpers stage neither Qd nor Aq), then its
-// own chunks as usual.
+// Segments (segments.h): a workgroup may own chunks [rb, re) of its head; it
+// first runs the state update alone over chunks [0, rb) (phase 1 without O,
+// phase 2 without O; the helpers stage neither Qd nor Aq), then its own chunks
+// as usual.  With SAVE each segment writes the states of its own chunks; the
+// prefix pass runs the same update code, so they equal one segment's bit for bit.
 template <int DK, int RULE, int DVB, bool SAVE>
 __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const bf16* __restrict__ v, const unsigned char* __restrict__ ws, const float* s0,
@@ -461,8 +462,8 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
     const int64_t bh = blk / nunit;
     const int vb = (blk % nunit) % nvb;
     const int sg = (blk % nunit) / nvb;
-    const int64_t rb = SAVE ? 0 : seg.c[sg], re = SAVE ? nchunks : seg.c[sg + 1];
-    const bool last_seg = SAVE || sg == seg.n - 1;
+    const int64_t rb = seg.c[sg], re = seg.c[sg + 1];
+    const bool last_seg = sg == seg.n - 1;
 
     if (wave < NSW) {
         // ======== state waves ============================================================
@@ -478,7 +479,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
         }
         wait_vmem_all();
         __syncthreads();                          // group 1 of the first chunk staged
-        if constexpr (!SAVE) {
+        {
             // prefix pass: S_{r+1} = Diag(gC) S_r + Kr^T Tb (V - Kd S_r) over chunks [0, rb)
             for (int64_t c = 0; c < rb; ++c) {
                 const int ln = opaque(lane);
@@ -735,7 +736,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             load1(rb + 1 < last ? rb + 1 : last, kFull);
         }
         __syncthreads();                          // group 1 of the first chunk staged
-        if constexpr (!SAVE) {
+        {
             for (int64_t c = 0; c < rb; ++c) {
                 stage2(kPrefix);
                 load2(c + 1 < plast ? c + 1 : plast, kPrefix);
@@ -806,11 +807,11 @@ hipError_t launch_split(const ChunkProblem& p, bf16* states, hipStream_t s)
     // (fewer 64-column blocks than CUs) the blocks are 32 columns wide, which
     // doubles the number of independent chains; each staged tile is then read
     // by twice as many workgroups (mostly from L2).
-    // Without saved states, a grid that still leaves CUs idle splits each
-    // head's chunks into segments (segments.h).
+    // A grid that still leaves CUs idle splits each head's chunks into
+    // segments (segments.h).
     const bool narrow = bh * (p.dv / 64) < ncu;
     const int64_t nblocks1 = bh * (p.dv / (narrow ? 32 : 64));
-    const SegSplit sp = seg_split(nchunks, nblocks1, states == nullptr, p.s0, p.s_final,
+    const SegSplit sp = seg_split(nchunks, nblocks1, true, p.s0, p.s_final,
                                   (size_t)bh * p.dk * p.dv * sizeof(float), kChainPrefixCost);
     const int nblocks = (int)(nblocks1 * sp.n);
     const dim3 grid((unsigned)nblocks);

@@ -225,6 +225,29 @@ def test_chain_segments_raw_projections(monkeypatch):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("nseg", [2, 4])
+@pytest.mark.parametrize("rule", ["add", "delta"])
+def test_chain_segments_saved_states(monkeypatch, rule, nseg):
+    # the state-keeping forward of the training path: every segment saves the
+    # states of its own chunks, so output, final state and all saved states
+    # equal the one-segment run bit for bit (ragged last chunk, s0 given)
+    import gated_delta_rule_27_amd as la
+    case = syn.Case("segchsave", 1, 2, 1250, 128, 128, rule, "channel", "bf16", gate_scale=1 / 16, s0_std=0.3,
+                    case_id=173)
+    x = syn.chunk_inputs(case)
+    d = lambda a: dev(a, case.dtype)
+    args = (d(x["q"]), d(x["k"]), d(x["v"]), d(x["g"]), d(x["beta"]), dev_state(x["s0"]))
+    monkeypatch.setenv("LINATTN_SEGMENTS", str(nseg))
+    on, sn, stn = la.chunk_fwd_save(*args, rule=rule, gate="channel")
+    monkeypatch.setenv("LINATTN_SEGMENTS", "1")
+    o1, s1, st1 = la.chunk_fwd_save(*args, rule=rule, gate="channel")
+    torch.cuda.synchronize()
+    note(f"[chain segments save] rule={rule} nseg={nseg}")
+    assert torch.equal(on, o1) and torch.equal(sn, s1) and torch.equal(stn, st1)
+    oref, sref = oracle_chunk(case, x, x["s0"])
+    assert rel_l2(host(on), oref) <= TOL["bf16"] and rel_l2(host(sn), sref) <= TOL["bf16"]
+
+
 def test_chain_segments_state_in_place():
     import gated_delta_rule_27_amd as la
     case = syn.Case("segchinplace", 1, 2, 1200, 128, 128, "delta", "channel", "bf16", gate_scale=1 / 16,
