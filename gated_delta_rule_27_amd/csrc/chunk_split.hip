@@ -402,7 +402,8 @@ __global__ __launch_bounds__(512, 1) void chunk_intra_channel_kernel(
 //     S[:, those columns] (fp32) as dk/16 MFMA result tiles; every product
 //     takes S, R or Z straight from registers (mfma.h), paired into K = 32
 //     products whose LDS operands are single 16-byte reads (pcol order, as
-//     kernel A stores them).
+//     kernel A stores them, with the conflict-free swizzle of mfma.h applied
+//     when the helpers stage the rows into LDS).
 //   * the four helper waves after them move everything between HBM and LDS: the chunk's
 //     staged operands, loaded into registers one chunk ahead, and the output.
 //     The state waves touch no global memory inside the loop.
@@ -498,7 +499,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                         const auto sp = pair_regs<bf16>(S[db], S[db + 1]);
 #pragma unroll
                         for (int li = 0; li < NL; ++li)
-                            P[li] = mma_pair<bf16>(pair_lds(&Kd[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
+                            P[li] = mma_pair<bf16>(pair_lds_sw(&Kd[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
                     }
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
@@ -507,8 +508,8 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                     const auto r01 = pair_regs<bf16>(R[0], R[1]), r23 = pair_regs<bf16>(R[2], R[3]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li) {
-                        Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
-                        if (li >= 2) Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                        Z[li] = mma_pair<bf16>(pair_lds_sw(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
+                        if (li >= 2) Z[li] = mma_pair<bf16>(pair_lds_sw(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
                     }
                 } else {
 #pragma unroll
@@ -521,8 +522,8 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                     const floatx4 gd = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gd[rr];
-                    S[db] = mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC + 32], LDC, ln), z23,
-                                           mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC], LDC, ln), z01, S[db]));
+                    S[db] = mma_pair<bf16>(pair_lds_sw(&KrT[16 * db * LDC + 32], LDC, ln), z23,
+                                           mma_pair<bf16>(pair_lds_sw(&KrT[16 * db * LDC], LDC, ln), z01, S[db]));
                 }
                 lds_barrier();
             }
@@ -550,7 +551,7 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                     const auto sp = pair_regs<bf16>(S[db], S[db + 1]);
 #pragma unroll
                     for (int li = 0; li < NL; ++li)
-                        P[li] = mma_pair<bf16>(pair_lds(&Kd[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
+                        P[li] = mma_pair<bf16>(pair_lds_sw(&Kd[16 * li * LDQ + 16 * db], LDQ, ln), sp, P[li]);
                 }
 #pragma unroll
                 for (int li = 0; li < NL; ++li)
@@ -561,8 +562,8 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                 const auto r01 = pair_regs<bf16>(R[0], R[1]), r23 = pair_regs<bf16>(R[2], R[3]);
 #pragma unroll
                 for (int li = 0; li < NL; ++li) {
-                    Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
-                    if (li >= 2) Z[li] = mma_pair<bf16>(pair_lds(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
+                    Z[li] = mma_pair<bf16>(pair_lds_sw(&Tb[16 * li * LDC], LDC, ln), r01, zero4());
+                    if (li >= 2) Z[li] = mma_pair<bf16>(pair_lds_sw(&Tb[16 * li * LDC + 32], LDC, ln), r23, Z[li]);
                 }
             } else {
 #pragma unroll
@@ -575,15 +576,15 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                 const auto sp = pair_regs<bf16>(S[db], S[db + 1]);
 #pragma unroll
                 for (int li = 0; li < NL; ++li)
-                    Ot[li] = mma_pair<bf16>(sp, pair_lds(&Qd[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
+                    Ot[li] = mma_pair<bf16>(sp, pair_lds_sw(&Qd[16 * li * LDQ + 16 * db], LDQ, ln), Ot[li]);
             }
             lds_barrier();
             // ---- phase 2: O^T += Z^T Aq^T ; S_{r+1} = Diag(gC) S_r + Kr^T Z ------------
             const auto z01 = pair_regs<bf16>(Z[0], Z[1]), z23 = pair_regs<bf16>(Z[2], Z[3]);
 #pragma unroll
             for (int lj = 0; lj < NL; ++lj) {
-                Ot[lj] = mma_pair<bf16>(z01, pair_lds(&Aq[16 * lj * LDC], LDC, ln), Ot[lj]);
-                if (lj >= 2) Ot[lj] = mma_pair<bf16>(z23, pair_lds(&Aq[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
+                Ot[lj] = mma_pair<bf16>(z01, pair_lds_sw(&Aq[16 * lj * LDC], LDC, ln), Ot[lj]);
+                if (lj >= 2) Ot[lj] = mma_pair<bf16>(z23, pair_lds_sw(&Aq[16 * lj * LDC + 32], LDC, ln), Ot[lj]);
             }
 #pragma unroll
             for (int lj = 0; lj < NL; ++lj) store_tile_t(&Os[16 * lj * LDV + n0], LDV, Ot[lj], ln);
@@ -592,8 +593,8 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
                 const floatx4 gd = *reinterpret_cast<const floatx4*>(&gC[16 * db + g4]);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) S[db][rr] *= gd[rr];
-                S[db] = mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC + 32], LDC, ln), z23,
-                                       mma_pair<bf16>(pair_lds(&KrT[16 * db * LDC], LDC, ln), z01, S[db]));
+                S[db] = mma_pair<bf16>(pair_lds_sw(&KrT[16 * db * LDC + 32], LDC, ln), z23,
+                                       mma_pair<bf16>(pair_lds_sw(&KrT[16 * db * LDC], LDC, ln), z01, S[db]));
             }
             lds_barrier();
         }
@@ -642,14 +643,15 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             for (int p = 0; p < VQ; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / DK, col = e % DK;
-                if constexpr (FULL) *reinterpret_cast<i4*>(&Qd[row * LDQ + col]) = rqd[p];
-                if constexpr (DELTA) *reinterpret_cast<i4*>(&Kd[row * LDQ + col]) = rkd[p];
+                const int cs = col ^ swz_x(row);
+                if constexpr (FULL) *reinterpret_cast<i4*>(&Qd[row * LDQ + cs]) = rqd[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(&Kd[row * LDQ + cs]) = rkd[p];
             }
 #pragma unroll
             for (int p = 0; p < VA; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / kC, col = e % kC;
-                if constexpr (DELTA) *reinterpret_cast<i4*>(&Tb[row * LDC + col]) = rtb[p];
+                if constexpr (DELTA) *reinterpret_cast<i4*>(&Tb[row * LDC + (col ^ swz_x(row))]) = rtb[p];
             }
 #pragma unroll
             for (int p = 0; p < VV; ++p) {
@@ -680,13 +682,13 @@ __global__ __launch_bounds__((DVB / 16 + 4) * 64, 1) void chunk_chain_kernel(
             for (int p = 0; p < VA; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / kC, col = e % kC;
-                if constexpr (FULL) *reinterpret_cast<i4*>(&Aq[row * LDC + col]) = raq[p];
+                if constexpr (FULL) *reinterpret_cast<i4*>(&Aq[row * LDC + (col ^ swz_x(row))]) = raq[p];
             }
 #pragma unroll
             for (int p = 0; p < VK; ++p) {
                 const int e = (p * NH + ht) * 8;
                 const int row = e / kC, col = e % kC;
-                *reinterpret_cast<i4*>(&KrT[row * LDC + col]) = rkr[p];
+                *reinterpret_cast<i4*>(&KrT[row * LDC + (col ^ swz_x(row))]) = rkr[p];
             }
             if (ht < DK / 4) *reinterpret_cast<i4*>(&gC[4 * ht]) = rg;
         };
