@@ -184,7 +184,7 @@ __device__ __forceinline__ void load_col16(float* x, const bf16* base, int ld, i
 // triangular L in LDS (Tm must hold zeros above its diagonal blocks); every
 // thread of the workgroup calls this, the results are in LDS on return.
 template <typename T>
-__device__ void tri_inverse(const T* Lm, T* Tm, T* Tb, const float* bet, int tid)
+__device__ __forceinline__ void tri_inverse(const T* Lm, T* Tm, T* Tb, const float* bet, int tid)
 {
     using C = BwdCfg<T, 64>;
     constexpr int LDC = C::LDC;
