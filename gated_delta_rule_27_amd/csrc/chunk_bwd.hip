@@ -77,13 +77,29 @@ __device__ __forceinline__ F16<T> frag_xk(const T* P, int ld, int x0, int k0, in
 template <typename T>
 __device__ __forceinline__ F16<T> frag_kx(const T* P, int ld, int x0, int k0, int lane)
 {
-    const T* p = P + (k0 + 4 * (lane >> 4)) * ld + x0 + (lane & 15);
-    F16<T> f;
-    f[0] = p[0];
-    f[1] = p[ld];
-    f[2] = p[2 * ld];
-    f[3] = p[3 * ld];
-    return f;
+    if constexpr (sizeof(T) == 2) {
+        // gfx950's LDS transpose read: each 16-lane group g reads the 4 x 16
+        // block at rows k0 + 4g .. k0 + 4g + 3, columns x0 .. x0 + 15, lane
+        // 4j + c of the group supplying the address of row j, columns 4c ..
+        // 4c + 3 (8 bytes), and lane i of the group receives column i of the
+        // four rows: the fragment in one read instead of four 2-byte reads
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s* LP;
+        const int w = lane & 15;
+        const T* p = P + (k0 + 4 * (lane >> 4) + (w >> 2)) * ld + x0 + 4 * (w & 3);
+        const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LP)(T*)p);
+        F16<T> f;
+        __builtin_memcpy(&f, &x, 8);
+        return f;
+    } else {
+        const T* p = P + (k0 + 4 * (lane >> 4)) * ld + x0 + (lane & 15);
+        F16<T> f;
+        f[0] = p[0];
+        f[1] = p[ld];
+        f[2] = p[2 * ld];
+        f[3] = p[3 * ld];
+        return f;
+    }
 }
 
 // acc += sum_{k in [kb, ke)} A(m0 + ., k) B(k, n0 + .) as a 16x16 result tile
