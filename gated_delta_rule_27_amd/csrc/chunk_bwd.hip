@@ -83,6 +83,8 @@ __device__ __forceinline__ F16<T> frag_kx(const T* P, int ld, int x0, int k0, in
         // 4j + c of the group supplying the address of row j, columns 4c ..
         // 4c + 3 (8 bytes), and lane i of the group receives column i of the
         // four rows: the fragment in one read instead of four 2-byte reads
+        // (each lane's 8 bytes must be aligned: ld and x0 are multiples of 4
+        // at every call)
         typedef short v4s __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) v4s* LP;
         const int w = lane & 15;
