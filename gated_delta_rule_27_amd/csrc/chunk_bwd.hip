@@ -1484,9 +1484,10 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
     constexpr int LDQ = C::LDQ, LDC = C::LDC, E = 8, J = 32, LDJ = J + 8;
     constexpr bool DELTA = RULE == kRuleDelta, GATED = GATE == kGateScalar;
     constexpr int NI = DK / 32;            // key-column tiles per wave (of dq, dk)
-    // value-block arrays of the loop (row-major and transposed copies), and the
-    // matrices of the final phase, in the same bytes
-    constexpr int LOOP_ELEMS = 5 * kC * LDJ + 2 * DK * LDJ + 3 * J * LDC + 2 * J * LDQ;
+    // value-block arrays of the loop (row-major: products that need them
+    // transposed read them with the LDS transpose read), and the matrices of
+    // the final phase, in the same bytes
+    constexpr int LOOP_ELEMS = 5 * kC * LDJ + 2 * DK * LDJ;
     constexpr int FIN_ELEMS = 5 * kC * LDC + 2 * DK * LDC;
     constexpr int REGION = 2 * (LOOP_ELEMS > FIN_ELEMS ? LOOP_ELEMS : FIN_ELEMS);
 
@@ -1514,11 +1515,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
     T* const dRs = dZs + kC * LDJ;
     T* const Ss = dRs + kC * LDJ;                   // [DK][LDJ]
     T* const dSs = Ss + DK * LDJ;
-    T* const dOT = dSs + DK * LDJ;                  // [J][LDC]
-    T* const RT = dOT + J * LDC;
-    T* const dZT = RT + J * LDC;
-    T* const ST = dZT + J * LDC;                    // [J][LDQ]
-    T* const dSnT = ST + J * LDQ;
     // final-phase arrays
     T* const Pm = reinterpret_cast<T*>(region);    // [C][LDC]
     T* const PT = Pm + kC * LDC;
@@ -1616,10 +1612,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
             if (i < kC * VR) {
                 *reinterpret_cast<i4*>(dOs + row * LDJ + c) = pdo[u];
                 *reinterpret_cast<i4*>(Zs + row * LDJ + c) = pv[u];
-                T x[E];
-                __builtin_memcpy(x, &pdo[u], 16);
-#pragma unroll
-                for (int e = 0; e < E; ++e) dOT[(c + e) * LDC + row] = x[e];
             }
         }
 #pragma unroll
@@ -1630,11 +1622,7 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
                 __builtin_memcpy(a, &ps[u], 16);
                 __builtin_memcpy(b, &pds[u], 16);
 #pragma unroll
-                for (int x = 0; x < E; ++x) {
-                    sdot += to_f32(a[x]) * to_f32(b[x]);
-                    ST[(c + x) * LDQ + row] = a[x];
-                    dSnT[(c + x) * LDQ + row] = b[x];
-                }
+                for (int x = 0; x < E; ++x) sdot += to_f32(a[x]) * to_f32(b[x]);
                 *reinterpret_cast<i4*>(Ss + row * LDJ + c) = ps[u];
                 *reinterpret_cast<i4*>(dSs + row * LDJ + c) = pds[u];
             }
@@ -1644,17 +1632,17 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
         // ---- step A: dZ = A^T dO + ->K dS ; R = V - <-K S_r ; d<-Q += dO S_r^T ----
         {
             const int lb = wave >> 1, jc = wave & 1;
-            const floatx4 a1 = tilek<T, true, true, kC>(zero4(), AqT, LDC, 16 * lb, dOT, LDC, 16 * jc, 0, lane);
+            const floatx4 a1 = tilek<T, true, false, kC>(zero4(), AqT, LDC, 16 * lb, dOs, LDJ, 16 * jc, 0, lane);
             // K dS and K S_r share their K fragments
             floatx4 a2 = zero4(), ks = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 32) {
                 const F16<T> a0 = frag_xk(Ks, LDQ, 16 * lb, k0, lane), a1f = frag_xk(Ks, LDQ, 16 * lb, k0 + 16, lane);
-                a2 = mma16x2<T>(a0, a1f, frag_xk(dSnT, LDQ, 16 * jc, k0, lane),
-                                frag_xk(dSnT, LDQ, 16 * jc, k0 + 16, lane), a2);
+                a2 = mma16x2<T>(a0, a1f, frag_kx(dSs, LDJ, 16 * jc, k0, lane),
+                                frag_kx(dSs, LDJ, 16 * jc, k0 + 16, lane), a2);
                 if constexpr (DELTA)
-                    ks = mma16x2<T>(a0, a1f, frag_xk(ST, LDQ, 16 * jc, k0, lane),
-                                    frag_xk(ST, LDQ, 16 * jc, k0 + 16, lane), ks);
+                    ks = mma16x2<T>(a0, a1f, frag_kx(Ss, LDJ, 16 * jc, k0, lane),
+                                    frag_kx(Ss, LDJ, 16 * jc, k0 + 16, lane), ks);
             }
             floatx4 dz;
 #pragma unroll
@@ -1663,7 +1651,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
                 dz[rr] = a1[rr] + (GATED ? expf(G[kC - 1] - G[l]) : 1.f) * a2[rr];
             }
             put(dZs, LDJ, 16 * lb, 16 * jc, dz, lane);
-            put_t(dZT, LDC, 16 * lb, 16 * jc, dz, lane);
             if constexpr (DELTA) {
                 floatx4 rv;
 #pragma unroll
@@ -1672,7 +1659,6 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
                     rv[rr] = to_f32(Zs[l * LDJ + 16 * jc + cl]) - gam[l] * ks[rr];
                 }
                 put(Rs, LDJ, 16 * lb, 16 * jc, rv, lane);
-                put_t(RT, LDC, 16 * lb, 16 * jc, rv, lane);
             } else {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -1688,8 +1674,8 @@ __global__ __launch_bounds__(kNT, 1) void bwd_grad_bf16_kernel(
         // ---- step B (delta): Z = Tb R ; dR = Tb^T dZ (= dv) ; dTb += dZ R^T ----
         if constexpr (DELTA) {
             const int lb = wave >> 1, jc = wave & 1;
-            const floatx4 z = tilek<T, true, true, kC>(zero4(), Tb, LDC, 16 * lb, RT, LDC, 16 * jc, 0, lane);
-            const floatx4 dr = tilek<T, true, true, kC>(zero4(), TbT, LDC, 16 * lb, dZT, LDC, 16 * jc, 0, lane);
+            const floatx4 z = tilek<T, true, false, kC>(zero4(), Tb, LDC, 16 * lb, Rs, LDJ, 16 * jc, 0, lane);
+            const floatx4 dr = tilek<T, true, false, kC>(zero4(), TbT, LDC, 16 * lb, dZs, LDJ, 16 * jc, 0, lane);
             put(Zs, LDJ, 16 * lb, 16 * jc, z, lane);
             put(dRs, LDJ, 16 * lb, 16 * jc, dr, lane);
 #pragma unroll
