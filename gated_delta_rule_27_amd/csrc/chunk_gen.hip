@@ -155,6 +155,53 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
     T* const Uw = reinterpret_cast<T*>(wc + L.u);
     const int64_t rowbase = bh * Tlen + t0;
 
+    // ---- token loads.  Thread tid owns the 4-element groups tid + j kGT of
+    // every staged [C][kKS] slice (row e / (kKS / 4), columns 4 (e % (kKS / 4))
+    // onwards).  Two register sets, A and B, hold the groups of q and k (and of
+    // the per-channel log-gate, or of v) of the next two slices: a set is
+    // refilled with the slice after next as soon as it has been staged, so each
+    // load has two slices' work to arrive (the first two the gate scan, those of
+    // the second pass over the key channels and of v the triangular solve).
+    constexpr int PE = C * kKS / 4;                  // 4-element groups of a slice
+    constexpr int PP = (PE + kGT - 1) / kGT;         // groups per thread
+    using R4 = typename Frag16<T>::type;             // four token values
+    struct Slice {
+        R4 q[PP], k[PP], g[CHAN ? PP : 1];
+    };
+    auto grp = [&](int j, int& row, int& cq) {
+        const int e = tid + j * kGT;
+        row = e / (kKS / 4);
+        cq = 4 * (e % (kKS / 4));
+        return PE % kGT == 0 || e < PE;
+    };
+    auto ld4 = [](const T* p) { return *reinterpret_cast<const R4*>(p); };
+    auto cvt4 = [](R4 x) { return floatx4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])}; };
+    // key channels sl kKS .. of q and k (and the log-gate); rows past the end
+    // read row 0 and are zeroed when staged
+    auto load_qk = [&](Slice& S, int sl) {
+#pragma unroll
+        for (int j = 0; j < PP; ++j) {
+            int row, cq;
+            if (grp(j, row, cq)) {
+                const int64_t off = (rowbase + (row < nrow ? row : 0)) * DK + sl * kKS + cq;
+                S.q[j] = ld4(q + off);
+                S.k[j] = ld4(k + off);
+                if constexpr (CHAN) S.g[j] = ld4(g + off);
+            }
+        }
+    };
+    // value columns vs kKS .. of v, into S.q
+    auto load_v = [&](Slice& S, int vs) {
+#pragma unroll
+        for (int j = 0; j < PP; ++j) {
+            int row, cq;
+            if (grp(j, row, cq)) S.q[j] = ld4(v + (rowbase + (row < nrow ? row : 0)) * DV + vs * kKS + cq);
+        }
+    };
+    Slice SA, SB;
+    load_qk(SA, 0);
+    load_qk(SB, 1);
+
     // ---- a1 (scalar gate) and beta: one wave, 64 rows at a time ------------------
     if (wave == 0) {
         float carry = 0.f;
@@ -198,20 +245,28 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
 
     // Stage key channels c0 .. c0 + kKS - 1 of q and k (and the per-channel
     // log-gate as its prefix within the chunk) into xs, ys (gs), fp32.
-    auto stage_qk = [&](int c0) {
+    auto stage_qk = [&](const Slice& S) {
         __syncthreads();
-        for (int e = tid; e < C * kKS / 4; e += kGT) {
-            const int row = e / (kKS / 4), cq = 4 * (e % (kKS / 4));
+#pragma unroll
+        for (int j = 0; j < PP; ++j) {
+            int row, cq;
+            if (!grp(j, row, cq)) continue;
             const bool ok = row < nrow;
-            const int64_t off = (rowbase + (ok ? row : 0)) * DK + c0 + cq;
-            const floatx4 qv = load4(q + off), kv = load4(k + off);
-            floatx4 gv = zero4();
-            if constexpr (CHAN) gv = load4(g + off);
+            const floatx4 qv = cvt4(S.q[j]), kv = cvt4(S.k[j]);
+            floatx4 xq, xk;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                xs[row * kLDS + cq + i] = ok ? mapqk(qv[i], rq[row]) : 0.f;
-                ys[row * kLDS + cq + i] = ok ? mapqk(kv[i], rk[row]) : 0.f;
-                if constexpr (CHAN) gs[row * kLDS + cq + i] = ok ? prep_gate(gv[i], prep) * kLog2e : 0.f;
+                xq[i] = ok ? mapqk(qv[i], rq[row]) : 0.f;
+                xk[i] = ok ? mapqk(kv[i], rk[row]) : 0.f;
+            }
+            *reinterpret_cast<floatx4*>(&xs[row * kLDS + cq]) = xq;
+            *reinterpret_cast<floatx4*>(&ys[row * kLDS + cq]) = xk;
+            if constexpr (CHAN) {
+                const floatx4 gv = cvt4(S.g[j]);
+                floatx4 xg;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xg[i] = ok ? prep_gate(gv[i], prep) * kLog2e : 0.f;
+                *reinterpret_cast<floatx4*>(&gs[row * kLDS + cq]) = xg;
             }
         }
         if constexpr (CHAN) {
@@ -243,46 +298,57 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
     floatx4 xa[MS], xn[MS];
 #pragma unroll
     for (int s = 0; s < MS; ++s) { xa[s] = zero4(); xn[s] = zero4(); }
-    for (int sl = 0; sl < NSL; ++sl) {
-        stage_qk(sl * kKS);
-#pragma unroll
-        for (int s = 0; s < MS; ++s) {
-            const int p = wave + NW * s;
-            if (p >= NTILE) continue;
-            int i, j;
-            tile_ij(p, i, j);
-            if constexpr (!CHAN) {
-                // x[rr] = q_l . k_m (and k_l . k_m), l = 16 i + g4 + rr, m = 16 j + cl
-#pragma unroll
-                for (int kk = 0; kk < kKS / 16; ++kk) {
-                    const floatx4 bk = load4(&ys[(16 * j + (lane & 15)) * kLDS + 16 * kk + 4 * (lane >> 4)]);
-                    xa[s] = mm16<T>(&xs[16 * i * kLDS + 16 * kk], kLDS, bk, xa[s], lane);
-                    if constexpr (DELTA) xn[s] = mm16<T>(&ys[16 * i * kLDS + 16 * kk], kLDS, bk, xn[s], lane);
-                }
-            } else {
-                // exact per-channel decay of every pair: 2^(G_lc - G_mc), m <= l
-                const int m = 16 * j + (lane & 15), lb = 16 * i + 4 * (lane >> 4);
-#pragma unroll 2
-                for (int c4 = 0; c4 < kKS; c4 += 4) {
-                    const floatx4 km = load4(&ys[m * kLDS + c4]);
-                    const floatx4 Gm = load4(&gs[m * kLDS + c4]);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int l = lb + rr;
-                        const floatx4 qv = load4(&xs[l * kLDS + c4]);
-                        const floatx4 Gl = load4(&gs[l * kLDS + c4]);
-                        floatx4 kv = zero4();
-                        if constexpr (DELTA) kv = load4(&ys[l * kLDS + c4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float t = m <= l ? km[e] * fast_exp2(Gl[e] - Gm[e]) : 0.f;
-                            xa[s][rr] = fmaf(qv[e], t, xa[s][rr]);
-                            if constexpr (DELTA) xn[s][rr] = fmaf(kv[e], t, xn[s][rr]);
+    // the score tiles of the staged slice
+    auto score_slice = [&]() {
+    #pragma unroll
+            for (int s = 0; s < MS; ++s) {
+                const int p = wave + NW * s;
+                if (p >= NTILE) continue;
+                int i, j;
+                tile_ij(p, i, j);
+                if constexpr (!CHAN) {
+                    // x[rr] = q_l . k_m (and k_l . k_m), l = 16 i + g4 + rr, m = 16 j + cl
+    #pragma unroll
+                    for (int kk = 0; kk < kKS / 16; ++kk) {
+                        const floatx4 bk = load4(&ys[(16 * j + (lane & 15)) * kLDS + 16 * kk + 4 * (lane >> 4)]);
+                        xa[s] = mm16<T>(&xs[16 * i * kLDS + 16 * kk], kLDS, bk, xa[s], lane);
+                        if constexpr (DELTA) xn[s] = mm16<T>(&ys[16 * i * kLDS + 16 * kk], kLDS, bk, xn[s], lane);
+                    }
+                } else {
+                    // exact per-channel decay of every pair: 2^(G_lc - G_mc), m <= l
+                    const int m = 16 * j + (lane & 15), lb = 16 * i + 4 * (lane >> 4);
+    #pragma unroll 2
+                    for (int c4 = 0; c4 < kKS; c4 += 4) {
+                        const floatx4 km = load4(&ys[m * kLDS + c4]);
+                        const floatx4 Gm = load4(&gs[m * kLDS + c4]);
+    #pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int l = lb + rr;
+                            const floatx4 qv = load4(&xs[l * kLDS + c4]);
+                            const floatx4 Gl = load4(&gs[l * kLDS + c4]);
+                            floatx4 kv = zero4();
+                            if constexpr (DELTA) kv = load4(&ys[l * kLDS + c4]);
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float t = m <= l ? km[e] * fast_exp2(Gl[e] - Gm[e]) : 0.f;
+                                xa[s][rr] = fmaf(qv[e], t, xa[s][rr]);
+                                if constexpr (DELTA) xn[s][rr] = fmaf(kv[e], t, xn[s][rr]);
+                            }
                         }
                     }
                 }
             }
-        }
+    };
+    // slices in pairs through the register sets A, B; the last two refill them
+    // with the first two slices again for the second pass
+#pragma unroll 1
+    for (int sl = 0; sl < NSL; sl += 2) {
+        stage_qk(SA);
+        load_qk(SA, sl + 2 < NSL ? sl + 2 : 0);
+        score_slice();
+        stage_qk(SB);
+        load_qk(SB, sl + 3 < NSL ? sl + 3 : 1);
+        score_slice();
     }
     mfma_settle();
     // Aq to the workspace, beta L to LDS (rows l = 16 i + g4 + rr, column m)
@@ -370,47 +436,111 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
         }
     };
 
-    // ---- operands of the state pass, slice by slice -----------------------------
-    for (int sl = 0; sl < NSL; ++sl) {
+    // four values as the token type, one 8- or 16-byte store
+    auto st4 = [](T* dst, floatx4 y) {
+        R4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = from_f32<T>(y[i]);
+        *reinterpret_cast<R4*>(dst) = w;
+    };
+    // ---- operands of the state pass for the staged slice sl ----------------------
+    auto operands = [&](int sl) {
         const int c0 = sl * kKS;
-        stage_qk(c0);
-        for (int e = tid; e < C * kKS; e += kGT) {
-            const int row = e / kKS, c = e % kKS;
-            const float G = CHAN ? gs[row * kLDS + c] : Gsc[row];
-            Qd[row * DK + c0 + c] = from_f32<T>(GATED ? xs[row * kLDS + c] * fast_exp2(G) : xs[row * kLDS + c]);
+        // <-Q: four channels of a row per thread
+#pragma unroll
+        for (int j = 0; j < PP; ++j) {
+            int row, cq;
+            if (!grp(j, row, cq)) continue;
+            const floatx4 x = *reinterpret_cast<const floatx4*>(&xs[row * kLDS + cq]);
+            floatx4 y;
+            if constexpr (CHAN) {
+                const floatx4 G = *reinterpret_cast<const floatx4*>(&gs[row * kLDS + cq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = x[i] * fast_exp2(G[i]);
+            } else {
+                const float d = GATED ? fast_exp2(Gsc[row]) : 1.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = x[i] * d;
+            }
+            st4(&Qd[row * DK + c0 + cq], y);
         }
-        for (int e = tid; e < C * kKS; e += kGT) {
-            const int c = e / C, row = e % C;
-            const float G = CHAN ? gs[row * kLDS + c] : Gsc[row];
+        // ->K^T: four rows of a channel per thread, rows fastest across lanes
+#pragma unroll
+        for (int j = 0; j < PP; ++j) {
+            const int e = tid + j * kGT;
+            if (PE % kGT != 0 && e >= PE) continue;
+            const int c = e / (C / 4), r0 = 4 * (e % (C / 4));
             const float Ge = CHAN ? gs[(C - 1) * kLDS + c] : Gsc[C - 1];
-            KrT[(c0 + c) * C + row] = from_f32<T>(GATED ? ys[row * kLDS + c] * fast_exp2(Ge - G) : ys[row * kLDS + c]);
+            floatx4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float G = CHAN ? gs[(r0 + i) * kLDS + c] : Gsc[r0 + i];
+                y[i] = ys[(r0 + i) * kLDS + c] * (GATED ? fast_exp2(Ge - G) : 1.f);
+            }
+            st4(&KrT[(c0 + c) * C + r0], y);
         }
         if (tid < kKS) gCw[c0 + tid] = GATED ? fast_exp2(CHAN ? gs[(C - 1) * kLDS + tid] : Gsc[C - 1]) : 1.f;
         if constexpr (DELTA) {
             // W = T (beta <-K): xs <- beta_m 2^(G_m) k_m
             __syncthreads();
-            for (int e = tid; e < C * kKS; e += kGT) {
-                const int row = e / kKS, c = e % kKS;
-                const float G = CHAN ? gs[row * kLDS + c] : Gsc[row];
-                xs[row * kLDS + c] = bet[row] * (GATED ? fast_exp2(G) : 1.f) * ys[row * kLDS + c];
+#pragma unroll
+            for (int j = 0; j < PP; ++j) {
+                int row, cq;
+                if (!grp(j, row, cq)) continue;
+                const floatx4 x = *reinterpret_cast<const floatx4*>(&ys[row * kLDS + cq]);
+                floatx4 y;
+                if constexpr (CHAN) {
+                    const floatx4 G = *reinterpret_cast<const floatx4*>(&gs[row * kLDS + cq]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] = bet[row] * fast_exp2(G[i]) * x[i];
+                } else {
+                    const float d = bet[row] * (GATED ? fast_exp2(Gsc[row]) : 1.f);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] = d * x[i];
+                }
+                *reinterpret_cast<floatx4*>(&xs[row * kLDS + cq]) = y;
             }
             __syncthreads();
             tb_product(Ww, DK, c0);
         }
+    };
+    // the last two slices refill A, B with the first two value slices
+#pragma unroll 1
+    for (int sl = 0; sl < NSL; sl += 2) {
+        stage_qk(SA);
+        if (sl + 2 < NSL) load_qk(SA, sl + 2);
+        else if (DELTA) load_v(SA, 0);
+        operands(sl);
+        stage_qk(SB);
+        if (sl + 3 < NSL) load_qk(SB, sl + 3);
+        else if (DELTA) load_v(SB, 1);
+        operands(sl + 1);
     }
     if constexpr (DELTA) {
         // U = T (beta V), kKS value columns at a time
-        for (int n0 = 0; n0 < DV; n0 += kKS) {
+        auto u_slice = [&](const Slice& S, int vs) {
             __syncthreads();
-            for (int e = tid; e < C * kKS / 4; e += kGT) {
-                const int row = e / (kKS / 4), cq = 4 * (e % (kKS / 4));
-                const bool ok = row < nrow;
-                const floatx4 vv = load4(v + (rowbase + (ok ? row : 0)) * DV + n0 + cq);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xs[row * kLDS + cq + i] = ok ? bet[row] * vv[i] : 0.f;
+            for (int j = 0; j < PP; ++j) {
+                int row, cq;
+                if (!grp(j, row, cq)) continue;
+                const bool ok = row < nrow;
+                const floatx4 vv = cvt4(S.q[j]);
+                floatx4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = ok ? bet[row] * vv[i] : 0.f;
+                *reinterpret_cast<floatx4*>(&xs[row * kLDS + cq]) = y;
             }
             __syncthreads();
-            tb_product(Uw, DV, n0);
+            tb_product(Uw, DV, vs * kKS);
+        };
+        const int nvs = DV / kKS;
+#pragma unroll 1
+        for (int vs = 0; vs < nvs; vs += 2) {
+            u_slice(SA, vs);
+            if (vs + 2 < nvs) load_v(SA, vs + 2);
+            u_slice(SB, vs + 1);
+            if (vs + 3 < nvs) load_v(SB, vs + 3);
         }
     }
 }
