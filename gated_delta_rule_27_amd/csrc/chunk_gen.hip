@@ -204,21 +204,28 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
 
     // ---- a1 (scalar gate) and beta: one wave, 64 rows at a time ------------------
     if (wave == 0) {
+        // every row's gate and beta loaded (rows past the end read row 0) before
+        // the first is used
+        constexpr int NH = (C + 63) / 64;
+        float gr[NH], br[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int l = 64 * h + lane;
+            const int lc = l < nrow ? l : 0;
+            gr[h] = (GATED && !CHAN) ? to_f32(g[rowbase + lc]) : 0.f;
+            br[h] = DELTA ? to_f32(beta[rowbase + lc]) : 0.f;
+        }
         float carry = 0.f;
-        for (int h = 0; h < C; h += 64) {
-            const int l = h + lane;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int l = 64 * h + lane;
             const bool ok = l < nrow;
-            float gv = 0.f;
-            if constexpr (GATED && !CHAN)
-                if (ok) gv = prep_gate(to_f32(g[rowbase + l]), prep) * kLog2e;
+            const float gv = (GATED && !CHAN && ok) ? prep_gate(gr[h], prep) * kLog2e : 0.f;
             const float G = wave_prefix_sum(gv) + carry;
             carry = wave_last(G);
             if (l < C) {
                 Gsc[l] = G;
-                float b = 0.f;
-                if constexpr (DELTA)
-                    if (ok) b = prep_beta(to_f32(beta[rowbase + l]), prep);
-                bet[l] = b;
+                bet[l] = (DELTA && ok) ? prep_beta(br[h], prep) : 0.f;
             }
         }
     }
@@ -252,20 +259,29 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
             int row, cq;
             if (!grp(j, row, cq)) continue;
             const bool ok = row < nrow;
-            const floatx4 qv = cvt4(S.q[j]), kv = cvt4(S.k[j]);
-            floatx4 xq, xk;
+            // (the map branches are uniform and taken once per group; values of
+            // the token type pass through unmapped exactly)
+            floatx4 xq = cvt4(S.q[j]), xk = cvt4(S.k[j]);
+            if (qkm != kQkAsIs) {
+                const float rnq = rq[row], rnk = rk[row];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xq[i] = ok ? mapqk(qv[i], rq[row]) : 0.f;
-                xk[i] = ok ? mapqk(kv[i], rk[row]) : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    xq[i] = mapqk(xq[i], rnq);
+                    xk[i] = mapqk(xk[i], rnk);
+                }
             }
+            if (!ok) xq = xk = zero4();
             *reinterpret_cast<floatx4*>(&xs[row * kLDS + cq]) = xq;
             *reinterpret_cast<floatx4*>(&ys[row * kLDS + cq]) = xk;
             if constexpr (CHAN) {
-                const floatx4 gv = cvt4(S.g[j]);
-                floatx4 xg;
+                floatx4 xg = cvt4(S.g[j]);
+                if (prep_gate_map(prep)) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xg[i] = ok ? prep_gate(gv[i], prep) * kLog2e : 0.f;
+                    for (int i = 0; i < 4; ++i) xg[i] = prep_gate(xg[i], prep);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xg[i] *= kLog2e;
+                if (!ok) xg = zero4();
                 *reinterpret_cast<floatx4*>(&gs[row * kLDS + cq]) = xg;
             }
         }
@@ -300,44 +316,44 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
     for (int s = 0; s < MS; ++s) { xa[s] = zero4(); xn[s] = zero4(); }
     // the score tiles of the staged slice
     auto score_slice = [&]() {
-    #pragma unroll
-            for (int s = 0; s < MS; ++s) {
-                const int p = wave + NW * s;
-                if (p >= NTILE) continue;
-                int i, j;
-                tile_ij(p, i, j);
-                if constexpr (!CHAN) {
-                    // x[rr] = q_l . k_m (and k_l . k_m), l = 16 i + g4 + rr, m = 16 j + cl
-    #pragma unroll
-                    for (int kk = 0; kk < kKS / 16; ++kk) {
-                        const floatx4 bk = load4(&ys[(16 * j + (lane & 15)) * kLDS + 16 * kk + 4 * (lane >> 4)]);
-                        xa[s] = mm16<T>(&xs[16 * i * kLDS + 16 * kk], kLDS, bk, xa[s], lane);
-                        if constexpr (DELTA) xn[s] = mm16<T>(&ys[16 * i * kLDS + 16 * kk], kLDS, bk, xn[s], lane);
-                    }
-                } else {
-                    // exact per-channel decay of every pair: 2^(G_lc - G_mc), m <= l
-                    const int m = 16 * j + (lane & 15), lb = 16 * i + 4 * (lane >> 4);
-    #pragma unroll 2
-                    for (int c4 = 0; c4 < kKS; c4 += 4) {
-                        const floatx4 km = load4(&ys[m * kLDS + c4]);
-                        const floatx4 Gm = load4(&gs[m * kLDS + c4]);
-    #pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int l = lb + rr;
-                            const floatx4 qv = load4(&xs[l * kLDS + c4]);
-                            const floatx4 Gl = load4(&gs[l * kLDS + c4]);
-                            floatx4 kv = zero4();
-                            if constexpr (DELTA) kv = load4(&ys[l * kLDS + c4]);
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float t = m <= l ? km[e] * fast_exp2(Gl[e] - Gm[e]) : 0.f;
-                                xa[s][rr] = fmaf(qv[e], t, xa[s][rr]);
-                                if constexpr (DELTA) xn[s][rr] = fmaf(kv[e], t, xn[s][rr]);
-                            }
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+            const int p = wave + NW * s;
+            if (p >= NTILE) continue;
+            int i, j;
+            tile_ij(p, i, j);
+            if constexpr (!CHAN) {
+                // x[rr] = q_l . k_m (and k_l . k_m), l = 16 i + g4 + rr, m = 16 j + cl
+#pragma unroll
+                for (int kk = 0; kk < kKS / 16; ++kk) {
+                    const floatx4 bk = load4(&ys[(16 * j + (lane & 15)) * kLDS + 16 * kk + 4 * (lane >> 4)]);
+                    xa[s] = mm16<T>(&xs[16 * i * kLDS + 16 * kk], kLDS, bk, xa[s], lane);
+                    if constexpr (DELTA) xn[s] = mm16<T>(&ys[16 * i * kLDS + 16 * kk], kLDS, bk, xn[s], lane);
+                }
+            } else {
+                // exact per-channel decay of every pair: 2^(G_lc - G_mc), m <= l
+                const int m = 16 * j + (lane & 15), lb = 16 * i + 4 * (lane >> 4);
+#pragma unroll 2
+                for (int c4 = 0; c4 < kKS; c4 += 4) {
+                    const floatx4 km = load4(&ys[m * kLDS + c4]);
+                    const floatx4 Gm = load4(&gs[m * kLDS + c4]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int l = lb + rr;
+                        const floatx4 qv = load4(&xs[l * kLDS + c4]);
+                        const floatx4 Gl = load4(&gs[l * kLDS + c4]);
+                        floatx4 kv = zero4();
+                        if constexpr (DELTA) kv = load4(&ys[l * kLDS + c4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float t = m <= l ? km[e] * fast_exp2(Gl[e] - Gm[e]) : 0.f;
+                            xa[s][rr] = fmaf(qv[e], t, xa[s][rr]);
+                            if constexpr (DELTA) xn[s][rr] = fmaf(kv[e], t, xn[s][rr]);
                         }
                     }
                 }
             }
+        }
     };
     // slices in pairs through the register sets A, B; the last two refill them
     // with the first two slices again for the second pass
@@ -358,14 +374,19 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
         if (p >= NTILE) continue;
         int i, j;
         tile_ij(p, i, j);
-        const int m = 16 * j + (lane & 15);
+        const int m = 16 * j + (lane & 15), l0 = 16 * i + 4 * (lane >> 4);
+        // branch-free: the row values read once as vectors, the decay of every
+        // position formed (its exponent clamped at 0 above the diagonal) and
+        // masked by selects
+        const float Gm = Gsc[m];
+        const floatx4 Gl = *reinterpret_cast<const floatx4*>(&Gsc[l0]);
+        const floatx4 bl = *reinterpret_cast<const floatx4*>(&bet[l0]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int l = 16 * i + 4 * (lane >> 4) + rr;
-            float dec = 1.f;
-            if constexpr (GATED && !CHAN) dec = m <= l ? fast_exp2(Gsc[l] - Gsc[m]) : 0.f;
+            const int l = l0 + rr;
+            const float dec = (GATED && !CHAN) ? fast_exp2(fminf(Gl[rr] - Gm, 0.f)) : 1.f;
             Aqw[l * C + m] = from_f32<T>(m <= l ? xa[s][rr] * dec : 0.f);
-            if constexpr (DELTA) Lm[l * LDL + m] = m < l ? bet[l] * xn[s][rr] * dec : 0.f;
+            if constexpr (DELTA) Lm[l * LDL + m] = m < l ? bl[rr] * xn[s][rr] * dec : 0.f;
         }
     }
     __syncthreads();
@@ -464,20 +485,27 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
             }
             st4(&Qd[row * DK + c0 + cq], y);
         }
-        // ->K^T: four rows of a channel per thread, rows fastest across lanes
+        // ->K^T: four channels of a row per thread, rows fastest across lanes
+        // (one vector LDS read; each of the four stores is contiguous across lanes)
 #pragma unroll
         for (int j = 0; j < PP; ++j) {
             const int e = tid + j * kGT;
             if (PE % kGT != 0 && e >= PE) continue;
-            const int c = e / (C / 4), r0 = 4 * (e % (C / 4));
-            const float Ge = CHAN ? gs[(C - 1) * kLDS + c] : Gsc[C - 1];
+            const int r = e % C, c4 = 4 * (e / C);
+            const floatx4 x = *reinterpret_cast<const floatx4*>(&ys[r * kLDS + c4]);
             floatx4 y;
+            if constexpr (CHAN) {
+                const floatx4 G = *reinterpret_cast<const floatx4*>(&gs[r * kLDS + c4]);
+                const floatx4 Ge = *reinterpret_cast<const floatx4*>(&gs[(C - 1) * kLDS + c4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float G = CHAN ? gs[(r0 + i) * kLDS + c] : Gsc[r0 + i];
-                y[i] = ys[(r0 + i) * kLDS + c] * (GATED ? fast_exp2(Ge - G) : 1.f);
+                for (int i = 0; i < 4; ++i) y[i] = x[i] * fast_exp2(Ge[i] - G[i]);
+            } else {
+                const float d = GATED ? fast_exp2(Gsc[C - 1] - Gsc[r]) : 1.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = x[i] * d;
             }
-            st4(&KrT[(c0 + c) * C + r0], y);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) KrT[(c0 + c4 + i) * C + r] = from_f32<T>(y[i]);
         }
         if (tid < kKS) gCw[c0 + tid] = GATED ? fast_exp2(CHAN ? gs[(C - 1) * kLDS + tid] : Gsc[C - 1]) : 1.f;
         if constexpr (DELTA) {
