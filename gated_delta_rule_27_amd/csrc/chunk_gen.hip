@@ -410,31 +410,42 @@ __global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
             }
         }
         __syncthreads();
-        // blocks below the diagonal, one block row at a time:
-        // T(i, j) = -T(i, i) sum_{kb = j}^{i - 1} L(i, kb) T(kb, j)
-        for (int i = 1; i < NB; ++i) {
-            constexpr int NJ = (8 + NW - 1) / NW;   // column blocks per wave
-            floatx4 X[NJ];
+        // blocks below the diagonal, column by column:
+        // T(i, j) = -T(i, i) sum_{kb = j}^{i - 1} L(i, kb) T(kb, j).
+        // Column j needs only its own blocks above row i, so wave j walks it down
+        // the rows with no barrier, holding the column in registers; L(i, j) is
+        // still read by the columns left of j, so the column goes to LDS (over
+        // L) after one barrier.  (Same products in the same order as row by row.)
+        static_assert(NW >= NB - 1, "one column block per wave");
+        {
+            floatx4 Tc[NB];
+            const int j = wave;
+            if (j < NB - 1) {
+                Tc[0] = zero4();
 #pragma unroll
-            for (int s2 = 0; s2 < NJ; ++s2) {
-                const int j = wave + NW * s2;
-                X[s2] = zero4();
-                if (j < i)
-                    for (int kb = j; kb < i; ++kb)
-                        X[s2] = mm16<float>(&Lm[16 * i * LDL + 16 * kb], LDL,
-                                            load_tile_rl(&Lm[16 * kb * LDL + 16 * j], LDL, lane), X[s2], lane);
+                for (int b = 0; b < NB; ++b)
+                    if (b == j) Tc[b] = load_tile_rl(&Lm[16 * b * LDL + 16 * b], LDL, lane);   // T(j, j)
+#pragma unroll
+                for (int i = 1; i < NB; ++i) {
+                    if (i <= j) continue;
+                    floatx4 X = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < NB - 1; ++kb)
+                        if (kb >= j && kb < i) X = mm16<float>(&Lm[16 * i * LDL + 16 * kb], LDL, Tc[kb], X, lane);
+                    const floatx4 t = mm16<float>(&Lm[16 * i * LDL + 16 * i], LDL, X, zero4(), lane);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) Tc[i][rr] = -t[rr];
+                }
             }
             mfma_settle();
             __syncthreads();
+            if (j < NB - 1) {
 #pragma unroll
-            for (int s2 = 0; s2 < NJ; ++s2) {
-                const int j = wave + NW * s2;
-                if (j < i) {
-                    const floatx4 t = mm16<float>(&Lm[16 * i * LDL + 16 * i], LDL, X[s2], zero4(), lane);
-                    mfma_settle();
+                for (int i = 1; i < NB; ++i) {
+                    if (i <= j) continue;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        Lm[(16 * i + 4 * (lane >> 4) + rr) * LDL + 16 * j + (lane & 15)] = -t[rr];
+                        Lm[(16 * i + 4 * (lane >> 4) + rr) * LDL + 16 * j + (lane & 15)] = Tc[i][rr];
                 }
             }
             __syncthreads();
