@@ -112,8 +112,15 @@ __device__ __forceinline__ void tile_ij(int p, int& i, int& j)
 // ===========================================================================
 // Intra-chunk kernel
 // ===========================================================================
+// At chunk 16 and 32 (bf16 tokens, no per-channel gate) eight waves per SIMD
+// fit in 64 VGPRs without spills; more resident workgroups hide more of each
+// one's latency.
+template <typename T, int C, int GATE>
+constexpr int gen_intra_min_waves() { return (C <= 32 && sizeof(T) == 2 && GATE != kGateChannel) ? 8 : 1; }
+
 template <typename T, int C, int DK, int RULE, int GATE>
-__global__ __launch_bounds__(64 * gen_waves(C)) void gen_intra_kernel(
+__global__ __launch_bounds__(64 * gen_waves(C))
+__attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void gen_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
     const T* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks, int DV,
     int prep)
