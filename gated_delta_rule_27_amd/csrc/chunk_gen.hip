@@ -257,8 +257,9 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
         return to_f32(from_f32<T>(y));
     };
 
-    // Stage key channels c0 .. c0 + kKS - 1 of q and k (and the per-channel
-    // log-gate as its prefix within the chunk) into xs, ys (gs), fp32.
+    // Stage the slice held in register set S (kKS key channels of q and k, and
+    // the per-channel log-gate as its prefix within the chunk) into xs, ys
+    // (gs), fp32.
     auto stage_qk = [&](const Slice& S) {
         __syncthreads();
 #pragma unroll
