@@ -112,25 +112,28 @@ __device__ __forceinline__ void tile_ij(int p, int& i, int& j)
 // ===========================================================================
 // Intra-chunk kernel
 // ===========================================================================
-// At chunk 16 and 32 (bf16 tokens, no per-channel gate) eight waves per SIMD
-// fit in 64 VGPRs without spills; more resident workgroups hide more of each
-// one's latency.
-template <typename T, int C, int GATE>
-constexpr int gen_intra_min_waves() { return (C <= 32 && sizeof(T) == 2 && GATE != kGateChannel) ? 8 : 1; }
+// Rows per workgroup of the intra kernel for chunk size CH: chunks of 16 or 32
+// tokens (gate none or scalar) run two or four to a workgroup as the diagonal
+// blocks of a 64-row tile, so all four waves have tiles and the per-workgroup
+// steps (gate scan, slice staging, barriers) are shared; else one chunk.
+__host__ __device__ constexpr int gen_tile(int CH, int gate) { return CH < 64 && gate != kGateChannel ? 64 : CH; }
 
-template <typename T, int C, int DK, int RULE, int GATE>
-__global__ __launch_bounds__(64 * gen_waves(C))
-__attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void gen_intra_kernel(
+template <typename T, int CH, int DK, int RULE, int GATE>
+__global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
     const T* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks, int DV,
     int prep)
 {
+    constexpr int C = gen_tile(CH, GATE);       // rows of the tile
+    constexpr int SUB = C / CH;                 // chunks in the tile
+    constexpr int BC = CH / 16;                 // 16-row blocks per chunk
     constexpr int NB = C / 16;
     constexpr bool DELTA = RULE == kRuleDelta;
     constexpr bool CHAN = GATE == kGateChannel;
     constexpr bool GATED = GATE != kGateNone;
     constexpr int NW = gen_waves(C), kGT = 64 * NW;
-    constexpr int NTILE = NB * (NB + 1) / 2;
+    constexpr int NTILE = SUB * BC * (BC + 1) / 2;   // causal 16x16 tiles inside the chunks
+    static_assert(SUB == 1 || (C == 64 && !CHAN), "several chunks per workgroup: 64-row tiles, no per-channel gate");
     constexpr int MS = (NTILE + NW - 1) / NW;    // causal tiles per wave
     constexpr int LDL = C + 4;                   // row stride of L and T
     constexpr int NSL = DK / kKS;                // key-channel slices
@@ -148,19 +151,32 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t ntile = (nchunks + SUB - 1) / SUB;          // workgroups per head
     const int64_t task = blockIdx.x;
-    const int64_t bh = task / nchunks, t0 = (task % nchunks) * C;
-    const int nrow = (int)(Tlen - t0 < C ? Tlen - t0 : C);      // rows of this chunk in the sequence
+    const int64_t bh = task / ntile, c0i = (task % ntile) * SUB, t0 = c0i * CH;
+    const int nrow = (int)(Tlen - t0 < C ? Tlen - t0 : C);      // rows of this tile in the sequence
     const int qkm = prep_qk_map(prep);
-    const GenWs L = gen_ws(C, DK, DV, (int)sizeof(T), DELTA);
-    unsigned char* wc = ws + task * L.bytes;
-    T* const Qd = reinterpret_cast<T*>(wc + L.qd);
-    T* const KrT = reinterpret_cast<T*>(wc + L.krt);
-    T* const Aqw = reinterpret_cast<T*>(wc + L.aq);
-    float* const gCw = reinterpret_cast<float*>(wc + L.gc);
-    T* const Ww = reinterpret_cast<T*>(wc + L.w);
-    T* const Uw = reinterpret_cast<T*>(wc + L.u);
+    // workspace piece at byte offset off of the tile's chunk sc (chunk rows
+    // sc CH .. of the tile); chunks past the head's last one are not written
+    const GenWs L = gen_ws(CH, DK, DV, (int)sizeof(T), DELTA);
+    unsigned char* const wc0 = ws + (bh * nchunks + c0i) * L.bytes;
+    auto wsp = [&](int sc, size_t off) { return wc0 + (size_t)sc * L.bytes + off; };
+    auto has = [&](int sc) { return SUB == 1 || c0i + sc < nchunks; };
     const int64_t rowbase = bh * Tlen + t0;
+    // (i, j) of the p-th causal 16x16 tile inside the tile's chunks
+    auto tile_of = [&](int p, int& i, int& j) {
+        if constexpr (SUB == 1) {
+            tile_ij(p, i, j);
+        } else {
+            constexpr int TPC = BC * (BC + 1) / 2;         // tiles per chunk
+            tile_ij(p % TPC, i, j);
+            i += (p / TPC) * BC;
+            j += (p / TPC) * BC;
+        }
+    };
+    // chunk of tile row r and its row inside that chunk
+    auto chunk_of = [](int r) { return SUB == 1 ? 0 : r / CH; };
+    auto row_in = [](int r) { return SUB == 1 ? r : r % CH; };
 
     // ---- token loads.  Thread tid owns the 4-element groups tid + j kGT of
     // every staged [C][kKS] slice (row e / (kKS / 4), columns 4 (e % (kKS / 4))
@@ -228,8 +244,14 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
             const int l = 64 * h + lane;
             const bool ok = l < nrow;
             const float gv = (GATED && !CHAN && ok) ? prep_gate(gr[h], prep) * kLog2e : 0.f;
-            const float G = wave_prefix_sum(gv) + carry;
+            float G = wave_prefix_sum(gv) + carry;
             carry = wave_last(G);
+            if constexpr (SUB > 1) {
+                // (one pass: C = 64) the prefix restarts at each chunk of the tile
+                const int st = (lane / CH) * CH;
+                const float base = __shfl(G, st > 0 ? st - 1 : 0, 64);
+                if (st > 0) G -= base;
+            }
             if (l < C) {
                 Gsc[l] = G;
                 bet[l] = (DELTA && ok) ? prep_beta(br[h], prep) : 0.f;
@@ -329,7 +351,7 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
             const int p = wave + NW * s;
             if (p >= NTILE) continue;
             int i, j;
-            tile_ij(p, i, j);
+            tile_of(p, i, j);
             if constexpr (!CHAN) {
                 // x[rr] = q_l . k_m (and k_l . k_m), l = 16 i + g4 + rr, m = 16 j + cl
 #pragma unroll
@@ -381,7 +403,7 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
         const int p = wave + NW * s;
         if (p >= NTILE) continue;
         int i, j;
-        tile_ij(p, i, j);
+        tile_of(p, i, j);
         const int m = 16 * j + (lane & 15), l0 = 16 * i + 4 * (lane >> 4);
         // branch-free: the row values read once as vectors, the decay of every
         // position formed (its exponent clamped at 0 above the diagonal) and
@@ -393,7 +415,9 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
         for (int rr = 0; rr < 4; ++rr) {
             const int l = l0 + rr;
             const float dec = (GATED && !CHAN) ? fast_exp2(fminf(Gl[rr] - Gm, 0.f)) : 1.f;
-            Aqw[l * C + m] = from_f32<T>(m <= l ? xa[s][rr] * dec : 0.f);
+            if (has(chunk_of(l)))
+                reinterpret_cast<T*>(wsp(chunk_of(l), L.aq))[row_in(l) * CH + row_in(m)] =
+                    from_f32<T>(m <= l ? xa[s][rr] * dec : 0.f);
             if constexpr (DELTA) Lm[l * LDL + m] = m < l ? bl[rr] * xn[s][rr] * dec : 0.f;
         }
     }
@@ -424,18 +448,20 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
         // the rows with no barrier, holding the column in registers; L(i, j) is
         // still read by the columns left of j, so the column goes to LDS (over
         // L) after one barrier.  (Same products in the same order as row by row.)
+        // With several chunks per tile only the blocks inside a chunk are solved.
         static_assert(NW >= NB - 1, "one column block per wave");
         {
             floatx4 Tc[NB];
             const int j = wave;
-            if (j < NB - 1) {
+            const bool col = j < NB - 1 && (SUB == 1 || j % BC < BC - 1);   // column with blocks below it in its chunk
+            if (col) {
                 Tc[0] = zero4();
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     if (b == j) Tc[b] = load_tile_rl(&Lm[16 * b * LDL + 16 * b], LDL, lane);   // T(j, j)
 #pragma unroll
                 for (int i = 1; i < NB; ++i) {
-                    if (i <= j) continue;
+                    if (i <= j || (SUB > 1 && i / BC != j / BC)) continue;
                     floatx4 X = zero4();
 #pragma unroll
                     for (int kb = 0; kb < NB - 1; ++kb)
@@ -447,10 +473,10 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
             }
             mfma_settle();
             __syncthreads();
-            if (j < NB - 1) {
+            if (col) {
 #pragma unroll
                 for (int i = 1; i < NB; ++i) {
-                    if (i <= j) continue;
+                    if (i <= j || (SUB > 1 && i / BC != j / BC)) continue;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
                         Lm[(16 * i + 4 * (lane >> 4) + rr) * LDL + 16 * j + (lane & 15)] = Tc[i][rr];
@@ -462,17 +488,22 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
 
     // ---- products T (beta X) for the staged slice in xs: tiles (lb, cb) of a
     // [C][kKS] block, written to dst (row stride ld) at column c0 --------------
-    auto tb_product = [&](T* dst, int ld, int c0) {
+    auto tb_product = [&](size_t off, int ld, int c0) {
         for (int p = wave; p < NB * (kKS / 16); p += NW) {
             const int lb = p / (kKS / 16), cb = p % (kKS / 16);
             floatx4 acc = zero4();
-            for (int mb = 0; mb <= lb; ++mb)
+            for (int mb = SUB == 1 ? 0 : (lb / BC) * BC; mb <= lb; ++mb)
                 acc = mm16<T>(&Lm[16 * lb * LDL + 16 * mb], LDL, load_tile_rl(&xs[16 * mb * kLDS + 16 * cb], kLDS, lane),
                               acc, lane);
             mfma_settle();
+            const int sc = chunk_of(16 * lb);              // the chunk of block row lb
+            if (has(sc)) {
+                T* const dst = reinterpret_cast<T*>(wsp(sc, off));
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                dst[(16 * lb + 4 * (lane >> 4) + rr) * ld + c0 + 16 * cb + (lane & 15)] = from_f32<T>(acc[rr]);
+                for (int rr = 0; rr < 4; ++rr)
+                    dst[(row_in(16 * lb) + 4 * (lane >> 4) + rr) * ld + c0 + 16 * cb + (lane & 15)] =
+                        from_f32<T>(acc[rr]);
+            }
         }
     };
 
@@ -502,7 +533,7 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = x[i] * d;
             }
-            st4(&Qd[row * DK + c0 + cq], y);
+            if (has(chunk_of(row))) st4(&reinterpret_cast<T*>(wsp(chunk_of(row), L.qd))[row_in(row) * DK + c0 + cq], y);
         }
         // ->K^T: four channels of a row per thread, rows fastest across lanes
         // (one vector LDS read; each of the four stores is contiguous across lanes)
@@ -519,14 +550,21 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = x[i] * fast_exp2(Ge[i] - G[i]);
             } else {
-                const float d = GATED ? fast_exp2(Gsc[C - 1] - Gsc[r]) : 1.f;
+                const float d = GATED ? fast_exp2(Gsc[chunk_of(r) * CH + CH - 1] - Gsc[r]) : 1.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = x[i] * d;
             }
+            if (has(chunk_of(r))) {
+                T* const krt = reinterpret_cast<T*>(wsp(chunk_of(r), L.krt));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) KrT[(c0 + c4 + i) * C + r] = from_f32<T>(y[i]);
+                for (int i = 0; i < 4; ++i) krt[(c0 + c4 + i) * CH + row_in(r)] = from_f32<T>(y[i]);
+            }
         }
-        if (tid < kKS) gCw[c0 + tid] = GATED ? fast_exp2(CHAN ? gs[(C - 1) * kLDS + tid] : Gsc[C - 1]) : 1.f;
+        if (tid < SUB * kKS && has(tid / kKS)) {
+            const int sc = tid / kKS, c = tid % kKS;
+            reinterpret_cast<float*>(wsp(sc, L.gc))[c0 + c] =
+                GATED ? fast_exp2(CHAN ? gs[(C - 1) * kLDS + c] : Gsc[sc * CH + CH - 1]) : 1.f;
+        }
         if constexpr (DELTA) {
             // W = T (beta <-K): xs <- beta_m 2^(G_m) k_m
             __syncthreads();
@@ -548,7 +586,7 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
                 *reinterpret_cast<floatx4*>(&xs[row * kLDS + cq]) = y;
             }
             __syncthreads();
-            tb_product(Ww, DK, c0);
+            tb_product(L.w, DK, c0);
         }
     };
     // the last two slices refill A, B with the first two value slices
@@ -579,7 +617,7 @@ __attribute__((amdgpu_waves_per_eu(gen_intra_min_waves<T, C, GATE>(), 8))) void 
                 *reinterpret_cast<floatx4*>(&xs[row * kLDS + cq]) = y;
             }
             __syncthreads();
-            tb_product(Uw, DV, vs * kKS);
+            tb_product(L.u, DV, vs * kKS);
         };
         const int nvs = DV / kKS;
 #pragma unroll 1
@@ -897,8 +935,9 @@ hipError_t launch_gen_t(const ChunkProblem& p, hipStream_t s)
     const int64_t bh = p.B * p.H;
     unsigned char* ws = static_cast<unsigned char*>(p.workspace);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((gen_intra_kernel<T, C, DK, RULE, GATE>), dim3((unsigned)(bh * nchunks)),
-                           dim3(64 * gen_waves(C)), 0, s,
+        constexpr int SUB = gen_tile(C, GATE) / C;         // chunks per workgroup
+        hipLaunchKernelGGL((gen_intra_kernel<T, C, DK, RULE, GATE>), dim3((unsigned)(bh * ((nchunks + SUB - 1) / SUB))),
+                           dim3(64 * gen_waves(gen_tile(C, GATE))), 0, s,
                            static_cast<const T*>(p.q), static_cast<const T*>(p.k), static_cast<const T*>(p.v),
                            static_cast<const T*>(p.g), static_cast<const T*>(p.beta), ws, p.T, nchunks, p.dv,
                            p.prep);
