@@ -16,9 +16,11 @@
 // Two kernels, the first over all chunks in parallel, the second walking each
 // head's chunks in order:
 //
-//   gen_intra_kernel   one workgroup per (b, h, chunk), 4 waves; stages q, k
-//     (and the per-channel gate) 32 key channels at a time in fp32 LDS and
-//     writes to the workspace, in the token type:
+//   gen_intra_kernel   one workgroup per (b, h, chunk), 4 waves (8 at chunk
+//     128); chunks of 16 or 32 tokens without the per-channel gate run four or
+//     two to a workgroup as the diagonal blocks of a 64-row tile.  It stages
+//     q, k (and the per-channel gate) 32 key channels at a time in fp32 LDS
+//     and writes each chunk's operands to the workspace, in the token type:
 //       a1  G = prefix of the log-gate (base 2; per channel or scalar)
 //       a2  Aq[l][m] = sum_c q_lc 2^(G_lc - G_mc) k_mc   (m <= l)
 //           scalar gate / no gate: a matrix-core product, decay applied after;
