@@ -66,12 +66,26 @@ def test_chunk64_generic_path(monkeypatch, rule, gate):
 
 
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 127, 128, 129, 255, 257])
-@pytest.mark.parametrize("chunk", [16, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 128])
 def test_lengths_around_chunk_boundaries(chunk, T):
+    # chunks of 16 and 32 tokens share a workgroup four or two at a time: these
+    # lengths leave the last workgroup of a head with fewer chunks than that
     case = syn.Case("csize_len", 1, 2, T, 128, 128, "delta", "scalar", "bf16", chunk=chunk, gate_scale=0.1,
                     s0_std=0.2, case_id=154)
     x = syn.chunk_inputs(case)
     check_chunk(case, x, s0=x["s0"])
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("rule,gate", [("add", "none"), ("delta", "none"), ("add", "scalar")])
+def test_shared_workgroup_rules(chunk, rule, gate):
+    # several heads, an odd number of chunks per head (the last workgroup of each
+    # head holds fewer chunks), both rules and gate kinds, fp32 and bf16 tokens
+    for dtype in ("bf16", "fp32"):
+        case = syn.Case("csize_shared", 2, 3, 4 * chunk + 7, 64, 128, rule, gate, dtype, chunk=chunk,
+                        gate_scale=0.1, s0_std=0.2, case_id=157)
+        x = syn.chunk_inputs(case)
+        check_chunk(case, x, s0=x["s0"])
 
 
 @pytest.mark.parametrize("chunk", [32, 128])
