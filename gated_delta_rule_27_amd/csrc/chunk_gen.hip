@@ -70,11 +70,8 @@ __device__ __forceinline__ typename Frag16<T>::type frag16_lds_sep(const T* M, i
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-// waves of the intra-chunk kernel: 8 at C = 128, whose LDS leaves one
-// workgroup per CU, else 4
+// waves of the intra-chunk kernel: 8 at C = 128, else 4
 __host__ __device__ constexpr int gen_waves(int C) { return C == 128 ? 8 : 4; }
-constexpr int kKS = 32;           // key / value channels per staged slice
-constexpr int kLDS = kKS + 4;     // row stride of a staged fp32 slice
 
 // Workspace of one chunk of one head: byte offsets of its pieces (256-byte
 // aligned), operands in the token type (element size esz), 2^(G_{C-1}) fp32.
@@ -120,8 +117,18 @@ __device__ __forceinline__ void tile_ij(int p, int& i, int& j)
 // steps (gate scan, slice staging, barriers) are shared; else one chunk.
 __host__ __device__ constexpr int gen_tile(int CH, int gate) { return CH < 64 && gate != kGateChannel ? 64 : CH; }
 
+// At chunk 128 (under 80 KB of LDS) two 8-wave workgroups share a CU when the
+// kernel keeps to 128 VGPRs, which it does without spills except for fp32
+// tokens with the per-channel gate.
+template <typename T, int CH, int GATE>
+constexpr int gen_intra_waves_per_simd()
+{
+    return gen_tile(CH, GATE) == 128 && !(sizeof(T) == 4 && GATE == kGateChannel) ? 4 : 1;
+}
+
 template <typename T, int CH, int DK, int RULE, int GATE>
-__global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_kernel(
+__global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE)))
+__attribute__((amdgpu_waves_per_eu(gen_intra_waves_per_simd<T, CH, GATE>(), 8))) void gen_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ g,
     const T* __restrict__ beta, unsigned char* __restrict__ ws, int64_t Tlen, int64_t nchunks, int DV,
     int prep)
@@ -137,14 +144,19 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
     constexpr int NTILE = SUB * BC * (BC + 1) / 2;   // causal 16x16 tiles inside the chunks
     static_assert(SUB == 1 || (C == 64 && !CHAN), "several chunks per workgroup: 64-row tiles, no per-channel gate");
     constexpr int MS = (NTILE + NW - 1) / NW;    // causal tiles per wave
-    constexpr int LDL = C + 4;                   // row stride of L and T
+    // key / value channels per staged slice (16 at C = 128, which with the
+    // packed blocks of T keeps the workgroup under 80 KB of LDS: two per CU)
+    constexpr int kKS = C == 128 ? 16 : 32;
+    constexpr int kLDS = kKS + 4;                // row stride of a staged fp32 slice
+    constexpr int LDB = 16 + 4;                  // row stride of a packed 16x16 block of L / T
+    constexpr int NLB = NB * (NB + 1) / 2;       // blocks on and below the diagonal
     constexpr int NSL = DK / kKS;                // key-channel slices
     static_assert(NB >= 1 && NB <= 8 && DK % kKS == 0, "chunk and head sizes");
 
     __shared__ __align__(16) float xs[C * kLDS];                  // q slice, later beta <-K or beta V
     __shared__ __align__(16) float ys[C * kLDS];                  // k slice
     __shared__ __align__(16) float gs[CHAN ? C * kLDS : 4];       // per-channel prefix (base 2)
-    __shared__ __align__(16) float Lm[DELTA ? C * LDL : 4];       // beta L, then T
+    __shared__ __align__(16) float Lm[DELTA ? NLB * 16 * LDB : 4]; // beta L, then T: blocks (i, j <= i) packed
     __shared__ __align__(16) float Gsc[C];                        // scalar prefix (base 2)
     __shared__ __align__(16) float bet[C];
     __shared__ __align__(16) float rq[C], rk[C];                  // 1 / |q_l|, 1 / |k_l| (L2 map)
@@ -165,6 +177,7 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
     auto wsp = [&](int sc, size_t off) { return wc0 + (size_t)sc * L.bytes + off; };
     auto has = [&](int sc) { return SUB == 1 || c0i + sc < nchunks; };
     const int64_t rowbase = bh * Tlen + t0;
+    auto lmb = [&](int i, int j) { return &Lm[(i * (i + 1) / 2 + j) * 16 * LDB]; };   // block (i, j), j <= i
     // (i, j) of the p-th causal 16x16 tile inside the tile's chunks
     auto tile_of = [&](int p, int& i, int& j) {
         if constexpr (SUB == 1) {
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
             if (has(chunk_of(l)))
                 reinterpret_cast<T*>(wsp(chunk_of(l), L.aq))[row_in(l) * CH + row_in(m)] =
                     from_f32<T>(m <= l ? xa[s][rr] * dec : 0.f);
-            if constexpr (DELTA) Lm[l * LDL + m] = m < l ? bl[rr] * xn[s][rr] * dec : 0.f;
+            if constexpr (DELTA) lmb(l >> 4, m >> 4)[(l & 15) * LDB + (m & 15)] = m < l ? bl[rr] * xn[s][rr] * dec : 0.f;
         }
     }
     __syncthreads();
@@ -436,11 +449,11 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
                 for (int t = 0; t < 16; ++t) {
                     float acc = t == jj ? 1.f : 0.f;
 #pragma unroll
-                    for (int s2 = 0; s2 < t; ++s2) acc = fmaf(-Lm[(16 * i + t) * LDL + 16 * i + s2], x[s2], acc);
+                    for (int s2 = 0; s2 < t; ++s2) acc = fmaf(-lmb(i, i)[t * LDB + s2], x[s2], acc);
                     x[t] = acc;
                 }
 #pragma unroll
-                for (int t = 0; t < 16; ++t) Lm[(16 * i + t) * LDL + 16 * i + jj] = x[t];
+                for (int t = 0; t < 16; ++t) lmb(i, i)[t * LDB + jj] = x[t];
             }
         }
         __syncthreads();
@@ -460,15 +473,15 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
                 Tc[0] = zero4();
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    if (b == j) Tc[b] = load_tile_rl(&Lm[16 * b * LDL + 16 * b], LDL, lane);   // T(j, j)
+                    if (b == j) Tc[b] = load_tile_rl(lmb(b, b), LDB, lane);   // T(j, j)
 #pragma unroll
                 for (int i = 1; i < NB; ++i) {
                     if (i <= j || (SUB > 1 && i / BC != j / BC)) continue;
                     floatx4 X = zero4();
 #pragma unroll
                     for (int kb = 0; kb < NB - 1; ++kb)
-                        if (kb >= j && kb < i) X = mm16<float>(&Lm[16 * i * LDL + 16 * kb], LDL, Tc[kb], X, lane);
-                    const floatx4 t = mm16<float>(&Lm[16 * i * LDL + 16 * i], LDL, X, zero4(), lane);
+                        if (kb >= j && kb < i) X = mm16<float>(lmb(i, kb), LDB, Tc[kb], X, lane);
+                    const floatx4 t = mm16<float>(lmb(i, i), LDB, X, zero4(), lane);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) Tc[i][rr] = -t[rr];
                 }
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
                     if (i <= j || (SUB > 1 && i / BC != j / BC)) continue;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        Lm[(16 * i + 4 * (lane >> 4) + rr) * LDL + 16 * j + (lane & 15)] = Tc[i][rr];
+                        lmb(i, j)[(4 * (lane >> 4) + rr) * LDB + (lane & 15)] = Tc[i][rr];
                 }
             }
             __syncthreads();
@@ -495,7 +508,7 @@ __global__ __launch_bounds__(64 * gen_waves(gen_tile(CH, GATE))) void gen_intra_
             const int lb = p / (kKS / 16), cb = p % (kKS / 16);
             floatx4 acc = zero4();
             for (int mb = SUB == 1 ? 0 : (lb / BC) * BC; mb <= lb; ++mb)
-                acc = mm16<T>(&Lm[16 * lb * LDL + 16 * mb], LDL, load_tile_rl(&xs[16 * mb * kLDS + 16 * cb], kLDS, lane),
+                acc = mm16<T>(lmb(lb, mb), LDB, load_tile_rl(&xs[16 * mb * kLDS + 16 * cb], kLDS, lane),
                               acc, lane);
             mfma_settle();
             const int sc = chunk_of(16 * lb);              // the chunk of block row lb
